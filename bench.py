@@ -1,0 +1,168 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV decode hot path on one MI355X.
+
+One step = one pass of the hot path over one synthetic batch:
+  kv_append of the batch's current tokens (one per sequence), then
+  paged_decode_attn over every sequence's cached keys (split-KV partitions
+  plus the log-sum-exp merge).
+Default workload: Llama-3.1-8B-shaped single-layer decode, batch 64,
+32 query / 8 KV heads, head_dim 128, context ~ U[512, 4096], 16-token
+blocks, shuffled pool of used blocks + 10 % (about 0.65 GB of bf16 K/V, more
+than the 256 MB Infinity Cache, so the pool is read from HBM every step).
+
+Prints ONE JSON line.  `value` = KV bytes the decode must read
+(sum_i ctx_i * 2 * Hkv * D * 2) / time per step, in GB/s; seq-steps/s and
+the split into kernels go in extra keys.  Inputs are resident in HBM before
+the timed region starts.
+"""
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def workload_by_name(name):
+    from paged_kv_cache_98_amd import workloads as W
+    table = {
+        "llama8b_decode": lambda: W.llama8b_decode(),
+        "long_context_decode": lambda: W.long_context_decode(),
+        "llama70b_decode_bs16": lambda: W.llama70b_decode(block_size=16),
+        "llama70b_decode_bs32": lambda: W.llama70b_decode(block_size=32),
+        "tiny_decode": lambda: W.tiny_decode(),
+    }
+    if name not in table:
+        raise SystemExit(f"unknown workload {name}; choose from {sorted(table)}")
+    return table[name]()
+
+
+def cpu_baseline(batch, w, reps=2):
+    """The fp64 oracle, as it stands, on the same batch (host copies)."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    q = batch.q.cpu()
+    kc, vc = batch.k_cache.cpu(), batch.v_cache.cpu()
+    bt, cl = batch.block_table.cpu(), batch.context_lens.cpu()
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.paged_attention(q, kc, vc, bt, cl, w.scale, num_threads=threads)
+        times.append(time.perf_counter() - t0)
+    t = min(times)
+    kv_bytes = sum(w.context_lens) * w.kv_token_bytes()
+    return {"value": round(kv_bytes / t / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"whole {w.name} batch ({w.num_seqs} seqs, sum ctx {sum(w.context_lens)}), "
+                      f"fp64 C + OpenMP, best of {reps}: {t:.3f} s per batch "
+                      f"({w.num_seqs / t:.2f} seq-steps/s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama8b_decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
+              "supported (decode shards by sequence or KV head with no exchange, see the "
+              "design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from paged_kv_cache_98_amd import binding as pkv
+    from paged_kv_cache_98_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workload_by_name(args.workload)
+    print(f"[bench] workload {w.describe()}", file=sys.stderr, flush=True)
+    b = W.materialize(w, device=dev, poison=False)
+    ws_bytes = pkv.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.max_context_len)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        pkv.kv_append(b.k_new, b.v_new, b.slot_mapping, b.k_cache, b.v_cache, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        pkv.paged_decode_attn(b.q, b.k_cache, b.v_cache, b.block_table, b.context_lens,
+                              w.scale, max_context_len=w.max_context_len, out=out,
+                              workspace=ws, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps, bracketed by device synchronisation
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    append_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    decode_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_per_step = wall * 1e3 / args.steps
+    kv_bytes = sum(w.context_lens) * w.kv_token_bytes()
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    dec_avg = statistics.mean(decode_ms)
+    achieved = kv_bytes / (dec_avg * 1e-3) / 1e9
+    print(f"[bench] step {ms_per_step * 1e3:.1f} us | decode avg {dec_avg * 1e3:.1f} us "
+          f"(median {statistics.median(decode_ms) * 1e3:.1f}, p10 "
+          f"{sorted(decode_ms)[len(decode_ms) // 10] * 1e3:.1f}, p90 "
+          f"{sorted(decode_ms)[(9 * len(decode_ms)) // 10] * 1e3:.1f}) | append avg "
+          f"{statistics.mean(append_ms) * 1e3:.1f} us | decode KV {achieved:.0f} GB/s",
+          file=sys.stderr, flush=True)
+
+    rec = {
+        "metric": "paged decode attn: achieved KV HBM GB/s (% of MI355X peak) + seq-steps/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "sum_context": sum(w.context_lens),
+                   "max_context": w.max_context_len, "num_blocks": w.num_blocks,
+                   "seed": w.seed},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "seq_steps_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
+        "kernels_us": {"kv_append": round(statistics.mean(append_ms) * 1e3, 2),
+                       "paged_decode_attn": round(dec_avg * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "kernel": "paged_decode_attn (partition + merge kernels)",
+                     "algorithmic_bytes_per_launch": kv_bytes},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(b, w)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,197 @@
+// api.hip -- the C ABI of libpagedkv.so (declared in include/pagedkv.h):
+// argument validation on the host, then the launch on the caller's stream.
+// Every check runs before anything is enqueued, so all error statuses can be
+// exercised without a GPU.
+#include <math.h>
+#include <stdint.h>
+
+#include "pagedkv.h"
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int max_partitions(int max_context_len) {
+    const int p = (max_context_len + pkv::kPartitionTokens - 1) / pkv::kPartitionTokens;
+    return p < 1 ? 1 : p;
+}
+
+// Shape checks shared by decode and prefill.
+int check_attention_shape(int max_blocks_per_seq, int max_context_len, int num_seqs,
+                          int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                          int out_dtype) {
+    if (out_dtype != PKV_OUT_F32 && out_dtype != PKV_OUT_BF16) return PKV_ERR_UNSUPPORTED;
+    if (head_dim != pkv::kHeadDim) return PKV_ERR_UNSUPPORTED;
+    if (block_size != 16 && block_size != 32) return PKV_ERR_UNSUPPORTED;
+    if (num_seqs < 0 || num_seqs > 65535 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+        max_blocks_per_seq < 0 || max_context_len < 0)
+        return PKV_ERR_SHAPE;
+    if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+    if (!supported_group(num_q_heads / num_kv_heads)) return PKV_ERR_UNSUPPORTED;
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PKV_ERR_SHAPE;
+    return PKV_OK;
+}
+
+int to_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH; }
+
+}  // namespace
+
+namespace pkv {
+
+size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim, int max_context_len) {
+    if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+    const int parts = max_partitions(max_context_len);
+    if (parts <= 1) return 0;
+    const size_t slots = (size_t)num_seqs * num_q_heads * parts;
+    return align_up(slots * sizeof(float2), 256) + slots * (size_t)head_dim * sizeof(float);
+}
+
+}  // namespace pkv
+
+extern "C" {
+
+const char* pkv_status_string(int status) {
+    switch (status) {
+        case PKV_OK: return "ok";
+        case PKV_ERR_NULL: return "a required pointer is NULL";
+        case PKV_ERR_SHAPE: return "inconsistent sizes";
+        case PKV_ERR_UNSUPPORTED: return "unsupported head_dim, block_size, group size or dtype";
+        case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+        case PKV_ERR_LAUNCH: return "HIP launch error";
+        case PKV_ERR_ALIGN: return "a bf16 or output array is not 16-byte aligned";
+        default: return "unknown status";
+    }
+}
+
+int pkv_version(void) { return kVersion; }
+
+int pkv_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                  int64_t num_tokens, void* k_cache, void* v_cache, int64_t num_blocks,
+                  int block_size, int num_kv_heads, int head_dim, void* stream) {
+    if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0) return PKV_ERR_SHAPE;
+    if (head_dim != pkv::kHeadDim) return PKV_ERR_UNSUPPORTED;
+    if (block_size != 16 && block_size != 32) return PKV_ERR_UNSUPPORTED;
+    if (num_tokens == 0) return PKV_OK;
+    if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PKV_ERR_NULL;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+        return PKV_ERR_ALIGN;
+    pkv::AppendArgs a;
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.v_new = static_cast<const uint16_t*>(v_new);
+    a.slot_mapping = slot_mapping;
+    a.num_tokens = num_tokens;
+    a.k_cache = static_cast<uint16_t*>(k_cache);
+    a.v_cache = static_cast<uint16_t*>(v_cache);
+    a.row_elems = num_kv_heads * head_dim;
+    return to_status(pkv::launch_kv_append(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t pkv_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim,
+                                  int max_context_len) {
+    return pkv::decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len);
+}
+
+int pkv_paged_decode_attn(void* out, int out_dtype, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* block_table,
+                          int max_blocks_per_seq, const int32_t* context_lens,
+                          int max_context_len, int num_seqs, int num_q_heads, int num_kv_heads,
+                          int head_dim, int block_size, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    int st = check_attention_shape(max_blocks_per_seq, max_context_len, num_seqs, num_q_heads,
+                                   num_kv_heads, head_dim, block_size, out_dtype);
+    if (st != PKV_OK) return st;
+    if (num_seqs == 0) return PKV_OK;
+    if (!out || !q || !k_cache || !v_cache || !block_table || !context_lens) return PKV_ERR_NULL;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+        return PKV_ERR_ALIGN;
+    const size_t need = pkv::decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                                    max_context_len);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(workspace)) return PKV_ERR_ALIGN;
+
+    pkv::DecodeArgs a;
+    a.out = out;
+    a.out_bf16 = out_dtype == PKV_OUT_BF16;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_cache = static_cast<const uint16_t*>(k_cache);
+    a.v_cache = static_cast<const uint16_t*>(v_cache);
+    a.block_table = block_table;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.context_lens = context_lens;
+    a.max_context_len = max_context_len;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.block_size = block_size;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.max_parts = max_partitions(max_context_len);
+    const size_t slots = (size_t)num_seqs * num_q_heads * a.max_parts;
+    a.part_ml = need ? static_cast<float2*>(workspace) : nullptr;
+    a.part_acc = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                 align_up(slots * sizeof(float2), 256))
+                      : nullptr;
+    return to_status(pkv::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t pkv_prefill_workspace_bytes(int num_seqs, int num_q_tokens, int num_q_heads, int head_dim,
+                                   int max_context_len) {
+    (void)num_seqs;
+    (void)num_q_tokens;
+    (void)num_q_heads;
+    (void)head_dim;
+    (void)max_context_len;
+    return 0;
+}
+
+int pkv_paged_prefill_attn(void* out, int out_dtype, const void* q, const int32_t* cu_q_lens,
+                           const void* k_cache, const void* v_cache, const int32_t* block_table,
+                           int max_blocks_per_seq, const int32_t* context_lens,
+                           int max_context_len, int max_q_len, int num_q_tokens, int num_seqs,
+                           int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                           float scale, int causal, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    int st = check_attention_shape(max_blocks_per_seq, max_context_len, num_seqs, num_q_heads,
+                                   num_kv_heads, head_dim, block_size, out_dtype);
+    if (st != PKV_OK) return st;
+    if (max_q_len < 0 || num_q_tokens < 0) return PKV_ERR_SHAPE;
+    if (max_q_len > max_context_len) return PKV_ERR_SHAPE;
+    if ((int64_t)num_q_tokens > (int64_t)num_seqs * max_q_len) return PKV_ERR_SHAPE;
+    if (num_seqs == 0 || num_q_tokens == 0) return PKV_OK;
+    if (!out || !q || !cu_q_lens || !k_cache || !v_cache || !block_table || !context_lens)
+        return PKV_ERR_NULL;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+        return PKV_ERR_ALIGN;
+
+    pkv::PrefillArgs a;
+    a.out = out;
+    a.out_bf16 = out_dtype == PKV_OUT_BF16;
+    a.q = static_cast<const uint16_t*>(q);
+    a.cu_q_lens = cu_q_lens;
+    a.k_cache = static_cast<const uint16_t*>(k_cache);
+    a.v_cache = static_cast<const uint16_t*>(v_cache);
+    a.block_table = block_table;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.context_lens = context_lens;
+    a.max_context_len = max_context_len;
+    a.max_q_len = max_q_len;
+    a.num_q_tokens = num_q_tokens;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.block_size = block_size;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.causal = causal != 0;
+    return to_status(pkv::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

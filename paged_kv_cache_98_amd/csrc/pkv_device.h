@@ -1,0 +1,69 @@
+// pkv_device.h -- device-side helpers shared by the gfx950 kernels of
+// libpagedkv: bf16 unpacking, the bf16 dot2 instruction, and 16-lane row
+// reductions built from DPP moves (a CDNA wave is 64 lanes = 4 rows of 16).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kHeadDim = 128;
+// Split-KV partition length in tokens.  A multiple of every supported block
+// size, so partitions start on block boundaries.
+constexpr int kPartitionTokens = 512;
+// Tokens per inner tile of the decode loop: 16 tokens = 4 KB of K (or V) for
+// one KV head, moved by one wave as four 128-bit loads per lane.
+constexpr int kTileTokens = 16;
+// A finite "minus infinity" for running maxima, so that a row that has seen
+// no key yet never produces exp2(-inf - -inf).
+constexpr float kNegBig = -1.0e30f;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 value of the low / high bf16 of a packed pair (exact: a bf16 is the
+// top half of the fp32 with the same value).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// c + a.lo * b.lo + a.hi * b.hi with bf16 pairs, fp32 accumulate
+// (v_dot2c_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
+}
+
+// DPP controls: quad permutations and rotations inside a 16-lane row.
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppRowRor4 = 0x124;  // row_ror:4
+constexpr int kDppRowRor8 = 0x128;  // row_ror:8
+
+// Sum over the 16 lanes of each row; every lane of the row receives it.
+__device__ __forceinline__ float row_sum16(float x) {
+    x += dpp_mov<kDppQuadXor1>(x);
+    x += dpp_mov<kDppQuadXor2>(x);
+    x += dpp_mov<kDppRowRor4>(x);
+    x += dpp_mov<kDppRowRor8>(x);
+    return x;
+}
+
+// Exchange across rows: value of lane ^ 16 / lane ^ 32 (LDS-crossbar permute).
+__device__ __forceinline__ float xor_lane(float x, int mask) {
+    int lane = __lane_id();
+    return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(x)));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+}  // namespace pkv

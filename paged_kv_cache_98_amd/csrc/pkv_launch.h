@@ -1,0 +1,70 @@
+// pkv_launch.h -- internal interface between the C-ABI entry points
+// (api.hip) and the kernel launchers.  Arguments arrive here already
+// validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct AppendArgs {
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    const int64_t* slot_mapping;
+    int64_t num_tokens;
+    uint16_t* k_cache;
+    uint16_t* v_cache;
+    int row_elems;  // num_kv_heads * head_dim
+};
+
+struct DecodeArgs {
+    void* out;
+    bool out_bf16;
+    const uint16_t* q;
+    const uint16_t* k_cache;
+    const uint16_t* v_cache;
+    const int32_t* block_table;
+    int max_blocks_per_seq;
+    const int32_t* context_lens;
+    int max_context_len;
+    int num_seqs;
+    int num_q_heads;
+    int num_kv_heads;
+    int block_size;
+    float scale_log2;  // scale * log2(e)
+    int max_parts;     // ceil(max_context_len / partition), >= 1
+    float2* part_ml;   // [num_seqs][num_q_heads][max_parts] (m, l)
+    float* part_acc;   // [num_seqs][num_q_heads][max_parts][head_dim]
+};
+
+struct PrefillArgs {
+    void* out;
+    bool out_bf16;
+    const uint16_t* q;
+    const int32_t* cu_q_lens;
+    const uint16_t* k_cache;
+    const uint16_t* v_cache;
+    const int32_t* block_table;
+    int max_blocks_per_seq;
+    const int32_t* context_lens;
+    int max_context_len;
+    int max_q_len;
+    int num_q_tokens;
+    int num_seqs;
+    int num_q_heads;
+    int num_kv_heads;
+    int block_size;
+    float scale_log2;
+    bool causal;
+};
+
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+// Bytes of decode workspace for these sizes (0 when no split is needed).
+size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim, int max_context_len);
+
+}  // namespace pkv

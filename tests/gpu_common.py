@@ -1,0 +1,72 @@
+"""Helpers for the GPU parity tests: the tolerance check and sampled-oracle
+plumbing.  The oracle is only ever fed generator inputs, never HIP outputs."""
+import numpy as np
+import torch
+
+import oracle
+
+MAX_ABS = 5e-3   # parity bar for fp32 outputs against the fp64 oracle
+REL_L2 = 1e-3
+
+
+def parity(gpu: torch.Tensor, ref: np.ndarray, max_abs=MAX_ABS, rel_l2=REL_L2, what=""):
+    g = gpu.detach().to(torch.float64).cpu().numpy()
+    assert g.shape == ref.shape, (what, g.shape, ref.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    err = np.abs(g - ref)
+    nref = np.linalg.norm(ref)
+    rel = np.linalg.norm(g - ref) / nref if nref > 0 else np.linalg.norm(g - ref)
+    print(f"[parity] {what}: max_abs={err.max():.3e} rel_l2={rel:.3e}", flush=True)
+    assert err.max() <= max_abs, f"{what}: max-abs {err.max():.3e} > {max_abs}"
+    assert rel <= rel_l2, f"{what}: rel-L2 {rel:.3e} > {rel_l2}"
+    return err.max(), rel
+
+
+def bf16_parity(gpu_bf16: torch.Tensor, ref: np.ndarray, what=""):
+    """bf16 output: within one bf16 rounding (2^-8 relative) of the fp64 value,
+    plus fp32 noise."""
+    g = gpu_bf16.detach().to(torch.float64).cpu().numpy()
+    assert np.all(np.isfinite(g))
+    bound = np.abs(ref) * 2.0 ** -8 + 1e-5
+    bad = np.abs(g - ref) > bound
+    print(f"[bf16] {what}: worst ratio {(np.abs(g - ref) / bound).max():.3f}", flush=True)
+    assert not bad.any(), f"{what}: {bad.sum()} bf16 outputs off by more than one rounding"
+
+
+def compact_subset(batch, seqs):
+    """Host copies of the blocks `seqs` use, with their block tables remapped
+    onto a compact pool (the oracle is invariant to physical relabelling).
+    Returns (k_pool, v_pool, block_table, context_lens, kept_rows_of_q)."""
+    w = batch.workload
+    bt = batch.block_table.cpu()
+    ctx = batch.context_lens.cpu()
+    rows = bt[seqs]
+    used = torch.unique(rows[rows >= 0]).to(torch.int64)
+    remap = torch.full((w.num_blocks,), -1, dtype=torch.int64)
+    remap[used] = torch.arange(used.numel())
+    nbt = torch.where(rows >= 0, remap[rows.clamp(min=0).to(torch.int64)], torch.tensor(-1))
+    dev_used = used.to(batch.k_cache.device)
+    k_sub = batch.k_cache.index_select(0, dev_used).cpu()
+    v_sub = batch.v_cache.index_select(0, dev_used).cpu()
+    return k_sub, v_sub, nbt.to(torch.int32), ctx[seqs]
+
+
+def oracle_decode_sample(batch, seqs):
+    """fp64 oracle for decode rows `seqs` of a (possibly huge) GPU batch."""
+    k_sub, v_sub, bt, ctx = compact_subset(batch, seqs)
+    q = batch.q.cpu()[seqs]
+    return oracle.paged_attention(q, k_sub, v_sub, bt, ctx, batch.workload.scale)
+
+
+def oracle_prefill_sample(batch, seqs, causal=True):
+    """fp64 oracle for sequences `seqs` (all their query rows) of a batch."""
+    k_sub, v_sub, bt, ctx = compact_subset(batch, seqs)
+    cu = batch.cu_q_lens.cpu()
+    q_all = batch.q.cpu()
+    rows = torch.cat([torch.arange(int(cu[i]), int(cu[i + 1])) for i in seqs])
+    lens = torch.tensor([int(cu[i + 1] - cu[i]) for i in seqs])
+    ncu = torch.zeros(len(seqs) + 1, dtype=torch.int32)
+    ncu[1:] = torch.cumsum(lens, 0)
+    out = oracle.paged_attention(q_all[rows], k_sub, v_sub, bt, ctx, batch.workload.scale,
+                                 cu_q_lens=ncu, causal=causal)
+    return out, rows
