@@ -87,7 +87,8 @@ def main():
     w = workload_by_name(args.workload)
     print(f"[bench] workload {w.describe()}", file=sys.stderr, flush=True)
     b = W.materialize(w, device=dev, poison=False)
-    ws_bytes = pkv.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.max_context_len)
+    ws_bytes = pkv.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads,
+                                          w.max_context_len)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
@@ -156,7 +157,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None,
-                     "kernel": "paged_decode_attn (partition + merge kernels)",
+                     "kernel": "paged_decode_attn (stream-K decode + merge kernels)",
                      "algorithmic_bytes_per_launch": kv_bytes},
     }
     if not args.no_cpu_baseline:

@@ -59,7 +59,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_kv_append.restype = _i32
     lib.pkv_kv_append.argtypes = [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _vp]
     lib.pkv_decode_workspace_bytes.restype = _sz
-    lib.pkv_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
+    lib.pkv_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
     lib.pkv_paged_decode_attn.restype = _i32
     lib.pkv_paged_decode_attn.argtypes = [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
                                           _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]
@@ -124,10 +124,10 @@ def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tens
                              _stream(stream)))
 
 
-def decode_workspace_bytes(num_seqs: int, num_q_heads: int, max_context_len: int,
-                           head_dim: int = 128) -> int:
-    return load_library().pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
-                                                      max_context_len)
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                           max_context_len: int, head_dim: int = 128) -> int:
+    return load_library().pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
+                                                      head_dim, max_context_len)
 
 
 def prefill_workspace_bytes(num_seqs: int, num_q_tokens: int, num_q_heads: int,
@@ -151,7 +151,7 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         max_context_len = int(context_lens.max().item()) if b else 0
     if out is None:
         out = torch.empty((b, hq, d), dtype=out_dtype, device=q.device)
-    need = lib.pkv_decode_workspace_bytes(b, hq, d, max_context_len)
+    need = lib.pkv_decode_workspace_bytes(b, hq, hkv, d, max_context_len)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None

@@ -11,18 +11,16 @@
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0
+// Decode keeps the per-sequence tile prefix sums in LDS: (num_seqs + 1) int32
+// must fit the 64 KB a workgroup may allocate.
+constexpr int kMaxDecodeSeqs = 16383;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-
-int max_partitions(int max_context_len) {
-    const int p = (max_context_len + pkv::kPartitionTokens - 1) / pkv::kPartitionTokens;
-    return p < 1 ? 1 : p;
-}
 
 // Shape checks shared by decode and prefill.
 int check_attention_shape(int max_blocks_per_seq, int max_context_len, int num_seqs,
@@ -43,18 +41,6 @@ int check_attention_shape(int max_blocks_per_seq, int max_context_len, int num_s
 int to_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH; }
 
 }  // namespace
-
-namespace pkv {
-
-size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim, int max_context_len) {
-    if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
-    const int parts = max_partitions(max_context_len);
-    if (parts <= 1) return 0;
-    const size_t slots = (size_t)num_seqs * num_q_heads * parts;
-    return align_up(slots * sizeof(float2), 256) + slots * (size_t)head_dim * sizeof(float);
-}
-
-}  // namespace pkv
 
 extern "C" {
 
@@ -94,9 +80,11 @@ int pkv_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapp
     return to_status(pkv::launch_kv_append(a, static_cast<hipStream_t>(stream)));
 }
 
-size_t pkv_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim,
+size_t pkv_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                                   int max_context_len) {
-    return pkv::decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len);
+    if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0) return 0;
+    return pkv::decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                       max_context_len);
 }
 
 int pkv_paged_decode_attn(void* out, int out_dtype, const void* q, const void* k_cache,
@@ -108,14 +96,15 @@ int pkv_paged_decode_attn(void* out, int out_dtype, const void* q, const void* k
     int st = check_attention_shape(max_blocks_per_seq, max_context_len, num_seqs, num_q_heads,
                                    num_kv_heads, head_dim, block_size, out_dtype);
     if (st != PKV_OK) return st;
+    if (num_seqs > kMaxDecodeSeqs) return PKV_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PKV_OK;
     if (!out || !q || !k_cache || !v_cache || !block_table || !context_lens) return PKV_ERR_NULL;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
         return PKV_ERR_ALIGN;
-    const size_t need = pkv::decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+    const size_t need = pkv::decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                     max_context_len);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
-    if (need > 0 && !aligned16(workspace)) return PKV_ERR_ALIGN;
+    if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PKV_ERR_ALIGN;
 
     pkv::DecodeArgs a;
     a.out = out;
@@ -132,12 +121,10 @@ int pkv_paged_decode_attn(void* out, int out_dtype, const void* q, const void* k
     a.num_kv_heads = num_kv_heads;
     a.block_size = block_size;
     a.scale_log2 = scale * 1.4426950408889634f;
-    a.max_parts = max_partitions(max_context_len);
-    const size_t slots = (size_t)num_seqs * num_q_heads * a.max_parts;
-    a.part_ml = need ? static_cast<float2*>(workspace) : nullptr;
-    a.part_acc = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                                 align_up(slots * sizeof(float2), 256))
-                      : nullptr;
+    a.cum = static_cast<int32_t*>(workspace);
+    a.records = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                         align_up((size_t)(num_seqs + 1) * sizeof(int32_t), 256));
+    a.max_workers = pkv::decode_max_workers(num_seqs, num_kv_heads, max_context_len);
     return to_status(pkv::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 

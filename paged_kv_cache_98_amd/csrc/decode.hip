@@ -1,5 +1,5 @@
-// decode.hip -- paged decode attention for gfx950: split-KV partitions with
-// a single-pass online softmax, then a log-sum-exp merge.
+// decode.hip -- paged decode attention for gfx950 with a single-pass online
+// softmax and a stream-K split of the keys over persistent waves.
 //
 // What it computes ("LLM 推理优化技术全景", "Flash Attention 深度剖析"): for
 // every sequence i and query head h,
@@ -8,30 +8,32 @@
 // over the sequence's context_lens[i] keys, which live in 16- or 32-token
 // physical blocks found through the block table ("LLM 推理引擎深度解析 ...",
 // section 2.1; "让 Agent 跑得快", section 五).  The keys are visited once, a
-// tile at a time, keeping a running maximum m and running sum l and
+// 16-token tile at a time, keeping a running maximum m and running sum l and
 // rescaling the accumulator by exp(m_old - m_new) whenever m grows (the
 // page's "在线 Softmax"); the division by l is deferred to the very end as in
-// its "Flash Attention v2 的改进".  Long contexts are cut into 512-token
-// partitions processed in parallel (the sequence-axis parallelism of the
-// same section); each partition leaves (m, l, unnormalised acc) and a merge
-// kernel combines them with the same exp(m_k - M) rescale.
+// its "Flash Attention v2 的改进".
 //
-// Work decomposition (one wavefront = 64 lanes = 4 rows of 16 lanes):
-//   * one wave per (sequence, KV head, partition); a workgroup holds the
-//     waves of 1, 2 or 4 consecutive KV heads of the same (sequence,
-//     partition), so the workgroup reads whole 2 KB token rows of the pool;
-//   * the G = Hq/Hkv query heads of the KV head are handled by the same wave,
-//     so each K/V byte is read from HBM once per KV head (GQA grouping);
-//   * a 16-token tile of one head is 4 KB of K and 4 KB of V: every lane
-//     moves 4 x 16 B of each.  Lane (row r, col c) holds dims 8c..8c+7 of
-//     tokens 4i + r, i = 0..3; its 16-lane row reduces the QK partial sums
-//     with DPP adds;
-//   * each 16-lane row is its own online-softmax stream (tokens = r mod 4)
-//     with its own m, l, acc; the four rows are merged at the end of the
-//     partition, so no cross-row traffic happens inside the loop;
-//   * the next tile's K/V loads are issued before the current tile's math.
-// Scores are kept in the log2 domain: s * scale * log2(e), exponentials are
-// v_exp_f32 (2^x).
+// Split of the work (the sequence-axis parallelism of that section, taken
+// to its balanced limit):
+//   * a segment is the keys of one (sequence, KV head); the G = Hq/Hkv query
+//     heads of the KV head ride along, so each K/V byte is read from HBM once
+//     per KV head (GQA grouping);
+//   * all segments' 16-token tiles are laid end to end, sequence-major, and
+//     cut into W equal contiguous ranges, one per persistent wave (W = what
+//     the chip holds at once).  A wave walks its range segment by segment:
+//     a segment it covers whole is finalised in place; a piece of a segment
+//     shared with other waves leaves (m, l, unnormalised acc) in the
+//     workspace, and the merge kernel combines the pieces with the same
+//     exp(m_k - M) rescale (a log-sum-exp merge);
+//   * so every wave streams the same number of bytes, no workgroup is
+//     launched without work, and long contexts split across many waves.
+// Inside a wave (64 lanes = 4 rows of 16): a tile of one head is 4 KB of K
+// and 4 KB of V, four 128-bit loads per lane each; lane (row r, col c) holds
+// dims 8c..8c+7 of tokens 4i + r, i = 0..3; the 16-lane row reduces the QK
+// partial sums with DPP adds; each row is its own online-softmax stream
+// (tokens = r mod 4) merged with the other rows at the end of a piece; the
+// next tile's loads are issued before the current tile's math.  Scores are
+// in the log2 domain (scale * log2 e folded in), exponentials are v_exp_f32.
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -45,14 +47,6 @@ struct Tile {
     uint4 k[kLoads];
     uint4 v[kLoads];
 };
-
-// Element offset of physical tile `tile` (16 tokens) of the partition.
-template <int BS>
-__device__ __forceinline__ size_t tile_base(int ids_reg, int tile, size_t row_elems) {
-    const int phys = __builtin_amdgcn_readlane(ids_reg, (tile * kTileTokens) / BS);
-    const int row0 = (tile * kTileTokens) % BS;
-    return ((size_t)phys * BS + row0) * row_elems;
-}
 
 __device__ __forceinline__ void load_tile(Tile& t, const uint16_t* __restrict__ kc,
                                           const uint16_t* __restrict__ vc, size_t base,
@@ -72,13 +66,16 @@ struct State {
     float m[G];       // running max (log2 domain), uniform across the row
     float l[G];       // running sum, uniform across the row
     float acc[G][8];  // unnormalised output, dims 8c..8c+7 of this lane
+    float alpha[G];   // last rescale factor exp2(m_old - m_new)
 };
 
 // One 16-token tile: QK, online-softmax update, PV.  `ntok_left` is the
 // number of valid tokens from the start of this tile (>= 16 for a full one).
+// Raw scores are maximised unscaled (the scale is >= 0 after the sign of q
+// absorbed a negative one) and scaled inside the exponent's FMA.
 template <int G, bool PARTIAL>
 __device__ __forceinline__ void process_tile(State<G>& st, const Tile& t, const uint4 (&qv)[G],
-                                             float scale_log2, int row, int ntok_left) {
+                                             float c, int row, int ntok_left) {
     float s[kLoads][G];
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
@@ -88,31 +85,43 @@ __device__ __forceinline__ void process_tile(State<G>& st, const Tile& t, const 
             d = dot2_bf16(t.k[i].y, qv[g].y, d);
             d = dot2_bf16(t.k[i].z, qv[g].z, d);
             d = dot2_bf16(t.k[i].w, qv[g].w, d);
-            d = row_sum16(d);
-            s[i][g] = d * scale_log2;
+            s[i][g] = row_sum16(d);
         }
         if (PARTIAL) {
+            // Tokens past the end may hold anything: they must not raise the
+            // maximum (lowest finite value, so that a zero scale stays finite)
+            // and get p = 0 below.
             const bool valid = (4 * i + row) < ntok_left;
 #pragma unroll
-            for (int g = 0; g < G; ++g) s[i][g] = valid ? s[i][g] : -INFINITY;
+            for (int g = 0; g < G; ++g) s[i][g] = valid ? s[i][g] : -3.402823466e38f;
         }
     }
     float p[kLoads][G];
+    bool grew = false;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        float bm = fmaxf(fmaxf(s[0][g], s[1][g]), fmaxf(s[2][g], s[3][g]));
+        const float bm = fmaxf(fmaxf(s[0][g], s[1][g]), fmaxf(s[2][g], s[3][g])) * c;
         const float mn = fmaxf(st.m[g], bm);
+        grew |= mn > st.m[g];
         const float alpha = fast_exp2(st.m[g] - mn);
         st.m[g] = mn;
         float sum = 0.0f;
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) {
-            p[i][g] = fast_exp2(s[i][g] - mn);
+            p[i][g] = fast_exp2(fmaf(s[i][g], c, -mn));
+            if (PARTIAL) p[i][g] = (4 * i + row) < ntok_left ? p[i][g] : 0.0f;
             sum += p[i][g];
         }
-        st.l[g] = st.l[g] * alpha + sum;
+        st.l[g] = fmaf(st.l[g], alpha, sum);
+        st.alpha[g] = alpha;
+    }
+    // The accumulator needs the exp(m_old - m_new) rescale only when some
+    // running maximum moved; after the first tiles that is rare.
+    if (__any(grew)) {
 #pragma unroll
-        for (int d = 0; d < 8; ++d) st.acc[g][d] *= alpha;
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int d = 0; d < 8; ++d) st.acc[g][d] *= st.alpha[g];
     }
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
@@ -138,11 +147,11 @@ __device__ __forceinline__ void process_tile(State<G>& st, const Tile& t, const 
 
 template <int G>
 __device__ __forceinline__ void process_any(State<G>& st, const Tile& t, const uint4 (&qv)[G],
-                                            float scale_log2, int row, int ntok_left) {
+                                            float c, int row, int ntok_left) {
     if (ntok_left >= kTileTokens)
-        process_tile<G, false>(st, t, qv, scale_log2, row, ntok_left);
+        process_tile<G, false>(st, t, qv, c, row, ntok_left);
     else
-        process_tile<G, true>(st, t, qv, scale_log2, row, ntok_left);
+        process_tile<G, true>(st, t, qv, c, row, ntok_left);
 }
 
 template <bool OUT_BF16>
@@ -161,182 +170,329 @@ __device__ __forceinline__ void store8(void* out, size_t elem, const float (&x)[
     }
 }
 
-// Grid: (max_partitions, num_kv_heads / waves_per_group, num_seqs); block:
-// 64 * waves_per_group threads.
+template <bool OUT_BF16>
+__device__ __forceinline__ void store1(void* out, size_t elem, float x) {
+    if (OUT_BF16) static_cast<uint16_t*>(out)[elem] = f32_to_bf16_rne(x);
+    else static_cast<float*>(out)[elem] = x;
+}
+
+constexpr int kWaves = 4;                 // independent waves per workgroup
+constexpr int kRecStride = kHeadDim + 4;  // floats per record: acc[128], m, l, 2 pad
+constexpr int kMinTilesPerWorker = 4;   // fewer waves for tiny batches
+constexpr int64_t kMaxWorkers = 8192;    // >= waves an MI355X holds (256 CUs x 32)
+
+// Worker w owns global tiles [worker_start(w), worker_start(w + 1)).
+__device__ __forceinline__ int64_t worker_start(int64_t w, int64_t U, int64_t W) {
+    return (w * U) / W;
+}
+// The worker whose range holds tile t.
+__device__ __forceinline__ int64_t worker_of(int64_t t, int64_t U, int64_t W) {
+    return ((t + 1) * W - 1) / U;
+}
+
+__device__ __forceinline__ int clamp_ctx(int ctx, int max_context_len) {
+    return ctx < 0 ? 0 : (ctx > max_context_len ? max_context_len : ctx);
+}
+
+// Sliding window over a block-table row: lane j of `cur` holds the id of
+// block base + j, lane j of `nxt` that of base + 64 + j.  Tiles are visited
+// in increasing order, so the window only ever moves forward by 64.
+struct IdWindow {
+    const int32_t* row;
+    int nblk;
+    int base;
+    int cur;
+    int nxt;
+    __device__ __forceinline__ void init(const int32_t* r, int n, int first, int lane) {
+        row = r;
+        nblk = n;
+        base = first;
+        cur = first + lane < n ? r[first + lane] : 0;
+        nxt = first + 64 + lane < n ? r[first + 64 + lane] : 0;
+    }
+    __device__ __forceinline__ int get(int blk, int lane) {
+        if (blk >= base + 64) {
+            cur = nxt;
+            base += 64;
+            nxt = base + 64 + lane < nblk ? row[base + 64 + lane] : 0;
+        }
+        return __builtin_amdgcn_readlane(cur, blk - base);
+    }
+};
+
+template <int BS>
+__device__ __forceinline__ size_t tile_elem(IdWindow& ids, int tile, size_t row_elems, int lane) {
+    const int tok = tile * kTileTokens;
+    const int phys = ids.get(tok / BS, lane);
+    return ((size_t)phys * BS + (tok % BS)) * row_elems;
+}
+
+// Grid: num_workers / 4 workgroups of 4 waves; dynamic LDS (num_seqs + 1)
+// int32 for the tile prefix sums.  Records: [W][2][G][kRecStride] floats.
 template <int BS, int G, bool OUT_BF16>
-__global__ void __launch_bounds__(256)
-decode_partition_kernel(void* __restrict__ out, float2* __restrict__ part_ml,
-                        float* __restrict__ part_acc, const uint16_t* __restrict__ q,
-                        const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
-                        const int32_t* __restrict__ block_table, int max_blocks_per_seq,
-                        const int32_t* __restrict__ context_lens, int max_context_len,
-                        int num_q_heads, int num_kv_heads, float scale_log2, int max_parts) {
+__global__ void __launch_bounds__(64 * kWaves)
+decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* __restrict__ cum_out,
+                      const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
+                      const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
+                      int max_blocks_per_seq, const int32_t* __restrict__ context_lens,
+                      int max_context_len, int num_seqs, int num_q_heads, int num_kv_heads,
+                      float scale_log2, int num_workers) {
     constexpr int D = kHeadDim;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int waves = blockDim.x >> 6;
-    const int part = blockIdx.x;
-    const int kvh = blockIdx.y * waves + wave;
-    const int seq = blockIdx.z;
+    extern __shared__ int32_t s_cum[];  // s_cum[i] = tiles (per KV head) of sequences < i
+    __shared__ int32_t s_part[64 * kWaves];
+    const int tid = threadIdx.x;
+
+    // ---- prefix sums of per-sequence tile counts (two-level block scan)
+    const int per = (num_seqs + 64 * kWaves - 1) / (64 * kWaves);
+    int local = 0;
+    for (int k = 0; k < per; ++k) {
+        const int i = tid * per + k;
+        if (i < num_seqs)
+            local += (clamp_ctx(context_lens[i], max_context_len) + kTileTokens - 1) / kTileTokens;
+    }
+    s_part[tid] = local;
+    __syncthreads();
+    for (int off = 1; off < 64 * kWaves; off <<= 1) {
+        const int v = tid >= off ? s_part[tid - off] : 0;
+        __syncthreads();
+        s_part[tid] += v;
+        __syncthreads();
+    }
+    int run = s_part[tid] - local;
+    for (int k = 0; k < per; ++k) {
+        const int i = tid * per + k;
+        if (i < num_seqs) {
+            s_cum[i] = run;
+            run += (clamp_ctx(context_lens[i], max_context_len) + kTileTokens - 1) / kTileTokens;
+        }
+    }
+    if (tid == 64 * kWaves - 1) s_cum[num_seqs] = s_part[tid];
+    __syncthreads();
+    if (blockIdx.x == 0)
+        for (int i = tid; i <= num_seqs; i += 64 * kWaves) cum_out[i] = s_cum[i];
+
+    const int64_t Hkv = num_kv_heads;
+    const int64_t U = Hkv * s_cum[num_seqs];
+    // never more workers than tiles, so every worker's range is non-empty
+    const int64_t W = num_workers < U ? num_workers : U;
+    const int lane = tid & 63;
     const int row = lane >> 4;
     const int col = lane & 15;
+    const int64_t w = (int64_t)blockIdx.x * kWaves + (tid >> 6);
+    int64_t t = w < W ? worker_start(w, U, W) : 0;
+    const int64_t t_end = w < W ? worker_start(w + 1, U, W) : 0;
 
-    int ctx = context_lens[seq];
-    ctx = ctx < 0 ? 0 : (ctx > max_context_len ? max_context_len : ctx);
-    const int nparts = (ctx + kPartitionTokens - 1) / kPartitionTokens;
-    const size_t head_row = ((size_t)seq * num_q_heads + (size_t)kvh * G) * D;
+    const uint32_t neg = scale_log2 < 0.0f ? 0x80008000u : 0u;
+    const float c = fabsf(scale_log2);
+    const size_t row_elems = (size_t)num_kv_heads * D;
+    const uint32_t four_rows = (uint32_t)(4 * row_elems);
+    bool first_piece = true;
 
-    if (ctx == 0) {
-        if (part == 0) {  // nothing to attend to: a defined all-zero row
-            for (int e = lane; e < G * D; e += 64) {
-                if (OUT_BF16) static_cast<uint16_t*>(out)[head_row + e] = 0;
-                else static_cast<float*>(out)[head_row + e] = 0.0f;
+    while (t < t_end) {
+        // segment holding tile t: sequence = last i with Hkv * cum[i] <= t
+        int lo = 0, hi = num_seqs;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (Hkv * s_cum[mid] <= t) lo = mid; else hi = mid;
+        }
+        const int seq = lo;
+        const int n = s_cum[seq + 1] - s_cum[seq];  // > 0: t lies inside this sequence
+        const int64_t rel = t - Hkv * s_cum[seq];
+        const int kvh = (int)(rel / n);
+        const int tile0 = (int)(rel % n);
+        const int64_t seg_t0 = Hkv * s_cum[seq] + (int64_t)kvh * n;
+        const int64_t seg_t1 = seg_t0 + n;
+        const int64_t piece_end = t_end < seg_t1 ? t_end : seg_t1;
+        const int ntile = (int)(piece_end - t);
+        const int ctx = clamp_ctx(context_lens[seq], max_context_len);
+
+        const size_t head_row = ((size_t)seq * num_q_heads + (size_t)kvh * G) * D;
+        uint4 qv[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            qv[g] = *reinterpret_cast<const uint4*>(q + head_row + (size_t)g * D + col * 8);
+            qv[g].x ^= neg; qv[g].y ^= neg; qv[g].z ^= neg; qv[g].w ^= neg;
+        }
+        State<G> st;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            st.m[g] = kNegBig;
+            st.l[g] = 0.0f;
+#pragma unroll
+            for (int d = 0; d < 8; ++d) st.acc[g][d] = 0.0f;
+        }
+
+        IdWindow ids;
+        ids.init(block_table + (size_t)seq * max_blocks_per_seq, (ctx + BS - 1) / BS,
+                 (tile0 * kTileTokens) / BS, lane);
+        const uint32_t lane_off = (uint32_t)(row * row_elems + (size_t)kvh * D + col * 8);
+
+        Tile a, b;
+        load_tile(a, k_cache, v_cache, tile_elem<BS>(ids, tile0, row_elems, lane), lane_off, four_rows);
+        for (int j = 0; j < ntile; j += 2) {
+            if (j + 1 < ntile)
+                load_tile(b, k_cache, v_cache, tile_elem<BS>(ids, tile0 + j + 1, row_elems, lane),
+                          lane_off, four_rows);
+            process_any<G>(st, a, qv, c, row, ctx - (tile0 + j) * kTileTokens);
+            if (j + 1 >= ntile) break;
+            if (j + 2 < ntile)
+                load_tile(a, k_cache, v_cache, tile_elem<BS>(ids, tile0 + j + 2, row_elems, lane),
+                          lane_off, four_rows);
+            process_any<G>(st, b, qv, c, row, ctx - (tile0 + j + 1) * kTileTokens);
+        }
+
+        // Merge the four row streams: M = max m_r, l = sum l_r 2^(m_r - M),
+        // acc = sum acc_r 2^(m_r - M).  A row that saw no token has
+        // m = kNegBig, l = 0, acc = 0 and drops out.
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float mx = fmaxf(st.m[g], xor_lane(st.m[g], 16));
+            mx = fmaxf(mx, xor_lane(mx, 32));
+            const float f = fast_exp2(st.m[g] - mx);
+            float lt = st.l[g] * f;
+            lt += xor_lane(lt, 16);
+            lt += xor_lane(lt, 32);
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                float x = st.acc[g][d] * f;
+                x += xor_lane(x, 16);
+                x += xor_lane(x, 32);
+                st.acc[g][d] = x;
+            }
+            st.m[g] = mx;
+            st.l[g] = lt;
+        }
+
+        const bool whole = (t == seg_t0) && (piece_end == seg_t1);
+        const int slot = first_piece ? 0 : 1;
+        // Row r stores heads g = r, r + 4, ...
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            if ((g & 3) != row) continue;
+            if (whole) {
+                const float inv = 1.0f / st.l[g];
+                float o[8];
+#pragma unroll
+                for (int d = 0; d < 8; ++d) o[d] = st.acc[g][d] * inv;
+                store8<OUT_BF16>(out, head_row + (size_t)g * D + col * 8, o);
+            } else {
+                float* r = rec + ((size_t)(w * 2 + slot) * G + g) * kRecStride;
+                float4* pa = reinterpret_cast<float4*>(r + col * 8);
+                pa[0] = make_float4(st.acc[g][0], st.acc[g][1], st.acc[g][2], st.acc[g][3]);
+                pa[1] = make_float4(st.acc[g][4], st.acc[g][5], st.acc[g][6], st.acc[g][7]);
+                if (col == 0) {
+                    r[D] = st.m[g];
+                    r[D + 1] = st.l[g];
+                }
             }
         }
-        return;
-    }
-    if (part >= nparts) return;
-
-    const int tok0 = part * kPartitionTokens;
-    const int ntok = min(kPartitionTokens, ctx - tok0);
-    const int ntiles = (ntok + kTileTokens - 1) / kTileTokens;
-    const int nblk = (ntok + BS - 1) / BS;
-
-    // Physical ids of this partition's blocks: lane j holds the j-th.
-    const int32_t* bt_row = block_table + (size_t)seq * max_blocks_per_seq + tok0 / BS;
-    const int ids = lane < nblk ? bt_row[lane] : 0;
-
-    uint4 qv[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-        qv[g] = *reinterpret_cast<const uint4*>(q + head_row + (size_t)g * D + col * 8);
-
-    State<G> st;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        st.m[g] = kNegBig;
-        st.l[g] = 0.0f;
-#pragma unroll
-        for (int d = 0; d < 8; ++d) st.acc[g][d] = 0.0f;
-    }
-
-    const size_t row_elems = (size_t)num_kv_heads * D;  // elements between token rows
-    const uint32_t lane_off = (uint32_t)(row * row_elems + (size_t)kvh * D + col * 8);
-    const uint32_t four_rows = (uint32_t)(4 * row_elems);
-
-    Tile a, b;
-    load_tile(a, k_cache, v_cache, tile_base<BS>(ids, 0, row_elems), lane_off, four_rows);
-    for (int j = 0; j < ntiles; j += 2) {
-        if (j + 1 < ntiles)
-            load_tile(b, k_cache, v_cache, tile_base<BS>(ids, j + 1, row_elems), lane_off, four_rows);
-        process_any<G>(st, a, qv, scale_log2, row, ntok - j * kTileTokens);
-        if (j + 1 >= ntiles) break;
-        if (j + 2 < ntiles)
-            load_tile(a, k_cache, v_cache, tile_base<BS>(ids, j + 2, row_elems), lane_off, four_rows);
-        process_any<G>(st, b, qv, scale_log2, row, ntok - (j + 1) * kTileTokens);
-    }
-
-    // Merge the four row streams: M = max m_r, l = sum l_r 2^(m_r - M),
-    // acc = sum acc_r 2^(m_r - M).  Row 0 always saw a valid token.
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        float mx = fmaxf(st.m[g], xor_lane(st.m[g], 16));
-        mx = fmaxf(mx, xor_lane(mx, 32));
-        const float f = fast_exp2(st.m[g] - mx);
-        float lt = st.l[g] * f;
-        lt += xor_lane(lt, 16);
-        lt += xor_lane(lt, 32);
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-            float x = st.acc[g][d] * f;
-            x += xor_lane(x, 16);
-            x += xor_lane(x, 32);
-            st.acc[g][d] = x;
-        }
-        st.m[g] = mx;
-        st.l[g] = lt;
-    }
-
-    // Row r stores heads g = r, r + 4, ...
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        if ((g & 3) != row) continue;
-        if (nparts == 1) {
-            const float inv = 1.0f / st.l[g];
-            float o[8];
-#pragma unroll
-            for (int d = 0; d < 8; ++d) o[d] = st.acc[g][d] * inv;
-            store8<OUT_BF16>(out, head_row + (size_t)g * D + col * 8, o);
-        } else {
-            const size_t slot = ((size_t)seq * num_q_heads + (size_t)kvh * G + g) * max_parts + part;
-            float4* pa = reinterpret_cast<float4*>(part_acc + slot * D + col * 8);
-            pa[0] = make_float4(st.acc[g][0], st.acc[g][1], st.acc[g][2], st.acc[g][3]);
-            pa[1] = make_float4(st.acc[g][4], st.acc[g][5], st.acc[g][6], st.acc[g][7]);
-            if (col == 0) part_ml[slot] = make_float2(st.m[g], st.l[g]);
-        }
+        first_piece = false;
+        t = piece_end;
     }
 }
 
-// Log-sum-exp merge of the partitions of one (sequence, query head) per
-// wave: M = max_k m_k, L = sum_k l_k 2^(m_k - M), out = sum_k acc_k 2^(m_k - M) / L.
-// Grid: (ceil(num_q_heads / 4), num_seqs); block: 256 (4 waves, one head each).
+// Finishes every (sequence, query head): zero rows for empty contexts, and
+// the log-sum-exp merge of a segment's pieces when several waves shared it:
+// M = max_k m_k, L = sum_k l_k 2^(m_k - M), out = sum_k acc_k 2^(m_k - M) / L.
+// Grid: (ceil(num_q_heads / 4), num_seqs); block: 4 waves, one query head each.
 template <bool OUT_BF16>
 __global__ void __launch_bounds__(256)
-decode_merge_kernel(void* __restrict__ out, const float2* __restrict__ part_ml,
-                    const float* __restrict__ part_acc, const int32_t* __restrict__ context_lens,
-                    int max_context_len, int num_q_heads, int max_parts) {
+decode_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
+                    const int32_t* __restrict__ cum, const int32_t* __restrict__ context_lens,
+                    int max_context_len, int num_seqs, int num_q_heads, int num_kv_heads,
+                    int num_workers) {
     constexpr int D = kHeadDim;
     const int lane = threadIdx.x & 63;
     const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int seq = blockIdx.y;
     if (h >= num_q_heads) return;
-    int ctx = context_lens[seq];
-    ctx = ctx < 0 ? 0 : (ctx > max_context_len ? max_context_len : ctx);
-    const int nparts = (ctx + kPartitionTokens - 1) / kPartitionTokens;
-    if (nparts <= 1) return;  // written directly by the partition kernel
+    const int G = num_q_heads / num_kv_heads;
+    const size_t e = ((size_t)seq * num_q_heads + h) * D + 2 * lane;
+    const int ctx = clamp_ctx(context_lens[seq], max_context_len);
+    if (ctx == 0) {  // nothing to attend to: a defined all-zero row
+        store1<OUT_BF16>(out, e, 0.0f);
+        store1<OUT_BF16>(out, e + 1, 0.0f);
+        return;
+    }
+    const int64_t Hkv = num_kv_heads;
+    const int64_t U = Hkv * cum[num_seqs];  // > 0: this sequence has tiles
+    const int64_t W = num_workers < U ? num_workers : U;
+    const int n = cum[seq + 1] - cum[seq];
+    const int kvh = h / G;
+    const int g = h % G;
+    const int64_t t0 = Hkv * cum[seq] + (int64_t)kvh * n;
+    const int64_t wf = worker_of(t0, U, W);
+    const int64_t wl = worker_of(t0 + n - 1, U, W);
+    if (wf == wl) return;  // finalised by its only wave
 
-    const size_t slot0 = ((size_t)seq * num_q_heads + h) * max_parts;
+    auto rec_of = [&](int64_t w) {
+        const int slot = (w == wf && worker_start(w, U, W) < t0) ? 1 : 0;
+        return rec + ((size_t)(w * 2 + slot) * G + g) * kRecStride;
+    };
     float mx = -INFINITY;
-    for (int p = lane; p < nparts; p += 64) mx = fmaxf(mx, part_ml[slot0 + p].x);
+    for (int64_t w = wf + lane; w <= wl; w += 64) mx = fmaxf(mx, rec_of(w)[D]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-
     float L = 0.0f, a0 = 0.0f, a1 = 0.0f;
-    const float2* acc2 = reinterpret_cast<const float2*>(part_acc);
-    for (int p = 0; p < nparts; ++p) {
-        const float2 ml = part_ml[slot0 + p];
-        const float w = fast_exp2(ml.x - mx);
-        L = fmaf(ml.y, w, L);
-        const float2 a = acc2[(slot0 + p) * (D / 2) + lane];
-        a0 = fmaf(a.x, w, a0);
-        a1 = fmaf(a.y, w, a1);
+    for (int64_t w = wf; w <= wl; ++w) {
+        const float* r = rec_of(w);
+        const float f = fast_exp2(r[D] - mx);
+        L = fmaf(r[D + 1], f, L);
+        const float2 a = *reinterpret_cast<const float2*>(r + 2 * lane);
+        a0 = fmaf(a.x, f, a0);
+        a1 = fmaf(a.y, f, a1);
     }
     const float inv = 1.0f / L;
-    const size_t e = ((size_t)seq * num_q_heads + h) * D + 2 * lane;
-    if (OUT_BF16) {
-        const uint32_t w = (uint32_t)f32_to_bf16_rne(a0 * inv) |
-                           ((uint32_t)f32_to_bf16_rne(a1 * inv) << 16);
-        *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + e) = w;
-    } else {
-        *reinterpret_cast<float2*>(static_cast<float*>(out) + e) = make_float2(a0 * inv, a1 * inv);
-    }
+    store1<OUT_BF16>(out, e, a0 * inv);
+    store1<OUT_BF16>(out, e + 1, a1 * inv);
+}
+
+// Workgroups of `kern` that one CU holds at once, for this much dynamic LDS
+// (a pure function of the kernel and the device, cached per thread).
+hipError_t resident_blocks_per_cu(const void* kern, size_t lds, int* out) {
+    struct Entry { const void* kern; size_t lds; int dev; int blocks; };
+    static thread_local Entry cache[16];
+    static thread_local int next = 0;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const size_t lds_key = (lds + 4095) / 4096 * 4096;
+    for (const Entry& c : cache)
+        if (c.kern == kern && c.lds == lds_key && c.dev == dev) { *out = c.blocks; return hipSuccess; }
+    int n = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 64 * kWaves, lds_key);
+    if (e != hipSuccess) return e;
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    *out = (n < 1 ? 1 : n) * cus;
+    cache[next] = Entry{kern, lds_key, dev, *out};
+    next = (next + 1) % 16;
+    return hipSuccess;
 }
 
 template <int BS, int G, bool OUT_BF16>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-    const int waves = (a.num_kv_heads % 4 == 0) ? 4 : (a.num_kv_heads % 2 == 0 ? 2 : 1);
-    dim3 grid(a.max_parts, a.num_kv_heads / waves, a.num_seqs);
-    dim3 block(64 * waves);
-    hipLaunchKernelGGL((decode_partition_kernel<BS, G, OUT_BF16>), grid, block, 0, stream, a.out,
-                       a.part_ml, a.part_acc, a.q, a.k_cache, a.v_cache, a.block_table,
-                       a.max_blocks_per_seq, a.context_lens, a.max_context_len, a.num_q_heads,
-                       a.num_kv_heads, a.scale_log2, a.max_parts);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.max_parts <= 1) return e;
+    auto kern = decode_streamk_kernel<BS, G, OUT_BF16>;
+    const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int32_t);
+    int resident = 0;
+    hipError_t e = resident_blocks_per_cu(reinterpret_cast<const void*>(kern), lds, &resident);
+    if (e != hipSuccess) return e;
+    // as many waves as the chip holds at once, never more than the records
+    // in the workspace allow (max_workers is a multiple of kWaves)
+    int64_t workers = (int64_t)resident * kWaves;
+    if (workers > a.max_workers) workers = a.max_workers;
+    const int grid = (int)(workers / kWaves);
+    hipLaunchKernelGGL((decode_streamk_kernel<BS, G, OUT_BF16>), dim3(grid), dim3(64 * kWaves), lds,
+                       stream, a.out, a.records, a.cum, a.q, a.k_cache, a.v_cache, a.block_table,
+                       a.max_blocks_per_seq, a.context_lens, a.max_context_len, a.num_seqs,
+                       a.num_q_heads, a.num_kv_heads, a.scale_log2, (int)workers);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     dim3 mgrid((a.num_q_heads + 3) / 4, a.num_seqs);
     hipLaunchKernelGGL((decode_merge_kernel<OUT_BF16>), mgrid, dim3(256), 0, stream, a.out,
-                       a.part_ml, a.part_acc, a.context_lens, a.max_context_len, a.num_q_heads,
-                       a.max_parts);
+                       a.records, a.cum, a.context_lens, a.max_context_len, a.num_seqs,
+                       a.num_q_heads, a.num_kv_heads, (int)workers);
     return hipGetLastError();
 }
 
@@ -358,6 +514,24 @@ hipError_t launch_decode_bs(const DecodeArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+int64_t decode_max_workers(int num_seqs, int num_kv_heads, int max_context_len) {
+    const int64_t tiles = (int64_t)num_kv_heads * num_seqs *
+                          ((max_context_len + kTileTokens - 1) / kTileTokens);
+    int64_t w = (tiles + kMinTilesPerWorker - 1) / kMinTilesPerWorker;
+    if (w > kMaxWorkers) w = kMaxWorkers;
+    w = (w + kWaves - 1) / kWaves * kWaves;
+    return w < kWaves ? kWaves : w;
+}
+
+size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                              int max_context_len) {
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
+    const int g = num_q_heads / num_kv_heads;
+    const size_t cum = ((size_t)(num_seqs + 1) * sizeof(int32_t) + 255) / 256 * 256;
+    return cum + (size_t)decode_max_workers(num_seqs, num_kv_heads, max_context_len) * 2 * g *
+                     kRecStride * sizeof(float);
+}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     return a.block_size == 16 ? launch_decode_bs<16>(a, stream) : launch_decode_bs<32>(a, stream);

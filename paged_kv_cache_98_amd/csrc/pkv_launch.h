@@ -33,10 +33,10 @@ struct DecodeArgs {
     int num_q_heads;
     int num_kv_heads;
     int block_size;
-    float scale_log2;  // scale * log2(e)
-    int max_parts;     // ceil(max_context_len / partition), >= 1
-    float2* part_ml;   // [num_seqs][num_q_heads][max_parts] (m, l)
-    float* part_acc;   // [num_seqs][num_q_heads][max_parts][head_dim]
+    float scale_log2;     // scale * log2(e)
+    int32_t* cum;         // workspace: [num_seqs + 1] tile prefix sums
+    float* records;       // workspace: [max_workers][2][G][head_dim + 4] partial results
+    int64_t max_workers;  // records available (a multiple of 4)
 };
 
 struct PrefillArgs {
@@ -64,7 +64,9 @@ hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
-// Bytes of decode workspace for these sizes (0 when no split is needed).
-size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim, int max_context_len);
+// Decode workspace: the tile prefix sums, then the partial-result records.
+size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                              int max_context_len);
+int64_t decode_max_workers(int num_seqs, int num_kv_heads, int max_context_len);
 
 }  // namespace pkv

@@ -70,23 +70,28 @@ def test_decode_validation(lib):
     assert decode(lib, maxctx=-1) == E.PKV_ERR_SHAPE
     assert decode(lib, q=MIS) == E.PKV_ERR_ALIGN
     assert decode(lib, k=MIS) == E.PKV_ERR_ALIGN
-    # long context needs a workspace
-    need = lib.pkv_decode_workspace_bytes(4, 8, 128, 2000)
+    # a workspace is always needed
+    need = lib.pkv_decode_workspace_bytes(4, 8, 2, 128, 2000)
     assert need > 0
     assert decode(lib, maxctx=2000, mb=200) == E.PKV_ERR_WORKSPACE
     assert decode(lib, maxctx=2000, mb=200, ws=P2, wsb=need - 1) == E.PKV_ERR_WORKSPACE
     assert decode(lib, maxctx=2000, mb=200, ws=MIS, wsb=need) == E.PKV_ERR_ALIGN
+    assert decode(lib, nseq=16384, ws=P2, wsb=1 << 30) == E.PKV_ERR_UNSUPPORTED
     # nothing to do is fine even with NULL pointers
     assert decode(lib, nseq=0, q=None, out=None) == E.PKV_OK
 
 
 def test_decode_workspace_size(lib):
-    assert lib.pkv_decode_workspace_bytes(64, 32, 128, 512) == 0        # one partition
-    assert lib.pkv_decode_workspace_bytes(0, 32, 128, 4096) == 0
-    n = lib.pkv_decode_workspace_bytes(64, 32, 128, 4096)                # 8 partitions
-    slots = 64 * 32 * 8
-    assert n >= slots * (128 + 2) * 4
-    assert n <= slots * (128 + 2) * 4 + 256
+    assert lib.pkv_decode_workspace_bytes(0, 32, 8, 128, 4096) == 0
+    assert lib.pkv_decode_workspace_bytes(4, 32, 6, 128, 4096) == 0     # Hq % Hkv
+    # prefix sums + at most 8192 waves x 2 records x G x (128 + 4) floats
+    n = lib.pkv_decode_workspace_bytes(64, 32, 8, 128, 4096)
+    assert n == 512 + 8192 * 2 * 4 * 132 * 4
+    # a tiny batch needs few waves: 2 heads x 4 seqs x 7 tiles / 4 -> 16 waves
+    n = lib.pkv_decode_workspace_bytes(4, 8, 2, 128, 100)
+    assert n == 256 + 16 * 2 * 4 * 132 * 4
+    # an empty context still gets its prefix sums and the minimum of 4 waves
+    assert lib.pkv_decode_workspace_bytes(4, 8, 2, 128, 0) == 256 + 4 * 2 * 4 * 132 * 4
 
 
 def prefill(lib, **kw):
