@@ -105,11 +105,12 @@ int pkv_kv_append(const void *k_new, const void *v_new, const int64_t *slot_mapp
 /*
  * Workspace needed by pkv_paged_decode_attn for these sizes (bytes; 0 only
  * for num_seqs == 0 or inconsistent head counts).  The keys of all
- * (sequence, KV head) pairs are split evenly over the waves the GPU holds; a
- * pair shared by several waves leaves per-wave partial results (running max,
- * running sum, unnormalised accumulator) in the workspace until a
- * log-sum-exp merge combines them.  At most 8192 waves x 2 records x
- * (Hq/Hkv) x 528 bytes, plus the per-sequence tile prefix sums.
+ * sequences are split evenly over the workgroups the GPU holds at once; a
+ * sequence shared by several workgroups leaves per-workgroup partial results
+ * (running max, running sum, unnormalised accumulator per query head) in the
+ * workspace until a log-sum-exp merge combines them.  At most 1024
+ * workgroups x 2 records x num_q_heads x 528 bytes, plus the per-sequence
+ * tile prefix sums.
  */
 size_t pkv_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                                   int max_context_len);
@@ -128,7 +129,7 @@ size_t pkv_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_head
  *   workspace      device scratch of at least pkv_decode_workspace_bytes()
  *                  bytes, 16-byte aligned; contents need no initialisation
  *                  and are garbage afterwards
- *   num_seqs       at most 16383 for this call
+ *   num_seqs       at most 16383 for this call; num_kv_heads 1..8 or 16
  *
  *   out[i, h, :] = sum_t softmax_t(scale * <q[i,h], K_i[t]>) V_i[t]
  * with K_i, V_i the KV head h / G rows of sequence i reached through its

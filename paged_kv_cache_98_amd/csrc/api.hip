@@ -15,6 +15,9 @@ constexpr int kVersion = 200;  // 0.2.0
 // Decode keeps the per-sequence tile prefix sums in LDS: (num_seqs + 1) int32
 // must fit the 64 KB a workgroup may allocate.
 constexpr int kMaxDecodeSeqs = 16383;
+// A decode workgroup serves up to 8 KV heads, one wave each; 16 heads run as
+// two groups of 8.
+constexpr int kMaxDecodeKvHeads = 16;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -97,6 +100,7 @@ int pkv_paged_decode_attn(void* out, int out_dtype, const void* q, const void* k
                                    num_kv_heads, head_dim, block_size, out_dtype);
     if (st != PKV_OK) return st;
     if (num_seqs > kMaxDecodeSeqs) return PKV_ERR_UNSUPPORTED;
+    if (num_kv_heads > 8 && num_kv_heads != kMaxDecodeKvHeads) return PKV_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PKV_OK;
     if (!out || !q || !k_cache || !v_cache || !block_table || !context_lens) return PKV_ERR_NULL;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
@@ -124,7 +128,7 @@ int pkv_paged_decode_attn(void* out, int out_dtype, const void* q, const void* k
     a.cum = static_cast<int32_t*>(workspace);
     a.records = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                          align_up((size_t)(num_seqs + 1) * sizeof(int32_t), 256));
-    a.max_workers = pkv::decode_max_workers(num_seqs, num_kv_heads, max_context_len);
+    a.max_workers = pkv::decode_max_workers(num_seqs, max_context_len);
     return to_status(pkv::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 

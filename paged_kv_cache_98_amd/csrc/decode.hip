@@ -15,18 +15,20 @@
 //
 // Split of the work (the sequence-axis parallelism of that section, taken
 // to its balanced limit):
-//   * a segment is the keys of one (sequence, KV head); the G = Hq/Hkv query
-//     heads of the KV head ride along, so each K/V byte is read from HBM once
-//     per KV head (GQA grouping);
-//   * all segments' 16-token tiles are laid end to end, sequence-major, and
-//     cut into W equal contiguous ranges, one per persistent wave (W = what
-//     the chip holds at once).  A wave walks its range segment by segment:
-//     a segment it covers whole is finalised in place; a piece of a segment
-//     shared with other waves leaves (m, l, unnormalised acc) in the
-//     workspace, and the merge kernel combines the pieces with the same
-//     exp(m_k - M) rescale (a log-sum-exp merge);
-//   * so every wave streams the same number of bytes, no workgroup is
-//     launched without work, and long contexts split across many waves.
+//   * a worker is a workgroup with one wave per KV head; the G = Hq/Hkv
+//     query heads of a KV head ride along in its wave, so each K/V byte is
+//     read from HBM once per KV head (GQA grouping), and the waves of a
+//     worker read each physical block's rows of all heads together
+//     (contiguous bs * Hkv * D bf16 of K, the same of V);
+//   * all sequences' 16-token tiles are laid end to end and cut into W
+//     equal contiguous ranges, one per persistent worker (W = what the chip
+//     holds at once).  A worker walks its range sequence by sequence: a
+//     sequence it covers whole is finalised in place; a piece of a sequence
+//     shared with other workers leaves (m, l, unnormalised acc) per query
+//     head in the workspace, and the merge kernel combines the pieces with
+//     the same exp(m_k - M) rescale (a log-sum-exp merge);
+//   * so every worker streams the same number of bytes, no workgroup is
+//     launched without work, and long contexts split across many workers.
 // Inside a wave (64 lanes = 4 rows of 16): a tile of one head is 4 KB of K
 // and 4 KB of V, four 128-bit loads per lane each; lane (row r, col c) holds
 // dims 8c..8c+7 of tokens 4i + r, i = 0..3; the 16-lane row reduces the QK
@@ -176,10 +178,13 @@ __device__ __forceinline__ void store1(void* out, size_t elem, float x) {
     else static_cast<float*>(out)[elem] = x;
 }
 
-constexpr int kWaves = 4;                 // independent waves per workgroup
 constexpr int kRecStride = kHeadDim + 4;  // floats per record: acc[128], m, l, 2 pad
 constexpr int kMinTilesPerWorker = 4;   // fewer waves for tiny batches
-constexpr int64_t kMaxWorkers = 8192;    // >= waves an MI355X holds (256 CUs x 32)
+// KV heads (one wave each) served by one workgroup: 8 while a wave fits in
+// 256 registers (two waves per SIMD), else 4.
+template <int G>
+constexpr int max_waves_per_worker() { return G <= 4 ? 8 : 4; }
+constexpr int64_t kMaxWorkers = 1024;    // workgroups of 8 waves an MI355X holds at most
 
 // Worker w owns global tiles [worker_start(w), worker_start(w + 1)).
 __device__ __forceinline__ int64_t worker_start(int64_t w, int64_t U, int64_t W) {
@@ -227,10 +232,15 @@ __device__ __forceinline__ size_t tile_elem(IdWindow& ids, int tile, size_t row_
     return ((size_t)phys * BS + (tok % BS)) * row_elems;
 }
 
-// Grid: num_workers / 4 workgroups of 4 waves; dynamic LDS (num_seqs + 1)
-// int32 for the tile prefix sums.  Records: [W][2][G][kRecStride] floats.
+// Grid: (num_workers, head groups); a workgroup has one wave per KV head of
+// its group (all KV heads when there are at most 8, else groups of 8);
+// dynamic LDS (num_seqs + 1) int32 for the tile prefix sums.  A worker
+// owns a contiguous range of (sequence, 16-token tile) units, and its waves
+// walk that range together, so each physical block's K rows of all heads
+// (bs * Hkv * D bf16, contiguous) are fetched at the same time.
+// Records: [W][2][num_q_heads][kRecStride] floats.
 template <int BS, int G, bool OUT_BF16>
-__global__ void __launch_bounds__(64 * kWaves)
+__global__ void __launch_bounds__(64 * max_waves_per_worker<G>())
 decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* __restrict__ cum_out,
                       const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
                       const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
@@ -239,11 +249,12 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
                       float scale_log2, int num_workers) {
     constexpr int D = kHeadDim;
     extern __shared__ int32_t s_cum[];  // s_cum[i] = tiles (per KV head) of sequences < i
-    __shared__ int32_t s_part[64 * kWaves];
+    __shared__ int32_t s_part[64 * max_waves_per_worker<G>()];
     const int tid = threadIdx.x;
+    const int nthr = blockDim.x;
 
     // ---- prefix sums of per-sequence tile counts (two-level block scan)
-    const int per = (num_seqs + 64 * kWaves - 1) / (64 * kWaves);
+    const int per = (num_seqs + nthr - 1) / nthr;
     int local = 0;
     for (int k = 0; k < per; ++k) {
         const int i = tid * per + k;
@@ -252,7 +263,7 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
     }
     s_part[tid] = local;
     __syncthreads();
-    for (int off = 1; off < 64 * kWaves; off <<= 1) {
+    for (int off = 1; off < nthr; off <<= 1) {
         const int v = tid >= off ? s_part[tid - off] : 0;
         __syncthreads();
         s_part[tid] += v;
@@ -266,19 +277,19 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
             run += (clamp_ctx(context_lens[i], max_context_len) + kTileTokens - 1) / kTileTokens;
         }
     }
-    if (tid == 64 * kWaves - 1) s_cum[num_seqs] = s_part[tid];
+    if (tid == nthr - 1) s_cum[num_seqs] = s_part[tid];
     __syncthreads();
-    if (blockIdx.x == 0)
-        for (int i = tid; i <= num_seqs; i += 64 * kWaves) cum_out[i] = s_cum[i];
+    if (blockIdx.x == 0 && blockIdx.y == 0)
+        for (int i = tid; i <= num_seqs; i += nthr) cum_out[i] = s_cum[i];
 
-    const int64_t Hkv = num_kv_heads;
-    const int64_t U = Hkv * s_cum[num_seqs];
+    const int64_t U = s_cum[num_seqs];
     // never more workers than tiles, so every worker's range is non-empty
     const int64_t W = num_workers < U ? num_workers : U;
     const int lane = tid & 63;
+    const int kvh = blockIdx.y * (nthr >> 6) + (tid >> 6);
     const int row = lane >> 4;
     const int col = lane & 15;
-    const int64_t w = (int64_t)blockIdx.x * kWaves + (tid >> 6);
+    const int64_t w = blockIdx.x;
     int64_t t = w < W ? worker_start(w, U, W) : 0;
     const int64_t t_end = w < W ? worker_start(w + 1, U, W) : 0;
 
@@ -286,22 +297,20 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
     const float c = fabsf(scale_log2);
     const size_t row_elems = (size_t)num_kv_heads * D;
     const uint32_t four_rows = (uint32_t)(4 * row_elems);
+    const uint32_t lane_off = (uint32_t)(row * row_elems + (size_t)kvh * D + col * 8);
     bool first_piece = true;
 
     while (t < t_end) {
-        // segment holding tile t: sequence = last i with Hkv * cum[i] <= t
+        // sequence holding tile t: the last i with cum[i] <= t
         int lo = 0, hi = num_seqs;
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
-            if (Hkv * s_cum[mid] <= t) lo = mid; else hi = mid;
+            if (s_cum[mid] <= t) lo = mid; else hi = mid;
         }
         const int seq = lo;
-        const int n = s_cum[seq + 1] - s_cum[seq];  // > 0: t lies inside this sequence
-        const int64_t rel = t - Hkv * s_cum[seq];
-        const int kvh = (int)(rel / n);
-        const int tile0 = (int)(rel % n);
-        const int64_t seg_t0 = Hkv * s_cum[seq] + (int64_t)kvh * n;
-        const int64_t seg_t1 = seg_t0 + n;
+        const int64_t seg_t0 = s_cum[seq];
+        const int64_t seg_t1 = s_cum[seq + 1];  // > t
+        const int tile0 = (int)(t - seg_t0);
         const int64_t piece_end = t_end < seg_t1 ? t_end : seg_t1;
         const int ntile = (int)(piece_end - t);
         const int ctx = clamp_ctx(context_lens[seq], max_context_len);
@@ -325,7 +334,6 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
         IdWindow ids;
         ids.init(block_table + (size_t)seq * max_blocks_per_seq, (ctx + BS - 1) / BS,
                  (tile0 * kTileTokens) / BS, lane);
-        const uint32_t lane_off = (uint32_t)(row * row_elems + (size_t)kvh * D + col * 8);
 
         Tile a, b;
         load_tile(a, k_cache, v_cache, tile_elem<BS>(ids, tile0, row_elems, lane), lane_off, four_rows);
@@ -376,7 +384,7 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
                 for (int d = 0; d < 8; ++d) o[d] = st.acc[g][d] * inv;
                 store8<OUT_BF16>(out, head_row + (size_t)g * D + col * 8, o);
             } else {
-                float* r = rec + ((size_t)(w * 2 + slot) * G + g) * kRecStride;
+                float* r = rec + ((size_t)(w * 2 + slot) * num_q_heads + (size_t)kvh * G + g) * kRecStride;
                 float4* pa = reinterpret_cast<float4*>(r + col * 8);
                 pa[0] = make_float4(st.acc[g][0], st.acc[g][1], st.acc[g][2], st.acc[g][3]);
                 pa[1] = make_float4(st.acc[g][4], st.acc[g][5], st.acc[g][6], st.acc[g][7]);
@@ -392,21 +400,19 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
 }
 
 // Finishes every (sequence, query head): zero rows for empty contexts, and
-// the log-sum-exp merge of a segment's pieces when several waves shared it:
-// M = max_k m_k, L = sum_k l_k 2^(m_k - M), out = sum_k acc_k 2^(m_k - M) / L.
+// the log-sum-exp merge of a sequence's pieces when several workers shared
+// it: M = max_k m_k, L = sum_k l_k 2^(m_k - M), out = sum_k acc_k 2^(m_k - M) / L.
 // Grid: (ceil(num_q_heads / 4), num_seqs); block: 4 waves, one query head each.
 template <bool OUT_BF16>
 __global__ void __launch_bounds__(256)
 decode_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
                     const int32_t* __restrict__ cum, const int32_t* __restrict__ context_lens,
-                    int max_context_len, int num_seqs, int num_q_heads, int num_kv_heads,
-                    int num_workers) {
+                    int max_context_len, int num_seqs, int num_q_heads, int num_workers) {
     constexpr int D = kHeadDim;
     const int lane = threadIdx.x & 63;
     const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int seq = blockIdx.y;
     if (h >= num_q_heads) return;
-    const int G = num_q_heads / num_kv_heads;
     const size_t e = ((size_t)seq * num_q_heads + h) * D + 2 * lane;
     const int ctx = clamp_ctx(context_lens[seq], max_context_len);
     if (ctx == 0) {  // nothing to attend to: a defined all-zero row
@@ -414,20 +420,16 @@ decode_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
         store1<OUT_BF16>(out, e + 1, 0.0f);
         return;
     }
-    const int64_t Hkv = num_kv_heads;
-    const int64_t U = Hkv * cum[num_seqs];  // > 0: this sequence has tiles
+    const int64_t U = cum[num_seqs];  // > 0: this sequence has tiles
     const int64_t W = num_workers < U ? num_workers : U;
-    const int n = cum[seq + 1] - cum[seq];
-    const int kvh = h / G;
-    const int g = h % G;
-    const int64_t t0 = Hkv * cum[seq] + (int64_t)kvh * n;
+    const int64_t t0 = cum[seq];
     const int64_t wf = worker_of(t0, U, W);
-    const int64_t wl = worker_of(t0 + n - 1, U, W);
-    if (wf == wl) return;  // finalised by its only wave
+    const int64_t wl = worker_of(cum[seq + 1] - 1, U, W);
+    if (wf == wl) return;  // finalised by its only worker
 
     auto rec_of = [&](int64_t w) {
         const int slot = (w == wf && worker_start(w, U, W) < t0) ? 1 : 0;
-        return rec + ((size_t)(w * 2 + slot) * G + g) * kRecStride;
+        return rec + ((size_t)(w * 2 + slot) * num_q_heads + h) * kRecStride;
     };
     float mx = -INFINITY;
     for (int64_t w = wf + lane; w <= wl; w += 64) mx = fmaxf(mx, rec_of(w)[D]);
@@ -449,8 +451,8 @@ decode_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
 
 // Workgroups of `kern` that one CU holds at once, for this much dynamic LDS
 // (a pure function of the kernel and the device, cached per thread).
-hipError_t resident_blocks_per_cu(const void* kern, size_t lds, int* out) {
-    struct Entry { const void* kern; size_t lds; int dev; int blocks; };
+hipError_t resident_blocks_per_cu(const void* kern, int threads, size_t lds, int* out) {
+    struct Entry { const void* kern; int threads; size_t lds; int dev; int blocks; };
     static thread_local Entry cache[16];
     static thread_local int next = 0;
     int dev = 0;
@@ -458,15 +460,18 @@ hipError_t resident_blocks_per_cu(const void* kern, size_t lds, int* out) {
     if (e != hipSuccess) return e;
     const size_t lds_key = (lds + 4095) / 4096 * 4096;
     for (const Entry& c : cache)
-        if (c.kern == kern && c.lds == lds_key && c.dev == dev) { *out = c.blocks; return hipSuccess; }
+        if (c.kern == kern && c.threads == threads && c.lds == lds_key && c.dev == dev) {
+            *out = c.blocks;
+            return hipSuccess;
+        }
     int n = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 64 * kWaves, lds_key);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, threads, lds_key);
     if (e != hipSuccess) return e;
     int cus = 0;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     *out = (n < 1 ? 1 : n) * cus;
-    cache[next] = Entry{kern, lds_key, dev, *out};
+    cache[next] = Entry{kern, threads, lds_key, dev, *out};
     next = (next + 1) % 16;
     return hipSuccess;
 }
@@ -474,25 +479,32 @@ hipError_t resident_blocks_per_cu(const void* kern, size_t lds, int* out) {
 template <int BS, int G, bool OUT_BF16>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     auto kern = decode_streamk_kernel<BS, G, OUT_BF16>;
+    constexpr int kMax = max_waves_per_worker<G>();
+    // head groups of kMax waves; the API admits 1..8 and 16 KV heads
+    const int waves = a.num_kv_heads <= kMax ? a.num_kv_heads
+                                             : (a.num_kv_heads % kMax == 0 ? kMax : 1);
+    const int groups = a.num_kv_heads / waves;
+    const int threads = 64 * waves;
     const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int32_t);
     int resident = 0;
-    hipError_t e = resident_blocks_per_cu(reinterpret_cast<const void*>(kern), lds, &resident);
+    hipError_t e = resident_blocks_per_cu(reinterpret_cast<const void*>(kern), threads, lds,
+                                          &resident);
     if (e != hipSuccess) return e;
-    // as many waves as the chip holds at once, never more than the records
-    // in the workspace allow (max_workers is a multiple of kWaves)
-    int64_t workers = (int64_t)resident * kWaves;
+    // as many workers as the chip holds at once, never more than the records
+    // in the workspace allow
+    int64_t workers = resident / groups;
     if (workers > a.max_workers) workers = a.max_workers;
-    const int grid = (int)(workers / kWaves);
-    hipLaunchKernelGGL((decode_streamk_kernel<BS, G, OUT_BF16>), dim3(grid), dim3(64 * kWaves), lds,
-                       stream, a.out, a.records, a.cum, a.q, a.k_cache, a.v_cache, a.block_table,
-                       a.max_blocks_per_seq, a.context_lens, a.max_context_len, a.num_seqs,
-                       a.num_q_heads, a.num_kv_heads, a.scale_log2, (int)workers);
+    if (workers < 1) workers = 1;
+    hipLaunchKernelGGL((decode_streamk_kernel<BS, G, OUT_BF16>), dim3((int)workers, groups), dim3(threads),
+                       lds, stream, a.out, a.records, a.cum, a.q, a.k_cache, a.v_cache,
+                       a.block_table, a.max_blocks_per_seq, a.context_lens, a.max_context_len,
+                       a.num_seqs, a.num_q_heads, a.num_kv_heads, a.scale_log2, (int)workers);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 mgrid((a.num_q_heads + 3) / 4, a.num_seqs);
     hipLaunchKernelGGL((decode_merge_kernel<OUT_BF16>), mgrid, dim3(256), 0, stream, a.out,
                        a.records, a.cum, a.context_lens, a.max_context_len, a.num_seqs,
-                       a.num_q_heads, a.num_kv_heads, (int)workers);
+                       a.num_q_heads, (int)workers);
     return hipGetLastError();
 }
 
@@ -515,21 +527,18 @@ hipError_t launch_decode_bs(const DecodeArgs& a, hipStream_t s) {
 
 }  // namespace
 
-int64_t decode_max_workers(int num_seqs, int num_kv_heads, int max_context_len) {
-    const int64_t tiles = (int64_t)num_kv_heads * num_seqs *
-                          ((max_context_len + kTileTokens - 1) / kTileTokens);
+int64_t decode_max_workers(int num_seqs, int max_context_len) {
+    const int64_t tiles = (int64_t)num_seqs * ((max_context_len + kTileTokens - 1) / kTileTokens);
     int64_t w = (tiles + kMinTilesPerWorker - 1) / kMinTilesPerWorker;
     if (w > kMaxWorkers) w = kMaxWorkers;
-    w = (w + kWaves - 1) / kWaves * kWaves;
-    return w < kWaves ? kWaves : w;
+    return w < 1 ? 1 : w;
 }
 
 size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                               int max_context_len) {
     if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
-    const int g = num_q_heads / num_kv_heads;
     const size_t cum = ((size_t)(num_seqs + 1) * sizeof(int32_t) + 255) / 256 * 256;
-    return cum + (size_t)decode_max_workers(num_seqs, num_kv_heads, max_context_len) * 2 * g *
+    return cum + (size_t)decode_max_workers(num_seqs, max_context_len) * 2 * num_q_heads *
                      kRecStride * sizeof(float);
 }
 

@@ -35,8 +35,8 @@ struct DecodeArgs {
     int block_size;
     float scale_log2;     // scale * log2(e)
     int32_t* cum;         // workspace: [num_seqs + 1] tile prefix sums
-    float* records;       // workspace: [max_workers][2][G][head_dim + 4] partial results
-    int64_t max_workers;  // records available (a multiple of 4)
+    float* records;       // workspace: [max_workers][2][num_q_heads][head_dim + 4] partials
+    int64_t max_workers;  // workers whose records fit the workspace
 };
 
 struct PrefillArgs {
@@ -67,6 +67,6 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 // Decode workspace: the tile prefix sums, then the partial-result records.
 size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                               int max_context_len);
-int64_t decode_max_workers(int num_seqs, int num_kv_heads, int max_context_len);
+int64_t decode_max_workers(int num_seqs, int max_context_len);
 
 }  // namespace pkv

@@ -77,6 +77,8 @@ def test_decode_validation(lib):
     assert decode(lib, maxctx=2000, mb=200, ws=P2, wsb=need - 1) == E.PKV_ERR_WORKSPACE
     assert decode(lib, maxctx=2000, mb=200, ws=MIS, wsb=need) == E.PKV_ERR_ALIGN
     assert decode(lib, nseq=16384, ws=P2, wsb=1 << 30) == E.PKV_ERR_UNSUPPORTED
+    assert decode(lib, hq=32, hkv=32, maxctx=100, ws=P2, wsb=1 << 30) == E.PKV_ERR_UNSUPPORTED
+    assert decode(lib, hq=48, hkv=12, maxctx=100, ws=P2, wsb=1 << 30) == E.PKV_ERR_UNSUPPORTED
     # nothing to do is fine even with NULL pointers
     assert decode(lib, nseq=0, q=None, out=None) == E.PKV_OK
 
@@ -84,14 +86,14 @@ def test_decode_validation(lib):
 def test_decode_workspace_size(lib):
     assert lib.pkv_decode_workspace_bytes(0, 32, 8, 128, 4096) == 0
     assert lib.pkv_decode_workspace_bytes(4, 32, 6, 128, 4096) == 0     # Hq % Hkv
-    # prefix sums + at most 8192 waves x 2 records x G x (128 + 4) floats
+    # prefix sums + at most 1024 workers x 2 records x Hq x (128 + 4) floats
     n = lib.pkv_decode_workspace_bytes(64, 32, 8, 128, 4096)
-    assert n == 512 + 8192 * 2 * 4 * 132 * 4
-    # a tiny batch needs few waves: 2 heads x 4 seqs x 7 tiles / 4 -> 16 waves
+    assert n == 512 + 1024 * 2 * 32 * 132 * 4
+    # a tiny batch needs few workers: 4 seqs x 7 tiles / 4 -> 7
     n = lib.pkv_decode_workspace_bytes(4, 8, 2, 128, 100)
-    assert n == 256 + 16 * 2 * 4 * 132 * 4
-    # an empty context still gets its prefix sums and the minimum of 4 waves
-    assert lib.pkv_decode_workspace_bytes(4, 8, 2, 128, 0) == 256 + 4 * 2 * 4 * 132 * 4
+    assert n == 256 + 7 * 2 * 8 * 132 * 4
+    # an empty context still gets its prefix sums and one worker
+    assert lib.pkv_decode_workspace_bytes(4, 8, 2, 128, 0) == 256 + 1 * 2 * 8 * 132 * 4
 
 
 def prefill(lib, **kw):
