@@ -1,8 +1,380 @@
-// prefill.hip -- placeholder until the MFMA chunked-prefill kernel lands.
+// prefill.hip -- chunked-prefill attention over the paged cache on gfx950
+// matrix cores (MFMA), causal, GQA-packed.
+//
+// What it computes ("LLM 推理优化技术全景", "Flash Attention 深度剖析 >
+// 分块算法" and "在线 Softmax"; "Chunked Prefill"): for query row r of
+// sequence i, at absolute position p = ctx_i - Lq_i + r, and query head h,
+//     out[row, h, :] = sum_{t <= p} exp(s_t - m) V[t, :] / sum_{t <= p} exp(s_t - m),
+//     s_t = scale * <q[row, h, :], K[t, :]>,
+// (all ctx_i keys when not causal).  Keys come from 16- or 32-token physical
+// blocks through the block table.  The page's outer loop over query blocks
+// is the grid; its inner loop over key/value blocks runs in each workgroup,
+// with S = Q K^T and O += P V on the matrix cores and the running max m /
+// sum l kept per query, so S never leaves the chip.
+//
+// Tiling (one workgroup = 4 waves, 128 "query columns"):
+//   * a workgroup owns one KV head and 128 / G consecutive query positions
+//     of one sequence; its 128 columns are (position, head) pairs, column
+//     c = (c / G)-th position, query head kvh * G + c % G, so every K/V tile
+//     staged in LDS serves all G query heads (GQA);
+//   * wave w owns columns 32w .. 32w + 31; with v_mfma_f32_32x32x16 the
+//     query index is the MFMA's N index (lane % 32) in both products:
+//       S^T[64 keys x 32 cols]  = K (A, from LDS) . Q^T (B, registers)
+//       O^T[128 dims x 32 cols] += V^T (A, from LDS) . P^T (B, registers)
+//     so each lane holds the scores of exactly one query column: the row max
+//     and sum are lane-local (plus one exchange with lane ^ 32), the rescale
+//     of O^T by exp(m_old - m_new) is lane-local, and P^T's accumulator
+//     layout is already the B operand of the second MFMA (the 16 keys of a
+//     k-step are taken in the order the accumulator holds them, and V^T is
+//     read from LDS in that same order);
+//   * QK^T runs on bf16 inputs (exact products, fp32 accumulate); P V runs on
+//     fp16: P in [0, 1] rounds with 2^-11 relative error (bf16 would give
+//     2^-8), and bf16 V converts to fp16 exactly for |v| in [2^-14, 65504];
+//   * K and V tiles of 64 keys are double-buffered in LDS: K as [key][dim]
+//     bf16, V transposed to [dim][key] fp16 while it is staged; the next
+//     tile's global loads are in flight while the current tile is computed.
+#include "pkv_device.h"
 #include "pkv_launch.h"
 
 namespace pkv {
 
-hipError_t launch_prefill(const PrefillArgs&, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int D = kHeadDim;
+constexpr int kKT = 64;          // keys per K/V tile
+constexpr int kCols = 128;       // query columns per workgroup
+constexpr int kThreads = 256;    // 4 waves
+constexpr int kKsStride = D + 8;      // bf16 elements per K row in LDS (272 B)
+constexpr int kVtStride = kKT + 4;    // fp16 elements per V^T row in LDS (136 B)
+constexpr int kKsElems = kKT * kKsStride;
+constexpr int kVtElems = D * kVtStride;
+
+struct PrefillIds {
+    const int32_t* row;
+    int nblk;
+    int base;
+    int cur;
+    int nxt;
+    __device__ __forceinline__ void init(const int32_t* r, int n, int lane) {
+        row = r;
+        nblk = n;
+        base = 0;
+        cur = lane < n ? r[lane] : 0;
+        nxt = 64 + lane < n ? r[64 + lane] : 0;
+    }
+    // id of block `blk` (wave-uniform, non-decreasing between calls)
+    __device__ __forceinline__ int get(int blk, int lane) {
+        while (blk >= base + 64) {
+            cur = nxt;
+            base += 64;
+            nxt = base + 64 + lane < nblk ? row[base + 64 + lane] : 0;
+        }
+        return __builtin_amdgcn_readlane(cur, blk - base);
+    }
+};
+
+// Global -> register staging of one 64-key tile: K chunks (4 x 16 B) and V
+// chunks (2 key pairs x 2 halves of the tile, 4 x 16 B) per thread.
+struct Stage {
+    uint4 k[4];
+    uint4 v[4];
+};
+
+template <int BS>
+__device__ __forceinline__ void stage_load(Stage& sg, PrefillIds& ids, const uint16_t* __restrict__ kc,
+                                           const uint16_t* __restrict__ vc, int k0, int kv_end,
+                                           size_t row_elems, int kvh, int tid, int lane) {
+    const int col = tid & 15;   // 16-byte chunk of a 256-byte row
+    const int kq = tid >> 4;    // 0..15
+    // ids of the tile's four 16-key groups, fetched in increasing order (the
+    // window only moves forward)
+    int id[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) id[i] = ids.get((k0 + 16 * i) / BS, lane);
+    // K: key k0 + kq + 16 i (group i)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int key = k0 + kq + 16 * i;
+        const size_t e = ((size_t)id[i] * BS + key % BS) * row_elems + (size_t)kvh * D + col * 8;
+        sg.k[i] = key < kv_end ? *reinterpret_cast<const uint4*>(kc + e) : make_uint4(0, 0, 0, 0);
+    }
+    // V: keys k0 + 2 kq + p + 32 j (p = pair member, j = tile half): group
+    // 2 j when 2 kq + p < 16, else group 2 j + 1
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int key = k0 + 2 * kq + p + 32 * j;
+            const int phys = (2 * kq + p) < 16 ? id[2 * j] : id[2 * j + 1];
+            const size_t e = ((size_t)phys * BS + key % BS) * row_elems + (size_t)kvh * D + col * 8;
+            sg.v[2 * j + p] = key < kv_end ? *reinterpret_cast<const uint4*>(vc + e)
+                                           : make_uint4(0, 0, 0, 0);
+        }
+    }
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+    f16x2_t h;
+    h[0] = (_Float16)a;
+    h[1] = (_Float16)b;
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ void stage_store(const Stage& sg, uint16_t* __restrict__ ks,
+                                            uint16_t* __restrict__ vt, int tid) {
+    const int col = tid & 15;
+    const int kq = tid >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint4*>(ks + (kq + 16 * i) * kKsStride + col * 8) = sg.k[i];
+    // V^T[dim][key] as fp16 pairs of adjacent keys
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const uint4 a = sg.v[2 * j];
+        const uint4 b = sg.v[2 * j + 1];
+        const uint32_t wa[4] = {a.x, a.y, a.z, a.w};
+        const uint32_t wb[4] = {b.x, b.y, b.z, b.w};
+        const int key = 2 * kq + 32 * j;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int d0 = col * 8 + 2 * w;
+            *reinterpret_cast<uint32_t*>(vt + d0 * kVtStride + key) =
+                pack_f16x2(bf16_lo(wa[w]), bf16_lo(wb[w]));
+            *reinterpret_cast<uint32_t*>(vt + (d0 + 1) * kVtStride + key) =
+                pack_f16x2(bf16_hi(wa[w]), bf16_hi(wb[w]));
+        }
+    }
+}
+
+// Grid: (num_q_tokens / (128 / G) + num_seqs, num_kv_heads); block 256.
+// Slot x of sequence i is x - T(i), T(i) = cu_q_lens[i] / P + i with
+// P = 128 / G positions per workgroup; T never skips a needed slot.
+template <int BS, int G, bool OUT_BF16>
+__global__ void __launch_bounds__(kThreads, 2)
+prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
+                    const int32_t* __restrict__ cu_q_lens, const uint16_t* __restrict__ k_cache,
+                    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
+                    int max_blocks_per_seq, const int32_t* __restrict__ context_lens,
+                    int max_context_len, int num_seqs, int num_q_heads, int num_kv_heads,
+                    float scale_log2, int causal, int decode_rows_elsewhere) {
+    constexpr int P = kCols / G;  // query positions per workgroup
+    __shared__ __attribute__((aligned(16))) uint16_t s_ks[2][kKsElems];
+    __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kVtElems];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int kvh = blockIdx.y;
+    const int slot = blockIdx.x;
+
+    // ---- which sequence owns this slot: 64-way search over T(i)
+    int lo = 0, hi = num_seqs;  // T(lo) <= slot < T(hi), T(num_seqs) = grid size
+    while (hi - lo > 1) {
+        const int step = (hi - lo + 63) / 64;
+        const int idx = lo + lane * step;
+        const bool ok = idx < hi && (cu_q_lens[idx] / P + idx) <= slot;
+        const unsigned long long m = __ballot(ok);  // low bits set, lane 0 always
+        const int last = 63 - __builtin_clzll(m);
+        lo = lo + last * step;
+        const int nh = lo + step;
+        hi = nh < hi ? nh : hi;
+    }
+    const int seq = lo;
+    const int q_begin = cu_q_lens[seq];
+    const int lq = cu_q_lens[seq + 1] - q_begin;
+    const int tile = slot - (q_begin / P + seq);
+    const int r0 = tile * P;
+    if (r0 >= lq) return;
+    if (decode_rows_elsewhere && lq == 1) return;
+    int ctx = context_lens[seq];
+    ctx = ctx < 0 ? 0 : (ctx > max_context_len ? max_context_len : ctx);
+    const int pos0 = ctx - lq;  // position of the chunk's first query row
+
+    // ---- this lane's query column
+    const int h = lane >> 5;              // half of the wave
+    const int c = wave * 32 + (lane & 31);
+    const int r = r0 + c / G;             // row inside the chunk
+    const int g = c % G;
+    const bool col_valid = r < lq;
+    const int pos = pos0 + r;
+    const int r_last = (r0 + P < lq ? r0 + P : lq) - 1;
+    const int kv_end = causal ? (pos0 + r_last + 1 < ctx ? pos0 + r_last + 1 : ctx) : ctx;
+    const int ntiles = (kv_end + kKT - 1) / kKT;
+
+    // Q^T fragments: k-step kk covers dims 16 kk + 8 h .. + 7 of this column;
+    // a negative scale moves into q's sign so maxima work on raw scores.
+    const uint32_t neg = scale_log2 < 0.0f ? 0x80008000u : 0u;
+    const float cl2 = fabsf(scale_log2);
+    bf16x8_t qf[8];
+    {
+        const size_t qrow = ((size_t)(q_begin + (col_valid ? r : 0)) * num_q_heads +
+                             (size_t)kvh * G + g) * D;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            uint4 w = col_valid ? *reinterpret_cast<const uint4*>(q + qrow + 16 * kk + 8 * h)
+                                : make_uint4(0, 0, 0, 0);
+            w.x ^= neg; w.y ^= neg; w.z ^= neg; w.w ^= neg;
+            qf[kk] = __builtin_bit_cast(bf16x8_t, w);
+        }
+    }
+
+    f32x16_t o[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[mb][e] = 0.0f;
+    float m_run = kNegBig;
+    float l_run = 0.0f;
+
+    const size_t row_elems = (size_t)num_kv_heads * D;
+    PrefillIds ids;
+    ids.init(block_table + (size_t)seq * max_blocks_per_seq, (ctx + BS - 1) / BS, lane);
+
+    Stage sg;
+    if (ntiles > 0) {
+        stage_load<BS>(sg, ids, k_cache, v_cache, 0, kv_end, row_elems, kvh, tid, lane);
+        stage_store(sg, s_ks[0], s_vt[0], tid);
+    }
+    __syncthreads();
+
+    for (int j = 0; j < ntiles; ++j) {
+        const int k0 = j * kKT;
+        const int buf = j & 1;
+        if (j + 1 < ntiles)
+            stage_load<BS>(sg, ids, k_cache, v_cache, k0 + kKT, kv_end, row_elems, kvh, tid, lane);
+
+        // ---- S^T = K . Q^T for keys k0 .. k0 + 63 (two 32-key blocks)
+        f32x16_t s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) s[kb][e] = 0.0f;
+            const uint16_t* krow = s_ks[buf] + (32 * kb + (lane & 31)) * kKsStride + 8 * h;
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(krow + 16 * kk));
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
+            }
+        }
+
+        // ---- online softmax for this lane's column (keys of both halves)
+        // element e of block kb is key k0 + 32 kb + 8 (e / 4) + 4 h + e % 4
+        const bool diag = causal ? (k0 + kKT - 1 > pos0 + r0) : false;
+        const bool tail = k0 + kKT > ctx;
+        float mt = -3.402823466e38f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * h + (e & 3);
+                bool ok = true;
+                if (diag) ok = key <= pos;
+                if (tail) ok = ok && key < ctx;
+                s[kb][e] = ok ? s[kb][e] : -3.402823466e38f;
+                mt = fmaxf(mt, s[kb][e]);
+            }
+        mt = fmaxf(mt, xor_lane(mt, 32));
+        const float mn = fmaxf(m_run, mt * cl2);
+        const float alpha = fast_exp2(m_run - mn);
+        m_run = mn;
+        if (__any(alpha != 1.0f)) {
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[mb][e] *= alpha;
+        }
+        float lsum = 0.0f;
+        f16x8_t pf[4];  // P^T fragments, k-step ks = keys 16 ks .. 16 ks + 15
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                float p = fast_exp2(fmaf(s[kb][e], cl2, -mn));
+                p = s[kb][e] == -3.402823466e38f ? 0.0f : p;
+                lsum += p;
+                pf[2 * kb + (e >> 3)][e & 7] = (_Float16)p;
+            }
+        l_run = fmaf(l_run, alpha, lsum);
+
+        // ---- O^T += V^T . P^T: A = V^T rows (dims), keys in accumulator order
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                const uint16_t* vrow = s_vt[buf] + (32 * mb + (lane & 31)) * kVtStride + 16 * ks + 4 * h;
+                const uint2 lo4 = *reinterpret_cast<const uint2*>(vrow);
+                const uint2 hi4 = *reinterpret_cast<const uint2*>(vrow + 8);
+                const f16x8_t a = __builtin_bit_cast(f16x8_t, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
+                o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[ks], o[mb], 0, 0, 0);
+            }
+        }
+
+        if (j + 1 < ntiles) stage_store(sg, s_ks[buf ^ 1], s_vt[buf ^ 1], tid);
+        __syncthreads();
+    }
+
+    // ---- finish: total l over both halves, then out = O / l
+    const float lt = l_run + xor_lane(l_run, 32);
+    if (!col_valid) return;
+    const float inv = ntiles > 0 ? 1.0f / lt : 0.0f;
+    const size_t orow = ((size_t)(q_begin + r) * num_q_heads + (size_t)kvh * G + g) * D;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            const int d0 = 32 * mb + 8 * e4 + 4 * h;
+            const float x0 = o[mb][4 * e4 + 0] * inv, x1 = o[mb][4 * e4 + 1] * inv;
+            const float x2 = o[mb][4 * e4 + 2] * inv, x3 = o[mb][4 * e4 + 3] * inv;
+            if (OUT_BF16) {
+                uint2 w;
+                w.x = (uint32_t)f32_to_bf16_rne(x0) | ((uint32_t)f32_to_bf16_rne(x1) << 16);
+                w.y = (uint32_t)f32_to_bf16_rne(x2) | ((uint32_t)f32_to_bf16_rne(x3) << 16);
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + orow + d0) = w;
+            } else {
+                *reinterpret_cast<float4*>(static_cast<float*>(out) + orow + d0) =
+                    make_float4(x0, x1, x2, x3);
+            }
+        }
+}
+
+template <int BS, int G, bool OUT_BF16>
+hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
+    constexpr int P = kCols / G;
+    const int slots = a.num_q_tokens / P + a.num_seqs;
+    dim3 grid(slots, a.num_kv_heads);
+    hipLaunchKernelGGL((prefill_mfma_kernel<BS, G, OUT_BF16>), grid, dim3(kThreads), 0, stream,
+                       a.out, a.q, a.cu_q_lens, a.k_cache, a.v_cache, a.block_table,
+                       a.max_blocks_per_seq, a.context_lens, a.max_context_len, a.num_seqs,
+                       a.num_q_heads, a.num_kv_heads, a.scale_log2, a.causal ? 1 : 0, 0);
+    return hipGetLastError();
+}
+
+template <int BS, int G>
+hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t s) {
+    return a.out_bf16 ? launch_prefill_t<BS, G, true>(a, s) : launch_prefill_t<BS, G, false>(a, s);
+}
+
+template <int BS>
+hipError_t launch_prefill_bs(const PrefillArgs& a, hipStream_t s) {
+    switch (a.num_q_heads / a.num_kv_heads) {
+        case 1: return launch_prefill_g<BS, 1>(a, s);
+        case 2: return launch_prefill_g<BS, 2>(a, s);
+        case 4: return launch_prefill_g<BS, 4>(a, s);
+        case 8: return launch_prefill_g<BS, 8>(a, s);
+        case 16: return launch_prefill_g<BS, 16>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+    return a.block_size == 16 ? launch_prefill_bs<16>(a, stream) : launch_prefill_bs<32>(a, stream);
+}
 
 }  // namespace pkv

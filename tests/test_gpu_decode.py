@@ -76,8 +76,10 @@ def test_decode_zero_context_rows_are_zero():
 def test_decode_bf16_output():
     w = W.llama8b_decode(batch=6, lo=100, hi=2500, seed=2300)
     bc = W.materialize(w, logical=True, poison=True)
-    out = run_decode(bc.to(DEV), out_dtype=torch.bfloat16)
-    bf16_parity(out, oracle_decode(bc), what="bf16 out")
+    b = bc.to(DEV)
+    out16 = run_decode(b, out_dtype=torch.bfloat16)
+    out32 = run_decode(b)
+    bf16_parity(out16, out32, oracle_decode(bc), what="decode bf16 out")
 
 
 def test_decode_scaled_down_8b_shape():
