@@ -27,6 +27,21 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak, published
+
+
+def attention_flops(w):
+    """Exact causal FLOPs: 2 D for q.k and 2 D for p.v per visible (query, key)
+    pair and query head."""
+    pairs = 0
+    for c, lq in zip(w.context_lens, w.q_lens):
+        # rows at positions c - lq .. c - 1 see c - lq + 1 .. c keys
+        pairs += lq * (c - lq) + lq * (lq + 1) // 2
+    return 4 * w.head_dim * w.num_q_heads * pairs
+
+
+def decode_kv_bytes(w):
+    return sum(c for c, lq in zip(w.context_lens, w.q_lens) if lq == 1) * w.kv_token_bytes()
 
 
 def workload_by_name(name):
@@ -37,6 +52,10 @@ def workload_by_name(name):
         "llama70b_decode_bs16": lambda: W.llama70b_decode(block_size=16),
         "llama70b_decode_bs32": lambda: W.llama70b_decode(block_size=32),
         "tiny_decode": lambda: W.tiny_decode(),
+        # chunked prefill: the 4 x 512-query chunks alone, then with the 128
+        # decodes riding along in the same call
+        "prefill_chunks": lambda: W.mixed_prefill(num_decodes=0),
+        "mixed_prefill": lambda: W.mixed_prefill(),
     }
     if name not in table:
         raise SystemExit(f"unknown workload {name}; choose from {sorted(table)}")
@@ -93,15 +112,26 @@ def main():
     out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
+    if not w.is_decode:
+        out = torch.empty((w.total_q, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+
+    def attend():
+        if w.is_decode:
+            pkv.paged_decode_attn(b.q, b.k_cache, b.v_cache, b.block_table, b.context_lens,
+                                  w.scale, max_context_len=w.max_context_len, out=out,
+                                  workspace=ws, stream=stream)
+        else:
+            pkv.paged_prefill_attn(b.q, b.cu_q_lens, b.k_cache, b.v_cache, b.block_table,
+                                   b.context_lens, w.scale, max_context_len=w.max_context_len,
+                                   max_q_len=w.max_q_len, causal=True, out=out, stream=stream)
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
         pkv.kv_append(b.k_new, b.v_new, b.slot_mapping, b.k_cache, b.v_cache, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        pkv.paged_decode_attn(b.q, b.k_cache, b.v_cache, b.block_table, b.context_lens,
-                              w.scale, max_context_len=w.max_context_len, out=out,
-                              workspace=ws, stream=stream)
+        attend()
         if ev is not None:
             ev[2].record(stream)
 
@@ -131,6 +161,33 @@ def main():
           f"{sorted(decode_ms)[(9 * len(decode_ms)) // 10] * 1e3:.1f}) | append avg "
           f"{statistics.mean(append_ms) * 1e3:.1f} us | decode KV {achieved:.0f} GB/s",
           file=sys.stderr, flush=True)
+
+    if not w.is_decode:
+        flops = attention_flops(w)
+        tflops = flops / (dec_avg * 1e-3) / 1e12
+        dkv = decode_kv_bytes(w)
+        print(f"[bench] prefill attn {dec_avg * 1e3:.1f} us: {tflops:.1f} TFLOP/s "
+              f"({100 * tflops / MFMA_BF16_PEAK_TFLOPS:.1f}% of MFMA peak), decode rows "
+              f"{dkv / (dec_avg * 1e-3) / 1e9:.0f} GB/s of KV", file=sys.stderr, flush=True)
+        rec = {
+            "metric": "paged prefill attn: MFMA TFLOP/s (exact causal FLOPs) + decode-row KV GB/s",
+            "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": w.name, **{k: v for k, v in w.describe().items()
+                                              if k != "workload"}},
+            "kernels_us": {"kv_append": round(statistics.mean(append_ms) * 1e3, 2),
+                           "paged_prefill_attn": round(dec_avg * 1e3, 2)},
+            "decode_rows_kv_gbs": round(dkv / (dec_avg * 1e-3) / 1e9, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "kernel": "paged_prefill_attn (MFMA chunk kernel)",
+                         "algorithmic_flops_per_launch": flops},
+        }
+        print(json.dumps(rec), flush=True)
+        return
 
     rec = {
         "metric": "paged decode attn: achieved KV HBM GB/s (% of MI355X peak) + seq-steps/s",

@@ -142,7 +142,11 @@ int pkv_paged_decode_attn(void *out, int out_dtype, const void *q, const void *k
                           int num_kv_heads, int head_dim, int block_size, float scale,
                           void *workspace, size_t workspace_bytes, void *stream);
 
-/* Workspace needed by pkv_paged_prefill_attn (bytes, >= 0). */
+/*
+ * Workspace needed by pkv_paged_prefill_attn (bytes, >= 0): the decode
+ * workspace for the batch's single-row sequences.  A call whose every
+ * sequence has exactly max_q_len > 1 rows needs none (workspace may be NULL).
+ */
 size_t pkv_prefill_workspace_bytes(int num_seqs, int num_q_tokens, int num_q_heads,
                                    int head_dim, int max_context_len);
 
@@ -164,8 +168,10 @@ size_t pkv_prefill_workspace_bytes(int num_seqs, int num_q_tokens, int num_q_hea
  *                  Lq_i <= context_lens[i] is required.
  *   max_q_len      host-side upper bound of Lq_i
  *   num_q_tokens   host-side total query rows (= cu_q_lens[num_seqs])
- * Rows with Lq_i == 1 take the bandwidth-bound decode path; longer chunks
- * take the MFMA path.  QK^T runs as bf16 x bf16 MFMA with fp32 accumulation;
+ * Rows with Lq_i == 1 take the bandwidth-bound decode path (the split-KV
+ * decode kernels, enqueued after the MFMA chunk kernel on the same stream);
+ * longer chunks take the MFMA path.  num_seqs <= 16383 and num_kv_heads in
+ * 1..8 or 16 when single-row sequences can be present.  QK^T runs as bf16 x bf16 MFMA with fp32 accumulation;
  * P V runs as fp16 x fp16 MFMA with fp32 accumulation, V converted from bf16
  * to fp16 in registers: exact for |v| in [2^-14, 65504]; smaller magnitudes
  * keep an absolute error below 2^-25, and |v| > 65504 is outside the

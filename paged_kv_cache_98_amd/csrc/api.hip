@@ -129,17 +129,17 @@ int pkv_paged_decode_attn(void* out, int out_dtype, const void* q, const void* k
     a.records = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                          align_up((size_t)(num_seqs + 1) * sizeof(int32_t), 256));
     a.max_workers = pkv::decode_max_workers(num_seqs, max_context_len);
+    a.cu_q_lens = nullptr;
     return to_status(pkv::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
 size_t pkv_prefill_workspace_bytes(int num_seqs, int num_q_tokens, int num_q_heads, int head_dim,
                                    int max_context_len) {
-    (void)num_seqs;
     (void)num_q_tokens;
-    (void)num_q_heads;
-    (void)head_dim;
-    (void)max_context_len;
-    return 0;
+    if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+    // the decode rows of a mixed batch use the decode kernels' workspace
+    // (records are per query head, so the KV head count does not matter)
+    return pkv::decode_workspace_bytes(num_seqs, num_q_heads, 1, head_dim, max_context_len);
 }
 
 int pkv_paged_prefill_attn(void* out, int out_dtype, const void* q, const int32_t* cu_q_lens,
@@ -149,8 +149,6 @@ int pkv_paged_prefill_attn(void* out, int out_dtype, const void* q, const int32_
                            int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                            float scale, int causal, void* workspace, size_t workspace_bytes,
                            void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     int st = check_attention_shape(max_blocks_per_seq, max_context_len, num_seqs, num_q_heads,
                                    num_kv_heads, head_dim, block_size, out_dtype);
     if (st != PKV_OK) return st;
@@ -162,6 +160,19 @@ int pkv_paged_prefill_attn(void* out, int out_dtype, const void* q, const int32_
         return PKV_ERR_NULL;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
         return PKV_ERR_ALIGN;
+    // Rows of sequences with a single query go to the bandwidth-bound decode
+    // kernels; they can exist unless every sequence has max_q_len > 1 rows.
+    const bool uniform_chunks = max_q_len > 1 && (int64_t)num_q_tokens == (int64_t)num_seqs * max_q_len;
+    const bool any_decode_rows = !uniform_chunks;
+    const bool decode_limits_ok = num_seqs <= kMaxDecodeSeqs &&
+                                  (num_kv_heads <= 8 || num_kv_heads == kMaxDecodeKvHeads);
+    if (any_decode_rows) {
+        if (!decode_limits_ok) return PKV_ERR_UNSUPPORTED;
+        const size_t need = pkv::decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
+                                                        head_dim, max_context_len);
+        if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+    }
 
     pkv::PrefillArgs a;
     a.out = out;
@@ -182,7 +193,35 @@ int pkv_paged_prefill_attn(void* out, int out_dtype, const void* q, const int32_
     a.block_size = block_size;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.causal = causal != 0;
-    return to_status(pkv::launch_prefill(a, static_cast<hipStream_t>(stream)));
+    a.decode_rows_elsewhere = any_decode_rows;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (max_q_len > 1) {
+        st = to_status(pkv::launch_prefill(a, s));
+        if (st != PKV_OK) return st;
+    }
+    if (!any_decode_rows) return PKV_OK;
+
+    pkv::DecodeArgs d;
+    d.out = out;
+    d.out_bf16 = a.out_bf16;
+    d.q = a.q;
+    d.k_cache = a.k_cache;
+    d.v_cache = a.v_cache;
+    d.block_table = block_table;
+    d.max_blocks_per_seq = max_blocks_per_seq;
+    d.context_lens = context_lens;
+    d.max_context_len = max_context_len;
+    d.num_seqs = num_seqs;
+    d.num_q_heads = num_q_heads;
+    d.num_kv_heads = num_kv_heads;
+    d.block_size = block_size;
+    d.scale_log2 = a.scale_log2;
+    d.cum = static_cast<int32_t*>(workspace);
+    d.records = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                         align_up((size_t)(num_seqs + 1) * sizeof(int32_t), 256));
+    d.max_workers = pkv::decode_max_workers(num_seqs, max_context_len);
+    d.cu_q_lens = cu_q_lens;
+    return to_status(pkv::launch_decode(d, s));
 }
 
 }  // extern "C"

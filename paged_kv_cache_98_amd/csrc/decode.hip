@@ -199,6 +199,22 @@ __device__ __forceinline__ int clamp_ctx(int ctx, int max_context_len) {
     return ctx < 0 ? 0 : (ctx > max_context_len ? max_context_len : ctx);
 }
 
+// With cu_q_lens (a mixed prefill batch) only sequences with exactly one
+// query row are decoded here, and their q / out row is cu_q_lens[i]; without
+// it every sequence is one row, row i.
+__device__ __forceinline__ bool is_decode_row(const int32_t* __restrict__ cu_q_lens, int i) {
+    return cu_q_lens == nullptr || cu_q_lens[i + 1] - cu_q_lens[i] == 1;
+}
+__device__ __forceinline__ int row_of(const int32_t* __restrict__ cu_q_lens, int i) {
+    return cu_q_lens == nullptr ? i : cu_q_lens[i];
+}
+__device__ __forceinline__ int tiles_of(const int32_t* __restrict__ context_lens,
+                                        const int32_t* __restrict__ cu_q_lens, int i,
+                                        int max_context_len) {
+    if (!is_decode_row(cu_q_lens, i)) return 0;
+    return (clamp_ctx(context_lens[i], max_context_len) + kTileTokens - 1) / kTileTokens;
+}
+
 // Sliding window over a block-table row: lane j of `cur` holds the id of
 // block base + j, lane j of `nxt` that of base + 64 + j.  Tiles are visited
 // in increasing order, so the window only ever moves forward by 64.
@@ -246,7 +262,7 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
                       const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
                       int max_blocks_per_seq, const int32_t* __restrict__ context_lens,
                       int max_context_len, int num_seqs, int num_q_heads, int num_kv_heads,
-                      float scale_log2, int num_workers) {
+                      float scale_log2, int num_workers, const int32_t* __restrict__ cu_q_lens) {
     constexpr int D = kHeadDim;
     extern __shared__ int32_t s_cum[];  // s_cum[i] = tiles (per KV head) of sequences < i
     __shared__ int32_t s_part[64 * max_waves_per_worker<G>()];
@@ -259,7 +275,7 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
     for (int k = 0; k < per; ++k) {
         const int i = tid * per + k;
         if (i < num_seqs)
-            local += (clamp_ctx(context_lens[i], max_context_len) + kTileTokens - 1) / kTileTokens;
+            local += tiles_of(context_lens, cu_q_lens, i, max_context_len);
     }
     s_part[tid] = local;
     __syncthreads();
@@ -274,7 +290,7 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
         const int i = tid * per + k;
         if (i < num_seqs) {
             s_cum[i] = run;
-            run += (clamp_ctx(context_lens[i], max_context_len) + kTileTokens - 1) / kTileTokens;
+            run += tiles_of(context_lens, cu_q_lens, i, max_context_len);
         }
     }
     if (tid == nthr - 1) s_cum[num_seqs] = s_part[tid];
@@ -315,7 +331,7 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
         const int ntile = (int)(piece_end - t);
         const int ctx = clamp_ctx(context_lens[seq], max_context_len);
 
-        const size_t head_row = ((size_t)seq * num_q_heads + (size_t)kvh * G) * D;
+        const size_t head_row = ((size_t)row_of(cu_q_lens, seq) * num_q_heads + (size_t)kvh * G) * D;
         uint4 qv[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -407,13 +423,15 @@ template <bool OUT_BF16>
 __global__ void __launch_bounds__(256)
 decode_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
                     const int32_t* __restrict__ cum, const int32_t* __restrict__ context_lens,
-                    int max_context_len, int num_seqs, int num_q_heads, int num_workers) {
+                    int max_context_len, int num_seqs, int num_q_heads, int num_workers,
+                    const int32_t* __restrict__ cu_q_lens) {
     constexpr int D = kHeadDim;
     const int lane = threadIdx.x & 63;
     const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int seq = blockIdx.y;
     if (h >= num_q_heads) return;
-    const size_t e = ((size_t)seq * num_q_heads + h) * D + 2 * lane;
+    if (!is_decode_row(cu_q_lens, seq)) return;  // a prefill chunk: not ours
+    const size_t e = ((size_t)row_of(cu_q_lens, seq) * num_q_heads + h) * D + 2 * lane;
     const int ctx = clamp_ctx(context_lens[seq], max_context_len);
     if (ctx == 0) {  // nothing to attend to: a defined all-zero row
         store1<OUT_BF16>(out, e, 0.0f);
@@ -498,13 +516,14 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((decode_streamk_kernel<BS, G, OUT_BF16>), dim3((int)workers, groups), dim3(threads),
                        lds, stream, a.out, a.records, a.cum, a.q, a.k_cache, a.v_cache,
                        a.block_table, a.max_blocks_per_seq, a.context_lens, a.max_context_len,
-                       a.num_seqs, a.num_q_heads, a.num_kv_heads, a.scale_log2, (int)workers);
+                       a.num_seqs, a.num_q_heads, a.num_kv_heads, a.scale_log2, (int)workers,
+                       a.cu_q_lens);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 mgrid((a.num_q_heads + 3) / 4, a.num_seqs);
     hipLaunchKernelGGL((decode_merge_kernel<OUT_BF16>), mgrid, dim3(256), 0, stream, a.out,
                        a.records, a.cum, a.context_lens, a.max_context_len, a.num_seqs,
-                       a.num_q_heads, (int)workers);
+                       a.num_q_heads, (int)workers, a.cu_q_lens);
     return hipGetLastError();
 }
 

@@ -37,6 +37,10 @@ struct DecodeArgs {
     int32_t* cum;         // workspace: [num_seqs + 1] tile prefix sums
     float* records;       // workspace: [max_workers][2][num_q_heads][head_dim + 4] partials
     int64_t max_workers;  // workers whose records fit the workspace
+    // NULL for a plain decode batch.  Set for the decode rows of a mixed
+    // prefill batch: only sequences with one query row are handled, reading
+    // and writing row cu_q_lens[i].
+    const int32_t* cu_q_lens;
 };
 
 struct PrefillArgs {
@@ -58,6 +62,7 @@ struct PrefillArgs {
     int block_size;
     float scale_log2;
     bool causal;
+    bool decode_rows_elsewhere;  // skip sequences with one query row
 };
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);

@@ -350,7 +350,8 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((prefill_mfma_kernel<BS, G, OUT_BF16>), grid, dim3(kThreads), 0, stream,
                        a.out, a.q, a.cu_q_lens, a.k_cache, a.v_cache, a.block_table,
                        a.max_blocks_per_seq, a.context_lens, a.max_context_len, a.num_seqs,
-                       a.num_q_heads, a.num_kv_heads, a.scale_log2, a.causal ? 1 : 0, 0);
+                       a.num_q_heads, a.num_kv_heads, a.scale_log2, a.causal ? 1 : 0,
+                       a.decode_rows_elsewhere ? 1 : 0);
     return hipGetLastError();
 }
 
