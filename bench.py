@@ -90,6 +90,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
@@ -100,6 +102,18 @@ def main():
     import torch
     from paged_kv_cache_98_amd import binding as pkv
     from paged_kv_cache_98_amd import workloads as W
+
+    if args.copy_calibration:
+        # A plain copy of known size: 1 GiB read + 1 GiB written per dispatch.
+        # Profiled with the FETCH_SIZE / WRITE_SIZE counters it gives the
+        # factor that turns those counters into bytes.
+        src = torch.ones(1 << 29, dtype=torch.int16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_dispatch": src.numel() * 2}), flush=True)
+        return
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
