@@ -50,17 +50,27 @@ struct Tile {
     uint4 v[kLoads];
 };
 
-__device__ __forceinline__ void load_tile(Tile& t, const uint16_t* __restrict__ kc,
-                                          const uint16_t* __restrict__ vc, size_t base,
-                                          uint32_t lane_off, uint32_t four_rows) {
+// Buffer resource over `base` (wave-uniform, so it lives in scalar
+// registers); word 3 is the gfx9-family raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, 0x7fffffff,
+                                             0x00020000);
+}
+
+// Loads one tile: `kt` / `vt` address the tile's first row for this KV head
+// in the K / V pool, `voff[i]` is this lane's byte offset of load group i
+// (tokens 4i + row, dims 8c .. 8c + 7): buffer loads with a scalar base and
+// a 32-bit lane offset, so no per-lane 64-bit addresses are kept.
+__device__ __forceinline__ void load_tile(Tile& t, const char* kt, const char* vt,
+                                          const uint32_t (&voff)[kLoads]) {
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kt);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vt);
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-        t.k[i] = *reinterpret_cast<const uint4*>(kc + base + lane_off + i * four_rows);
-    }
+    for (int i = 0; i < kLoads; ++i)
+        t.k[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, voff[i], 0, 0));
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-        t.v[i] = *reinterpret_cast<const uint4*>(vc + base + lane_off + i * four_rows);
-    }
+    for (int i = 0; i < kLoads; ++i)
+        t.v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff[i], 0, 0));
 }
 
 template <int G>
@@ -147,15 +157,6 @@ __device__ __forceinline__ void process_tile(State<G>& st, const Tile& t, const 
     }
 }
 
-template <int G>
-__device__ __forceinline__ void process_any(State<G>& st, const Tile& t, const uint4 (&qv)[G],
-                                            float c, int row, int ntok_left) {
-    if (ntok_left >= kTileTokens)
-        process_tile<G, false>(st, t, qv, c, row, ntok_left);
-    else
-        process_tile<G, true>(st, t, qv, c, row, ntok_left);
-}
-
 template <bool OUT_BF16>
 __device__ __forceinline__ void store8(void* out, size_t elem, const float (&x)[8]) {
     if (OUT_BF16) {
@@ -235,17 +236,21 @@ struct IdWindow {
         if (blk >= base + 64) {
             cur = nxt;
             base += 64;
-            nxt = base + 64 + lane < nblk ? row[base + 64 + lane] : 0;
+            // clamped rather than masked: the load lands straight in `nxt`
+            // and nothing waits for it until the window moves again
+            const int k = base + 64 + lane;
+            nxt = row[k < nblk ? k : nblk - 1];
         }
         return __builtin_amdgcn_readlane(cur, blk - base);
     }
 };
 
+// Byte offset (wave-uniform) of a tile's first token row in a pool.
 template <int BS>
-__device__ __forceinline__ size_t tile_elem(IdWindow& ids, int tile, size_t row_elems, int lane) {
+__device__ __forceinline__ size_t tile_bytes(IdWindow& ids, int tile, size_t row_bytes, int lane) {
     const int tok = tile * kTileTokens;
     const int phys = ids.get(tok / BS, lane);
-    return ((size_t)phys * BS + (tok % BS)) * row_elems;
+    return ((size_t)phys * BS + (tok % BS)) * row_bytes;
 }
 
 // Grid: (num_workers, head groups); a workgroup has one wave per KV head of
@@ -311,9 +316,13 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
 
     const uint32_t neg = scale_log2 < 0.0f ? 0x80008000u : 0u;
     const float c = fabsf(scale_log2);
-    const size_t row_elems = (size_t)num_kv_heads * D;
-    const uint32_t four_rows = (uint32_t)(4 * row_elems);
-    const uint32_t lane_off = (uint32_t)(row * row_elems + (size_t)kvh * D + col * 8);
+    const size_t row_bytes = (size_t)num_kv_heads * D * sizeof(uint16_t);
+    uint32_t voff[kLoads];
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i)
+        voff[i] = (uint32_t)((4 * i + row) * row_bytes + ((size_t)kvh * D + col * 8) * sizeof(uint16_t));
+    const char* kbase = reinterpret_cast<const char*>(k_cache);
+    const char* vbase = reinterpret_cast<const char*>(v_cache);
     bool first_piece = true;
 
     while (t < t_end) {
@@ -351,18 +360,46 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
         ids.init(block_table + (size_t)seq * max_blocks_per_seq, (ctx + BS - 1) / BS,
                  (tile0 * kTileTokens) / BS, lane);
 
+        // Two-deep load pipeline over the piece's tiles 0 .. n-1 (buffers a
+        // and b alternate).  The steady-state loop issues both of its loads
+        // unconditionally, so while one buffer is processed the other's
+        // eight loads stay in flight (a load issued on some paths only would
+        // force the wait counters to drain it).  Only the sequence's last
+        // tile can be partial, and it is never inside the loop.
+        const int n = ntile;
+        const bool tail = piece_end == seg_t1 && (ctx % kTileTokens) != 0;
+        auto fetch = [&](Tile& x, int j) {
+            const size_t o = tile_bytes<BS>(ids, tile0 + j, row_bytes, lane);
+            load_tile(x, kbase + o, vbase + o, voff);
+        };
+        auto finish = [&](const Tile& x, int j) {
+            if (tail && j == n - 1)
+                process_tile<G, true>(st, x, qv, c, row, ctx - (tile0 + j) * kTileTokens);
+            else
+                process_tile<G, false>(st, x, qv, c, row, kTileTokens);
+        };
         Tile a, b;
-        load_tile(a, k_cache, v_cache, tile_elem<BS>(ids, tile0, row_elems, lane), lane_off, four_rows);
-        for (int j = 0; j < ntile; j += 2) {
-            if (j + 1 < ntile)
-                load_tile(b, k_cache, v_cache, tile_elem<BS>(ids, tile0 + j + 1, row_elems, lane),
-                          lane_off, four_rows);
-            process_any<G>(st, a, qv, c, row, ctx - (tile0 + j) * kTileTokens);
-            if (j + 1 >= ntile) break;
-            if (j + 2 < ntile)
-                load_tile(a, k_cache, v_cache, tile_elem<BS>(ids, tile0 + j + 2, row_elems, lane),
-                          lane_off, four_rows);
-            process_any<G>(st, b, qv, c, row, ctx - (tile0 + j + 1) * kTileTokens);
+        fetch(a, 0);
+        if (n == 1) {
+            finish(a, 0);
+        } else {
+            fetch(b, 1);
+            int j = 0;
+            for (; j + 3 < n; j += 2) {  // tiles j + 2 and j + 3 exist and are full
+                process_tile<G, false>(st, a, qv, c, row, kTileTokens);
+                fetch(a, j + 2);
+                process_tile<G, false>(st, b, qv, c, row, kTileTokens);
+                fetch(b, j + 3);
+            }
+            // two or three tiles left: j (in a), j + 1 (in b), maybe j + 2
+            process_tile<G, false>(st, a, qv, c, row, kTileTokens);
+            if (n - j == 3) {
+                fetch(a, j + 2);
+                process_tile<G, false>(st, b, qv, c, row, kTileTokens);
+                finish(a, j + 2);
+            } else {
+                finish(b, j + 1);
+            }
         }
 
         // Merge the four row streams: M = max m_r, l = sum l_r 2^(m_r - M),

@@ -102,6 +102,48 @@ def test_decode_is_deterministic_and_permutation_invariant():
     assert torch.equal(o1, op)
 
 
+def test_decode_workspace_garbage_reuse_and_graph_replay():
+    """Sequences shared by several workers are merged by whichever finishes
+    last, found through per-(sequence, KV head) arrival cells in the
+    workspace.  A workspace of random bytes, the same workspace reused, and
+    graph replays (each replay repeats the captured call's tag) all give the
+    same bits, within the oracle's bar."""
+    # enough tiles (3282) for more key ranges than resident workgroups, so
+    # ranges are claimed dynamically as well
+    w = W.make_workload("ws", [8000, 17, 16000, 9000, 12500, 1, 7000], num_q_heads=32,
+                        num_kv_heads=8, block_size=16, seed=2500)
+    bc = W.materialize(w, logical=True, poison=True)
+    b = bc.to(DEV)
+    need = pkv.decode_workspace_bytes(w.num_seqs, 32, 8, w.max_context_len)
+    gen = torch.Generator(device=DEV).manual_seed(7)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device=DEV, generator=gen)
+    call = lambda out=None: pkv.paged_decode_attn(
+        b.q, b.k_cache, b.v_cache, b.block_table, b.context_lens, w.scale,
+        max_context_len=w.max_context_len, out=out, workspace=ws)
+    o1 = call()
+    o2 = call()
+    torch.cuda.synchronize()
+    parity(o1, oracle_decode(bc), what="garbage workspace")
+    assert torch.equal(o1, o2)
+    out = torch.zeros_like(o1)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out)
+    for r in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, o1), f"graph replay {r}"
+        assert torch.equal(call(), o1), f"eager call after replay {r}"
+
+
 FULL = {
     "llama8b_decode_b64": lambda: W.llama8b_decode(),
     "long_context_decode_b8": lambda: W.long_context_decode(),
