@@ -39,18 +39,22 @@ __device__ __forceinline__ float dpp_mov(float x) {
         float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
 }
 
-// DPP controls: quad permutations and rotations inside a 16-lane row.
-constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
-constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
-constexpr int kDppRowRor4 = 0x124;  // row_ror:4
-constexpr int kDppRowRor8 = 0x128;  // row_ror:8
+// DPP controls: quad permutations and mirrors inside a 16-lane row.
+constexpr int kDppQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7 - i in each half row
+constexpr int kDppRowMirror = 0x140;      // lane i <-> 15 - i in the row
 
-// Sum over the 16 lanes of each row; every lane of the row receives it.
+// Sum over the 16 lanes of each row; every lane of the row receives the
+// same bits.  Each step adds two partners that hold equal values within
+// their groups (pairs, quads, half rows), so both sides compute A + B and
+// B + A, which round alike; rotations would pair lanes asymmetrically and
+// leave quads with differently rounded totals.
 __device__ __forceinline__ float row_sum16(float x) {
     x += dpp_mov<kDppQuadXor1>(x);
     x += dpp_mov<kDppQuadXor2>(x);
-    x += dpp_mov<kDppRowRor4>(x);
-    x += dpp_mov<kDppRowRor8>(x);
+    x += dpp_mov<kDppRowHalfMirror>(x);
+    x += dpp_mov<kDppRowMirror>(x);
     return x;
 }
 
