@@ -50,21 +50,14 @@ struct Tile {
     uint4 v[kLoads];
 };
 
-// Buffer resource over `base` (wave-uniform, so it lives in scalar
-// registers); word 3 is the gfx9-family raw-buffer format.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, 0x7fffffff,
-                                             0x00020000);
-}
-
 // Loads one tile: `kt` / `vt` address the tile's first row for this KV head
 // in the K / V pool, `voff[i]` is this lane's byte offset of load group i
 // (tokens 4i + row, dims 8c .. 8c + 7): buffer loads with a scalar base and
 // a 32-bit lane offset, so no per-lane 64-bit addresses are kept.
 __device__ __forceinline__ void load_tile(Tile& t, const char* kt, const char* vt,
                                           const uint32_t (&voff)[kLoads]) {
-    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kt);
-    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vt);
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kt);
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vt);
 #pragma unroll
     for (int i = 0; i < kLoads; ++i)
         t.k[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, voff[i], 0, 0));
@@ -486,18 +479,41 @@ decode_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
         const int slot = (w == wf && worker_start(w, U, W) < t0) ? 1 : 0;
         return rec + ((size_t)(w * 2 + slot) * num_q_heads + h) * kRecStride;
     };
-    float mx = -INFINITY;
-    for (int64_t w = wf + lane; w <= wl; w += 64) mx = fmaxf(mx, rec_of(w)[D]);
+    // maximum over the pieces' running maxima, one piece per lane; the
+    // first 64 pieces' (m, l) stay in their lanes
+    float2 ml0 = make_float2(-INFINITY, 0.0f);
+    if (wf + lane <= wl) ml0 = *reinterpret_cast<const float2*>(rec_of(wf + lane) + D);
+    float mx = ml0.x;
+    for (int64_t w = wf + 64 + lane; w <= wl; w += 64) mx = fmaxf(mx, rec_of(w)[D]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    // then the pieces in worker order, 64 at a time: lane k holds the scale
+    // exp2(m - mx) and the sum l of piece base + k, and the accumulator
+    // rows are loaded eight pieces ahead of their use
     float L = 0.0f, a0 = 0.0f, a1 = 0.0f;
-    for (int64_t w = wf; w <= wl; ++w) {
-        const float* r = rec_of(w);
-        const float f = fast_exp2(r[D] - mx);
-        L = fmaf(r[D + 1], f, L);
-        const float2 a = *reinterpret_cast<const float2*>(r + 2 * lane);
-        a0 = fmaf(a.x, f, a0);
-        a1 = fmaf(a.y, f, a1);
+    for (int64_t base = wf; base <= wl; base += 64) {
+        const int cnt = wl - base + 1 < 64 ? (int)(wl - base + 1) : 64;
+        float2 ml = ml0;
+        if (base != wf)
+            ml = lane < cnt ? *reinterpret_cast<const float2*>(rec_of(base + lane) + D)
+                            : make_float2(-INFINITY, 0.0f);
+        const float fk = lane < cnt ? fast_exp2(ml.x - mx) : 0.0f;
+        const float lk = ml.y;
+        for (int k = 0; k < cnt; k += 8) {
+            float2 av[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                av[u] = k + u < cnt ? *reinterpret_cast<const float2*>(rec_of(base + k + u) + 2 * lane)
+                                    : make_float2(0.0f, 0.0f);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (k + u >= cnt) break;
+                const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fk), k + u));
+                L = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(lk), k + u)), f, L);
+                a0 = fmaf(av[u].x, f, a0);
+                a1 = fmaf(av[u].y, f, a1);
+            }
+        }
     }
     const float inv = 1.0f / L;
     store1<OUT_BF16>(out, e, a0 * inv);

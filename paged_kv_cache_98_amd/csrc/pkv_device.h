@@ -21,6 +21,16 @@ constexpr float kNegBig = -1.0e30f;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+// Raw buffer resource over `base` (wave-uniform, so it lives in scalar
+// registers) spanning 2^31 - 1 bytes; word 3 is the gfx9-family raw-buffer
+// format.  A lane offset at or past kBufferOob reads zeros without touching
+// memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff,
+                                             0x00020000);
+}
+constexpr uint32_t kBufferOob = 0x80000000u;
+
 // fp32 value of the low / high bf16 of a packed pair (exact: a bf16 is the
 // top half of the fp32 with the same value).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -85,35 +85,59 @@ struct Stage {
     uint4 v[4];
 };
 
+// This thread's byte offsets inside a block for its staging loads: row
+// within the block times the row pitch, plus its 16-byte chunk of the head's
+// 256 bytes.  K load i carries key k0 + kq + 16 i, V load 2 j + p key
+// k0 + 2 kq + p + 32 j; k0 is a multiple of 64, hence of the block size, so
+// the offsets are the same for every tile.
 template <int BS>
-__device__ __forceinline__ void stage_load(Stage& sg, PrefillIds& ids, const uint16_t* __restrict__ kc,
-                                           const uint16_t* __restrict__ vc, int k0, int kv_end,
-                                           size_t row_elems, int kvh, int tid, int lane) {
-    const int col = tid & 15;   // 16-byte chunk of a 256-byte row
-    const int kq = tid >> 4;    // 0..15
+__device__ __forceinline__ void stage_offsets(uint32_t (&koff)[4], uint32_t (&voff)[4],
+                                              uint32_t row_bytes, int tid) {
+    const int col = tid & 15;
+    const int kq = tid >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) koff[i] = (uint32_t)((kq + 16 * i) % BS) * row_bytes + col * 16;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+            voff[2 * j + p] = (uint32_t)((2 * kq + p + 32 * j) % BS) * row_bytes + col * 16;
+}
+
+// Loads one 64-key tile into registers.  Every load of a wave reads one
+// physical block: K load i lies in the tile's 16-key group i, V load 2 j + p
+// in group 2 j + (kq >= 8), and kq = 4 wave + lane / 16 is at least 8 for
+// waves 2 and 3 only.  So the block's address is a scalar buffer base and
+// the lane offsets are the fixed ones above; keys past kv_end read zeros
+// without a memory access.  kbase / vbase point at this KV head's slice of
+// block 0 of the pools.
+template <int BS>
+__device__ __forceinline__ void stage_load(Stage& sg, PrefillIds& ids, const char* kbase,
+                                           const char* vbase, int k0, int kv_end,
+                                           size_t block_bytes, const uint32_t (&koff)[4],
+                                           const uint32_t (&voff)[4], int tid, int lane) {
+    const int kq = tid >> 4;
+    const bool upper = (tid >> 6) >= 2;  // wave-uniform: kq >= 8
     // ids of the tile's four 16-key groups, fetched in increasing order (the
     // window only moves forward)
     int id[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) id[i] = ids.get((k0 + 16 * i) / BS, lane);
-    // K: key k0 + kq + 16 i (group i)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int key = k0 + kq + 16 * i;
-        const size_t e = ((size_t)id[i] * BS + key % BS) * row_elems + (size_t)kvh * D + col * 8;
-        sg.k[i] = key < kv_end ? *reinterpret_cast<const uint4*>(kc + e) : make_uint4(0, 0, 0, 0);
+        const __amdgpu_buffer_rsrc_t r = buffer_rsrc(kbase + (size_t)id[i] * block_bytes);
+        const uint32_t o = k0 + kq + 16 * i < kv_end ? koff[i] : kBufferOob;
+        sg.k[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0));
     }
-    // V: keys k0 + 2 kq + p + 32 j (p = pair member, j = tile half): group
-    // 2 j when 2 kq + p < 16, else group 2 j + 1
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
+        const __amdgpu_buffer_rsrc_t r =
+            buffer_rsrc(vbase + (size_t)(upper ? id[2 * j + 1] : id[2 * j]) * block_bytes);
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            const int key = k0 + 2 * kq + p + 32 * j;
-            const int phys = (2 * kq + p) < 16 ? id[2 * j] : id[2 * j + 1];
-            const size_t e = ((size_t)phys * BS + key % BS) * row_elems + (size_t)kvh * D + col * 8;
-            sg.v[2 * j + p] = key < kv_end ? *reinterpret_cast<const uint4*>(vc + e)
-                                           : make_uint4(0, 0, 0, 0);
+            const uint32_t o = k0 + 2 * kq + p + 32 * j < kv_end ? voff[2 * j + p] : kBufferOob;
+            sg.v[2 * j + p] =
+                __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0));
         }
     }
 }
@@ -149,6 +173,52 @@ __device__ __forceinline__ void stage_store(const Stage& sg, uint16_t* __restric
                 pack_f16x2(bf16_hi(wa[w]), bf16_hi(wb[w]));
         }
     }
+}
+
+// Online-softmax step for one 64-key tile of this lane's query column:
+// scores s (raw, both 32-key halves; element e of half kb is key
+// k0 + 32 kb + 8 (e / 4) + 4 h + e % 4) -> P^T fragments (fp16) and the
+// updated running max / sum, with O rescaled when the max moved.  MASK
+// (diagonal or last tile only) drops keys after the column's position or
+// past the context.
+template <bool MASK>
+__device__ __forceinline__ void softmax_tile(f32x16_t (&s)[2], f16x8_t (&pf)[4], f32x16_t (&o)[4],
+                                             float& m_run, float& l_run, float cl2, int k0, int h,
+                                             int pos, int ctx, bool diag) {
+    float mt = -3.402823466e38f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            if (MASK) {
+                const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * h + (e & 3);
+                const bool ok = (!diag || key <= pos) && key < ctx;
+                s[kb][e] = ok ? s[kb][e] : -3.402823466e38f;
+            }
+            mt = fmaxf(mt, s[kb][e]);
+        }
+    mt = fmaxf(mt, xor_lane(mt, 32));
+    const float mn = fmaxf(m_run, mt * cl2);
+    const float alpha = fast_exp2(m_run - mn);
+    m_run = mn;
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[mb][e] *= alpha;
+    }
+    float lsum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            float p = fast_exp2(fmaf(s[kb][e], cl2, -mn));
+            // a dropped key must give 0 even for a zero scale
+            if (MASK) p = s[kb][e] == -3.402823466e38f ? 0.0f : p;
+            lsum += p;
+            pf[2 * kb + (e >> 3)][e & 7] = (_Float16)p;
+        }
+    l_run = fmaf(l_run, alpha, lsum);
 }
 
 // Grid: (num_q_tokens / (128 / G) + num_seqs, num_kv_heads); block 256.
@@ -231,13 +301,18 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
     float m_run = kNegBig;
     float l_run = 0.0f;
 
-    const size_t row_elems = (size_t)num_kv_heads * D;
+    const uint32_t row_bytes = (uint32_t)num_kv_heads * D * sizeof(uint16_t);
+    const size_t block_bytes = (size_t)BS * row_bytes;
+    const char* kbase = reinterpret_cast<const char*>(k_cache) + (size_t)kvh * D * sizeof(uint16_t);
+    const char* vbase = reinterpret_cast<const char*>(v_cache) + (size_t)kvh * D * sizeof(uint16_t);
+    uint32_t koff[4], voff[4];
+    stage_offsets<BS>(koff, voff, row_bytes, tid);
     PrefillIds ids;
     ids.init(block_table + (size_t)seq * max_blocks_per_seq, (ctx + BS - 1) / BS, lane);
 
     Stage sg;
     if (ntiles > 0) {
-        stage_load<BS>(sg, ids, k_cache, v_cache, 0, kv_end, row_elems, kvh, tid, lane);
+        stage_load<BS>(sg, ids, kbase, vbase, 0, kv_end, block_bytes, koff, voff, tid, lane);
         stage_store(sg, s_ks[0], s_vt[0], tid);
     }
     __syncthreads();
@@ -246,60 +321,32 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
         const int k0 = j * kKT;
         const int buf = j & 1;
         if (j + 1 < ntiles)
-            stage_load<BS>(sg, ids, k_cache, v_cache, k0 + kKT, kv_end, row_elems, kvh, tid, lane);
+            stage_load<BS>(sg, ids, kbase, vbase, k0 + kKT, kv_end, block_bytes, koff, voff, tid,
+                           lane);
 
-        // ---- S^T = K . Q^T for keys k0 .. k0 + 63 (two 32-key blocks)
+        // ---- S^T = K . Q^T for keys k0 .. k0 + 63 (two 32-key blocks); the
+        // first k-step adds to an inline zero
         f32x16_t s[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) s[kb][e] = 0.0f;
             const uint16_t* krow = s_ks[buf] + (32 * kb + (lane & 31)) * kKsStride + 8 * h;
+            const f32x16_t zero = {};
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
                 const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(krow + 16 * kk));
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], kk == 0 ? zero : s[kb], 0, 0, 0);
             }
         }
 
-        // ---- online softmax for this lane's column (keys of both halves)
-        // element e of block kb is key k0 + 32 kb + 8 (e / 4) + 4 h + e % 4
+        // ---- online softmax for this lane's column; only the tile that
+        // reaches the diagonal or the context's end needs masks
         const bool diag = causal ? (k0 + kKT - 1 > pos0 + r0) : false;
         const bool tail = k0 + kKT > ctx;
-        float mt = -3.402823466e38f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * h + (e & 3);
-                bool ok = true;
-                if (diag) ok = key <= pos;
-                if (tail) ok = ok && key < ctx;
-                s[kb][e] = ok ? s[kb][e] : -3.402823466e38f;
-                mt = fmaxf(mt, s[kb][e]);
-            }
-        mt = fmaxf(mt, xor_lane(mt, 32));
-        const float mn = fmaxf(m_run, mt * cl2);
-        const float alpha = fast_exp2(m_run - mn);
-        m_run = mn;
-        if (__any(alpha != 1.0f)) {
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) o[mb][e] *= alpha;
-        }
-        float lsum = 0.0f;
         f16x8_t pf[4];  // P^T fragments, k-step ks = keys 16 ks .. 16 ks + 15
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                float p = fast_exp2(fmaf(s[kb][e], cl2, -mn));
-                p = s[kb][e] == -3.402823466e38f ? 0.0f : p;
-                lsum += p;
-                pf[2 * kb + (e >> 3)][e & 7] = (_Float16)p;
-            }
-        l_run = fmaf(l_run, alpha, lsum);
+        if (diag || tail)
+            softmax_tile<true>(s, pf, o, m_run, l_run, cl2, k0, h, pos, ctx, diag);
+        else
+            softmax_tile<false>(s, pf, o, m_run, l_run, cl2, k0, h, pos, ctx, diag);
 
         // ---- O^T += V^T . P^T: A = V^T rows (dims), keys in accumulator order
 #pragma unroll
