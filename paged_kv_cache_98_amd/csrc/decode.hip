@@ -263,11 +263,13 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
                       float scale_log2, int num_workers, const int32_t* __restrict__ cu_q_lens) {
     constexpr int D = kHeadDim;
     extern __shared__ int32_t s_cum[];  // s_cum[i] = tiles (per KV head) of sequences < i
-    __shared__ int32_t s_part[64 * max_waves_per_worker<G>()];
+    __shared__ int32_t s_part[max_waves_per_worker<G>()];  // the waves' tile totals
     const int tid = threadIdx.x;
     const int nthr = blockDim.x;
 
-    // ---- prefix sums of per-sequence tile counts (two-level block scan)
+    // ---- prefix sums of per-sequence tile counts: each thread sums `per`
+    // consecutive sequences, each wave scans its 64 sums with lane
+    // shuffles, and one barrier passes the waves' totals around
     const int per = (num_seqs + nthr - 1) / nthr;
     int local = 0;
     for (int k = 0; k < per; ++k) {
@@ -275,15 +277,20 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
         if (i < num_seqs)
             local += tiles_of(context_lens, cu_q_lens, i, max_context_len);
     }
-    s_part[tid] = local;
-    __syncthreads();
-    for (int off = 1; off < nthr; off <<= 1) {
-        const int v = tid >= off ? s_part[tid - off] : 0;
-        __syncthreads();
-        s_part[tid] += v;
-        __syncthreads();
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if ((tid & 63) >= off) incl += y;
     }
-    int run = s_part[tid] - local;
+    if ((tid & 63) == 63) s_part[tid >> 6] = incl;
+    __syncthreads();
+    int run = incl - local, total = 0;
+    for (int k = 0; k < nthr / 64; ++k) {
+        const int t = s_part[k];
+        run += k < (tid >> 6) ? t : 0;
+        total += t;
+    }
     for (int k = 0; k < per; ++k) {
         const int i = tid * per + k;
         if (i < num_seqs) {
@@ -291,7 +298,7 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
             run += tiles_of(context_lens, cu_q_lens, i, max_context_len);
         }
     }
-    if (tid == nthr - 1) s_cum[num_seqs] = s_part[tid];
+    if (tid == 0) s_cum[num_seqs] = total;
     __syncthreads();
     if (blockIdx.x == 0 && blockIdx.y == 0)
         for (int i = tid; i <= num_seqs; i += nthr) cum_out[i] = s_cum[i];
