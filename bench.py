@@ -40,6 +40,30 @@ def attention_flops(w):
     return 4 * w.head_dim * w.num_q_heads * pairs
 
 
+def hbm_traffic(workload_name):
+    """HBM bytes per call (read + written) of the attention kernels, from the
+    rocprofv3 byte counters recorded in profiles/hbm_traffic.json, scaled by
+    the same counters' reading for a plain device copy; None when the
+    recorded kernel sources differ from the ones in this tree."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        wl = rec["workloads"][workload_name]
+        for src, digest in wl["sources_sha256"].items():
+            with open(os.path.join(ROOT, src), "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest() != digest:
+                    return None
+        cal = rec["calibration"]
+        fs = cal["copy_bytes_read"] / (cal["fetch_kib"] * 1024.0)
+        ws = cal["copy_bytes_written"] / (cal["write_kib"] * 1024.0)
+        return round(sum(k["fetch_kib"] * 1024.0 * fs + k["write_kib"] * 1024.0 * ws
+                         for k in wl["kernels"].values()))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def decode_kv_bytes(w):
     return sum(c for c, lq in zip(w.context_lens, w.q_lens) if lq == 1) * w.kv_token_bytes()
 
@@ -196,7 +220,8 @@ def main():
             "decode_rows_kv_gbs": round(dkv / (dec_avg * 1e-3) / 1e9, 1),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": hbm_traffic(w.name),
                          "kernel": "paged_prefill_attn (MFMA chunk kernel)",
                          "algorithmic_flops_per_launch": flops},
         }
@@ -227,7 +252,7 @@ def main():
                        "paged_decode_attn": round(dec_avg * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": hbm_traffic(w.name),
                      "kernel": "paged_decode_attn (stream-K decode + merge kernels)",
                      "algorithmic_bytes_per_launch": kv_bytes},
     }
