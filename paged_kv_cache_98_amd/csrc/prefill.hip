@@ -175,50 +175,49 @@ __device__ __forceinline__ void stage_store(const Stage& sg, uint16_t* __restric
     }
 }
 
-// Online-softmax step for one 64-key tile of this lane's query column:
-// scores s (raw, both 32-key halves; element e of half kb is key
-// k0 + 32 kb + 8 (e / 4) + 4 h + e % 4) -> P^T fragments (fp16) and the
-// updated running max / sum, with O rescaled when the max moved.  MASK
-// (diagonal or last tile only) drops keys after the column's position or
-// past the context.
+// Online-softmax step for one 32-key half tile of this lane's query column:
+// raw scores s (element e is key kb0 + 8 (e / 4) + 4 h + e % 4) -> P^T
+// fragments (fp16, k-steps of 16 keys) and the updated running max / sum,
+// with O rescaled.  MASK (diagonal or last tile only) drops keys after the
+// column's position or past the context.
 template <bool MASK>
-__device__ __forceinline__ void softmax_tile(f32x16_t (&s)[2], f16x8_t (&pf)[4], f32x16_t (&o)[4],
-                                             float& m_run, float& l_run, float cl2, int k0, int h,
+__device__ __forceinline__ void softmax_half(f32x16_t& s, f16x8_t (&pf)[2], f32x16_t (&o)[4],
+                                             float& m_run, float& l_run, float cl2, int kb0, int h,
                                              int pos, int ctx, bool diag) {
-    float mt = -3.402823466e38f;
+    // four independent partial maxima / sums, so neither is one long
+    // dependent chain
+    float mt4[4] = {-3.402823466e38f, -3.402823466e38f, -3.402823466e38f, -3.402823466e38f};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            if (MASK) {
-                const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * h + (e & 3);
-                const bool ok = (!diag || key <= pos) && key < ctx;
-                s[kb][e] = ok ? s[kb][e] : -3.402823466e38f;
-            }
-            mt = fmaxf(mt, s[kb][e]);
+    for (int e = 0; e < 16; ++e) {
+        if (MASK) {
+            const int key = kb0 + 8 * (e >> 2) + 4 * h + (e & 3);
+            const bool ok = (!diag || key <= pos) && key < ctx;
+            s[e] = ok ? s[e] : -3.402823466e38f;
         }
+        mt4[e & 3] = fmaxf(mt4[e & 3], s[e]);
+    }
+    float mt = fmaxf(fmaxf(mt4[0], mt4[1]), fmaxf(mt4[2], mt4[3]));
     mt = fmaxf(mt, xor_lane(mt, 32));
     const float mn = fmaxf(m_run, mt * cl2);
     const float alpha = fast_exp2(m_run - mn);
     m_run = mn;
-    if (__any(alpha != 1.0f)) {
+    // rescaled every time (a multiply by exactly 1 when the maximum did not
+    // move): a branch around it makes the compiler copy O between the two
+    // versions it then has
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) o[mb][e] *= alpha;
+        for (int e = 0; e < 16; ++e) o[mb][e] *= alpha;
+    float ls4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        float p = fast_exp2(fmaf(s[e], cl2, -mn));
+        // a dropped key must give 0 even for a zero scale
+        if (MASK) p = s[e] == -3.402823466e38f ? 0.0f : p;
+        ls4[e & 3] += p;
+        pf[e >> 3][e & 7] = (_Float16)p;
     }
-    float lsum = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            float p = fast_exp2(fmaf(s[kb][e], cl2, -mn));
-            // a dropped key must give 0 even for a zero scale
-            if (MASK) p = s[kb][e] == -3.402823466e38f ? 0.0f : p;
-            lsum += p;
-            pf[2 * kb + (e >> 3)][e & 7] = (_Float16)p;
-        }
-    l_run = fmaf(l_run, alpha, lsum);
+    l_run = fmaf(l_run, alpha, (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]));
 }
 
 // Grid: (num_q_tokens / (128 / G) + num_seqs, num_kv_heads); block 256.
@@ -324,40 +323,38 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
             stage_load<BS>(sg, ids, kbase, vbase, k0 + kKT, kv_end, block_bytes, koff, voff, tid,
                            lane);
 
-        // ---- S^T = K . Q^T for keys k0 .. k0 + 63 (two 32-key blocks); the
-        // first k-step adds to an inline zero
-        f32x16_t s[2];
+        // ---- the tile in two 32-key halves, each S^T = K . Q^T (the first
+        // k-step adds to an inline zero), online softmax, then
+        // O^T += V^T . P^T with A = V^T rows (dims) and the keys in
+        // accumulator order; only the tile that reaches the causal diagonal
+        // or the context's end needs masks
+        const bool masked = (causal && (k0 + kKT - 1 > pos0 + r0)) || k0 + kKT > ctx;
+        const bool diag = causal != 0;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+            f32x16_t sc;
             const uint16_t* krow = s_ks[buf] + (32 * kb + (lane & 31)) * kKsStride + 8 * h;
             const f32x16_t zero = {};
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
                 const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(krow + 16 * kk));
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], kk == 0 ? zero : s[kb], 0, 0, 0);
+                sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], kk == 0 ? zero : sc, 0, 0, 0);
             }
-        }
-
-        // ---- online softmax for this lane's column; only the tile that
-        // reaches the diagonal or the context's end needs masks
-        const bool diag = causal ? (k0 + kKT - 1 > pos0 + r0) : false;
-        const bool tail = k0 + kKT > ctx;
-        f16x8_t pf[4];  // P^T fragments, k-step ks = keys 16 ks .. 16 ks + 15
-        if (diag || tail)
-            softmax_tile<true>(s, pf, o, m_run, l_run, cl2, k0, h, pos, ctx, diag);
-        else
-            softmax_tile<false>(s, pf, o, m_run, l_run, cl2, k0, h, pos, ctx, diag);
-
-        // ---- O^T += V^T . P^T: A = V^T rows (dims), keys in accumulator order
+            f16x8_t pf[2];  // P^T fragments, keys 16 ks .. 16 ks + 15 of the half
+            if (masked)
+                softmax_half<true>(sc, pf, o, m_run, l_run, cl2, k0 + 32 * kb, h, pos, ctx, diag);
+            else
+                softmax_half<false>(sc, pf, o, m_run, l_run, cl2, k0 + 32 * kb, h, pos, ctx, diag);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+            for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                const uint16_t* vrow = s_vt[buf] + (32 * mb + (lane & 31)) * kVtStride + 16 * ks + 4 * h;
-                const uint2 lo4 = *reinterpret_cast<const uint2*>(vrow);
-                const uint2 hi4 = *reinterpret_cast<const uint2*>(vrow + 8);
-                const f16x8_t a = __builtin_bit_cast(f16x8_t, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
-                o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[ks], o[mb], 0, 0, 0);
+                for (int mb = 0; mb < 4; ++mb) {
+                    const uint16_t* vrow = s_vt[buf] + (32 * mb + (lane & 31)) * kVtStride + 32 * kb + 16 * ks + 4 * h;
+                    const uint2 lo4 = *reinterpret_cast<const uint2*>(vrow);
+                    const uint2 hi4 = *reinterpret_cast<const uint2*>(vrow + 8);
+                    const f16x8_t a = __builtin_bit_cast(f16x8_t, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
+                    o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[ks], o[mb], 0, 0, 0);
+                }
             }
         }
 
