@@ -390,6 +390,14 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
                 fetch(a, j + 2);
                 process_tile<G, false>(st, b, qv, c, row, kTileTokens);
                 fetch(b, j + 3);
+                // Eight waves stream their heads with nothing else tying them
+                // together, and two share each SIMD: left alone they drift
+                // tens of microseconds apart and the last ones finish alone,
+                // at half the loads in flight.  A barrier per tile pair keeps
+                // them in step (it waits for no load).  Four waves per
+                // workgroup, whose math is the tighter limit, do better
+                // without it.
+                if (max_waves_per_worker<G>() == 8) __syncthreads();
             }
             // two or three tiles left: j (in a), j + 1 (in b), maybe j + 2
             process_tile<G, false>(st, a, qv, c, row, kTileTokens);
