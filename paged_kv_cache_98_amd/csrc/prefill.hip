@@ -50,7 +50,13 @@ constexpr int kKT = 64;          // keys per K/V tile
 constexpr int kCols = 128;       // query columns per workgroup
 constexpr int kThreads = 256;    // 4 waves
 constexpr int kKsStride = D + 8;      // bf16 elements per K row in LDS (272 B)
-constexpr int kVtStride = kKT + 4;    // fp16 elements per V^T row in LDS (136 B)
+// V^T rows in LDS: 64 keys + 8 fp16 of padding (144 B), with the sixteen
+// 4-key groups of row d stored at group index g ^ vt_swizzle(d).  With
+// both, the staging stores (four bytes, two keys of one dim per lane) and
+// the MFMA operand reads (eight bytes, four keys per lane) each touch every
+// bank equally often.
+constexpr int kVtStride = kKT + 8;
+__device__ __forceinline__ int vt_swizzle(int d) { return (d >> 3) & 15; }
 constexpr int kKsElems = kKT * kKsStride;
 constexpr int kVtElems = D * kVtStride;
 
@@ -156,21 +162,23 @@ __device__ __forceinline__ void stage_store(const Stage& sg, uint16_t* __restric
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         *reinterpret_cast<uint4*>(ks + (kq + 16 * i) * kKsStride + col * 8) = sg.k[i];
-    // V^T[dim][key] as fp16 pairs of adjacent keys
+    // V^T[dim][key] as fp16 pairs of adjacent keys: keys 2 kq + 32 j and
+    // the next one are in group kq / 2 + 8 j at offset 2 (kq % 2); this
+    // thread's dims 8 col .. 8 col + 7 all have swizzle col, so the group
+    // lands at (kq / 2 ^ col) ^ 8 j
+    uint16_t* vcol = vt + col * 8 * kVtStride + 4 * ((kq / 2) ^ col) + 2 * (kq % 2);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const uint4 a = sg.v[2 * j];
         const uint4 b = sg.v[2 * j + 1];
         const uint32_t wa[4] = {a.x, a.y, a.z, a.w};
         const uint32_t wb[4] = {b.x, b.y, b.z, b.w};
-        const int key = 2 * kq + 32 * j;
+        // XOR with 8 j flips bit 3 of the group index: +-32 fp16
+        uint16_t* vj = vcol + (j == 0 ? 0 : (((kq / 2) ^ col) & 8 ? -32 : 32));
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            const int d0 = col * 8 + 2 * w;
-            *reinterpret_cast<uint32_t*>(vt + d0 * kVtStride + key) =
-                pack_f16x2(bf16_lo(wa[w]), bf16_lo(wb[w]));
-            *reinterpret_cast<uint32_t*>(vt + (d0 + 1) * kVtStride + key) =
-                pack_f16x2(bf16_hi(wa[w]), bf16_hi(wb[w]));
+            *reinterpret_cast<uint32_t*>(vj + (2 * w) * kVtStride) = pack_f16x2(bf16_lo(wa[w]), bf16_lo(wb[w]));
+            *reinterpret_cast<uint32_t*>(vj + (2 * w + 1) * kVtStride) = pack_f16x2(bf16_hi(wa[w]), bf16_hi(wb[w]));
         }
     }
 }
@@ -316,6 +324,9 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
     }
     __syncthreads();
 
+    // this lane's part of its V^T operand addresses (see the PV loop)
+    const int vt_lo = (lane & 31) * kVtStride + 4 * (h ^ ((lane & 31) >> 3));
+    const int vt_hi = (lane & 31) * kVtStride + 4 * ((h ^ ((lane & 31) >> 3)) ^ 2);
     for (int j = 0; j < ntiles; ++j) {
         const int k0 = j * kKT;
         const int buf = j & 1;
@@ -349,9 +360,15 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
             for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
                 for (int mb = 0; mb < 4; ++mb) {
-                    const uint16_t* vrow = s_vt[buf] + (32 * mb + (lane & 31)) * kVtStride + 32 * kb + 16 * ks + 4 * h;
-                    const uint2 lo4 = *reinterpret_cast<const uint2*>(vrow);
-                    const uint2 hi4 = *reinterpret_cast<const uint2*>(vrow + 8);
+                    // keys 16 ks + 4 h .. + 3 and 16 ks + 8 + 4 h .. + 3 of the
+                    // half are groups g = 8 kb + 4 ks + h and g + 2 of row
+                    // d = 32 mb + L, swizzle 4 mb + L / 8: the lane's part
+                    // (h ^ L / 8, and that ^ 2) is in vt_lo / vt_hi, the rest
+                    // is a constant offset
+                    const int cg = 4 * ((2 * kb + ks) ^ mb);
+                    const uint16_t* vrow = s_vt[buf] + 32 * mb * kVtStride + 4 * cg;
+                    const uint2 lo4 = *reinterpret_cast<const uint2*>(vrow + vt_lo);
+                    const uint2 hi4 = *reinterpret_cast<const uint2*>(vrow + vt_hi);
                     const f16x8_t a = __builtin_bit_cast(f16x8_t, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
                     o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[ks], o[mb], 0, 0, 0);
                 }
