@@ -33,6 +33,8 @@
 //   * K and V tiles of 64 keys are double-buffered in LDS: K as [key][dim]
 //     bf16, V transposed to [dim][key] fp16 while it is staged; the next
 //     tile's global loads are in flight while the current tile is computed.
+#include <type_traits>
+
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -327,20 +329,18 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
     // this lane's part of its V^T operand addresses (see the PV loop)
     const int vt_lo = (lane & 31) * kVtStride + 4 * (h ^ ((lane & 31) >> 3));
     const int vt_hi = (lane & 31) * kVtStride + 4 * ((h ^ ((lane & 31) >> 3)) ^ 2);
-    for (int j = 0; j < ntiles; ++j) {
+    // One 64-key tile: load the next tile (NEXT), the tile in two 32-key
+    // halves -- each S^T = K . Q^T (the first k-step adds to an inline zero),
+    // online softmax, then O^T += V^T . P^T with A = V^T rows (dims) and the
+    // keys in accumulator order -- then stage the next tile in LDS.
+    const bool diag = causal != 0;
+    auto run_tile = [&](int j, auto mask_c, bool next) {
+        constexpr bool MASK = decltype(mask_c)::value;
         const int k0 = j * kKT;
         const int buf = j & 1;
-        if (j + 1 < ntiles)
+        if (next)
             stage_load<BS>(sg, ids, kbase, vbase, k0 + kKT, kv_end, block_bytes, koff, voff, tid,
                            lane);
-
-        // ---- the tile in two 32-key halves, each S^T = K . Q^T (the first
-        // k-step adds to an inline zero), online softmax, then
-        // O^T += V^T . P^T with A = V^T rows (dims) and the keys in
-        // accumulator order; only the tile that reaches the causal diagonal
-        // or the context's end needs masks
-        const bool masked = (causal && (k0 + kKT - 1 > pos0 + r0)) || k0 + kKT > ctx;
-        const bool diag = causal != 0;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             f32x16_t sc;
@@ -352,10 +352,7 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
                 sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], kk == 0 ? zero : sc, 0, 0, 0);
             }
             f16x8_t pf[2];  // P^T fragments, keys 16 ks .. 16 ks + 15 of the half
-            if (masked)
-                softmax_half<true>(sc, pf, o, m_run, l_run, cl2, k0 + 32 * kb, h, pos, ctx, diag);
-            else
-                softmax_half<false>(sc, pf, o, m_run, l_run, cl2, k0 + 32 * kb, h, pos, ctx, diag);
+            softmax_half<MASK>(sc, pf, o, m_run, l_run, cl2, k0 + 32 * kb, h, pos, ctx, diag);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
@@ -374,10 +371,21 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
                 }
             }
         }
-
-        if (j + 1 < ntiles) stage_store(sg, s_ks[buf ^ 1], s_vt[buf ^ 1], tid);
+        if (next) stage_store(sg, s_ks[buf ^ 1], s_vt[buf ^ 1], tid);
         __syncthreads();
-    }
+    };
+    // Only tiles that reach the causal diagonal (k0 + 63 > pos0 + r0) or the
+    // context's end (k0 + 64 > ctx) need masks; they are the last ones.  The
+    // tiles before them, all with a next tile, run in a loop of their own with
+    // no branch in its body.
+    const int first_pos = pos0 + r0;
+    const int j_diag = causal ? (first_pos >= kKT - 1 ? (first_pos - (kKT - 1)) / kKT + 1 : 0) : ntiles;
+    const int j_tail = ctx >= kKT ? (ctx - kKT) / kKT + 1 : 0;
+    int j_plain = j_diag < j_tail ? j_diag : j_tail;
+    j_plain = j_plain < ntiles - 1 ? j_plain : ntiles - 1;
+    int j = 0;
+    for (; j < j_plain; ++j) run_tile(j, std::false_type{}, true);
+    for (; j < ntiles; ++j) run_tile(j, std::true_type{}, j + 1 < ntiles);
 
     // ---- finish: total l over both halves, then out = O / l
     const float lt = l_run + xor_lane(l_run, 32);
