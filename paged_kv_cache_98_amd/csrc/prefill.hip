@@ -190,6 +190,8 @@ __device__ __forceinline__ void stage_store(const Stage& sg, uint16_t* __restric
 // fragments (fp16, k-steps of 16 keys) and the updated running max / sum,
 // with O rescaled.  MASK (diagonal or last tile only) drops keys after the
 // column's position or past the context.
+constexpr float kLazyMax = 8.0f;  // p < 2^8 between rescales
+
 template <bool MASK>
 __device__ __forceinline__ void softmax_half(f32x16_t& s, f16x8_t (&pf)[2], f32x16_t (&o)[4],
                                              float& m_run, float& l_run, float cl2, int kb0, int h,
@@ -207,17 +209,22 @@ __device__ __forceinline__ void softmax_half(f32x16_t& s, f16x8_t (&pf)[2], f32x
         mt4[e & 3] = fmaxf(mt4[e & 3], s[e]);
     }
     float mt = fmaxf(fmaxf(mt4[0], mt4[1]), fmaxf(mt4[2], mt4[3]));
-    mt = fmaxf(mt, xor_lane(mt, 32));
-    const float mn = fmaxf(m_run, mt * cl2);
-    const float alpha = fast_exp2(m_run - mn);
-    m_run = mn;
-    // rescaled every time (a multiply by exactly 1 when the maximum did not
-    // move): a branch around it makes the compiler copy O between the two
-    // versions it then has
+    mt = fmaxf(mt, xor_lane(mt, 32)) * cl2;
+    // Lazy reference maximum: m_run moves only when a score exceeds it by
+    // more than kLazyMax (log2 units), so p = 2^(s - m_run) stays below
+    // 2^kLazyMax (far inside fp16) and O and l are rescaled only on those
+    // rare jumps; softmax does not depend on which reference is used.
+    float alpha = 1.0f;
+    if (__any(mt > m_run + kLazyMax)) {
+        const float mn = mt > m_run + kLazyMax ? mt : m_run;
+        alpha = fast_exp2(m_run - mn);
+        m_run = mn;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) o[mb][e] *= alpha;
+            for (int e = 0; e < 16; ++e) o[mb][e] *= alpha;
+    }
+    const float mn = m_run;
     float ls4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
