@@ -348,18 +348,24 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
         if (next)
             stage_load<BS>(sg, ids, kbase, vbase, k0 + kKT, kv_end, block_bytes, koff, voff, tid,
                            lane);
+        // S for both halves first, so that each half's softmax (VALU) has
+        // matrix-core work in flight beside it: the second half's S during
+        // the first softmax, the first half's P V during the second
+        f32x16_t sc[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            f32x16_t sc;
             const uint16_t* krow = s_ks[buf] + (32 * kb + (lane & 31)) * kKsStride + 8 * h;
             const f32x16_t zero = {};
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
                 const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(krow + 16 * kk));
-                sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], kk == 0 ? zero : sc, 0, 0, 0);
+                sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], kk == 0 ? zero : sc[kb], 0, 0, 0);
             }
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
             f16x8_t pf[2];  // P^T fragments, keys 16 ks .. 16 ks + 15 of the half
-            softmax_half<MASK>(sc, pf, o, m_run, l_run, cl2, k0 + 32 * kb, h, pos, ctx, diag);
+            softmax_half<MASK>(sc[kb], pf, o, m_run, l_run, cl2, k0 + 32 * kb, h, pos, ctx, diag);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
