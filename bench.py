@@ -121,7 +121,7 @@ def main():
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
+        print(f"bench.py: the benchmark runs on exactly one GPU; --gpus {args.gpus} is not "
               "supported (decode shards by sequence or KV head with no exchange, see the "
               "design notes)", file=sys.stderr)
         sys.exit(2)
