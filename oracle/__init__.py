@@ -11,7 +11,9 @@ Contents
   * ``online``: fp64 replicas of the single-pass online-softmax recurrence and
     of the log-sum-exp merge of partition summaries.
   * ``sizing``: the pages' KV-cache and block-memory formulas.
-  * ``blocks``: the pages' toy block pool (allocate / free / refcount).
+  * ``blocks``: the pages' block pool (allocate / free / fork / append with
+    copy-on-write, reference counts) and the whole-block copy of
+    copy-on-write.
 
 Every function names the passage it follows.  Functions without an
 independent pin say "parity unpinned" in their docstring (none at present).

@@ -1,0 +1,191 @@
+"""The oracle's block pool and whole-block copy pinned to what the pages fix:
+block counts and waste, on-demand growth, the pool sketch's order of blocks,
+release, sharing under reference counts and copy-on-write."""
+import random
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.blocks import BlockPool, copy_blocks as oracle_copy_blocks
+
+
+# ---------------------------------------------------------------- oracle pins
+
+def smallest_blocks(n, bs):
+    """Brute force: the fewest bs-token blocks that hold n tokens."""
+    k = 0
+    while k * bs < n:
+        k += 1
+    return k
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_pin_blocks_and_waste(bs):
+    """A sequence holds the fewest blocks that fit it, and wastes at most
+    block_size - 1 slots: 15 for 16-token blocks ("让 Agent 跑得快", sections
+    二 and 五)."""
+    pool = BlockPool(10_000, bs)
+    worst = 0
+    for n in range(0, 6 * bs + 3):
+        pool.allocate(n, n)
+        held = len(pool.tables[n])
+        assert held == smallest_blocks(n, bs)
+        waste = held * bs - n
+        assert 0 <= waste <= bs - 1
+        worst = max(worst, waste)
+    assert worst == bs - 1
+    pool.check()
+
+
+def test_pin_on_demand_growth():
+    """One more block each time 16 tokens have filled the last one
+    ("让 Agent 跑得快", section 五, allocation flow)."""
+    pool = BlockPool(64, 16)
+    pool.allocate("s", 0)
+    taken_at = []
+    for tok in range(1, 100):
+        before = pool.num_free()
+        slots, copies = pool.append("s", 1)
+        assert copies == []
+        if pool.num_free() != before:
+            assert before - pool.num_free() == 1
+            taken_at.append(tok)
+    assert taken_at == [1, 17, 33, 49, 65, 81, 97]
+    pool.check()
+
+
+def test_pin_pool_sketch_worked_example():
+    """The pool sketch of "LLM 推理引擎深度解析", section 2.1, run by hand on a
+    10-block pool: blocks come off the front of the free list and go back at
+    its end; too few free blocks raise MemoryError; freeing an unknown id
+    does nothing."""
+    pool = BlockPool(10, 16)
+    assert pool.allocate("A", 50) == [0, 1, 2, 3]          # ceil(50/16) = 4
+    with pytest.raises(MemoryError):
+        pool.allocate("B", 100)                            # needs 7, 6 free
+    assert list(pool.free_list) == [4, 5, 6, 7, 8, 9]      # nothing taken
+    pool.free("A")
+    assert list(pool.free_list) == [4, 5, 6, 7, 8, 9, 0, 1, 2, 3]
+    assert pool.allocate("B", 100) == [4, 5, 6, 7, 8, 9, 0]
+    pool.free("nobody")
+    assert list(pool.free_list) == [1, 2, 3]
+    pool.check()
+
+
+def test_pin_freed_blocks_reusable():
+    """A finished request's blocks are at once usable by any other request
+    ("让 Agent 跑得快", section 五, release flow)."""
+    pool = BlockPool(8, 16)
+    pool.allocate(1, 8 * 16)
+    with pytest.raises(MemoryError):
+        pool.allocate(2, 1)
+    pool.free(1)
+    assert sorted(pool.allocate(2, 8 * 16)) == list(range(8))
+
+
+def test_pin_shared_system_prompt():
+    """50 requests sharing one 5000-token system prompt hold one physical copy
+    of it ("让 Agent 跑得快", section 五, shared prefix).  Reading: a shared,
+    partly filled last block (5000 = 312 x 16 + 8) is copied on each request's
+    first write (section 二, Copy-on-Write), except by the last holder."""
+    pool = BlockPool(1000, 16)
+    prompt = pool.allocate("prompt", 5000)
+    assert len(prompt) == 313
+    for r in range(50):
+        pool.fork("prompt", r)
+    assert pool.num_free() == 1000 - 313                    # one physical copy
+    assert all(pool.refcount[b] == 51 for b in prompt)
+    pool.free("prompt")
+    assert all(pool.refcount[b] == 50 for b in prompt)
+    n_copies = 0
+    for r in range(50):
+        slots, copies = pool.append(r, 1)
+        n_copies += len(copies)
+        assert pool.tables[r][:312] == prompt[:312]         # full blocks stay shared
+        assert slots == [pool.tables[r][312] * 16 + 8]
+        if copies:
+            assert copies == [(prompt[312], pool.tables[r][312])]
+    assert n_copies == 49                                   # the last holder writes in place
+    assert pool.tables[49][312] == prompt[312]
+    assert pool.num_free() == 1000 - 313 - 49
+    pool.check()
+
+
+def test_pin_copy_on_write_fork():
+    """Forked sequences share blocks; the writer gets a private copy, the other
+    keeps the original; a full shared last block is never copied: the next
+    token opens a fresh block ("让 Agent 跑得快", section 二, Copy-on-Write)."""
+    pool = BlockPool(16, 16)
+    pool.allocate("p", 20)                                   # blocks 0, 1 (4 tokens in 1)
+    pool.fork("p", "c")
+    slots, copies = pool.append("c", 3)
+    assert copies == [(1, 2)]
+    assert pool.tables["c"] == [0, 2] and pool.tables["p"] == [0, 1]
+    assert slots == [2 * 16 + 4, 2 * 16 + 5, 2 * 16 + 6]
+    assert pool.refcount[:3] == [2, 1, 1]
+    # a shared FULL last block: the parent fills block 1, forks, and both write
+    pool.append("p", 12)                                     # block 1 now full (32 tokens)
+    pool.fork("p", "d")
+    s1, c1 = pool.append("d", 1)
+    s2, c2 = pool.append("p", 1)
+    assert c1 == [] and c2 == []
+    assert s1 == [3 * 16] and s2 == [4 * 16]
+    assert pool.tables["d"][:2] == pool.tables["p"][:2] == [0, 1]
+    pool.check()
+
+
+def test_pin_all_or_nothing():
+    """An append that needs a copy and a new block, with one free block, fails
+    and changes nothing (reading: a call that cannot finish changes nothing)."""
+    pool = BlockPool(3, 16)
+    pool.allocate("p", 20)                                   # blocks 0, 1
+    pool.fork("p", "c")
+    snap = (list(pool.free_list), list(pool.refcount), {k: list(v) for k, v in pool.tables.items()},
+            dict(pool.lengths))
+    with pytest.raises(MemoryError):
+        pool.append("c", 13)                                 # copy of block 1 + a new block
+    assert snap == (list(pool.free_list), list(pool.refcount),
+                    {k: list(v) for k, v in pool.tables.items()}, dict(pool.lengths))
+    slots, copies = pool.append("c", 12)                     # the copy alone fits
+    assert copies == [(1, 2)] and len(slots) == 12
+    pool.check()
+
+
+def test_pin_slots_reach_every_token_once():
+    """Slots of all sequences' tokens are distinct, lie in the sequence's own
+    blocks at row position % block_size, and agree with the block table."""
+    rng = random.Random(5)
+    pool = BlockPool(200, 16)
+    owner = {}
+    for s in range(12):
+        pool.allocate(s, 0)
+        for _ in range(rng.randrange(1, 6)):
+            slots, copies = pool.append(s, rng.randrange(0, 40))
+            assert copies == []
+            for sl in slots:
+                assert sl not in owner
+                owner[sl] = s
+    for s in range(12):
+        n = pool.lengths[s]
+        for pos in range(n):
+            sl = pool.tables[s][pos // 16] * 16 + pos % 16
+            assert owner[sl] == s
+    pool.check()
+
+
+def test_pin_copy_blocks_matches_append():
+    """The whole-block copy equals re-appending the source block's rows into
+    the destination's slots through the fp64 oracle's own kv_append."""
+    rng = np.random.default_rng(7)
+    nb, bs, hkv, d = 12, 16, 2, 128
+    k = rng.integers(0, 1 << 16, size=(nb, bs, hkv, d), dtype=np.uint16)
+    v = rng.integers(0, 1 << 16, size=(nb, bs, hkv, d), dtype=np.uint16)
+    pairs = [(3, 7), (0, 11), (5, 2), (-1, 4), (6, 12)]      # the last two name no block
+    ko, vo = oracle_copy_blocks(k, v, pairs)
+    slots = np.concatenate([dst * bs + np.arange(bs) for _, dst in pairs[:3]]).astype(np.int64)
+    k_rows = np.concatenate([k[src] for src, _ in pairs[:3]])
+    v_rows = np.concatenate([v[src] for src, _ in pairs[:3]])
+    ka, va = oracle.kv_append(k_rows, v_rows, slots, k, v)
+    assert np.array_equal(ko, ka) and np.array_equal(vo, va)
+    assert np.array_equal(ko[4], k[4]) and np.array_equal(ko[7], k[3])
