@@ -67,8 +67,181 @@ def hbm_traffic(workload_name):
         return None
 
 
+# What each recorded workload's traffic covers: the kernels whose counters are
+# summed per call, the sources they are built from (a change to any of them
+# voids the record), and the bench.py arguments the counters are taken on.
+TRAFFIC_SPEC = {
+    "llama8b_decode_b64": {"kernels": ["decode_streamk_kernel", "decode_merge_kernel"],
+                           "sources": ["paged_kv_cache_98_amd/csrc/decode.hip",
+                                       "paged_kv_cache_98_amd/csrc/pkv_device.h"],
+                           "args": ""},
+    "mixed_prefill_c4x512_d0": {"kernels": ["prefill_mfma_kernel"],
+                                "sources": ["paged_kv_cache_98_amd/csrc/prefill.hip",
+                                            "paged_kv_cache_98_amd/csrc/pkv_device.h"],
+                                "args": "--workload prefill_chunks"},
+    "cow_copy_4096x32k": {"kernels": ["copy_blocks_kernel"],
+                          "sources": ["paged_kv_cache_98_amd/csrc/kv_append.hip"],
+                          "args": "--workload cow_copy"},
+}
+
+
+def _pmc_per_dispatch(run_dir, kernel_substrings):
+    """Mean per-dispatch counter value (KiB) of each matching kernel in a
+    rocprofv3 --pmc CSV output directory."""
+    import collections
+    import csv
+    import glob
+    import re
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"]
+                if not any(k in name for k in kernel_substrings):
+                    continue
+                m = re.search(r"(\w+_kernel(<[^>]*>)?)", name)
+                per[m.group(1) if m else name][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {k: sum(d.values()) / len(d) for k, d in per.items() if d}
+
+
+def record_traffic(workload, fetch_dir, write_dir):
+    """Write workload's entry of profiles/hbm_traffic.json from a FETCH_SIZE and
+    a WRITE_SIZE run (``calibration`` takes the plain-copy runs instead)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    with open(path) as f:
+        rec = json.load(f)
+    if workload == "calibration":
+        fetch = _pmc_per_dispatch(fetch_dir, ["__amd_rocclr_copyBuffer"])
+        write = _pmc_per_dispatch(write_dir, ["__amd_rocclr_copyBuffer"])
+        (fk,), (wk,) = fetch.values(), write.values()
+        rec["calibration"].update({"fetch_kib": round(fk, 1), "write_kib": round(wk, 1)})
+    else:
+        spec = TRAFFIC_SPEC[workload]
+        fetch = _pmc_per_dispatch(fetch_dir, spec["kernels"])
+        write = _pmc_per_dispatch(write_dir, spec["kernels"])
+        if not fetch or set(fetch) != set(write):
+            raise SystemExit(f"counter runs disagree on kernels: {sorted(fetch)} vs {sorted(write)}")
+        digests = {}
+        for src in spec["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                digests[src] = hashlib.sha256(f.read()).hexdigest()
+        rec["workloads"][workload] = {
+            "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d <dir> "
+                       "-o p -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline "
+                       + spec["args"],
+            "sources_sha256": digests,
+            "kernels": {k: {"fetch_kib": round(fetch[k], 1), "write_kib": round(write[k], 1)}
+                        for k in sorted(fetch)},
+        }
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec["workloads"].get(workload, rec["calibration"]), indent=1))
+
+
 def decode_kv_bytes(w):
     return sum(c for c, lq in zip(w.context_lens, w.q_lens) if lq == 1) * w.kv_token_bytes()
+
+
+COPY_WORKLOAD = "cow_copy_4096x32k"
+
+
+def bench_copy_blocks(args):
+    """copy_blocks on its own: 4096 (source, destination) pairs of
+    Llama-3.1-8B-shaped blocks (16 tokens x 8 KV heads x 128 x bf16 = 32 KiB
+    of K and as much of V) in a 16384-block pool (0.5 GiB per pool, so the
+    copies stream from HBM), destinations distinct and never a source.  Bytes
+    per pair: K and V blocks each read once and written once = 128 KiB.
+    Also times the native block manager on the host: one decode step of 256
+    beams (64 prompts x 4 beams, forked after a 1000-token prompt) = one
+    batched append of a token per beam (returning slots and copies) and the
+    block table of all beams, both through the Python binding."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_98_amd import binding as pkv
+
+    nb, bs, hkv, d, npairs = 16384, 16, 8, 128, 4096
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = torch.Generator(device=dev).manual_seed(2024)
+    k = torch.randn((nb, bs, hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn((nb, bs, hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    rng = np.random.default_rng(2025)
+    perm = rng.permutation(nb)
+    pairs_np = np.stack([rng.choice(perm[npairs:], size=npairs), perm[:npairs]], 1).astype(np.int64)
+    pairs = torch.from_numpy(pairs_np).to(dev)
+    stream = torch.cuda.current_stream()
+    block_bytes = bs * hkv * d * 2
+    bytes_per_call = npairs * 4 * block_bytes
+    for _ in range(args.warmup):
+        pkv.copy_blocks(k, v, pairs, stream=stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        pkv.copy_blocks(k, v, pairs, stream=stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in evs:
+        e[0].record(stream)
+        pkv.copy_blocks(k, v, pairs, stream=stream)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    call_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in evs)
+    achieved = bytes_per_call / (call_ms * 1e-3) / 1e9
+
+    # host manager: 64 prompts x 4 beams, 6 decode steps timed
+    with pkv.BlockManager(64 * 4 * 80, bs) as bm:
+        beams = []
+        for p in range(64):
+            bm.allocate(p * 10, 1000)
+            for j in range(1, 5):
+                bm.fork(p * 10, p * 10 + j)
+                beams.append(p * 10 + j)
+            bm.free(p * 10)
+        host_us = []
+        beams = torch.tensor(beams, dtype=torch.int64)
+        ones = torch.ones(len(beams), dtype=torch.int64)
+        for _ in range(6):
+            t1 = time.perf_counter()
+            bm.append_batch(beams, ones)
+            bm.block_table(beams, 80)
+            host_us.append((time.perf_counter() - t1) * 1e6)
+    print(f"[bench] copy_blocks {call_ms * 1e3:.1f} us per call of {npairs} pairs: "
+          f"{achieved:.0f} GB/s | host manager {statistics.median(host_us):.0f} us per "
+          f"256-beam step", file=sys.stderr, flush=True)
+    rec = {
+        "metric": "copy_blocks (copy-on-write block copies): HBM GB/s",
+        "value": round(bytes_per_call / (ms_per_step * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": COPY_WORKLOAD, "num_pairs": npairs, "num_blocks": nb,
+                   "block_size": bs, "num_kv_heads": hkv, "head_dim": d},
+        "kernels_us": {"copy_blocks": round(call_ms * 1e3, 2)},
+        "host_block_manager_us_per_256_beam_step": round(statistics.median(host_us), 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": hbm_traffic(COPY_WORKLOAD),
+                     "kernel": "copy_blocks", "algorithmic_bytes_per_launch": bytes_per_call},
+    }
+    if not args.no_cpu_baseline:
+        from oracle.blocks import copy_blocks as oracle_copy_blocks
+        sample = 512
+        kc = k[:nb // 4].view(torch.int16).cpu().numpy()
+        vc = v[:nb // 4].view(torch.int16).cpu().numpy()
+        sp = pairs_np[(pairs_np < nb // 4).all(1)][:sample]
+        t2 = time.perf_counter()
+        oracle_copy_blocks(kc, vc, sp.tolist())
+        dt = time.perf_counter() - t2
+        rec["cpu_baseline"] = {
+            "value": round(len(sp) * 4 * block_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{len(sp)} pairs of the same mapping inside a {nb // 4}-block host copy "
+                      f"of the pools (numpy, one thread): {dt * 1e3:.1f} ms including its "
+                      f"copy of both pools"}
+    print(json.dumps(rec), flush=True)
 
 
 def workload_by_name(name):
@@ -119,7 +292,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
+    ap.add_argument("--record-traffic", nargs=3, metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR"),
+                    help="no benchmark: record WORKLOAD's HBM bytes (or 'calibration') in "
+                         "profiles/hbm_traffic.json from rocprofv3 FETCH_SIZE / WRITE_SIZE runs")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py: the benchmark runs on exactly one GPU; --gpus {args.gpus} is not "
               "supported (decode shards by sequence or KV head with no exchange, see the "
@@ -140,6 +319,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_per_dispatch": src.numel() * 2}), flush=True)
+        return
+
+    if args.workload in ("cow_copy", COPY_WORKLOAD):
+        bench_copy_blocks(args)
         return
 
     dev = torch.device("cuda:0")

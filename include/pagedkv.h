@@ -17,12 +17,13 @@
  *    in its "Flash Attention v2 的改进"), and "Chunked Prefill" (prompts
  *    processed in equal chunks, decodes batched with them).
  *
- * Conventions shared by every call
+ * Conventions shared by every device call (the block manager at the end of
+ * this header is host-only and has its own)
  *  - Every array argument is a DEVICE pointer, allocated and owned by the
  *    caller, who keeps it alive until the enqueued work has finished.  The
- *    library allocates nothing, frees nothing and keeps no state between
- *    calls; concurrent calls on different streams are safe when their output
- *    buffers (and workspaces) do not overlap.
+ *    library allocates no device memory, frees nothing and keeps no state
+ *    between calls; concurrent calls on different streams are safe when their
+ *    output buffers (and workspaces) do not overlap.
  *  - `stream` is a hipStream_t (NULL = the null stream).  All work is
  *    enqueued asynchronously on it; no call synchronises.
  *  - Element types: K/V pools, q, k_new, v_new are bf16; block tables,
@@ -69,7 +70,10 @@ enum pkv_status {
     PKV_ERR_UNSUPPORTED = -3, /* head_dim, block_size, group size or dtype not built */
     PKV_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
     PKV_ERR_LAUNCH = -5,      /* the HIP runtime reported an error at launch */
-    PKV_ERR_ALIGN = -6        /* a bf16 array is not 16-byte aligned */
+    PKV_ERR_ALIGN = -6,       /* a bf16 array is not 16-byte aligned */
+    PKV_ERR_NO_MEMORY = -7,   /* block manager: too few free blocks; nothing changed */
+    PKV_ERR_STATE = -8,       /* block manager: unknown or already existing sequence id */
+    PKV_ERR_HOST_ALLOC = -9   /* block manager: host memory ran out; nothing changed */
 };
 
 enum pkv_out_dtype {
@@ -184,6 +188,134 @@ int pkv_paged_prefill_attn(void *out, int out_dtype, const void *q, const int32_
                            int num_q_tokens, int num_seqs, int num_q_heads, int num_kv_heads,
                            int head_dim, int block_size, float scale, int causal,
                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * copy_blocks -- whole-block copies inside the pools, the device half of
+ * copy-on-write ("让 Agent 跑得快：LLM 推理服务", section 二, "Copy-on-Write":
+ * a shared block is copied only when a sequence must write into it, and that
+ * sequence's table entry then points at the copy).
+ *
+ *   k_cache, v_cache  pools [num_blocks][block_size][num_kv_heads][head_dim]
+ *                  bf16 (read at the sources, written at the destinations)
+ *   block_mapping  [num_pairs][2] int64 DEVICE array of (source, destination)
+ *                  physical block ids, as pkv_bm_append returns them; every
+ *                  row of block `source` (all heads, K and V) is copied to
+ *                  block `destination`, bit for bit.  A pair with an id
+ *                  outside [0, num_blocks) is skipped on the device.
+ *                  Destinations must be distinct and no destination may be
+ *                  the source of another pair of the same call (the copies
+ *                  run in no particular order).
+ * num_pairs == 0 is a no-op.  Pools 16-byte aligned.
+ */
+int pkv_copy_blocks(void *k_cache, void *v_cache, int64_t num_blocks, int block_size,
+                    int num_kv_heads, int head_dim, const int64_t *block_mapping,
+                    int64_t num_pairs, void *stream);
+
+/*
+ * Block manager -- the host-side bookkeeping that produces block tables and
+ * slot mappings.  ("LLM 推理引擎深度解析：vLLM、SGLang 与 TensorRT-LLM 的核心
+ * 优化原理", section 2.1 "PagedAttention": a pool of fixed-size physical
+ * blocks with a free list, a sequence of n tokens holding ceil(n /
+ * block_size) not necessarily contiguous blocks, allocation failing when too
+ * few are free, freeing returning a sequence's blocks; "让 Agent 跑得快：LLM
+ * 推理服务", section 五: blocks taken on demand, one more whenever the last
+ * is full, so at most block_size - 1 slots per sequence unused, and block
+ * tables sharing physical blocks under a reference count; same page,
+ * section 二, "Copy-on-Write": forked sequences share blocks and a shared
+ * block is copied before a write.)
+ *
+ * Conventions of the pkv_bm_* calls
+ *  - They run on the host only and touch no GPU; every array argument is a
+ *    HOST pointer owned by the caller.  The manager owns its host memory
+ *    until pkv_bm_destroy.  One manager must not be used from two threads at
+ *    once; different managers are independent.
+ *  - Physical block ids are 0 ... num_blocks - 1.  Blocks leave the front of
+ *    the free list and return to its back when their count drops to zero.
+ *  - Sequence ids are any int64 values chosen by the caller.
+ *  - A call that fails returns a negative status and changes nothing
+ *    (in particular PKV_ERR_NO_MEMORY leaves every table and count as it was).
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+
+/* A manager of num_blocks (0 ... 2^31 - 1) blocks of block_size token rows,
+ * all free; NULL on bad sizes or when host memory runs out. */
+pkv_block_manager *pkv_bm_create(int64_t num_blocks, int block_size);
+
+/* Release the manager (NULL is a no-op). */
+void pkv_bm_destroy(pkv_block_manager *bm);
+
+/* Free blocks, or -1 for a NULL manager. */
+int64_t pkv_bm_num_free(const pkv_block_manager *bm);
+
+/* New sequence seq_id holding num_tokens (>= 0) tokens: takes
+ * ceil(num_tokens / block_size) blocks.  PKV_ERR_STATE if seq_id exists,
+ * PKV_ERR_NO_MEMORY if too few blocks are free. */
+int pkv_bm_allocate(pkv_block_manager *bm, int64_t seq_id, int64_t num_tokens);
+
+/* Drop seq_id; each of its blocks loses one reference and returns to the free
+ * list at zero.  An unknown seq_id is ignored (PKV_OK). */
+int pkv_bm_free(pkv_block_manager *bm, int64_t seq_id);
+
+/* New sequence child with parent's tokens and blocks, every block gaining a
+ * reference (nothing is copied).  PKV_ERR_STATE if parent is unknown or
+ * child exists. */
+int pkv_bm_fork(pkv_block_manager *bm, int64_t parent, int64_t child);
+
+/*
+ * Room for num_tokens (>= 0) more tokens of seq_id.
+ *   slots        [num_tokens] int64 (written): the slot of each new token in
+ *                order, slot = block * block_size + position % block_size,
+ *                ready for pkv_kv_append's slot_mapping
+ *   copies       [max_copies][2] int64 (written): (source, destination)
+ *                blocks to copy with pkv_copy_blocks BEFORE the new tokens
+ *                are written; may be NULL when max_copies is 0
+ *   num_copies   (written) copies produced: 0, or 1 when the sequence's
+ *                partly filled last block is shared (its count is above 1):
+ *                the copy takes a fresh block, the table entry moves to it
+ *                and the old block loses a reference.  A token that opens a
+ *                new block takes a fresh private block and never copies.
+ * PKV_ERR_NO_MEMORY if the copy and the new blocks need more than the free
+ * list holds; PKV_ERR_SHAPE if a copy is needed and max_copies < 1.
+ */
+int pkv_bm_append(pkv_block_manager *bm, int64_t seq_id, int64_t num_tokens, int64_t *slots,
+                  int64_t *copies, int64_t max_copies, int64_t *num_copies);
+
+/*
+ * pkv_bm_append for a whole batch in one call: sequence seq_ids[i] gets
+ * num_tokens[i] (>= 0) more tokens, in order (an id may repeat).
+ *   slots        [sum num_tokens] int64 (written): the batch's slots, entry
+ *                by entry, each entry's in token order
+ *   copies       [max_copies][2] int64 (written): the copies of all entries
+ *                in order (at most one per entry, so num_seqs rows always
+ *                suffice); may be NULL when max_copies is 0
+ *   num_copies   (written) rows of copies used
+ * All or nothing: if any entry fails (unknown id PKV_ERR_STATE, too few
+ * blocks PKV_ERR_NO_MEMORY, copies full PKV_ERR_SHAPE) the entries before
+ * it are undone, the free list included, and nothing has changed.
+ */
+int pkv_bm_append_batch(pkv_block_manager *bm, const int64_t *seq_ids, const int64_t *num_tokens,
+                        int num_seqs, int64_t *slots, int64_t *copies, int64_t max_copies,
+                        int64_t *num_copies);
+
+/* Tokens and blocks held by seq_id (PKV_ERR_STATE if unknown). */
+int pkv_bm_seq_info(const pkv_block_manager *bm, int64_t seq_id, int64_t *num_tokens,
+                    int64_t *num_blocks);
+
+/* Reference count of one block (0 = free); PKV_ERR_SHAPE if out of range. */
+int pkv_bm_refcount(const pkv_block_manager *bm, int64_t block, int32_t *count);
+
+/*
+ * Block table and context lengths of num_seqs sequences, in the layout the
+ * attention calls read.
+ *   seq_ids       [num_seqs] int64
+ *   table         [num_seqs][max_blocks_per_seq] int32 (written): row i holds
+ *                 seq_ids[i]'s blocks in logical order, then -1
+ *   context_lens  [num_seqs] int32 (written): tokens held
+ * PKV_ERR_STATE for an unknown id, PKV_ERR_SHAPE if a sequence holds more
+ * than max_blocks_per_seq blocks; nothing is written then.
+ */
+int pkv_bm_block_table(const pkv_block_manager *bm, const int64_t *seq_ids, int num_seqs,
+                       int32_t *table, int max_blocks_per_seq, int32_t *context_lens);
 
 #ifdef __cplusplus
 }

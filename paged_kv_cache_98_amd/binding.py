@@ -1,10 +1,12 @@
 """ctypes binding of libpagedkv.so: argument marshalling only.
 
-Every function takes torch tensors that already live on the GPU, passes
-their device pointers and sizes to the C ABI (include/pagedkv.h) on torch's
-current stream, and turns a negative status into an exception.  All
-arithmetic happens in the HIP kernels; there is no CPU fallback: without the
-built library, or with CPU tensors, these functions raise.
+Every attention and pool function takes torch tensors that already live on
+the GPU, passes their device pointers and sizes to the C ABI
+(include/pagedkv.h) on torch's current stream, and turns a negative status
+into an exception.  All arithmetic happens in the HIP kernels; there is no
+CPU fallback: without the built library, or with CPU tensors, these
+functions raise.  BlockManager wraps the library's host-side block pool
+(pkv_bm_*), whose bookkeeping runs in the library's C++ code.
 """
 from __future__ import annotations
 
@@ -24,11 +26,18 @@ PKV_ERR_UNSUPPORTED = -3
 PKV_ERR_WORKSPACE = -4
 PKV_ERR_LAUNCH = -5
 PKV_ERR_ALIGN = -6
+PKV_ERR_NO_MEMORY = -7
+PKV_ERR_STATE = -8
+PKV_ERR_HOST_ALLOC = -9
 PKV_OUT_F32 = 0
 PKV_OUT_BF16 = 1
 
 EXPORTED = ("pkv_status_string", "pkv_version", "pkv_kv_append", "pkv_decode_workspace_bytes",
-            "pkv_paged_decode_attn", "pkv_prefill_workspace_bytes", "pkv_paged_prefill_attn")
+            "pkv_paged_decode_attn", "pkv_prefill_workspace_bytes", "pkv_paged_prefill_attn",
+            "pkv_copy_blocks", "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free",
+            "pkv_bm_allocate", "pkv_bm_free", "pkv_bm_fork", "pkv_bm_append", "pkv_bm_append_batch",
+            "pkv_bm_seq_info",
+            "pkv_bm_refcount", "pkv_bm_block_table")
 
 _lib = None
 
@@ -41,6 +50,17 @@ class PagedKVError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{msg} (status {status})")
         self.status = status
+
+
+class OutOfBlocks(PagedKVError, MemoryError):
+    """PKV_ERR_NO_MEMORY: the block pool has too few free blocks."""
+
+
+class UnknownSequence(PagedKVError, KeyError):
+    """PKV_ERR_STATE: a sequence id that is unknown, or already exists."""
+
+    def __str__(self):  # KeyError would quote the message
+        return RuntimeError.__str__(self)
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -69,6 +89,30 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_paged_prefill_attn.argtypes = [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
                                            _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                            _vp, _sz, _vp]
+    lib.pkv_copy_blocks.restype = _i32
+    lib.pkv_copy_blocks.argtypes = [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _i64, _vp]
+    lib.pkv_bm_create.restype = _vp
+    lib.pkv_bm_create.argtypes = [_i64, _i32]
+    lib.pkv_bm_destroy.restype = None
+    lib.pkv_bm_destroy.argtypes = [_vp]
+    lib.pkv_bm_num_free.restype = _i64
+    lib.pkv_bm_num_free.argtypes = [_vp]
+    lib.pkv_bm_allocate.restype = _i32
+    lib.pkv_bm_allocate.argtypes = [_vp, _i64, _i64]
+    lib.pkv_bm_free.restype = _i32
+    lib.pkv_bm_free.argtypes = [_vp, _i64]
+    lib.pkv_bm_fork.restype = _i32
+    lib.pkv_bm_fork.argtypes = [_vp, _i64, _i64]
+    lib.pkv_bm_append.restype = _i32
+    lib.pkv_bm_append.argtypes = [_vp, _i64, _i64, _vp, _vp, _i64, _vp]
+    lib.pkv_bm_append_batch.restype = _i32
+    lib.pkv_bm_append_batch.argtypes = [_vp, _vp, _vp, _i32, _vp, _vp, _i64, _vp]
+    lib.pkv_bm_seq_info.restype = _i32
+    lib.pkv_bm_seq_info.argtypes = [_vp, _i64, _vp, _vp]
+    lib.pkv_bm_refcount.restype = _i32
+    lib.pkv_bm_refcount.argtypes = [_vp, _i64, _vp]
+    lib.pkv_bm_block_table.restype = _i32
+    lib.pkv_bm_block_table.argtypes = [_vp, _vp, _i32, _vp, _i32, _vp]
     _lib = lib
     return lib
 
@@ -78,8 +122,10 @@ def status_string(status: int) -> str:
 
 
 def _check(status: int):
-    if status != PKV_OK:
-        raise PagedKVError(status, status_string(status))
+    if status == PKV_OK:
+        return
+    cls = {PKV_ERR_NO_MEMORY: OutOfBlocks, PKV_ERR_STATE: UnknownSequence}.get(status, PagedKVError)
+    raise cls(status, status_string(status))
 
 
 def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
@@ -193,3 +239,141 @@ def paged_prefill_attn(q: torch.Tensor, cu_q_lens: torch.Tensor, k_cache: torch.
         max_q_len, tq, nseq, hq, hkv, d, bs, float(scale), 1 if causal else 0, ws_ptr, ws_len,
         _stream(stream)))
     return out
+
+
+def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_mapping: torch.Tensor,
+                stream=None) -> None:
+    """pkv_copy_blocks: for each row (src, dst) of block_mapping [P, 2]
+    (int64, on the GPU), copy pool block src to block dst in K and V."""
+    lib = load_library()
+    nb, bs, hkv, d = k_cache.shape
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("K and V pools differ in shape")
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [num_pairs, 2]")
+    _check(lib.pkv_copy_blocks(_dev(k_cache, "k_cache", torch.bfloat16),
+                               _dev(v_cache, "v_cache", torch.bfloat16), nb, bs, hkv, d,
+                               _dev(block_mapping, "block_mapping", torch.int64),
+                               block_mapping.shape[0], _stream(stream)))
+
+
+def _host_i64(x) -> torch.Tensor:
+    """A contiguous int64 CPU tensor of x (no copy when x already is one)."""
+    if isinstance(x, torch.Tensor):
+        if x.is_cuda:
+            raise TypeError("block-manager arguments live on the host")
+        if x.dtype == torch.int64 and x.is_contiguous():
+            return x
+        return x.to(torch.int64).contiguous()
+    return torch.tensor(list(x), dtype=torch.int64)
+
+
+class BlockManager:
+    """The library's host-side pool of physical KV blocks (pkv_bm_*).
+
+    Sequences are named by caller-chosen int ids.  append() returns the slots
+    to hand to kv_append and the (source, destination) block copies to run
+    with copy_blocks first; block_table() returns the table and context
+    lengths the attention calls read.  Running out of blocks raises
+    OutOfBlocks (a MemoryError) and changes nothing; an unknown or repeated
+    sequence id raises UnknownSequence (a KeyError).
+    """
+
+    def __init__(self, num_blocks: int, block_size: int = 16):
+        self._lib = load_library()
+        h = self._lib.pkv_bm_create(num_blocks, block_size)
+        if not h:
+            raise ValueError(f"cannot create a block manager of {num_blocks} x {block_size}")
+        self._h = h
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            self._lib.pkv_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def _handle(self):
+        if not self._h:
+            raise ValueError("block manager is closed")
+        return self._h
+
+    def num_free(self) -> int:
+        return self._lib.pkv_bm_num_free(self._handle())
+
+    def allocate(self, seq_id: int, num_tokens: int) -> None:
+        _check(self._lib.pkv_bm_allocate(self._handle(), seq_id, num_tokens))
+
+    def free(self, seq_id: int) -> None:
+        _check(self._lib.pkv_bm_free(self._handle(), seq_id))
+
+    def fork(self, parent: int, child: int) -> None:
+        _check(self._lib.pkv_bm_fork(self._handle(), parent, child))
+
+    def append(self, seq_id: int, num_tokens: int):
+        """Room for num_tokens more tokens: (slots int64 [num_tokens],
+        copies int64 [num_copies, 2]) as CPU tensors."""
+        if num_tokens < 0:
+            raise ValueError("num_tokens >= 0 required")
+        slots = torch.empty(num_tokens, dtype=torch.int64)
+        copies = torch.empty((1, 2), dtype=torch.int64)
+        n = ctypes.c_int64(0)
+        _check(self._lib.pkv_bm_append(self._handle(), seq_id, num_tokens,
+                                       slots.data_ptr() if num_tokens else None,
+                                       copies.data_ptr(), 1, ctypes.byref(n)))
+        return slots, copies[:n.value].clone()
+
+    def append_batch(self, seq_ids, num_tokens):
+        """append() for many sequences in one library call, all or nothing:
+        (slots int64 [sum num_tokens] in entry order, copies int64 [n, 2]).
+        seq_ids and num_tokens may be int sequences or int64 CPU tensors
+        (passed without conversion)."""
+        ids, counts = _host_i64(seq_ids), _host_i64(num_tokens)
+        n = ids.numel()
+        if counts.numel() != n:
+            raise ValueError("seq_ids and num_tokens differ in length")
+        total = int(counts.sum()) if n else 0
+        slots = torch.empty(total + 1, dtype=torch.int64)  # +1: an address even when empty
+        copies = torch.empty((max(n, 1), 2), dtype=torch.int64)
+        nc = ctypes.c_int64(0)
+        _check(self._lib.pkv_bm_append_batch(self._handle(), ids.data_ptr() if n else None,
+                                             counts.data_ptr() if n else None, n,
+                                             slots.data_ptr(), copies.data_ptr(), n,
+                                             ctypes.byref(nc)))
+        return slots[:total], copies[:nc.value]
+
+    def seq_info(self, seq_id: int):
+        """(tokens held, blocks held) of seq_id."""
+        t, b = ctypes.c_int64(0), ctypes.c_int64(0)
+        _check(self._lib.pkv_bm_seq_info(self._handle(), seq_id, ctypes.byref(t), ctypes.byref(b)))
+        return t.value, b.value
+
+    def refcount(self, block: int) -> int:
+        c = ctypes.c_int32(0)
+        _check(self._lib.pkv_bm_refcount(self._handle(), block, ctypes.byref(c)))
+        return c.value
+
+    def block_table(self, seq_ids, max_blocks_per_seq: int):
+        """(table int32 [n, max_blocks_per_seq] padded with -1, context_lens
+        int32 [n]) as CPU tensors, for the sequences in seq_ids in order
+        (an int sequence or an int64 CPU tensor)."""
+        ids = _host_i64(seq_ids)
+        n = ids.numel()
+        if max_blocks_per_seq < 0:
+            raise ValueError("max_blocks_per_seq >= 0 required")
+        # one spare element so that an empty table still has an address
+        buf = torch.empty(n * max_blocks_per_seq + 1, dtype=torch.int32)
+        lens = torch.empty(n, dtype=torch.int32)
+        _check(self._lib.pkv_bm_block_table(self._handle(), ids.data_ptr() if n else None, n,
+                                            buf.data_ptr(), max_blocks_per_seq,
+                                            lens.data_ptr() if n else None))
+        return buf[:n * max_blocks_per_seq].view(n, max_blocks_per_seq), lens

@@ -1,6 +1,7 @@
-"""Build libpagedkv.so (gfx950) from csrc/*.hip with hipcc.
+"""Build libpagedkv.so (gfx950) from csrc/*.hip and csrc/*.cpp with hipcc.
 
-Each source compiles to its own object in parallel, then one link.  Flags:
+Each source compiles to its own object in parallel, then one link; .cpp
+files hold host-only code and compile as plain C++ (-x c++).  Flags:
   --offload-arch=gfx950       MI355X only
   -O3 -std=c++17 -fPIC
   -Xclang -target-feature -Xclang -packed-fp32-ops
@@ -34,12 +35,13 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 
 
 def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
 def _compile(src, verbose):
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + COMMON + ["-c", src, "-o", obj]
+    lang = ["-x", "c++"] if src.endswith(".cpp") else []
+    cmd = [hipcc()] + COMMON + lang + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

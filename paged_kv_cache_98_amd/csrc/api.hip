@@ -56,6 +56,9 @@ const char* pkv_status_string(int status) {
         case PKV_ERR_WORKSPACE: return "workspace missing or too small";
         case PKV_ERR_LAUNCH: return "HIP launch error";
         case PKV_ERR_ALIGN: return "a bf16 or output array is not 16-byte aligned";
+        case PKV_ERR_NO_MEMORY: return "not enough free KV blocks";
+        case PKV_ERR_STATE: return "unknown or already existing sequence id";
+        case PKV_ERR_HOST_ALLOC: return "host memory allocation failed";
         default: return "unknown status";
     }
 }
@@ -81,6 +84,25 @@ int pkv_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapp
     a.v_cache = static_cast<uint16_t*>(v_cache);
     a.row_elems = num_kv_heads * head_dim;
     return to_status(pkv::launch_kv_append(a, static_cast<hipStream_t>(stream)));
+}
+
+int pkv_copy_blocks(void* k_cache, void* v_cache, int64_t num_blocks, int block_size,
+                    int num_kv_heads, int head_dim, const int64_t* block_mapping,
+                    int64_t num_pairs, void* stream) {
+    if (num_pairs < 0 || num_blocks < 0 || num_kv_heads <= 0) return PKV_ERR_SHAPE;
+    if (head_dim != pkv::kHeadDim) return PKV_ERR_UNSUPPORTED;
+    if (block_size != 16 && block_size != 32) return PKV_ERR_UNSUPPORTED;
+    if (num_pairs == 0) return PKV_OK;
+    if (!k_cache || !v_cache || !block_mapping) return PKV_ERR_NULL;
+    if (!aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_ALIGN;
+    pkv::CopyBlocksArgs a;
+    a.k_cache = static_cast<uint16_t*>(k_cache);
+    a.v_cache = static_cast<uint16_t*>(v_cache);
+    a.block_mapping = block_mapping;
+    a.num_pairs = num_pairs;
+    a.num_blocks = num_blocks;
+    a.block_elems = (int64_t)block_size * num_kv_heads * head_dim;
+    return to_status(pkv::launch_copy_blocks(a, static_cast<hipStream_t>(stream)));
 }
 
 size_t pkv_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,

@@ -1,0 +1,300 @@
+// block_manager.cpp -- host-side pool of physical KV blocks: the bookkeeping
+// that produces the block tables and slot mappings the attention calls read.
+//
+// What it implements:
+//   * "LLM 推理引擎深度解析：vLLM、SGLang 与 TensorRT-LLM 的核心优化原理",
+//     section 2.1 "PagedAttention": a pool of num_blocks fixed-size blocks
+//     with a free list; a sequence of n tokens holds ceil(n / block_size)
+//     blocks, which need not be contiguous; allocation fails (no memory)
+//     when too few are free; freeing returns a sequence's blocks, and
+//     freeing an unknown id does nothing;
+//   * "让 Agent 跑得快：LLM 推理服务", section 五: blocks are taken on
+//     demand, one more each time the last one is full, so at most
+//     block_size - 1 slots per sequence are unused; block tables may share
+//     physical blocks under a reference count;
+//   * same page, section 二, "Copy-on-Write": writing a new token into a
+//     shared, partly filled last block first copies that block to a fresh
+//     one and repoints the table entry (the caller performs the returned
+//     copies on the device with pkv_copy_blocks before writing); a block
+//     whose count drops to zero returns to the pool.
+// Blocks leave the front of the free list and come back at its end.  A call
+// that would run out of blocks part-way changes nothing.  The free list is a
+// ring of num_blocks entries (a block is free at most once), so giving blocks
+// back never allocates and cannot fail half-way.
+#include <algorithm>
+#include <cstdint>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "pagedkv.h"
+
+struct pkv_block_manager {
+    struct Seq {
+        std::vector<int64_t> blocks;
+        int64_t length = 0;
+    };
+    int64_t num_blocks = 0;
+    int block_size = 16;
+    std::vector<int64_t> ring;  // free list: ring[head], ... (num_free entries)
+    int64_t head = 0;
+    int64_t num_free = 0;
+    std::vector<int32_t> refcount;
+    std::unordered_map<int64_t, Seq> seqs;
+
+    int64_t blocks_for(int64_t tokens) const { return (tokens + block_size - 1) / block_size; }
+    int64_t take() {
+        const int64_t b = ring[(size_t)head];
+        head = head + 1 == num_blocks ? 0 : head + 1;
+        --num_free;
+        refcount[(size_t)b] = 1;
+        return b;
+    }
+    void release(int64_t b) {
+        if (--refcount[(size_t)b] == 0) {
+            int64_t tail = head + num_free;
+            if (tail >= num_blocks) tail -= num_blocks;
+            ring[(size_t)tail] = b;
+            ++num_free;
+        }
+    }
+    // Undo of take(): b goes back to the FRONT of the free list, so undoing
+    // takes in reverse order restores the list exactly.
+    void untake(int64_t b) {
+        refcount[(size_t)b] = 0;
+        head = head == 0 ? num_blocks - 1 : head - 1;
+        ring[(size_t)head] = b;
+        ++num_free;
+    }
+
+    // What one append changed, enough to put it back.
+    struct Undo {
+        Seq* seq;
+        int64_t old_length;
+        size_t old_blocks;
+        int64_t cow_old;  // -1: no copy
+    };
+
+    // Room for n more tokens of s: slots written, at most one copy (src, dst)
+    // written to copy_pair when room_for_copy.  Changes nothing on failure.
+    int append(Seq& s, int64_t n, int64_t* slots, int64_t* copy_pair, bool room_for_copy,
+               Undo* undo) {
+        const int bs = block_size;
+        undo->seq = &s;
+        undo->old_length = s.length;
+        undo->old_blocks = s.blocks.size();
+        undo->cow_old = -1;
+        if (n == 0) return PKV_OK;
+        // what the pool must supply: a copy of a shared partly filled last
+        // block, and one block per boundary crossed
+        const bool last_shared = s.length % bs != 0 && refcount[(size_t)s.blocks.back()] > 1;
+        const int64_t new_blocks = blocks_for(s.length + n) - (int64_t)s.blocks.size();
+        if ((last_shared ? 1 : 0) + new_blocks > num_free) return PKV_ERR_NO_MEMORY;
+        if (last_shared && !room_for_copy) return PKV_ERR_SHAPE;
+        try {
+            s.blocks.reserve(s.blocks.size() + (size_t)new_blocks);
+        } catch (...) {
+            return PKV_ERR_HOST_ALLOC;
+        }
+        if (last_shared) {
+            const int64_t old = s.blocks.back();
+            const int64_t dst = take();
+            copy_pair[0] = old;
+            copy_pair[1] = dst;
+            undo->cow_old = old;
+            release(old);  // stays above zero: it was shared
+            s.blocks.back() = dst;
+        }
+        for (int64_t i = 0; i < n; ++i) {
+            const int64_t pos = s.length + i;
+            if (pos / bs == (int64_t)s.blocks.size()) s.blocks.push_back(take());
+            slots[i] = s.blocks[(size_t)(pos / bs)] * bs + pos % bs;
+        }
+        s.length += n;
+        return PKV_OK;
+    }
+
+    void rollback(const Undo& u) {
+        Seq& s = *u.seq;
+        while (s.blocks.size() > u.old_blocks) {
+            untake(s.blocks.back());
+            s.blocks.pop_back();
+        }
+        if (u.cow_old >= 0) {
+            untake(s.blocks.back());
+            ++refcount[(size_t)u.cow_old];
+            s.blocks.back() = u.cow_old;
+        }
+        s.length = u.old_length;
+    }
+};
+
+extern "C" {
+
+pkv_block_manager* pkv_bm_create(int64_t num_blocks, int block_size) {
+    if (num_blocks < 0 || num_blocks > INT32_MAX || block_size <= 0) return nullptr;
+    pkv_block_manager* bm = new (std::nothrow) pkv_block_manager;
+    if (bm == nullptr) return nullptr;
+    try {
+        bm->num_blocks = num_blocks;
+        bm->block_size = block_size;
+        bm->refcount.assign((size_t)num_blocks, 0);
+        bm->ring.resize((size_t)num_blocks);
+        for (int64_t b = 0; b < num_blocks; ++b) bm->ring[(size_t)b] = b;
+        bm->num_free = num_blocks;
+    } catch (...) {
+        delete bm;
+        return nullptr;
+    }
+    return bm;
+}
+
+void pkv_bm_destroy(pkv_block_manager* bm) { delete bm; }
+
+int64_t pkv_bm_num_free(const pkv_block_manager* bm) {
+    return bm == nullptr ? -1 : bm->num_free;
+}
+
+int pkv_bm_allocate(pkv_block_manager* bm, int64_t seq_id, int64_t num_tokens) {
+    if (bm == nullptr) return PKV_ERR_NULL;
+    if (num_tokens < 0) return PKV_ERR_SHAPE;
+    if (bm->seqs.count(seq_id)) return PKV_ERR_STATE;
+    const int64_t need = bm->blocks_for(num_tokens);
+    if (need > bm->num_free) return PKV_ERR_NO_MEMORY;
+    try {
+        pkv_block_manager::Seq s;
+        s.blocks.reserve((size_t)need);
+        s.length = num_tokens;
+        auto& slot = bm->seqs[seq_id];  // may throw before anything is taken
+        for (int64_t i = 0; i < need; ++i) s.blocks.push_back(bm->take());
+        slot = std::move(s);
+    } catch (...) {
+        return PKV_ERR_HOST_ALLOC;
+    }
+    return PKV_OK;
+}
+
+int pkv_bm_free(pkv_block_manager* bm, int64_t seq_id) {
+    if (bm == nullptr) return PKV_ERR_NULL;
+    auto it = bm->seqs.find(seq_id);
+    if (it == bm->seqs.end()) return PKV_OK;
+    for (int64_t b : it->second.blocks) bm->release(b);
+    bm->seqs.erase(it);
+    return PKV_OK;
+}
+
+int pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child) {
+    if (bm == nullptr) return PKV_ERR_NULL;
+    auto it = bm->seqs.find(parent);
+    if (it == bm->seqs.end() || bm->seqs.count(child)) return PKV_ERR_STATE;
+    try {
+        pkv_block_manager::Seq s = it->second;  // copy before inserting (rehash)
+        bm->seqs.emplace(child, std::move(s));
+    } catch (...) {
+        return PKV_ERR_HOST_ALLOC;
+    }
+    for (int64_t b : bm->seqs.at(child).blocks) ++bm->refcount[b];
+    return PKV_OK;
+}
+
+int pkv_bm_append(pkv_block_manager* bm, int64_t seq_id, int64_t num_tokens, int64_t* slots,
+                  int64_t* copies, int64_t max_copies, int64_t* num_copies) {
+    if (bm == nullptr || num_copies == nullptr || (num_tokens > 0 && slots == nullptr))
+        return PKV_ERR_NULL;
+    if (num_tokens < 0 || max_copies < 0) return PKV_ERR_SHAPE;
+    auto it = bm->seqs.find(seq_id);
+    if (it == bm->seqs.end()) return PKV_ERR_STATE;
+    *num_copies = 0;
+    pkv_block_manager::Undo undo;
+    const int st = bm->append(it->second, num_tokens, slots, copies,
+                              copies != nullptr && max_copies >= 1, &undo);
+    if (st == PKV_OK && undo.cow_old >= 0) *num_copies = 1;
+    return st;
+}
+
+int pkv_bm_append_batch(pkv_block_manager* bm, const int64_t* seq_ids, const int64_t* num_tokens,
+                        int num_seqs, int64_t* slots, int64_t* copies, int64_t max_copies,
+                        int64_t* num_copies) {
+    if (bm == nullptr || num_copies == nullptr) return PKV_ERR_NULL;
+    if (num_seqs < 0 || max_copies < 0) return PKV_ERR_SHAPE;
+    *num_copies = 0;
+    if (num_seqs == 0) return PKV_OK;
+    if (seq_ids == nullptr || num_tokens == nullptr) return PKV_ERR_NULL;
+    int64_t total = 0;
+    for (int i = 0; i < num_seqs; ++i) {
+        if (num_tokens[i] < 0) return PKV_ERR_SHAPE;
+        total += num_tokens[i];
+    }
+    if (total > 0 && slots == nullptr) return PKV_ERR_NULL;
+    std::vector<pkv_block_manager::Undo> log;
+    try {
+        log.reserve((size_t)num_seqs);
+    } catch (...) {
+        return PKV_ERR_HOST_ALLOC;
+    }
+    int64_t done_tokens = 0, done_copies = 0;
+    int st = PKV_OK;
+    for (int i = 0; i < num_seqs && st == PKV_OK; ++i) {
+        auto it = bm->seqs.find(seq_ids[i]);
+        if (it == bm->seqs.end()) {
+            st = PKV_ERR_STATE;
+            break;
+        }
+        pkv_block_manager::Undo undo;
+        st = bm->append(it->second, num_tokens[i], slots + done_tokens,
+                        copies == nullptr ? nullptr : copies + 2 * done_copies,
+                        copies != nullptr && done_copies < max_copies, &undo);
+        if (st != PKV_OK) break;
+        log.push_back(undo);
+        done_tokens += num_tokens[i];
+        if (undo.cow_old >= 0) ++done_copies;
+    }
+    if (st != PKV_OK) {
+        for (auto u = log.rbegin(); u != log.rend(); ++u) bm->rollback(*u);
+        return st;
+    }
+    *num_copies = done_copies;
+    return PKV_OK;
+}
+
+int pkv_bm_seq_info(const pkv_block_manager* bm, int64_t seq_id, int64_t* num_tokens,
+                    int64_t* num_blocks) {
+    if (bm == nullptr || num_tokens == nullptr || num_blocks == nullptr) return PKV_ERR_NULL;
+    auto it = bm->seqs.find(seq_id);
+    if (it == bm->seqs.end()) return PKV_ERR_STATE;
+    *num_tokens = it->second.length;
+    *num_blocks = (int64_t)it->second.blocks.size();
+    return PKV_OK;
+}
+
+int pkv_bm_refcount(const pkv_block_manager* bm, int64_t block, int32_t* count) {
+    if (bm == nullptr || count == nullptr) return PKV_ERR_NULL;
+    if (block < 0 || block >= bm->num_blocks) return PKV_ERR_SHAPE;
+    *count = bm->refcount[(size_t)block];
+    return PKV_OK;
+}
+
+int pkv_bm_block_table(const pkv_block_manager* bm, const int64_t* seq_ids, int num_seqs,
+                       int32_t* table, int max_blocks_per_seq, int32_t* context_lens) {
+    if (bm == nullptr) return PKV_ERR_NULL;
+    if (num_seqs < 0 || max_blocks_per_seq < 0) return PKV_ERR_SHAPE;
+    if (num_seqs == 0) return PKV_OK;
+    if (seq_ids == nullptr || table == nullptr || context_lens == nullptr) return PKV_ERR_NULL;
+    for (int i = 0; i < num_seqs; ++i) {
+        auto it = bm->seqs.find(seq_ids[i]);
+        if (it == bm->seqs.end()) return PKV_ERR_STATE;
+        if ((int64_t)it->second.blocks.size() > max_blocks_per_seq ||
+            it->second.length > INT32_MAX)
+            return PKV_ERR_SHAPE;
+    }
+    for (int i = 0; i < num_seqs; ++i) {
+        const auto& s = bm->seqs.at(seq_ids[i]);
+        int32_t* row = table + (size_t)i * max_blocks_per_seq;
+        std::fill(row, row + max_blocks_per_seq, -1);
+        for (size_t j = 0; j < s.blocks.size(); ++j) row[j] = (int32_t)s.blocks[j];
+        context_lens[i] = (int32_t)s.length;
+    }
+    return PKV_OK;
+}
+
+}  // extern "C"

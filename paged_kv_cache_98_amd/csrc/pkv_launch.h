@@ -19,6 +19,15 @@ struct AppendArgs {
     int row_elems;  // num_kv_heads * head_dim
 };
 
+struct CopyBlocksArgs {
+    uint16_t* k_cache;
+    uint16_t* v_cache;
+    const int64_t* block_mapping;  // [num_pairs][2] (source, destination)
+    int64_t num_pairs;
+    int64_t num_blocks;
+    int64_t block_elems;  // block_size * num_kv_heads * head_dim
+};
+
 struct DecodeArgs {
     void* out;
     bool out_bf16;
@@ -66,6 +75,7 @@ struct PrefillArgs {
 };
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 

@@ -1,0 +1,181 @@
+"""GPU parity of copy_blocks (bit-exact against the oracle's whole-block copy)
+and an end-to-end copy-on-write decode: the native block manager's tables,
+slots and copies drive copy_blocks, kv_append and paged_decode_attn, and the
+result is checked against the fp64 oracle run on each sequence's tokens laid
+out afresh (so the oracle never sees the manager's tables)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.blocks import copy_blocks as oracle_copy_blocks
+from paged_kv_cache_98_amd import binding as pkv
+from tests.gpu_common import parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def random_bits(shape, seed, device="cpu"):
+    """bf16 tensors with uniformly random bit patterns (NaNs and infinities
+    included: the copy must move bits, not values)."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    return torch.randint(-32768, 32768, shape, generator=g, device=device,
+                         dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+
+
+def bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def cow_pairs(num_blocks, num_pairs, seed, invalid=0):
+    """Distinct destinations, none of them a source; plus `invalid` pairs
+    naming blocks outside the pool (skipped by the kernel)."""
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(num_blocks)
+    dst = perm[:num_pairs]
+    src = rng.choice(perm[num_pairs:], size=num_pairs)
+    pairs = np.stack([src, dst], 1).astype(np.int64)
+    bad = np.array([[-1, perm[-1]], [perm[-1], num_blocks], [num_blocks + 5, -3],
+                    [perm[-2], -1 << 40]], dtype=np.int64)[:invalid]
+    out = np.concatenate([pairs, bad]) if invalid else pairs
+    return out[rng.permutation(len(out))]
+
+
+@pytest.mark.parametrize("num_blocks,bs,hkv,num_pairs", [
+    (64, 16, 8, 1), (200, 16, 8, 37), (96, 32, 16, 20), (50, 16, 1, 24), (33, 32, 2, 16)])
+def test_copy_blocks_bit_exact(num_blocks, bs, hkv, num_pairs):
+    d = 128
+    print(f"[copy_blocks] nb={num_blocks} bs={bs} hkv={hkv} pairs={num_pairs}", flush=True)
+    k = random_bits((num_blocks, bs, hkv, d), seed=num_blocks * 7 + 1)
+    v = random_bits((num_blocks, bs, hkv, d), seed=num_blocks * 7 + 2)
+    pairs = cow_pairs(num_blocks, num_pairs, seed=num_pairs, invalid=4)
+    ref_k, ref_v = oracle_copy_blocks(bits(k), bits(v), pairs.tolist())
+    kd, vd = k.to(DEV), v.to(DEV)
+    pkv.copy_blocks(kd, vd, torch.from_numpy(pairs).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(kd), ref_k)
+    assert np.array_equal(bits(vd), ref_v)
+    # nothing else moved: an empty mapping is a no-op
+    pkv.copy_blocks(kd, vd, torch.empty((0, 2), dtype=torch.int64, device=DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(kd), ref_k)
+
+
+def test_copy_blocks_many_pairs_sampled():
+    """More work units than the launch's 65536 workgroups (8300 pairs x 8
+    slices of a 32 x 16 x 128 block), so each workgroup loops; sampled pairs
+    and untouched blocks are checked on the host."""
+    nb, bs, hkv, d, npairs = 16700, 32, 16, 128, 8300
+    print(f"[copy_blocks] large nb={nb} pairs={npairs}", flush=True)
+    k = random_bits((nb, bs, hkv, d), seed=11, device=DEV)
+    v = random_bits((nb, bs, hkv, d), seed=12, device=DEV)
+    pairs = cow_pairs(nb, npairs, seed=13)
+    rng = np.random.default_rng(14)
+    pick = rng.choice(npairs, size=48, replace=False)
+    dst_set = set(pairs[:, 1].tolist())
+    untouched = [b for b in rng.choice(nb, size=200, replace=False).tolist() if b not in dst_set][:24]
+    src_before_k = {int(pairs[i, 0]): bits(k[int(pairs[i, 0])]) for i in pick}
+    src_before_v = {int(pairs[i, 0]): bits(v[int(pairs[i, 0])]) for i in pick}
+    keep_k = {b: bits(k[b]) for b in untouched}
+    pkv.copy_blocks(k, v, torch.from_numpy(pairs).to(DEV))
+    torch.cuda.synchronize()
+    for i in pick:
+        s, t = int(pairs[i, 0]), int(pairs[i, 1])
+        assert np.array_equal(bits(k[t]), src_before_k[s]), (s, t)
+        assert np.array_equal(bits(v[t]), src_before_v[s]), (s, t)
+    for b in untouched:
+        assert np.array_equal(bits(k[b]), keep_k[b]), b
+    del k, v
+    torch.cuda.empty_cache()
+
+
+class DenseSeqs:
+    """Each sequence's K/V rows in order, kept on the host: what the cache
+    must hold, whatever blocks the manager chose."""
+
+    def __init__(self):
+        self.k, self.v = {}, {}
+
+    def fork(self, parent, child):
+        self.k[child] = list(self.k[parent])
+        self.v[child] = list(self.v[parent])
+
+    def add(self, s, k_rows, v_rows):
+        self.k.setdefault(s, []).extend(bits(k_rows))
+        self.v.setdefault(s, []).extend(bits(v_rows))
+
+    def oracle_decode(self, seqs, q, bs, scale):
+        """fp64 oracle over a fresh contiguous layout of the given sequences."""
+        lens = [len(self.k[s]) for s in seqs]
+        nblk = [-(-n // bs) for n in lens]
+        hkv, d = self.k[seqs[0]][0].shape
+        kp = np.zeros((sum(nblk), bs, hkv, d), np.uint16)
+        vp = np.zeros_like(kp)
+        bt = np.full((len(seqs), max(nblk)), -1, np.int32)
+        base = 0
+        for i, s in enumerate(seqs):
+            rows_k = np.stack(self.k[s])
+            rows_v = np.stack(self.v[s])
+            flat_k = kp.reshape(-1, hkv, d)
+            flat_v = vp.reshape(-1, hkv, d)
+            flat_k[base * bs: base * bs + lens[i]] = rows_k
+            flat_v[base * bs: base * bs + lens[i]] = rows_v
+            bt[i, :nblk[i]] = np.arange(base, base + nblk[i])
+            base += nblk[i]
+        return oracle.paged_attention(q, kp, vp, bt, np.array(lens, np.int32), scale)
+
+
+@pytest.mark.parametrize("bs,prompt_len", [(16, 1000), (32, 777), (16, 64)])
+def test_beam_fork_decode_end_to_end(bs, prompt_len):
+    """A prompt is written, forked into 4 beams (the parent freed), and the
+    beams decode 6 steps, one beam forking again at step 2; each step runs
+    the manager's copies, appends each beam's token and decodes all beams."""
+    hq, hkv, d, nb = 32, 8, 128, 400
+    scale = d ** -0.5
+    print(f"[beam] bs={bs} prompt={prompt_len}", flush=True)
+    gen = torch.Generator().manual_seed(bs * 1000 + prompt_len)
+
+    def randn(*shape):
+        return torch.randn(shape, generator=gen).to(torch.bfloat16)
+
+    k_pool = torch.zeros((nb, bs, hkv, d), dtype=torch.bfloat16, device=DEV)
+    v_pool = torch.zeros_like(k_pool)
+    dense = DenseSeqs()
+    copies_seen = 0
+    with pkv.BlockManager(nb, bs) as bm:
+        def write(seq, k_rows, v_rows):
+            nonlocal copies_seen
+            slots, copies = bm.append(seq, k_rows.shape[0])
+            if copies.numel():
+                copies_seen += copies.shape[0]
+                pkv.copy_blocks(k_pool, v_pool, copies.to(DEV))
+            pkv.kv_append(k_rows.to(DEV), v_rows.to(DEV), slots.to(DEV), k_pool, v_pool)
+            dense.add(seq, k_rows, v_rows)
+
+        bm.allocate(0, 0)
+        write(0, randn(prompt_len, hkv, d), randn(prompt_len, hkv, d))
+        beams = [1, 2, 3, 4]
+        for b in beams:
+            bm.fork(0, b)
+            dense.fork(0, b)
+        bm.free(0)
+        for step in range(6):
+            if step == 2:
+                bm.fork(2, 5)
+                dense.fork(2, 5)
+                beams.append(5)
+            for b in beams:
+                write(b, randn(1, hkv, d), randn(1, hkv, d))
+            q = randn(len(beams), hq, d)
+            width = max(bm.seq_info(b)[1] for b in beams)
+            table, lens = bm.block_table(beams, width)
+            out = pkv.paged_decode_attn(q.to(DEV), k_pool, v_pool, table.to(DEV), lens.to(DEV),
+                                        scale, max_context_len=int(lens.max()))
+            torch.cuda.synchronize()
+            ref = dense.oracle_decode(beams, q, bs, scale)
+            parity(out, ref, what=f"beam step {step} bs={bs}")
+        # the partly filled prompt block was shared: copies happened exactly
+        # when a beam wrote into a block someone else still held
+        assert copies_seen >= (3 if prompt_len % bs else 0)
