@@ -14,6 +14,8 @@ Contents
   * ``blocks``: the pages' block pool (allocate / free / fork / append with
     copy-on-write, reference counts) and the whole-block copy of
     copy-on-write.
+  * ``fp8``: the E4M3 format, the quantised append and the fp64 decode over
+    an FP8 cache with per-cache scales.
 
 Every function names the passage it follows.  Functions without an
 independent pin say "parity unpinned" in their docstring (none at present).

@@ -1,0 +1,124 @@
+"""The FP8 (E4M3) oracle pinned: the format's defining values, the encoder
+against brute-force nearest-value search, the quantiser's direction and
+clamp, the quantised append against the C oracle's byte copy, and the FP8
+decode against the C oracle's bf16 attention on exactly representable
+values."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import fp8
+
+
+def test_pin_format_values():
+    """OCP E4M3: bias 7, 3 mantissa bits, subnormals m * 2^-9, S.1111.111 NaN."""
+    v = fp8.e4m3_value
+    assert v(0x38) == 1.0 and v(0x40) == 2.0 and v(0x30) == 0.5
+    assert v(0x7E) == 448.0 and v(0xFE) == -448.0
+    assert v(0x77) == 240.0                      # 1.875 * 2^7
+    assert v(0x08) == 2.0 ** -6 and v(0x01) == 2.0 ** -9 and v(0x07) == 7 * 2.0 ** -9
+    assert v(0x00) == 0.0 and np.signbit(v(0x80))
+    assert np.isnan(v(0x7F)) and np.isnan(v(0xFF))
+    pos = v(np.arange(127))
+    assert np.all(np.diff(pos) > 0)              # 127 distinct, increasing
+    # ulp doubles at each binade above the subnormals
+    assert v(0x09) - v(0x08) == 2.0 ** -9 and v(0x79) - v(0x78) == 2.0 ** 5
+
+
+def brute_encode(y):
+    vals = fp8.e4m3_value(np.arange(127))
+    out = []
+    for x in np.asarray(y, dtype=np.float32):
+        d = np.abs(vals - abs(float(x)))
+        best = np.flatnonzero(d == d.min())
+        c = int(best[0]) if len(best) == 1 else int([b for b in best if b % 2 == 0][0])
+        out.append((0x80 if np.signbit(x) else 0) | c)
+    return np.array(out, dtype=np.uint8)
+
+
+def test_pin_encode_against_brute_force():
+    rng = np.random.default_rng(3)
+    mag = np.exp(rng.uniform(np.log(2.0 ** -12), np.log(448.0), size=4000))
+    y = (mag * rng.choice([-1.0, 1.0], size=mag.size)).astype(np.float32)
+    y = np.clip(y, -448.0, 448.0).astype(np.float32)
+    assert np.array_equal(fp8.e4m3_encode(y), brute_encode(y))
+
+
+def test_pin_encode_midpoints_and_round_trip():
+    vals = fp8.e4m3_value(np.arange(127))
+    for c in range(126):
+        mid = np.float32((vals[c] + vals[c + 1]) / 2)        # exact: <= 5 significant bits
+        assert float(mid) == (vals[c] + vals[c + 1]) / 2
+        even = c if c % 2 == 0 else c + 1
+        assert fp8.e4m3_encode(mid) == even, c
+        assert fp8.e4m3_encode(np.nextafter(mid, np.float32(0))) == c
+        assert fp8.e4m3_encode(np.nextafter(mid, np.float32(1000))) == c + 1
+        assert fp8.e4m3_encode(-mid) == 0x80 | even
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    assert np.array_equal(fp8.e4m3_encode(fp8.e4m3_value(codes).astype(np.float32)), codes)
+    with pytest.raises(ValueError):
+        fp8.e4m3_encode(np.float32(449.0))
+
+
+def bf16_bits(x):
+    return (np.asarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_pin_quantise_divides_and_clamps():
+    x = bf16_bits([3.0, -3.0, 1000.0, -1000.0, 0.0, 1.0 / 1024])
+    # dividing by 0.5 doubles: 3 -> 6 (a multiply would give 1.5)
+    assert list(fp8.quantise(x, 0.5)) == [int(fp8.e4m3_encode(np.float32(6.0))),
+                                          int(fp8.e4m3_encode(np.float32(-6.0))),
+                                          0x7E, 0xFE, 0x00,
+                                          int(fp8.e4m3_encode(np.float32(1.0 / 512)))]
+    assert fp8.e4m3_value(fp8.quantise(bf16_bits([6.0]), 2.0))[0] == 3.0
+    # a non-power-of-two scale: the result is the E4M3 value nearest to the
+    # correctly rounded float32 quotient (here 1/3 * 3 rounds back to 1)
+    third = np.float32(1.0) / np.float32(3.0)
+    assert fp8.quantise(bf16_bits([1.0]), 1.0 / 3.0) == fp8.e4m3_encode(np.float32(1.0) / third)
+
+
+def test_pin_append_matches_byte_copy():
+    """Quantised append = quantise, then the C oracle's row copy into the
+    same slots (codes carried in uint16 rows)."""
+    rng = np.random.default_rng(5)
+    nb, bs, hkv, d, t = 6, 16, 2, 128, 40
+    k_new = bf16_bits(rng.standard_normal((t, hkv, d)))
+    v_new = bf16_bits(rng.standard_normal((t, hkv, d)))
+    slots = rng.permutation(nb * bs)[:t].astype(np.int64)
+    slots[::7] = -1
+    k0 = rng.integers(0, 256, size=(nb, bs, hkv, d), dtype=np.uint8)
+    v0 = rng.integers(0, 256, size=(nb, bs, hkv, d), dtype=np.uint8)
+    kc, vc = fp8.kv_append_fp8(k_new, v_new, slots, k0, v0, 0.25, 0.125)
+    kq = fp8.quantise(k_new, 0.25).astype(np.uint16)
+    vq = fp8.quantise(v_new, 0.125).astype(np.uint16)
+    ka, va = oracle.kv_append(kq, vq, slots, k0.astype(np.uint16), v0.astype(np.uint16))
+    assert np.array_equal(kc, ka.astype(np.uint8)) and np.array_equal(vc, va.astype(np.uint8))
+
+
+@pytest.mark.parametrize("k_scale,v_scale", [(1.0, 1.0), (0.125, 4.0)])
+def test_pin_decode_against_bf16_oracle(k_scale, v_scale):
+    """Every E4M3 value is a bf16 value, so pools holding the codes' values as
+    bf16 give the C oracle's attention over the same keys; power-of-two
+    scales fold exactly into the score scale and the output."""
+    rng = np.random.default_rng(9)
+    b, hq, hkv, d, bs, nb = 5, 8, 2, 128, 16, 40
+    ctx = np.array([1, 17, 64, 100, 0], dtype=np.int32)
+    kc = rng.integers(0, 256, size=(nb, bs, hkv, d), dtype=np.uint8)
+    vc = rng.integers(0, 256, size=(nb, bs, hkv, d), dtype=np.uint8)
+    for c in (kc, vc):
+        c[c == 0x7F] = 0x3F
+        c[c == 0xFF] = 0xBF
+    # keep scores moderate: clearing bit 5 leaves exponent fields 0-3 and
+    # 8-11, so |value| < 32 (and no NaN code, which needs bit 5)
+    kc &= 0xDF
+    vc &= 0xDF
+    bt = rng.permutation(nb)[: b * 8].reshape(b, 8).astype(np.int32)
+    q = bf16_bits(rng.standard_normal((b, hq, d)) * 0.3)
+    scale = 2.0 ** -4
+    got = fp8.paged_decode_fp8(q, kc, vc, k_scale, v_scale, bt, ctx, scale)
+    kb = bf16_bits(fp8.e4m3_value(kc).astype(np.float32))
+    vb = bf16_bits(fp8.e4m3_value(vc).astype(np.float32))
+    ref = oracle.paged_attention(q, kb, vb, bt, ctx, scale * k_scale) * v_scale
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+    assert np.all(got[4] == 0.0)
