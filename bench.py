@@ -79,6 +79,10 @@ TRAFFIC_SPEC = {
                                 "sources": ["paged_kv_cache_98_amd/csrc/prefill.hip",
                                             "paged_kv_cache_98_amd/csrc/pkv_device.h"],
                                 "args": "--workload prefill_chunks"},
+    "llama8b_decode_b64_fp8": {"kernels": ["decode_streamk_kernel", "decode_merge_kernel"],
+                               "sources": ["paged_kv_cache_98_amd/csrc/decode.hip",
+                                           "paged_kv_cache_98_amd/csrc/pkv_device.h"],
+                               "args": "--workload llama8b_decode_fp8"},
     "cow_copy_4096x32k": {"kernels": ["copy_blocks_kernel"],
                           "sources": ["paged_kv_cache_98_amd/csrc/kv_append.hip"],
                           "args": "--workload cow_copy"},
@@ -252,6 +256,8 @@ def workload_by_name(name):
         "llama70b_decode_bs16": lambda: W.llama70b_decode(block_size=16),
         "llama70b_decode_bs32": lambda: W.llama70b_decode(block_size=32),
         "tiny_decode": lambda: W.tiny_decode(),
+        # the 8B-shaped batch over an FP8 (E4M3) cache
+        "llama8b_decode_fp8": lambda: W.llama8b_decode(),
         # chunked prefill: the 4 x 512-query chunks alone, then with the 128
         # decodes riding along in the same call
         "prefill_chunks": lambda: W.mixed_prefill(num_decodes=0),
@@ -281,6 +287,35 @@ def cpu_baseline(batch, w, reps=2):
             "sample": f"whole {w.name} batch ({w.num_seqs} seqs, sum ctx {sum(w.context_lens)}), "
                       f"fp64 C + OpenMP, best of {reps}: {t:.3f} s per batch "
                       f"({w.num_seqs / t:.2f} seq-steps/s)"}
+
+
+def cpu_baseline_fp8(batch, w, seqs=8):
+    """The fp64 FP8-cache oracle (numpy, one process), as it stands, on the
+    first `seqs` sequences of the batch (host copies of their blocks)."""
+    import numpy as np
+    import torch
+    from oracle import fp8
+    from paged_kv_cache_98_amd import workloads as W
+    bt = batch.block_table.cpu()
+    ctx = list(w.context_lens)[:seqs]
+    need = [-(-c // w.block_size) for c in ctx]
+    ids = torch.cat([bt[i, :need[i]] for i in range(seqs)]).to(torch.int64)
+    kc = batch.k_cache.index_select(0, ids.to(batch.k_cache.device)).cpu().numpy()
+    vc = batch.v_cache.index_select(0, ids.to(batch.v_cache.device)).cpu().numpy()
+    table = np.full((seqs, max(need)), -1, dtype=np.int32)
+    base = 0
+    for i in range(seqs):
+        table[i, :need[i]] = np.arange(base, base + need[i])
+        base += need[i]
+    q = batch.q[:seqs].cpu().view(torch.int16).numpy().view(np.uint16)
+    t0 = time.perf_counter()
+    fp8.paged_decode_fp8(q, kc, vc, W.FP8_SCALE, W.FP8_SCALE, table, np.array(ctx, np.int32),
+                         w.scale)
+    t = time.perf_counter() - t0
+    kv_bytes = sum(ctx) * w.kv_token_bytes() // 2
+    return {"value": round(kv_bytes / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {seqs} sequences of the batch (sum ctx {sum(ctx)}), fp64 numpy: "
+                      f"{t:.3f} s ({seqs / t:.2f} seq-steps/s)"}
 
 
 def main():
@@ -328,8 +363,15 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = workload_by_name(args.workload)
-    print(f"[bench] workload {w.describe()}", file=sys.stderr, flush=True)
+    kv_fp8 = args.workload.endswith("_fp8")
+    wname = w.name + ("_fp8" if kv_fp8 else "")
+    print(f"[bench] workload {w.describe()}{' FP8 KV' if kv_fp8 else ''}", file=sys.stderr,
+          flush=True)
     b = W.materialize(w, device=dev, poison=False)
+    if kv_fp8:
+        # E4M3 code pools made by torch's float8 cast; the bf16 pools go
+        b.k_cache, b.v_cache = W.fp8_pools(b)
+        torch.cuda.empty_cache()
     ws_bytes = pkv.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads,
                                           w.max_context_len)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
@@ -340,7 +382,12 @@ def main():
         out = torch.empty((w.total_q, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
 
     def attend():
-        if w.is_decode:
+        if kv_fp8:
+            pkv.paged_decode_attn_fp8(b.q, b.k_cache, b.v_cache, W.FP8_SCALE, W.FP8_SCALE,
+                                      b.block_table, b.context_lens, w.scale,
+                                      max_context_len=w.max_context_len, out=out, workspace=ws,
+                                      stream=stream)
+        elif w.is_decode:
             pkv.paged_decode_attn(b.q, b.k_cache, b.v_cache, b.block_table, b.context_lens,
                                   w.scale, max_context_len=w.max_context_len, out=out,
                                   workspace=ws, stream=stream)
@@ -352,7 +399,11 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        pkv.kv_append(b.k_new, b.v_new, b.slot_mapping, b.k_cache, b.v_cache, stream=stream)
+        if kv_fp8:
+            pkv.kv_append_fp8(b.k_new, b.v_new, b.slot_mapping, b.k_cache, b.v_cache,
+                              W.FP8_SCALE, W.FP8_SCALE, stream=stream)
+        else:
+            pkv.kv_append(b.k_new, b.v_new, b.slot_mapping, b.k_cache, b.v_cache, stream=stream)
         if ev is not None:
             ev[1].record(stream)
         attend()
@@ -388,7 +439,8 @@ def main():
 
     append_ms = [e[0].elapsed_time(e[1]) for e in evs]
     decode_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    kv_bytes = sum(w.context_lens) * w.kv_token_bytes()
+    # bytes a decode must read: one byte per value in an FP8 cache
+    kv_bytes = sum(w.context_lens) * w.kv_token_bytes() // (2 if kv_fp8 else 1)
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     dec_avg = statistics.mean(decode_ms)
     achieved = kv_bytes / (dec_avg * 1e-3) / 1e9
@@ -428,7 +480,9 @@ def main():
         return
 
     rec = {
-        "metric": "paged decode attn: achieved KV HBM GB/s (% of MI355X peak) + seq-steps/s",
+        "metric": ("paged decode attn over an FP8 (E4M3) KV cache: achieved KV HBM GB/s + "
+                   "seq-steps/s" if kv_fp8 else
+                   "paged decode attn: achieved KV HBM GB/s (% of MI355X peak) + seq-steps/s"),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -438,9 +492,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3 KV, bf16 q" if kv_fp8 else "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
+        "config": {"workload": wname, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "sum_context": sum(w.context_lens),
                    "max_context": w.max_context_len, "num_blocks": w.num_blocks,
@@ -452,12 +506,12 @@ def main():
                        "paged_decode_attn": round(dec_avg * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": hbm_traffic(w.name),
+                     "traffic": hbm_traffic(wname),
                      "kernel": "paged_decode_attn (stream-K decode + merge kernels)",
                      "algorithmic_bytes_per_launch": kv_bytes},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(b, w)
+        rec["cpu_baseline"] = cpu_baseline_fp8(b, w) if kv_fp8 else cpu_baseline(b, w)
     print(json.dumps(rec), flush=True)
 
 

@@ -73,7 +73,8 @@ enum pkv_status {
     PKV_ERR_ALIGN = -6,       /* a bf16 array is not 16-byte aligned */
     PKV_ERR_NO_MEMORY = -7,   /* block manager: too few free blocks; nothing changed */
     PKV_ERR_STATE = -8,       /* block manager: unknown or already existing sequence id */
-    PKV_ERR_HOST_ALLOC = -9   /* block manager: host memory ran out; nothing changed */
+    PKV_ERR_HOST_ALLOC = -9,  /* block manager: host memory ran out; nothing changed */
+    PKV_ERR_VALUE = -10       /* an FP8 cache scale is not finite and positive */
 };
 
 enum pkv_out_dtype {
@@ -145,6 +146,48 @@ int pkv_paged_decode_attn(void *out, int out_dtype, const void *q, const void *k
                           int max_context_len, int num_seqs, int num_q_heads,
                           int num_kv_heads, int head_dim, int block_size, float scale,
                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * FP8 KV cache ("让 Agent 跑得快：LLM 推理服务", section 四, FP8 量化: one byte
+ * per value, half of bf16, so the bandwidth-bound decode moves half the
+ * bytes; "LLM推理工程实战", section 5.3, KV Cache量化: the cache itself stored
+ * quantised, as vLLM's kv_cache_dtype=fp8).
+ *
+ * Format: OCP FP8 E4M3 codes (sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits, subnormals m * 2^-9, no infinities, S.1111.111 = NaN, largest
+ * finite 448), one byte per value, in pools laid out exactly like the bf16
+ * ones: [num_blocks][block_size][num_kv_heads][head_dim] uint8.  The cache
+ * has one scale for K and one for V, chosen by the caller (finite, > 0):
+ * the value a code stands for is E4M3(code) * scale.
+ */
+
+/*
+ * kv_append_fp8 -- quantise new tokens' K and V rows into their slots.
+ * Arguments as pkv_kv_append, except that k_cache / v_cache are the FP8
+ * pools and k_scale / v_scale their scales.  Each bf16 value x is stored as
+ * the E4M3 code nearest to x / scale (one correctly rounded binary32
+ * division), clamped to +-448, ties to the even code.  Inputs must be
+ * finite.  PKV_ERR_VALUE for a scale that is not finite and positive.
+ */
+int pkv_kv_append_fp8(const void *k_new, const void *v_new, const int64_t *slot_mapping,
+                      int64_t num_tokens, void *k_cache, void *v_cache, int64_t num_blocks,
+                      int block_size, int num_kv_heads, int head_dim, float k_scale,
+                      float v_scale, void *stream);
+
+/*
+ * paged_decode_attn_fp8 -- pkv_paged_decode_attn over FP8 pools:
+ *   out[i, h, :] = sum_t softmax_t(scale * <q[i,h], k_scale * Kc_i[t]>) v_scale * Vc_i[t]
+ * with Kc, Vc the E4M3 values of the codes.  Same arguments, workspace and
+ * limits as pkv_paged_decode_attn, plus the two scales.  The codes are
+ * widened in registers (K to bf16 pairs, exactly; V to fp32); accumulation
+ * is fp32.  Codes of tokens past a sequence's length are never used.
+ */
+int pkv_paged_decode_attn_fp8(void *out, int out_dtype, const void *q, const void *k_cache,
+                              const void *v_cache, float k_scale, float v_scale,
+                              const int32_t *block_table, int max_blocks_per_seq,
+                              const int32_t *context_lens, int max_context_len, int num_seqs,
+                              int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                              float scale, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Workspace needed by pkv_paged_prefill_attn (bytes, >= 0): the decode

@@ -29,12 +29,13 @@ PKV_ERR_ALIGN = -6
 PKV_ERR_NO_MEMORY = -7
 PKV_ERR_STATE = -8
 PKV_ERR_HOST_ALLOC = -9
+PKV_ERR_VALUE = -10
 PKV_OUT_F32 = 0
 PKV_OUT_BF16 = 1
 
 EXPORTED = ("pkv_status_string", "pkv_version", "pkv_kv_append", "pkv_decode_workspace_bytes",
             "pkv_paged_decode_attn", "pkv_prefill_workspace_bytes", "pkv_paged_prefill_attn",
-            "pkv_copy_blocks", "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free",
+            "pkv_kv_append_fp8", "pkv_paged_decode_attn_fp8", "pkv_copy_blocks", "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free",
             "pkv_bm_allocate", "pkv_bm_free", "pkv_bm_fork", "pkv_bm_append", "pkv_bm_append_batch",
             "pkv_bm_seq_info",
             "pkv_bm_refcount", "pkv_bm_block_table")
@@ -89,6 +90,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_paged_prefill_attn.argtypes = [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
                                            _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                            _vp, _sz, _vp]
+    lib.pkv_kv_append_fp8.restype = _i32
+    lib.pkv_kv_append_fp8.argtypes = [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _f32,
+                                      _f32, _vp]
+    lib.pkv_paged_decode_attn_fp8.restype = _i32
+    lib.pkv_paged_decode_attn_fp8.argtypes = [_vp, _i32, _vp, _vp, _vp, _f32, _f32, _vp, _i32, _vp,
+                                              _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz,
+                                              _vp]
     lib.pkv_copy_blocks.restype = _i32
     lib.pkv_copy_blocks.argtypes = [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _i64, _vp]
     lib.pkv_bm_create.restype = _vp
@@ -168,6 +176,55 @@ def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tens
                              _dev(k_cache, "k_cache", torch.bfloat16),
                              _dev(v_cache, "v_cache", torch.bfloat16), nb, bs, hkv, d,
                              _stream(stream)))
+
+
+def kv_append_fp8(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                  k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: float, v_scale: float,
+                  stream=None) -> None:
+    """pkv_kv_append_fp8: quantise k_new/v_new [T, Hkv, D] (bf16) into the FP8
+    pools [NB, bs, Hkv, D] (uint8 E4M3 codes) at slot_mapping [T]."""
+    lib = load_library()
+    nb, bs, hkv, d = k_cache.shape
+    t = slot_mapping.shape[0]
+    if k_new.shape != (t, hkv, d) or v_new.shape != k_new.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between new rows, slots and pools")
+    _check(lib.pkv_kv_append_fp8(_dev(k_new, "k_new", torch.bfloat16),
+                                 _dev(v_new, "v_new", torch.bfloat16),
+                                 _dev(slot_mapping, "slot_mapping", torch.int64), t,
+                                 _dev(k_cache, "k_cache", torch.uint8),
+                                 _dev(v_cache, "v_cache", torch.uint8), nb, bs, hkv, d,
+                                 float(k_scale), float(v_scale), _stream(stream)))
+
+
+def paged_decode_attn_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          k_scale: float, v_scale: float, block_table: torch.Tensor,
+                          context_lens: torch.Tensor, scale: float,
+                          max_context_len: Optional[int] = None,
+                          out: Optional[torch.Tensor] = None, out_dtype=torch.float32,
+                          workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """pkv_paged_decode_attn_fp8: q [B, Hq, D] bf16 over FP8 pools (uint8
+    E4M3 codes, values code * k_scale / v_scale) -> out [B, Hq, D]."""
+    lib = load_library()
+    b, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if d2 != d or block_table.dim() != 2 or block_table.shape[0] != b:
+        raise ValueError("shape mismatch")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if b else 0
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=out_dtype, device=q.device)
+    need = lib.pkv_decode_workspace_bytes(b, hq, hkv, d, max_context_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pkv_paged_decode_attn_fp8(
+        _dev(out, "out"), _out_code(out.dtype), _dev(q, "q", torch.bfloat16),
+        _dev(k_cache, "k_cache", torch.uint8), _dev(v_cache, "v_cache", torch.uint8),
+        float(k_scale), float(v_scale), _dev(block_table, "block_table", torch.int32),
+        block_table.shape[1], _dev(context_lens, "context_lens", torch.int32), max_context_len,
+        b, hq, hkv, d, bs, float(scale), ws_ptr, ws_len, _stream(stream)))
+    return out
 
 
 def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,

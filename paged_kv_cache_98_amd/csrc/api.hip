@@ -21,6 +21,9 @@ constexpr int kMaxDecodeKvHeads = 16;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// A cache scale: finite and positive.
+bool valid_scale(float s) { return s > 0.0f && s <= 3.402823466e38f; }
+
 bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -59,6 +62,7 @@ const char* pkv_status_string(int status) {
         case PKV_ERR_NO_MEMORY: return "not enough free KV blocks";
         case PKV_ERR_STATE: return "unknown or already existing sequence id";
         case PKV_ERR_HOST_ALLOC: return "host memory allocation failed";
+        case PKV_ERR_VALUE: return "a scale is not finite and positive";
         default: return "unknown status";
     }
 }
@@ -112,17 +116,22 @@ size_t pkv_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_head
                                        max_context_len);
 }
 
-int pkv_paged_decode_attn(void* out, int out_dtype, const void* q, const void* k_cache,
-                          const void* v_cache, const int32_t* block_table,
-                          int max_blocks_per_seq, const int32_t* context_lens,
-                          int max_context_len, int num_seqs, int num_q_heads, int num_kv_heads,
-                          int head_dim, int block_size, float scale, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and launch shared by the bf16 and FP8 decode calls.
+int decode_call(void* out, int out_dtype, const void* q, const void* k_cache, const void* v_cache,
+                bool kv_fp8, float k_scale, float v_scale, const int32_t* block_table,
+                int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
+                int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                float scale, void* workspace, size_t workspace_bytes, void* stream) {
     int st = check_attention_shape(max_blocks_per_seq, max_context_len, num_seqs, num_q_heads,
                                    num_kv_heads, head_dim, block_size, out_dtype);
     if (st != PKV_OK) return st;
     if (num_seqs > kMaxDecodeSeqs) return PKV_ERR_UNSUPPORTED;
     if (num_kv_heads > 8 && num_kv_heads != kMaxDecodeKvHeads) return PKV_ERR_UNSUPPORTED;
+    if (kv_fp8 && !(valid_scale(k_scale) && valid_scale(v_scale))) return PKV_ERR_VALUE;
     if (num_seqs == 0) return PKV_OK;
     if (!out || !q || !k_cache || !v_cache || !block_table || !context_lens) return PKV_ERR_NULL;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
@@ -136,8 +145,10 @@ int pkv_paged_decode_attn(void* out, int out_dtype, const void* q, const void* k
     a.out = out;
     a.out_bf16 = out_dtype == PKV_OUT_BF16;
     a.q = static_cast<const uint16_t*>(q);
-    a.k_cache = static_cast<const uint16_t*>(k_cache);
-    a.v_cache = static_cast<const uint16_t*>(v_cache);
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.kv_fp8 = kv_fp8;
+    a.out_scale = kv_fp8 ? v_scale : 1.0f;
     a.block_table = block_table;
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.context_lens = context_lens;
@@ -147,12 +158,66 @@ int pkv_paged_decode_attn(void* out, int out_dtype, const void* q, const void* k
     a.num_kv_heads = num_kv_heads;
     a.block_size = block_size;
     a.scale_log2 = scale * 1.4426950408889634f;
+    if (kv_fp8) a.scale_log2 *= k_scale;
     a.cum = static_cast<int32_t*>(workspace);
     a.records = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                          align_up((size_t)(num_seqs + 1) * sizeof(int32_t), 256));
     a.max_workers = pkv::decode_max_workers(num_seqs, max_context_len);
     a.cu_q_lens = nullptr;
     return to_status(pkv::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_decode_attn(void* out, int out_dtype, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* block_table,
+                          int max_blocks_per_seq, const int32_t* context_lens,
+                          int max_context_len, int num_seqs, int num_q_heads, int num_kv_heads,
+                          int head_dim, int block_size, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    return decode_call(out, out_dtype, q, k_cache, v_cache, false, 1.0f, 1.0f, block_table,
+                       max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
+                       num_kv_heads, head_dim, block_size, scale, workspace, workspace_bytes,
+                       stream);
+}
+
+int pkv_paged_decode_attn_fp8(void* out, int out_dtype, const void* q, const void* k_cache,
+                              const void* v_cache, float k_scale, float v_scale,
+                              const int32_t* block_table, int max_blocks_per_seq,
+                              const int32_t* context_lens, int max_context_len, int num_seqs,
+                              int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                              float scale, void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_call(out, out_dtype, q, k_cache, v_cache, true, k_scale, v_scale, block_table,
+                       max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
+                       num_kv_heads, head_dim, block_size, scale, workspace, workspace_bytes,
+                       stream);
+}
+
+int pkv_kv_append_fp8(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                      int64_t num_tokens, void* k_cache, void* v_cache, int64_t num_blocks,
+                      int block_size, int num_kv_heads, int head_dim, float k_scale,
+                      float v_scale, void* stream) {
+    if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0) return PKV_ERR_SHAPE;
+    if (head_dim != pkv::kHeadDim) return PKV_ERR_UNSUPPORTED;
+    if (block_size != 16 && block_size != 32) return PKV_ERR_UNSUPPORTED;
+    if (!(valid_scale(k_scale) && valid_scale(v_scale))) return PKV_ERR_VALUE;
+    if (num_tokens == 0) return PKV_OK;
+    if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PKV_ERR_NULL;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+        return PKV_ERR_ALIGN;
+    pkv::AppendFp8Args a;
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.v_new = static_cast<const uint16_t*>(v_new);
+    a.slot_mapping = slot_mapping;
+    a.num_tokens = num_tokens;
+    a.k_cache = static_cast<uint8_t*>(k_cache);
+    a.v_cache = static_cast<uint8_t*>(v_cache);
+    a.row_elems = num_kv_heads * head_dim;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    return to_status(pkv::launch_kv_append_fp8(a, static_cast<hipStream_t>(stream)));
 }
 
 size_t pkv_prefill_workspace_bytes(int num_seqs, int num_q_tokens, int num_q_heads, int head_dim,

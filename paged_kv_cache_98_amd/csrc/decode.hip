@@ -43,27 +43,75 @@ namespace pkv {
 
 namespace {
 
-constexpr int kLoads = kTileTokens / 4;  // 128-bit loads per lane per tile (K or V)
+constexpr int kLoads = kTileTokens / 4;  // loads per lane per tile (K or V)
 
+// How the pools store a value.  A lane's share of one token row of one head
+// is always eight values (dims 8c .. 8c + 7): a 16-byte word of bf16, or an
+// 8-byte word of FP8 codes.
+//   * K comes out as four bf16 pairs for the dot2 instructions (E4M3 to
+//     bf16 is exact: every E4M3 value is a bf16 value);
+//   * V comes out as eight floats.
+// The FP8 cache's two scales are applied outside the tile loop: k_scale
+// inside the score scale, v_scale on the finished output.
+struct KvBf16 {
+    static constexpr int kElemBytes = 2;
+    using Word = uint4;
+    static __device__ __forceinline__ Word load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    }
+    static __device__ __forceinline__ uint4 k_pairs(const Word& w) { return w; }
+    static __device__ __forceinline__ void v_floats(const Word& w, float (&v)[8]) {
+        v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+        v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+        v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
+        v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+    }
+};
+
+// FP8 codes in the OCP E4M3 format, decoded by the hardware conversions.
+struct KvFp8 {
+    static constexpr int kElemBytes = 1;
+    using Word = uint2;
+    static __device__ __forceinline__ Word load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    }
+    template <bool HIGH>  // codes 2, 3 of the word instead of 0, 1
+    static __device__ __forceinline__ uint32_t pair(uint32_t codes) {
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(
+                                                (int)codes, 1.0f, HIGH));
+    }
+    static __device__ __forceinline__ uint4 k_pairs(const Word& w) {
+        return make_uint4(pair<false>(w.x), pair<true>(w.x), pair<false>(w.y), pair<true>(w.y));
+    }
+    static __device__ __forceinline__ void v_floats(const Word& w, float (&v)[8]) {
+        const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
+        const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+        const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
+        const auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+        v[0] = a[0]; v[1] = a[1]; v[2] = b[0]; v[3] = b[1];
+        v[4] = c[0]; v[5] = c[1]; v[6] = d[0]; v[7] = d[1];
+    }
+};
+
+template <typename KV>
 struct Tile {
-    uint4 k[kLoads];
-    uint4 v[kLoads];
+    typename KV::Word k[kLoads];
+    typename KV::Word v[kLoads];
 };
 
 // Loads one tile: `kt` / `vt` address the tile's first row for this KV head
 // in the K / V pool, `voff[i]` is this lane's byte offset of load group i
 // (tokens 4i + row, dims 8c .. 8c + 7): buffer loads with a scalar base and
 // a 32-bit lane offset, so no per-lane 64-bit addresses are kept.
-__device__ __forceinline__ void load_tile(Tile& t, const char* kt, const char* vt,
+template <typename KV>
+__device__ __forceinline__ void load_tile(Tile<KV>& t, const char* kt, const char* vt,
                                           const uint32_t (&voff)[kLoads]) {
     const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kt);
     const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vt);
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i)
-        t.k[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, voff[i], 0, 0));
+    for (int i = 0; i < kLoads; ++i) t.k[i] = KV::load(rk, voff[i]);
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i)
-        t.v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff[i], 0, 0));
+    for (int i = 0; i < kLoads; ++i) t.v[i] = KV::load(rv, voff[i]);
 }
 
 template <int G>
@@ -78,18 +126,19 @@ struct State {
 // number of valid tokens from the start of this tile (>= 16 for a full one).
 // Raw scores are maximised unscaled (the scale is >= 0 after the sign of q
 // absorbed a negative one) and scaled inside the exponent's FMA.
-template <int G, bool PARTIAL>
-__device__ __forceinline__ void process_tile(State<G>& st, const Tile& t, const uint4 (&qv)[G],
+template <typename KV, int G, bool PARTIAL>
+__device__ __forceinline__ void process_tile(State<G>& st, const Tile<KV>& t, const uint4 (&qv)[G],
                                              float c, int row, int ntok_left) {
     float s[kLoads][G];
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
+        const uint4 k = KV::k_pairs(t.k[i]);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            float d = dot2_bf16(t.k[i].x, qv[g].x, 0.0f);
-            d = dot2_bf16(t.k[i].y, qv[g].y, d);
-            d = dot2_bf16(t.k[i].z, qv[g].z, d);
-            d = dot2_bf16(t.k[i].w, qv[g].w, d);
+            float d = dot2_bf16(k.x, qv[g].x, 0.0f);
+            d = dot2_bf16(k.y, qv[g].y, d);
+            d = dot2_bf16(k.z, qv[g].z, d);
+            d = dot2_bf16(k.w, qv[g].w, d);
             s[i][g] = row_sum16(d);
         }
         if (PARTIAL) {
@@ -131,10 +180,7 @@ __device__ __forceinline__ void process_tile(State<G>& st, const Tile& t, const 
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
         float v[8];
-        v[0] = bf16_lo(t.v[i].x); v[1] = bf16_hi(t.v[i].x);
-        v[2] = bf16_lo(t.v[i].y); v[3] = bf16_hi(t.v[i].y);
-        v[4] = bf16_lo(t.v[i].z); v[5] = bf16_hi(t.v[i].z);
-        v[6] = bf16_lo(t.v[i].w); v[7] = bf16_hi(t.v[i].w);
+        KV::v_floats(t.v[i], v);
         if (PARTIAL) {
             // A masked token has p = 0, but its pool slot may hold anything
             // (NaN included): zero the value so 0 * v stays 0.
@@ -253,14 +299,15 @@ __device__ __forceinline__ size_t tile_bytes(IdWindow& ids, int tile, size_t row
 // walk that range together, so each physical block's K rows of all heads
 // (bs * Hkv * D bf16, contiguous) are fetched at the same time.
 // Records: [W][2][num_q_heads][kRecStride] floats.
-template <int BS, int G, bool OUT_BF16>
+template <typename KV, int BS, int G, bool OUT_BF16>
 __global__ void __launch_bounds__(64 * max_waves_per_worker<G>())
 decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* __restrict__ cum_out,
-                      const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
-                      const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
+                      const uint16_t* __restrict__ q, const void* __restrict__ k_cache,
+                      const void* __restrict__ v_cache, const int32_t* __restrict__ block_table,
                       int max_blocks_per_seq, const int32_t* __restrict__ context_lens,
                       int max_context_len, int num_seqs, int num_q_heads, int num_kv_heads,
-                      float scale_log2, int num_workers, const int32_t* __restrict__ cu_q_lens) {
+                      float scale_log2, float out_scale, int num_workers,
+                      const int32_t* __restrict__ cu_q_lens) {
     constexpr int D = kHeadDim;
     extern __shared__ int32_t s_cum[];  // s_cum[i] = tiles (per KV head) of sequences < i
     __shared__ int32_t s_part[max_waves_per_worker<G>()];  // the waves' tile totals
@@ -316,11 +363,11 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
 
     const uint32_t neg = scale_log2 < 0.0f ? 0x80008000u : 0u;
     const float c = fabsf(scale_log2);
-    const size_t row_bytes = (size_t)num_kv_heads * D * sizeof(uint16_t);
+    const size_t row_bytes = (size_t)num_kv_heads * D * KV::kElemBytes;
     uint32_t voff[kLoads];
 #pragma unroll
     for (int i = 0; i < kLoads; ++i)
-        voff[i] = (uint32_t)((4 * i + row) * row_bytes + ((size_t)kvh * D + col * 8) * sizeof(uint16_t));
+        voff[i] = (uint32_t)((4 * i + row) * row_bytes + ((size_t)kvh * D + col * 8) * KV::kElemBytes);
     const char* kbase = reinterpret_cast<const char*>(k_cache);
     const char* vbase = reinterpret_cast<const char*>(v_cache);
     bool first_piece = true;
@@ -368,17 +415,17 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
         // tile can be partial, and it is never inside the loop.
         const int n = ntile;
         const bool tail = piece_end == seg_t1 && (ctx % kTileTokens) != 0;
-        auto fetch = [&](Tile& x, int j) {
+        auto fetch = [&](Tile<KV>& x, int j) {
             const size_t o = tile_bytes<BS>(ids, tile0 + j, row_bytes, lane);
             load_tile(x, kbase + o, vbase + o, voff);
         };
-        auto finish = [&](const Tile& x, int j) {
+        auto finish = [&](const Tile<KV>& x, int j) {
             if (tail && j == n - 1)
-                process_tile<G, true>(st, x, qv, c, row, ctx - (tile0 + j) * kTileTokens);
+                process_tile<KV, G, true>(st, x, qv, c, row, ctx - (tile0 + j) * kTileTokens);
             else
-                process_tile<G, false>(st, x, qv, c, row, kTileTokens);
+                process_tile<KV, G, false>(st, x, qv, c, row, kTileTokens);
         };
-        Tile a, b;
+        Tile<KV> a, b;
         fetch(a, 0);
         if (n == 1) {
             finish(a, 0);
@@ -386,9 +433,9 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
             fetch(b, 1);
             int j = 0;
             for (; j + 3 < n; j += 2) {  // tiles j + 2 and j + 3 exist and are full
-                process_tile<G, false>(st, a, qv, c, row, kTileTokens);
+                process_tile<KV, G, false>(st, a, qv, c, row, kTileTokens);
                 fetch(a, j + 2);
-                process_tile<G, false>(st, b, qv, c, row, kTileTokens);
+                process_tile<KV, G, false>(st, b, qv, c, row, kTileTokens);
                 fetch(b, j + 3);
                 // Eight waves stream their heads with nothing else tying them
                 // together, and two share each SIMD: left alone they drift
@@ -400,10 +447,10 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
                 if (max_waves_per_worker<G>() == 8) __syncthreads();
             }
             // two or three tiles left: j (in a), j + 1 (in b), maybe j + 2
-            process_tile<G, false>(st, a, qv, c, row, kTileTokens);
+            process_tile<KV, G, false>(st, a, qv, c, row, kTileTokens);
             if (n - j == 3) {
                 fetch(a, j + 2);
-                process_tile<G, false>(st, b, qv, c, row, kTileTokens);
+                process_tile<KV, G, false>(st, b, qv, c, row, kTileTokens);
                 finish(a, j + 2);
             } else {
                 finish(b, j + 1);
@@ -439,7 +486,7 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
         for (int g = 0; g < G; ++g) {
             if ((g & 3) != row) continue;
             if (whole) {
-                const float inv = 1.0f / st.l[g];
+                const float inv = out_scale / st.l[g];
                 float o[8];
 #pragma unroll
                 for (int d = 0; d < 8; ++d) o[d] = st.acc[g][d] * inv;
@@ -469,7 +516,7 @@ __global__ void __launch_bounds__(256)
 decode_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
                     const int32_t* __restrict__ cum, const int32_t* __restrict__ context_lens,
                     int max_context_len, int num_seqs, int num_q_heads, int num_workers,
-                    const int32_t* __restrict__ cu_q_lens) {
+                    float out_scale, const int32_t* __restrict__ cu_q_lens) {
     constexpr int D = kHeadDim;
     const int lane = threadIdx.x & 63;
     const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -530,7 +577,7 @@ decode_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
             }
         }
     }
-    const float inv = 1.0f / L;
+    const float inv = out_scale / L;
     store1<OUT_BF16>(out, e, a0 * inv);
     store1<OUT_BF16>(out, e + 1, a1 * inv);
 }
@@ -562,9 +609,9 @@ hipError_t resident_blocks_per_cu(const void* kern, int threads, size_t lds, int
     return hipSuccess;
 }
 
-template <int BS, int G, bool OUT_BF16>
+template <typename KV, int BS, int G, bool OUT_BF16>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-    auto kern = decode_streamk_kernel<BS, G, OUT_BF16>;
+    auto kern = decode_streamk_kernel<KV, BS, G, OUT_BF16>;
     constexpr int kMax = max_waves_per_worker<G>();
     // head groups of kMax waves; the API admits 1..8 and 16 KV heads
     const int waves = a.num_kv_heads <= kMax ? a.num_kv_heads
@@ -581,35 +628,41 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     int64_t workers = resident / groups;
     if (workers > a.max_workers) workers = a.max_workers;
     if (workers < 1) workers = 1;
-    hipLaunchKernelGGL((decode_streamk_kernel<BS, G, OUT_BF16>), dim3((int)workers, groups), dim3(threads),
-                       lds, stream, a.out, a.records, a.cum, a.q, a.k_cache, a.v_cache,
-                       a.block_table, a.max_blocks_per_seq, a.context_lens, a.max_context_len,
-                       a.num_seqs, a.num_q_heads, a.num_kv_heads, a.scale_log2, (int)workers,
-                       a.cu_q_lens);
+    hipLaunchKernelGGL((decode_streamk_kernel<KV, BS, G, OUT_BF16>), dim3((int)workers, groups),
+                       dim3(threads), lds, stream, a.out, a.records, a.cum, a.q, a.k_cache,
+                       a.v_cache, a.block_table, a.max_blocks_per_seq, a.context_lens,
+                       a.max_context_len, a.num_seqs, a.num_q_heads, a.num_kv_heads, a.scale_log2,
+                       a.out_scale, (int)workers, a.cu_q_lens);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 mgrid((a.num_q_heads + 3) / 4, a.num_seqs);
     hipLaunchKernelGGL((decode_merge_kernel<OUT_BF16>), mgrid, dim3(256), 0, stream, a.out,
                        a.records, a.cum, a.context_lens, a.max_context_len, a.num_seqs,
-                       a.num_q_heads, (int)workers, a.cu_q_lens);
+                       a.num_q_heads, (int)workers, a.out_scale, a.cu_q_lens);
     return hipGetLastError();
 }
 
-template <int BS, int G>
+template <typename KV, int BS, int G>
 hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s) {
-    return a.out_bf16 ? launch_decode_t<BS, G, true>(a, s) : launch_decode_t<BS, G, false>(a, s);
+    return a.out_bf16 ? launch_decode_t<KV, BS, G, true>(a, s)
+                      : launch_decode_t<KV, BS, G, false>(a, s);
 }
 
-template <int BS>
+template <typename KV, int BS>
 hipError_t launch_decode_bs(const DecodeArgs& a, hipStream_t s) {
     switch (a.num_q_heads / a.num_kv_heads) {
-        case 1: return launch_decode_g<BS, 1>(a, s);
-        case 2: return launch_decode_g<BS, 2>(a, s);
-        case 4: return launch_decode_g<BS, 4>(a, s);
-        case 8: return launch_decode_g<BS, 8>(a, s);
-        case 16: return launch_decode_g<BS, 16>(a, s);
+        case 1: return launch_decode_g<KV, BS, 1>(a, s);
+        case 2: return launch_decode_g<KV, BS, 2>(a, s);
+        case 4: return launch_decode_g<KV, BS, 4>(a, s);
+        case 8: return launch_decode_g<KV, BS, 8>(a, s);
+        case 16: return launch_decode_g<KV, BS, 16>(a, s);
         default: return hipErrorInvalidValue;
     }
+}
+
+template <typename KV>
+hipError_t launch_decode_kv(const DecodeArgs& a, hipStream_t s) {
+    return a.block_size == 16 ? launch_decode_bs<KV, 16>(a, s) : launch_decode_bs<KV, 32>(a, s);
 }
 
 }  // namespace
@@ -630,7 +683,7 @@ size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, i
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-    return a.block_size == 16 ? launch_decode_bs<16>(a, stream) : launch_decode_bs<32>(a, stream);
+    return a.kv_fp8 ? launch_decode_kv<KvFp8>(a, stream) : launch_decode_kv<KvBf16>(a, stream);
 }
 
 }  // namespace pkv

@@ -9,6 +9,15 @@
 // of Hkv * D bf16 is Hkv * D / 8 words, so consecutive threads write
 // consecutive words of one row (coalesced).  Negative slots are skipped.
 //
+// The FP8 variant ("让 Agent 跑得快", section 四: one byte per value, half
+// the bytes of bf16; "LLM推理工程实战", section 5.3: the KV cache stored
+// quantised) writes OCP E4M3 codes: each value x becomes the E4M3 value
+// nearest to x / scale (one correctly rounded binary32 division, clamped to
+// +-448 first, since the hardware conversion rounds to nearest even but
+// turns magnitudes past 464 into NaN), with the cache's own scale for K and
+// for V.  A thread turns one 16-byte word (eight bf16) into one 8-byte word
+// of codes.
+//
 // Copy-on-write ("让 Agent 跑得快", section 二, "Copy-on-Write"): before a
 // sequence writes into a block it shares, the block is copied whole (every
 // row and head of K and V) to a fresh block; block b is the contiguous
@@ -33,6 +42,39 @@ kv_append_kernel(const uint4* __restrict__ k_new, const uint4* __restrict__ v_ne
         const int64_t dst = s * words_per_row + c;
         k_cache[dst] = k_new[w];
         v_cache[dst] = v_new[w];
+    }
+}
+
+constexpr float kE4m3Max = 448.0f;
+
+// Eight bf16 values -> eight E4M3 codes (byte i = value i).
+__device__ __forceinline__ uint2 quantise8(uint4 x, float scale) {
+    float y[8] = {bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y),
+                  bf16_lo(x.z), bf16_hi(x.z), bf16_lo(x.w), bf16_hi(x.w)};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(y[i] / scale, -kE4m3Max), kE4m3Max);
+    uint2 r;
+    r.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    r.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)r.x, true);
+    r.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+    r.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], (int)r.y, true);
+    return r;
+}
+
+__global__ void __launch_bounds__(256)
+kv_append_fp8_kernel(const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
+                     const int64_t* __restrict__ slot_mapping, int64_t num_words,
+                     uint2* __restrict__ k_cache, uint2* __restrict__ v_cache, int words_per_row,
+                     float k_scale, float v_scale) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < num_words; w += stride) {
+        const int64_t t = w / words_per_row;
+        const int64_t c = w - t * words_per_row;
+        const int64_t s = slot_mapping[t];
+        if (s < 0) continue;
+        const int64_t dst = s * words_per_row + c;
+        k_cache[dst] = quantise8(k_new[w], k_scale);
+        v_cache[dst] = quantise8(v_new[w], v_scale);
     }
 }
 
@@ -93,6 +135,19 @@ hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(copy_blocks_kernel, dim3(blocks), dim3(kCopyThreads), 0, stream,
                        reinterpret_cast<u32x4_t*>(a.k_cache), reinterpret_cast<u32x4_t*>(a.v_cache),
                        a.block_mapping, a.num_pairs, slices, a.num_blocks, block_words);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_append_fp8(const AppendFp8Args& a, hipStream_t stream) {
+    const int words_per_row = a.row_elems / 8;  // 16-byte words of bf16 in, 8-byte words out
+    const int64_t num_words = a.num_tokens * words_per_row;
+    if (num_words == 0) return hipSuccess;
+    const int64_t want = (num_words + 255) / 256;
+    const int blocks = (int)(want < 65536 ? want : 65536);
+    hipLaunchKernelGGL(kv_append_fp8_kernel, dim3(blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const uint4*>(a.k_new), reinterpret_cast<const uint4*>(a.v_new),
+                       a.slot_mapping, num_words, reinterpret_cast<uint2*>(a.k_cache),
+                       reinterpret_cast<uint2*>(a.v_cache), words_per_row, a.k_scale, a.v_scale);
     return hipGetLastError();
 }
 

@@ -19,6 +19,18 @@ struct AppendArgs {
     int row_elems;  // num_kv_heads * head_dim
 };
 
+struct AppendFp8Args {
+    const uint16_t* k_new;  // bf16
+    const uint16_t* v_new;
+    const int64_t* slot_mapping;
+    int64_t num_tokens;
+    uint8_t* k_cache;  // E4M3 codes
+    uint8_t* v_cache;
+    int row_elems;  // num_kv_heads * head_dim
+    float k_scale;
+    float v_scale;
+};
+
 struct CopyBlocksArgs {
     uint16_t* k_cache;
     uint16_t* v_cache;
@@ -32,8 +44,10 @@ struct DecodeArgs {
     void* out;
     bool out_bf16;
     const uint16_t* q;
-    const uint16_t* k_cache;
-    const uint16_t* v_cache;
+    const void* k_cache;  // bf16, or FP8 (E4M3) codes when kv_fp8
+    const void* v_cache;
+    bool kv_fp8 = false;
+    float out_scale = 1.0f;  // multiplies the output (the FP8 cache's v_scale)
     const int32_t* block_table;
     int max_blocks_per_seq;
     const int32_t* context_lens;
@@ -42,7 +56,7 @@ struct DecodeArgs {
     int num_q_heads;
     int num_kv_heads;
     int block_size;
-    float scale_log2;     // scale * log2(e)
+    float scale_log2;     // scale * log2(e) (times k_scale for an FP8 cache)
     int32_t* cum;         // workspace: [num_seqs + 1] tile prefix sums
     float* records;       // workspace: [max_workers][2][num_q_heads][head_dim + 4] partials
     int64_t max_workers;  // workers whose records fit the workspace
@@ -75,6 +89,7 @@ struct PrefillArgs {
 };
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_kv_append_fp8(const AppendFp8Args& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

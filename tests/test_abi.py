@@ -37,8 +37,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for s in (0, -1, -2, -3, -4, -5, -6):
-        assert binding.status_string(s)
+    for s in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10):
+        assert binding.status_string(s) != "unknown status"
     assert binding.status_string(-99) == "unknown status"
     assert lib.pkv_version() >= 100
 
@@ -137,6 +137,38 @@ def test_append_validation(lib):
     assert append(lib, hkv=0) == E.PKV_ERR_SHAPE
     assert append(lib, kn=MIS) == E.PKV_ERR_ALIGN
     assert append(lib, t=0, kn=None) == E.PKV_OK
+
+
+def decode_fp8(lib, **kw):
+    a = dict(out=P, out_dtype=0, q=P, k=P, v=P, ks=0.5, vs=0.25, bt=P, mb=8, cl=P, maxctx=100,
+             nseq=4, hq=8, hkv=2, d=128, bs=16, scale=0.1, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.pkv_paged_decode_attn_fp8(a["out"], a["out_dtype"], a["q"], a["k"], a["v"],
+                                         a["ks"], a["vs"], a["bt"], a["mb"], a["cl"], a["maxctx"],
+                                         a["nseq"], a["hq"], a["hkv"], a["d"], a["bs"], a["scale"],
+                                         a["ws"], a["wsb"], a["stream"])
+
+
+def test_fp8_validation(lib):
+    E = binding
+    inf, nan = float("inf"), float("nan")
+    for ks, vs in ((0.0, 1.0), (1.0, -2.0), (inf, 1.0), (1.0, nan)):
+        assert decode_fp8(lib, ks=ks, vs=vs) == E.PKV_ERR_VALUE
+        assert lib.pkv_kv_append_fp8(P, P, P, 5, P, P, 10, 16, 8, 128, ks, vs, None) == E.PKV_ERR_VALUE
+    assert decode_fp8(lib, q=None) == E.PKV_ERR_NULL
+    assert decode_fp8(lib, k=MIS) == E.PKV_ERR_ALIGN
+    assert decode_fp8(lib, d=64) == E.PKV_ERR_UNSUPPORTED
+    assert decode_fp8(lib, hq=6, hkv=4) == E.PKV_ERR_SHAPE
+    assert decode_fp8(lib, maxctx=2000, mb=200) == E.PKV_ERR_WORKSPACE
+    assert decode_fp8(lib, nseq=0, q=None) == E.PKV_OK
+    ap = lambda **kw: lib.pkv_kv_append_fp8(*[kw.get(n, v) for n, v in (
+        ("kn", P), ("vn", P), ("sm", P), ("t", 5), ("kc", P), ("vc", P), ("nb", 10), ("bs", 16),
+        ("hkv", 8), ("d", 128), ("ks", 1.0), ("vs", 1.0), ("stream", None))])
+    assert ap(sm=None) == E.PKV_ERR_NULL
+    assert ap(vc=MIS) == E.PKV_ERR_ALIGN
+    assert ap(bs=8) == E.PKV_ERR_UNSUPPORTED
+    assert ap(t=-1) == E.PKV_ERR_SHAPE
+    assert ap(t=0, kn=None) == E.PKV_OK
 
 
 def test_binding_refuses_cpu_tensors():

@@ -103,13 +103,11 @@ def test_decode_is_deterministic_and_permutation_invariant():
 
 
 def test_decode_workspace_garbage_reuse_and_graph_replay():
-    """Sequences shared by several workers are merged by whichever finishes
-    last, found through per-(sequence, KV head) arrival cells in the
-    workspace.  A workspace of random bytes, the same workspace reused, and
-    graph replays (each replay repeats the captured call's tag) all give the
-    same bits, within the oracle's bar."""
-    # enough tiles (3282) for more key ranges than resident workgroups, so
-    # ranges are claimed dynamically as well
+    """Sequences split over several workers leave partial records in the
+    workspace, which the merge kernel combines.  A workspace of random
+    bytes, the same workspace reused, and graph replays all give the same
+    bits, within the oracle's bar."""
+    # long sequences (3282 tiles in all) are split over many workers
     w = W.make_workload("ws", [8000, 17, 16000, 9000, 12500, 1, 7000], num_q_heads=32,
                         num_kv_heads=8, block_size=16, seed=2500)
     bc = W.materialize(w, logical=True, poison=True)

@@ -1,0 +1,169 @@
+"""GPU parity of the FP8 (E4M3) KV cache: the quantised append bit for bit
+against the oracle's quantiser, and decode attention over FP8 pools against
+the fp64 oracle on the same codes (codes made by torch's own float8 cast,
+never by this library)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import fp8
+from paged_kv_cache_98_amd import binding as pkv
+from paged_kv_cache_98_amd import workloads as W
+from tests.gpu_common import bf16_parity, parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+EDGE_CTX = [1, 15, 16, 17, 31, 32, 33, 100, 511, 512, 513, 1023, 1024, 1025, 2047, 3000]
+
+
+def bits16(t):
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def codes(t):
+    return t.detach().cpu().numpy()
+
+
+def run_fp8(q, kc, vc, bt, ctx, w, k_scale=W.FP8_SCALE, v_scale=W.FP8_SCALE, out_dtype=torch.float32):
+    return pkv.paged_decode_attn_fp8(q, kc, vc, k_scale, v_scale, bt, ctx, w.scale,
+                                     max_context_len=w.max_context_len, out_dtype=out_dtype)
+
+
+def oracle_fp8(b_cpu, kc, vc, k_scale=W.FP8_SCALE, v_scale=W.FP8_SCALE):
+    w = b_cpu.workload
+    return fp8.paged_decode_fp8(bits16(b_cpu.q), codes(kc), codes(vc), k_scale, v_scale,
+                                b_cpu.block_table.numpy(), b_cpu.context_lens.numpy(), w.scale)
+
+
+def edge_values(scale):
+    """bf16 values around E4M3 rounding points of x / scale: each code's value
+    and the midpoints to its neighbour (exact for power-of-two scales), the
+    clamp region and zeros."""
+    vals = fp8.e4m3_value(np.arange(127))
+    mids = (vals[:-1] + vals[1:]) / 2
+    xs = np.concatenate([vals, mids, [448.0, 460.0, 470.0, 1e4, 0.0]]) * scale
+    xs = np.concatenate([xs, -xs]).astype(np.float32)
+    return torch.from_numpy(xs).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("bs,hkv,k_scale,v_scale", [
+    (16, 8, 1.0, 2.0 ** -5), (32, 2, 0.0371, 0.113), (16, 1, 2.0 ** -6, 3.0e-3)])
+def test_kv_append_fp8_bit_exact(bs, hkv, k_scale, v_scale):
+    print(f"[fp8 append] bs={bs} hkv={hkv} scales={k_scale},{v_scale}", flush=True)
+    g = torch.Generator().manual_seed(bs * 10 + hkv)
+    nb, t, d = 48, 300, 128
+    mag = torch.exp2(torch.randint(-16, 12, (t, hkv, d), generator=g).float())
+    k_new = (torch.randn((t, hkv, d), generator=g) * mag).to(torch.bfloat16)
+    v_new = (torch.randn((t, hkv, d), generator=g) * mag.flip(0)).to(torch.bfloat16)
+    ev = edge_values(k_scale)
+    k_new.view(-1)[: ev.numel()] = ev
+    v_new.view(-1)[-ev.numel():] = edge_values(v_scale)
+    slots = torch.randperm(nb * bs, generator=g)[:t].to(torch.int64)
+    slots[::11] = -1
+    k0 = torch.randint(0, 256, (nb, bs, hkv, d), generator=g, dtype=torch.int32).to(torch.uint8)
+    v0 = torch.randint(0, 256, (nb, bs, hkv, d), generator=g, dtype=torch.int32).to(torch.uint8)
+    ref_k, ref_v = fp8.kv_append_fp8(bits16(k_new), bits16(v_new), slots.numpy(), codes(k0),
+                                     codes(v0), k_scale, v_scale)
+    kd, vd = k0.to(DEV), v0.to(DEV)
+    pkv.kv_append_fp8(k_new.to(DEV), v_new.to(DEV), slots.to(DEV), kd, vd, k_scale, v_scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes(kd), ref_k)
+    assert np.array_equal(codes(vd), ref_v)
+
+
+def test_decode_fp8_tiny():
+    w = W.tiny_decode()
+    bc = W.materialize(w, logical=True, poison=True)
+    kc, vc = W.fp8_pools(bc)
+    ref = oracle_fp8(bc, kc, vc)
+    b = bc.to(DEV)
+    out = run_fp8(b.q, kc.to(DEV), vc.to(DEV), b.block_table, b.context_lens, w)
+    torch.cuda.synchronize()
+    parity(out, ref, what="fp8 tiny")
+    parity(out, ref, max_abs=5e-5, rel_l2=2e-5, what="fp8 tiny (fp32-level)")
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("group", [1, 2, 4, 8, 16])
+def test_decode_fp8_groups_and_edges(bs, group):
+    hkv = 2
+    w = W.make_workload(f"fp8_edges_g{group}_bs{bs}", EDGE_CTX, num_q_heads=hkv * group,
+                        num_kv_heads=hkv, block_size=bs, seed=3000 + group + bs)
+    bc = W.materialize(w, logical=True, poison=True)
+    kc, vc = W.fp8_pools(bc)
+    b = bc.to(DEV)
+    out = run_fp8(b.q, kc.to(DEV), vc.to(DEV), b.block_table, b.context_lens, w)
+    torch.cuda.synchronize()
+    parity(out, oracle_fp8(bc, kc, vc), what=w.name)
+
+
+@pytest.mark.parametrize("hkv", [1, 8, 16])
+def test_decode_fp8_kv_heads_and_scales(hkv):
+    k_scale, v_scale = 0.0371, 0.113
+    w = W.make_workload(f"fp8_hkv{hkv}", [5, 700, 0, 1500], num_q_heads=hkv * 4,
+                        num_kv_heads=hkv, block_size=16, seed=3100 + hkv)
+    bc = W.materialize(w, logical=True, poison=True)
+    kc, vc = W.fp8_pools(bc, k_scale, v_scale)
+    b = bc.to(DEV)
+    out = run_fp8(b.q, kc.to(DEV), vc.to(DEV), b.block_table, b.context_lens, w, k_scale, v_scale)
+    torch.cuda.synchronize()
+    assert torch.all(out[2] == 0)
+    parity(out, oracle_fp8(bc, kc, vc, k_scale, v_scale), what=w.name)
+
+
+def test_decode_fp8_bf16_output_and_determinism():
+    w = W.llama8b_decode(batch=6, lo=100, hi=2500, seed=3200)
+    bc = W.materialize(w, logical=True, poison=True)
+    kc, vc = W.fp8_pools(bc)
+    b = bc.to(DEV)
+    kd, vd = kc.to(DEV), vc.to(DEV)
+    o16 = run_fp8(b.q, kd, vd, b.block_table, b.context_lens, w, out_dtype=torch.bfloat16)
+    o32 = run_fp8(b.q, kd, vd, b.block_table, b.context_lens, w)
+    o32b = run_fp8(b.q, kd, vd, b.block_table, b.context_lens, w)
+    torch.cuda.synchronize()
+    assert torch.equal(o32, o32b)
+    bf16_parity(o16, o32, oracle_fp8(bc, kc, vc), what="fp8 decode bf16 out")
+
+
+def test_fp8_append_then_decode():
+    """The current tokens are quantised into the cache on the GPU, then
+    decoded; the oracle quantises the same bf16 rows itself."""
+    w = W.llama8b_decode(batch=5, lo=40, hi=900, seed=3300)
+    bc = W.materialize(w, logical=True, poison=True)
+    kc, vc = W.fp8_pools(bc)
+    ref_k, ref_v = fp8.kv_append_fp8(bits16(bc.k_new), bits16(bc.v_new),
+                                     bc.slot_mapping.numpy(), codes(kc), codes(vc),
+                                     W.FP8_SCALE, W.FP8_SCALE)
+    ref = fp8.paged_decode_fp8(bits16(bc.q), ref_k, ref_v, W.FP8_SCALE, W.FP8_SCALE,
+                               bc.block_table.numpy(), bc.context_lens.numpy(), w.scale)
+    b = bc.to(DEV)
+    kd, vd = kc.to(DEV), vc.to(DEV)
+    pkv.kv_append_fp8(b.k_new, b.v_new, b.slot_mapping, kd, vd, W.FP8_SCALE, W.FP8_SCALE)
+    out = run_fp8(b.q, kd, vd, b.block_table, b.context_lens, w)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes(kd), ref_k) and np.array_equal(codes(vd), ref_v)
+    parity(out, ref, what="fp8 append + decode")
+
+
+def test_decode_fp8_full_8b_batch_sampled():
+    """The full 64-sequence 8B-shaped batch in the launch configuration the
+    benchmark times; sampled sequences checked against the oracle."""
+    w = W.llama8b_decode()
+    print(f"[fp8 full] {w.name}", flush=True)
+    b = W.materialize(w, device=DEV, poison=True)
+    kd, vd = W.fp8_pools(b)
+    out = run_fp8(b.q, kd, vd, b.block_table, b.context_lens, w)
+    torch.cuda.synchronize()
+    ctx = list(w.context_lens)
+    seqs = sorted({ctx.index(max(ctx)), ctx.index(min(ctx)), 0, 17, 42, 63})
+    bt = b.block_table.cpu()
+    for i in seqs:
+        n = ctx[i]
+        ids = bt[i, : -(-n // w.block_size)].to(torch.int64)
+        sub_k = codes(kd.index_select(0, ids.to(DEV)))
+        sub_v = codes(vd.index_select(0, ids.to(DEV)))
+        ref = fp8.paged_decode_fp8(bits16(b.q[i:i + 1]), sub_k, sub_v, W.FP8_SCALE, W.FP8_SCALE,
+                                   np.arange(len(ids), dtype=np.int32)[None, :],
+                                   np.array([n], dtype=np.int32), w.scale)
+        parity(out[i:i + 1], ref, what=f"fp8 full batch seq {i} (ctx {n})")
