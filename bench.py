@@ -261,6 +261,8 @@ def workload_by_name(name):
         # chunked prefill: the 4 x 512-query chunks alone, then with the 128
         # decodes riding along in the same call
         "prefill_chunks": lambda: W.mixed_prefill(num_decodes=0),
+        # speculative-decoding verification: 6 causal query rows per sequence
+        "spec_verify": lambda: W.spec_verify(),
         "mixed_prefill": lambda: W.mixed_prefill(),
     }
     if name not in table:
@@ -450,6 +452,33 @@ def main():
           f"{sorted(decode_ms)[(9 * len(decode_ms)) // 10] * 1e3:.1f}) | append avg "
           f"{statistics.mean(append_ms) * 1e3:.1f} us | decode KV {achieved:.0f} GB/s",
           file=sys.stderr, flush=True)
+
+    if not w.is_decode and w.max_q_len <= 16:
+        # a verify batch reads every key once per KV head for a handful of
+        # query rows: bandwidth-bound like a decode
+        flops = attention_flops(w)
+        print(f"[bench] verify attn {dec_avg * 1e3:.1f} us: KV {achieved:.0f} GB/s, "
+              f"{flops / (dec_avg * 1e-3) / 1e12:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        rec = {
+            "metric": "paged verify attn (few causal query rows per sequence): achieved KV "
+                      "HBM GB/s + verified tokens/s",
+            "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": w.name, **{k: v for k, v in w.describe().items()
+                                              if k != "workload"}},
+            "tokens_per_s": round(w.total_q / (ms_per_step * 1e-3), 1),
+            "kernels_us": {"kv_append": round(statistics.mean(append_ms) * 1e3, 2),
+                           "paged_prefill_attn": round(dec_avg * 1e3, 2)},
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": hbm_traffic(w.name),
+                         "kernel": "paged_prefill_attn (few-row chunks)",
+                         "algorithmic_bytes_per_launch": kv_bytes},
+        }
+        print(json.dumps(rec), flush=True)
+        return
 
     if not w.is_decode:
         flops = attention_flops(w)

@@ -178,6 +178,19 @@ def llama70b_decode(batch: int = 256, block_size: int = 16, median: float = 1024
                          block_size=block_size, seed=seed)
 
 
+def spec_verify(batch: int = 64, gamma: int = 5, lo: int = 512, hi: int = 4096,
+                block_size: int = 16, seed: int = 1006) -> Workload:
+    """Speculative-decoding verification ("让 Agent 跑得快：LLM 推理服务",
+    section 六: a draft model proposes gamma tokens, typically 5, and the
+    target checks them in one parallel prefill): each sequence appends its
+    last accepted token and the gamma drafts, gamma + 1 causal query rows at
+    the end of a context ~ U[lo, hi] (which includes them); 8B-shaped heads."""
+    g = torch.Generator().manual_seed(seed)
+    ctx = torch.randint(lo, hi + 1, (batch,), generator=g).tolist()
+    return make_workload(f"spec_verify_b{batch}_q{gamma + 1}", ctx, [gamma + 1] * batch,
+                         block_size=block_size, seed=seed)
+
+
 def mixed_prefill(num_chunks: int = 4, chunk: int = 512, num_decodes: int = 128,
                   prefix: int = 800, tail_lo: int = 64, tail_hi: int = 2048,
                   block_size: int = 16, seed: int = 1005) -> Workload:

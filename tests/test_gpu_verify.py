@@ -1,0 +1,56 @@
+"""GPU parity of speculative-decoding verification: a few causal query rows
+per sequence (the last accepted token and the drafts) through
+paged_prefill_attn, against the fp64 oracle."""
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_98_amd import binding as pkv
+from paged_kv_cache_98_amd import workloads as W
+from tests.gpu_common import oracle_prefill_sample, parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+# (context length including the new rows, new rows): row groups that end at,
+# straddle and start tile and block edges, and whole prompts of 2..8 tokens
+VERIFY = [(6, 6), (7, 6), (63, 6), (64, 6), (65, 6), (66, 6), (69, 6), (128, 2), (129, 3),
+          (130, 8), (1000, 6), (4097, 6), (2, 2), (512, 5), (513, 4), (300, 7)]
+
+
+def run(b):
+    w = b.workload
+    return pkv.paged_prefill_attn(b.q, b.cu_q_lens, b.k_cache, b.v_cache, b.block_table,
+                                  b.context_lens, w.scale, max_context_len=w.max_context_len,
+                                  max_q_len=w.max_q_len, causal=True)
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("group", [1, 4, 8])
+def test_verify_rows_around_edges(bs, group):
+    hkv = 2
+    w = W.make_workload(f"verify_g{group}_bs{bs}", [c for c, _ in VERIFY], [q for _, q in VERIFY],
+                        num_q_heads=hkv * group, num_kv_heads=hkv, block_size=bs,
+                        seed=4000 + group + bs)
+    bc = W.materialize(w, logical=True, poison=True)
+    ref = oracle.paged_attention(bc.q, bc.k_cache, bc.v_cache, bc.block_table, bc.context_lens,
+                                 w.scale, cu_q_lens=bc.cu_q_lens, causal=True)
+    out = run(bc.to(DEV))
+    torch.cuda.synchronize()
+    parity(out, ref, what=w.name)
+
+
+def test_verify_full_batch_sampled():
+    """The 64-sequence verify batch (6 rows each) in the launch configuration
+    the benchmark times; sampled sequences, every row, against the oracle."""
+    w = W.spec_verify()
+    print(f"[case] {w.describe()}", flush=True)
+    b = W.materialize(w, device=DEV, poison=True)
+    out = run(b)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(out))
+    ctx = list(w.context_lens)
+    seqs = sorted({ctx.index(max(ctx)), ctx.index(min(ctx)), 0, 31, 63})
+    ref, rows = oracle_prefill_sample(b, seqs)
+    parity(out[rows], ref, what=f"verify full batch, sequences {seqs}")
