@@ -36,6 +36,26 @@ Readings where the pages leave a step open:
     block when it is shared.
   * Slots follow the slot-mapping convention of kv_append:
     slot = physical_block * block_size + position % block_size.
+
+Prefix caching ("让 Agent 跑得快", section 七, vLLM's automatic prefix
+caching): a full block is identified by its parent block's identity, its
+own tokens and an optional extra key (a cache salt); allocation first looks
+the prompt's full blocks up in order, takes every hit (reference count + 1,
+into the block table) and stops at the first miss, from where the prompt
+must be prefilled; released blocks go back to the free queue and stay
+matchable until they are reused.  Readings:
+  * the identity is the exact chain (parent identity, tokens, salt), kept
+    here as nested tuples, so two blocks match only if their whole prefixes
+    and salts are equal; the salt enters every block's identity;
+  * a prompt's full blocks are registered when it is allocated (their K/V is
+    the caller's to compute before another request reads them); partly
+    filled blocks and blocks filled later by appends are not registered;
+  * taking a block from the free list for new contents (allocation, append,
+    copy) drops its registration: the front of the list, the longest-freed
+    block, is evicted first; a newer registration of the same identity
+    replaces an older one;
+  * a hit on a free block takes it out of the free list; the all-or-nothing
+    check counts those blocks as no longer free.
 """
 from collections import deque
 
@@ -50,6 +70,8 @@ class BlockPool:
         self.refcount = [0] * num_blocks
         self.tables = {}   # seq_id -> [physical block ids]
         self.lengths = {}  # seq_id -> tokens held
+        self.cache = {}    # block identity -> physical block
+        self.key_of = [None] * num_blocks
 
     def num_free(self) -> int:
         return len(self.free_list)
@@ -57,6 +79,11 @@ class BlockPool:
     def _take(self) -> int:
         b = self.free_list.popleft()
         self.refcount[b] = 1
+        key = self.key_of[b]
+        if key is not None:  # new contents: the registration goes
+            if self.cache.get(key) == b:
+                del self.cache[key]
+            self.key_of[b] = None
         return b
 
     def _release(self, b: int) -> None:
@@ -76,6 +103,43 @@ class BlockPool:
         self.tables[seq_id] = [self._take() for _ in range(need)]
         self.lengths[seq_id] = seq_len
         return list(self.tables[seq_id])
+
+    def allocate_cached(self, seq_id, tokens, salt: int = 0):
+        """A new sequence holding `tokens`, reusing cached full blocks.
+
+        Returns (blocks, cached_tokens): the block table and the number of
+        leading tokens whose K/V the hits already hold (prefill starts there).
+        """
+        if seq_id in self.tables:
+            raise KeyError(f"sequence {seq_id} exists")
+        tokens = [int(t) for t in tokens]
+        bs = self.block_size
+        n = len(tokens)
+        keys, key = [], None
+        for i in range(n // bs):
+            key = (key, tuple(tokens[i * bs:(i + 1) * bs]), int(salt))
+            keys.append(key)
+        hits = []
+        for key in keys:
+            b = self.cache.get(key)
+            if b is None:
+                break
+            hits.append(b)
+        new = -(-n // bs) - len(hits)
+        free_hits = sum(1 for b in hits if self.refcount[b] == 0)
+        if new > len(self.free_list) - free_hits:
+            raise MemoryError("not enough free KV blocks")
+        for b in hits:
+            if self.refcount[b] == 0:
+                self.free_list.remove(b)
+            self.refcount[b] += 1
+        blocks = hits + [self._take() for _ in range(new)]
+        for i in range(len(hits), len(keys)):
+            self.cache[keys[i]] = blocks[i]
+            self.key_of[blocks[i]] = keys[i]
+        self.tables[seq_id] = blocks
+        self.lengths[seq_id] = n
+        return list(blocks), len(hits) * bs
 
     def free(self, seq_id: int) -> None:
         """Drop a sequence; blocks nobody else references go back to the pool.
@@ -154,6 +218,8 @@ class BlockPool:
             assert (b in free) == (self.refcount[b] == 0), b
         for s, blocks in self.tables.items():
             assert len(blocks) == -(-self.lengths[s] // self.block_size), s
+        for key, b in self.cache.items():
+            assert self.key_of[b] == key, (b, "registration out of step")
 
 
 def copy_blocks(k_cache, v_cache, pairs):

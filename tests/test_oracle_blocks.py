@@ -189,3 +189,111 @@ def test_pin_copy_blocks_matches_append():
     ka, va = oracle.kv_append(k_rows, v_rows, slots, k, v)
     assert np.array_equal(ko, ka) and np.array_equal(vo, va)
     assert np.array_equal(ko[4], k[4]) and np.array_equal(ko[7], k[3])
+
+
+# ------------------------------------------------------------ prefix cache
+
+def prompt(*parts):
+    return [t for p in parts for t in p]
+
+
+SYS = list(range(1000, 1800))          # an 800-token system prompt: 50 full 16-token blocks
+
+
+def test_pin_prefix_cache_hit_and_prefill_start():
+    """A second request with the same system prompt takes the cached blocks
+    (reference count + 1, in its table) and prefills from the first miss
+    ("让 Agent 跑得快", section 七, steps 2-3)."""
+    pool = BlockPool(200, 16)
+    a, cached_a = pool.allocate_cached("a", prompt(SYS, [1, 2, 3]))
+    assert cached_a == 0 and len(a) == 51
+    b, cached_b = pool.allocate_cached("b", prompt(SYS, [7, 8, 9, 10]))
+    assert cached_b == 800                              # prefill starts at token 800
+    assert b[:50] == a[:50] and b[50] != a[50]
+    assert all(pool.refcount[x] == 2 for x in a[:50]) and pool.refcount[a[50]] == 1
+    assert pool.num_free() == 200 - 52
+    pool.check()
+
+
+def test_pin_prefix_cache_only_full_blocks():
+    """Only complete blocks are cached; a partly filled block is not
+    ("让 Agent 跑得快", section 三: block-granular matching)."""
+    pool = BlockPool(20, 16)
+    pool.allocate_cached("a", list(range(20)))          # one full block + 4 tokens
+    _, cached = pool.allocate_cached("b", list(range(20)))
+    assert cached == 16
+    assert len(pool.cache) == 1
+    _, cached = pool.allocate_cached("c", list(range(15)))
+    assert cached == 0                                   # the first block is not full here
+
+
+def test_pin_prefix_cache_chain_continuity():
+    """A block hits only if every block before it hits: the same tokens after
+    a different first block miss ("让 Agent 跑得快", section 七, the hash
+    chain)."""
+    pool = BlockPool(20, 16)
+    x, y, z = [1] * 16, [2] * 16, [3] * 16
+    pool.allocate_cached("a", prompt(x, y))
+    _, cached = pool.allocate_cached("b", prompt(z, y))
+    assert cached == 0
+    _, cached = pool.allocate_cached("c", prompt(x, z))
+    assert cached == 16
+
+
+def test_pin_prefix_cache_survives_release_until_reused():
+    """Released blocks return to the free queue and stay matchable; once the
+    free queue hands them out again their registration is gone (section 七,
+    step 4)."""
+    pool = BlockPool(6, 16)
+    toks = list(range(64))                               # 4 full blocks
+    blocks, _ = pool.allocate_cached("a", toks)
+    pool.free("a")
+    assert pool.num_free() == 6 and len(pool.cache) == 4
+    again, cached = pool.allocate_cached("b", toks)
+    assert cached == 64 and again == blocks and pool.num_free() == 2
+    pool.free("b")
+    # the free queue is now [4, 5, 0, 1, 2, 3]: three fresh blocks evict block 0
+    pool.allocate("c", 48)
+    assert pool.tables["c"] == [4, 5, 0]
+    assert len(pool.cache) == 3                          # block 0's registration is gone
+    pool.free("c")
+    _, cached = pool.allocate_cached("d", toks)
+    assert cached == 0                                   # the chain broke at block 0
+    pool.check()
+
+
+def test_pin_prefix_cache_salt_isolates():
+    """The same tokens under another cache salt never match (section 七,
+    cache_salt)."""
+    pool = BlockPool(20, 16)
+    pool.allocate_cached("a", list(range(32)), salt=1)
+    assert pool.allocate_cached("b", list(range(32)), salt=2)[1] == 0
+    assert pool.allocate_cached("c", list(range(32)), salt=1)[1] == 32
+
+
+def test_pin_prefix_cache_hit_rate_depends_on_where_prompts_differ():
+    """Fixed system prompt first and the varying question last: every
+    request after the first reuses the prompt; a varying token in front
+    (a timestamp) makes every block miss (section 七, hit rates)."""
+    pool = BlockPool(5000, 16)
+    hits_end, hits_front = [], []
+    for r in range(10):
+        hits_end.append(pool.allocate_cached(("end", r), prompt(SYS, [r] * 40))[1])
+        hits_front.append(pool.allocate_cached(("front", r), prompt([r], SYS, [5] * 39))[1])
+    assert hits_end == [0] + [800] * 9
+    assert hits_front == [0] * 10
+
+
+def test_pin_prefix_cache_free_hits_count_against_room():
+    """A hit on a free block leaves the free list: an allocation that needs
+    every free block plus one cached free block fails and changes nothing."""
+    pool = BlockPool(4, 16)
+    pool.allocate_cached("a", list(range(32)))          # blocks 0, 1 cached
+    pool.free("a")
+    snap = (list(pool.free_list), list(pool.refcount), dict(pool.cache))
+    with pytest.raises(MemoryError):
+        pool.allocate_cached("b", list(range(32)) + list(range(100, 148)))  # 2 hits + 3 new
+    assert snap == (list(pool.free_list), list(pool.refcount), dict(pool.cache))
+    blocks, cached = pool.allocate_cached("b", list(range(32)) + list(range(100, 132)))
+    assert cached == 32 and blocks[:2] == [0, 1]
+    pool.check()
