@@ -160,7 +160,9 @@ def bench_copy_blocks(args):
     Also times the native block manager on the host: one decode step of 256
     beams (64 prompts x 4 beams, forked after a 1000-token prompt) = one
     batched append of a token per beam (returning slots and copies) and the
-    block table of all beams, both through the Python binding."""
+    block table of all beams, both through the Python binding; and the
+    prefix cache: 64 prompts sharing an 800-token system prompt, each
+    allocated with its block lookups (microseconds per prompt)."""
     import numpy as np
     import torch
     from paged_kv_cache_98_amd import binding as pkv
@@ -212,6 +214,20 @@ def bench_copy_blocks(args):
             bm.append_batch(beams, ones)
             bm.block_table(beams, 80)
             host_us.append((time.perf_counter() - t1) * 1e6)
+    # prefix cache: 64 prompts = one 800-token system prompt + a private tail
+    # ~ U[64, 2048] (the mixed batch's shape), allocated with lookups
+    gp = torch.Generator().manual_seed(2026)
+    system = torch.randint(0, 32000, (800,), generator=gp, dtype=torch.int32)
+    tails = torch.randint(64, 2049, (64,), generator=gp).tolist()
+    prompts = [torch.cat([system, torch.randint(0, 32000, (t,), generator=gp, dtype=torch.int32)])
+               for t in tails]
+    with pkv.BlockManager(16384, bs) as bm:
+        t1 = time.perf_counter()
+        cached = [bm.allocate_cached(i, p) for i, p in enumerate(prompts)]
+        pc_us = (time.perf_counter() - t1) * 1e6 / len(prompts)
+    prompt_tokens = sum(p.numel() for p in prompts)
+    print(f"[bench] prefix cache: {pc_us:.1f} us per 64-prompt allocation, "
+          f"{sum(cached)} of {prompt_tokens} prompt tokens cached", file=sys.stderr, flush=True)
     print(f"[bench] copy_blocks {call_ms * 1e3:.1f} us per call of {npairs} pairs: "
           f"{achieved:.0f} GB/s | host manager {statistics.median(host_us):.0f} us per "
           f"256-beam step", file=sys.stderr, flush=True)
@@ -225,6 +241,8 @@ def bench_copy_blocks(args):
                    "block_size": bs, "num_kv_heads": hkv, "head_dim": d},
         "kernels_us": {"copy_blocks": round(call_ms * 1e3, 2)},
         "host_block_manager_us_per_256_beam_step": round(statistics.median(host_us), 1),
+        "host_prefix_cache": {"us_per_prompt": round(pc_us, 1), "prompts": len(prompts),
+                              "prompt_tokens": prompt_tokens, "cached_tokens": sum(cached)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": hbm_traffic(COPY_WORKLOAD),

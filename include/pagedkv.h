@@ -295,6 +295,32 @@ int64_t pkv_bm_num_free(const pkv_block_manager *bm);
  * PKV_ERR_NO_MEMORY if too few blocks are free. */
 int pkv_bm_allocate(pkv_block_manager *bm, int64_t seq_id, int64_t num_tokens);
 
+/*
+ * Prefix caching ("让 Agent 跑得快：LLM 推理服务", section 七, automatic prefix
+ * caching).  A new sequence seq_id holding the prompt tokens[0 .. num_tokens)
+ * reuses cached blocks: its full blocks are identified by the chain of
+ * (parent block's identity, the block's block_size tokens, salt) and looked
+ * up in order; every hit joins the table with one more reference, and the
+ * lookup stops at the first miss.  The remaining blocks are taken from the
+ * free list and the prompt's new full blocks are registered (their K/V is
+ * the caller's to write, from *num_cached_tokens on, before another request
+ * reads them).  Released blocks stay matchable until the free list hands
+ * them out again for new contents (allocation, append or copy), which drops
+ * their registration, the longest-freed first.  Partly filled blocks and
+ * blocks filled by later appends are not registered.  A different salt
+ * never matches (tenant isolation).  Matching compares the stored tokens,
+ * salt and parent hash, so a hash collision gives a miss, never a wrong hit.
+ *   num_cached_tokens  (written) leading tokens already held by the hits, a
+ *                      multiple of block_size: prefill starts there
+ * PKV_ERR_STATE if seq_id exists; PKV_ERR_NO_MEMORY if the new blocks do not
+ * fit (free cached hits count as taken); nothing changes on failure.
+ */
+int pkv_bm_allocate_cached(pkv_block_manager *bm, int64_t seq_id, const int32_t *tokens,
+                           int64_t num_tokens, int64_t salt, int64_t *num_cached_tokens);
+
+/* Registered (matchable) blocks, or -1 for a NULL manager. */
+int64_t pkv_bm_num_cached(const pkv_block_manager *bm);
+
 /* Drop seq_id; each of its blocks loses one reference and returns to the free
  * list at zero.  An unknown seq_id is ignored (PKV_OK). */
 int pkv_bm_free(pkv_block_manager *bm, int64_t seq_id);

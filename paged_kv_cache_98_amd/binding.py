@@ -36,7 +36,7 @@ PKV_OUT_BF16 = 1
 EXPORTED = ("pkv_status_string", "pkv_version", "pkv_kv_append", "pkv_decode_workspace_bytes",
             "pkv_paged_decode_attn", "pkv_prefill_workspace_bytes", "pkv_paged_prefill_attn",
             "pkv_kv_append_fp8", "pkv_paged_decode_attn_fp8", "pkv_copy_blocks", "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free",
-            "pkv_bm_allocate", "pkv_bm_free", "pkv_bm_fork", "pkv_bm_append", "pkv_bm_append_batch",
+            "pkv_bm_allocate", "pkv_bm_allocate_cached", "pkv_bm_num_cached", "pkv_bm_free", "pkv_bm_fork", "pkv_bm_append", "pkv_bm_append_batch",
             "pkv_bm_seq_info",
             "pkv_bm_refcount", "pkv_bm_block_table")
 
@@ -107,6 +107,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_bm_num_free.argtypes = [_vp]
     lib.pkv_bm_allocate.restype = _i32
     lib.pkv_bm_allocate.argtypes = [_vp, _i64, _i64]
+    lib.pkv_bm_allocate_cached.restype = _i32
+    lib.pkv_bm_allocate_cached.argtypes = [_vp, _i64, _vp, _i64, _i64, _vp]
+    lib.pkv_bm_num_cached.restype = _i64
+    lib.pkv_bm_num_cached.argtypes = [_vp]
     lib.pkv_bm_free.restype = _i32
     lib.pkv_bm_free.argtypes = [_vp, _i64]
     lib.pkv_bm_fork.restype = _i32
@@ -369,6 +373,24 @@ class BlockManager:
 
     def allocate(self, seq_id: int, num_tokens: int) -> None:
         _check(self._lib.pkv_bm_allocate(self._handle(), seq_id, num_tokens))
+
+    def allocate_cached(self, seq_id: int, tokens, salt: int = 0) -> int:
+        """A new sequence holding the prompt `tokens` (int32 values, a
+        sequence or CPU tensor), reusing cached full blocks; returns the
+        number of leading tokens the hits already hold (prefill starts
+        there)."""
+        t = tokens if isinstance(tokens, torch.Tensor) else torch.tensor(list(tokens), dtype=torch.int32)
+        if t.is_cuda:
+            raise TypeError("block-manager arguments live on the host")
+        t = t.to(torch.int32).contiguous()
+        n = ctypes.c_int64(0)
+        _check(self._lib.pkv_bm_allocate_cached(self._handle(), seq_id,
+                                                t.data_ptr() if t.numel() else None, t.numel(),
+                                                int(salt), ctypes.byref(n)))
+        return n.value
+
+    def num_cached(self) -> int:
+        return self._lib.pkv_bm_num_cached(self._handle())
 
     def free(self, seq_id: int) -> None:
         _check(self._lib.pkv_bm_free(self._handle(), seq_id))

@@ -17,17 +17,50 @@
 //     one and repoints the table entry (the caller performs the returned
 //     copies on the device with pkv_copy_blocks before writing); a block
 //     whose count drops to zero returns to the pool.
-// Blocks leave the front of the free list and come back at its end.  A call
-// that would run out of blocks part-way changes nothing.  The free list is a
-// ring of num_blocks entries (a block is free at most once), so giving blocks
-// back never allocates and cannot fail half-way.
+//   * same page, section 七 (automatic prefix caching): a full block is
+//     identified by its parent block's identity, its tokens and an optional
+//     cache salt; allocating a prompt looks its full blocks up in order,
+//     takes every hit (reference count + 1) and stops at the first miss,
+//     from where the prompt must be prefilled; released blocks stay
+//     matchable in the free queue until it hands them out again.
+// Blocks leave the front of the free list and come back at its end; a hit
+// on a free cached block takes it out of the middle, so the list is doubly
+// linked over block ids.  Taking a block for new contents drops its cache
+// registration (the longest-freed cached block is evicted first).  The
+// cache is an open-addressing table of 64-bit chain hashes; every entry
+// keeps its block's parent hash, salt and tokens, which a lookup compares,
+// so a hash collision is a miss, never a wrong hit.  Both structures have
+// a fixed capacity (the table is sized at the first cached allocation), so
+// giving blocks back and undoing a failed batch never allocate.  A call
+// that would run out of blocks part-way changes nothing.
 #include <algorithm>
 #include <cstdint>
+#include <cstring>
 #include <new>
 #include <unordered_map>
 #include <vector>
 
 #include "pagedkv.h"
+
+namespace {
+
+constexpr uint64_t kRootHash = 0x6a09e667f3bcc908ull;  // parent of a prompt's first block
+
+uint64_t mix64(uint64_t x) {  // the splitmix64 finaliser
+    x ^= x >> 30;
+    x *= 0xbf58476d1ce4e5b9ull;
+    x ^= x >> 27;
+    x *= 0x94d049bb133111ebull;
+    return x ^ (x >> 31);
+}
+
+uint64_t chain_hash(uint64_t parent, int64_t salt, const int32_t* tokens, int n) {
+    uint64_t h = mix64(parent ^ mix64((uint64_t)salt + 0x9e3779b97f4a7c15ull));
+    for (int i = 0; i < n; ++i) h = mix64(h ^ (uint32_t)tokens[i]) + (uint64_t)i;
+    return h;
+}
+
+}  // namespace
 
 struct pkv_block_manager {
     struct Seq {
@@ -36,35 +69,124 @@ struct pkv_block_manager {
     };
     int64_t num_blocks = 0;
     int block_size = 16;
-    std::vector<int64_t> ring;  // free list: ring[head], ... (num_free entries)
-    int64_t head = 0;
-    int64_t num_free = 0;
+    // free list, doubly linked through prev / next (-1 ends it)
+    std::vector<int64_t> prev, next;
+    int64_t head = -1, tail = -1, num_free = 0;
     std::vector<int32_t> refcount;
     std::unordered_map<int64_t, Seq> seqs;
+    // prefix cache: per block, its registration (valid while has_key);
+    // `evicted` remembers whether the last take() dropped a live entry
+    std::vector<uint8_t> has_key, evicted;
+    std::vector<uint64_t> key_hash, key_parent;
+    std::vector<int64_t> key_salt;
+    std::vector<int32_t> key_tokens;  // [num_blocks][block_size], sized with the table
+    std::vector<uint64_t> slot_hash;  // open addressing, linear probing
+    std::vector<int64_t> slot_block;  // -1: empty
+    int64_t cached = 0;
 
     int64_t blocks_for(int64_t tokens) const { return (tokens + block_size - 1) / block_size; }
-    int64_t take() {
-        const int64_t b = ring[(size_t)head];
-        head = head + 1 == num_blocks ? 0 : head + 1;
+
+    // ---- free list
+    void link_back(int64_t b) {
+        prev[(size_t)b] = tail;
+        next[(size_t)b] = -1;
+        if (tail >= 0) next[(size_t)tail] = b; else head = b;
+        tail = b;
+        ++num_free;
+    }
+    void link_front(int64_t b) {
+        next[(size_t)b] = head;
+        prev[(size_t)b] = -1;
+        if (head >= 0) prev[(size_t)head] = b; else tail = b;
+        head = b;
+        ++num_free;
+    }
+    void unlink(int64_t b) {
+        const int64_t p = prev[(size_t)b], n = next[(size_t)b];
+        if (p >= 0) next[(size_t)p] = n; else head = n;
+        if (n >= 0) prev[(size_t)n] = p; else tail = p;
         --num_free;
+    }
+
+    // ---- cache table
+    size_t slot_of(uint64_t h) const { return (size_t)(mix64(h) & (slot_hash.size() - 1)); }
+    int64_t find(uint64_t h) const {
+        if (slot_hash.empty()) return -1;
+        for (size_t i = slot_of(h);; i = (i + 1) & (slot_hash.size() - 1)) {
+            if (slot_block[i] < 0) return -1;
+            if (slot_hash[i] == h) return slot_block[i];
+        }
+    }
+    void put(uint64_t h, int64_t b) {  // insert or replace; the table never fills
+        size_t i = slot_of(h);
+        while (slot_block[i] >= 0 && slot_hash[i] != h) i = (i + 1) & (slot_hash.size() - 1);
+        if (slot_block[i] < 0) ++cached;
+        slot_hash[i] = h;
+        slot_block[i] = b;
+    }
+    void erase(uint64_t h) {  // backward-shift deletion keeps probe runs unbroken
+        const size_t mask = slot_hash.size() - 1;
+        size_t i = slot_of(h);
+        while (slot_block[i] >= 0 && slot_hash[i] != h) i = (i + 1) & mask;
+        if (slot_block[i] < 0) return;
+        --cached;
+        for (size_t j = (i + 1) & mask;; j = (j + 1) & mask) {
+            if (slot_block[j] < 0) break;
+            const size_t home = slot_of(slot_hash[j]);
+            // move j back into the hole at i unless its home lies in (i, j]
+            if (((j - home) & mask) >= ((j - i) & mask)) {
+                slot_hash[i] = slot_hash[j];
+                slot_block[i] = slot_block[j];
+                i = j;
+            }
+        }
+        slot_block[i] = -1;
+    }
+    bool ensure_cache() {  // sized once, at the first cached allocation
+        if (!slot_hash.empty()) return true;
+        try {
+            size_t cap = 16;
+            while (cap < 2 * (size_t)num_blocks) cap <<= 1;
+            key_tokens.resize((size_t)num_blocks * (size_t)block_size);
+            slot_hash.assign(cap, 0);
+            slot_block.assign(cap, -1);
+        } catch (...) {
+            key_tokens.clear();
+            slot_hash.clear();
+            slot_block.clear();
+            return false;
+        }
+        return true;
+    }
+
+    // ---- taking and returning blocks
+    int64_t take() {
+        const int64_t b = head;
+        unlink(b);
         refcount[(size_t)b] = 1;
+        evicted[(size_t)b] = 0;
+        if (has_key[(size_t)b]) {  // new contents: the registration goes
+            if (find(key_hash[(size_t)b]) == b) {
+                erase(key_hash[(size_t)b]);
+                evicted[(size_t)b] = 1;
+            }
+            has_key[(size_t)b] = 0;
+        }
         return b;
     }
     void release(int64_t b) {
-        if (--refcount[(size_t)b] == 0) {
-            int64_t tail = head + num_free;
-            if (tail >= num_blocks) tail -= num_blocks;
-            ring[(size_t)tail] = b;
-            ++num_free;
-        }
+        if (--refcount[(size_t)b] == 0) link_back(b);
     }
-    // Undo of take(): b goes back to the FRONT of the free list, so undoing
-    // takes in reverse order restores the list exactly.
+    // Undo of take(): b goes back to the FRONT of the free list with its
+    // registration, so undoing takes in reverse order restores everything.
     void untake(int64_t b) {
         refcount[(size_t)b] = 0;
-        head = head == 0 ? num_blocks - 1 : head - 1;
-        ring[(size_t)head] = b;
-        ++num_free;
+        link_front(b);
+        if (evicted[(size_t)b]) {
+            has_key[(size_t)b] = 1;
+            put(key_hash[(size_t)b], b);
+            evicted[(size_t)b] = 0;
+        }
     }
 
     // What one append changed, enough to put it back.
@@ -138,10 +260,16 @@ pkv_block_manager* pkv_bm_create(int64_t num_blocks, int block_size) {
     try {
         bm->num_blocks = num_blocks;
         bm->block_size = block_size;
-        bm->refcount.assign((size_t)num_blocks, 0);
-        bm->ring.resize((size_t)num_blocks);
-        for (int64_t b = 0; b < num_blocks; ++b) bm->ring[(size_t)b] = b;
-        bm->num_free = num_blocks;
+        const size_t n = (size_t)num_blocks;
+        bm->refcount.assign(n, 0);
+        bm->prev.assign(n, -1);
+        bm->next.assign(n, -1);
+        bm->has_key.assign(n, 0);
+        bm->evicted.assign(n, 0);
+        bm->key_hash.assign(n, 0);
+        bm->key_parent.assign(n, 0);
+        bm->key_salt.assign(n, 0);
+        for (int64_t b = 0; b < num_blocks; ++b) bm->link_back(b);
     } catch (...) {
         delete bm;
         return nullptr;
@@ -173,6 +301,70 @@ int pkv_bm_allocate(pkv_block_manager* bm, int64_t seq_id, int64_t num_tokens) {
     }
     return PKV_OK;
 }
+
+int pkv_bm_allocate_cached(pkv_block_manager* bm, int64_t seq_id, const int32_t* tokens,
+                           int64_t num_tokens, int64_t salt, int64_t* num_cached_tokens) {
+    if (bm == nullptr || num_cached_tokens == nullptr || (num_tokens > 0 && tokens == nullptr))
+        return PKV_ERR_NULL;
+    if (num_tokens < 0) return PKV_ERR_SHAPE;
+    if (bm->seqs.count(seq_id)) return PKV_ERR_STATE;
+    const int bs = bm->block_size;
+    const int64_t nfull = num_tokens / bs;
+    const int64_t nblk = bm->blocks_for(num_tokens);
+    if (nfull > 0 && !bm->ensure_cache()) return PKV_ERR_HOST_ALLOC;
+    std::vector<uint64_t> h;
+    pkv_block_manager::Seq s;
+    try {
+        h.resize((size_t)nfull);
+        s.blocks.reserve((size_t)nblk);
+    } catch (...) {
+        return PKV_ERR_HOST_ALLOC;
+    }
+    uint64_t parent = kRootHash;
+    for (int64_t i = 0; i < nfull; ++i) {
+        h[(size_t)i] = chain_hash(parent, salt, tokens + i * bs, bs);
+        parent = h[(size_t)i];
+    }
+    // hits: the leading full blocks whose whole key matches
+    int64_t hits = 0, free_hits = 0;
+    for (; hits < nfull; ++hits) {
+        const int64_t b = bm->find(h[(size_t)hits]);
+        if (b < 0 || !bm->has_key[(size_t)b]) break;
+        const size_t k = (size_t)b;
+        const uint64_t want_parent = hits == 0 ? kRootHash : h[(size_t)hits - 1];
+        if (bm->key_parent[k] != want_parent || bm->key_salt[k] != salt ||
+            std::memcmp(&bm->key_tokens[k * bs], tokens + hits * bs, sizeof(int32_t) * bs) != 0)
+            break;
+        if (bm->refcount[k] == 0) ++free_hits;
+        s.blocks.push_back(b);
+    }
+    if (nblk - hits > bm->num_free - free_hits) return PKV_ERR_NO_MEMORY;
+    try {
+        bm->seqs.emplace(seq_id, pkv_block_manager::Seq{});  // before any change
+    } catch (...) {
+        return PKV_ERR_HOST_ALLOC;
+    }
+    for (int64_t b : s.blocks) {
+        if (bm->refcount[(size_t)b] == 0) bm->unlink(b);
+        ++bm->refcount[(size_t)b];
+    }
+    for (int64_t i = hits; i < nblk; ++i) s.blocks.push_back(bm->take());
+    for (int64_t i = hits; i < nfull; ++i) {  // register the new full blocks
+        const size_t k = (size_t)s.blocks[(size_t)i];
+        bm->key_hash[k] = h[(size_t)i];
+        bm->key_parent[k] = i == 0 ? kRootHash : h[(size_t)i - 1];
+        bm->key_salt[k] = salt;
+        std::memcpy(&bm->key_tokens[k * bs], tokens + i * bs, sizeof(int32_t) * bs);
+        bm->has_key[k] = 1;
+        bm->put(h[(size_t)i], (int64_t)k);
+    }
+    s.length = num_tokens;
+    bm->seqs[seq_id] = std::move(s);
+    *num_cached_tokens = hits * bs;
+    return PKV_OK;
+}
+
+int64_t pkv_bm_num_cached(const pkv_block_manager* bm) { return bm == nullptr ? -1 : bm->cached; }
 
 int pkv_bm_free(pkv_block_manager* bm, int64_t seq_id) {
     if (bm == nullptr) return PKV_ERR_NULL;

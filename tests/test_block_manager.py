@@ -332,3 +332,104 @@ def test_append_batch_abi_edges(lib):
         assert n.value == 1 and list(copies)[:2] == [0, 3]
     finally:
         lib.pkv_bm_destroy(h)
+
+
+@pytest.mark.parametrize("seed,num_blocks,bs", [(21, 30, 16), (22, 300, 16), (23, 30, 32),
+                                                 (24, 40, 5)])
+def test_native_prefix_cache_matches_oracle(seed, num_blocks, bs):
+    """Cached allocations of prompts built from a few shared prefixes (some
+    block-aligned, some not) under two salts, mixed with plain allocations,
+    appends, forks and frees: the native manager's hits, tables, reference
+    counts and registrations equal the oracle's at every step."""
+    rng = random.Random(seed)
+    pool, nat = BlockPool(num_blocks, bs), Native(num_blocks, bs)
+    prefixes = [list(range(100 + 1000 * k, 100 + 1000 * k + length))
+                for k, length in enumerate([3 * bs, 5 * bs + 3, 2 * bs, bs - 1])]
+    ids = list(range(12))
+    seen = {"hit": 0, "nomem": 0, "cached_ok": 0}
+    for step in range(1200):
+        op = rng.choices(["cached", "alloc", "append", "fork", "free"], weights=[4, 1, 3, 1, 2])[0]
+        s = rng.choice(ids)
+        if op == "cached":
+            toks = rng.choice(prefixes) + [rng.randrange(50) for _ in range(rng.randrange(0, 3 * bs))]
+            salt = rng.choice([0, 0, 0, 7])
+            try:
+                ref = ("ok", pool.allocate_cached(s, toks, salt)[1])
+            except MemoryError:
+                ref = ("nomem", None)
+            except KeyError:
+                ref = ("state", None)
+            try:
+                got = ("ok", nat.bm.allocate_cached(s, toks, salt))
+            except MemoryError:
+                got = ("nomem", None)
+            except KeyError:
+                got = ("state", None)
+            assert got == ref, (step, s, len(toks), salt)
+            if ref[0] == "ok":
+                seen["cached_ok"] += 1
+                seen["hit"] += ref[1] > 0
+            seen["nomem"] += ref[0] == "nomem"
+        elif op == "alloc":
+            n = rng.randrange(0, 4 * bs)
+            got = outcome(nat.allocate, s, n)[0]
+            assert got == outcome(pool.allocate, s, n)[0]
+            seen["nomem"] += got == "nomem"
+        elif op == "append" and s in pool.tables:
+            n = rng.choice([1, 1, 2, rng.randrange(1, 2 * bs)])
+            got = outcome(nat.append, s, n)
+            assert got == outcome(pool.append, s, n), step
+            seen["nomem"] += got[0] == "nomem"
+        elif op == "fork" and s in pool.tables:
+            c = rng.choice(ids)
+            if c not in pool.tables:
+                pool.fork(s, c)
+                nat.fork(s, c)
+        elif op == "free":
+            pool.free(s)
+            nat.free(s)
+        pool.check()
+        compare_state(nat, pool, ids)
+        assert nat.bm.num_cached() == len(pool.cache), step
+    assert seen["cached_ok"] > 100 and seen["hit"] > 30, seen
+    if num_blocks < 100:
+        assert seen["nomem"] > 0, seen
+    nat.bm.close()
+
+
+def test_native_prefix_cache_batch_rollback_restores_registrations():
+    """A failed batch append that had evicted cached blocks puts their
+    registrations back: a later cached allocation still hits."""
+    bs = 16
+    with binding.BlockManager(6, bs) as bm:
+        toks = list(range(64))                        # 4 full blocks
+        assert bm.allocate_cached(1, toks) == 0
+        bm.free(1)                                    # free queue [4, 5, 0, 1, 2, 3], 4 cached
+        bm.allocate(2, 1)                             # takes block 4
+        bm.allocate(3, 1)                             # takes block 5
+        # seq 2 needs 2 more blocks (evicting 0 and 1), seq 3 needs 8: no room
+        with pytest.raises(MemoryError):
+            bm.append_batch([2, 3], [31, 130])
+        assert bm.num_cached() == 4 and bm.num_free() == 4
+        bm.free(2)
+        bm.free(3)
+        assert bm.allocate_cached(4, toks) == 64
+
+
+def test_allocate_cached_abi_edges(lib):
+    E = binding
+    h = lib.pkv_bm_create(4, 16)
+    try:
+        n = ctypes.c_int64(-1)
+        assert lib.pkv_bm_allocate_cached(h, 1, None, 5, 0, ctypes.byref(n)) == E.PKV_ERR_NULL
+        assert lib.pkv_bm_allocate_cached(h, 1, None, -1, 0, ctypes.byref(n)) == E.PKV_ERR_SHAPE
+        assert lib.pkv_bm_allocate_cached(h, 1, None, 0, 0, ctypes.byref(n)) == E.PKV_OK
+        assert n.value == 0 and lib.pkv_bm_num_cached(h) == 0
+        toks = (ctypes.c_int32 * 80)(*range(80))
+        assert lib.pkv_bm_allocate_cached(h, 1, toks, 10, 0, ctypes.byref(n)) == E.PKV_ERR_STATE
+        assert lib.pkv_bm_allocate_cached(h, 2, toks, 80, 0, ctypes.byref(n)) == E.PKV_ERR_NO_MEMORY
+        assert lib.pkv_bm_allocate_cached(h, 2, toks, 64, 0, ctypes.byref(n)) == E.PKV_OK
+        assert n.value == 0 and lib.pkv_bm_num_cached(h) == 4 and lib.pkv_bm_num_free(h) == 0
+        assert lib.pkv_bm_num_cached(None) == -1
+    finally:
+        lib.pkv_bm_destroy(h)
