@@ -226,7 +226,7 @@ def bench_copy_blocks(args):
         cached = [bm.allocate_cached(i, p) for i, p in enumerate(prompts)]
         pc_us = (time.perf_counter() - t1) * 1e6 / len(prompts)
     prompt_tokens = sum(p.numel() for p in prompts)
-    print(f"[bench] prefix cache: {pc_us:.1f} us per 64-prompt allocation, "
+    print(f"[bench] prefix cache: {pc_us:.1f} us per prompt (64 prompts), "
           f"{sum(cached)} of {prompt_tokens} prompt tokens cached", file=sys.stderr, flush=True)
     print(f"[bench] copy_blocks {call_ms * 1e3:.1f} us per call of {npairs} pairs: "
           f"{achieved:.0f} GB/s | host manager {statistics.median(host_us):.0f} us per "
@@ -281,6 +281,7 @@ def workload_by_name(name):
         "prefill_chunks": lambda: W.mixed_prefill(num_decodes=0),
         # speculative-decoding verification: 6 causal query rows per sequence
         "spec_verify": lambda: W.spec_verify(),
+        "spec_verify_long": lambda: W.spec_verify(batch=8, lo=32768, hi=131072, seed=1007),
         "mixed_prefill": lambda: W.mixed_prefill(),
     }
     if name not in table:
@@ -392,8 +393,10 @@ def main():
         # E4M3 code pools made by torch's float8 cast; the bf16 pools go
         b.k_cache, b.v_cache = W.fp8_pools(b)
         torch.cuda.empty_cache()
-    ws_bytes = pkv.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads,
-                                          w.max_context_len)
+    ws_bytes = (pkv.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads,
+                                           w.max_context_len) if w.is_decode else
+                pkv.prefill_workspace_bytes(w.num_seqs, w.total_q, w.max_q_len, w.num_q_heads,
+                                            w.num_kv_heads, w.max_context_len))
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
@@ -414,7 +417,8 @@ def main():
         else:
             pkv.paged_prefill_attn(b.q, b.cu_q_lens, b.k_cache, b.v_cache, b.block_table,
                                    b.context_lens, w.scale, max_context_len=w.max_context_len,
-                                   max_q_len=w.max_q_len, causal=True, out=out, stream=stream)
+                                   max_q_len=w.max_q_len, causal=True, out=out,
+                                   workspace=ws if ws_bytes else None, stream=stream)
 
     def step(ev=None):
         if ev is not None:

@@ -190,12 +190,21 @@ int pkv_paged_decode_attn_fp8(void *out, int out_dtype, const void *q, const voi
                               float scale, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Workspace needed by pkv_paged_prefill_attn (bytes, >= 0): the decode
- * workspace for the batch's single-row sequences.  A call whose every
- * sequence has exactly max_q_len > 1 rows needs none (workspace may be NULL).
+ * Workspace needed by pkv_paged_prefill_attn (bytes, >= 0; 0 for
+ * inconsistent sizes).  Two parts, either of which may be absent: the
+ * decode workspace for the batch's single-row sequences, and the records of
+ * the key-range split.  The split applies to short chunks (max_q_len *
+ * num_q_heads / num_kv_heads <= 64, as in speculative-decoding
+ * verification) when their (128-column slot, KV head) items are fewer than
+ * 256 (too few to fill the chip, as with a few long contexts): each item's
+ * keys are cut into at most 32 pieces of at least 512 keys, aiming at about
+ * 2048 workgroups, and every (piece, query row, query head) has a record
+ * of 132 floats.  A call whose every sequence has exactly max_q_len > 1 rows
+ * and no split needs none (workspace may be NULL).
  */
-size_t pkv_prefill_workspace_bytes(int num_seqs, int num_q_tokens, int num_q_heads,
-                                   int head_dim, int max_context_len);
+size_t pkv_prefill_workspace_bytes(int num_seqs, int num_q_tokens, int max_q_len,
+                                   int num_q_heads, int num_kv_heads, int head_dim,
+                                   int max_context_len);
 
 /*
  * paged_prefill_attn -- a chunk of queries per sequence (causal), decode rows
@@ -217,7 +226,9 @@ size_t pkv_prefill_workspace_bytes(int num_seqs, int num_q_tokens, int num_q_hea
  *   num_q_tokens   host-side total query rows (= cu_q_lens[num_seqs])
  * Rows with Lq_i == 1 take the bandwidth-bound decode path (the split-KV
  * decode kernels, enqueued after the MFMA chunk kernel on the same stream);
- * longer chunks take the MFMA path.  num_seqs <= 16383 and num_kv_heads in
+ * longer chunks take the MFMA path.  Short chunks over long contexts (the
+ * workspace comment above) split each chunk's keys into pieces handled by
+ * separate workgroups, merged by a log-sum-exp fold in a second kernel.  num_seqs <= 16383 and num_kv_heads in
  * 1..8 or 16 when single-row sequences can be present.  QK^T runs as bf16 x bf16 MFMA with fp32 accumulation;
  * P V runs as fp16 x fp16 MFMA with fp32 accumulation, V converted from bf16
  * to fp16 in registers: exact for |v| in [2^-14, 65504]; smaller magnitudes

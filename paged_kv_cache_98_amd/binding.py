@@ -85,7 +85,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_paged_decode_attn.argtypes = [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
                                           _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]
     lib.pkv_prefill_workspace_bytes.restype = _sz
-    lib.pkv_prefill_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
+    lib.pkv_prefill_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32]
     lib.pkv_paged_prefill_attn.restype = _i32
     lib.pkv_paged_prefill_attn.argtypes = [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
                                            _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
@@ -237,10 +237,11 @@ def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,
                                                       head_dim, max_context_len)
 
 
-def prefill_workspace_bytes(num_seqs: int, num_q_tokens: int, num_q_heads: int,
-                            max_context_len: int, head_dim: int = 128) -> int:
-    return load_library().pkv_prefill_workspace_bytes(num_seqs, num_q_tokens, num_q_heads,
-                                                      head_dim, max_context_len)
+def prefill_workspace_bytes(num_seqs: int, num_q_tokens: int, max_q_len: int, num_q_heads: int,
+                            num_kv_heads: int, max_context_len: int, head_dim: int = 128) -> int:
+    return load_library().pkv_prefill_workspace_bytes(num_seqs, num_q_tokens, max_q_len,
+                                                      num_q_heads, num_kv_heads, head_dim,
+                                                      max_context_len)
 
 
 def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -287,7 +288,7 @@ def paged_prefill_attn(q: torch.Tensor, cu_q_lens: torch.Tensor, k_cache: torch.
         raise ValueError("shape mismatch")
     if out is None:
         out = torch.empty((tq, hq, d), dtype=out_dtype, device=q.device)
-    need = lib.pkv_prefill_workspace_bytes(nseq, tq, hq, d, max_context_len)
+    need = lib.pkv_prefill_workspace_bytes(nseq, tq, max_q_len, hq, hkv, d, max_context_len)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None

@@ -46,6 +46,25 @@ int check_attention_shape(int max_blocks_per_seq, int max_context_len, int num_s
 
 int to_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH; }
 
+// Prefill workspace: the decode kernels' part for single-row sequences,
+// then, when the call's chunks are split over key ranges, the pieces'
+// records at *records_offset.
+size_t prefill_workspace(int num_seqs, int num_q_tokens, int max_q_len, int num_q_heads,
+                         int num_kv_heads, int head_dim, int max_context_len,
+                         size_t* records_offset) {
+    // records are per query head, so the KV head count does not matter here
+    const size_t dec = pkv::decode_workspace_bytes(num_seqs, num_q_heads, 1, head_dim,
+                                                   max_context_len);
+    int split_tiles = 0, max_pieces = 1;
+    pkv::prefill_split_plan(max_q_len, num_q_heads / num_kv_heads, max_context_len, num_seqs,
+                            num_kv_heads, &split_tiles, &max_pieces);
+    if (records_offset) *records_offset = 0;
+    if (split_tiles == 0) return dec;
+    const size_t off = align_up(dec, 256);
+    if (records_offset) *records_offset = off;
+    return off + pkv::prefill_record_bytes(num_q_tokens, num_q_heads, max_pieces);
+}
+
 }  // namespace
 
 extern "C" {
@@ -220,13 +239,14 @@ int pkv_kv_append_fp8(const void* k_new, const void* v_new, const int64_t* slot_
     return to_status(pkv::launch_kv_append_fp8(a, static_cast<hipStream_t>(stream)));
 }
 
-size_t pkv_prefill_workspace_bytes(int num_seqs, int num_q_tokens, int num_q_heads, int head_dim,
+size_t pkv_prefill_workspace_bytes(int num_seqs, int num_q_tokens, int max_q_len,
+                                   int num_q_heads, int num_kv_heads, int head_dim,
                                    int max_context_len) {
-    (void)num_q_tokens;
-    if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
-    // the decode rows of a mixed batch use the decode kernels' workspace
-    // (records are per query head, so the KV head count does not matter)
-    return pkv::decode_workspace_bytes(num_seqs, num_q_heads, 1, head_dim, max_context_len);
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        num_q_tokens < 0 || max_q_len < 0 || num_q_heads % num_kv_heads != 0)
+        return 0;
+    return prefill_workspace(num_seqs, num_q_tokens, max_q_len, num_q_heads, num_kv_heads,
+                             head_dim, max_context_len, nullptr);
 }
 
 int pkv_paged_prefill_attn(void* out, int out_dtype, const void* q, const int32_t* cu_q_lens,
@@ -253,12 +273,21 @@ int pkv_paged_prefill_attn(void* out, int out_dtype, const void* q, const int32_
     const bool any_decode_rows = !uniform_chunks;
     const bool decode_limits_ok = num_seqs <= kMaxDecodeSeqs &&
                                   (num_kv_heads <= 8 || num_kv_heads == kMaxDecodeKvHeads);
-    if (any_decode_rows) {
-        if (!decode_limits_ok) return PKV_ERR_UNSUPPORTED;
-        const size_t need = pkv::decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
-                                                        head_dim, max_context_len);
+    float* records = nullptr;
+    int split_tiles = 0, max_pieces = 1;
+    pkv::prefill_split_plan(max_q_len, num_q_heads / num_kv_heads, max_context_len, num_seqs,
+                            num_kv_heads, &split_tiles, &max_pieces);
+    if (any_decode_rows && !decode_limits_ok) return PKV_ERR_UNSUPPORTED;
+    if (any_decode_rows || split_tiles > 0) {
+        size_t rec_off = 0;
+        const size_t need = any_decode_rows || split_tiles > 0
+            ? prefill_workspace(num_seqs, num_q_tokens, max_q_len, num_q_heads, num_kv_heads,
+                                head_dim, max_context_len, &rec_off)
+            : 0;
         if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
         if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+        if (split_tiles > 0)
+            records = reinterpret_cast<float*>(static_cast<char*>(workspace) + rec_off);
     }
 
     pkv::PrefillArgs a;
@@ -281,6 +310,9 @@ int pkv_paged_prefill_attn(void* out, int out_dtype, const void* q, const int32_
     a.scale_log2 = scale * 1.4426950408889634f;
     a.causal = causal != 0;
     a.decode_rows_elsewhere = any_decode_rows;
+    a.split_tiles = split_tiles;
+    a.max_pieces = max_pieces;
+    a.records = records;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (max_q_len > 1) {
         st = to_status(pkv::launch_prefill(a, s));

@@ -86,6 +86,10 @@ struct PrefillArgs {
     float scale_log2;
     bool causal;
     bool decode_rows_elsewhere;  // skip sequences with one query row
+    // key split of few-row chunks (prefill_split_plan); 0 = none
+    int split_tiles = 0;
+    int max_pieces = 1;
+    float* records = nullptr;  // workspace: [max_pieces][num_q_tokens][num_q_heads][132]
 };
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
@@ -93,6 +97,14 @@ hipError_t launch_kv_append_fp8(const AppendFp8Args& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+// Key split of a prefill call whose chunks have at most 64 query columns
+// per workgroup (max_q_len * group <= 64) and whose items leave most of the
+// chip idle: pieces of split_tiles 64-key tiles, at most max_pieces per
+// item; split_tiles = 0 means no split.
+void prefill_split_plan(int max_q_len, int group, int max_context_len, int num_seqs,
+                        int num_kv_heads, int* split_tiles, int* max_pieces);
+size_t prefill_record_bytes(int num_q_tokens, int num_q_heads, int max_pieces);
 
 // Decode workspace: the tile prefix sums, then the partial-result records.
 size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,

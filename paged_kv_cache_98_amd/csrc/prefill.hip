@@ -33,6 +33,18 @@
 //   * K and V tiles of 64 keys are double-buffered in LDS: K as [key][dim]
 //     bf16, V transposed to [dim][key] fp16 while it is staged; the next
 //     tile's global loads are in flight while the current tile is computed.
+//
+// Key split (chunks of a few rows, as in speculative-decoding verification:
+// at most 64 of the 128 columns used): such a call reads every key once
+// per KV head for a handful of queries, so it is bandwidth-bound.  When its
+// (slot, KV head) items are too few to fill the chip (a few long contexts),
+// a workgroup takes one piece of at most split_tiles key tiles of its item
+// instead of the whole item; an item of one piece finishes in place,
+// the pieces of a longer one leave their unnormalised O, reference maximum
+// m and sum l per real column in the workspace, and prefill_merge_kernel
+// combines them: M = max m_k, L = sum l_k 2^(m_k - M),
+// out = sum O_k 2^(m_k - M) / L (the sequence-axis parallelism of "Flash
+// Attention v2 的改进").
 #include <type_traits>
 
 #include "pkv_device.h"
@@ -68,12 +80,13 @@ struct PrefillIds {
     int base;
     int cur;
     int nxt;
-    __device__ __forceinline__ void init(const int32_t* r, int n, int lane) {
+    // window starting at block `first`
+    __device__ __forceinline__ void init(const int32_t* r, int n, int first, int lane) {
         row = r;
         nblk = n;
-        base = 0;
-        cur = lane < n ? r[lane] : 0;
-        nxt = 64 + lane < n ? r[64 + lane] : 0;
+        base = first;
+        cur = first + lane < n ? r[first + lane] : 0;
+        nxt = first + 64 + lane < n ? r[first + 64 + lane] : 0;
     }
     // id of block `blk` (wave-uniform, non-decreasing between calls)
     __device__ __forceinline__ int get(int blk, int lane) {
@@ -237,9 +250,29 @@ __device__ __forceinline__ void softmax_half(f32x16_t& s, f16x8_t (&pf)[2], f32x
     l_run = fmaf(l_run, alpha, (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]));
 }
 
-// Grid: (num_q_tokens / (128 / G) + num_seqs, num_kv_heads); block 256.
-// Slot x of sequence i is x - T(i), T(i) = cu_q_lens[i] / P + i with
-// P = 128 / G positions per workgroup; T never skips a needed slot.
+constexpr int kRecStride = D + 4;  // floats per split record: O[128], m, l, 2 pad
+constexpr int kMinSplitTiles = 8;  // a piece streams at least 512 keys ...
+constexpr int kMaxPieces = 32;     // ... and an item has at most 32 pieces
+constexpr int64_t kSplitBelowItems = 256;
+constexpr int64_t kSplitTargetGroups = 2048;
+
+// Key tiles of the (slot, KV head) item that holds query row r of a
+// sequence with lq rows and context ctx (the slot's last row decides).
+template <int G>
+__device__ __forceinline__ int item_tiles(int r, int lq, int ctx, int causal) {
+    constexpr int P = kCols / G;
+    const int r0 = r / P * P;
+    const int r_last = (r0 + P < lq ? r0 + P : lq) - 1;
+    const int pos0 = ctx - lq;
+    const int kv_end = causal ? (pos0 + r_last + 1 < ctx ? pos0 + r_last + 1 : ctx) : ctx;
+    return (kv_end + kKT - 1) / kKT;
+}
+
+// Grid: ((num_q_tokens / (128 / G) + num_seqs) * max_pieces, num_kv_heads);
+// block 256.  x / max_pieces is the slot, x % max_pieces the piece (always 0
+// without a key split).  Slot y of sequence i is y - T(i),
+// T(i) = cu_q_lens[i] / P + i with P = 128 / G positions per workgroup; T
+// never skips a needed slot.
 template <int BS, int G, bool OUT_BF16>
 __global__ void __launch_bounds__(kThreads, 2)
 prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
@@ -247,7 +280,8 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
                     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
                     int max_blocks_per_seq, const int32_t* __restrict__ context_lens,
                     int max_context_len, int num_seqs, int num_q_heads, int num_kv_heads,
-                    float scale_log2, int causal, int decode_rows_elsewhere) {
+                    float scale_log2, int causal, int decode_rows_elsewhere, int split_tiles,
+                    int max_pieces, float* __restrict__ rec, int num_q_tokens) {
     constexpr int P = kCols / G;  // query positions per workgroup
     __shared__ __attribute__((aligned(16))) uint16_t s_ks[2][kKsElems];
     __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kVtElems];
@@ -256,7 +290,8 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int kvh = blockIdx.y;
-    const int slot = blockIdx.x;
+    const int slot = blockIdx.x / max_pieces;
+    const int piece = blockIdx.x - slot * max_pieces;
 
     // ---- which sequence owns this slot: 64-way search over T(i)
     int lo = 0, hi = num_seqs;  // T(lo) <= slot < T(hi), T(num_seqs) = grid size
@@ -291,6 +326,15 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
     const int r_last = (r0 + P < lq ? r0 + P : lq) - 1;
     const int kv_end = causal ? (pos0 + r_last + 1 < ctx ? pos0 + r_last + 1 : ctx) : ctx;
     const int ntiles = (kv_end + kKT - 1) / kKT;
+    // this workgroup's key tiles [t0, t1) and the item's piece count
+    int t0 = 0, t1 = ntiles, npieces = 1;
+    if (split_tiles > 0) {
+        t0 = piece * split_tiles;
+        if (piece > 0 && t0 >= ntiles) return;  // piece 0 also covers ntiles == 0
+        t1 = t0 + split_tiles < ntiles ? t0 + split_tiles : ntiles;
+        npieces = (ntiles + split_tiles - 1) / split_tiles;
+        npieces = npieces > 1 ? npieces : 1;
+    }
 
     // Q^T fragments: k-step kk covers dims 16 kk + 8 h .. + 7 of this column;
     // a negative scale moves into q's sign so maxima work on raw scores.
@@ -324,12 +368,14 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
     uint32_t koff[4], voff[4];
     stage_offsets<BS>(koff, voff, row_bytes, tid);
     PrefillIds ids;
-    ids.init(block_table + (size_t)seq * max_blocks_per_seq, (ctx + BS - 1) / BS, lane);
+    ids.init(block_table + (size_t)seq * max_blocks_per_seq, (ctx + BS - 1) / BS,
+             t0 * kKT / BS, lane);
 
     Stage sg;
-    if (ntiles > 0) {
-        stage_load<BS>(sg, ids, kbase, vbase, 0, kv_end, block_bytes, koff, voff, tid, lane);
-        stage_store(sg, s_ks[0], s_vt[0], tid);
+    if (t1 > t0) {
+        stage_load<BS>(sg, ids, kbase, vbase, t0 * kKT, kv_end, block_bytes, koff, voff, tid,
+                       lane);
+        stage_store(sg, s_ks[t0 & 1], s_vt[t0 & 1], tid);
     }
     __syncthreads();
 
@@ -390,19 +436,50 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
     // Only tiles that reach the causal diagonal (k0 + 63 > pos0 + r0) or the
     // context's end (k0 + 64 > ctx) need masks; they are the last ones.  The
     // tiles before them, all with a next tile, run in a loop of their own with
-    // no branch in its body.
+    // no branch in its body.  (A piece's last tile always takes the masked
+    // path; its masks then drop nothing.)
+    // A wave none of whose columns is a real query row (short chunks: a verify
+    // chunk of 6 rows x 4 heads fills 24 of the 128 columns) only stages its
+    // share of every tile for the others and meets them at each tile's
+    // barrier; its results would be discarded.
+    if (r0 + (wave * 32) / G >= lq) {
+        for (int jj = t0; jj < t1; ++jj) {
+            if (jj + 1 < t1) {
+                stage_load<BS>(sg, ids, kbase, vbase, (jj + 1) * kKT, kv_end, block_bytes, koff,
+                               voff, tid, lane);
+                stage_store(sg, s_ks[(jj + 1) & 1], s_vt[(jj + 1) & 1], tid);
+            }
+            __syncthreads();
+        }
+        return;
+    }
     const int first_pos = pos0 + r0;
     const int j_diag = causal ? (first_pos >= kKT - 1 ? (first_pos - (kKT - 1)) / kKT + 1 : 0) : ntiles;
     const int j_tail = ctx >= kKT ? (ctx - kKT) / kKT + 1 : 0;
     int j_plain = j_diag < j_tail ? j_diag : j_tail;
-    j_plain = j_plain < ntiles - 1 ? j_plain : ntiles - 1;
-    int j = 0;
+    j_plain = j_plain < t1 - 1 ? j_plain : t1 - 1;
+    int j = t0;
     for (; j < j_plain; ++j) run_tile(j, std::false_type{}, true);
-    for (; j < ntiles; ++j) run_tile(j, std::true_type{}, j + 1 < ntiles);
+    for (; j < t1; ++j) run_tile(j, std::true_type{}, j + 1 < t1);
 
     // ---- finish: total l over both halves, then out = O / l
     const float lt = l_run + xor_lane(l_run, 32);
     if (!col_valid) return;
+    if (npieces > 1) {  // one piece of several: the record of this column
+        float* rp = rec + (((size_t)piece * num_q_tokens + (size_t)(q_begin + r)) * num_q_heads +
+                           (size_t)kvh * G + g) * kRecStride;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4)
+                *reinterpret_cast<float4*>(rp + 32 * mb + 8 * e4 + 4 * h) =
+                    make_float4(o[mb][4 * e4], o[mb][4 * e4 + 1], o[mb][4 * e4 + 2], o[mb][4 * e4 + 3]);
+        if (h == 0) {
+            rp[D] = m_run;
+            rp[D + 1] = lt;
+        }
+        return;
+    }
     const float inv = ntiles > 0 ? 1.0f / lt : 0.0f;
     const size_t orow = ((size_t)(q_begin + r) * num_q_heads + (size_t)kvh * G + g) * D;
 #pragma unroll
@@ -424,16 +501,87 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
         }
 }
 
+// Combines the pieces of split items.  Grid: (num_seqs, ceil(max_q_len *
+// num_q_heads / 4)); block: 4 waves, one (row, query head) each; lane k
+// holds piece k's m and l, and dims 2 lane, 2 lane + 1 of the output.
+template <int G, bool OUT_BF16>
+__global__ void __launch_bounds__(256)
+prefill_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
+                     const int32_t* __restrict__ cu_q_lens, const int32_t* __restrict__ context_lens,
+                     int max_context_len, int num_q_heads, int num_q_tokens, int causal,
+                     int decode_rows_elsewhere, int split_tiles) {
+    const int lane = threadIdx.x & 63;
+    const int seq = blockIdx.x;
+    const int item = blockIdx.y * 4 + (threadIdx.x >> 6);
+    const int q_begin = cu_q_lens[seq];
+    const int lq = cu_q_lens[seq + 1] - q_begin;
+    const int r = item / num_q_heads;
+    const int head = item - r * num_q_heads;
+    if (r >= lq) return;
+    if (decode_rows_elsewhere && lq == 1) return;
+    int ctx = context_lens[seq];
+    ctx = ctx < 0 ? 0 : (ctx > max_context_len ? max_context_len : ctx);
+    const int npieces = (item_tiles<G>(r, lq, ctx, causal) + split_tiles - 1) / split_tiles;
+    if (npieces <= 1) return;  // finished in place
+    auto rec_of = [&](int k) {
+        return rec + (((size_t)k * num_q_tokens + (size_t)(q_begin + r)) * num_q_heads + head) *
+                         kRecStride;
+    };
+    float2 ml = make_float2(-INFINITY, 0.0f);
+    if (lane < npieces) ml = *reinterpret_cast<const float2*>(rec_of(lane) + D);
+    float mx = ml.x;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    const float fk = lane < npieces ? fast_exp2(ml.x - mx) : 0.0f;
+    float lsum = ml.y * fk;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) lsum += __shfl_xor(lsum, o);
+    // eight pieces' rows in flight at a time
+    float a0 = 0.0f, a1 = 0.0f;
+    for (int k = 0; k < npieces; k += 8) {
+        float2 av[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            av[u] = k + u < npieces ? *reinterpret_cast<const float2*>(rec_of(k + u) + 2 * lane)
+                                    : make_float2(0.0f, 0.0f);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int kk = k + u < 63 ? k + u : 63;
+            const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fk), kk));
+            a0 = fmaf(av[u].x, f, a0);
+            a1 = fmaf(av[u].y, f, a1);
+        }
+    }
+    const float inv = 1.0f / lsum;
+    const size_t e = ((size_t)(q_begin + r) * num_q_heads + head) * D + 2 * lane;
+    if (OUT_BF16) {
+        const uint32_t w = (uint32_t)f32_to_bf16_rne(a0 * inv) |
+                           ((uint32_t)f32_to_bf16_rne(a1 * inv) << 16);
+        *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + e) = w;
+    } else {
+        *reinterpret_cast<float2*>(static_cast<float*>(out) + e) = make_float2(a0 * inv, a1 * inv);
+    }
+}
+
 template <int BS, int G, bool OUT_BF16>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     constexpr int P = kCols / G;
     const int slots = a.num_q_tokens / P + a.num_seqs;
-    dim3 grid(slots, a.num_kv_heads);
+    const int pieces = a.split_tiles > 0 ? a.max_pieces : 1;
+    dim3 grid(slots * pieces, a.num_kv_heads);
     hipLaunchKernelGGL((prefill_mfma_kernel<BS, G, OUT_BF16>), grid, dim3(kThreads), 0, stream,
                        a.out, a.q, a.cu_q_lens, a.k_cache, a.v_cache, a.block_table,
                        a.max_blocks_per_seq, a.context_lens, a.max_context_len, a.num_seqs,
                        a.num_q_heads, a.num_kv_heads, a.scale_log2, a.causal ? 1 : 0,
-                       a.decode_rows_elsewhere ? 1 : 0);
+                       a.decode_rows_elsewhere ? 1 : 0, a.split_tiles, pieces, a.records,
+                       a.num_q_tokens);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.split_tiles == 0) return e;
+    dim3 mgrid(a.num_seqs, (a.max_q_len * a.num_q_heads + 3) / 4);
+    hipLaunchKernelGGL((prefill_merge_kernel<G, OUT_BF16>), mgrid, dim3(256), 0, stream, a.out,
+                       a.records, a.cu_q_lens, a.context_lens, a.max_context_len, a.num_q_heads,
+                       a.num_q_tokens, a.causal ? 1 : 0, a.decode_rows_elsewhere ? 1 : 0,
+                       a.split_tiles);
     return hipGetLastError();
 }
 
@@ -455,6 +603,33 @@ hipError_t launch_prefill_bs(const PrefillArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+void prefill_split_plan(int max_q_len, int group, int max_context_len, int num_seqs,
+                        int num_kv_heads, int* split_tiles, int* max_pieces) {
+    *split_tiles = 0;
+    *max_pieces = 1;
+    // only chunks with few query columns per workgroup stream keys ...
+    if (max_q_len < 2 || max_q_len * group > kCols / 2) return;
+    // ... and only when their items leave most of the chip idle: below half
+    // of the 512 workgroups an MI355X runs at once (two per CU), the pieces
+    // aim at about 2048 workgroups
+    const int64_t items = (int64_t)num_seqs * num_kv_heads *
+                          ((max_q_len + kCols / group - 1) / (kCols / group));
+    if (items >= kSplitBelowItems) return;
+    const int64_t want = (kSplitTargetGroups + items - 1) / items;
+    const int pieces_goal = (int)(want < kMaxPieces ? want : kMaxPieces);
+    const int tiles = (max_context_len + kKT - 1) / kKT;
+    int s = (tiles + pieces_goal - 1) / pieces_goal;
+    s = s > kMinSplitTiles ? s : kMinSplitTiles;
+    const int pieces = (tiles + s - 1) / s;
+    if (pieces < 2) return;
+    *split_tiles = s;
+    *max_pieces = pieces;
+}
+
+size_t prefill_record_bytes(int num_q_tokens, int num_q_heads, int max_pieces) {
+    return (size_t)max_pieces * num_q_tokens * num_q_heads * kRecStride * sizeof(float);
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     return a.block_size == 16 ? launch_prefill_bs<16>(a, stream) : launch_prefill_bs<32>(a, stream);

@@ -189,3 +189,23 @@ def test_product_path_does_not_touch_the_oracle():
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "liboracle" not in text and "pkv_oracle" not in text, f
+
+
+def test_prefill_workspace_size(lib):
+    ws = lib.pkv_prefill_workspace_bytes
+    dec = lambda b, ctx: lib.pkv_decode_workspace_bytes(b, 32, 8, 128, ctx)
+    up = lambda x: (x + 255) // 256 * 256
+    # 512-row chunks: no key split, only the decode part
+    assert ws(4, 2048, 512, 32, 8, 128, 4096) == dec(4, 4096)
+    # 64 six-row verify chunks x 8 KV heads = 512 items fill the chip: no split
+    assert ws(64, 384, 6, 32, 8, 128, 4096) == dec(64, 4096)
+    # 8 of them (64 items) over 100k tokens: 1563 tiles in pieces of 49, 32 pieces
+    assert ws(8, 48, 6, 32, 8, 128, 100000) == up(dec(8, 100000)) + 32 * 48 * 32 * 132 * 4
+    # 16 sequences x 2 KV heads over 4097 tokens: 65 tiles, 64 pieces wanted,
+    # at least 8 tiles each -> pieces of 8, 9 of them
+    assert ws(16, 96, 6, 8, 2, 128, 4097) == (
+        up(lib.pkv_decode_workspace_bytes(16, 8, 2, 128, 4097)) + 9 * 96 * 8 * 132 * 4)
+    # short contexts (8 tiles or fewer) or wide chunks (6 x 16 > 64 columns): no split
+    assert ws(8, 48, 6, 32, 8, 128, 512) == dec(8, 512)
+    assert ws(8, 48, 6, 32, 2, 128, 100000) == dec(8, 100000)
+    assert ws(4, 10, 4, 32, 6, 128, 100) == 0                       # Hq % Hkv

@@ -54,3 +54,35 @@ def test_verify_full_batch_sampled():
     seqs = sorted({ctx.index(max(ctx)), ctx.index(min(ctx)), 0, 31, 63})
     ref, rows = oracle_prefill_sample(b, seqs)
     parity(out[rows], ref, what=f"verify full batch, sequences {seqs}")
+
+
+def test_verify_split_variants():
+    """Key-split chunks in every setting the split meets: 16 query heads per
+    KV head with 4 rows (64 columns, the largest split case), non-causal,
+    bf16 output, single-row sequences in the same call (whose decode
+    workspace sits in front of the split records), and bitwise
+    determinism."""
+    from tests.gpu_common import bf16_parity
+    cases = [(3000, 4), (2500, 1), (40, 3), (1800, 2), (4100, 4), (700, 1), (129, 4)]
+    w = W.make_workload("verify_split_g16", [c for c, _ in cases], [q for _, q in cases],
+                        num_q_heads=32, num_kv_heads=2, block_size=16, seed=4100)
+    bc = W.materialize(w, logical=True, poison=True)
+    b = bc.to(DEV)
+    need = pkv.prefill_workspace_bytes(w.num_seqs, w.total_q, w.max_q_len, 32, 2,
+                                       w.max_context_len)
+    assert need > pkv.decode_workspace_bytes(w.num_seqs, 32, 2, w.max_context_len)
+    for causal in (True, False):
+        ref = oracle.paged_attention(bc.q, bc.k_cache, bc.v_cache, bc.block_table,
+                                     bc.context_lens, w.scale, cu_q_lens=bc.cu_q_lens,
+                                     causal=causal)
+        call = lambda dt: pkv.paged_prefill_attn(
+            b.q, b.cu_q_lens, b.k_cache, b.v_cache, b.block_table, b.context_lens, w.scale,
+            max_context_len=w.max_context_len, max_q_len=w.max_q_len, causal=causal,
+            out_dtype=dt)
+        o32 = call(torch.float32)
+        o32b = call(torch.float32)
+        o16 = call(torch.bfloat16)
+        torch.cuda.synchronize()
+        assert torch.equal(o32, o32b)
+        parity(o32, ref, what=f"split g16 causal={causal}")
+        bf16_parity(o16, o32, ref, what=f"split g16 bf16 causal={causal}")
