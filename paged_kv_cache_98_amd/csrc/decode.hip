@@ -53,8 +53,11 @@ constexpr int kLoads = kTileTokens / 4;  // loads per lane per tile (K or V)
 //   * V comes out as eight floats.
 // The FP8 cache's two scales are applied outside the tile loop: k_scale
 // inside the score scale, v_scale on the finished output.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
 struct KvBf16 {
     static constexpr int kElemBytes = 2;
+    static constexpr bool kPairedPV = false;
     using Word = uint4;
     static __device__ __forceinline__ Word load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
         return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
@@ -69,8 +72,15 @@ struct KvBf16 {
 };
 
 // FP8 codes in the OCP E4M3 format, decoded by the hardware conversions.
+// Its P V runs on fp16 dot products over token pairs: a lane's tokens i and
+// i + 1 give, for every dim, the pair (v_i, v_i+1) (a byte permute puts the
+// two codes side by side, one conversion widens them to fp16 exactly) and
+// (p_i, p_i+1) rounds to fp16 once per query head, so one v_dot2_f32_f16
+// does the work of two fp32 FMAs.  P is in [0, 1] and rounds with 2^-11
+// relative error, as in the chunked-prefill kernel.
 struct KvFp8 {
     static constexpr int kElemBytes = 1;
+    static constexpr bool kPairedPV = true;
     using Word = uint2;
     static __device__ __forceinline__ Word load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
         return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
@@ -90,6 +100,22 @@ struct KvFp8 {
         const auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
         v[0] = a[0]; v[1] = a[1]; v[2] = b[0]; v[3] = b[1];
         v[4] = c[0]; v[5] = c[1]; v[6] = d[0]; v[7] = d[1];
+    }
+    // vp[d] = (value of token a at dim d, value of token b at dim d)
+    static __device__ __forceinline__ void v_pairs(const Word& a, const Word& b, f16x2_t (&vp)[8]) {
+        // bytes (a.k, b.k, a.k+1, b.k+1) of the two words, k = 0 and 2
+        const uint32_t w0 = __builtin_amdgcn_perm(b.x, a.x, 0x05010400u);
+        const uint32_t w1 = __builtin_amdgcn_perm(b.x, a.x, 0x07030602u);
+        const uint32_t w2 = __builtin_amdgcn_perm(b.y, a.y, 0x05010400u);
+        const uint32_t w3 = __builtin_amdgcn_perm(b.y, a.y, 0x07030602u);
+        vp[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w0, 1.0f, false);
+        vp[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w0, 1.0f, true);
+        vp[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w1, 1.0f, false);
+        vp[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w1, 1.0f, true);
+        vp[4] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w2, 1.0f, false);
+        vp[5] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w2, 1.0f, true);
+        vp[6] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w3, 1.0f, false);
+        vp[7] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w3, 1.0f, true);
     }
 };
 
@@ -119,7 +145,7 @@ struct State {
     float m[G];       // running max (log2 domain), uniform across the row
     float l[G];       // running sum, uniform across the row
     float acc[G][8];  // unnormalised output, dims 8c..8c+7 of this lane
-    float alpha[G];   // last rescale factor exp2(m_old - m_new)
+    float alpha[G];   // last rescale factor exp2(m_old - m_new) (bf16 pools)
 };
 
 // One 16-token tile: QK, online-softmax update, PV.  `ntok_left` is the
@@ -151,47 +177,98 @@ __device__ __forceinline__ void process_tile(State<G>& st, const Tile<KV>& t, co
         }
     }
     float p[kLoads][G];
-    bool grew = false;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const float bm = fmaxf(fmaxf(s[0][g], s[1][g]), fmaxf(s[2][g], s[3][g])) * c;
-        const float mn = fmaxf(st.m[g], bm);
-        grew |= mn > st.m[g];
-        const float alpha = fast_exp2(st.m[g] - mn);
-        st.m[g] = mn;
-        float sum = 0.0f;
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
-            p[i][g] = fast_exp2(fmaf(s[i][g], c, -mn));
-            if (PARTIAL) p[i][g] = (4 * i + row) < ntok_left ? p[i][g] : 0.0f;
-            sum += p[i][g];
-        }
-        st.l[g] = fmaf(st.l[g], alpha, sum);
-        st.alpha[g] = alpha;
-    }
-    // The accumulator needs the exp(m_old - m_new) rescale only when some
-    // running maximum moved; after the first tiles that is rare.
-    if (__any(grew)) {
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int d = 0; d < 8; ++d) st.acc[g][d] *= st.alpha[g];
-    }
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-        float v[8];
-        KV::v_floats(t.v[i], v);
-        if (PARTIAL) {
-            // A masked token has p = 0, but its pool slot may hold anything
-            // (NaN included): zero the value so 0 * v stays 0.
-            const bool valid = (4 * i + row) < ntok_left;
-#pragma unroll
-            for (int d = 0; d < 8; ++d) v[d] = valid ? v[d] : 0.0f;
-        }
+    if constexpr (KV::kPairedPV) {
+        float m_old[G], sum[G];
+        bool grew = false;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
+            const float bm = fmaxf(fmaxf(s[0][g], s[1][g]), fmaxf(s[2][g], s[3][g])) * c;
+            const float mn = fmaxf(st.m[g], bm);
+            grew |= mn > st.m[g];
+            m_old[g] = st.m[g];
+            st.m[g] = mn;
+            sum[g] = 0.0f;
 #pragma unroll
-            for (int d = 0; d < 8; ++d) st.acc[g][d] = fmaf(p[i][g], v[d], st.acc[g][d]);
+            for (int i = 0; i < kLoads; ++i) {
+                p[i][g] = fast_exp2(fmaf(s[i][g], c, -mn));
+                if (PARTIAL) p[i][g] = (4 * i + row) < ntok_left ? p[i][g] : 0.0f;
+                sum[g] += p[i][g];
+            }
+        }
+        // The exp(m_old - m_new) rescale of l and the accumulator is needed only
+        // when some running maximum moved; after the first tiles that is rare
+        // (an unmoved maximum gives exactly 1 either way).
+        float alpha[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) alpha[g] = 1.0f;
+        if (__any(grew)) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                alpha[g] = fast_exp2(m_old[g] - st.m[g]);
+#pragma unroll
+                for (int d = 0; d < 8; ++d) st.acc[g][d] *= alpha[g];
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) st.l[g] = fmaf(st.l[g], alpha[g], sum[g]);
+    } else {
+        bool grew = false;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float bm = fmaxf(fmaxf(s[0][g], s[1][g]), fmaxf(s[2][g], s[3][g])) * c;
+            const float mn = fmaxf(st.m[g], bm);
+            grew |= mn > st.m[g];
+            const float alpha = fast_exp2(st.m[g] - mn);
+            st.m[g] = mn;
+            float sum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kLoads; ++i) {
+                p[i][g] = fast_exp2(fmaf(s[i][g], c, -mn));
+                if (PARTIAL) p[i][g] = (4 * i + row) < ntok_left ? p[i][g] : 0.0f;
+                sum += p[i][g];
+            }
+            st.l[g] = fmaf(st.l[g], alpha, sum);
+            st.alpha[g] = alpha;
+        }
+        // The accumulator needs the exp(m_old - m_new) rescale only when some
+        // running maximum moved; after the first tiles that is rare.
+        if (__any(grew)) {
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int d = 0; d < 8; ++d) st.acc[g][d] *= st.alpha[g];
+        }
+    }
+    if constexpr (KV::kPairedPV && !PARTIAL) {
+#pragma unroll
+        for (int i = 0; i < kLoads; i += 2) {
+            f16x2_t vp[8];
+            KV::v_pairs(t.v[i], t.v[i + 1], vp);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const f16x2_t pp = {(_Float16)p[i][g], (_Float16)p[i + 1][g]};
+#pragma unroll
+                for (int d = 0; d < 8; ++d)
+                    st.acc[g][d] = __builtin_amdgcn_fdot2(vp[d], pp, st.acc[g][d], false);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            float v[8];
+            KV::v_floats(t.v[i], v);
+            if (PARTIAL) {
+                // A masked token has p = 0, but its pool slot may hold anything
+                // (NaN included): zero the value so 0 * v stays 0.
+                const bool valid = (4 * i + row) < ntok_left;
+#pragma unroll
+                for (int d = 0; d < 8; ++d) v[d] = valid ? v[d] : 0.0f;
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+#pragma unroll
+                for (int d = 0; d < 8; ++d) st.acc[g][d] = fmaf(p[i][g], v[d], st.acc[g][d]);
+            }
         }
     }
 }
