@@ -34,7 +34,10 @@
 // dims 8c..8c+7 of tokens 4i + r, i = 0..3; the 16-lane row reduces the QK
 // partial sums with DPP adds; each row is its own online-softmax stream
 // (tokens = r mod 4) merged with the other rows at the end of a piece; the
-// next tile's loads are issued before the current tile's math.  Scores are
+// next tile's loads are issued before the current tile's math.  An FP8
+// cache (one byte per value) uses the same layout with 64-bit loads, or,
+// for up to 4 query heads per KV head, 8 rows of 8 lanes holding 16 dims of
+// 2 tokens each (see the storage policies below).  Scores are
 // in the log2 domain (scale * log2 e folded in), exponentials are v_exp_f32.
 #include "pkv_device.h"
 #include "pkv_launch.h"
@@ -43,26 +46,30 @@ namespace pkv {
 
 namespace {
 
-constexpr int kLoads = kTileTokens / 4;  // loads per lane per tile (K or V)
-
-// How the pools store a value.  A lane's share of one token row of one head
-// is always eight values (dims 8c .. 8c + 7): a 16-byte word of bf16, or an
-// 8-byte word of FP8 codes.
-//   * K comes out as four bf16 pairs for the dot2 instructions (E4M3 to
-//     bf16 is exact: every E4M3 value is a bf16 value);
-//   * V comes out as eight floats.
+// How the pools store a value, and the lane layout that goes with it.  A
+// wave sees a 16-token tile of one KV head as rows of kRowLanes lanes: lane
+// (row r, col c) holds dims kDims c .. kDims c + kDims - 1 of the tile's
+// tokens kRows i + r, i = 0 .. kLoads - 1, one word per token, and the
+// kRowLanes lanes of a row reduce their partial dot products with DPP.
+//   * K comes out as bf16 pairs for the dot2 instructions (E4M3 to bf16 is
+//     exact: every E4M3 value is a bf16 value);
+//   * V comes out as floats, or, for FP8, as fp16 pairs over two tokens.
 // The FP8 cache's two scales are applied outside the tile loop: k_scale
 // inside the score scale, v_scale on the finished output.
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
+// bf16 pools: 8 dims (16 bytes) per lane and token, rows of 16 lanes.
 struct KvBf16 {
     static constexpr int kElemBytes = 2;
+    static constexpr int kDims = 8;
     static constexpr bool kPairedPV = false;
     using Word = uint4;
     static __device__ __forceinline__ Word load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
         return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
     }
-    static __device__ __forceinline__ uint4 k_pairs(const Word& w) { return w; }
+    static __device__ __forceinline__ void k_pairs(const Word& w, uint32_t (&kp)[4]) {
+        kp[0] = w.x; kp[1] = w.y; kp[2] = w.z; kp[3] = w.w;
+    }
     static __device__ __forceinline__ void v_floats(const Word& w, float (&v)[8]) {
         v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
         v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
@@ -72,80 +79,135 @@ struct KvBf16 {
 };
 
 // FP8 codes in the OCP E4M3 format, decoded by the hardware conversions.
-// Its P V runs on fp16 dot products over token pairs: a lane's tokens i and
-// i + 1 give, for every dim, the pair (v_i, v_i+1) (a byte permute puts the
-// two codes side by side, one conversion widens them to fp16 exactly) and
-// (p_i, p_i+1) rounds to fp16 once per query head, so one v_dot2_f32_f16
-// does the work of two fp32 FMAs.  P is in [0, 1] and rounds with 2^-11
-// relative error, as in the chunked-prefill kernel.
-struct KvFp8 {
+// Their P V runs on fp16 dot products over token pairs: a lane's tokens i
+// and i + 1 give, for every dim, the pair (v_i, v_i+1) (a byte permute puts
+// the two codes side by side, one conversion widens them to fp16 exactly)
+// and (p_i, p_i+1) rounds to fp16 once per query head, so one
+// v_dot2_f32_f16 does the work of two fp32 FMAs.  P is in [0, 1] and rounds
+// with 2^-11 relative error, as in the chunked-prefill kernel.
+template <int NWORDS>  // 32-bit words of codes per lane and token
+struct KvFp8Base {
     static constexpr int kElemBytes = 1;
+    static constexpr int kDims = 4 * NWORDS;
     static constexpr bool kPairedPV = true;
-    using Word = uint2;
-    static __device__ __forceinline__ Word load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-        return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-    }
     template <bool HIGH>  // codes 2, 3 of the word instead of 0, 1
-    static __device__ __forceinline__ uint32_t pair(uint32_t codes) {
+    static __device__ __forceinline__ uint32_t bf16_pair(uint32_t codes) {
         return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(
                                                 (int)codes, 1.0f, HIGH));
     }
-    static __device__ __forceinline__ uint4 k_pairs(const Word& w) {
-        return make_uint4(pair<false>(w.x), pair<true>(w.x), pair<false>(w.y), pair<true>(w.y));
+    static __device__ __forceinline__ void k_pairs_of(const uint32_t (&w)[NWORDS],
+                                                      uint32_t (&kp)[2 * NWORDS]) {
+#pragma unroll
+        for (int j = 0; j < NWORDS; ++j) {
+            kp[2 * j] = bf16_pair<false>(w[j]);
+            kp[2 * j + 1] = bf16_pair<true>(w[j]);
+        }
     }
-    static __device__ __forceinline__ void v_floats(const Word& w, float (&v)[8]) {
-        const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
-        const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
-        const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
-        const auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
-        v[0] = a[0]; v[1] = a[1]; v[2] = b[0]; v[3] = b[1];
-        v[4] = c[0]; v[5] = c[1]; v[6] = d[0]; v[7] = d[1];
+    static __device__ __forceinline__ void v_floats_of(const uint32_t (&w)[NWORDS],
+                                                       float (&v)[4 * NWORDS]) {
+#pragma unroll
+        for (int j = 0; j < NWORDS; ++j) {
+            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[j], false);
+            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[j], true);
+            v[4 * j] = lo[0]; v[4 * j + 1] = lo[1]; v[4 * j + 2] = hi[0]; v[4 * j + 3] = hi[1];
+        }
     }
-    // vp[d] = (value of token a at dim d, value of token b at dim d)
-    static __device__ __forceinline__ void v_pairs(const Word& a, const Word& b, f16x2_t (&vp)[8]) {
+    // vp[e] = (value of token a, value of token b) at dim 4 j + e: word j of
+    // each token holds dims 4 j .. 4 j + 3
+    static __device__ __forceinline__ void pairs4(uint32_t a, uint32_t b, f16x2_t (&vp)[4]) {
         // bytes (a.k, b.k, a.k+1, b.k+1) of the two words, k = 0 and 2
-        const uint32_t w0 = __builtin_amdgcn_perm(b.x, a.x, 0x05010400u);
-        const uint32_t w1 = __builtin_amdgcn_perm(b.x, a.x, 0x07030602u);
-        const uint32_t w2 = __builtin_amdgcn_perm(b.y, a.y, 0x05010400u);
-        const uint32_t w3 = __builtin_amdgcn_perm(b.y, a.y, 0x07030602u);
+        const uint32_t w0 = __builtin_amdgcn_perm(b, a, 0x05010400u);
+        const uint32_t w1 = __builtin_amdgcn_perm(b, a, 0x07030602u);
         vp[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w0, 1.0f, false);
         vp[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w0, 1.0f, true);
         vp[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w1, 1.0f, false);
         vp[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w1, 1.0f, true);
-        vp[4] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w2, 1.0f, false);
-        vp[5] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w2, 1.0f, true);
-        vp[6] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w3, 1.0f, false);
-        vp[7] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w3, 1.0f, true);
+    }
+};
+
+// FP8 pools, 8 dims (8 bytes) per lane and token, rows of 16 lanes: for 8
+// and 16 query heads per KV head, whose accumulators fill the registers.
+struct KvFp8 : KvFp8Base<2> {
+    using Word = uint2;
+    static __device__ __forceinline__ Word load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    }
+    static __device__ __forceinline__ void k_pairs(const Word& w, uint32_t (&kp)[4]) {
+        k_pairs_of({w.x, w.y}, kp);
+    }
+    static __device__ __forceinline__ void v_floats(const Word& w, float (&v)[8]) {
+        v_floats_of({w.x, w.y}, v);
+    }
+    static __device__ __forceinline__ void v_pairs4(const Word& a, const Word& b, int j,
+                                                    f16x2_t (&vp)[4]) {
+        pairs4(j == 0 ? a.x : a.y, j == 0 ? b.x : b.y, vp);
+    }
+};
+
+// FP8 pools, 16 dims (16 bytes) per lane and token, rows of 8 lanes: half
+// the lanes share a token, so the row sums take three DPP steps instead of
+// four and each softmax value is computed by 8 lanes instead of 16 (up to 4
+// query heads per KV head).
+struct KvFp8Wide : KvFp8Base<4> {
+    using Word = uint4;
+    static __device__ __forceinline__ Word load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    }
+    static __device__ __forceinline__ void k_pairs(const Word& w, uint32_t (&kp)[8]) {
+        k_pairs_of({w.x, w.y, w.z, w.w}, kp);
+    }
+    static __device__ __forceinline__ void v_floats(const Word& w, float (&v)[16]) {
+        v_floats_of({w.x, w.y, w.z, w.w}, v);
+    }
+    static __device__ __forceinline__ void v_pairs4(const Word& a, const Word& b, int j,
+                                                    f16x2_t (&vp)[4]) {
+        const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
+        const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+        pairs4(aw[j], bw[j], vp);
     }
 };
 
 template <typename KV>
+struct Layout {
+    static constexpr int kDims = KV::kDims;                  // per lane and token
+    static constexpr int kRowLanes = kHeadDim / kDims;       // lanes sharing a token
+    static constexpr int kRows = 64 / kRowLanes;             // tokens per load
+    static constexpr int kLoads = kTileTokens / kRows;       // loads per lane per tile
+};
+
+template <int LANES>
+__device__ __forceinline__ float row_sum(float x) {
+    if constexpr (LANES == 16) return row_sum16(x);
+    else return row_sum8(x);
+}
+
+template <typename KV>
 struct Tile {
-    typename KV::Word k[kLoads];
-    typename KV::Word v[kLoads];
+    typename KV::Word k[Layout<KV>::kLoads];
+    typename KV::Word v[Layout<KV>::kLoads];
 };
 
 // Loads one tile: `kt` / `vt` address the tile's first row for this KV head
 // in the K / V pool, `voff[i]` is this lane's byte offset of load group i
-// (tokens 4i + row, dims 8c .. 8c + 7): buffer loads with a scalar base and
-// a 32-bit lane offset, so no per-lane 64-bit addresses are kept.
+// (tokens kRows i + row, its dims): buffer loads with a scalar base and a
+// 32-bit lane offset, so no per-lane 64-bit addresses are kept.
 template <typename KV>
 __device__ __forceinline__ void load_tile(Tile<KV>& t, const char* kt, const char* vt,
-                                          const uint32_t (&voff)[kLoads]) {
+                                          const uint32_t (&voff)[Layout<KV>::kLoads]) {
     const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kt);
     const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vt);
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) t.k[i] = KV::load(rk, voff[i]);
+    for (int i = 0; i < Layout<KV>::kLoads; ++i) t.k[i] = KV::load(rk, voff[i]);
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) t.v[i] = KV::load(rv, voff[i]);
+    for (int i = 0; i < Layout<KV>::kLoads; ++i) t.v[i] = KV::load(rv, voff[i]);
 }
 
-template <int G>
+template <int G, int ND>
 struct State {
-    float m[G];       // running max (log2 domain), uniform across the row
-    float l[G];       // running sum, uniform across the row
-    float acc[G][8];  // unnormalised output, dims 8c..8c+7 of this lane
-    float alpha[G];   // last rescale factor exp2(m_old - m_new) (bf16 pools)
+    float m[G];        // running max (log2 domain), uniform across the row
+    float l[G];        // running sum, uniform across the row
+    float acc[G][ND];  // unnormalised output, this lane's dims
+    float alpha[G];    // last rescale factor exp2(m_old - m_new) (bf16 pools)
 };
 
 // One 16-token tile: QK, online-softmax update, PV.  `ntok_left` is the
@@ -153,25 +215,29 @@ struct State {
 // Raw scores are maximised unscaled (the scale is >= 0 after the sign of q
 // absorbed a negative one) and scaled inside the exponent's FMA.
 template <typename KV, int G, bool PARTIAL>
-__device__ __forceinline__ void process_tile(State<G>& st, const Tile<KV>& t, const uint4 (&qv)[G],
-                                             float c, int row, int ntok_left) {
+__device__ __forceinline__ void process_tile(State<G, KV::kDims>& st, const Tile<KV>& t,
+                                             const uint32_t (&qv)[G][KV::kDims / 2], float c,
+                                             int row, int ntok_left) {
+    constexpr int kLoads = Layout<KV>::kLoads;
+    constexpr int kRows = Layout<KV>::kRows;
+    constexpr int ND = KV::kDims;
     float s[kLoads][G];
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-        const uint4 k = KV::k_pairs(t.k[i]);
+        uint32_t k[ND / 2];
+        KV::k_pairs(t.k[i], k);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            float d = dot2_bf16(k.x, qv[g].x, 0.0f);
-            d = dot2_bf16(k.y, qv[g].y, d);
-            d = dot2_bf16(k.z, qv[g].z, d);
-            d = dot2_bf16(k.w, qv[g].w, d);
-            s[i][g] = row_sum16(d);
+            float d = dot2_bf16(k[0], qv[g][0], 0.0f);
+#pragma unroll
+            for (int j = 1; j < ND / 2; ++j) d = dot2_bf16(k[j], qv[g][j], d);
+            s[i][g] = row_sum<Layout<KV>::kRowLanes>(d);
         }
         if (PARTIAL) {
             // Tokens past the end may hold anything: they must not raise the
             // maximum (lowest finite value, so that a zero scale stays finite)
             // and get p = 0 below.
-            const bool valid = (4 * i + row) < ntok_left;
+            const bool valid = (kRows * i + row) < ntok_left;
 #pragma unroll
             for (int g = 0; g < G; ++g) s[i][g] = valid ? s[i][g] : -3.402823466e38f;
         }
@@ -182,7 +248,9 @@ __device__ __forceinline__ void process_tile(State<G>& st, const Tile<KV>& t, co
         bool grew = false;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            const float bm = fmaxf(fmaxf(s[0][g], s[1][g]), fmaxf(s[2][g], s[3][g])) * c;
+            float bm = kLoads == 4 ? fmaxf(fmaxf(s[0][g], s[1][g]), fmaxf(s[2][g], s[3][g]))
+                                   : fmaxf(s[0][g], s[1][g]);
+            bm *= c;
             const float mn = fmaxf(st.m[g], bm);
             grew |= mn > st.m[g];
             m_old[g] = st.m[g];
@@ -191,7 +259,7 @@ __device__ __forceinline__ void process_tile(State<G>& st, const Tile<KV>& t, co
 #pragma unroll
             for (int i = 0; i < kLoads; ++i) {
                 p[i][g] = fast_exp2(fmaf(s[i][g], c, -mn));
-                if (PARTIAL) p[i][g] = (4 * i + row) < ntok_left ? p[i][g] : 0.0f;
+                if (PARTIAL) p[i][g] = (kRows * i + row) < ntok_left ? p[i][g] : 0.0f;
                 sum[g] += p[i][g];
             }
         }
@@ -206,7 +274,7 @@ __device__ __forceinline__ void process_tile(State<G>& st, const Tile<KV>& t, co
             for (int g = 0; g < G; ++g) {
                 alpha[g] = fast_exp2(m_old[g] - st.m[g]);
 #pragma unroll
-                for (int d = 0; d < 8; ++d) st.acc[g][d] *= alpha[g];
+                for (int d = 0; d < ND; ++d) st.acc[g][d] *= alpha[g];
             }
         }
 #pragma unroll
@@ -215,7 +283,9 @@ __device__ __forceinline__ void process_tile(State<G>& st, const Tile<KV>& t, co
         bool grew = false;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            const float bm = fmaxf(fmaxf(s[0][g], s[1][g]), fmaxf(s[2][g], s[3][g])) * c;
+            float bm = kLoads == 4 ? fmaxf(fmaxf(s[0][g], s[1][g]), fmaxf(s[2][g], s[3][g]))
+                                   : fmaxf(s[0][g], s[1][g]);
+            bm *= c;
             const float mn = fmaxf(st.m[g], bm);
             grew |= mn > st.m[g];
             const float alpha = fast_exp2(st.m[g] - mn);
@@ -224,7 +294,7 @@ __device__ __forceinline__ void process_tile(State<G>& st, const Tile<KV>& t, co
 #pragma unroll
             for (int i = 0; i < kLoads; ++i) {
                 p[i][g] = fast_exp2(fmaf(s[i][g], c, -mn));
-                if (PARTIAL) p[i][g] = (4 * i + row) < ntok_left ? p[i][g] : 0.0f;
+                if (PARTIAL) p[i][g] = (kRows * i + row) < ntok_left ? p[i][g] : 0.0f;
                 sum += p[i][g];
             }
             st.l[g] = fmaf(st.l[g], alpha, sum);
@@ -236,38 +306,44 @@ __device__ __forceinline__ void process_tile(State<G>& st, const Tile<KV>& t, co
 #pragma unroll
             for (int g = 0; g < G; ++g)
 #pragma unroll
-                for (int d = 0; d < 8; ++d) st.acc[g][d] *= st.alpha[g];
+                for (int d = 0; d < ND; ++d) st.acc[g][d] *= st.alpha[g];
         }
     }
     if constexpr (KV::kPairedPV && !PARTIAL) {
 #pragma unroll
         for (int i = 0; i < kLoads; i += 2) {
-            f16x2_t vp[8];
-            KV::v_pairs(t.v[i], t.v[i + 1], vp);
+            f16x2_t pp[G];
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const f16x2_t pp = {(_Float16)p[i][g], (_Float16)p[i + 1][g]};
+            for (int g = 0; g < G; ++g) pp[g] = f16x2_t{(_Float16)p[i][g], (_Float16)p[i + 1][g]};
+            // four dims at a time, so few pairs are live at once
 #pragma unroll
-                for (int d = 0; d < 8; ++d)
-                    st.acc[g][d] = __builtin_amdgcn_fdot2(vp[d], pp, st.acc[g][d], false);
+            for (int j = 0; j < ND / 4; ++j) {
+                f16x2_t vp[4];
+                KV::v_pairs4(t.v[i], t.v[i + 1], j, vp);
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        st.acc[g][4 * j + e] =
+                            __builtin_amdgcn_fdot2(vp[e], pp[g], st.acc[g][4 * j + e], false);
             }
         }
     } else {
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) {
-            float v[8];
+            float v[ND];
             KV::v_floats(t.v[i], v);
             if (PARTIAL) {
                 // A masked token has p = 0, but its pool slot may hold anything
                 // (NaN included): zero the value so 0 * v stays 0.
-                const bool valid = (4 * i + row) < ntok_left;
+                const bool valid = (kRows * i + row) < ntok_left;
 #pragma unroll
-                for (int d = 0; d < 8; ++d) v[d] = valid ? v[d] : 0.0f;
+                for (int d = 0; d < ND; ++d) v[d] = valid ? v[d] : 0.0f;
             }
 #pragma unroll
             for (int g = 0; g < G; ++g) {
 #pragma unroll
-                for (int d = 0; d < 8; ++d) st.acc[g][d] = fmaf(p[i][g], v[d], st.acc[g][d]);
+                for (int d = 0; d < ND; ++d) st.acc[g][d] = fmaf(p[i][g], v[d], st.acc[g][d]);
             }
         }
     }
@@ -430,10 +506,12 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
     const int64_t U = s_cum[num_seqs];
     // never more workers than tiles, so every worker's range is non-empty
     const int64_t W = num_workers < U ? num_workers : U;
+    using L = Layout<KV>;
+    constexpr int ND = KV::kDims;
     const int lane = tid & 63;
     const int kvh = blockIdx.y * (nthr >> 6) + (tid >> 6);
-    const int row = lane >> 4;
-    const int col = lane & 15;
+    const int row = lane / L::kRowLanes;
+    const int col = lane % L::kRowLanes;
     const int64_t w = blockIdx.x;
     int64_t t = w < W ? worker_start(w, U, W) : 0;
     const int64_t t_end = w < W ? worker_start(w + 1, U, W) : 0;
@@ -441,10 +519,11 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
     const uint32_t neg = scale_log2 < 0.0f ? 0x80008000u : 0u;
     const float c = fabsf(scale_log2);
     const size_t row_bytes = (size_t)num_kv_heads * D * KV::kElemBytes;
-    uint32_t voff[kLoads];
+    uint32_t voff[L::kLoads];
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i)
-        voff[i] = (uint32_t)((4 * i + row) * row_bytes + ((size_t)kvh * D + col * 8) * KV::kElemBytes);
+    for (int i = 0; i < L::kLoads; ++i)
+        voff[i] = (uint32_t)((L::kRows * i + row) * row_bytes +
+                             ((size_t)kvh * D + col * ND) * KV::kElemBytes);
     const char* kbase = reinterpret_cast<const char*>(k_cache);
     const char* vbase = reinterpret_cast<const char*>(v_cache);
     bool first_piece = true;
@@ -465,19 +544,23 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
         const int ctx = clamp_ctx(context_lens[seq], max_context_len);
 
         const size_t head_row = ((size_t)row_of(cu_q_lens, seq) * num_q_heads + (size_t)kvh * G) * D;
-        uint4 qv[G];
+        uint32_t qv[G][ND / 2];  // this lane's dims of each query head, bf16 pairs
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            qv[g] = *reinterpret_cast<const uint4*>(q + head_row + (size_t)g * D + col * 8);
-            qv[g].x ^= neg; qv[g].y ^= neg; qv[g].z ^= neg; qv[g].w ^= neg;
-        }
-        State<G> st;
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int w8 = 0; w8 < ND / 8; ++w8) {
+                const uint4 x = *reinterpret_cast<const uint4*>(q + head_row + (size_t)g * D +
+                                                                col * ND + 8 * w8);
+                qv[g][4 * w8] = x.x ^ neg; qv[g][4 * w8 + 1] = x.y ^ neg;
+                qv[g][4 * w8 + 2] = x.z ^ neg; qv[g][4 * w8 + 3] = x.w ^ neg;
+            }
+        State<G, ND> st;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             st.m[g] = kNegBig;
             st.l[g] = 0.0f;
 #pragma unroll
-            for (int d = 0; d < 8; ++d) st.acc[g][d] = 0.0f;
+            for (int d = 0; d < ND; ++d) st.acc[g][d] = 0.0f;
         }
 
         IdWindow ids;
@@ -534,22 +617,23 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
             }
         }
 
-        // Merge the four row streams: M = max m_r, l = sum l_r 2^(m_r - M),
+        // Merge the row streams: M = max m_r, l = sum l_r 2^(m_r - M),
         // acc = sum acc_r 2^(m_r - M).  A row that saw no token has
         // m = kNegBig, l = 0, acc = 0 and drops out.
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            float mx = fmaxf(st.m[g], xor_lane(st.m[g], 16));
-            mx = fmaxf(mx, xor_lane(mx, 32));
+            float mx = st.m[g];
+#pragma unroll
+            for (int o = L::kRowLanes; o < 64; o <<= 1) mx = fmaxf(mx, xor_lane(mx, o));
             const float f = fast_exp2(st.m[g] - mx);
             float lt = st.l[g] * f;
-            lt += xor_lane(lt, 16);
-            lt += xor_lane(lt, 32);
 #pragma unroll
-            for (int d = 0; d < 8; ++d) {
+            for (int o = L::kRowLanes; o < 64; o <<= 1) lt += xor_lane(lt, o);
+#pragma unroll
+            for (int d = 0; d < ND; ++d) {
                 float x = st.acc[g][d] * f;
-                x += xor_lane(x, 16);
-                x += xor_lane(x, 32);
+#pragma unroll
+                for (int o = L::kRowLanes; o < 64; o <<= 1) x += xor_lane(x, o);
                 st.acc[g][d] = x;
             }
             st.m[g] = mx;
@@ -558,21 +642,26 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
 
         const bool whole = (t == seg_t0) && (piece_end == seg_t1);
         const int slot = first_piece ? 0 : 1;
-        // Row r stores heads g = r, r + 4, ...
+        // Row r stores heads g = r, r + kRows, ...
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            if ((g & 3) != row) continue;
+            if (g % L::kRows != row) continue;
             if (whole) {
                 const float inv = out_scale / st.l[g];
-                float o[8];
 #pragma unroll
-                for (int d = 0; d < 8; ++d) o[d] = st.acc[g][d] * inv;
-                store8<OUT_BF16>(out, head_row + (size_t)g * D + col * 8, o);
+                for (int w8 = 0; w8 < ND / 8; ++w8) {
+                    float o[8];
+#pragma unroll
+                    for (int d = 0; d < 8; ++d) o[d] = st.acc[g][8 * w8 + d] * inv;
+                    store8<OUT_BF16>(out, head_row + (size_t)g * D + col * ND + 8 * w8, o);
+                }
             } else {
                 float* r = rec + ((size_t)(w * 2 + slot) * num_q_heads + (size_t)kvh * G + g) * kRecStride;
-                float4* pa = reinterpret_cast<float4*>(r + col * 8);
-                pa[0] = make_float4(st.acc[g][0], st.acc[g][1], st.acc[g][2], st.acc[g][3]);
-                pa[1] = make_float4(st.acc[g][4], st.acc[g][5], st.acc[g][6], st.acc[g][7]);
+                float4* pa = reinterpret_cast<float4*>(r + col * ND);
+#pragma unroll
+                for (int w4 = 0; w4 < ND / 4; ++w4)
+                    pa[w4] = make_float4(st.acc[g][4 * w4], st.acc[g][4 * w4 + 1],
+                                         st.acc[g][4 * w4 + 2], st.acc[g][4 * w4 + 3]);
                 if (col == 0) {
                     r[D] = st.m[g];
                     r[D + 1] = st.l[g];
@@ -742,6 +831,22 @@ hipError_t launch_decode_kv(const DecodeArgs& a, hipStream_t s) {
     return a.block_size == 16 ? launch_decode_bs<KV, 16>(a, s) : launch_decode_bs<KV, 32>(a, s);
 }
 
+// FP8 pools: the wide layout (16 dims per lane) up to 4 query heads per KV
+// head; with 8 or 16 its accumulators would take more registers than the
+// VALU work it saves (8: 491 VGPRs, measured 8 % slower than the narrow
+// layout), so those keep 8 dims per lane.
+template <int BS>
+hipError_t launch_decode_fp8_bs(const DecodeArgs& a, hipStream_t s) {
+    switch (a.num_q_heads / a.num_kv_heads) {
+        case 1: return launch_decode_g<KvFp8Wide, BS, 1>(a, s);
+        case 2: return launch_decode_g<KvFp8Wide, BS, 2>(a, s);
+        case 4: return launch_decode_g<KvFp8Wide, BS, 4>(a, s);
+        case 8: return launch_decode_g<KvFp8, BS, 8>(a, s);
+        case 16: return launch_decode_g<KvFp8, BS, 16>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
 int64_t decode_max_workers(int num_seqs, int max_context_len) {
@@ -760,7 +865,10 @@ size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, i
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-    return a.kv_fp8 ? launch_decode_kv<KvFp8>(a, stream) : launch_decode_kv<KvBf16>(a, stream);
+    if (a.kv_fp8)
+        return a.block_size == 16 ? launch_decode_fp8_bs<16>(a, stream)
+                                  : launch_decode_fp8_bs<32>(a, stream);
+    return launch_decode_kv<KvBf16>(a, stream);
 }
 
 }  // namespace pkv

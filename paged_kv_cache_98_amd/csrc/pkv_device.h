@@ -68,6 +68,14 @@ __device__ __forceinline__ float row_sum16(float x) {
     return x;
 }
 
+// The same over each half row of 8 lanes (a wave seen as 8 rows of 8).
+__device__ __forceinline__ float row_sum8(float x) {
+    x += dpp_mov<kDppQuadXor1>(x);
+    x += dpp_mov<kDppQuadXor2>(x);
+    x += dpp_mov<kDppRowHalfMirror>(x);
+    return x;
+}
+
 // Exchange across rows: value of lane ^ 16 / lane ^ 32 (LDS-crossbar permute).
 __device__ __forceinline__ float xor_lane(float x, int mask) {
     int lane = __lane_id();
