@@ -16,6 +16,8 @@ Contents
     copy-on-write.
   * ``fp8``: the E4M3 format, the quantised append and the fp64 decode over
     an FP8 cache with per-cache scales.
+  * ``tree``: fp64 attention of token-tree verification chunks (each node
+    sees the context and its own path).
 
 Every function names the passage it follows.  Functions without an
 independent pin say "parity unpinned" in their docstring (none at present).
