@@ -282,6 +282,8 @@ def workload_by_name(name):
         # speculative-decoding verification: 6 causal query rows per sequence
         "spec_verify": lambda: W.spec_verify(),
         "spec_verify_long": lambda: W.spec_verify(batch=8, lo=32768, hi=131072, seed=1007),
+        # token-tree verification: 16-node candidate trees per sequence
+        "spec_verify_tree": lambda: W.spec_verify_tree(),
         "mixed_prefill": lambda: W.mixed_prefill(),
     }
     if name not in table:
@@ -403,6 +405,8 @@ def main():
 
     if not w.is_decode:
         out = torch.empty((w.total_q, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    is_tree = args.workload == "spec_verify_tree"
+    tree_mask = W.tree_masks(w).to(dev) if is_tree else None
 
     def attend():
         if kv_fp8:
@@ -418,7 +422,8 @@ def main():
             pkv.paged_prefill_attn(b.q, b.cu_q_lens, b.k_cache, b.v_cache, b.block_table,
                                    b.context_lens, w.scale, max_context_len=w.max_context_len,
                                    max_q_len=w.max_q_len, causal=True, out=out,
-                                   workspace=ws if ws_bytes else None, stream=stream)
+                                   workspace=ws if ws_bytes else None, stream=stream,
+                                   tree_mask=tree_mask)
 
     def step(ev=None):
         if ev is not None:
@@ -482,8 +487,10 @@ def main():
         print(f"[bench] verify attn {dec_avg * 1e3:.1f} us: KV {achieved:.0f} GB/s, "
               f"{flops / (dec_avg * 1e-3) / 1e12:.1f} TFLOP/s", file=sys.stderr, flush=True)
         rec = {
-            "metric": "paged verify attn (few causal query rows per sequence): achieved KV "
-                      "HBM GB/s + verified tokens/s",
+            "metric": ("paged token-tree verify attn (a candidate tree per sequence, each node "
+                       "seeing its path): achieved KV HBM GB/s + verified tokens/s" if is_tree
+                       else "paged verify attn (few causal query rows per sequence): achieved "
+                            "KV HBM GB/s + verified tokens/s"),
             "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -496,7 +503,8 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": hbm_traffic(w.name),
-                         "kernel": "paged_prefill_attn (few-row chunks)",
+                         "kernel": ("paged_prefill_attn_tree (few-row chunks, tree masks)"
+                                    if is_tree else "paged_prefill_attn (few-row chunks)"),
                          "algorithmic_bytes_per_launch": kv_bytes},
         }
         print(json.dumps(rec), flush=True)

@@ -397,6 +397,34 @@ int pkv_bm_refcount(const pkv_block_manager *bm, int64_t block, int32_t *count);
 int pkv_bm_block_table(const pkv_block_manager *bm, const int64_t *seq_ids, int num_seqs,
                        int32_t *table, int max_blocks_per_seq, int32_t *context_lens);
 
+/*
+ * paged_prefill_attn_tree -- token-tree verification ("让 Agent 跑得快：LLM
+ * 推理服务", section 六, Token Tree Verification: the draft candidates form a
+ * tree, checked by the target model in one pass).  Arguments as
+ * pkv_paged_prefill_attn with causal = 1, plus
+ *   tree_mask   [num_q_tokens] uint64 device array: the Lq_i new tokens of
+ *               sequence i are the nodes of its tree in topological order
+ *               (every node after its parent); query row r sees every
+ *               cached key before the new tokens and new token j exactly
+ *               when bit j of tree_mask[cu_q_lens[i] + r] is set (its path
+ *               to the root, itself included).  Bits above r are ignored:
+ *               a node never sees a later one.  A mask of bits 0 .. r gives
+ *               plain causal attention.
+ * Every node must see itself (bit r of its own mask set), so that each row
+ * sees at least one key.  tree_mask must be 8-byte aligned (PKV_ERR_ALIGN)
+ * and non-NULL when there are rows (PKV_ERR_NULL); max_q_len <= 64
+ * (PKV_ERR_UNSUPPORTED otherwise).  Sequences with a single row take the
+ * decode path, as in pkv_paged_prefill_attn.
+ */
+int pkv_paged_prefill_attn_tree(void *out, int out_dtype, const void *q,
+                                const int32_t *cu_q_lens, const uint64_t *tree_mask,
+                                const void *k_cache, const void *v_cache,
+                                const int32_t *block_table, int max_blocks_per_seq,
+                                const int32_t *context_lens, int max_context_len, int max_q_len,
+                                int num_q_tokens, int num_seqs, int num_q_heads, int num_kv_heads,
+                                int head_dim, int block_size, float scale, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

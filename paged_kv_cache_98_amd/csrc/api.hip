@@ -18,6 +18,8 @@ constexpr int kMaxDecodeSeqs = 16383;
 // A decode workgroup serves up to 8 KV heads, one wave each; 16 heads run as
 // two groups of 8.
 constexpr int kMaxDecodeKvHeads = 16;
+// A token-tree mask is one 64-bit word per node.
+constexpr int kMaxTreeNodes = 64;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -249,13 +251,17 @@ size_t pkv_prefill_workspace_bytes(int num_seqs, int num_q_tokens, int max_q_len
                              head_dim, max_context_len, nullptr);
 }
 
-int pkv_paged_prefill_attn(void* out, int out_dtype, const void* q, const int32_t* cu_q_lens,
-                           const void* k_cache, const void* v_cache, const int32_t* block_table,
-                           int max_blocks_per_seq, const int32_t* context_lens,
-                           int max_context_len, int max_q_len, int num_q_tokens, int num_seqs,
-                           int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                           float scale, int causal, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+}  // extern "C"
+
+namespace {
+
+int prefill_call(void* out, int out_dtype, const void* q, const int32_t* cu_q_lens,
+                 const void* k_cache, const void* v_cache, const int32_t* block_table,
+                 int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
+                 int max_q_len, int num_q_tokens, int num_seqs, int num_q_heads,
+                 int num_kv_heads, int head_dim, int block_size, float scale, int causal,
+                 const uint64_t* tree_mask, void* workspace, size_t workspace_bytes,
+                 void* stream) {
     int st = check_attention_shape(max_blocks_per_seq, max_context_len, num_seqs, num_q_heads,
                                    num_kv_heads, head_dim, block_size, out_dtype);
     if (st != PKV_OK) return st;
@@ -313,6 +319,7 @@ int pkv_paged_prefill_attn(void* out, int out_dtype, const void* q, const int32_
     a.split_tiles = split_tiles;
     a.max_pieces = max_pieces;
     a.records = records;
+    a.tree_mask = tree_mask;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (max_q_len > 1) {
         st = to_status(pkv::launch_prefill(a, s));
@@ -341,6 +348,40 @@ int pkv_paged_prefill_attn(void* out, int out_dtype, const void* q, const int32_
     d.max_workers = pkv::decode_max_workers(num_seqs, max_context_len);
     d.cu_q_lens = cu_q_lens;
     return to_status(pkv::launch_decode(d, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_prefill_attn(void* out, int out_dtype, const void* q, const int32_t* cu_q_lens,
+                           const void* k_cache, const void* v_cache, const int32_t* block_table,
+                           int max_blocks_per_seq, const int32_t* context_lens,
+                           int max_context_len, int max_q_len, int num_q_tokens, int num_seqs,
+                           int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                           float scale, int causal, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    return prefill_call(out, out_dtype, q, cu_q_lens, k_cache, v_cache, block_table,
+                        max_blocks_per_seq, context_lens, max_context_len, max_q_len,
+                        num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                        scale, causal, nullptr, workspace, workspace_bytes, stream);
+}
+
+int pkv_paged_prefill_attn_tree(void* out, int out_dtype, const void* q,
+                                const int32_t* cu_q_lens, const uint64_t* tree_mask,
+                                const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, int max_blocks_per_seq,
+                                const int32_t* context_lens, int max_context_len, int max_q_len,
+                                int num_q_tokens, int num_seqs, int num_q_heads, int num_kv_heads,
+                                int head_dim, int block_size, float scale, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    if (max_q_len > kMaxTreeNodes) return PKV_ERR_UNSUPPORTED;
+    if (num_seqs > 0 && num_q_tokens > 0 && !tree_mask) return PKV_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(tree_mask) & 7) return PKV_ERR_ALIGN;
+    return prefill_call(out, out_dtype, q, cu_q_lens, k_cache, v_cache, block_table,
+                        max_blocks_per_seq, context_lens, max_context_len, max_q_len,
+                        num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                        scale, 1, tree_mask, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -90,6 +90,7 @@ struct PrefillArgs {
     int split_tiles = 0;
     int max_pieces = 1;
     float* records = nullptr;  // workspace: [max_pieces][num_q_tokens][num_q_heads][132]
+    const uint64_t* tree_mask = nullptr;  // [num_q_tokens] token-tree masks, or none
 };
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);

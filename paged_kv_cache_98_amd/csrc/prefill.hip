@@ -34,6 +34,12 @@
 //     bf16, V transposed to [dim][key] fp16 while it is staged; the next
 //     tile's global loads are in flight while the current tile is computed.
 //
+// Token trees ("让 Agent 跑得快", section 六, Token Tree Verification): with
+// a mask per query row, a verify chunk's rows are the nodes of a draft tree
+// in topological order, and row r sees the cached context plus the chunk's
+// tokens j whose bit is set in its mask (its path to the root); the masks
+// are applied, with the causal limit, in the tiles that hold chunk keys.
+//
 // Key split (chunks of a few rows, as in speculative-decoding verification:
 // at most 64 of the 128 columns used): such a call reads every key once
 // per KV head for a handful of queries, so it is bandwidth-bound.  When its
@@ -208,7 +214,8 @@ constexpr float kLazyMax = 8.0f;  // p < 2^8 between rescales
 template <bool MASK>
 __device__ __forceinline__ void softmax_half(f32x16_t& s, f16x8_t (&pf)[2], f32x16_t (&o)[4],
                                              float& m_run, float& l_run, float cl2, int kb0, int h,
-                                             int pos, int ctx, bool diag) {
+                                             int pos, int ctx, bool diag, uint64_t tmask,
+                                             int tbase) {
     // four independent partial maxima / sums, so neither is one long
     // dependent chain
     float mt4[4] = {-3.402823466e38f, -3.402823466e38f, -3.402823466e38f, -3.402823466e38f};
@@ -216,7 +223,10 @@ __device__ __forceinline__ void softmax_half(f32x16_t& s, f16x8_t (&pf)[2], f32x
     for (int e = 0; e < 16; ++e) {
         if (MASK) {
             const int key = kb0 + 8 * (e >> 2) + 4 * h + (e & 3);
-            const bool ok = (!diag || key <= pos) && key < ctx;
+            // a token-tree node also drops the chunk's keys off its path
+            // (key - tbase < 64 wherever the mask is read)
+            const bool ok = (!diag || key <= pos) && key < ctx &&
+                            (key < tbase || ((tmask >> ((key - tbase) & 63)) & 1));
             s[e] = ok ? s[e] : -3.402823466e38f;
         }
         mt4[e & 3] = fmaxf(mt4[e & 3], s[e]);
@@ -281,7 +291,8 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
                     int max_blocks_per_seq, const int32_t* __restrict__ context_lens,
                     int max_context_len, int num_seqs, int num_q_heads, int num_kv_heads,
                     float scale_log2, int causal, int decode_rows_elsewhere, int split_tiles,
-                    int max_pieces, float* __restrict__ rec, int num_q_tokens) {
+                    int max_pieces, float* __restrict__ rec, int num_q_tokens,
+                    const uint64_t* __restrict__ tree_mask) {
     constexpr int P = kCols / G;  // query positions per workgroup
     __shared__ __attribute__((aligned(16))) uint16_t s_ks[2][kKsElems];
     __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kVtElems];
@@ -387,6 +398,9 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
     // online softmax, then O^T += V^T . P^T with A = V^T rows (dims) and the
     // keys in accumulator order -- then stage the next tile in LDS.
     const bool diag = causal != 0;
+    // this column's token-tree mask over the chunk's keys (none: all seen)
+    const int tbase = tree_mask ? pos0 : 0x7fffffff;
+    const uint64_t tmask = tree_mask && col_valid ? tree_mask[q_begin + r] : ~0ull;
     auto run_tile = [&](int j, auto mask_c, bool next) {
         constexpr bool MASK = decltype(mask_c)::value;
         const int k0 = j * kKT;
@@ -411,7 +425,8 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             f16x8_t pf[2];  // P^T fragments, keys 16 ks .. 16 ks + 15 of the half
-            softmax_half<MASK>(sc[kb], pf, o, m_run, l_run, cl2, k0 + 32 * kb, h, pos, ctx, diag);
+            softmax_half<MASK>(sc[kb], pf, o, m_run, l_run, cl2, k0 + 32 * kb, h, pos, ctx, diag,
+                               tmask, tbase);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
@@ -453,7 +468,9 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
         }
         return;
     }
-    const int first_pos = pos0 + r0;
+    // with token-tree masks every key of the chunk may be dropped, so masks
+    // start at the chunk's first position
+    const int first_pos = tree_mask ? pos0 : pos0 + r0;
     const int j_diag = causal ? (first_pos >= kKT - 1 ? (first_pos - (kKT - 1)) / kKT + 1 : 0) : ntiles;
     const int j_tail = ctx >= kKT ? (ctx - kKT) / kKT + 1 : 0;
     int j_plain = j_diag < j_tail ? j_diag : j_tail;
@@ -574,7 +591,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
                        a.max_blocks_per_seq, a.context_lens, a.max_context_len, a.num_seqs,
                        a.num_q_heads, a.num_kv_heads, a.scale_log2, a.causal ? 1 : 0,
                        a.decode_rows_elsewhere ? 1 : 0, a.split_tiles, pieces, a.records,
-                       a.num_q_tokens);
+                       a.num_q_tokens, a.tree_mask);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.split_tiles == 0) return e;
     dim3 mgrid(a.num_seqs, (a.max_q_len * a.num_q_heads + 3) / 4);

@@ -191,6 +191,37 @@ def spec_verify(batch: int = 64, gamma: int = 5, lo: int = 512, hi: int = 4096,
                          block_size=block_size, seed=seed)
 
 
+def spec_verify_tree(batch: int = 64, nodes: int = 16, lo: int = 512, hi: int = 4096,
+                     block_size: int = 16, seed: int = 1008) -> Workload:
+    """Token-tree verification ("让 Agent 跑得快：LLM 推理服务", section 六,
+    Token Tree Verification): each sequence appends a tree of `nodes`
+    candidate tokens (the last accepted token as its root) at the end of a
+    context ~ U[lo, hi]; the masks come from tree_masks().  8B-shaped heads."""
+    g = torch.Generator().manual_seed(seed)
+    ctx = torch.randint(lo, hi + 1, (batch,), generator=g).tolist()
+    return make_workload(f"spec_tree_b{batch}_n{nodes}", ctx, [nodes] * batch,
+                         block_size=block_size, seed=seed)
+
+
+def tree_masks(w: Workload, seed: int = None) -> torch.Tensor:
+    """One random tree per sequence over its new tokens, in topological
+    order: node 0 is the root and node r > 0 hangs under a uniformly drawn
+    earlier node.  Node r's mask has bit j set for every node j on its path
+    to the root, itself included.  [total_q] int64 (the uint64 bit
+    patterns), on the host."""
+    g = torch.Generator().manual_seed(w.seed + 77 if seed is None else seed)
+    out = []
+    for lq in w.q_lens:
+        if lq > 64:
+            raise ValueError("a tree has at most 64 nodes")
+        paths = []
+        for r in range(lq):
+            up = paths[int(torch.randint(0, r, (1,), generator=g))] if r else 0
+            paths.append(up | (1 << r))
+        out += [m - (1 << 64) if m >> 63 else m for m in paths]
+    return torch.tensor(out, dtype=torch.int64)
+
+
 def mixed_prefill(num_chunks: int = 4, chunk: int = 512, num_decodes: int = 128,
                   prefix: int = 800, tail_lo: int = 64, tail_hi: int = 2048,
                   block_size: int = 16, seed: int = 1005) -> Workload:

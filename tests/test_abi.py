@@ -120,6 +120,30 @@ def test_prefill_validation(lib):
     assert prefill(lib, nq=0, q=None) == E.PKV_OK
 
 
+def prefill_tree(lib, **kw):
+    a = dict(out=P, out_dtype=0, q=P, cu=P, tm=P, k=P, v=P, bt=P, mb=8, cl=P, maxctx=100,
+             maxq=50, nq=60, nseq=4, hq=8, hkv=2, d=128, bs=16, scale=0.1, ws=None, wsb=0,
+             stream=None)
+    a.update(kw)
+    return lib.pkv_paged_prefill_attn_tree(a["out"], a["out_dtype"], a["q"], a["cu"], a["tm"],
+                                           a["k"], a["v"], a["bt"], a["mb"], a["cl"],
+                                           a["maxctx"], a["maxq"], a["nq"], a["nseq"], a["hq"],
+                                           a["hkv"], a["d"], a["bs"], a["scale"], a["ws"],
+                                           a["wsb"], a["stream"])
+
+
+def test_prefill_tree_validation(lib):
+    E = binding
+    assert prefill_tree(lib, tm=None) == E.PKV_ERR_NULL
+    assert prefill_tree(lib, tm=ctypes.c_void_p(0x10004)) == E.PKV_ERR_ALIGN
+    assert prefill_tree(lib, maxq=65) == E.PKV_ERR_UNSUPPORTED  # one 64-bit word per node
+    assert prefill_tree(lib, cu=None) == E.PKV_ERR_NULL
+    assert prefill_tree(lib, maxq=101) == E.PKV_ERR_UNSUPPORTED
+    assert prefill_tree(lib, nq=201) == E.PKV_ERR_SHAPE
+    assert prefill_tree(lib, out=MIS) == E.PKV_ERR_ALIGN
+    assert prefill_tree(lib, nq=0, q=None, tm=None) == E.PKV_OK
+
+
 def append(lib, **kw):
     a = dict(kn=P, vn=P, sm=P, t=5, kc=P, vc=P, nb=10, bs=16, hkv=8, d=128, stream=None)
     a.update(kw)
