@@ -192,15 +192,16 @@ int pkv_paged_decode_attn_fp8(void *out, int out_dtype, const void *q, const voi
 /*
  * Workspace needed by pkv_paged_prefill_attn (bytes, >= 0; 0 for
  * inconsistent sizes).  Two parts, either of which may be absent: the
- * decode workspace for the batch's single-row sequences, and the records of
- * the key-range split.  The split applies to short chunks (max_q_len *
- * num_q_heads / num_kv_heads <= 64, as in speculative-decoding
- * verification) when their (128-column slot, KV head) items are fewer than
- * 256 (too few to fill the chip, as with a few long contexts): each item's
- * keys are cut into at most 32 pieces of at least 512 keys, aiming at about
- * 2048 workgroups, and every (piece, query row, query head) has a record
- * of 132 floats.  A call whose every sequence has exactly max_q_len > 1 rows
- * and no split needs none (workspace may be NULL).
+ * decode workspace for the batch's single-row sequences, and the part of the
+ * stream-K chunk path.  That path takes calls whose chunks fit one
+ * workgroup (2 <= max_q_len and max_q_len * num_q_heads / num_kv_heads <=
+ * 128 query columns, as in speculative-decoding verification): its part is
+ * the (num_seqs + 1) int32 unit prefix sums, 256-byte aligned, then records
+ * of 132 floats for 2 * max_q_len * (num_q_heads / num_kv_heads) columns
+ * of each of up to min(1024, num_seqs * num_kv_heads *
+ * ceil(max_context_len / 64)) workers.  A call whose every sequence has
+ * exactly max_q_len rows, more than 128 query columns per KV head, needs
+ * none (workspace may be NULL).  num_q_tokens is checked for consistency.
  */
 size_t pkv_prefill_workspace_bytes(int num_seqs, int num_q_tokens, int max_q_len,
                                    int num_q_heads, int num_kv_heads, int head_dim,
@@ -226,10 +227,12 @@ size_t pkv_prefill_workspace_bytes(int num_seqs, int num_q_tokens, int max_q_len
  *   num_q_tokens   host-side total query rows (= cu_q_lens[num_seqs])
  * Rows with Lq_i == 1 take the bandwidth-bound decode path (the split-KV
  * decode kernels, enqueued after the MFMA chunk kernel on the same stream);
- * longer chunks take the MFMA path.  Short chunks over long contexts (the
- * workspace comment above) split each chunk's keys into pieces handled by
- * separate workgroups, merged by a log-sum-exp fold in a second kernel.  num_seqs <= 16383 and num_kv_heads in
- * 1..8 or 16 when single-row sequences can be present.  QK^T runs as bf16 x bf16 MFMA with fp32 accumulation;
+ * longer chunks take the MFMA path.  Chunks that fit one workgroup (the
+ * workspace comment above) run stream-K: all (sequence, KV head, 64-key
+ * tile) units cut into equal ranges over the workgroups the GPU holds at
+ * once, items shared by two workers merged by a log-sum-exp fold in a
+ * second kernel.  num_seqs <= 16383 and num_kv_heads in 1..8 or 16 when
+ * single-row sequences can be present.  QK^T runs as bf16 x bf16 MFMA with fp32 accumulation;
  * P V runs as fp16 x fp16 MFMA with fp32 accumulation, V converted from bf16
  * to fp16 in registers: exact for |v| in [2^-14, 65504]; smaller magnitudes
  * keep an absolute error below 2^-25, and |v| > 65504 is outside the

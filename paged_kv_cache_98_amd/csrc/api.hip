@@ -49,22 +49,20 @@ int check_attention_shape(int max_blocks_per_seq, int max_context_len, int num_s
 int to_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH; }
 
 // Prefill workspace: the decode kernels' part for single-row sequences,
-// then, when the call's chunks are split over key ranges, the pieces'
-// records at *records_offset.
-size_t prefill_workspace(int num_seqs, int num_q_tokens, int max_q_len, int num_q_heads,
-                         int num_kv_heads, int head_dim, int max_context_len,
-                         size_t* records_offset) {
-    // records are per query head, so the KV head count does not matter here
+// then, when the call's chunks fit one workgroup (stream-K), that kernel's
+// prefix sums and records at *chunk_offset.
+size_t prefill_workspace(int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads,
+                         int head_dim, int max_context_len, size_t* chunk_offset) {
+    // decode records are per query head, so the KV head count does not matter here
     const size_t dec = pkv::decode_workspace_bytes(num_seqs, num_q_heads, 1, head_dim,
                                                    max_context_len);
-    int split_tiles = 0, max_pieces = 1;
-    pkv::prefill_split_plan(max_q_len, num_q_heads / num_kv_heads, max_context_len, num_seqs,
-                            num_kv_heads, &split_tiles, &max_pieces);
-    if (records_offset) *records_offset = 0;
-    if (split_tiles == 0) return dec;
+    if (chunk_offset) *chunk_offset = 0;
+    const int group = num_q_heads / num_kv_heads;
+    if (!pkv::prefill_streamk(max_q_len, group)) return dec;
     const size_t off = align_up(dec, 256);
-    if (records_offset) *records_offset = off;
-    return off + pkv::prefill_record_bytes(num_q_tokens, num_q_heads, max_pieces);
+    if (chunk_offset) *chunk_offset = off;
+    return off + pkv::prefill_streamk_bytes(num_seqs, max_q_len, group, num_kv_heads,
+                                            max_context_len);
 }
 
 }  // namespace
@@ -247,8 +245,8 @@ size_t pkv_prefill_workspace_bytes(int num_seqs, int num_q_tokens, int max_q_len
     if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         num_q_tokens < 0 || max_q_len < 0 || num_q_heads % num_kv_heads != 0)
         return 0;
-    return prefill_workspace(num_seqs, num_q_tokens, max_q_len, num_q_heads, num_kv_heads,
-                             head_dim, max_context_len, nullptr);
+    return prefill_workspace(num_seqs, max_q_len, num_q_heads, num_kv_heads, head_dim,
+                             max_context_len, nullptr);
 }
 
 }  // extern "C"
@@ -279,21 +277,14 @@ int prefill_call(void* out, int out_dtype, const void* q, const int32_t* cu_q_le
     const bool any_decode_rows = !uniform_chunks;
     const bool decode_limits_ok = num_seqs <= kMaxDecodeSeqs &&
                                   (num_kv_heads <= 8 || num_kv_heads == kMaxDecodeKvHeads);
-    float* records = nullptr;
-    int split_tiles = 0, max_pieces = 1;
-    pkv::prefill_split_plan(max_q_len, num_q_heads / num_kv_heads, max_context_len, num_seqs,
-                            num_kv_heads, &split_tiles, &max_pieces);
+    const bool streamk = pkv::prefill_streamk(max_q_len, num_q_heads / num_kv_heads);
     if (any_decode_rows && !decode_limits_ok) return PKV_ERR_UNSUPPORTED;
-    if (any_decode_rows || split_tiles > 0) {
-        size_t rec_off = 0;
-        const size_t need = any_decode_rows || split_tiles > 0
-            ? prefill_workspace(num_seqs, num_q_tokens, max_q_len, num_q_heads, num_kv_heads,
-                                head_dim, max_context_len, &rec_off)
-            : 0;
+    size_t chunk_off = 0;
+    if (any_decode_rows || streamk) {
+        const size_t need = prefill_workspace(num_seqs, max_q_len, num_q_heads, num_kv_heads,
+                                              head_dim, max_context_len, &chunk_off);
         if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
         if (!aligned16(workspace)) return PKV_ERR_ALIGN;
-        if (split_tiles > 0)
-            records = reinterpret_cast<float*>(static_cast<char*>(workspace) + rec_off);
     }
 
     pkv::PrefillArgs a;
@@ -316,9 +307,14 @@ int prefill_call(void* out, int out_dtype, const void* q, const int32_t* cu_q_le
     a.scale_log2 = scale * 1.4426950408889634f;
     a.causal = causal != 0;
     a.decode_rows_elsewhere = any_decode_rows;
-    a.split_tiles = split_tiles;
-    a.max_pieces = max_pieces;
-    a.records = records;
+    a.streamk = streamk;
+    if (streamk) {
+        char* base = static_cast<char*>(workspace) + chunk_off;
+        a.cum = reinterpret_cast<int32_t*>(base);
+        a.records = reinterpret_cast<float*>(
+            base + align_up((size_t)(num_seqs + 1) * sizeof(int32_t), 256));
+        a.max_workers = pkv::prefill_streamk_max_workers(num_seqs, num_kv_heads, max_context_len);
+    }
     a.tree_mask = tree_mask;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (max_q_len > 1) {

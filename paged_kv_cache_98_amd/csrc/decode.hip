@@ -379,15 +379,6 @@ template <int G>
 constexpr int max_waves_per_worker() { return G <= 4 ? 8 : 4; }
 constexpr int64_t kMaxWorkers = 1024;    // workgroups of 8 waves an MI355X holds at most
 
-// Worker w owns global tiles [worker_start(w), worker_start(w + 1)).
-__device__ __forceinline__ int64_t worker_start(int64_t w, int64_t U, int64_t W) {
-    return (w * U) / W;
-}
-// The worker whose range holds tile t.
-__device__ __forceinline__ int64_t worker_of(int64_t t, int64_t U, int64_t W) {
-    return ((t + 1) * W - 1) / U;
-}
-
 __device__ __forceinline__ int clamp_ctx(int ctx, int max_context_len) {
     return ctx < 0 ? 0 : (ctx > max_context_len ? max_context_len : ctx);
 }
@@ -748,33 +739,6 @@ decode_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
     store1<OUT_BF16>(out, e + 1, a1 * inv);
 }
 
-// Workgroups of `kern` that one CU holds at once, for this much dynamic LDS
-// (a pure function of the kernel and the device, cached per thread).
-hipError_t resident_blocks_per_cu(const void* kern, int threads, size_t lds, int* out) {
-    struct Entry { const void* kern; int threads; size_t lds; int dev; int blocks; };
-    static thread_local Entry cache[16];
-    static thread_local int next = 0;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    const size_t lds_key = (lds + 4095) / 4096 * 4096;
-    for (const Entry& c : cache)
-        if (c.kern == kern && c.threads == threads && c.lds == lds_key && c.dev == dev) {
-            *out = c.blocks;
-            return hipSuccess;
-        }
-    int n = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, threads, lds_key);
-    if (e != hipSuccess) return e;
-    int cus = 0;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    *out = (n < 1 ? 1 : n) * cus;
-    cache[next] = Entry{kern, threads, lds_key, dev, *out};
-    next = (next + 1) % 16;
-    return hipSuccess;
-}
-
 template <typename KV, int BS, int G, bool OUT_BF16>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     auto kern = decode_streamk_kernel<KV, BS, G, OUT_BF16>;
@@ -786,7 +750,7 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     const int threads = 64 * waves;
     const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int32_t);
     int resident = 0;
-    hipError_t e = resident_blocks_per_cu(reinterpret_cast<const void*>(kern), threads, lds,
+    hipError_t e = resident_workgroups(reinterpret_cast<const void*>(kern), threads, lds,
                                           &resident);
     if (e != hipSuccess) return e;
     // as many workers as the chip holds at once, never more than the records
@@ -848,6 +812,33 @@ hipError_t launch_decode_fp8_bs(const DecodeArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+// Workgroups of `kern` the device holds at once, for this much dynamic LDS
+// (a pure function of the kernel and the device, cached per thread).
+hipError_t resident_workgroups(const void* kern, int threads, size_t lds, int* out) {
+    struct Entry { const void* kern; int threads; size_t lds; int dev; int blocks; };
+    static thread_local Entry cache[16];
+    static thread_local int next = 0;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const size_t lds_key = (lds + 4095) / 4096 * 4096;
+    for (const Entry& c : cache)
+        if (c.kern == kern && c.threads == threads && c.lds == lds_key && c.dev == dev) {
+            *out = c.blocks;
+            return hipSuccess;
+        }
+    int n = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, threads, lds_key);
+    if (e != hipSuccess) return e;
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    *out = (n < 1 ? 1 : n) * cus;
+    cache[next] = Entry{kern, threads, lds_key, dev, *out};
+    next = (next + 1) % 16;
+    return hipSuccess;
+}
 
 int64_t decode_max_workers(int num_seqs, int max_context_len) {
     const int64_t tiles = (int64_t)num_seqs * ((max_context_len + kTileTokens - 1) / kTileTokens);

@@ -88,4 +88,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// Stream-K ranges: U work units laid end to end, cut into W equal contiguous
+// ranges.  Worker w owns units [worker_start(w), worker_start(w + 1)).
+__device__ __forceinline__ int64_t worker_start(int64_t w, int64_t U, int64_t W) {
+    return (w * U) / W;
+}
+// The worker whose range holds unit t.
+__device__ __forceinline__ int64_t worker_of(int64_t t, int64_t U, int64_t W) {
+    return ((t + 1) * W - 1) / U;
+}
+
 }  // namespace pkv

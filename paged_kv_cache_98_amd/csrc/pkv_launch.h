@@ -86,10 +86,11 @@ struct PrefillArgs {
     float scale_log2;
     bool causal;
     bool decode_rows_elsewhere;  // skip sequences with one query row
-    // key split of few-row chunks (prefill_split_plan); 0 = none
-    int split_tiles = 0;
-    int max_pieces = 1;
-    float* records = nullptr;  // workspace: [max_pieces][num_q_tokens][num_q_heads][132]
+    // chunks that fit one workgroup run stream-K (prefill_streamk)
+    bool streamk = false;
+    int32_t* cum = nullptr;      // workspace: [num_seqs + 1] unit prefix sums
+    float* records = nullptr;    // workspace: [max_workers][2][max_q_len * group][132]
+    int64_t max_workers = 0;     // workers whose records fit the workspace
     const uint64_t* tree_mask = nullptr;  // [num_q_tokens] token-tree masks, or none
 };
 
@@ -99,13 +100,18 @@ hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
-// Key split of a prefill call whose chunks have at most 64 query columns
-// per workgroup (max_q_len * group <= 64) and whose items leave most of the
-// chip idle: pieces of split_tiles 64-key tiles, at most max_pieces per
-// item; split_tiles = 0 means no split.
-void prefill_split_plan(int max_q_len, int group, int max_context_len, int num_seqs,
-                        int num_kv_heads, int* split_tiles, int* max_pieces);
-size_t prefill_record_bytes(int num_q_tokens, int num_q_heads, int max_pieces);
+// A prefill call whose chunks fit one workgroup (2 <= max_q_len and
+// max_q_len * group <= 128 query columns) runs stream-K over its key tiles;
+// its workspace part is a prefix-sum array and up to
+// prefill_streamk_max_workers workers' records (prefill_streamk_bytes).
+bool prefill_streamk(int max_q_len, int group);
+int64_t prefill_streamk_max_workers(int num_seqs, int num_kv_heads, int max_context_len);
+size_t prefill_streamk_bytes(int num_seqs, int max_q_len, int group, int num_kv_heads,
+                             int max_context_len);
+
+// Workgroups of `kern` the device holds at once with this block size and
+// dynamic LDS (all CUs; cached per kernel and device).
+hipError_t resident_workgroups(const void* kern, int threads, size_t lds, int* out);
 
 // Decode workspace: the tile prefix sums, then the partial-result records.
 size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,

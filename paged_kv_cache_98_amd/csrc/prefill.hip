@@ -40,17 +40,16 @@
 // tokens j whose bit is set in its mask (its path to the root); the masks
 // are applied, with the causal limit, in the tiles that hold chunk keys.
 //
-// Key split (chunks of a few rows, as in speculative-decoding verification:
-// at most 64 of the 128 columns used): such a call reads every key once
-// per KV head for a handful of queries, so it is bandwidth-bound.  When its
-// (slot, KV head) items are too few to fill the chip (a few long contexts),
-// a workgroup takes one piece of at most split_tiles key tiles of its item
-// instead of the whole item; an item of one piece finishes in place,
-// the pieces of a longer one leave their unnormalised O, reference maximum
-// m and sum l per real column in the workspace, and prefill_merge_kernel
-// combines them: M = max m_k, L = sum l_k 2^(m_k - M),
-// out = sum O_k 2^(m_k - M) / L (the sequence-axis parallelism of "Flash
-// Attention v2 的改进").
+// Stream-K for chunks that fit one workgroup (every sequence's rows in one
+// slot, as in speculative-decoding verification): such a call reads every
+// key once per KV head for a few queries, so it is bandwidth-bound, and one
+// workgroup per item would last as long as the longest context.  Instead
+// the items' key tiles are laid end to end and cut into equal ranges, one
+// per resident workgroup; items split between workers leave their
+// unnormalised O, reference maximum m and sum l per column in the
+// workspace, and prefill_streamk_merge_kernel combines them:
+// M = max m_k, L = sum l_k 2^(m_k - M), out = sum O_k 2^(m_k - M) / L (the
+// sequence-axis parallelism of "Flash Attention v2 的改进").
 #include <type_traits>
 
 #include "pkv_device.h"
@@ -260,71 +259,28 @@ __device__ __forceinline__ void softmax_half(f32x16_t& s, f16x8_t (&pf)[2], f32x
     l_run = fmaf(l_run, alpha, (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]));
 }
 
-constexpr int kRecStride = D + 4;  // floats per split record: O[128], m, l, 2 pad
-constexpr int kMinSplitTiles = 8;  // a piece streams at least 512 keys ...
-constexpr int kMaxPieces = 32;     // ... and an item has at most 32 pieces
-constexpr int64_t kSplitBelowItems = 256;
-constexpr int64_t kSplitTargetGroups = 2048;
+constexpr int kRecStride = D + 4;  // floats per partial record: O[128], m, l, 2 pad
+constexpr int64_t kMaxChunkWorkers = 1024;  // stream-K workgroups, at most
 
-// Key tiles of the (slot, KV head) item that holds query row r of a
-// sequence with lq rows and context ctx (the slot's last row decides).
-template <int G>
-__device__ __forceinline__ int item_tiles(int r, int lq, int ctx, int causal) {
-    constexpr int P = kCols / G;
-    const int r0 = r / P * P;
-    const int r_last = (r0 + P < lq ? r0 + P : lq) - 1;
-    const int pos0 = ctx - lq;
-    const int kv_end = causal ? (pos0 + r_last + 1 < ctx ? pos0 + r_last + 1 : ctx) : ctx;
-    return (kv_end + kKT - 1) / kKT;
-}
-
-// Grid: ((num_q_tokens / (128 / G) + num_seqs) * max_pieces, num_kv_heads);
-// block 256.  x / max_pieces is the slot, x % max_pieces the piece (always 0
-// without a key split).  Slot y of sequence i is y - T(i),
-// T(i) = cu_q_lens[i] / P + i with P = 128 / G positions per workgroup; T
-// never skips a needed slot.
+// Key tiles [t0, t1) of one item -- a sequence's KV head kvh and its query
+// rows r0 .. r0 + P - 1, P = 128 / G, of a chunk of lq rows ending at
+// position ctx - 1 -- on the calling workgroup.  Every wave of the
+// workgroup calls it with the same arguments (rec_col aside) and meets the
+// same barriers, and the tile buffers are free again when it returns.
+// rec_col is this lane's column record, or NULL for the final output: with
+// a record the unnormalised O^T, the reference maximum m and the sum l are
+// stored instead of O / l.
 template <int BS, int G, bool OUT_BF16>
-__global__ void __launch_bounds__(kThreads, 2)
-prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
-                    const int32_t* __restrict__ cu_q_lens, const uint16_t* __restrict__ k_cache,
-                    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
-                    int max_blocks_per_seq, const int32_t* __restrict__ context_lens,
-                    int max_context_len, int num_seqs, int num_q_heads, int num_kv_heads,
-                    float scale_log2, int causal, int decode_rows_elsewhere, int split_tiles,
-                    int max_pieces, float* __restrict__ rec, int num_q_tokens,
-                    const uint64_t* __restrict__ tree_mask) {
+__device__ __forceinline__ void chunk_item(
+    uint16_t (&s_ks)[2][kKsElems], uint16_t (&s_vt)[2][kVtElems], void* __restrict__ out,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
+    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ bt_row, int num_q_heads,
+    int num_kv_heads, float scale_log2, int causal, const uint64_t* __restrict__ tree_mask,
+    int q_begin, int lq, int ctx, int kvh, int r0, int t0, int t1, float* rec_col) {
     constexpr int P = kCols / G;  // query positions per workgroup
-    __shared__ __attribute__((aligned(16))) uint16_t s_ks[2][kKsElems];
-    __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kVtElems];
-
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int kvh = blockIdx.y;
-    const int slot = blockIdx.x / max_pieces;
-    const int piece = blockIdx.x - slot * max_pieces;
-
-    // ---- which sequence owns this slot: 64-way search over T(i)
-    int lo = 0, hi = num_seqs;  // T(lo) <= slot < T(hi), T(num_seqs) = grid size
-    while (hi - lo > 1) {
-        const int step = (hi - lo + 63) / 64;
-        const int idx = lo + lane * step;
-        const bool ok = idx < hi && (cu_q_lens[idx] / P + idx) <= slot;
-        const unsigned long long m = __ballot(ok);  // low bits set, lane 0 always
-        const int last = 63 - __builtin_clzll(m);
-        lo = lo + last * step;
-        const int nh = lo + step;
-        hi = nh < hi ? nh : hi;
-    }
-    const int seq = lo;
-    const int q_begin = cu_q_lens[seq];
-    const int lq = cu_q_lens[seq + 1] - q_begin;
-    const int tile = slot - (q_begin / P + seq);
-    const int r0 = tile * P;
-    if (r0 >= lq) return;
-    if (decode_rows_elsewhere && lq == 1) return;
-    int ctx = context_lens[seq];
-    ctx = ctx < 0 ? 0 : (ctx > max_context_len ? max_context_len : ctx);
     const int pos0 = ctx - lq;  // position of the chunk's first query row
 
     // ---- this lane's query column
@@ -337,15 +293,6 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
     const int r_last = (r0 + P < lq ? r0 + P : lq) - 1;
     const int kv_end = causal ? (pos0 + r_last + 1 < ctx ? pos0 + r_last + 1 : ctx) : ctx;
     const int ntiles = (kv_end + kKT - 1) / kKT;
-    // this workgroup's key tiles [t0, t1) and the item's piece count
-    int t0 = 0, t1 = ntiles, npieces = 1;
-    if (split_tiles > 0) {
-        t0 = piece * split_tiles;
-        if (piece > 0 && t0 >= ntiles) return;  // piece 0 also covers ntiles == 0
-        t1 = t0 + split_tiles < ntiles ? t0 + split_tiles : ntiles;
-        npieces = (ntiles + split_tiles - 1) / split_tiles;
-        npieces = npieces > 1 ? npieces : 1;
-    }
 
     // Q^T fragments: k-step kk covers dims 16 kk + 8 h .. + 7 of this column;
     // a negative scale moves into q's sign so maxima work on raw scores.
@@ -379,8 +326,7 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
     uint32_t koff[4], voff[4];
     stage_offsets<BS>(koff, voff, row_bytes, tid);
     PrefillIds ids;
-    ids.init(block_table + (size_t)seq * max_blocks_per_seq, (ctx + BS - 1) / BS,
-             t0 * kKT / BS, lane);
+    ids.init(bt_row, (ctx + BS - 1) / BS, t0 * kKT / BS, lane);
 
     Stage sg;
     if (t1 > t0) {
@@ -451,12 +397,13 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
     // Only tiles that reach the causal diagonal (k0 + 63 > pos0 + r0) or the
     // context's end (k0 + 64 > ctx) need masks; they are the last ones.  The
     // tiles before them, all with a next tile, run in a loop of their own with
-    // no branch in its body.  (A piece's last tile always takes the masked
+    // no branch in its body.  (A segment's last tile always takes the masked
     // path; its masks then drop nothing.)
     // A wave none of whose columns is a real query row (short chunks: a verify
     // chunk of 6 rows x 4 heads fills 24 of the 128 columns) only stages its
     // share of every tile for the others and meets them at each tile's
-    // barrier; its results would be discarded.
+    // barrier; its results would be discarded.  It leaves after the last
+    // barrier, when no wave reads the tile buffers any more.
     if (r0 + (wave * 32) / G >= lq) {
         for (int jj = t0; jj < t1; ++jj) {
             if (jj + 1 < t1) {
@@ -482,9 +429,8 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
     // ---- finish: total l over both halves, then out = O / l
     const float lt = l_run + xor_lane(l_run, 32);
     if (!col_valid) return;
-    if (npieces > 1) {  // one piece of several: the record of this column
-        float* rp = rec + (((size_t)piece * num_q_tokens + (size_t)(q_begin + r)) * num_q_heads +
-                           (size_t)kvh * G + g) * kRecStride;
+    if (rec_col) {  // part of the item's keys: the record of this column
+        float* rp = rec_col;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -518,15 +464,199 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
         }
 }
 
-// Combines the pieces of split items.  Grid: (num_seqs, ceil(max_q_len *
-// num_q_heads / 4)); block: 4 waves, one (row, query head) each; lane k
-// holds piece k's m and l, and dims 2 lane, 2 lane + 1 of the output.
+
+// Grid: (num_q_tokens / P + num_seqs, num_kv_heads), P = 128 / G query
+// positions per workgroup; block 256.  Slot y of sequence i is y - T(i),
+// T(i) = cu_q_lens[i] / P + i; T never skips a needed slot.  Each
+// workgroup runs all key tiles of its (slot, KV head) item.
+template <int BS, int G, bool OUT_BF16>
+__global__ void __launch_bounds__(kThreads, 2)
+prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
+                    const int32_t* __restrict__ cu_q_lens, const uint16_t* __restrict__ k_cache,
+                    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
+                    int max_blocks_per_seq, const int32_t* __restrict__ context_lens,
+                    int max_context_len, int num_seqs, int num_q_heads, int num_kv_heads,
+                    float scale_log2, int causal, int decode_rows_elsewhere,
+                    const uint64_t* __restrict__ tree_mask) {
+    constexpr int P = kCols / G;
+    __shared__ __attribute__((aligned(16))) uint16_t s_ks[2][kKsElems];
+    __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kVtElems];
+    const int lane = threadIdx.x & 63;
+    const int kvh = blockIdx.y;
+    const int slot = blockIdx.x;
+
+    // ---- which sequence owns this slot: 64-way search over T(i)
+    int lo = 0, hi = num_seqs;  // T(lo) <= slot < T(hi), T(num_seqs) = grid size
+    while (hi - lo > 1) {
+        const int step = (hi - lo + 63) / 64;
+        const int idx = lo + lane * step;
+        const bool ok = idx < hi && (cu_q_lens[idx] / P + idx) <= slot;
+        const unsigned long long m = __ballot(ok);  // low bits set, lane 0 always
+        const int last = 63 - __builtin_clzll(m);
+        lo = lo + last * step;
+        const int nh = lo + step;
+        hi = nh < hi ? nh : hi;
+    }
+    const int seq = lo;
+    const int q_begin = cu_q_lens[seq];
+    const int lq = cu_q_lens[seq + 1] - q_begin;
+    const int r0 = (slot - (q_begin / P + seq)) * P;
+    if (r0 >= lq) return;
+    if (decode_rows_elsewhere && lq == 1) return;
+    int ctx = context_lens[seq];
+    ctx = ctx < 0 ? 0 : (ctx > max_context_len ? max_context_len : ctx);
+    const int pos0 = ctx - lq;
+    const int r_last = (r0 + P < lq ? r0 + P : lq) - 1;
+    const int kv_end = causal ? (pos0 + r_last + 1 < ctx ? pos0 + r_last + 1 : ctx) : ctx;
+    chunk_item<BS, G, OUT_BF16>(s_ks, s_vt, out, q, k_cache, v_cache,
+                                block_table + (size_t)seq * max_blocks_per_seq, num_q_heads,
+                                num_kv_heads, scale_log2, causal, tree_mask, q_begin, lq, ctx, kvh,
+                                r0, 0, (kv_end + kKT - 1) / kKT, nullptr);
+}
+
+// Stream-K units of sequence i in a call of chunks that fit one workgroup
+// (Lq <= max_q_len <= P): one per (KV head, 64-key tile) when its rows are
+// ours.  A sequence with more rows than max_q_len breaks the call's
+// contract; it gets no units (its columns would fall outside the records).
+__device__ __forceinline__ int streamk_units(const int32_t* __restrict__ cu_q_lens,
+                                             const int32_t* __restrict__ context_lens, int i,
+                                             int max_context_len, int max_q_len, int num_kv_heads,
+                                             int decode_rows_elsewhere) {
+    const int lq = cu_q_lens[i + 1] - cu_q_lens[i];
+    if (lq <= 0 || lq > max_q_len || (decode_rows_elsewhere && lq == 1)) return 0;
+    int ctx = context_lens[i];
+    ctx = ctx < 0 ? 0 : (ctx > max_context_len ? max_context_len : ctx);
+    return num_kv_heads * ((ctx + kKT - 1) / kKT);
+}
+
+// Chunks that fit one workgroup (every sequence's rows are one slot, as in
+// speculative-decoding verification) read each key once per KV head for a
+// few queries: bandwidth-bound, with items of very different lengths.  A
+// grid of one workgroup per item lasts as long as its longest context, so
+// here the items' key tiles are laid end to end -- sequence-major, then KV
+// head, then tile -- and cut into num_workers equal contiguous ranges, one
+// per resident workgroup (as the decode kernel does).  A worker runs the
+// items of its range in order; an item it covers whole finishes in place,
+// a partial one (at most the first and the last of its range) leaves per
+// column records in slot 0 or 1 of the worker, which
+// prefill_streamk_merge_kernel folds in worker order.
+// Grid: (num_workers); block 256; dynamic LDS (num_seqs + 1) int32 for the
+// unit prefix sums, which workgroup 0 also stores in cum_out.
+// Records: [num_workers][2][max_q_len * G][kRecStride] floats, column
+// c = r G + g.
+template <int BS, int G, bool OUT_BF16>
+__global__ void __launch_bounds__(kThreads, 2)
+prefill_streamk_kernel(void* __restrict__ out, float* __restrict__ rec,
+                       int32_t* __restrict__ cum_out, const uint16_t* __restrict__ q,
+                       const int32_t* __restrict__ cu_q_lens, const uint16_t* __restrict__ k_cache,
+                       const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
+                       int max_blocks_per_seq, const int32_t* __restrict__ context_lens,
+                       int max_context_len, int num_seqs, int num_q_heads, int num_kv_heads,
+                       float scale_log2, int causal, int decode_rows_elsewhere, int num_workers,
+                       int max_q_len, const uint64_t* __restrict__ tree_mask) {
+    const int rec_cols = max_q_len * G;  // columns per record slot
+    __shared__ __attribute__((aligned(16))) uint16_t s_ks[2][kKsElems];
+    __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kVtElems];
+    __shared__ int32_t s_part[kThreads / 64];
+    extern __shared__ int32_t s_cum[];  // s_cum[i] = units of sequences < i
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+
+    // ---- prefix sums of per-sequence units: each thread sums `per`
+    // consecutive sequences, each wave scans its 64 sums with lane shuffles,
+    // one barrier passes the waves' totals around
+    const int per = (num_seqs + kThreads - 1) / kThreads;
+    int local = 0;
+    for (int k = 0; k < per; ++k) {
+        const int i = tid * per + k;
+        if (i < num_seqs)
+            local += streamk_units(cu_q_lens, context_lens, i, max_context_len, max_q_len,
+                                   num_kv_heads, decode_rows_elsewhere);
+    }
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    if (lane == 63) s_part[tid >> 6] = incl;
+    __syncthreads();
+    int run = incl - local, total = 0;
+#pragma unroll
+    for (int k = 0; k < kThreads / 64; ++k) {
+        const int t = s_part[k];
+        run += k < (tid >> 6) ? t : 0;
+        total += t;
+    }
+    for (int k = 0; k < per; ++k) {
+        const int i = tid * per + k;
+        if (i < num_seqs) {
+            s_cum[i] = run;
+            run += streamk_units(cu_q_lens, context_lens, i, max_context_len, max_q_len,
+                                 num_kv_heads, decode_rows_elsewhere);
+        }
+    }
+    if (tid == 0) s_cum[num_seqs] = total;
+    __syncthreads();
+    if (blockIdx.x == 0)
+        for (int i = tid; i <= num_seqs; i += kThreads) cum_out[i] = s_cum[i];
+
+    const int64_t U = s_cum[num_seqs];
+    // never more workers than units, so every worker's range is non-empty
+    const int64_t W = num_workers < U ? num_workers : U;
+    const int64_t w = blockIdx.x;
+    if (w >= W) return;  // the whole workgroup
+    int64_t t = worker_start(w, U, W);
+    const int64_t t_end = worker_start(w + 1, U, W);
+    const int col = (tid >> 6) * 32 + (lane & 31);  // this lane's query column
+    int slot = 0;
+    while (t < t_end) {
+        // sequence holding unit t: the last i with s_cum[i] <= t
+        int lo = 0, hi = num_seqs;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_cum[mid] <= t) lo = mid; else hi = mid;
+        }
+        const int seq = lo;
+        const int q_begin = cu_q_lens[seq];
+        const int lq = cu_q_lens[seq + 1] - q_begin;
+        int ctx = context_lens[seq];
+        ctx = ctx < 0 ? 0 : (ctx > max_context_len ? max_context_len : ctx);
+        const int n = (ctx + kKT - 1) / kKT;  // tiles per KV head, >= 1 here
+        const int64_t u = t - s_cum[seq];
+        const int kvh = (int)(u / n);
+        const int tile0 = (int)(u - (int64_t)kvh * n);
+        const int64_t item_end = t + (n - tile0);
+        const int64_t seg_end = t_end < item_end ? t_end : item_end;
+        const int t1 = tile0 + (int)(seg_end - t);
+        // columns past the chunk's rows never write, so their record
+        // address (beyond rec_cols) is never used
+        float* rc = (tile0 != 0 || t1 != n)
+                        ? rec + ((size_t)(w * 2 + slot) * rec_cols + col) * kRecStride
+                        : nullptr;
+        chunk_item<BS, G, OUT_BF16>(s_ks, s_vt, out, q, k_cache, v_cache,
+                                    block_table + (size_t)seq * max_blocks_per_seq, num_q_heads,
+                                    num_kv_heads, scale_log2, causal, tree_mask, q_begin, lq, ctx,
+                                    kvh, 0, tile0, t1, rc);
+        slot = 1;
+        t = seg_end;
+    }
+}
+
+// Finishes the rows of prefill_streamk_kernel's items that several workers
+// shared, folding their records in worker order:
+// M = max_k m_k, L = sum_k l_k 2^(m_k - M), out = sum_k O_k 2^(m_k - M) / L
+// (the sequence-axis parallelism of "Flash Attention v2 的改进"); rows of a
+// sequence with no key get zeros.
+// Grid: (num_seqs, ceil(max_q_len * num_q_heads / 4)); block: 4 waves, one
+// (row, query head) each; lane k holds piece k's m and l, and dims 2 lane,
+// 2 lane + 1 of the output.
 template <int G, bool OUT_BF16>
 __global__ void __launch_bounds__(256)
-prefill_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
-                     const int32_t* __restrict__ cu_q_lens, const int32_t* __restrict__ context_lens,
-                     int max_context_len, int num_q_heads, int num_q_tokens, int causal,
-                     int decode_rows_elsewhere, int split_tiles) {
+prefill_streamk_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
+                             const int32_t* __restrict__ cum, const int32_t* __restrict__ cu_q_lens,
+                             int num_seqs, int num_q_heads, int num_kv_heads, int num_workers,
+                             int rec_cols, int decode_rows_elsewhere) {
     const int lane = threadIdx.x & 63;
     const int seq = blockIdx.x;
     const int item = blockIdx.y * 4 + (threadIdx.x >> 6);
@@ -535,70 +665,108 @@ prefill_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
     const int r = item / num_q_heads;
     const int head = item - r * num_q_heads;
     if (r >= lq) return;
-    if (decode_rows_elsewhere && lq == 1) return;
-    int ctx = context_lens[seq];
-    ctx = ctx < 0 ? 0 : (ctx > max_context_len ? max_context_len : ctx);
-    const int npieces = (item_tiles<G>(r, lq, ctx, causal) + split_tiles - 1) / split_tiles;
-    if (npieces <= 1) return;  // finished in place
-    auto rec_of = [&](int k) {
-        return rec + (((size_t)k * num_q_tokens + (size_t)(q_begin + r)) * num_q_heads + head) *
-                         kRecStride;
+    if (decode_rows_elsewhere && lq == 1) return;  // a decode row: not ours
+    const size_t e = ((size_t)(q_begin + r) * num_q_heads + head) * D + 2 * lane;
+    auto store2 = [&](float x0, float x1) {
+        if (OUT_BF16) {
+            const uint32_t v = (uint32_t)f32_to_bf16_rne(x0) | ((uint32_t)f32_to_bf16_rne(x1) << 16);
+            *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + e) = v;
+        } else {
+            *reinterpret_cast<float2*>(static_cast<float*>(out) + e) = make_float2(x0, x1);
+        }
     };
-    float2 ml = make_float2(-INFINITY, 0.0f);
-    if (lane < npieces) ml = *reinterpret_cast<const float2*>(rec_of(lane) + D);
-    float mx = ml.x;
+    const int64_t units = cum[seq + 1] - cum[seq];
+    if (units == 0) {  // no key to attend to
+        store2(0.0f, 0.0f);
+        return;
+    }
+    const int64_t n = units / num_kv_heads;
+    const int64_t start = cum[seq] + (int64_t)(head / G) * n;
+    const int64_t U = cum[num_seqs];
+    const int64_t W = num_workers < U ? num_workers : U;
+    const int64_t wf = worker_of(start, U, W);
+    const int64_t wl = worker_of(start + n - 1, U, W);
+    if (wf == wl) return;  // finished in place by its only worker
+    const int col = r * G + head % G;
+    auto rec_of = [&](int64_t w) {
+        const int slot = (w == wf && worker_start(w, U, W) < start) ? 1 : 0;
+        return rec + ((size_t)(w * 2 + slot) * rec_cols + col) * kRecStride;
+    };
+    // maximum over the pieces' reference maxima, one piece per lane; the
+    // first 64 pieces' (m, l) stay in their lanes
+    float2 ml0 = make_float2(-INFINITY, 0.0f);
+    if (wf + lane <= wl) ml0 = *reinterpret_cast<const float2*>(rec_of(wf + lane) + D);
+    float mx = ml0.x;
+    for (int64_t w = wf + 64 + lane; w <= wl; w += 64) mx = fmaxf(mx, rec_of(w)[D]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    const float fk = lane < npieces ? fast_exp2(ml.x - mx) : 0.0f;
-    float lsum = ml.y * fk;
+    // then the pieces in worker order, 64 at a time: lane k holds the scale
+    // exp2(m - mx) and the sum l of piece base + k; the O rows are loaded
+    // eight pieces ahead of their use
+    float L = 0.0f, a0 = 0.0f, a1 = 0.0f;
+    for (int64_t base = wf; base <= wl; base += 64) {
+        const int cnt = wl - base + 1 < 64 ? (int)(wl - base + 1) : 64;
+        float2 ml = ml0;
+        if (base != wf)
+            ml = lane < cnt ? *reinterpret_cast<const float2*>(rec_of(base + lane) + D)
+                            : make_float2(-INFINITY, 0.0f);
+        const float fk = lane < cnt ? fast_exp2(ml.x - mx) : 0.0f;
+        const float lk = ml.y;
+        for (int k = 0; k < cnt; k += 8) {
+            float2 av[8];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) lsum += __shfl_xor(lsum, o);
-    // eight pieces' rows in flight at a time
-    float a0 = 0.0f, a1 = 0.0f;
-    for (int k = 0; k < npieces; k += 8) {
-        float2 av[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-            av[u] = k + u < npieces ? *reinterpret_cast<const float2*>(rec_of(k + u) + 2 * lane)
+            for (int u = 0; u < 8; ++u)
+                av[u] = k + u < cnt ? *reinterpret_cast<const float2*>(rec_of(base + k + u) + 2 * lane)
                                     : make_float2(0.0f, 0.0f);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int kk = k + u < 63 ? k + u : 63;
-            const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fk), kk));
-            a0 = fmaf(av[u].x, f, a0);
-            a1 = fmaf(av[u].y, f, a1);
+            for (int u = 0; u < 8; ++u) {
+                if (k + u >= cnt) break;
+                const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fk), k + u));
+                L = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(lk), k + u)), f, L);
+                a0 = fmaf(av[u].x, f, a0);
+                a1 = fmaf(av[u].y, f, a1);
+            }
         }
     }
-    const float inv = 1.0f / lsum;
-    const size_t e = ((size_t)(q_begin + r) * num_q_heads + head) * D + 2 * lane;
-    if (OUT_BF16) {
-        const uint32_t w = (uint32_t)f32_to_bf16_rne(a0 * inv) |
-                           ((uint32_t)f32_to_bf16_rne(a1 * inv) << 16);
-        *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + e) = w;
-    } else {
-        *reinterpret_cast<float2*>(static_cast<float*>(out) + e) = make_float2(a0 * inv, a1 * inv);
-    }
+    const float inv = 1.0f / L;
+    store2(a0 * inv, a1 * inv);
 }
 
 template <int BS, int G, bool OUT_BF16>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     constexpr int P = kCols / G;
+    if (a.streamk) {
+        auto kern = prefill_streamk_kernel<BS, G, OUT_BF16>;
+        const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int32_t);
+        int resident = 0;
+        hipError_t e = resident_workgroups(reinterpret_cast<const void*>(kern), kThreads, lds,
+                                           &resident);
+        if (e != hipSuccess) return e;
+        // as many workers as the chip holds at once, never more than the
+        // records in the workspace allow
+        int64_t workers = resident < a.max_workers ? resident : a.max_workers;
+        if (workers < 1) workers = 1;
+        hipLaunchKernelGGL(kern, dim3((int)workers), dim3(kThreads), lds, stream, a.out,
+                           a.records, a.cum, a.q, a.cu_q_lens, a.k_cache, a.v_cache,
+                           a.block_table, a.max_blocks_per_seq, a.context_lens,
+                           a.max_context_len, a.num_seqs, a.num_q_heads, a.num_kv_heads,
+                           a.scale_log2, a.causal ? 1 : 0, a.decode_rows_elsewhere ? 1 : 0,
+                           (int)workers, a.max_q_len, a.tree_mask);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        dim3 mgrid(a.num_seqs, (a.max_q_len * a.num_q_heads + 3) / 4);
+        hipLaunchKernelGGL((prefill_streamk_merge_kernel<G, OUT_BF16>), mgrid, dim3(256), 0,
+                           stream, a.out, a.records, a.cum, a.cu_q_lens, a.num_seqs,
+                           a.num_q_heads, a.num_kv_heads, (int)workers, a.max_q_len * G,
+                           a.decode_rows_elsewhere ? 1 : 0);
+        return hipGetLastError();
+    }
     const int slots = a.num_q_tokens / P + a.num_seqs;
-    const int pieces = a.split_tiles > 0 ? a.max_pieces : 1;
-    dim3 grid(slots * pieces, a.num_kv_heads);
-    hipLaunchKernelGGL((prefill_mfma_kernel<BS, G, OUT_BF16>), grid, dim3(kThreads), 0, stream,
-                       a.out, a.q, a.cu_q_lens, a.k_cache, a.v_cache, a.block_table,
-                       a.max_blocks_per_seq, a.context_lens, a.max_context_len, a.num_seqs,
-                       a.num_q_heads, a.num_kv_heads, a.scale_log2, a.causal ? 1 : 0,
-                       a.decode_rows_elsewhere ? 1 : 0, a.split_tiles, pieces, a.records,
-                       a.num_q_tokens, a.tree_mask);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.split_tiles == 0) return e;
-    dim3 mgrid(a.num_seqs, (a.max_q_len * a.num_q_heads + 3) / 4);
-    hipLaunchKernelGGL((prefill_merge_kernel<G, OUT_BF16>), mgrid, dim3(256), 0, stream, a.out,
-                       a.records, a.cu_q_lens, a.context_lens, a.max_context_len, a.num_q_heads,
-                       a.num_q_tokens, a.causal ? 1 : 0, a.decode_rows_elsewhere ? 1 : 0,
-                       a.split_tiles);
+    hipLaunchKernelGGL((prefill_mfma_kernel<BS, G, OUT_BF16>), dim3(slots, a.num_kv_heads),
+                       dim3(kThreads), 0, stream, a.out, a.q, a.cu_q_lens, a.k_cache, a.v_cache,
+                       a.block_table, a.max_blocks_per_seq, a.context_lens, a.max_context_len,
+                       a.num_seqs, a.num_q_heads, a.num_kv_heads, a.scale_log2,
+                       a.causal ? 1 : 0, a.decode_rows_elsewhere ? 1 : 0, a.tree_mask);
     return hipGetLastError();
 }
 
@@ -621,31 +789,22 @@ hipError_t launch_prefill_bs(const PrefillArgs& a, hipStream_t s) {
 
 }  // namespace
 
-void prefill_split_plan(int max_q_len, int group, int max_context_len, int num_seqs,
-                        int num_kv_heads, int* split_tiles, int* max_pieces) {
-    *split_tiles = 0;
-    *max_pieces = 1;
-    // only chunks with few query columns per workgroup stream keys ...
-    if (max_q_len < 2 || max_q_len * group > kCols / 2) return;
-    // ... and only when their items leave most of the chip idle: below half
-    // of the 512 workgroups an MI355X runs at once (two per CU), the pieces
-    // aim at about 2048 workgroups
-    const int64_t items = (int64_t)num_seqs * num_kv_heads *
-                          ((max_q_len + kCols / group - 1) / (kCols / group));
-    if (items >= kSplitBelowItems) return;
-    const int64_t want = (kSplitTargetGroups + items - 1) / items;
-    const int pieces_goal = (int)(want < kMaxPieces ? want : kMaxPieces);
-    const int tiles = (max_context_len + kKT - 1) / kKT;
-    int s = (tiles + pieces_goal - 1) / pieces_goal;
-    s = s > kMinSplitTiles ? s : kMinSplitTiles;
-    const int pieces = (tiles + s - 1) / s;
-    if (pieces < 2) return;
-    *split_tiles = s;
-    *max_pieces = pieces;
+bool prefill_streamk(int max_q_len, int group) {
+    return max_q_len >= 2 && max_q_len * group <= kCols;
 }
 
-size_t prefill_record_bytes(int num_q_tokens, int num_q_heads, int max_pieces) {
-    return (size_t)max_pieces * num_q_tokens * num_q_heads * kRecStride * sizeof(float);
+int64_t prefill_streamk_max_workers(int num_seqs, int num_kv_heads, int max_context_len) {
+    const int64_t units =
+        (int64_t)num_seqs * num_kv_heads * ((max_context_len + kKT - 1) / kKT);
+    const int64_t w = units < kMaxChunkWorkers ? units : kMaxChunkWorkers;
+    return w < 1 ? 1 : w;
+}
+
+size_t prefill_streamk_bytes(int num_seqs, int max_q_len, int group, int num_kv_heads,
+                             int max_context_len) {
+    const size_t cum = ((size_t)(num_seqs + 1) * sizeof(int32_t) + 255) / 256 * 256;
+    return cum + (size_t)prefill_streamk_max_workers(num_seqs, num_kv_heads, max_context_len) *
+                     2 * max_q_len * group * kRecStride * sizeof(float);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {

@@ -219,17 +219,21 @@ def test_prefill_workspace_size(lib):
     ws = lib.pkv_prefill_workspace_bytes
     dec = lambda b, ctx: lib.pkv_decode_workspace_bytes(b, 32, 8, 128, ctx)
     up = lambda x: (x + 255) // 256 * 256
-    # 512-row chunks: no key split, only the decode part
+    sk = lambda b, lq, g, hkv, ctx: (up((b + 1) * 4) + min(1024, b * hkv * -(-ctx // 64))
+                                     * 2 * lq * g * 132 * 4)
+    # 512-row chunks (2048 columns per KV head): only the decode part
     assert ws(4, 2048, 512, 32, 8, 128, 4096) == dec(4, 4096)
-    # 64 six-row verify chunks x 8 KV heads = 512 items fill the chip: no split
-    assert ws(64, 384, 6, 32, 8, 128, 4096) == dec(64, 4096)
-    # 8 of them (64 items) over 100k tokens: 1563 tiles in pieces of 49, 32 pieces
-    assert ws(8, 48, 6, 32, 8, 128, 100000) == up(dec(8, 100000)) + 32 * 48 * 32 * 132 * 4
-    # 16 sequences x 2 KV heads over 4097 tokens: 65 tiles, 64 pieces wanted,
-    # at least 8 tiles each -> pieces of 8, 9 of them
-    assert ws(16, 96, 6, 8, 2, 128, 4097) == (
-        up(lib.pkv_decode_workspace_bytes(16, 8, 2, 128, 4097)) + 9 * 96 * 8 * 132 * 4)
-    # short contexts (8 tiles or fewer) or wide chunks (6 x 16 > 64 columns): no split
-    assert ws(8, 48, 6, 32, 8, 128, 512) == dec(8, 512)
-    assert ws(8, 48, 6, 32, 2, 128, 100000) == dec(8, 100000)
+    # 64 six-row verify chunks (24 columns per KV head): stream-K part,
+    # 64 x 8 x 64 units -> 1024 workers' records
+    assert ws(64, 384, 6, 32, 8, 128, 4096) == up(dec(64, 4096)) + sk(64, 6, 4, 8, 4096)
+    # few units: at most one worker per unit (2 seqs x 2 heads x 2 tiles)
+    assert ws(2, 12, 6, 8, 2, 128, 100) == (
+        up(lib.pkv_decode_workspace_bytes(2, 8, 2, 128, 100)) + up(3 * 4) + 8 * 2 * 6 * 4 * 132 * 4)
+    # 32 rows x 4 heads = 128 columns still fit; 33 rows do not
+    assert ws(8, 256, 32, 32, 8, 128, 5000) == up(dec(8, 5000)) + sk(8, 32, 4, 8, 5000)
+    assert ws(8, 264, 33, 32, 8, 128, 5000) == dec(8, 5000)
+    # 16 query heads per KV head: up to 8 rows
+    assert ws(8, 64, 8, 32, 2, 128, 5000) == (
+        up(lib.pkv_decode_workspace_bytes(8, 32, 2, 128, 5000)) + sk(8, 8, 16, 2, 5000))
+    assert ws(8, 72, 9, 32, 2, 128, 5000) == lib.pkv_decode_workspace_bytes(8, 32, 2, 128, 5000)
     assert ws(4, 10, 4, 32, 6, 128, 100) == 0                       # Hq % Hkv

@@ -72,8 +72,9 @@ def test_tree_chain_masks_equal_causal():
 
 
 def test_tree_key_split():
-    """Few trees over long contexts take the key split (pieces merged after
-    the chunk kernel); fp32 and bf16 output, bitwise determinism."""
+    """Few trees over long contexts: every item is shared by several
+    stream-K workers and merged after the chunk kernel; fp32 and bf16
+    output, bitwise determinism."""
     cases = [(3000, 16), (2500, 9), (40, 3), (4100, 16), (700, 1), (1800, 12)]
     w = W.make_workload("tree_split_g4", [c for c, _ in cases], [q for _, q in cases],
                         num_q_heads=8, num_kv_heads=2, block_size=16, seed=5200)

@@ -57,10 +57,10 @@ def test_verify_full_batch_sampled():
 
 
 def test_verify_split_variants():
-    """Key-split chunks in every setting the split meets: 16 query heads per
-    KV head with 4 rows (64 columns, the largest split case), non-causal,
-    bf16 output, single-row sequences in the same call (whose decode
-    workspace sits in front of the split records), and bitwise
+    """Stream-K chunks (items shared between workers, merged after the chunk
+    kernel) in every setting they meet: 16 query heads per KV head with 4
+    rows, non-causal, bf16 output, single-row sequences in the same call
+    (whose decode workspace sits in front of the stream-K part), and bitwise
     determinism."""
     from tests.gpu_common import bf16_parity
     cases = [(3000, 4), (2500, 1), (40, 3), (1800, 2), (4100, 4), (700, 1), (129, 4)]
@@ -86,3 +86,25 @@ def test_verify_split_variants():
         assert torch.equal(o32, o32b)
         parity(o32, ref, what=f"split g16 causal={causal}")
         bf16_parity(o16, o32, ref, what=f"split g16 bf16 causal={causal}")
+
+
+@pytest.mark.parametrize("name,hq,hkv,cases", [
+    # the widest calls the stream-K path takes: 128 query columns per KV head
+    ("sk_g16_r8", 32, 2, [(3000, 8), (50, 8), (900, 1), (2100, 5), (8, 8), (77, 0)]),
+    ("sk_g4_r32", 16, 4, [(2000, 32), (32, 32), (700, 1), (4097, 17), (100, 0), (65, 32)]),
+    ("sk_g1_r128", 2, 2, [(1500, 128), (128, 128), (3000, 77), (129, 1)]),
+    # one long item over every worker: more pieces than the merge's 64 lanes
+    ("sk_one_long", 4, 1, [(100000, 6)]),
+])
+def test_streamk_widths_and_many_pieces(name, hq, hkv, cases):
+    print(f"[stream-K] {name}", flush=True)
+    w = W.make_workload(name, [c for c, _ in cases], [q for _, q in cases], num_q_heads=hq,
+                        num_kv_heads=hkv, block_size=16, seed=4200 + hq + hkv)
+    assert pkv.prefill_workspace_bytes(w.num_seqs, w.total_q, w.max_q_len, hq, hkv,
+                                       w.max_context_len) > 0
+    bc = W.materialize(w, logical=True, poison=True)
+    ref = oracle.paged_attention(bc.q, bc.k_cache, bc.v_cache, bc.block_table, bc.context_lens,
+                                 w.scale, cu_q_lens=bc.cu_q_lens, causal=True)
+    out = run(bc.to(DEV))
+    torch.cuda.synchronize()
+    parity(out, ref, what=name)
