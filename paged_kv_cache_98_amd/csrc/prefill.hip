@@ -157,8 +157,10 @@ __device__ __forceinline__ void stage_load(Stage& sg, PrefillIds& ids, const cha
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const __amdgpu_buffer_rsrc_t r =
-            buffer_rsrc(vbase + (size_t)(upper ? id[2 * j + 1] : id[2 * j]) * block_bytes);
+        // the id is wave-uniform (upper is); readfirstlane lets the compiler
+        // keep the resource in scalar registers instead of a waterfall loop
+        const int vid = __builtin_amdgcn_readfirstlane(upper ? id[2 * j + 1] : id[2 * j]);
+        const __amdgpu_buffer_rsrc_t r = buffer_rsrc(vbase + (size_t)vid * block_bytes);
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const uint32_t o = k0 + 2 * kq + p + 32 * j < kv_end ? voff[2 * j + p] : kBufferOob;
