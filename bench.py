@@ -83,15 +83,15 @@ TRAFFIC_SPEC = {
                                "sources": ["paged_kv_cache_98_amd/csrc/decode.hip",
                                            "paged_kv_cache_98_amd/csrc/pkv_device.h"],
                                "args": "--workload llama8b_decode_fp8"},
-    "spec_verify_b64_q6": {"kernels": ["prefill_mfma_kernel", "prefill_merge_kernel"],
+    "spec_verify_b64_q6": {"kernels": ["prefill_streamk_kernel", "prefill_streamk_merge_kernel"],
                            "sources": ["paged_kv_cache_98_amd/csrc/prefill.hip",
                                        "paged_kv_cache_98_amd/csrc/pkv_device.h"],
                            "args": "--workload spec_verify"},
-    "spec_verify_b8_q6": {"kernels": ["prefill_mfma_kernel", "prefill_merge_kernel"],
+    "spec_verify_b8_q6": {"kernels": ["prefill_streamk_kernel", "prefill_streamk_merge_kernel"],
                           "sources": ["paged_kv_cache_98_amd/csrc/prefill.hip",
                                       "paged_kv_cache_98_amd/csrc/pkv_device.h"],
                           "args": "--workload spec_verify_long"},
-    "spec_tree_b64_n16": {"kernels": ["prefill_mfma_kernel", "prefill_merge_kernel"],
+    "spec_tree_b64_n16": {"kernels": ["prefill_streamk_kernel", "prefill_streamk_merge_kernel"],
                           "sources": ["paged_kv_cache_98_amd/csrc/prefill.hip",
                                       "paged_kv_cache_98_amd/csrc/pkv_device.h"],
                           "args": "--workload spec_verify_tree"},
