@@ -53,6 +53,11 @@ class PagedKVError(RuntimeError):
         self.status = status
 
 
+class InvalidArgument(PagedKVError, ValueError):
+    """NULL, shape, alignment, unsupported-size, workspace or value errors:
+    the arguments of a call, rejected before anything is launched."""
+
+
 class OutOfBlocks(PagedKVError, MemoryError):
     """PKV_ERR_NO_MEMORY: the block pool has too few free blocks."""
 
@@ -140,7 +145,10 @@ def status_string(status: int) -> str:
 def _check(status: int):
     if status == PKV_OK:
         return
-    cls = {PKV_ERR_NO_MEMORY: OutOfBlocks, PKV_ERR_STATE: UnknownSequence}.get(status, PagedKVError)
+    cls = {PKV_ERR_NO_MEMORY: OutOfBlocks, PKV_ERR_STATE: UnknownSequence,
+           PKV_ERR_NULL: InvalidArgument, PKV_ERR_SHAPE: InvalidArgument,
+           PKV_ERR_UNSUPPORTED: InvalidArgument, PKV_ERR_WORKSPACE: InvalidArgument,
+           PKV_ERR_ALIGN: InvalidArgument, PKV_ERR_VALUE: InvalidArgument}.get(status, PagedKVError)
     raise cls(status, status_string(status))
 
 

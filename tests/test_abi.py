@@ -237,3 +237,21 @@ def test_prefill_workspace_size(lib):
         up(lib.pkv_decode_workspace_bytes(8, 32, 2, 128, 5000)) + sk(8, 8, 16, 2, 5000))
     assert ws(8, 72, 9, 32, 2, 128, 5000) == lib.pkv_decode_workspace_bytes(8, 32, 2, 128, 5000)
     assert ws(4, 10, 4, 32, 6, 128, 100) == 0                       # Hq % Hkv
+
+
+def test_binding_error_classes():
+    """Argument errors raise ValueError (InvalidArgument); pool exhaustion
+    MemoryError; unknown sequences KeyError; launch failures stay
+    PagedKVError (a RuntimeError)."""
+    E = binding
+    for st in (E.PKV_ERR_NULL, E.PKV_ERR_SHAPE, E.PKV_ERR_UNSUPPORTED, E.PKV_ERR_WORKSPACE,
+               E.PKV_ERR_ALIGN, E.PKV_ERR_VALUE):
+        with pytest.raises(ValueError):
+            E._check(st)
+    with pytest.raises(MemoryError):
+        E._check(E.PKV_ERR_NO_MEMORY)
+    with pytest.raises(KeyError):
+        E._check(E.PKV_ERR_STATE)
+    with pytest.raises(RuntimeError):
+        E._check(E.PKV_ERR_LAUNCH)
+    E._check(E.PKV_OK)
