@@ -21,6 +21,10 @@ Readings where the pages leave a step open:
   * Decode attention over the FP8 cache is the bf16 decode of the other
     oracle functions applied to the dequantised keys and values:
     out = softmax_t(scale * <q, k_scale * Kc[t]>) . (v_scale * Vc[t]).
+  * Chunked prefill over the FP8 cache is the same with a chunk of Lq query
+    rows per sequence at positions ctx - Lq .. ctx - 1, each seeing the keys
+    up to its own position when causal ("LLM 推理优化技术全景", Chunked
+    Prefill), as the bf16 chunk oracle does.
 """
 import numpy as np
 
@@ -127,4 +131,48 @@ def paged_decode_fp8(q_bf16_bits, k_codes, v_codes, k_scale, v_scale, block_tabl
             s = float(scale) * (k[:, kv, :] @ q[i, h])
             p = np.exp(s - s.max())
             out[i, h] = (p @ v[:, kv, :]) / p.sum()
+    return out
+
+
+def paged_prefill_fp8(q_bf16_bits, k_codes, v_codes, k_scale, v_scale, block_table,
+                      context_lens, cu_q_lens, scale, causal=True):
+    """fp64 chunked attention over FP8 pools: sequence i has query rows
+    cu_q_lens[i] .. cu_q_lens[i + 1] - 1; row r sits at position
+    context_lens[i] - Lq_i + r and sees keys 0 .. position (all
+    context_lens[i] keys when not causal), dequantised (code value x cache
+    scale), with the stable three-sweep softmax.  Returns [sum Lq, Hq, D]
+    float64."""
+    qb = np.asarray(q_bf16_bits).astype(np.uint16).astype(np.uint32) << 16
+    q = qb.view(np.float32).astype(np.float64)
+    kc, vc = np.asarray(k_codes, dtype=np.uint8), np.asarray(v_codes, dtype=np.uint8)
+    bt = np.asarray(block_table, dtype=np.int64)
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    cu = np.asarray(cu_q_lens, dtype=np.int64)
+    nb, bs, hkv, d = kc.shape
+    t, hq, d2 = q.shape
+    if d2 != d or hq % hkv or bt.shape[0] != ctx.shape[0] or cu.shape[0] != ctx.shape[0] + 1:
+        raise ValueError("shape mismatch")
+    if cu[-1] != t:
+        raise ValueError("cu_q_lens does not end at the number of query rows")
+    g = hq // hkv
+    out = np.zeros((t, hq, d), dtype=np.float64)
+    for i in range(ctx.shape[0]):
+        n, lq = int(ctx[i]), int(cu[i + 1] - cu[i])
+        if lq == 0 or n == 0:
+            continue
+        if lq > n:
+            raise ValueError(f"sequence {i}: {lq} query rows over {n} keys")
+        nblk = -(-n // bs)
+        ids = bt[i, :nblk]
+        if np.any(ids < 0) or np.any(ids >= nb):
+            raise ValueError(f"sequence {i}: block id outside the pool")
+        k = e4m3_value(kc[ids].reshape(nblk * bs, hkv, d)[:n]) * float(k_scale)
+        v = e4m3_value(vc[ids].reshape(nblk * bs, hkv, d)[:n]) * float(v_scale)
+        for r in range(lq):
+            seen = n - lq + r + 1 if causal else n
+            for h in range(hq):
+                kv = h // g
+                s_ = float(scale) * (k[:seen, kv, :] @ q[cu[i] + r, h])
+                p_ = np.exp(s_ - s_.max())
+                out[cu[i] + r, h] = (p_ @ v[:seen, kv, :]) / p_.sum()
     return out

@@ -122,3 +122,29 @@ def test_pin_decode_against_bf16_oracle(k_scale, v_scale):
     ref = oracle.paged_attention(q, kb, vb, bt, ctx, scale * k_scale) * v_scale
     assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
     assert np.all(got[4] == 0.0)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_pin_prefill_against_bf16_oracle(causal):
+    """The chunked FP8 reference equals the C oracle's chunked attention over
+    pools holding the codes' values as bf16 (every E4M3 value is a bf16
+    value), with power-of-two scales folded into the score scale and the
+    output; a single-row sequence equals the FP8 decode reference."""
+    rng = np.random.default_rng(10)
+    hq, hkv, d, bs, nb = 8, 2, 128, 16, 60
+    ctx = np.array([37, 141, 64, 100, 9], dtype=np.int32)
+    lq = np.array([37, 20, 1, 7, 3], dtype=np.int32)
+    cu = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    kc = rng.integers(0, 256, size=(nb, bs, hkv, d), dtype=np.uint8) & 0xDF
+    vc = rng.integers(0, 256, size=(nb, bs, hkv, d), dtype=np.uint8) & 0xDF
+    bt = rng.permutation(nb)[: 5 * 10].reshape(5, 10).astype(np.int32)
+    q = bf16_bits(rng.standard_normal((int(cu[-1]), hq, d)) * 0.3)
+    scale, k_scale, v_scale = 2.0 ** -4, 0.5, 8.0
+    got = fp8.paged_prefill_fp8(q, kc, vc, k_scale, v_scale, bt, ctx, cu, scale, causal=causal)
+    kb = bf16_bits(fp8.e4m3_value(kc).astype(np.float32))
+    vb = bf16_bits(fp8.e4m3_value(vc).astype(np.float32))
+    ref = oracle.paged_attention(q, kb, vb, bt, ctx, scale * k_scale, cu_q_lens=cu,
+                                 causal=causal) * v_scale
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+    dec = fp8.paged_decode_fp8(q[cu[2]:cu[3]], kc, vc, k_scale, v_scale, bt[2:3], ctx[2:3], scale)
+    assert np.allclose(got[cu[2]:cu[3]], dec, rtol=1e-12, atol=1e-12)
