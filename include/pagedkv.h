@@ -401,6 +401,25 @@ int pkv_bm_block_table(const pkv_block_manager *bm, const int64_t *seq_ids, int 
                        int32_t *table, int max_blocks_per_seq, int32_t *context_lens);
 
 /*
+ * paged_prefill_attn_fp8 -- pkv_paged_prefill_attn over FP8 (E4M3) pools
+ * (the format and scales of pkv_paged_decode_attn_fp8): k_cache / v_cache
+ * hold one code byte per value, [num_blocks][block_size][num_kv_heads]
+ * [head_dim]; keys and values are code value x k_scale / v_scale.  The chunk
+ * kernels widen the codes to bf16 (K) and fp16 (V) as they stage a tile, so
+ * the tile math is that of the bf16 call; single-row sequences take the FP8
+ * decode path.  Workspace as pkv_prefill_workspace_bytes.  Scales must be
+ * finite and > 0 (PKV_ERR_VALUE).
+ */
+int pkv_paged_prefill_attn_fp8(void *out, int out_dtype, const void *q,
+                               const int32_t *cu_q_lens, const void *k_cache,
+                               const void *v_cache, float k_scale, float v_scale,
+                               const int32_t *block_table, int max_blocks_per_seq,
+                               const int32_t *context_lens, int max_context_len, int max_q_len,
+                               int num_q_tokens, int num_seqs, int num_q_heads, int num_kv_heads,
+                               int head_dim, int block_size, float scale, int causal,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * paged_prefill_attn_tree -- token-tree verification ("让 Agent 跑得快：LLM
  * 推理服务", section 六, Token Tree Verification: the draft candidates form a
  * tree, checked by the target model in one pass).  Arguments as

@@ -254,7 +254,8 @@ size_t pkv_prefill_workspace_bytes(int num_seqs, int num_q_tokens, int max_q_len
 namespace {
 
 int prefill_call(void* out, int out_dtype, const void* q, const int32_t* cu_q_lens,
-                 const void* k_cache, const void* v_cache, const int32_t* block_table,
+                 const void* k_cache, const void* v_cache, bool kv_fp8, float k_scale,
+                 float v_scale, const int32_t* block_table,
                  int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
                  int max_q_len, int num_q_tokens, int num_seqs, int num_q_heads,
                  int num_kv_heads, int head_dim, int block_size, float scale, int causal,
@@ -265,6 +266,7 @@ int prefill_call(void* out, int out_dtype, const void* q, const int32_t* cu_q_le
     if (st != PKV_OK) return st;
     if (max_q_len < 0 || num_q_tokens < 0) return PKV_ERR_SHAPE;
     if (max_q_len > max_context_len) return PKV_ERR_SHAPE;
+    if (kv_fp8 && !(valid_scale(k_scale) && valid_scale(v_scale))) return PKV_ERR_VALUE;
     if ((int64_t)num_q_tokens > (int64_t)num_seqs * max_q_len) return PKV_ERR_SHAPE;
     if (num_seqs == 0 || num_q_tokens == 0) return PKV_OK;
     if (!out || !q || !cu_q_lens || !k_cache || !v_cache || !block_table || !context_lens)
@@ -305,6 +307,9 @@ int prefill_call(void* out, int out_dtype, const void* q, const int32_t* cu_q_le
     a.num_kv_heads = num_kv_heads;
     a.block_size = block_size;
     a.scale_log2 = scale * 1.4426950408889634f;
+    if (kv_fp8) a.scale_log2 *= k_scale;
+    a.kv_fp8 = kv_fp8;
+    a.out_scale = kv_fp8 ? v_scale : 1.0f;
     a.causal = causal != 0;
     a.decode_rows_elsewhere = any_decode_rows;
     a.streamk = streamk;
@@ -338,6 +343,8 @@ int prefill_call(void* out, int out_dtype, const void* q, const int32_t* cu_q_le
     d.num_kv_heads = num_kv_heads;
     d.block_size = block_size;
     d.scale_log2 = a.scale_log2;
+    d.kv_fp8 = kv_fp8;
+    d.out_scale = a.out_scale;
     d.cum = static_cast<int32_t*>(workspace);
     d.records = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                          align_up((size_t)(num_seqs + 1) * sizeof(int32_t), 256));
@@ -357,8 +364,21 @@ int pkv_paged_prefill_attn(void* out, int out_dtype, const void* q, const int32_
                            int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                            float scale, int causal, void* workspace, size_t workspace_bytes,
                            void* stream) {
-    return prefill_call(out, out_dtype, q, cu_q_lens, k_cache, v_cache, block_table,
-                        max_blocks_per_seq, context_lens, max_context_len, max_q_len,
+    return prefill_call(out, out_dtype, q, cu_q_lens, k_cache, v_cache, false, 1.0f, 1.0f,
+                        block_table, max_blocks_per_seq, context_lens, max_context_len, max_q_len,
+                        num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                        scale, causal, nullptr, workspace, workspace_bytes, stream);
+}
+
+int pkv_paged_prefill_attn_fp8(void* out, int out_dtype, const void* q, const int32_t* cu_q_lens,
+                               const void* k_cache, const void* v_cache, float k_scale,
+                               float v_scale, const int32_t* block_table, int max_blocks_per_seq,
+                               const int32_t* context_lens, int max_context_len, int max_q_len,
+                               int num_q_tokens, int num_seqs, int num_q_heads, int num_kv_heads,
+                               int head_dim, int block_size, float scale, int causal,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_call(out, out_dtype, q, cu_q_lens, k_cache, v_cache, true, k_scale, v_scale,
+                        block_table, max_blocks_per_seq, context_lens, max_context_len, max_q_len,
                         num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                         scale, causal, nullptr, workspace, workspace_bytes, stream);
 }
@@ -374,8 +394,8 @@ int pkv_paged_prefill_attn_tree(void* out, int out_dtype, const void* q,
     if (max_q_len > kMaxTreeNodes) return PKV_ERR_UNSUPPORTED;
     if (num_seqs > 0 && num_q_tokens > 0 && !tree_mask) return PKV_ERR_NULL;
     if (reinterpret_cast<uintptr_t>(tree_mask) & 7) return PKV_ERR_ALIGN;
-    return prefill_call(out, out_dtype, q, cu_q_lens, k_cache, v_cache, block_table,
-                        max_blocks_per_seq, context_lens, max_context_len, max_q_len,
+    return prefill_call(out, out_dtype, q, cu_q_lens, k_cache, v_cache, false, 1.0f, 1.0f,
+                        block_table, max_blocks_per_seq, context_lens, max_context_len, max_q_len,
                         num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                         scale, 1, tree_mask, workspace, workspace_bytes, stream);
 }

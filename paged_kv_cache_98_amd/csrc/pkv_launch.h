@@ -71,8 +71,10 @@ struct PrefillArgs {
     bool out_bf16;
     const uint16_t* q;
     const int32_t* cu_q_lens;
-    const uint16_t* k_cache;
-    const uint16_t* v_cache;
+    const void* k_cache;  // bf16, or FP8 (E4M3) codes when kv_fp8
+    const void* v_cache;
+    bool kv_fp8 = false;
+    float out_scale = 1.0f;  // multiplies the output (the FP8 cache's v_scale)
     const int32_t* block_table;
     int max_blocks_per_seq;
     const int32_t* context_lens;

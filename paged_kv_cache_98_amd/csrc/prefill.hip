@@ -205,6 +205,99 @@ __device__ __forceinline__ void stage_store(const Stage& sg, uint16_t* __restric
     }
 }
 
+// FP8 (E4M3) pools: a 64-key tile of one KV head is 8 KB of K codes and 8 KB
+// of V codes.  Thread t stages K rows t / 8 and t / 8 + 32 and V rows
+// 2 (t / 8) and 2 (t / 8) + 1, bytes (dims) 16 (t % 8) .. + 15 of each; in
+// LDS the tile takes the layouts of the bf16 path, K widened to bf16 and V
+// to fp16 (both exact for E4M3 values), so the tile math is the same.  The
+// scales are applied outside: k_scale in the score scale, v_scale in the
+// final division.
+struct StageFp8 {
+    uint4 k[2];
+    uint4 v[2];
+};
+
+template <int BS>
+__device__ __forceinline__ void stage_offsets_fp8(uint32_t (&koff)[4], uint32_t (&voff)[4],
+                                                  uint32_t row_bytes, int tid) {
+    const int col = tid & 7;
+    const int kq = tid >> 3;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) koff[i] = (uint32_t)((kq + 32 * i) % BS) * row_bytes + col * 16;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) voff[p] = (uint32_t)((2 * kq + p) % BS) * row_bytes + col * 16;
+    koff[2] = koff[3] = voff[2] = voff[3] = 0;
+}
+
+// A wave's K load i lies in the tile's 16-key group wave / 2 + 2 i and its V
+// loads in group `wave` (t / 8 = 8 wave + lane / 8), one physical block each.
+template <int BS>
+__device__ __forceinline__ void stage_load_fp8(StageFp8& sg, PrefillIds& ids, const char* kbase,
+                                               const char* vbase, int k0, int kv_end,
+                                               size_t block_bytes, const uint32_t (&koff)[4],
+                                               const uint32_t (&voff)[4], int tid, int lane) {
+    const int kq = tid >> 3;
+    const int wave = tid >> 6;
+    int id[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) id[i] = ids.get((k0 + 16 * i) / BS, lane);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int kid = __builtin_amdgcn_readfirstlane(id[(wave >> 1) + 2 * i]);
+        const __amdgpu_buffer_rsrc_t r = buffer_rsrc(kbase + (size_t)kid * block_bytes);
+        const uint32_t o = k0 + kq + 32 * i < kv_end ? koff[i] : kBufferOob;
+        sg.k[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0));
+    }
+    const int vid = __builtin_amdgcn_readfirstlane(id[wave]);
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(vbase + (size_t)vid * block_bytes);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const uint32_t o = k0 + 2 * kq + p < kv_end ? voff[p] : kBufferOob;
+        sg.v[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0));
+    }
+}
+
+__device__ __forceinline__ void stage_store_fp8(const StageFp8& sg, uint16_t* __restrict__ ks,
+                                                uint16_t* __restrict__ vt, int tid) {
+    const int col = tid & 7;
+    const int kq = tid >> 3;
+    // K: 16 codes -> 16 bf16 in row kq + 32 i, elements 16 col .. + 15
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const uint32_t w[4] = {sg.k[i].x, sg.k[i].y, sg.k[i].z, sg.k[i].w};
+        uint32_t b[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            b[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[j], 1.0f, false));
+            b[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[j], 1.0f, true));
+        }
+        uint16_t* row = ks + (kq + 32 * i) * kKsStride + 16 * col;
+        *reinterpret_cast<uint4*>(row) = make_uint4(b[0], b[1], b[2], b[3]);
+        *reinterpret_cast<uint4*>(row + 8) = make_uint4(b[4], b[5], b[6], b[7]);
+    }
+    // V^T: keys 2 kq and 2 kq + 1 are the pair at offset 2 (kq % 2) of
+    // 4-key group kq / 2; dim d = 16 col + 4 j + e takes the fp16 pair
+    // (key 2 kq, key 2 kq + 1), its group stored at (kq / 2) ^ swizzle(d)
+    const uint32_t a[4] = {sg.v[0].x, sg.v[0].y, sg.v[0].z, sg.v[0].w};
+    const uint32_t c[4] = {sg.v[1].x, sg.v[1].y, sg.v[1].z, sg.v[1].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        // bytes (a.k, c.k, a.k+1, c.k+1) of the two rows' words, k = 0 and 2
+        const uint32_t w0 = __builtin_amdgcn_perm(c[j], a[j], 0x05010400u);
+        const uint32_t w1 = __builtin_amdgcn_perm(c[j], a[j], 0x07030602u);
+        const f16x2_t vp[4] = {__builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w0, 1.0f, false),
+                               __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w0, 1.0f, true),
+                               __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w1, 1.0f, false),
+                               __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w1, 1.0f, true)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int d = 16 * col + 4 * j + e;
+            *reinterpret_cast<uint32_t*>(vt + d * kVtStride + 4 * ((kq >> 1) ^ vt_swizzle(d)) +
+                                         2 * (kq & 1)) = __builtin_bit_cast(uint32_t, vp[e]);
+        }
+    }
+}
+
 // Online-softmax step for one 32-key half tile of this lane's query column:
 // raw scores s (element e is key kb0 + 8 (e / 4) + 4 h + e % 4) -> P^T
 // fragments (fp16, k-steps of 16 keys) and the updated running max / sum,
@@ -272,13 +365,14 @@ constexpr int64_t kMaxChunkWorkers = 1024;  // stream-K workgroups, at most
 // rec_col is this lane's column record, or NULL for the final output: with
 // a record the unnormalised O^T, the reference maximum m and the sum l are
 // stored instead of O / l.
-template <int BS, int G, bool OUT_BF16>
+template <int BS, int G, bool OUT_BF16, bool FP8>
 __device__ __forceinline__ void chunk_item(
     uint16_t (&s_ks)[2][kKsElems], uint16_t (&s_vt)[2][kVtElems], void* __restrict__ out,
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
-    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ bt_row, int num_q_heads,
-    int num_kv_heads, float scale_log2, int causal, const uint64_t* __restrict__ tree_mask,
-    int q_begin, int lq, int ctx, int kvh, int r0, int t0, int t1, float* rec_col) {
+    const uint16_t* __restrict__ q, const void* __restrict__ k_cache,
+    const void* __restrict__ v_cache, const int32_t* __restrict__ bt_row, int num_q_heads,
+    int num_kv_heads, float scale_log2, float out_scale, int causal,
+    const uint64_t* __restrict__ tree_mask, int q_begin, int lq, int ctx, int kvh, int r0, int t0,
+    int t1, float* rec_col) {
     constexpr int P = kCols / G;  // query positions per workgroup
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -321,20 +415,35 @@ __device__ __forceinline__ void chunk_item(
     float m_run = kNegBig;
     float l_run = 0.0f;
 
-    const uint32_t row_bytes = (uint32_t)num_kv_heads * D * sizeof(uint16_t);
+    constexpr int kElem = FP8 ? 1 : 2;  // bytes per cached value
+    const uint32_t row_bytes = (uint32_t)num_kv_heads * D * kElem;
     const size_t block_bytes = (size_t)BS * row_bytes;
-    const char* kbase = reinterpret_cast<const char*>(k_cache) + (size_t)kvh * D * sizeof(uint16_t);
-    const char* vbase = reinterpret_cast<const char*>(v_cache) + (size_t)kvh * D * sizeof(uint16_t);
+    const char* kbase = reinterpret_cast<const char*>(k_cache) + (size_t)kvh * D * kElem;
+    const char* vbase = reinterpret_cast<const char*>(v_cache) + (size_t)kvh * D * kElem;
     uint32_t koff[4], voff[4];
-    stage_offsets<BS>(koff, voff, row_bytes, tid);
+    if constexpr (FP8)
+        stage_offsets_fp8<BS>(koff, voff, row_bytes, tid);
+    else
+        stage_offsets<BS>(koff, voff, row_bytes, tid);
     PrefillIds ids;
     ids.init(bt_row, (ctx + BS - 1) / BS, t0 * kKT / BS, lane);
-
-    Stage sg;
+    using StageT = std::conditional_t<FP8, StageFp8, Stage>;
+    auto load_next = [&](StageT& x, int k0n) {
+        if constexpr (FP8)
+            stage_load_fp8<BS>(x, ids, kbase, vbase, k0n, kv_end, block_bytes, koff, voff, tid, lane);
+        else
+            stage_load<BS>(x, ids, kbase, vbase, k0n, kv_end, block_bytes, koff, voff, tid, lane);
+    };
+    auto store_tile = [&](const StageT& x, int b) {
+        if constexpr (FP8)
+            stage_store_fp8(x, s_ks[b], s_vt[b], tid);
+        else
+            stage_store(x, s_ks[b], s_vt[b], tid);
+    };
+    StageT sg;
     if (t1 > t0) {
-        stage_load<BS>(sg, ids, kbase, vbase, t0 * kKT, kv_end, block_bytes, koff, voff, tid,
-                       lane);
-        stage_store(sg, s_ks[t0 & 1], s_vt[t0 & 1], tid);
+        load_next(sg, t0 * kKT);
+        store_tile(sg, t0 & 1);
     }
     __syncthreads();
 
@@ -354,8 +463,7 @@ __device__ __forceinline__ void chunk_item(
         const int k0 = j * kKT;
         const int buf = j & 1;
         if (next)
-            stage_load<BS>(sg, ids, kbase, vbase, k0 + kKT, kv_end, block_bytes, koff, voff, tid,
-                           lane);
+            load_next(sg, k0 + kKT);
         // S for both halves first, so that each half's softmax (VALU) has
         // matrix-core work in flight beside it: the second half's S during
         // the first softmax, the first half's P V during the second
@@ -393,7 +501,7 @@ __device__ __forceinline__ void chunk_item(
                 }
             }
         }
-        if (next) stage_store(sg, s_ks[buf ^ 1], s_vt[buf ^ 1], tid);
+        if (next) store_tile(sg, buf ^ 1);
         __syncthreads();
     };
     // Only tiles that reach the causal diagonal (k0 + 63 > pos0 + r0) or the
@@ -409,9 +517,8 @@ __device__ __forceinline__ void chunk_item(
     if (r0 + (wave * 32) / G >= lq) {
         for (int jj = t0; jj < t1; ++jj) {
             if (jj + 1 < t1) {
-                stage_load<BS>(sg, ids, kbase, vbase, (jj + 1) * kKT, kv_end, block_bytes, koff,
-                               voff, tid, lane);
-                stage_store(sg, s_ks[(jj + 1) & 1], s_vt[(jj + 1) & 1], tid);
+                load_next(sg, (jj + 1) * kKT);
+                store_tile(sg, (jj + 1) & 1);
             }
             __syncthreads();
         }
@@ -445,7 +552,7 @@ __device__ __forceinline__ void chunk_item(
         }
         return;
     }
-    const float inv = ntiles > 0 ? 1.0f / lt : 0.0f;
+    const float inv = ntiles > 0 ? out_scale / lt : 0.0f;
     const size_t orow = ((size_t)(q_begin + r) * num_q_heads + (size_t)kvh * G + g) * D;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
@@ -471,14 +578,14 @@ __device__ __forceinline__ void chunk_item(
 // positions per workgroup; block 256.  Slot y of sequence i is y - T(i),
 // T(i) = cu_q_lens[i] / P + i; T never skips a needed slot.  Each
 // workgroup runs all key tiles of its (slot, KV head) item.
-template <int BS, int G, bool OUT_BF16>
+template <int BS, int G, bool OUT_BF16, bool FP8>
 __global__ void __launch_bounds__(kThreads, 2)
 prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
-                    const int32_t* __restrict__ cu_q_lens, const uint16_t* __restrict__ k_cache,
-                    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
+                    const int32_t* __restrict__ cu_q_lens, const void* __restrict__ k_cache,
+                    const void* __restrict__ v_cache, const int32_t* __restrict__ block_table,
                     int max_blocks_per_seq, const int32_t* __restrict__ context_lens,
                     int max_context_len, int num_seqs, int num_q_heads, int num_kv_heads,
-                    float scale_log2, int causal, int decode_rows_elsewhere,
+                    float scale_log2, float out_scale, int causal, int decode_rows_elsewhere,
                     const uint64_t* __restrict__ tree_mask) {
     constexpr int P = kCols / G;
     __shared__ __attribute__((aligned(16))) uint16_t s_ks[2][kKsElems];
@@ -510,10 +617,11 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
     const int pos0 = ctx - lq;
     const int r_last = (r0 + P < lq ? r0 + P : lq) - 1;
     const int kv_end = causal ? (pos0 + r_last + 1 < ctx ? pos0 + r_last + 1 : ctx) : ctx;
-    chunk_item<BS, G, OUT_BF16>(s_ks, s_vt, out, q, k_cache, v_cache,
-                                block_table + (size_t)seq * max_blocks_per_seq, num_q_heads,
-                                num_kv_heads, scale_log2, causal, tree_mask, q_begin, lq, ctx, kvh,
-                                r0, 0, (kv_end + kKT - 1) / kKT, nullptr);
+    chunk_item<BS, G, OUT_BF16, FP8>(s_ks, s_vt, out, q, k_cache, v_cache,
+                                     block_table + (size_t)seq * max_blocks_per_seq, num_q_heads,
+                                     num_kv_heads, scale_log2, out_scale, causal, tree_mask,
+                                     q_begin, lq, ctx, kvh, r0, 0, (kv_end + kKT - 1) / kKT,
+                                     nullptr);
 }
 
 // Stream-K units of sequence i in a call of chunks that fit one workgroup
@@ -546,16 +654,16 @@ __device__ __forceinline__ int streamk_units(const int32_t* __restrict__ cu_q_le
 // unit prefix sums, which workgroup 0 also stores in cum_out.
 // Records: [num_workers][2][max_q_len * G][kRecStride] floats, column
 // c = r G + g.
-template <int BS, int G, bool OUT_BF16>
+template <int BS, int G, bool OUT_BF16, bool FP8>
 __global__ void __launch_bounds__(kThreads, 2)
 prefill_streamk_kernel(void* __restrict__ out, float* __restrict__ rec,
                        int32_t* __restrict__ cum_out, const uint16_t* __restrict__ q,
-                       const int32_t* __restrict__ cu_q_lens, const uint16_t* __restrict__ k_cache,
-                       const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
+                       const int32_t* __restrict__ cu_q_lens, const void* __restrict__ k_cache,
+                       const void* __restrict__ v_cache, const int32_t* __restrict__ block_table,
                        int max_blocks_per_seq, const int32_t* __restrict__ context_lens,
                        int max_context_len, int num_seqs, int num_q_heads, int num_kv_heads,
-                       float scale_log2, int causal, int decode_rows_elsewhere, int num_workers,
-                       int max_q_len, const uint64_t* __restrict__ tree_mask) {
+                       float scale_log2, float out_scale, int causal, int decode_rows_elsewhere,
+                       int num_workers, int max_q_len, const uint64_t* __restrict__ tree_mask) {
     const int rec_cols = max_q_len * G;  // columns per record slot
     __shared__ __attribute__((aligned(16))) uint16_t s_ks[2][kKsElems];
     __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kVtElems];
@@ -636,10 +744,10 @@ prefill_streamk_kernel(void* __restrict__ out, float* __restrict__ rec,
         float* rc = (tile0 != 0 || t1 != n)
                         ? rec + ((size_t)(w * 2 + slot) * rec_cols + col) * kRecStride
                         : nullptr;
-        chunk_item<BS, G, OUT_BF16>(s_ks, s_vt, out, q, k_cache, v_cache,
-                                    block_table + (size_t)seq * max_blocks_per_seq, num_q_heads,
-                                    num_kv_heads, scale_log2, causal, tree_mask, q_begin, lq, ctx,
-                                    kvh, 0, tile0, t1, rc);
+        chunk_item<BS, G, OUT_BF16, FP8>(s_ks, s_vt, out, q, k_cache, v_cache,
+                                         block_table + (size_t)seq * max_blocks_per_seq,
+                                         num_q_heads, num_kv_heads, scale_log2, out_scale, causal,
+                                         tree_mask, q_begin, lq, ctx, kvh, 0, tile0, t1, rc);
         slot = 1;
         t = seg_end;
     }
@@ -658,7 +766,7 @@ __global__ void __launch_bounds__(256)
 prefill_streamk_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
                              const int32_t* __restrict__ cum, const int32_t* __restrict__ cu_q_lens,
                              int num_seqs, int num_q_heads, int num_kv_heads, int num_workers,
-                             int rec_cols, int decode_rows_elsewhere) {
+                             int rec_cols, int decode_rows_elsewhere, float out_scale) {
     const int lane = threadIdx.x & 63;
     const int seq = blockIdx.x;
     const int item = blockIdx.y * 4 + (threadIdx.x >> 6);
@@ -730,15 +838,15 @@ prefill_streamk_merge_kernel(void* __restrict__ out, const float* __restrict__ r
             }
         }
     }
-    const float inv = 1.0f / L;
+    const float inv = out_scale / L;
     store2(a0 * inv, a1 * inv);
 }
 
-template <int BS, int G, bool OUT_BF16>
+template <int BS, int G, bool OUT_BF16, bool FP8>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     constexpr int P = kCols / G;
     if (a.streamk) {
-        auto kern = prefill_streamk_kernel<BS, G, OUT_BF16>;
+        auto kern = prefill_streamk_kernel<BS, G, OUT_BF16, FP8>;
         const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int32_t);
         int resident = 0;
         hipError_t e = resident_workgroups(reinterpret_cast<const void*>(kern), kThreads, lds,
@@ -752,29 +860,34 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
                            a.records, a.cum, a.q, a.cu_q_lens, a.k_cache, a.v_cache,
                            a.block_table, a.max_blocks_per_seq, a.context_lens,
                            a.max_context_len, a.num_seqs, a.num_q_heads, a.num_kv_heads,
-                           a.scale_log2, a.causal ? 1 : 0, a.decode_rows_elsewhere ? 1 : 0,
-                           (int)workers, a.max_q_len, a.tree_mask);
+                           a.scale_log2, a.out_scale, a.causal ? 1 : 0,
+                           a.decode_rows_elsewhere ? 1 : 0, (int)workers, a.max_q_len,
+                           a.tree_mask);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         dim3 mgrid(a.num_seqs, (a.max_q_len * a.num_q_heads + 3) / 4);
         hipLaunchKernelGGL((prefill_streamk_merge_kernel<G, OUT_BF16>), mgrid, dim3(256), 0,
                            stream, a.out, a.records, a.cum, a.cu_q_lens, a.num_seqs,
                            a.num_q_heads, a.num_kv_heads, (int)workers, a.max_q_len * G,
-                           a.decode_rows_elsewhere ? 1 : 0);
+                           a.decode_rows_elsewhere ? 1 : 0, a.out_scale);
         return hipGetLastError();
     }
     const int slots = a.num_q_tokens / P + a.num_seqs;
-    hipLaunchKernelGGL((prefill_mfma_kernel<BS, G, OUT_BF16>), dim3(slots, a.num_kv_heads),
+    hipLaunchKernelGGL((prefill_mfma_kernel<BS, G, OUT_BF16, FP8>), dim3(slots, a.num_kv_heads),
                        dim3(kThreads), 0, stream, a.out, a.q, a.cu_q_lens, a.k_cache, a.v_cache,
                        a.block_table, a.max_blocks_per_seq, a.context_lens, a.max_context_len,
-                       a.num_seqs, a.num_q_heads, a.num_kv_heads, a.scale_log2,
+                       a.num_seqs, a.num_q_heads, a.num_kv_heads, a.scale_log2, a.out_scale,
                        a.causal ? 1 : 0, a.decode_rows_elsewhere ? 1 : 0, a.tree_mask);
     return hipGetLastError();
 }
 
 template <int BS, int G>
 hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t s) {
-    return a.out_bf16 ? launch_prefill_t<BS, G, true>(a, s) : launch_prefill_t<BS, G, false>(a, s);
+    if (a.kv_fp8)
+        return a.out_bf16 ? launch_prefill_t<BS, G, true, true>(a, s)
+                          : launch_prefill_t<BS, G, false, true>(a, s);
+    return a.out_bf16 ? launch_prefill_t<BS, G, true, false>(a, s)
+                      : launch_prefill_t<BS, G, false, false>(a, s);
 }
 
 template <int BS>

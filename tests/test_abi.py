@@ -239,6 +239,19 @@ def test_prefill_workspace_size(lib):
     assert ws(4, 10, 4, 32, 6, 128, 100) == 0                       # Hq % Hkv
 
 
+def test_prefill_fp8_validation(lib):
+    E = binding
+    f = lib.pkv_paged_prefill_attn_fp8
+    args = lambda ks=1.0, vs=1.0, nq=60, q=P: (P, 0, q, P, P, P, ks, vs, P, 8, P, 100, 50, nq, 4,
+                                             8, 2, 128, 16, 0.1, 1, None, 0, None)
+    assert f(*args(ks=0.0)) == E.PKV_ERR_VALUE
+    assert f(*args(vs=-1.0)) == E.PKV_ERR_VALUE
+    assert f(*args(ks=float("inf"))) == E.PKV_ERR_VALUE
+    assert f(*args(ks=float("nan"))) == E.PKV_ERR_VALUE
+    assert f(*args(nq=201)) == E.PKV_ERR_SHAPE
+    assert f(*args(nq=0, q=None)) == E.PKV_OK
+
+
 def test_binding_error_classes():
     """Argument errors raise ValueError (InvalidArgument); pool exhaustion
     MemoryError; unknown sequences KeyError; launch failures stay

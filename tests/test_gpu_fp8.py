@@ -169,3 +169,69 @@ def test_decode_fp8_full_8b_batch_sampled():
                                    np.arange(len(ids), dtype=np.int32)[None, :],
                                    np.array([n], dtype=np.int32), w.scale)
         parity(out[i:i + 1], ref, what=f"fp8 full batch seq {i} (ctx {n})")
+
+
+# (context length including the chunk, chunk rows): whole prompts, chunks
+# straddling key tiles, decode rows and an empty sequence in the same call
+FP8_CHUNKS = [(37, 37), (141, 100), (300, 200), (64, 1), (520, 129), (1000, 64), (77, 0),
+              (700, 1)]
+
+
+def oracle_prefill_fp8(bc, kc, vc, causal, k_scale, v_scale):
+    w = bc.workload
+    return fp8.paged_prefill_fp8(bits16(bc.q), codes(kc), codes(vc), k_scale, v_scale,
+                                 bc.block_table.numpy(), bc.context_lens.numpy(),
+                                 bc.cu_q_lens.numpy(), w.scale, causal=causal)
+
+
+def run_prefill_fp8(b, kd, vd, causal, k_scale, v_scale, out_dtype=torch.float32):
+    w = b.workload
+    return pkv.paged_prefill_attn_fp8(b.q, b.cu_q_lens, kd, vd, k_scale, v_scale, b.block_table,
+                                      b.context_lens, w.scale, max_context_len=w.max_context_len,
+                                      max_q_len=w.max_q_len, causal=causal, out_dtype=out_dtype)
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("group", [1, 4, 16])
+def test_prefill_fp8_chunks(bs, group):
+    """Wide chunks (the grid kernel) and decode rows (the FP8 decode path)
+    over FP8 pools, causal and not, non-power-of-two scales."""
+    hkv, k_scale, v_scale = 2, 0.0371, 0.113
+    w = W.make_workload(f"fp8_chunks_g{group}_bs{bs}", [c for c, _ in FP8_CHUNKS],
+                        [q for _, q in FP8_CHUNKS], num_q_heads=hkv * group, num_kv_heads=hkv,
+                        block_size=bs, seed=3400 + group + bs)
+    print(f"[fp8 prefill] {w.name}", flush=True)
+    bc = W.materialize(w, logical=True, poison=True)
+    kc, vc = W.fp8_pools(bc, k_scale, v_scale)
+    b = bc.to(DEV)
+    kd, vd = kc.to(DEV), vc.to(DEV)
+    for causal in (True, False):
+        out = run_prefill_fp8(b, kd, vd, causal, k_scale, v_scale)
+        torch.cuda.synchronize()
+        parity(out, oracle_prefill_fp8(bc, kc, vc, causal, k_scale, v_scale),
+               what=f"{w.name} causal={causal}")
+
+
+@pytest.mark.parametrize("group,rows", [(4, 6), (8, 16), (16, 8)])
+def test_prefill_fp8_streamk(group, rows):
+    """Chunks that fit one workgroup run stream-K over FP8 pools: items cut
+    between workers are merged with the v_scale; bf16 output equals the fp32
+    output rounded; determinism."""
+    from tests.gpu_common import bf16_parity
+    cases = [(3000, rows), (2500, 1), (40, 3), (4100, rows), (700, rows - 1), (129, 2)]
+    w = W.make_workload(f"fp8_streamk_g{group}_r{rows}", [c for c, _ in cases],
+                        [q for _, q in cases], num_q_heads=2 * group, num_kv_heads=2,
+                        block_size=16, seed=3500 + group + rows)
+    print(f"[fp8 stream-K] {w.name}", flush=True)
+    bc = W.materialize(w, logical=True, poison=True)
+    kc, vc = W.fp8_pools(bc)
+    b = bc.to(DEV)
+    kd, vd = kc.to(DEV), vc.to(DEV)
+    o32 = run_prefill_fp8(b, kd, vd, True, W.FP8_SCALE, W.FP8_SCALE)
+    o32b = run_prefill_fp8(b, kd, vd, True, W.FP8_SCALE, W.FP8_SCALE)
+    o16 = run_prefill_fp8(b, kd, vd, True, W.FP8_SCALE, W.FP8_SCALE, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o32, o32b)
+    ref = oracle_prefill_fp8(bc, kc, vc, True, W.FP8_SCALE, W.FP8_SCALE)
+    parity(o32, ref, what=w.name)
+    bf16_parity(o16, o32, ref, what=w.name + " bf16 out")
