@@ -297,6 +297,9 @@ def workload_by_name(name):
         # token-tree verification: 16-node candidate trees per sequence
         "spec_verify_tree": lambda: W.spec_verify_tree(),
         "mixed_prefill": lambda: W.mixed_prefill(),
+        # the chunk and verify batches over an FP8 (E4M3) cache
+        "prefill_chunks_fp8": lambda: W.mixed_prefill(num_decodes=0),
+        "spec_verify_fp8": lambda: W.spec_verify(),
     }
     if name not in table:
         raise SystemExit(f"unknown workload {name}; choose from {sorted(table)}")
@@ -421,11 +424,17 @@ def main():
     tree_mask = W.tree_masks(w).to(dev) if is_tree else None
 
     def attend():
-        if kv_fp8:
+        if kv_fp8 and w.is_decode:
             pkv.paged_decode_attn_fp8(b.q, b.k_cache, b.v_cache, W.FP8_SCALE, W.FP8_SCALE,
                                       b.block_table, b.context_lens, w.scale,
                                       max_context_len=w.max_context_len, out=out, workspace=ws,
                                       stream=stream)
+        elif kv_fp8:
+            pkv.paged_prefill_attn_fp8(b.q, b.cu_q_lens, b.k_cache, b.v_cache, W.FP8_SCALE,
+                                       W.FP8_SCALE, b.block_table, b.context_lens, w.scale,
+                                       max_context_len=w.max_context_len, max_q_len=w.max_q_len,
+                                       causal=True, out=out,
+                                       workspace=ws if ws_bytes else None, stream=stream)
         elif w.is_decode:
             pkv.paged_decode_attn(b.q, b.k_cache, b.v_cache, b.block_table, b.context_lens,
                                   w.scale, max_context_len=w.max_context_len, out=out,
@@ -505,10 +514,11 @@ def main():
                             "KV HBM GB/s + verified tokens/s"),
             "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "fp8-e4m3 KV, bf16 q" if kv_fp8 else "bf16",
             "data": "synthetic",
-            "config": {"workload": w.name, **{k: v for k, v in w.describe().items()
-                                              if k != "workload"}},
+            "config": {"workload": wname, **{k: v for k, v in w.describe().items()
+                                             if k != "workload"}},
             "tokens_per_s": round(w.total_q / (ms_per_step * 1e-3), 1),
             "kernels_us": {"kv_append": round(statistics.mean(append_ms) * 1e3, 2),
                            "paged_prefill_attn": round(dec_avg * 1e3, 2)},
@@ -533,10 +543,11 @@ def main():
             "metric": "paged prefill attn: MFMA TFLOP/s (exact causal FLOPs) + decode-row KV GB/s",
             "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "fp8-e4m3 KV, bf16 q" if kv_fp8 else "bf16",
             "data": "synthetic",
-            "config": {"workload": w.name, **{k: v for k, v in w.describe().items()
-                                              if k != "workload"}},
+            "config": {"workload": wname, **{k: v for k, v in w.describe().items()
+                                             if k != "workload"}},
             "kernels_us": {"kv_append": round(statistics.mean(append_ms) * 1e3, 2),
                            "paged_prefill_attn": round(dec_avg * 1e3, 2)},
             "decode_rows_kv_gbs": round(dkv / (dec_avg * 1e-3) / 1e9, 1),
