@@ -306,30 +306,34 @@ def workload_by_name(name):
     return table[name]()
 
 
-def cpu_baseline(batch, w, reps=2):
-    """The fp64 oracle, as it stands, on the same batch (host copies)."""
+def cpu_baseline(batch, w, min_seconds=10.0):
+    """The fp64 oracle, as it stands, on the same batch (host copies),
+    repeated over the whole batch for at least min_seconds; the rate is the
+    mean over all repetitions."""
     import oracle
     threads = len(os.sched_getaffinity(0))
     q = batch.q.cpu()
     kc, vc = batch.k_cache.cpu(), batch.v_cache.cpu()
     bt, cl = batch.block_table.cpu(), batch.context_lens.cpu()
-    times = []
-    for _ in range(reps):
+    reps, total = 0, 0.0
+    while reps < 2 or total < min_seconds:
         t0 = time.perf_counter()
         oracle.paged_attention(q, kc, vc, bt, cl, w.scale, num_threads=threads)
-        times.append(time.perf_counter() - t0)
-    t = min(times)
+        total += time.perf_counter() - t0
+        reps += 1
+    t = total / reps
     kv_bytes = sum(w.context_lens) * w.kv_token_bytes()
     return {"value": round(kv_bytes / t / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"whole {w.name} batch ({w.num_seqs} seqs, sum ctx {sum(w.context_lens)}), "
-                      f"fp64 C + OpenMP, best of {reps}: {t:.3f} s per batch "
-                      f"({w.num_seqs / t:.2f} seq-steps/s)"}
+                      f"fp64 C + OpenMP, {reps} repetitions in {total:.1f} s: {t:.3f} s per "
+                      f"batch on average ({w.num_seqs / t:.2f} seq-steps/s)"}
 
 
-def cpu_baseline_fp8(batch, w, seqs=8):
+def cpu_baseline_fp8(batch, w, seqs=8, min_seconds=10.0):
     """The fp64 FP8-cache oracle (numpy, one process), as it stands, on the
-    first `seqs` sequences of the batch (host copies of their blocks)."""
+    first `seqs` sequences of the batch (host copies of their blocks),
+    repeated for at least min_seconds; the rate is the mean."""
     import numpy as np
     import torch
     from oracle import fp8
@@ -346,14 +350,19 @@ def cpu_baseline_fp8(batch, w, seqs=8):
         table[i, :need[i]] = np.arange(base, base + need[i])
         base += need[i]
     q = batch.q[:seqs].cpu().view(torch.int16).numpy().view(np.uint16)
-    t0 = time.perf_counter()
-    fp8.paged_decode_fp8(q, kc, vc, W.FP8_SCALE, W.FP8_SCALE, table, np.array(ctx, np.int32),
-                         w.scale)
-    t = time.perf_counter() - t0
+    reps, total = 0, 0.0
+    while reps < 2 or total < min_seconds:
+        t0 = time.perf_counter()
+        fp8.paged_decode_fp8(q, kc, vc, W.FP8_SCALE, W.FP8_SCALE, table,
+                             np.array(ctx, np.int32), w.scale)
+        total += time.perf_counter() - t0
+        reps += 1
+    t = total / reps
     kv_bytes = sum(ctx) * w.kv_token_bytes() // 2
     return {"value": round(kv_bytes / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {seqs} sequences of the batch (sum ctx {sum(ctx)}), fp64 numpy: "
-                      f"{t:.3f} s ({seqs / t:.2f} seq-steps/s)"}
+            "sample": f"first {seqs} sequences of the batch (sum ctx {sum(ctx)}), fp64 numpy, "
+                      f"{reps} repetitions in {total:.1f} s: {t:.3f} s each on average "
+                      f"({seqs / t:.2f} seq-steps/s)"}
 
 
 def main():
