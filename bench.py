@@ -95,6 +95,14 @@ TRAFFIC_SPEC = {
                           "sources": ["paged_kv_cache_98_amd/csrc/prefill.hip",
                                       "paged_kv_cache_98_amd/csrc/pkv_device.h"],
                           "args": "--workload spec_verify_tree"},
+    "spec_verify_b64_q6_fp8": {"kernels": ["prefill_streamk_kernel", "prefill_streamk_merge_kernel"],
+                               "sources": ["paged_kv_cache_98_amd/csrc/prefill.hip",
+                                           "paged_kv_cache_98_amd/csrc/pkv_device.h"],
+                               "args": "--workload spec_verify_fp8"},
+    "mixed_prefill_c4x512_d0_fp8": {"kernels": ["prefill_mfma_kernel"],
+                                    "sources": ["paged_kv_cache_98_amd/csrc/prefill.hip",
+                                                "paged_kv_cache_98_amd/csrc/pkv_device.h"],
+                                    "args": "--workload prefill_chunks_fp8"},
     "cow_copy_4096x32k": {"kernels": ["copy_blocks_kernel"],
                           "sources": ["paged_kv_cache_98_amd/csrc/kv_append.hip"],
                           "args": "--workload cow_copy"},
