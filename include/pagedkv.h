@@ -232,7 +232,8 @@ size_t pkv_prefill_workspace_bytes(int num_seqs, int num_q_tokens, int max_q_len
  * tile) units cut into equal ranges over the workgroups the GPU holds at
  * once, items shared by two workers merged by a log-sum-exp fold in a
  * second kernel.  num_seqs <= 16383 and num_kv_heads in 1..8 or 16 when
- * single-row sequences can be present.  QK^T runs as bf16 x bf16 MFMA with fp32 accumulation;
+ * single-row sequences can be present; num_seqs <= 16383 for chunks that fit
+ * one workgroup (PKV_ERR_UNSUPPORTED otherwise).  QK^T runs as bf16 x bf16 MFMA with fp32 accumulation;
  * P V runs as fp16 x fp16 MFMA with fp32 accumulation, V converted from bf16
  * to fp16 in registers: exact for |v| in [2^-14, 65504]; smaller magnitudes
  * keep an absolute error below 2^-25, and |v| > 65504 is outside the

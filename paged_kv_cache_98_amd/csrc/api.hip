@@ -281,6 +281,9 @@ int prefill_call(void* out, int out_dtype, const void* q, const int32_t* cu_q_le
                                   (num_kv_heads <= 8 || num_kv_heads == kMaxDecodeKvHeads);
     const bool streamk = pkv::prefill_streamk(max_q_len, num_q_heads / num_kv_heads);
     if (any_decode_rows && !decode_limits_ok) return PKV_ERR_UNSUPPORTED;
+    // the stream-K chunk kernel keeps the sequences' unit prefix sums in LDS
+    // beside its two tile buffers
+    if (streamk && num_seqs > kMaxDecodeSeqs) return PKV_ERR_UNSUPPORTED;
     size_t chunk_off = 0;
     if (any_decode_rows || streamk) {
         const size_t need = prefill_workspace(num_seqs, max_q_len, num_q_heads, num_kv_heads,

@@ -118,6 +118,8 @@ def test_prefill_validation(lib):
     assert prefill(lib, hq=8, hkv=3) == E.PKV_ERR_SHAPE
     assert prefill(lib, out=MIS) == E.PKV_ERR_ALIGN
     assert prefill(lib, nq=0, q=None) == E.PKV_OK
+    # few-row chunks (stream-K) keep per-sequence prefix sums in LDS
+    assert prefill(lib, nseq=16384, maxq=6, nq=16384 * 6, ws=P2, wsb=1 << 40) == E.PKV_ERR_UNSUPPORTED
 
 
 def prefill_tree(lib, **kw):
