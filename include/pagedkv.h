@@ -448,6 +448,21 @@ int pkv_paged_prefill_attn_tree(void *out, int out_dtype, const void *q,
                                 int head_dim, int block_size, float scale, void *workspace,
                                 size_t workspace_bytes, void *stream);
 
+/*
+ * paged_prefill_attn_tree_fp8 -- token-tree verification (as
+ * pkv_paged_prefill_attn_tree) over FP8 (E4M3) pools with k_scale / v_scale
+ * (as pkv_paged_prefill_attn_fp8).
+ */
+int pkv_paged_prefill_attn_tree_fp8(void *out, int out_dtype, const void *q,
+                                    const int32_t *cu_q_lens, const uint64_t *tree_mask,
+                                    const void *k_cache, const void *v_cache, float k_scale,
+                                    float v_scale, const int32_t *block_table,
+                                    int max_blocks_per_seq, const int32_t *context_lens,
+                                    int max_context_len, int max_q_len, int num_q_tokens,
+                                    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                    int block_size, float scale, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

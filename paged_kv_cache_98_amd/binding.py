@@ -35,7 +35,7 @@ PKV_OUT_BF16 = 1
 
 EXPORTED = ("pkv_status_string", "pkv_version", "pkv_kv_append", "pkv_decode_workspace_bytes",
             "pkv_paged_decode_attn", "pkv_prefill_workspace_bytes", "pkv_paged_prefill_attn",
-            "pkv_paged_prefill_attn_tree", "pkv_paged_prefill_attn_fp8", "pkv_kv_append_fp8", "pkv_paged_decode_attn_fp8", "pkv_copy_blocks", "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free",
+            "pkv_paged_prefill_attn_tree", "pkv_paged_prefill_attn_fp8", "pkv_paged_prefill_attn_tree_fp8", "pkv_kv_append_fp8", "pkv_paged_decode_attn_fp8", "pkv_copy_blocks", "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free",
             "pkv_bm_allocate", "pkv_bm_allocate_cached", "pkv_bm_num_cached", "pkv_bm_free", "pkv_bm_fork", "pkv_bm_append", "pkv_bm_append_batch",
             "pkv_bm_seq_info",
             "pkv_bm_refcount", "pkv_bm_block_table")
@@ -106,6 +106,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_paged_prefill_attn_fp8.argtypes = [_vp, _i32, _vp, _vp, _vp, _vp, _f32, _f32, _vp,
                                                _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                                _i32, _i32, _f32, _i32, _vp, _sz, _vp]
+    lib.pkv_paged_prefill_attn_tree_fp8.restype = _i32
+    lib.pkv_paged_prefill_attn_tree_fp8.argtypes = [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _f32,
+                                                    _f32, _vp, _i32, _vp, _i32, _i32, _i32,
+                                                    _i32, _i32, _i32, _i32, _i32, _f32, _vp,
+                                                    _sz, _vp]
     lib.pkv_paged_decode_attn_fp8.restype = _i32
     lib.pkv_paged_decode_attn_fp8.argtypes = [_vp, _i32, _vp, _vp, _vp, _f32, _f32, _vp, _i32, _vp,
                                               _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz,
@@ -221,11 +226,13 @@ def paged_prefill_attn_fp8(q: torch.Tensor, cu_q_lens: torch.Tensor, k_cache: to
                            block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
                            max_context_len: int, max_q_len: int, causal: bool = True,
                            out: Optional[torch.Tensor] = None, out_dtype=torch.float32,
-                           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                           workspace: Optional[torch.Tensor] = None, stream=None,
+                           tree_mask: Optional[torch.Tensor] = None) -> torch.Tensor:
     """pkv_paged_prefill_attn_fp8: chunks of query rows (q [sum Lq, Hq, D]
     bf16) over FP8 pools (uint8 E4M3 codes, values code * k_scale /
     v_scale) -> out [sum Lq, Hq, D]; single-row sequences take the FP8
-    decode path."""
+    decode path.  With tree_mask ([sum Lq] int64 on the GPU) the chunks are
+    token trees (pkv_paged_prefill_attn_tree_fp8; causal implied)."""
     lib = load_library()
     tq, hq, d = q.shape
     nb, bs, hkv, d2 = k_cache.shape
@@ -239,6 +246,18 @@ def paged_prefill_attn_fp8(q: torch.Tensor, cu_q_lens: torch.Tensor, k_cache: to
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if tree_mask is not None:
+        if tree_mask.shape != (tq,):
+            raise ValueError("tree_mask must hold one mask per query row")
+        _check(lib.pkv_paged_prefill_attn_tree_fp8(
+            _dev(out, "out"), _out_code(out.dtype), _dev(q, "q", torch.bfloat16),
+            _dev(cu_q_lens, "cu_q_lens", torch.int32), _dev(tree_mask, "tree_mask", torch.int64),
+            _dev(k_cache, "k_cache", torch.uint8), _dev(v_cache, "v_cache", torch.uint8),
+            float(k_scale), float(v_scale), _dev(block_table, "block_table", torch.int32),
+            block_table.shape[1], _dev(context_lens, "context_lens", torch.int32),
+            max_context_len, max_q_len, tq, nseq, hq, hkv, d, bs, float(scale), ws_ptr, ws_len,
+            _stream(stream)))
+        return out
     _check(lib.pkv_paged_prefill_attn_fp8(
         _dev(out, "out"), _out_code(out.dtype), _dev(q, "q", torch.bfloat16),
         _dev(cu_q_lens, "cu_q_lens", torch.int32), _dev(k_cache, "k_cache", torch.uint8),

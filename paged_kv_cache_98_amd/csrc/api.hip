@@ -403,4 +403,22 @@ int pkv_paged_prefill_attn_tree(void* out, int out_dtype, const void* q,
                         scale, 1, tree_mask, workspace, workspace_bytes, stream);
 }
 
+int pkv_paged_prefill_attn_tree_fp8(void* out, int out_dtype, const void* q,
+                                    const int32_t* cu_q_lens, const uint64_t* tree_mask,
+                                    const void* k_cache, const void* v_cache, float k_scale,
+                                    float v_scale, const int32_t* block_table,
+                                    int max_blocks_per_seq, const int32_t* context_lens,
+                                    int max_context_len, int max_q_len, int num_q_tokens,
+                                    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                    int block_size, float scale, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    if (max_q_len > kMaxTreeNodes) return PKV_ERR_UNSUPPORTED;
+    if (num_seqs > 0 && num_q_tokens > 0 && !tree_mask) return PKV_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(tree_mask) & 7) return PKV_ERR_ALIGN;
+    return prefill_call(out, out_dtype, q, cu_q_lens, k_cache, v_cache, true, k_scale, v_scale,
+                        block_table, max_blocks_per_seq, context_lens, max_context_len, max_q_len,
+                        num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                        scale, 1, tree_mask, workspace, workspace_bytes, stream);
+}
+
 }  // extern "C"

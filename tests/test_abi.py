@@ -254,6 +254,17 @@ def test_prefill_fp8_validation(lib):
     assert f(*args(nq=0, q=None)) == E.PKV_OK
 
 
+def test_prefill_tree_fp8_validation(lib):
+    E = binding
+    f = lib.pkv_paged_prefill_attn_tree_fp8
+    args = lambda tm=P, ks=1.0, maxq=50: (P, 0, P, P, tm, P, P, ks, 1.0, P, 8, P, 100, maxq, 60, 4,
+                                          8, 2, 128, 16, 0.1, None, 0, None)
+    assert f(*args(tm=None)) == E.PKV_ERR_NULL
+    assert f(*args(tm=ctypes.c_void_p(0x10004))) == E.PKV_ERR_ALIGN
+    assert f(*args(maxq=65)) == E.PKV_ERR_UNSUPPORTED
+    assert f(*args(ks=0.0)) == E.PKV_ERR_VALUE
+
+
 def test_binding_error_classes():
     """Argument errors raise ValueError (InvalidArgument); pool exhaustion
     MemoryError; unknown sequences KeyError; launch failures stay

@@ -113,3 +113,28 @@ def test_tree_full_batch_sampled():
             np.array([0, rows.stop - rows.start], np.int32),
             masks[rows].numpy().view(np.uint64), w.scale)
         parity(out[rows], ref, what=f"tree full batch seq {i} (ctx {ctx[i]})")
+
+
+def test_tree_over_fp8_pools():
+    """Token trees over FP8 (E4M3) pools: the reference is the tree oracle
+    on the codes' values, which are bf16 values (a power-of-two scale folds
+    in exactly), codes made by torch's float8 cast."""
+    from oracle import fp8
+    w = W.make_workload("tree_fp8_g4", [c for c, _ in TREES], [q for _, q in TREES],
+                        num_q_heads=8, num_kv_heads=2, block_size=16, seed=5300)
+    print(f"[tree fp8] {w.name}", flush=True)
+    bc = W.materialize(w, logical=True, poison=True)
+    kc, vc = W.fp8_pools(bc)
+    masks = W.tree_masks(w)
+    kv = [torch.from_numpy((fp8.e4m3_value(c.numpy()) * W.FP8_SCALE).astype(np.float32))
+          .to(torch.bfloat16) for c in (kc, vc)]
+    ref = tree.paged_attention_tree(bits16(bc.q), bits16(kv[0]), bits16(kv[1]),
+                                    bc.block_table.numpy(), bc.context_lens.numpy(),
+                                    bc.cu_q_lens.numpy(), masks.numpy().view(np.uint64), w.scale)
+    b = bc.to(DEV)
+    out = pkv.paged_prefill_attn_fp8(b.q, b.cu_q_lens, kc.to(DEV), vc.to(DEV), W.FP8_SCALE,
+                                     W.FP8_SCALE, b.block_table, b.context_lens, w.scale,
+                                     max_context_len=w.max_context_len, max_q_len=w.max_q_len,
+                                     tree_mask=masks.to(DEV))
+    torch.cuda.synchronize()
+    parity(out, ref, what=w.name)
