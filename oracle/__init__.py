@@ -14,8 +14,8 @@ Contents
   * ``blocks``: the pages' block pool (allocate / free / fork / append with
     copy-on-write, reference counts) and the whole-block copy of
     copy-on-write.
-  * ``fp8``: the E4M3 format, the quantised append and the fp64 decode over
-    an FP8 cache with per-cache scales.
+  * ``fp8``: the E4M3 format, the quantised append and the fp64 decode and
+    chunked prefill over an FP8 cache with per-cache scales.
   * ``tree``: fp64 attention of token-tree verification chunks (each node
     sees the context and its own path).
 
