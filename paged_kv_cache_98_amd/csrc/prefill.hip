@@ -575,7 +575,8 @@ __device__ __forceinline__ void chunk_item(
 
 
 // Grid: (num_q_tokens / P + num_seqs, num_kv_heads), P = 128 / G query
-// positions per workgroup; block 256.  Slot y of sequence i is y - T(i),
+// positions per workgroup, remapped XCD by XCD; block 256.  Slot y of
+// sequence i is y - T(i),
 // T(i) = cu_q_lens[i] / P + i; T never skips a needed slot.  Each
 // workgroup runs all key tiles of its (slot, KV head) item.
 template <int BS, int G, bool OUT_BF16, bool FP8>
@@ -591,8 +592,16 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
     __shared__ __attribute__((aligned(16))) uint16_t s_ks[2][kKsElems];
     __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kVtElems];
     const int lane = threadIdx.x & 63;
-    const int kvh = blockIdx.y;
-    const int slot = blockIdx.x;
+    // The dispatcher deals workgroups to the 8 XCDs in turn, each with its
+    // own L2: give each XCD a contiguous run of (KV head, slot) items, so the
+    // query slots that read the same keys share one L2 (a bijection of the
+    // grid onto itself).
+    const int nwg = gridDim.x * gridDim.y;
+    const int lin = blockIdx.y * gridDim.x + blockIdx.x;
+    const int per = nwg / 8, rem = nwg % 8, xcd = lin % 8;
+    const int item = xcd * per + (xcd < rem ? xcd : rem) + lin / 8;
+    const int kvh = item / gridDim.x;
+    const int slot = item - kvh * gridDim.x;
 
     // ---- which sequence owns this slot: 64-way search over T(i)
     int lo = 0, hi = num_seqs;  // T(lo) <= slot < T(hi), T(num_seqs) = grid size
