@@ -767,26 +767,34 @@ prefill_streamk_kernel(void* __restrict__ out, float* __restrict__ rec,
 // M = max_k m_k, L = sum_k l_k 2^(m_k - M), out = sum_k O_k 2^(m_k - M) / L
 // (the sequence-axis parallelism of "Flash Attention v2 的改进"); rows of a
 // sequence with no key get zeros.
-// Grid: (num_seqs, ceil(max_q_len * num_q_heads / 4)); block: 4 waves, one
-// (row, query head) each; lane k holds piece k's m and l, and dims 2 lane,
-// 2 lane + 1 of the output.
-template <int G, bool OUT_BF16>
+// Grid: (num_seqs, ceil(max_q_len * num_q_heads / CG / 4)); block: 4 waves,
+// one (row, CG consecutive query heads of one KV head) each: their columns
+// share one set of pieces, so a wave issues the (m, l) and the first A O rows
+// of all CG columns before it waits for any.  Lane k holds piece k's m and l,
+// and dims 2 lane, 2 lane + 1 of the output.
+template <int G, int CG, bool OUT_BF16>
 __global__ void __launch_bounds__(256)
 prefill_streamk_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
                              const int32_t* __restrict__ cum, const int32_t* __restrict__ cu_q_lens,
                              int num_seqs, int num_q_heads, int num_kv_heads, int num_workers,
                              int rec_cols, int decode_rows_elsewhere, float out_scale) {
+    static_assert(G % CG == 0, "a wave's columns belong to one KV head");
+    constexpr int A = CG == 1 ? 8 : 4;  // O rows loaded together per column
     const int lane = threadIdx.x & 63;
     const int seq = blockIdx.x;
     const int item = blockIdx.y * 4 + (threadIdx.x >> 6);
     const int q_begin = cu_q_lens[seq];
     const int lq = cu_q_lens[seq + 1] - q_begin;
-    const int r = item / num_q_heads;
-    const int head = item - r * num_q_heads;
+    const int per_row = num_q_heads / CG;
+    const int r = item / per_row;
+    const int h0 = (item - r * per_row) * CG;  // first query head of the wave
+    const int kvh = h0 / G;
     if (r >= lq) return;
     if (decode_rows_elsewhere && lq == 1) return;  // a decode row: not ours
-    const size_t e = ((size_t)(q_begin + r) * num_q_heads + head) * D + 2 * lane;
-    auto store2 = [&](float x0, float x1) {
+    // element (head h0 + c, dims 2 lane, 2 lane + 1) of the row
+    const size_t e0 = ((size_t)(q_begin + r) * num_q_heads + h0) * D + 2 * lane;
+    auto store2 = [&](int c, float x0, float x1) {
+        const size_t e = e0 + (size_t)c * D;
         if (OUT_BF16) {
             const uint32_t v = (uint32_t)f32_to_bf16_rne(x0) | ((uint32_t)f32_to_bf16_rne(x1) << 16);
             *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + e) = v;
@@ -796,59 +804,80 @@ prefill_streamk_merge_kernel(void* __restrict__ out, const float* __restrict__ r
     };
     const int64_t units = cum[seq + 1] - cum[seq];
     if (units == 0) {  // no key to attend to
-        store2(0.0f, 0.0f);
+#pragma unroll
+        for (int c = 0; c < CG; ++c) store2(c, 0.0f, 0.0f);
         return;
     }
     const int64_t n = units / num_kv_heads;
-    const int64_t start = cum[seq] + (int64_t)(head / G) * n;
+    const int64_t start = cum[seq] + (int64_t)kvh * n;
     const int64_t U = cum[num_seqs];
     const int64_t W = num_workers < U ? num_workers : U;
     const int64_t wf = worker_of(start, U, W);
     const int64_t wl = worker_of(start + n - 1, U, W);
     if (wf == wl) return;  // finished in place by its only worker
-    const int col = r * G + head % G;
-    auto rec_of = [&](int64_t w) {
-        const int slot = (w == wf && worker_start(w, U, W) < start) ? 1 : 0;
-        return rec + ((size_t)(w * 2 + slot) * rec_cols + col) * kRecStride;
+    const int slot_f = worker_start(wf, U, W) < start ? 1 : 0;
+    // record column of query head h0 + c: r G + (h0 + c) % G
+    auto rec_of = [&](int64_t w, int c) {
+        const int slot = w == wf ? slot_f : 0;
+        return rec + ((size_t)(w * 2 + slot) * rec_cols + r * G + h0 % G + c) * kRecStride;
     };
-    // maximum over the pieces' reference maxima, one piece per lane; the
-    // first 64 pieces' (m, l) stay in their lanes
-    float2 ml0 = make_float2(-INFINITY, 0.0f);
-    if (wf + lane <= wl) ml0 = *reinterpret_cast<const float2*>(rec_of(wf + lane) + D);
-    float mx = ml0.x;
-    for (int64_t w = wf + 64 + lane; w <= wl; w += 64) mx = fmaxf(mx, rec_of(w)[D]);
+    // (m, l) of the first 64 pieces, one per lane, and the first A pieces'
+    // O rows, for each column
+    float2 ml0[CG];
+    float2 av0[CG][A];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    // then the pieces in worker order, 64 at a time: lane k holds the scale
-    // exp2(m - mx) and the sum l of piece base + k; the O rows are loaded
-    // eight pieces ahead of their use
-    float L = 0.0f, a0 = 0.0f, a1 = 0.0f;
-    for (int64_t base = wf; base <= wl; base += 64) {
-        const int cnt = wl - base + 1 < 64 ? (int)(wl - base + 1) : 64;
-        float2 ml = ml0;
-        if (base != wf)
-            ml = lane < cnt ? *reinterpret_cast<const float2*>(rec_of(base + lane) + D)
-                            : make_float2(-INFINITY, 0.0f);
-        const float fk = lane < cnt ? fast_exp2(ml.x - mx) : 0.0f;
-        const float lk = ml.y;
-        for (int k = 0; k < cnt; k += 8) {
-            float2 av[8];
+    for (int c = 0; c < CG; ++c) {
+        ml0[c] = wf + lane <= wl ? *reinterpret_cast<const float2*>(rec_of(wf + lane, c) + D)
+                                 : make_float2(-INFINITY, 0.0f);
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                av[u] = k + u < cnt ? *reinterpret_cast<const float2*>(rec_of(base + k + u) + 2 * lane)
+        for (int u = 0; u < A; ++u)
+            av0[c][u] = wf + u <= wl
+                            ? *reinterpret_cast<const float2*>(rec_of(wf + u, c) + 2 * lane)
+                            : make_float2(0.0f, 0.0f);
+    }
+#pragma unroll
+    for (int c = 0; c < CG; ++c) {
+        float mx = ml0[c].x;
+        for (int64_t w = wf + 64 + lane; w <= wl; w += 64) mx = fmaxf(mx, rec_of(w, c)[D]);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        // the pieces in worker order, 64 at a time: lane k holds the
+        // scale exp2(m - mx) and the sum l of piece base + k; past the
+        // first A, the O rows are loaded A pieces at a time
+        float L = 0.0f, a0 = 0.0f, a1 = 0.0f;
+        for (int64_t base = wf; base <= wl; base += 64) {
+            const int cnt = wl - base + 1 < 64 ? (int)(wl - base + 1) : 64;
+            float2 ml = ml0[c];
+            if (base != wf)
+                ml = lane < cnt ? *reinterpret_cast<const float2*>(rec_of(base + lane, c) + D)
+                                : make_float2(-INFINITY, 0.0f);
+            const float fk = lane < cnt ? fast_exp2(ml.x - mx) : 0.0f;
+            const float lk = ml.y;
+            for (int k = 0; k < cnt; k += A) {
+                float2 av[A];
+                if (base == wf && k == 0) {
+#pragma unroll
+                    for (int u = 0; u < A; ++u) av[u] = av0[c][u];
+                } else {
+#pragma unroll
+                    for (int u = 0; u < A; ++u)
+                        av[u] = k + u < cnt
+                                    ? *reinterpret_cast<const float2*>(rec_of(base + k + u, c) + 2 * lane)
                                     : make_float2(0.0f, 0.0f);
+                }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                if (k + u >= cnt) break;
-                const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fk), k + u));
-                L = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(lk), k + u)), f, L);
-                a0 = fmaf(av[u].x, f, a0);
-                a1 = fmaf(av[u].y, f, a1);
+                for (int u = 0; u < A; ++u) {
+                    if (k + u >= cnt) break;
+                    const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fk), k + u));
+                    L = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(lk), k + u)), f, L);
+                    a0 = fmaf(av[u].x, f, a0);
+                    a1 = fmaf(av[u].y, f, a1);
+                }
             }
         }
+        const float inv = out_scale / L;
+        store2(c, a0 * inv, a1 * inv);
     }
-    const float inv = out_scale / L;
-    store2(a0 * inv, a1 * inv);
 }
 
 template <int BS, int G, bool OUT_BF16, bool FP8>
@@ -874,11 +903,22 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
                            a.tree_mask);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        dim3 mgrid(a.num_seqs, (a.max_q_len * a.num_q_heads + 3) / 4);
-        hipLaunchKernelGGL((prefill_streamk_merge_kernel<G, OUT_BF16>), mgrid, dim3(256), 0,
-                           stream, a.out, a.records, a.cum, a.cu_q_lens, a.num_seqs,
-                           a.num_q_heads, a.num_kv_heads, (int)workers, a.max_q_len * G,
-                           a.decode_rows_elsewhere ? 1 : 0, a.out_scale);
+        // With about as many items (sequence, KV head) as workers, an item
+        // is cut into two pieces or so and a merge wave takes the query heads
+        // of one KV head together (4 columns' loads in flight: the 16-node
+        // tree batch 176.5 -> 171.0 us per call, the 6-row verify batch
+        // 130.8 -> 129.3); with many pieces per item one column per wave
+        // gives more waves to the longer folds (8 long sequences: 440.5
+        // against 448.1 us with 4 columns).
+        constexpr int CG = G < 4 ? G : 4;
+        const int64_t items = (int64_t)a.num_seqs * a.num_kv_heads;
+        const int cols = 2 * items >= workers ? CG : 1;
+        dim3 mgrid(a.num_seqs, (a.max_q_len * (a.num_q_heads / cols) + 3) / 4);
+        auto merge = cols == 1 ? prefill_streamk_merge_kernel<G, 1, OUT_BF16>
+                               : prefill_streamk_merge_kernel<G, CG, OUT_BF16>;
+        hipLaunchKernelGGL(merge, mgrid, dim3(256), 0, stream, a.out, a.records, a.cum,
+                           a.cu_q_lens, a.num_seqs, a.num_q_heads, a.num_kv_heads, (int)workers,
+                           a.max_q_len * G, a.decode_rows_elsewhere ? 1 : 0, a.out_scale);
         return hipGetLastError();
     }
     const int slots = a.num_q_tokens / P + a.num_seqs;
