@@ -587,11 +587,12 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
                     int max_blocks_per_seq, const int32_t* __restrict__ context_lens,
                     int max_context_len, int num_seqs, int num_q_heads, int num_kv_heads,
                     float scale_log2, float out_scale, int causal, int decode_rows_elsewhere,
-                    const uint64_t* __restrict__ tree_mask) {
+                    const uint64_t* __restrict__ tree_mask, int pair_cus) {
     constexpr int P = kCols / G;
     __shared__ __attribute__((aligned(16))) uint16_t s_ks[2][kKsElems];
     __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kVtElems];
-    const int lane = threadIdx.x & 63;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
     // The dispatcher deals workgroups to the 8 XCDs in turn, each with its
     // own L2: give each XCD a contiguous run of (KV head, slot) items, so the
     // query slots that read the same keys share one L2 (a bijection of the
@@ -599,7 +600,65 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
     const int nwg = gridDim.x * gridDim.y;
     const int lin = blockIdx.y * gridDim.x + blockIdx.x;
     const int per = nwg / 8, rem = nwg % 8, xcd = lin % 8;
-    const int item = xcd * per + (xcd < rem ? xcd : rem) + lin / 8;
+    const int run0 = xcd * per + (xcd < rem ? xcd : rem);
+    int item = run0 + lin / 8;
+    if (pair_cus > 0) {
+        // Within an XCD the dispatcher hands workgroups to its pair_cus CUs
+        // in turn, two per CU, so run positions p and p + pair_cus share a
+        // CU, and the one left alone when its partner ends runs faster.
+        // Causal slots differ in key tiles (up to 1.3x the mean for 512-row
+        // chunks), so the run is taken in order of work: positions
+        // 0 .. pair_cus - 1 get the heaviest items and the next pair_cus
+        // positions the lighter half of the first 2 pair_cus in reverse, so
+        // each CU holds a heavy and a light item; the rest follow in order.
+        // A permutation of the run (ties by position), so still a bijection.
+        const int cnt = per + (xcd < rem ? 1 : 0);
+        int* s_cu = reinterpret_cast<int*>(&s_ks[0][0]);  // cu_q_lens, context_lens, works
+        int* s_ctx = s_cu + num_seqs + 1;
+        int* s_w = s_ctx + num_seqs;
+        int* s_pick = s_w + cnt;
+        for (int i = tid; i <= num_seqs; i += kThreads) {
+            s_cu[i] = cu_q_lens[i];
+            if (i < num_seqs) s_ctx[i] = context_lens[i];
+        }
+        __syncthreads();
+        for (int t = tid; t < cnt; t += kThreads) {
+            const int sl = (run0 + t) % (int)gridDim.x;
+            int lo = 0, hi = num_seqs;  // the last i with T(i) = cu_q_lens[i] / P + i <= sl
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (s_cu[mid] / P + mid <= sl) lo = mid; else hi = mid;
+            }
+            const int lq = s_cu[lo + 1] - s_cu[lo];
+            const int r0 = (sl - (s_cu[lo] / P + lo)) * P;
+            int work = 0;
+            if (r0 < lq && !(decode_rows_elsewhere && lq == 1)) {
+                int ctx = s_ctx[lo];
+                ctx = ctx < 0 ? 0 : (ctx > max_context_len ? max_context_len : ctx);
+                const int r_last = (r0 + P < lq ? r0 + P : lq) - 1;
+                const int kv_end = causal ? (ctx - lq + r_last + 1 < ctx ? ctx - lq + r_last + 1 : ctx)
+                                          : ctx;
+                work = (kv_end + kKT - 1) / kKT;
+            }
+            s_w[t] = work;
+        }
+        __syncthreads();
+        const int p = lin / 8;
+        const int m = cnt < 2 * pair_cus ? cnt : 2 * pair_cus;
+        const int want = p < pair_cus ? p : (p < m ? m + pair_cus - 1 - p : p);
+        for (int t = tid; t < cnt; t += kThreads) {
+            const int wt = s_w[t];
+            int rank = 0;
+            for (int u = 0; u < cnt; ++u) {
+                const int wu = s_w[u];
+                rank += (wu > wt || (wu == wt && u < t)) ? 1 : 0;
+            }
+            if (rank == want) *s_pick = t;
+        }
+        __syncthreads();
+        item = run0 + *s_pick;
+        __syncthreads();  // the LDS goes back to the K tiles
+    }
     const int kvh = item / gridDim.x;
     const int slot = item - kvh * gridDim.x;
 
@@ -922,11 +981,30 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
         return hipGetLastError();
     }
     const int slots = a.num_q_tokens / P + a.num_seqs;
-    hipLaunchKernelGGL((prefill_mfma_kernel<BS, G, OUT_BF16, FP8>), dim3(slots, a.num_kv_heads),
+    // Pair heavy and light slots on each CU when the whole grid is at most
+    // about two rounds of the chip (the order is ranked in each workgroup,
+    // in LDS the K tiles take later).
+    auto kern = prefill_mfma_kernel<BS, G, OUT_BF16, FP8>;
+    int pair_cus = 0;
+    {
+        int resident = 0, cus = 0, dev = 0;
+        hipError_t e = resident_workgroups(reinterpret_cast<const void*>(kern), kThreads, 0,
+                                           &resident);
+        if (e == hipSuccess) e = hipGetDevice(&dev);
+        if (e == hipSuccess)
+            e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        const int64_t per = ((int64_t)slots * a.num_kv_heads + 7) / 8;
+        const int h = cus / 8;
+        if (cus % 8 == 0 && resident == 2 * cus && per <= 4 * h && a.num_seqs <= 4096 &&
+            2 * (int64_t)a.num_seqs + 2 + per <= (int64_t)(kKsElems * 2 * sizeof(uint16_t) / sizeof(int)))
+            pair_cus = h;
+    }
+    hipLaunchKernelGGL(kern, dim3(slots, a.num_kv_heads),
                        dim3(kThreads), 0, stream, a.out, a.q, a.cu_q_lens, a.k_cache, a.v_cache,
                        a.block_table, a.max_blocks_per_seq, a.context_lens, a.max_context_len,
                        a.num_seqs, a.num_q_heads, a.num_kv_heads, a.scale_log2, a.out_scale,
-                       a.causal ? 1 : 0, a.decode_rows_elsewhere ? 1 : 0, a.tree_mask);
+                       a.causal ? 1 : 0, a.decode_rows_elsewhere ? 1 : 0, a.tree_mask, pair_cus);
     return hipGetLastError();
 }
 
