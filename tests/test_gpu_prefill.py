@@ -114,3 +114,26 @@ def test_prefill_full_size_mixed_sampled():
     bt_rows = bt_sub[[where[s] for s, _ in picks]]
     ref = oracle.paged_attention(b.q.cpu()[rows], k_sub, v_sub, bt_rows, ctx_rows, w.scale)
     parity(out[rows], ref, what=f"mixed full size, {len(rows)} sampled rows")
+
+
+@pytest.mark.parametrize("num_seqs,group,hkv", [(280, 4, 2), (130, 8, 1)])
+def test_prefill_many_ragged_chunks(num_seqs, group, hkv):
+    """Hundreds of ragged chunks (0 to 48 rows, decode rows among them) in
+    one grid call small enough that its workgroups take their items in the
+    heavy/light pairing order, which ranks every XCD run's items over the
+    call's sequences (more of them than a workgroup has threads)."""
+    rng = np.random.default_rng(3200 + num_seqs)
+    ql = [int(x) for x in rng.integers(0, 49, num_seqs)]
+    ql[7] = 48  # max_q_len * G > 128: the grid kernel, not stream-K
+    ql[11], ql[12] = 1, 0
+    ctx = [q + int(p) for q, p in zip(ql, rng.integers(0, 300, num_seqs))]
+    w = W.make_workload(f"many_chunks_{num_seqs}_g{group}", ctx, ql, num_q_heads=hkv * group,
+                        num_kv_heads=hkv, block_size=16, seed=3300 + num_seqs)
+    P = 128 // group
+    per_xcd = -(-(sum(ql) // P + num_seqs) * hkv // 8)
+    assert per_xcd <= 4 * 32, "the case is meant to take the pairing order"
+    print(f"[many chunks] {w.name} rows {sum(ql)} items per XCD {per_xcd}", flush=True)
+    bc = W.materialize(w, logical=True, poison=True)
+    out = run_prefill(bc.to(DEV))
+    torch.cuda.synchronize()
+    parity(out, oracle_prefill(bc), what=w.name)
