@@ -164,6 +164,10 @@ def record_traffic(workload, fetch_dir, write_dir):
     print(json.dumps(rec["workloads"].get(workload, rec["calibration"]), indent=1))
 
 
+# the kernels one paged_decode_attn call launches
+DECODE_KERNEL = "paged_decode_attn (stream-K decode + merge kernels)"
+
+
 def decode_kv_bytes(w):
     return sum(c for c, lq in zip(w.context_lens, w.q_lens) if lq == 1) * w.kv_token_bytes()
 
@@ -336,6 +340,59 @@ def cpu_baseline(batch, w, min_seconds=10.0):
             "sample": f"whole {w.name} batch ({w.num_seqs} seqs, sum ctx {sum(w.context_lens)}), "
                       f"fp64 C + OpenMP, {reps} repetitions in {total:.1f} s: {t:.3f} s per "
                       f"batch on average ({w.num_seqs / t:.2f} seq-steps/s)"}
+
+
+def cpu_baseline_1t(batch, w, seqs=8, min_seconds=5.0):
+    """The same fp64 oracle on ONE host thread, on the first `seqs` sequences
+    of the batch (host copies of their blocks), repeated for at least
+    min_seconds; the rate is the mean over the repetitions."""
+    import oracle
+    bt = batch.block_table.cpu()[:seqs]
+    cl = batch.context_lens.cpu()[:seqs]
+    q = batch.q.cpu()[:seqs]
+    kc, vc = batch.k_cache.cpu(), batch.v_cache.cpu()
+    reps, total = 0, 0.0
+    while reps < 2 or total < min_seconds:
+        t0 = time.perf_counter()
+        oracle.paged_attention(q, kc, vc, bt, cl, w.scale, num_threads=1)
+        total += time.perf_counter() - t0
+        reps += 1
+    t = total / reps
+    kv_bytes = int(cl.sum()) * w.kv_token_bytes()
+    return {"value": round(kv_bytes / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {seqs} sequences of the {w.name} batch (sum ctx {int(cl.sum())}), "
+                      f"fp64 C, one thread, {reps} repetitions in {total:.1f} s: {t:.3f} s each "
+                      f"on average ({seqs / t:.2f} seq-steps/s)"}
+
+
+def hbm_ceiling(dev):
+    """Streaming rates of plain torch kernels on this GPU, the practical
+    ceiling next to the 8 TB/s spec: a 1 GiB device copy (bytes read +
+    written per second) and a sum over 2 GiB of fp32 (bytes read per
+    second); median of 10 event-timed runs each."""
+    import torch
+    src = torch.ones(1 << 29, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    big = torch.ones(1 << 29, dtype=torch.float32, device=dev)
+    res = {}
+    for name, fn, nbytes in (("copy_read_write", lambda: dst.copy_(src), 2 * src.numel() * 2),
+                             ("sum_read", lambda: big.sum(), big.numel() * 4)):
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        res[name] = round(nbytes / statistics.median(ts) / 1e9, 1)
+    del src, dst, big
+    torch.cuda.empty_cache()
+    return {"unit": "GB/s", **res,
+            "what": "torch device copy of 1 GiB (read + written) and torch sum over 2 GiB fp32 "
+                    "(read), median of 10 event-timed runs"}
 
 
 def cpu_baseline_fp8(batch, w, seqs=8, min_seconds=10.0):
@@ -606,11 +663,18 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": hbm_traffic(wname),
-                     "kernel": "paged_decode_attn (stream-K decode + merge kernels)",
-                     "algorithmic_bytes_per_launch": kv_bytes},
+                     "kernel": DECODE_KERNEL,
+                     "algorithmic_bytes_per_launch": kv_bytes,
+                     "timing": "mean HIP-event duration of the decode call over K calls of a "
+                               "second pass, events on the library's stream around each call"},
+        "value_timing": "wall clock over K un-evented steps (kv_append + paged_decode_attn), "
+                        "bracketed by device synchronisation",
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline_fp8(b, w) if kv_fp8 else cpu_baseline(b, w)
+        if not kv_fp8:
+            rec["cpu_baseline_1t"] = cpu_baseline_1t(b, w)
+        rec["hbm_ceiling"] = hbm_ceiling(dev)
     print(json.dumps(rec), flush=True)
 
 

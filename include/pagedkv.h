@@ -46,9 +46,10 @@
  *  - Errors are detected on the host BEFORE anything is enqueued (so they
  *    can be tested without a GPU): the call returns a negative status and
  *    nothing is launched.  PKV_ERR_LAUNCH reports a HIP error after launch.
- *    Values inside device arrays are not validated: a block id outside the
- *    pool, a slot outside the pool or a context length above
- *    max_blocks_per_seq * block_size is undefined behaviour.  A context
+ *    Values inside device arrays are not validated, apart from the slots of
+ *    the append calls and the block ids of pkv_copy_blocks (skipped when
+ *    outside the pool): a block-table entry outside the pool or a context
+ *    length above max_blocks_per_seq * block_size is undefined behaviour.  A context
  *    length above `max_context_len` is clamped to it on the device.
  *  - Determinism: results are bitwise reproducible run to run for the same
  *    inputs and arguments (no floating-point atomics).
@@ -95,12 +96,14 @@ int pkv_version(void);
  *
  *   k_new, v_new   [num_tokens][num_kv_heads][head_dim] bf16 (read)
  *   slot_mapping   [num_tokens] int64 (read): token t goes to physical block
- *                  slot / block_size, row slot % block_size; slot < 0 skips t.
- *                  Two tokens with the same slot in one call is a caller
- *                  error (which one lands is unspecified).
+ *                  slot / block_size, row slot % block_size; slot < 0 skips t,
+ *                  and so does slot >= num_blocks * block_size (a stale
+ *                  mapping cannot write outside the pools).  Two tokens with
+ *                  the same slot in one call is a caller error (which one
+ *                  lands is unspecified).
  *   k_cache, v_cache  pools (written only at the given slots)
- *   num_blocks     pool size in blocks (for the caller's bookkeeping; slots
- *                  are not range-checked on the device)
+ *   num_blocks     pool size in blocks: slots are checked against it on the
+ *                  device
  * The copy is bit-exact.  num_tokens == 0 is a no-op.
  */
 int pkv_kv_append(const void *k_new, const void *v_new, const int64_t *slot_mapping,
@@ -122,6 +125,15 @@ size_t pkv_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_head
 
 /*
  * paged_decode_attn -- one query row per sequence against its cached keys.
+ * ("LLM 推理优化技术全景", "Flash Attention 深度剖析 > 在线 Softmax": the keys
+ * are visited once, block by block, keeping a running maximum m and running
+ * sum l and rescaling the partial output by exp(m_old - m_new) when m grows;
+ * "Flash Attention v2 的改进": the division by l is deferred to the end and the
+ * work is also split along the sequence axis, here into pieces whose partial
+ * results are merged by the same rescale; "Prefill vs Decode": decode reads
+ * the whole cached K/V for one query row, so it is bound by HBM bandwidth;
+ * the gather through the block table is that of "LLM 推理引擎深度解析：vLLM、
+ * SGLang 与 TensorRT-LLM 的核心优化原理", section 2.1 "PagedAttention".)
  *
  *   out            [num_seqs][num_q_heads][head_dim], fp32 or bf16 (written)
  *   q              [num_seqs][num_q_heads][head_dim] bf16

@@ -106,6 +106,7 @@ int pkv_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapp
     a.k_cache = static_cast<uint16_t*>(k_cache);
     a.v_cache = static_cast<uint16_t*>(v_cache);
     a.row_elems = num_kv_heads * head_dim;
+    a.num_slots = num_blocks * block_size;
     return to_status(pkv::launch_kv_append(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -234,6 +235,7 @@ int pkv_kv_append_fp8(const void* k_new, const void* v_new, const int64_t* slot_
     a.k_cache = static_cast<uint8_t*>(k_cache);
     a.v_cache = static_cast<uint8_t*>(v_cache);
     a.row_elems = num_kv_heads * head_dim;
+    a.num_slots = num_blocks * block_size;
     a.k_scale = k_scale;
     a.v_scale = v_scale;
     return to_status(pkv::launch_kv_append_fp8(a, static_cast<hipStream_t>(stream)));

@@ -7,7 +7,9 @@
 // + row starts at element s * Hkv * D, so the copy needs only the slot.
 // Each thread moves one 16-byte word of K and the same word of V; a token row
 // of Hkv * D bf16 is Hkv * D / 8 words, so consecutive threads write
-// consecutive words of one row (coalesced).  Negative slots are skipped.
+// consecutive words of one row (coalesced).  Negative slots are skipped, and
+// so is a slot past the pool's last row, so a stale slot mapping cannot write
+// outside the pools.
 //
 // The FP8 variant ("让 Agent 跑得快", section 四: one byte per value, half
 // the bytes of bf16; "LLM推理工程实战", section 5.3: the KV cache stored
@@ -32,13 +34,14 @@ namespace {
 __global__ void __launch_bounds__(256)
 kv_append_kernel(const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
                  const int64_t* __restrict__ slot_mapping, int64_t num_words,
-                 uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, int words_per_row) {
+                 uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, int words_per_row,
+                 int64_t num_slots) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < num_words; w += stride) {
         const int64_t t = w / words_per_row;
         const int64_t c = w - t * words_per_row;
         const int64_t s = slot_mapping[t];
-        if (s < 0) continue;
+        if (s < 0 || s >= num_slots) continue;
         const int64_t dst = s * words_per_row + c;
         k_cache[dst] = k_new[w];
         v_cache[dst] = v_new[w];
@@ -65,13 +68,13 @@ __global__ void __launch_bounds__(256)
 kv_append_fp8_kernel(const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
                      const int64_t* __restrict__ slot_mapping, int64_t num_words,
                      uint2* __restrict__ k_cache, uint2* __restrict__ v_cache, int words_per_row,
-                     float k_scale, float v_scale) {
+                     float k_scale, float v_scale, int64_t num_slots) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < num_words; w += stride) {
         const int64_t t = w / words_per_row;
         const int64_t c = w - t * words_per_row;
         const int64_t s = slot_mapping[t];
-        if (s < 0) continue;
+        if (s < 0 || s >= num_slots) continue;
         const int64_t dst = s * words_per_row + c;
         k_cache[dst] = quantise8(k_new[w], k_scale);
         v_cache[dst] = quantise8(v_new[w], v_scale);
@@ -147,7 +150,8 @@ hipError_t launch_kv_append_fp8(const AppendFp8Args& a, hipStream_t stream) {
     hipLaunchKernelGGL(kv_append_fp8_kernel, dim3(blocks), dim3(256), 0, stream,
                        reinterpret_cast<const uint4*>(a.k_new), reinterpret_cast<const uint4*>(a.v_new),
                        a.slot_mapping, num_words, reinterpret_cast<uint2*>(a.k_cache),
-                       reinterpret_cast<uint2*>(a.v_cache), words_per_row, a.k_scale, a.v_scale);
+                       reinterpret_cast<uint2*>(a.v_cache), words_per_row, a.k_scale, a.v_scale,
+                       a.num_slots);
     return hipGetLastError();
 }
 
@@ -160,7 +164,7 @@ hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(kv_append_kernel, dim3(blocks), dim3(256), 0, stream,
                        reinterpret_cast<const uint4*>(a.k_new), reinterpret_cast<const uint4*>(a.v_new),
                        a.slot_mapping, num_words, reinterpret_cast<uint4*>(a.k_cache),
-                       reinterpret_cast<uint4*>(a.v_cache), words_per_row);
+                       reinterpret_cast<uint4*>(a.v_cache), words_per_row, a.num_slots);
     return hipGetLastError();
 }
 

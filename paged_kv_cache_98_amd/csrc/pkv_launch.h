@@ -17,6 +17,7 @@ struct AppendArgs {
     uint16_t* k_cache;
     uint16_t* v_cache;
     int row_elems;  // num_kv_heads * head_dim
+    int64_t num_slots;  // num_blocks * block_size: slots at or past it are skipped
 };
 
 struct AppendFp8Args {
@@ -27,6 +28,7 @@ struct AppendFp8Args {
     uint8_t* k_cache;  // E4M3 codes
     uint8_t* v_cache;
     int row_elems;  // num_kv_heads * head_dim
+    int64_t num_slots;  // num_blocks * block_size: slots at or past it are skipped
     float k_scale;
     float v_scale;
 };

@@ -22,22 +22,49 @@ def parity(gpu: torch.Tensor, ref: np.ndarray, max_abs=MAX_ABS, rel_l2=REL_L2, w
     return err.max(), rel
 
 
-def bf16_parity(gpu_bf16: torch.Tensor, gpu_f32: torch.Tensor, ref: np.ndarray, what=""):
-    """bf16 output: bit-identical to the same kernel's fp32 output rounded to
-    nearest even, and within the fp64 oracle's tolerance widened by one bf16
-    rounding (2^-9 relative; rel-L2 of rounding alone is ~1.6e-3)."""
+def _bf16_rne(x):
+    """fp64 values rounded to nearest even bf16 (through fp32, which is exact
+    to within far less than a bf16 ulp here), returned as fp64."""
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).double().numpy()
+
+
+def _bf16_ulp(x):
+    """Spacing of bf16 values at |x| (8 significant bits; bf16's normal range
+    starts at 2^-126)."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
+    return np.exp2(e - 7)
+
+
+def bf16_parity(gpu_bf16: torch.Tensor, gpu_f32: torch.Tensor, ref: np.ndarray, what="",
+                fp32_err=2e-6, min_within=0.999):
+    """bf16 output, held to one bf16 ulp of the fp64 oracle rounded to nearest
+    even (the reading for a bf16 output): bit-identical to the same kernel's
+    fp32 output rounded to nearest even, and per element
+    |out - RNE(ref)| <= ulp(RNE(ref)) + fp32_err, where fp32_err bounds the
+    fp32 output's own error against the oracle (the rounding of an fp32 value
+    and of the exact one can then differ by one ulp, and by more only where
+    that error exceeds an ulp, i.e. for values of magnitude below about
+    2^8 fp32_err).  fp32_err is that kernel's fp32 error level: 2e-6 for the
+    fp32-FMA decode, 1e-3 where P rounds to fp16 (prefill, verify and the
+    FP8 paths).  A share min_within of the elements must be within one ulp
+    with no allowance at all: 99.9 % for the decode; for the fp16-P kernels,
+    whose fp32 error exceeds an ulp on the smallest outputs, the share is
+    given by the caller."""
     assert gpu_bf16.dtype == torch.bfloat16
     rounded = gpu_f32.to(torch.bfloat16)
     same = torch.equal(gpu_bf16.view(torch.int16), rounded.view(torch.int16))
     assert same, f"{what}: bf16 output differs from the rounded fp32 output"
     g = gpu_bf16.detach().to(torch.float64).cpu().numpy()
     assert np.all(np.isfinite(g))
-    # the fp32 bar plus one rounding to bf16 (half an ulp <= 2^-8 |x|)
-    excess = np.abs(g - ref) - 2.0 ** -8 * np.abs(ref)
-    rel = np.linalg.norm(g - ref) / np.linalg.norm(ref)
-    print(f"[bf16] {what}: max(|err| - 2^-8|ref|)={excess.max():.3e} rel_l2={rel:.3e}", flush=True)
-    assert excess.max() <= MAX_ABS, f"{what}: bf16 error beyond fp32 bar + one rounding"
-    assert rel <= REL_L2 + 2.0 ** -9, f"{what}: bf16 rel-L2 {rel:.3e}"
+    r16 = _bf16_rne(ref)
+    ulp = _bf16_ulp(r16)
+    err = np.abs(g - r16)
+    excess = err - ulp
+    within = float(np.mean(err <= ulp))
+    print(f"[bf16] {what}: max(|out - RNE(ref)| - ulp)={excess.max():.3e} "
+          f"within one ulp {100 * within:.4f} %", flush=True)
+    assert excess.max() <= fp32_err, f"{what}: bf16 output beyond one ulp of RNE(oracle)"
+    assert within >= min_within, f"{what}: only {100 * within:.3f} % within one ulp"
 
 
 def compact_subset(batch, seqs):

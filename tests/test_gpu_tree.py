@@ -89,7 +89,8 @@ def test_tree_key_split():
     assert torch.equal(o32, o32b)
     ref = oracle_tree(bc, masks)
     parity(o32, ref, what=w.name)
-    bf16_parity(o16, o32, ref, what=w.name + " bf16 out")
+    bf16_parity(o16, o32, ref, what=w.name + " bf16 out",
+                fp32_err=1e-3, min_within=0.95)
 
 
 def test_tree_full_batch_sampled():
