@@ -179,9 +179,9 @@ int decode_call(void* out, int out_dtype, const void* q, const void* k_cache, co
     a.block_size = block_size;
     a.scale_log2 = scale * 1.4426950408889634f;
     if (kv_fp8) a.scale_log2 *= k_scale;
-    a.cum = static_cast<int32_t*>(workspace);
+    a.seq_workers = static_cast<int32_t*>(workspace);
     a.records = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                         align_up((size_t)(num_seqs + 1) * sizeof(int32_t), 256));
+                                         align_up((size_t)2 * num_seqs * sizeof(int32_t), 256));
     a.max_workers = pkv::decode_max_workers(num_seqs, max_context_len);
     a.cu_q_lens = nullptr;
     return to_status(pkv::launch_decode(a, static_cast<hipStream_t>(stream)));
@@ -350,9 +350,9 @@ int prefill_call(void* out, int out_dtype, const void* q, const int32_t* cu_q_le
     d.scale_log2 = a.scale_log2;
     d.kv_fp8 = kv_fp8;
     d.out_scale = a.out_scale;
-    d.cum = static_cast<int32_t*>(workspace);
+    d.seq_workers = static_cast<int32_t*>(workspace);
     d.records = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                         align_up((size_t)(num_seqs + 1) * sizeof(int32_t), 256));
+                                         align_up((size_t)2 * num_seqs * sizeof(int32_t), 256));
     d.max_workers = pkv::decode_max_workers(num_seqs, max_context_len);
     d.cu_q_lens = cu_q_lens;
     return to_status(pkv::launch_decode(d, s));

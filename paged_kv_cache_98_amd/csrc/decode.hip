@@ -378,6 +378,11 @@ constexpr int kMinTilesPerWorker = 4;   // fewer waves for tiny batches
 template <int G>
 constexpr int max_waves_per_worker() { return G <= 4 ? 8 : 4; }
 constexpr int64_t kMaxWorkers = 1024;    // workgroups of 8 waves an MI355X holds at most
+// Cost of a sequence boundary inside a worker's range, in quarter tiles
+// (per query heads per KV head: the tile math grows with G, the boundary's
+// round trips do not).
+template <int G>
+constexpr int64_t seq_cost() { return G <= 4 ? 6 : 16; }
 
 __device__ __forceinline__ int clamp_ctx(int ctx, int max_context_len) {
     return ctx < 0 ? 0 : (ctx > max_context_len ? max_context_len : ctx);
@@ -445,7 +450,7 @@ __device__ __forceinline__ size_t tile_bytes(IdWindow& ids, int tile, size_t row
 // Records: [W][2][num_q_heads][kRecStride] floats.
 template <typename KV, int BS, int G, bool OUT_BF16>
 __global__ void __launch_bounds__(64 * max_waves_per_worker<G>())
-decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* __restrict__ cum_out,
+decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* __restrict__ seq_workers,
                       const uint16_t* __restrict__ q, const void* __restrict__ k_cache,
                       const void* __restrict__ v_cache, const int32_t* __restrict__ block_table,
                       int max_blocks_per_seq, const int32_t* __restrict__ context_lens,
@@ -491,8 +496,6 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
     }
     if (tid == 0) s_cum[num_seqs] = total;
     __syncthreads();
-    if (blockIdx.x == 0 && blockIdx.y == 0)
-        for (int i = tid; i <= num_seqs; i += nthr) cum_out[i] = s_cum[i];
 
     const int64_t U = s_cum[num_seqs];
     // never more workers than tiles, so every worker's range is non-empty
@@ -504,8 +507,29 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
     const int row = lane / L::kRowLanes;
     const int col = lane % L::kRowLanes;
     const int64_t w = blockIdx.x;
-    int64_t t = w < W ? worker_start(w, U, W) : 0;
-    const int64_t t_end = w < W ? worker_start(w + 1, U, W) : 0;
+    // Ranges of equal cost, not equal tiles: a tile costs 4 units and every
+    // sequence boundary kSeqCost more (a worker that starts a new sequence
+    // restarts its load pipeline and loads another query and block-id
+    // window), so workers that cross more boundaries get fewer tiles.
+    // Worker wi starts at the first tile t with cost(t) >= wi * total / W,
+    // cost(t) = 4 t + kSeqCost * seq(t); the sequence is found among the
+    // costs of the sequences' first tiles.
+    constexpr int64_t kSeqCost = seq_cost<G>();
+    const int64_t cost_total = 4 * U + kSeqCost * (int64_t)(num_seqs - 1);
+    auto range_start = [&](int64_t wi) -> int64_t {
+        if (wi >= W) return U;
+        const int64_t target = wi * cost_total / W;
+        int lo = 0, hi = num_seqs;  // largest i with 4 cum[i] + kSeqCost i <= target
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (4 * (int64_t)s_cum[mid] + kSeqCost * (int64_t)mid <= target) lo = mid; else hi = mid;
+        }
+        int64_t tt = (target - kSeqCost * (int64_t)lo + 3) / 4;
+        tt = tt < s_cum[lo] ? s_cum[lo] : tt;
+        return tt > s_cum[lo + 1] ? s_cum[lo + 1] : tt;
+    };
+    int64_t t = w < W ? range_start(w) : 0;
+    const int64_t t_end = w < W ? range_start(w + 1) : 0;
 
     const uint32_t neg = scale_log2 < 0.0f ? 0x80008000u : 0u;
     const float c = fabsf(scale_log2);
@@ -633,6 +657,12 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
 
         const bool whole = (t == seg_t0) && (piece_end == seg_t1);
         const int slot = first_piece ? 0 : 1;
+        // which workers hold a sequence's first and last tiles (and the
+        // record slot of the first), for the merge kernel
+        if (tid == 0 && blockIdx.y == 0) {
+            if (t == seg_t0) seq_workers[seq] = (int32_t)w | (slot << 30);
+            if (piece_end == seg_t1) seq_workers[num_seqs + seq] = (int32_t)w;
+        }
         // Row r stores heads g = r, r + kRows, ...
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -671,8 +701,8 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
 template <bool OUT_BF16>
 __global__ void __launch_bounds__(256)
 decode_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
-                    const int32_t* __restrict__ cum, const int32_t* __restrict__ context_lens,
-                    int max_context_len, int num_seqs, int num_q_heads, int num_workers,
+                    const int32_t* __restrict__ seq_workers, const int32_t* __restrict__ context_lens,
+                    int max_context_len, int num_seqs, int num_q_heads,
                     float out_scale, const int32_t* __restrict__ cu_q_lens) {
     constexpr int D = kHeadDim;
     const int lane = threadIdx.x & 63;
@@ -687,15 +717,15 @@ decode_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
         store1<OUT_BF16>(out, e + 1, 0.0f);
         return;
     }
-    const int64_t U = cum[num_seqs];  // > 0: this sequence has tiles
-    const int64_t W = num_workers < U ? num_workers : U;
-    const int64_t t0 = cum[seq];
-    const int64_t wf = worker_of(t0, U, W);
-    const int64_t wl = worker_of(cum[seq + 1] - 1, U, W);
+    // the workers holding the sequence's first and last tiles (it has tiles)
+    const int32_t first = seq_workers[seq];
+    const int64_t wf = first & 0x3fffffff;
+    const int64_t wl = seq_workers[num_seqs + seq];
     if (wf == wl) return;  // finalised by its only worker
+    const int slot_f = (first >> 30) & 1;
 
     auto rec_of = [&](int64_t w) {
-        const int slot = (w == wf && worker_start(w, U, W) < t0) ? 1 : 0;
+        const int slot = w == wf ? slot_f : 0;
         return rec + ((size_t)(w * 2 + slot) * num_q_heads + h) * kRecStride;
     };
     // maximum over the pieces' running maxima, one piece per lane; the
@@ -759,7 +789,7 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     if (workers > a.max_workers) workers = a.max_workers;
     if (workers < 1) workers = 1;
     hipLaunchKernelGGL((decode_streamk_kernel<KV, BS, G, OUT_BF16>), dim3((int)workers, groups),
-                       dim3(threads), lds, stream, a.out, a.records, a.cum, a.q, a.k_cache,
+                       dim3(threads), lds, stream, a.out, a.records, a.seq_workers, a.q, a.k_cache,
                        a.v_cache, a.block_table, a.max_blocks_per_seq, a.context_lens,
                        a.max_context_len, a.num_seqs, a.num_q_heads, a.num_kv_heads, a.scale_log2,
                        a.out_scale, (int)workers, a.cu_q_lens);
@@ -767,8 +797,8 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     dim3 mgrid((a.num_q_heads + 3) / 4, a.num_seqs);
     hipLaunchKernelGGL((decode_merge_kernel<OUT_BF16>), mgrid, dim3(256), 0, stream, a.out,
-                       a.records, a.cum, a.context_lens, a.max_context_len, a.num_seqs,
-                       a.num_q_heads, (int)workers, a.out_scale, a.cu_q_lens);
+                       a.records, a.seq_workers, a.context_lens, a.max_context_len, a.num_seqs,
+                       a.num_q_heads, a.out_scale, a.cu_q_lens);
     return hipGetLastError();
 }
 
@@ -850,7 +880,7 @@ int64_t decode_max_workers(int num_seqs, int max_context_len) {
 size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                               int max_context_len) {
     if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
-    const size_t cum = ((size_t)(num_seqs + 1) * sizeof(int32_t) + 255) / 256 * 256;
+    const size_t cum = ((size_t)2 * num_seqs * sizeof(int32_t) + 255) / 256 * 256;
     return cum + (size_t)decode_max_workers(num_seqs, max_context_len) * 2 * num_q_heads *
                      kRecStride * sizeof(float);
 }

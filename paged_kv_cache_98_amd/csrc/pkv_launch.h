@@ -59,7 +59,7 @@ struct DecodeArgs {
     int num_kv_heads;
     int block_size;
     float scale_log2;     // scale * log2(e) (times k_scale for an FP8 cache)
-    int32_t* cum;         // workspace: [num_seqs + 1] tile prefix sums
+    int32_t* seq_workers; // workspace: [2][num_seqs] workers holding each sequence's first / last tile
     float* records;       // workspace: [max_workers][2][num_q_heads][head_dim + 4] partials
     int64_t max_workers;  // workers whose records fit the workspace
     // NULL for a plain decode batch.  Set for the decode rows of a mixed
@@ -117,7 +117,8 @@ size_t prefill_streamk_bytes(int num_seqs, int max_q_len, int group, int num_kv_
 // dynamic LDS (all CUs; cached per kernel and device).
 hipError_t resident_workgroups(const void* kern, int threads, size_t lds, int* out);
 
-// Decode workspace: the tile prefix sums, then the partial-result records.
+// Decode workspace: which workers hold each sequence's first and last tiles,
+// then the partial-result records.
 size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                               int max_context_len);
 int64_t decode_max_workers(int num_seqs, int max_context_len);

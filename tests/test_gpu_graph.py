@@ -35,9 +35,12 @@ def replay_and_check(step, out, stream, replays=3):
         assert torch.equal(out, ref), f"eager call after replay {k}"
 
 
-def test_graph_decode_step():
-    w = W.llama8b_decode(batch=12, lo=100, hi=3000, seed=6100)
-    print(f"[graph decode] {w.name}", flush=True)
+@pytest.mark.parametrize("batch,lo,hi", [(12, 100, 3000), (64, 512, 4096)])
+def test_graph_decode_step(batch, lo, hi):
+    """A small batch and the full 8B-shaped one (most sequences shared by
+    several workers and merged by the second kernel)."""
+    w = W.llama8b_decode(batch=batch, lo=lo, hi=hi, seed=6100)
+    print(f"[graph decode] {w.name} batch {batch}", flush=True)
     b = W.materialize(w, device=DEV, poison=True)
     ws = torch.empty(pkv.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads,
                                                 w.max_context_len), dtype=torch.uint8, device=DEV)
