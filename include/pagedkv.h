@@ -75,7 +75,8 @@ enum pkv_status {
     PKV_ERR_NO_MEMORY = -7,   /* block manager: too few free blocks; nothing changed */
     PKV_ERR_STATE = -8,       /* block manager: unknown or already existing sequence id */
     PKV_ERR_HOST_ALLOC = -9,  /* block manager: host memory ran out; nothing changed */
-    PKV_ERR_VALUE = -10       /* an FP8 cache scale is not finite and positive */
+    PKV_ERR_VALUE = -10,      /* an FP8 cache scale is not finite and positive */
+    PKV_ERR_SCRATCH = -11     /* the call needs more than the library's fixed scratch */
 };
 
 enum pkv_out_dtype {
@@ -158,6 +159,32 @@ int pkv_paged_decode_attn(void *out, int out_dtype, const void *q, const void *k
                           int max_context_len, int num_seqs, int num_q_heads,
                           int num_kv_heads, int head_dim, int block_size, float scale,
                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * paged_decode_attn_noalloc -- pkv_paged_decode_attn for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments and results (the same
+ * kernels, bit for bit) without the workspace: its partial results live in
+ * a fixed scratch array inside the library, pkv_decode_noalloc_max_bytes()
+ * bytes on each GPU, held until the process ends.  The call allocates and
+ * frees nothing (no hipMalloc, no library routine that allocates).
+ *   PKV_ERR_SCRATCH  pkv_decode_workspace_bytes() of these sizes exceeds
+ *                    the scratch (checked on the host, nothing launched)
+ *   PKV_ERR_LAUNCH   also when the scratch's device address cannot be found
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's contents (nothing in it needs clearing): calls that overlap on one
+ * GPU (different streams, or several threads) race and must be serialised
+ * by the caller.
+ */
+int pkv_paged_decode_attn_noalloc(void *out, int out_dtype, const void *q, const void *k_cache,
+                                  const void *v_cache, const int32_t *block_table,
+                                  int max_blocks_per_seq, const int32_t *context_lens,
+                                  int max_context_len, int num_seqs, int num_q_heads,
+                                  int num_kv_heads, int head_dim, int block_size, float scale,
+                                  void *stream);
+
+/* Size of the fixed scratch of pkv_paged_decode_attn_noalloc, in bytes. */
+size_t pkv_decode_noalloc_max_bytes(void);
 
 /*
  * FP8 KV cache ("让 Agent 跑得快：LLM 推理服务", section 四, FP8 量化: one byte

@@ -30,6 +30,7 @@ PKV_ERR_NO_MEMORY = -7
 PKV_ERR_STATE = -8
 PKV_ERR_HOST_ALLOC = -9
 PKV_ERR_VALUE = -10
+PKV_ERR_SCRATCH = -11
 PKV_OUT_F32 = 0
 PKV_OUT_BF16 = 1
 
@@ -38,7 +39,8 @@ EXPORTED = ("pkv_status_string", "pkv_version", "pkv_kv_append", "pkv_decode_wor
             "pkv_paged_prefill_attn_tree", "pkv_paged_prefill_attn_fp8", "pkv_paged_prefill_attn_tree_fp8", "pkv_kv_append_fp8", "pkv_paged_decode_attn_fp8", "pkv_copy_blocks", "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free",
             "pkv_bm_allocate", "pkv_bm_allocate_cached", "pkv_bm_num_cached", "pkv_bm_free", "pkv_bm_fork", "pkv_bm_append", "pkv_bm_append_batch",
             "pkv_bm_seq_info",
-            "pkv_bm_refcount", "pkv_bm_block_table")
+            "pkv_bm_refcount", "pkv_bm_block_table", "pkv_paged_decode_attn_noalloc",
+            "pkv_decode_noalloc_max_bytes")
 
 _lib = None
 
@@ -89,6 +91,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_paged_decode_attn.restype = _i32
     lib.pkv_paged_decode_attn.argtypes = [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
                                           _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]
+    lib.pkv_paged_decode_attn_noalloc.restype = _i32
+    lib.pkv_paged_decode_attn_noalloc.argtypes = [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
+                                                  _i32, _i32, _i32, _i32, _i32, _f32, _vp]
+    lib.pkv_decode_noalloc_max_bytes.restype = _sz
+    lib.pkv_decode_noalloc_max_bytes.argtypes = []
     lib.pkv_prefill_workspace_bytes.restype = _sz
     lib.pkv_prefill_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32]
     lib.pkv_paged_prefill_attn.restype = _i32
@@ -157,7 +164,8 @@ def _check(status: int):
     cls = {PKV_ERR_NO_MEMORY: OutOfBlocks, PKV_ERR_STATE: UnknownSequence,
            PKV_ERR_NULL: InvalidArgument, PKV_ERR_SHAPE: InvalidArgument,
            PKV_ERR_UNSUPPORTED: InvalidArgument, PKV_ERR_WORKSPACE: InvalidArgument,
-           PKV_ERR_ALIGN: InvalidArgument, PKV_ERR_VALUE: InvalidArgument}.get(status, PagedKVError)
+           PKV_ERR_ALIGN: InvalidArgument, PKV_ERR_VALUE: InvalidArgument,
+           PKV_ERR_SCRATCH: InvalidArgument}.get(status, PagedKVError)
     raise cls(status, status_string(status))
 
 
@@ -339,6 +347,30 @@ def paged_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         _dev(context_lens, "context_lens", torch.int32), max_context_len, b, hq, hkv, d, bs,
         float(scale), ws_ptr, ws_len, _stream(stream)))
     return out
+
+
+def paged_decode_attn_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                              block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                              max_context_len: int, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """pkv_paged_decode_attn_noalloc: pkv_paged_decode_attn with the library's
+    fixed scratch instead of a workspace; the caller passes `out` (nothing is
+    allocated here either)."""
+    lib = load_library()
+    b, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if d2 != d or block_table.dim() != 2 or block_table.shape[0] != b:
+        raise ValueError("shape mismatch")
+    _check(lib.pkv_paged_decode_attn_noalloc(
+        _dev(out, "out"), _out_code(out.dtype), _dev(q, "q", torch.bfloat16),
+        _dev(k_cache, "k_cache", torch.bfloat16), _dev(v_cache, "v_cache", torch.bfloat16),
+        _dev(block_table, "block_table", torch.int32), block_table.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), max_context_len, b, hq, hkv, d, bs,
+        float(scale), _stream(stream)))
+    return out
+
+
+def decode_noalloc_max_bytes() -> int:
+    return load_library().pkv_decode_noalloc_max_bytes()
 
 
 def paged_prefill_attn(q: torch.Tensor, cu_q_lens: torch.Tensor, k_cache: torch.Tensor,

@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "pagedkv.h"
 #include "pkv_device.h"
 #include "pkv_launch.h"
@@ -48,6 +50,38 @@ int check_attention_shape(int max_blocks_per_seq, int max_context_len, int num_s
 
 int to_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH; }
 
+// The fixed scratch of pkv_paged_decode_attn_noalloc: the decode workspace
+// of calls that may not allocate, in the library's own device memory.  Each
+// GPU the library runs on holds its own copy until the process ends.  In
+// host code `scratch` names a host-side stand-in: its device address is
+// fetched once per device (hipGetSymbolAddress, that device current) and
+// only that address is passed on.
+constexpr size_t kScratchBytes = (size_t)80 << 20;
+__device__ __attribute__((aligned(256))) static char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch, or NULL (with *err set).
+void* scratch_address(hipError_t* err) {
+    int dev = 0;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
 // Prefill workspace: the decode kernels' part for single-row sequences,
 // then, when the call's chunks fit one workgroup (stream-K), that kernel's
 // prefix sums and records at *chunk_offset.
@@ -82,6 +116,7 @@ const char* pkv_status_string(int status) {
         case PKV_ERR_STATE: return "unknown or already existing sequence id";
         case PKV_ERR_HOST_ALLOC: return "host memory allocation failed";
         case PKV_ERR_VALUE: return "a scale is not finite and positive";
+        case PKV_ERR_SCRATCH: return "the call needs more than the library's fixed scratch";
         default: return "unknown status";
     }
 }
@@ -145,7 +180,8 @@ int decode_call(void* out, int out_dtype, const void* q, const void* k_cache, co
                 bool kv_fp8, float k_scale, float v_scale, const int32_t* block_table,
                 int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
                 int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                float scale, void* workspace, size_t workspace_bytes, void* stream) {
+                float scale, void* workspace, size_t workspace_bytes, void* stream,
+                bool fixed_scratch = false) {
     int st = check_attention_shape(max_blocks_per_seq, max_context_len, num_seqs, num_q_heads,
                                    num_kv_heads, head_dim, block_size, out_dtype);
     if (st != PKV_OK) return st;
@@ -158,6 +194,13 @@ int decode_call(void* out, int out_dtype, const void* q, const void* k_cache, co
         return PKV_ERR_ALIGN;
     const size_t need = pkv::decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                     max_context_len);
+    if (fixed_scratch) {
+        if (need > kScratchBytes) return PKV_ERR_SCRATCH;
+        hipError_t e = hipSuccess;
+        workspace = scratch_address(&e);
+        if (!workspace) return PKV_ERR_LAUNCH;
+        workspace_bytes = kScratchBytes;
+    }
     if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
     if (!aligned16(workspace)) return PKV_ERR_ALIGN;
 
@@ -202,6 +245,19 @@ int pkv_paged_decode_attn(void* out, int out_dtype, const void* q, const void* k
                        num_kv_heads, head_dim, block_size, scale, workspace, workspace_bytes,
                        stream);
 }
+
+int pkv_paged_decode_attn_noalloc(void* out, int out_dtype, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_table,
+                                  int max_blocks_per_seq, const int32_t* context_lens,
+                                  int max_context_len, int num_seqs, int num_q_heads,
+                                  int num_kv_heads, int head_dim, int block_size, float scale,
+                                  void* stream) {
+    return decode_call(out, out_dtype, q, k_cache, v_cache, false, 1.0f, 1.0f, block_table,
+                       max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
+                       num_kv_heads, head_dim, block_size, scale, nullptr, 0, stream, true);
+}
+
+size_t pkv_decode_noalloc_max_bytes(void) { return kScratchBytes; }
 
 int pkv_paged_decode_attn_fp8(void* out, int out_dtype, const void* q, const void* k_cache,
                               const void* v_cache, float k_scale, float v_scale,

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for s in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10):
+    for s in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11):
         assert binding.status_string(s) != "unknown status"
     assert binding.status_string(-99) == "unknown status"
     assert lib.pkv_version() >= 100
@@ -81,6 +81,35 @@ def test_decode_validation(lib):
     assert decode(lib, hq=48, hkv=12, maxctx=100, ws=P2, wsb=1 << 30) == E.PKV_ERR_UNSUPPORTED
     # nothing to do is fine even with NULL pointers
     assert decode(lib, nseq=0, q=None, out=None) == E.PKV_OK
+
+
+def test_decode_noalloc_validation(lib):
+    """The allocation-free decode checks its arguments like the workspace
+    call, and rejects sizes whose workspace would exceed its fixed scratch,
+    all on the host before anything touches a device."""
+    E = binding
+    cap = lib.pkv_decode_noalloc_max_bytes()
+    assert cap == 80 << 20
+
+    def call(**kw):
+        a = dict(out=P, out_dtype=0, q=P, k=P, v=P, bt=P, mb=8, cl=P, maxctx=100, nseq=4, hq=8,
+                 hkv=2, d=128, bs=16, scale=0.1, stream=None)
+        a.update(kw)
+        return lib.pkv_paged_decode_attn_noalloc(a["out"], a["out_dtype"], a["q"], a["k"],
+                                                 a["v"], a["bt"], a["mb"], a["cl"], a["maxctx"],
+                                                 a["nseq"], a["hq"], a["hkv"], a["d"], a["bs"],
+                                                 a["scale"], a["stream"])
+    assert call(q=None) == E.PKV_ERR_NULL
+    assert call(d=64) == E.PKV_ERR_UNSUPPORTED
+    assert call(k=MIS) == E.PKV_ERR_ALIGN
+    assert call(nseq=0, q=None, out=None) == E.PKV_OK
+    # 128 query heads over 1024 workers: 2 x 1024 x 128 x 528 bytes of records
+    big = dict(nseq=64, hq=128, hkv=16, maxctx=100000, mb=6250)
+    assert lib.pkv_decode_workspace_bytes(64, 128, 16, 128, 100000) > cap
+    assert call(**big) == E.PKV_ERR_SCRATCH
+    # the 8B- and 70B-shaped batches fit
+    assert lib.pkv_decode_workspace_bytes(64, 32, 8, 128, 4096) <= cap
+    assert lib.pkv_decode_workspace_bytes(256, 64, 8, 128, 8192) <= cap
 
 
 def test_decode_workspace_size(lib):
