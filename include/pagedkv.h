@@ -264,9 +264,12 @@ size_t pkv_prefill_workspace_bytes(int num_seqs, int num_q_tokens, int max_q_len
  *                  Lq_i <= context_lens[i] is required.
  *   max_q_len      host-side upper bound of Lq_i
  *   num_q_tokens   host-side total query rows (= cu_q_lens[num_seqs])
- * Rows with Lq_i == 1 take the bandwidth-bound decode path (the split-KV
- * decode kernels, enqueued after the MFMA chunk kernel on the same stream);
- * longer chunks take the MFMA path.  Chunks that fit one workgroup (the
+ * Rows with Lq_i == 1 take the bandwidth-bound decode path and longer
+ * chunks the MFMA path.  When the call has both and its chunks do not fit
+ * one workgroup, one grid runs them side by side on a 256-CU device (a
+ * stream-K decode worker beside a chunk workgroup on every CU), then the
+ * decode merge kernel; on another device the decode kernels follow the
+ * chunk kernel on the same stream.  Chunks that fit one workgroup (the
  * workspace comment above) run stream-K: all (sequence, KV head, 64-key
  * tile) units cut into equal ranges over the workgroups the GPU holds at
  * once, items shared by two workers merged by a log-sum-exp fold in a

@@ -383,11 +383,7 @@ int prefill_call(void* out, int out_dtype, const void* q, const int32_t* cu_q_le
     }
     a.tree_mask = tree_mask;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (max_q_len > 1) {
-        st = to_status(pkv::launch_prefill(a, s));
-        if (st != PKV_OK) return st;
-    }
-    if (!any_decode_rows) return PKV_OK;
+    if (!any_decode_rows) return to_status(pkv::launch_prefill(a, s));
 
     pkv::DecodeArgs d;
     d.out = out;
@@ -411,6 +407,15 @@ int prefill_call(void* out, int out_dtype, const void* q, const int32_t* cu_q_le
                                          align_up((size_t)2 * num_seqs * sizeof(int32_t), 256));
     d.max_workers = pkv::decode_max_workers(num_seqs, max_context_len);
     d.cu_q_lens = cu_q_lens;
+    if (max_q_len > 1 && !streamk) {
+        // chunks and decode rows in one grid, sharing the CUs
+        const hipError_t e = pkv::launch_mixed(a, d, s);
+        if (e != hipErrorNotSupported) return to_status(e);
+    }
+    if (max_q_len > 1) {
+        st = to_status(pkv::launch_prefill(a, s));
+        if (st != PKV_OK) return st;
+    }
     return to_status(pkv::launch_decode(d, s));
 }
 

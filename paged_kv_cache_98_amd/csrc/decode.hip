@@ -1,453 +1,18 @@
-// decode.hip -- paged decode attention for gfx950 with a single-pass online
-// softmax and a stream-K split of the keys over persistent waves.
-//
-// What it computes ("LLM 推理优化技术全景", "Flash Attention 深度剖析"): for
-// every sequence i and query head h,
-//     out[i,h,:] = sum_t exp(s_t - m) V[t,:] / sum_t exp(s_t - m),
-//     s_t = scale * <q[i,h,:], K[t,:]>,
-// over the sequence's context_lens[i] keys, which live in 16- or 32-token
-// physical blocks found through the block table ("LLM 推理引擎深度解析 ...",
-// section 2.1; "让 Agent 跑得快", section 五).  The keys are visited once, a
-// 16-token tile at a time, keeping a running maximum m and running sum l and
-// rescaling the accumulator by exp(m_old - m_new) whenever m grows (the
-// page's "在线 Softmax"); the division by l is deferred to the very end as in
-// its "Flash Attention v2 的改进".
-//
-// Split of the work (the sequence-axis parallelism of that section, taken
-// to its balanced limit):
-//   * a worker is a workgroup with one wave per KV head; the G = Hq/Hkv
-//     query heads of a KV head ride along in its wave, so each K/V byte is
-//     read from HBM once per KV head (GQA grouping), and the waves of a
-//     worker read each physical block's rows of all heads together
-//     (contiguous bs * Hkv * D bf16 of K, the same of V);
-//   * all sequences' 16-token tiles are laid end to end and cut into W
-//     equal contiguous ranges, one per persistent worker (W = what the chip
-//     holds at once).  A worker walks its range sequence by sequence: a
-//     sequence it covers whole is finalised in place; a piece of a sequence
-//     shared with other workers leaves (m, l, unnormalised acc) per query
-//     head in the workspace, and the merge kernel combines the pieces with
-//     the same exp(m_k - M) rescale (a log-sum-exp merge);
-//   * so every worker streams the same number of bytes, no workgroup is
-//     launched without work, and long contexts split across many workers.
-// Inside a wave (64 lanes = 4 rows of 16): a tile of one head is 4 KB of K
-// and 4 KB of V, four 128-bit loads per lane each; lane (row r, col c) holds
-// dims 8c..8c+7 of tokens 4i + r, i = 0..3; the 16-lane row reduces the QK
-// partial sums with DPP adds; each row is its own online-softmax stream
-// (tokens = r mod 4) merged with the other rows at the end of a piece; the
-// next tile's loads are issued before the current tile's math.  An FP8
-// cache (one byte per value) uses the same layout with 64-bit loads, or,
-// for up to 4 query heads per KV head, 8 rows of 8 lanes holding 16 dims of
-// 2 tokens each (see the storage policies below).  Scores are
-// in the log2 domain (scale * log2 e folded in), exponentials are v_exp_f32.
-#include "pkv_device.h"
-#include "pkv_launch.h"
+// decode.hip -- paged decode attention for gfx950: the stream-K decode
+// kernel (the worker of decode_core.h over a grid of persistent workgroups),
+// the log-sum-exp merge of sequences shared by several workers, and the
+// launchers.
+#include "decode_core.h"
 
 namespace pkv {
 
 namespace {
 
-// How the pools store a value, and the lane layout that goes with it.  A
-// wave sees a 16-token tile of one KV head as rows of kRowLanes lanes: lane
-// (row r, col c) holds dims kDims c .. kDims c + kDims - 1 of the tile's
-// tokens kRows i + r, i = 0 .. kLoads - 1, one word per token, and the
-// kRowLanes lanes of a row reduce their partial dot products with DPP.
-//   * K comes out as bf16 pairs for the dot2 instructions (E4M3 to bf16 is
-//     exact: every E4M3 value is a bf16 value);
-//   * V comes out as floats, or, for FP8, as fp16 pairs over two tokens.
-// The FP8 cache's two scales are applied outside the tile loop: k_scale
-// inside the score scale, v_scale on the finished output.
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-
-// bf16 pools: 8 dims (16 bytes) per lane and token, rows of 16 lanes.
-struct KvBf16 {
-    static constexpr int kElemBytes = 2;
-    static constexpr int kDims = 8;
-    static constexpr bool kPairedPV = false;
-    using Word = uint4;
-    static __device__ __forceinline__ Word load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-    }
-    static __device__ __forceinline__ void k_pairs(const Word& w, uint32_t (&kp)[4]) {
-        kp[0] = w.x; kp[1] = w.y; kp[2] = w.z; kp[3] = w.w;
-    }
-    static __device__ __forceinline__ void v_floats(const Word& w, float (&v)[8]) {
-        v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
-        v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
-        v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
-        v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
-    }
-};
-
-// FP8 codes in the OCP E4M3 format, decoded by the hardware conversions.
-// Their P V runs on fp16 dot products over token pairs: a lane's tokens i
-// and i + 1 give, for every dim, the pair (v_i, v_i+1) (a byte permute puts
-// the two codes side by side, one conversion widens them to fp16 exactly)
-// and (p_i, p_i+1) rounds to fp16 once per query head, so one
-// v_dot2_f32_f16 does the work of two fp32 FMAs.  P is in [0, 1] and rounds
-// with 2^-11 relative error, as in the chunked-prefill kernel.
-template <int NWORDS>  // 32-bit words of codes per lane and token
-struct KvFp8Base {
-    static constexpr int kElemBytes = 1;
-    static constexpr int kDims = 4 * NWORDS;
-    static constexpr bool kPairedPV = true;
-    template <bool HIGH>  // codes 2, 3 of the word instead of 0, 1
-    static __device__ __forceinline__ uint32_t bf16_pair(uint32_t codes) {
-        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(
-                                                (int)codes, 1.0f, HIGH));
-    }
-    static __device__ __forceinline__ void k_pairs_of(const uint32_t (&w)[NWORDS],
-                                                      uint32_t (&kp)[2 * NWORDS]) {
-#pragma unroll
-        for (int j = 0; j < NWORDS; ++j) {
-            kp[2 * j] = bf16_pair<false>(w[j]);
-            kp[2 * j + 1] = bf16_pair<true>(w[j]);
-        }
-    }
-    static __device__ __forceinline__ void v_floats_of(const uint32_t (&w)[NWORDS],
-                                                       float (&v)[4 * NWORDS]) {
-#pragma unroll
-        for (int j = 0; j < NWORDS; ++j) {
-            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[j], false);
-            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[j], true);
-            v[4 * j] = lo[0]; v[4 * j + 1] = lo[1]; v[4 * j + 2] = hi[0]; v[4 * j + 3] = hi[1];
-        }
-    }
-    // vp[e] = (value of token a, value of token b) at dim 4 j + e: word j of
-    // each token holds dims 4 j .. 4 j + 3
-    static __device__ __forceinline__ void pairs4(uint32_t a, uint32_t b, f16x2_t (&vp)[4]) {
-        // bytes (a.k, b.k, a.k+1, b.k+1) of the two words, k = 0 and 2
-        const uint32_t w0 = __builtin_amdgcn_perm(b, a, 0x05010400u);
-        const uint32_t w1 = __builtin_amdgcn_perm(b, a, 0x07030602u);
-        vp[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w0, 1.0f, false);
-        vp[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w0, 1.0f, true);
-        vp[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w1, 1.0f, false);
-        vp[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w1, 1.0f, true);
-    }
-};
-
-// FP8 pools, 8 dims (8 bytes) per lane and token, rows of 16 lanes: for 8
-// and 16 query heads per KV head, whose accumulators fill the registers.
-struct KvFp8 : KvFp8Base<2> {
-    using Word = uint2;
-    static __device__ __forceinline__ Word load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-        return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-    }
-    static __device__ __forceinline__ void k_pairs(const Word& w, uint32_t (&kp)[4]) {
-        k_pairs_of({w.x, w.y}, kp);
-    }
-    static __device__ __forceinline__ void v_floats(const Word& w, float (&v)[8]) {
-        v_floats_of({w.x, w.y}, v);
-    }
-    static __device__ __forceinline__ void v_pairs4(const Word& a, const Word& b, int j,
-                                                    f16x2_t (&vp)[4]) {
-        pairs4(j == 0 ? a.x : a.y, j == 0 ? b.x : b.y, vp);
-    }
-};
-
-// FP8 pools, 16 dims (16 bytes) per lane and token, rows of 8 lanes: half
-// the lanes share a token, so the row sums take three DPP steps instead of
-// four and each softmax value is computed by 8 lanes instead of 16 (up to 4
-// query heads per KV head).
-struct KvFp8Wide : KvFp8Base<4> {
-    using Word = uint4;
-    static __device__ __forceinline__ Word load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-    }
-    static __device__ __forceinline__ void k_pairs(const Word& w, uint32_t (&kp)[8]) {
-        k_pairs_of({w.x, w.y, w.z, w.w}, kp);
-    }
-    static __device__ __forceinline__ void v_floats(const Word& w, float (&v)[16]) {
-        v_floats_of({w.x, w.y, w.z, w.w}, v);
-    }
-    static __device__ __forceinline__ void v_pairs4(const Word& a, const Word& b, int j,
-                                                    f16x2_t (&vp)[4]) {
-        const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
-        const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
-        pairs4(aw[j], bw[j], vp);
-    }
-};
-
-template <typename KV>
-struct Layout {
-    static constexpr int kDims = KV::kDims;                  // per lane and token
-    static constexpr int kRowLanes = kHeadDim / kDims;       // lanes sharing a token
-    static constexpr int kRows = 64 / kRowLanes;             // tokens per load
-    static constexpr int kLoads = kTileTokens / kRows;       // loads per lane per tile
-};
-
-template <int LANES>
-__device__ __forceinline__ float row_sum(float x) {
-    if constexpr (LANES == 16) return row_sum16(x);
-    else return row_sum8(x);
-}
-
-template <typename KV>
-struct Tile {
-    typename KV::Word k[Layout<KV>::kLoads];
-    typename KV::Word v[Layout<KV>::kLoads];
-};
-
-// Loads one tile: `kt` / `vt` address the tile's first row for this KV head
-// in the K / V pool, `voff[i]` is this lane's byte offset of load group i
-// (tokens kRows i + row, its dims): buffer loads with a scalar base and a
-// 32-bit lane offset, so no per-lane 64-bit addresses are kept.
-template <typename KV>
-__device__ __forceinline__ void load_tile(Tile<KV>& t, const char* kt, const char* vt,
-                                          const uint32_t (&voff)[Layout<KV>::kLoads]) {
-    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kt);
-    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vt);
-#pragma unroll
-    for (int i = 0; i < Layout<KV>::kLoads; ++i) t.k[i] = KV::load(rk, voff[i]);
-#pragma unroll
-    for (int i = 0; i < Layout<KV>::kLoads; ++i) t.v[i] = KV::load(rv, voff[i]);
-}
-
-template <int G, int ND>
-struct State {
-    float m[G];        // running max (log2 domain), uniform across the row
-    float l[G];        // running sum, uniform across the row
-    float acc[G][ND];  // unnormalised output, this lane's dims
-    float alpha[G];    // last rescale factor exp2(m_old - m_new) (bf16 pools)
-};
-
-// One 16-token tile: QK, online-softmax update, PV.  `ntok_left` is the
-// number of valid tokens from the start of this tile (>= 16 for a full one).
-// Raw scores are maximised unscaled (the scale is >= 0 after the sign of q
-// absorbed a negative one) and scaled inside the exponent's FMA.
-template <typename KV, int G, bool PARTIAL>
-__device__ __forceinline__ void process_tile(State<G, KV::kDims>& st, const Tile<KV>& t,
-                                             const uint32_t (&qv)[G][KV::kDims / 2], float c,
-                                             int row, int ntok_left) {
-    constexpr int kLoads = Layout<KV>::kLoads;
-    constexpr int kRows = Layout<KV>::kRows;
-    constexpr int ND = KV::kDims;
-    float s[kLoads][G];
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-        uint32_t k[ND / 2];
-        KV::k_pairs(t.k[i], k);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float d = dot2_bf16(k[0], qv[g][0], 0.0f);
-#pragma unroll
-            for (int j = 1; j < ND / 2; ++j) d = dot2_bf16(k[j], qv[g][j], d);
-            s[i][g] = row_sum<Layout<KV>::kRowLanes>(d);
-        }
-        if (PARTIAL) {
-            // Tokens past the end may hold anything: they must not raise the
-            // maximum (lowest finite value, so that a zero scale stays finite)
-            // and get p = 0 below.
-            const bool valid = (kRows * i + row) < ntok_left;
-#pragma unroll
-            for (int g = 0; g < G; ++g) s[i][g] = valid ? s[i][g] : -3.402823466e38f;
-        }
-    }
-    float p[kLoads][G];
-    if constexpr (KV::kPairedPV) {
-        float m_old[G], sum[G];
-        bool grew = false;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float bm = kLoads == 4 ? fmaxf(fmaxf(s[0][g], s[1][g]), fmaxf(s[2][g], s[3][g]))
-                                   : fmaxf(s[0][g], s[1][g]);
-            bm *= c;
-            const float mn = fmaxf(st.m[g], bm);
-            grew |= mn > st.m[g];
-            m_old[g] = st.m[g];
-            st.m[g] = mn;
-            sum[g] = 0.0f;
-#pragma unroll
-            for (int i = 0; i < kLoads; ++i) {
-                p[i][g] = fast_exp2(fmaf(s[i][g], c, -mn));
-                if (PARTIAL) p[i][g] = (kRows * i + row) < ntok_left ? p[i][g] : 0.0f;
-                sum[g] += p[i][g];
-            }
-        }
-        // The exp(m_old - m_new) rescale of l and the accumulator is needed only
-        // when some running maximum moved; after the first tiles that is rare
-        // (an unmoved maximum gives exactly 1 either way).
-        float alpha[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) alpha[g] = 1.0f;
-        if (__any(grew)) {
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                alpha[g] = fast_exp2(m_old[g] - st.m[g]);
-#pragma unroll
-                for (int d = 0; d < ND; ++d) st.acc[g][d] *= alpha[g];
-            }
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) st.l[g] = fmaf(st.l[g], alpha[g], sum[g]);
-    } else {
-        bool grew = false;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float bm = kLoads == 4 ? fmaxf(fmaxf(s[0][g], s[1][g]), fmaxf(s[2][g], s[3][g]))
-                                   : fmaxf(s[0][g], s[1][g]);
-            bm *= c;
-            const float mn = fmaxf(st.m[g], bm);
-            grew |= mn > st.m[g];
-            const float alpha = fast_exp2(st.m[g] - mn);
-            st.m[g] = mn;
-            float sum = 0.0f;
-#pragma unroll
-            for (int i = 0; i < kLoads; ++i) {
-                p[i][g] = fast_exp2(fmaf(s[i][g], c, -mn));
-                if (PARTIAL) p[i][g] = (kRows * i + row) < ntok_left ? p[i][g] : 0.0f;
-                sum += p[i][g];
-            }
-            st.l[g] = fmaf(st.l[g], alpha, sum);
-            st.alpha[g] = alpha;
-        }
-        // The accumulator needs the exp(m_old - m_new) rescale only when some
-        // running maximum moved; after the first tiles that is rare.
-        if (__any(grew)) {
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-#pragma unroll
-                for (int d = 0; d < ND; ++d) st.acc[g][d] *= st.alpha[g];
-        }
-    }
-    if constexpr (KV::kPairedPV && !PARTIAL) {
-#pragma unroll
-        for (int i = 0; i < kLoads; i += 2) {
-            f16x2_t pp[G];
-#pragma unroll
-            for (int g = 0; g < G; ++g) pp[g] = f16x2_t{(_Float16)p[i][g], (_Float16)p[i + 1][g]};
-            // four dims at a time, so few pairs are live at once
-#pragma unroll
-            for (int j = 0; j < ND / 4; ++j) {
-                f16x2_t vp[4];
-                KV::v_pairs4(t.v[i], t.v[i + 1], j, vp);
-#pragma unroll
-                for (int g = 0; g < G; ++g)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        st.acc[g][4 * j + e] =
-                            __builtin_amdgcn_fdot2(vp[e], pp[g], st.acc[g][4 * j + e], false);
-            }
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
-            float v[ND];
-            KV::v_floats(t.v[i], v);
-            if (PARTIAL) {
-                // A masked token has p = 0, but its pool slot may hold anything
-                // (NaN included): zero the value so 0 * v stays 0.
-                const bool valid = (kRows * i + row) < ntok_left;
-#pragma unroll
-                for (int d = 0; d < ND; ++d) v[d] = valid ? v[d] : 0.0f;
-            }
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-#pragma unroll
-                for (int d = 0; d < ND; ++d) st.acc[g][d] = fmaf(p[i][g], v[d], st.acc[g][d]);
-            }
-        }
-    }
-}
-
-template <bool OUT_BF16>
-__device__ __forceinline__ void store8(void* out, size_t elem, const float (&x)[8]) {
-    if (OUT_BF16) {
-        uint4 w;
-        w.x = (uint32_t)f32_to_bf16_rne(x[0]) | ((uint32_t)f32_to_bf16_rne(x[1]) << 16);
-        w.y = (uint32_t)f32_to_bf16_rne(x[2]) | ((uint32_t)f32_to_bf16_rne(x[3]) << 16);
-        w.z = (uint32_t)f32_to_bf16_rne(x[4]) | ((uint32_t)f32_to_bf16_rne(x[5]) << 16);
-        w.w = (uint32_t)f32_to_bf16_rne(x[6]) | ((uint32_t)f32_to_bf16_rne(x[7]) << 16);
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + elem) = w;
-    } else {
-        float4* o = reinterpret_cast<float4*>(static_cast<float*>(out) + elem);
-        o[0] = make_float4(x[0], x[1], x[2], x[3]);
-        o[1] = make_float4(x[4], x[5], x[6], x[7]);
-    }
-}
-
-template <bool OUT_BF16>
-__device__ __forceinline__ void store1(void* out, size_t elem, float x) {
-    if (OUT_BF16) static_cast<uint16_t*>(out)[elem] = f32_to_bf16_rne(x);
-    else static_cast<float*>(out)[elem] = x;
-}
-
-constexpr int kRecStride = kHeadDim + 4;  // floats per record: acc[128], m, l, 2 pad
-constexpr int kMinTilesPerWorker = 4;   // fewer waves for tiny batches
-// KV heads (one wave each) served by one workgroup: 8 while a wave fits in
-// 256 registers (two waves per SIMD), else 4.
-template <int G>
-constexpr int max_waves_per_worker() { return G <= 4 ? 8 : 4; }
-constexpr int64_t kMaxWorkers = 1024;    // workgroups of 8 waves an MI355X holds at most
-// Cost of a sequence boundary inside a worker's range, in quarter tiles
-// (per query heads per KV head: the tile math grows with G, the boundary's
-// round trips do not).
-template <int G>
-constexpr int64_t seq_cost() { return G <= 4 ? 6 : 16; }
-
-__device__ __forceinline__ int clamp_ctx(int ctx, int max_context_len) {
-    return ctx < 0 ? 0 : (ctx > max_context_len ? max_context_len : ctx);
-}
-
-// With cu_q_lens (a mixed prefill batch) only sequences with exactly one
-// query row are decoded here, and their q / out row is cu_q_lens[i]; without
-// it every sequence is one row, row i.
-__device__ __forceinline__ bool is_decode_row(const int32_t* __restrict__ cu_q_lens, int i) {
-    return cu_q_lens == nullptr || cu_q_lens[i + 1] - cu_q_lens[i] == 1;
-}
-__device__ __forceinline__ int row_of(const int32_t* __restrict__ cu_q_lens, int i) {
-    return cu_q_lens == nullptr ? i : cu_q_lens[i];
-}
-__device__ __forceinline__ int tiles_of(const int32_t* __restrict__ context_lens,
-                                        const int32_t* __restrict__ cu_q_lens, int i,
-                                        int max_context_len) {
-    if (!is_decode_row(cu_q_lens, i)) return 0;
-    return (clamp_ctx(context_lens[i], max_context_len) + kTileTokens - 1) / kTileTokens;
-}
-
-// Sliding window over a block-table row: lane j of `cur` holds the id of
-// block base + j, lane j of `nxt` that of base + 64 + j.  Tiles are visited
-// in increasing order, so the window only ever moves forward by 64.
-struct IdWindow {
-    const int32_t* row;
-    int nblk;
-    int base;
-    int cur;
-    int nxt;
-    __device__ __forceinline__ void init(const int32_t* r, int n, int first, int lane) {
-        row = r;
-        nblk = n;
-        base = first;
-        cur = first + lane < n ? r[first + lane] : 0;
-        nxt = first + 64 + lane < n ? r[first + 64 + lane] : 0;
-    }
-    __device__ __forceinline__ int get(int blk, int lane) {
-        if (blk >= base + 64) {
-            cur = nxt;
-            base += 64;
-            // clamped rather than masked: the load lands straight in `nxt`
-            // and nothing waits for it until the window moves again
-            const int k = base + 64 + lane;
-            nxt = row[k < nblk ? k : nblk - 1];
-        }
-        return __builtin_amdgcn_readlane(cur, blk - base);
-    }
-};
-
-// Byte offset (wave-uniform) of a tile's first token row in a pool.
-template <int BS>
-__device__ __forceinline__ size_t tile_bytes(IdWindow& ids, int tile, size_t row_bytes, int lane) {
-    const int tok = tile * kTileTokens;
-    const int phys = ids.get(tok / BS, lane);
-    return ((size_t)phys * BS + (tok % BS)) * row_bytes;
-}
+using namespace dec;
 
 // Grid: (num_workers, head groups); a workgroup has one wave per KV head of
 // its group (all KV heads when there are at most 8, else groups of 8);
-// dynamic LDS (num_seqs + 1) int32 for the tile prefix sums.  A worker
-// owns a contiguous range of (sequence, 16-token tile) units, and its waves
-// walk that range together, so each physical block's K rows of all heads
-// (bs * Hkv * D bf16, contiguous) are fetched at the same time.
-// Records: [W][2][num_q_heads][kRecStride] floats.
+// dynamic LDS (num_seqs + 1) int32 for the tile prefix sums.
 template <typename KV, int BS, int G, bool OUT_BF16>
 __global__ void __launch_bounds__(64 * max_waves_per_worker<G>())
 decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* __restrict__ seq_workers,
@@ -457,241 +22,12 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
                       int max_context_len, int num_seqs, int num_q_heads, int num_kv_heads,
                       float scale_log2, float out_scale, int num_workers,
                       const int32_t* __restrict__ cu_q_lens) {
-    constexpr int D = kHeadDim;
-    extern __shared__ int32_t s_cum[];  // s_cum[i] = tiles (per KV head) of sequences < i
-    __shared__ int32_t s_part[max_waves_per_worker<G>()];  // the waves' tile totals
-    const int tid = threadIdx.x;
-    const int nthr = blockDim.x;
-
-    // ---- prefix sums of per-sequence tile counts: each thread sums `per`
-    // consecutive sequences, each wave scans its 64 sums with lane
-    // shuffles, and one barrier passes the waves' totals around
-    const int per = (num_seqs + nthr - 1) / nthr;
-    int local = 0;
-    for (int k = 0; k < per; ++k) {
-        const int i = tid * per + k;
-        if (i < num_seqs)
-            local += tiles_of(context_lens, cu_q_lens, i, max_context_len);
-    }
-    int incl = local;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off);
-        if ((tid & 63) >= off) incl += y;
-    }
-    if ((tid & 63) == 63) s_part[tid >> 6] = incl;
-    __syncthreads();
-    int run = incl - local, total = 0;
-    for (int k = 0; k < nthr / 64; ++k) {
-        const int t = s_part[k];
-        run += k < (tid >> 6) ? t : 0;
-        total += t;
-    }
-    for (int k = 0; k < per; ++k) {
-        const int i = tid * per + k;
-        if (i < num_seqs) {
-            s_cum[i] = run;
-            run += tiles_of(context_lens, cu_q_lens, i, max_context_len);
-        }
-    }
-    if (tid == 0) s_cum[num_seqs] = total;
-    __syncthreads();
-
-    const int64_t U = s_cum[num_seqs];
-    // never more workers than tiles, so every worker's range is non-empty
-    const int64_t W = num_workers < U ? num_workers : U;
-    using L = Layout<KV>;
-    constexpr int ND = KV::kDims;
-    const int lane = tid & 63;
-    const int kvh = blockIdx.y * (nthr >> 6) + (tid >> 6);
-    const int row = lane / L::kRowLanes;
-    const int col = lane % L::kRowLanes;
-    const int64_t w = blockIdx.x;
-    // Ranges of equal cost, not equal tiles: a tile costs 4 units and every
-    // sequence boundary kSeqCost more (a worker that starts a new sequence
-    // restarts its load pipeline and loads another query and block-id
-    // window), so workers that cross more boundaries get fewer tiles.
-    // Worker wi starts at the first tile t with cost(t) >= wi * total / W,
-    // cost(t) = 4 t + kSeqCost * seq(t); the sequence is found among the
-    // costs of the sequences' first tiles.
-    constexpr int64_t kSeqCost = seq_cost<G>();
-    const int64_t cost_total = 4 * U + kSeqCost * (int64_t)(num_seqs - 1);
-    auto range_start = [&](int64_t wi) -> int64_t {
-        if (wi >= W) return U;
-        const int64_t target = wi * cost_total / W;
-        int lo = 0, hi = num_seqs;  // largest i with 4 cum[i] + kSeqCost i <= target
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (4 * (int64_t)s_cum[mid] + kSeqCost * (int64_t)mid <= target) lo = mid; else hi = mid;
-        }
-        int64_t tt = (target - kSeqCost * (int64_t)lo + 3) / 4;
-        tt = tt < s_cum[lo] ? s_cum[lo] : tt;
-        return tt > s_cum[lo + 1] ? s_cum[lo + 1] : tt;
-    };
-    int64_t t = w < W ? range_start(w) : 0;
-    const int64_t t_end = w < W ? range_start(w + 1) : 0;
-
-    const uint32_t neg = scale_log2 < 0.0f ? 0x80008000u : 0u;
-    const float c = fabsf(scale_log2);
-    const size_t row_bytes = (size_t)num_kv_heads * D * KV::kElemBytes;
-    uint32_t voff[L::kLoads];
-#pragma unroll
-    for (int i = 0; i < L::kLoads; ++i)
-        voff[i] = (uint32_t)((L::kRows * i + row) * row_bytes +
-                             ((size_t)kvh * D + col * ND) * KV::kElemBytes);
-    const char* kbase = reinterpret_cast<const char*>(k_cache);
-    const char* vbase = reinterpret_cast<const char*>(v_cache);
-    bool first_piece = true;
-
-    while (t < t_end) {
-        // sequence holding tile t: the last i with cum[i] <= t
-        int lo = 0, hi = num_seqs;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (s_cum[mid] <= t) lo = mid; else hi = mid;
-        }
-        const int seq = lo;
-        const int64_t seg_t0 = s_cum[seq];
-        const int64_t seg_t1 = s_cum[seq + 1];  // > t
-        const int tile0 = (int)(t - seg_t0);
-        const int64_t piece_end = t_end < seg_t1 ? t_end : seg_t1;
-        const int ntile = (int)(piece_end - t);
-        const int ctx = clamp_ctx(context_lens[seq], max_context_len);
-
-        const size_t head_row = ((size_t)row_of(cu_q_lens, seq) * num_q_heads + (size_t)kvh * G) * D;
-        uint32_t qv[G][ND / 2];  // this lane's dims of each query head, bf16 pairs
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int w8 = 0; w8 < ND / 8; ++w8) {
-                const uint4 x = *reinterpret_cast<const uint4*>(q + head_row + (size_t)g * D +
-                                                                col * ND + 8 * w8);
-                qv[g][4 * w8] = x.x ^ neg; qv[g][4 * w8 + 1] = x.y ^ neg;
-                qv[g][4 * w8 + 2] = x.z ^ neg; qv[g][4 * w8 + 3] = x.w ^ neg;
-            }
-        State<G, ND> st;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            st.m[g] = kNegBig;
-            st.l[g] = 0.0f;
-#pragma unroll
-            for (int d = 0; d < ND; ++d) st.acc[g][d] = 0.0f;
-        }
-
-        IdWindow ids;
-        ids.init(block_table + (size_t)seq * max_blocks_per_seq, (ctx + BS - 1) / BS,
-                 (tile0 * kTileTokens) / BS, lane);
-
-        // Two-deep load pipeline over the piece's tiles 0 .. n-1 (buffers a
-        // and b alternate).  The steady-state loop issues both of its loads
-        // unconditionally, so while one buffer is processed the other's
-        // eight loads stay in flight (a load issued on some paths only would
-        // force the wait counters to drain it).  Only the sequence's last
-        // tile can be partial, and it is never inside the loop.
-        const int n = ntile;
-        const bool tail = piece_end == seg_t1 && (ctx % kTileTokens) != 0;
-        auto fetch = [&](Tile<KV>& x, int j) {
-            const size_t o = tile_bytes<BS>(ids, tile0 + j, row_bytes, lane);
-            load_tile(x, kbase + o, vbase + o, voff);
-        };
-        auto finish = [&](const Tile<KV>& x, int j) {
-            if (tail && j == n - 1)
-                process_tile<KV, G, true>(st, x, qv, c, row, ctx - (tile0 + j) * kTileTokens);
-            else
-                process_tile<KV, G, false>(st, x, qv, c, row, kTileTokens);
-        };
-        Tile<KV> a, b;
-        fetch(a, 0);
-        if (n == 1) {
-            finish(a, 0);
-        } else {
-            fetch(b, 1);
-            int j = 0;
-            for (; j + 3 < n; j += 2) {  // tiles j + 2 and j + 3 exist and are full
-                process_tile<KV, G, false>(st, a, qv, c, row, kTileTokens);
-                fetch(a, j + 2);
-                process_tile<KV, G, false>(st, b, qv, c, row, kTileTokens);
-                fetch(b, j + 3);
-                // Eight waves stream their heads with nothing else tying them
-                // together, and two share each SIMD: left alone they drift
-                // tens of microseconds apart and the last ones finish alone,
-                // at half the loads in flight.  A barrier per tile pair keeps
-                // them in step (it waits for no load).  Four waves per
-                // workgroup, whose math is the tighter limit, do better
-                // without it.
-                if (max_waves_per_worker<G>() == 8) __syncthreads();
-            }
-            // two or three tiles left: j (in a), j + 1 (in b), maybe j + 2
-            process_tile<KV, G, false>(st, a, qv, c, row, kTileTokens);
-            if (n - j == 3) {
-                fetch(a, j + 2);
-                process_tile<KV, G, false>(st, b, qv, c, row, kTileTokens);
-                finish(a, j + 2);
-            } else {
-                finish(b, j + 1);
-            }
-        }
-
-        // Merge the row streams: M = max m_r, l = sum l_r 2^(m_r - M),
-        // acc = sum acc_r 2^(m_r - M).  A row that saw no token has
-        // m = kNegBig, l = 0, acc = 0 and drops out.
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float mx = st.m[g];
-#pragma unroll
-            for (int o = L::kRowLanes; o < 64; o <<= 1) mx = fmaxf(mx, xor_lane(mx, o));
-            const float f = fast_exp2(st.m[g] - mx);
-            float lt = st.l[g] * f;
-#pragma unroll
-            for (int o = L::kRowLanes; o < 64; o <<= 1) lt += xor_lane(lt, o);
-#pragma unroll
-            for (int d = 0; d < ND; ++d) {
-                float x = st.acc[g][d] * f;
-#pragma unroll
-                for (int o = L::kRowLanes; o < 64; o <<= 1) x += xor_lane(x, o);
-                st.acc[g][d] = x;
-            }
-            st.m[g] = mx;
-            st.l[g] = lt;
-        }
-
-        const bool whole = (t == seg_t0) && (piece_end == seg_t1);
-        const int slot = first_piece ? 0 : 1;
-        // which workers hold a sequence's first and last tiles (and the
-        // record slot of the first), for the merge kernel
-        if (tid == 0 && blockIdx.y == 0) {
-            if (t == seg_t0) seq_workers[seq] = (int32_t)w | (slot << 30);
-            if (piece_end == seg_t1) seq_workers[num_seqs + seq] = (int32_t)w;
-        }
-        // Row r stores heads g = r, r + kRows, ...
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            if (g % L::kRows != row) continue;
-            if (whole) {
-                const float inv = out_scale / st.l[g];
-#pragma unroll
-                for (int w8 = 0; w8 < ND / 8; ++w8) {
-                    float o[8];
-#pragma unroll
-                    for (int d = 0; d < 8; ++d) o[d] = st.acc[g][8 * w8 + d] * inv;
-                    store8<OUT_BF16>(out, head_row + (size_t)g * D + col * ND + 8 * w8, o);
-                }
-            } else {
-                float* r = rec + ((size_t)(w * 2 + slot) * num_q_heads + (size_t)kvh * G + g) * kRecStride;
-                float4* pa = reinterpret_cast<float4*>(r + col * ND);
-#pragma unroll
-                for (int w4 = 0; w4 < ND / 4; ++w4)
-                    pa[w4] = make_float4(st.acc[g][4 * w4], st.acc[g][4 * w4 + 1],
-                                         st.acc[g][4 * w4 + 2], st.acc[g][4 * w4 + 3]);
-                if (col == 0) {
-                    r[D] = st.m[g];
-                    r[D + 1] = st.l[g];
-                }
-            }
-        }
-        first_piece = false;
-        t = piece_end;
-    }
+    extern __shared__ int32_t s_cum[];
+    __shared__ int32_t s_part[max_waves_per_worker<G>()];
+    decode_worker<KV, BS, G, OUT_BF16, max_waves_per_worker<G>()>(
+        out, rec, seq_workers, q, k_cache, v_cache, block_table, max_blocks_per_seq,
+        context_lens, max_context_len, num_seqs, num_q_heads, num_kv_heads, scale_log2, out_scale,
+        num_workers, cu_q_lens, s_cum, s_part, blockIdx.x, blockIdx.y);
 }
 
 // Finishes every (sequence, query head): zero rows for empty contexts, and
@@ -795,11 +131,7 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
                        a.out_scale, (int)workers, a.cu_q_lens);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 mgrid((a.num_q_heads + 3) / 4, a.num_seqs);
-    hipLaunchKernelGGL((decode_merge_kernel<OUT_BF16>), mgrid, dim3(256), 0, stream, a.out,
-                       a.records, a.seq_workers, a.context_lens, a.max_context_len, a.num_seqs,
-                       a.num_q_heads, a.out_scale, a.cu_q_lens);
-    return hipGetLastError();
+    return launch_decode_merge(a, stream);
 }
 
 template <typename KV, int BS, int G>
@@ -883,6 +215,19 @@ size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, i
     const size_t cum = ((size_t)2 * num_seqs * sizeof(int32_t) + 255) / 256 * 256;
     return cum + (size_t)decode_max_workers(num_seqs, max_context_len) * 2 * num_q_heads *
                      kRecStride * sizeof(float);
+}
+
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
+    dim3 mgrid((a.num_q_heads + 3) / 4, a.num_seqs);
+    if (a.out_bf16)
+        hipLaunchKernelGGL((decode_merge_kernel<true>), mgrid, dim3(256), 0, stream, a.out,
+                           a.records, a.seq_workers, a.context_lens, a.max_context_len,
+                           a.num_seqs, a.num_q_heads, a.out_scale, a.cu_q_lens);
+    else
+        hipLaunchKernelGGL((decode_merge_kernel<false>), mgrid, dim3(256), 0, stream, a.out,
+                           a.records, a.seq_workers, a.context_lens, a.max_context_len,
+                           a.num_seqs, a.num_q_heads, a.out_scale, a.cu_q_lens);
+    return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {

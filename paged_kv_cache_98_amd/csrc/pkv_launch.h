@@ -102,6 +102,13 @@ hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_kv_append_fp8(const AppendFp8Args& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// The log-sum-exp merge of the decode rows shared by several workers (the
+// second kernel of launch_decode, on its own after launch_mixed).
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
+// A mixed batch in one grid: the chunks' MFMA items and the decode rows'
+// stream-K workers co-resident on the CUs, then the decode merge.  Returns
+// hipErrorNotSupported (nothing launched) for calls it does not take.
+hipError_t launch_mixed(const PrefillArgs& a, const DecodeArgs& d, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 // A prefill call whose chunks fit one workgroup (2 <= max_q_len and

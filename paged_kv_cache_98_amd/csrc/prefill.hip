@@ -52,6 +52,7 @@
 // sequence-axis parallelism of "Flash Attention v2 的改进").
 #include <type_traits>
 
+#include "decode_core.h"
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -574,6 +575,53 @@ __device__ __forceinline__ void chunk_item(
 }
 
 
+// Query slot `slot` of KV head kvh in a grid of num_q_tokens / P + num_seqs
+// slots per KV head, P = 128 / G query positions each: slot y belongs to
+// sequence i with T(i) <= y < T(i + 1), T(i) = cu_q_lens[i] / P + i (T never
+// skips a needed slot), and holds its rows (y - T(i)) P onwards; runs all
+// its key tiles, or nothing for a slot past its chunk's rows or (with the
+// decode rows taken elsewhere) of a single-row sequence.
+template <int BS, int G, bool OUT_BF16, bool FP8>
+__device__ __forceinline__ void run_slot(
+    uint16_t (&s_ks)[2][kKsElems], uint16_t (&s_vt)[2][kVtElems], void* __restrict__ out,
+    const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q_lens,
+    const void* __restrict__ k_cache, const void* __restrict__ v_cache,
+    const int32_t* __restrict__ block_table, int max_blocks_per_seq,
+    const int32_t* __restrict__ context_lens, int max_context_len, int num_seqs,
+    int num_q_heads, int num_kv_heads, float scale_log2, float out_scale, int causal,
+    int decode_rows_elsewhere, const uint64_t* __restrict__ tree_mask, int kvh, int slot) {
+    constexpr int P = kCols / G;
+    const int lane = threadIdx.x & 63;
+    // ---- which sequence owns this slot: 64-way search over T(i)
+    int lo = 0, hi = num_seqs;  // T(lo) <= slot < T(hi), T(num_seqs) = grid size
+    while (hi - lo > 1) {
+        const int step = (hi - lo + 63) / 64;
+        const int idx = lo + lane * step;
+        const bool ok = idx < hi && (cu_q_lens[idx] / P + idx) <= slot;
+        const unsigned long long m = __ballot(ok);  // low bits set, lane 0 always
+        const int last = 63 - __builtin_clzll(m);
+        lo = lo + last * step;
+        const int nh = lo + step;
+        hi = nh < hi ? nh : hi;
+    }
+    const int seq = lo;
+    const int q_begin = cu_q_lens[seq];
+    const int lq = cu_q_lens[seq + 1] - q_begin;
+    const int r0 = (slot - (q_begin / P + seq)) * P;
+    if (r0 >= lq) return;
+    if (decode_rows_elsewhere && lq == 1) return;
+    int ctx = context_lens[seq];
+    ctx = ctx < 0 ? 0 : (ctx > max_context_len ? max_context_len : ctx);
+    const int pos0 = ctx - lq;
+    const int r_last = (r0 + P < lq ? r0 + P : lq) - 1;
+    const int kv_end = causal ? (pos0 + r_last + 1 < ctx ? pos0 + r_last + 1 : ctx) : ctx;
+    chunk_item<BS, G, OUT_BF16, FP8>(s_ks, s_vt, out, q, k_cache, v_cache,
+                                     block_table + (size_t)seq * max_blocks_per_seq, num_q_heads,
+                                     num_kv_heads, scale_log2, out_scale, causal, tree_mask,
+                                     q_begin, lq, ctx, kvh, r0, 0, (kv_end + kKT - 1) / kKT,
+                                     nullptr);
+}
+
 // Grid: (num_q_tokens / P + num_seqs, num_kv_heads), P = 128 / G query
 // positions per workgroup, remapped XCD by XCD; block 256.  Slot y of
 // sequence i is y - T(i),
@@ -661,35 +709,60 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
     }
     const int kvh = item / gridDim.x;
     const int slot = item - kvh * gridDim.x;
+    run_slot<BS, G, OUT_BF16, FP8>(s_ks, s_vt, out, q, cu_q_lens, k_cache, v_cache, block_table,
+                                   max_blocks_per_seq, context_lens, max_context_len, num_seqs,
+                                   num_q_heads, num_kv_heads, scale_log2, out_scale, causal,
+                                   decode_rows_elsewhere, tree_mask, kvh, slot);
+}
 
-    // ---- which sequence owns this slot: 64-way search over T(i)
-    int lo = 0, hi = num_seqs;  // T(lo) <= slot < T(hi), T(num_seqs) = grid size
-    while (hi - lo > 1) {
-        const int step = (hi - lo + 63) / 64;
-        const int idx = lo + lane * step;
-        const bool ok = idx < hi && (cu_q_lens[idx] / P + idx) <= slot;
-        const unsigned long long m = __ballot(ok);  // low bits set, lane 0 always
-        const int last = 63 - __builtin_clzll(m);
-        lo = lo + last * step;
-        const int nh = lo + step;
-        hi = nh < hi ? nh : hi;
+// A mixed batch in one grid ("LLM 推理优化技术全景", Chunked Prefill,
+// decode-maximal batching: the compute-bound chunk and the bandwidth-bound
+// decodes share the machine).  The dispatcher deals workgroups to the 8 XCDs
+// in turn and, inside an XCD, to its CUs in turn, two per CU; so the first
+// dec_per_xcd workgroups of each XCD's run are decode workers (stream-K
+// ranges over the decode rows' keys, one head group of up to 4 KV heads
+// each) and take one slot on every CU, and the rest are the chunks' query
+// slots, an XCD-contiguous run each (as prefill_mfma_kernel deals them),
+// which take the other slot and every slot freed later.  The decode workers'
+// partial results are merged by the decode merge kernel afterwards.
+// LDS: the chunk path's K / V^T tile buffers; a decode worker keeps its tile
+// prefix sums in them instead.
+template <int BS, int G, bool OUT_BF16, bool FP8>
+__global__ void __launch_bounds__(kThreads, 2)
+mixed_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
+             const int32_t* __restrict__ cu_q_lens, const void* __restrict__ k_cache,
+             const void* __restrict__ v_cache, const int32_t* __restrict__ block_table,
+             int max_blocks_per_seq, const int32_t* __restrict__ context_lens,
+             int max_context_len, int num_seqs, int num_q_heads, int num_kv_heads,
+             float scale_log2, float out_scale, int causal, float* __restrict__ dec_rec,
+             int32_t* __restrict__ dec_seq_workers, int dec_workers, int dec_groups,
+             int dec_per_xcd, int num_slots, int chunk_per_xcd,
+             const uint64_t* __restrict__ tree_mask) {
+    __shared__ __attribute__((aligned(16))) uint16_t s_ks[2][kKsElems];
+    __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kVtElems];
+    const int b = blockIdx.x;
+    const int xcd = b % 8;
+    const int k = b / 8;
+    if (k < dec_per_xcd) {
+        const int d = xcd * dec_per_xcd + k;
+        if (d >= dec_workers * dec_groups) return;
+        int32_t* s_cum = reinterpret_cast<int32_t*>(&s_ks[0][0]);
+        int32_t* s_part = reinterpret_cast<int32_t*>(&s_vt[0][0]);
+        using KV = std::conditional_t<FP8, std::conditional_t<(G <= 4), dec::KvFp8Wide, dec::KvFp8>,
+                                      dec::KvBf16>;
+        dec::decode_worker<KV, BS, G, OUT_BF16, kThreads / 64>(
+            out, dec_rec, dec_seq_workers, q, k_cache, v_cache, block_table, max_blocks_per_seq,
+            context_lens, max_context_len, num_seqs, num_q_heads, num_kv_heads, scale_log2,
+            out_scale, dec_workers, cu_q_lens, s_cum, s_part, d % dec_workers, d / dec_workers);
+        return;
     }
-    const int seq = lo;
-    const int q_begin = cu_q_lens[seq];
-    const int lq = cu_q_lens[seq + 1] - q_begin;
-    const int r0 = (slot - (q_begin / P + seq)) * P;
-    if (r0 >= lq) return;
-    if (decode_rows_elsewhere && lq == 1) return;
-    int ctx = context_lens[seq];
-    ctx = ctx < 0 ? 0 : (ctx > max_context_len ? max_context_len : ctx);
-    const int pos0 = ctx - lq;
-    const int r_last = (r0 + P < lq ? r0 + P : lq) - 1;
-    const int kv_end = causal ? (pos0 + r_last + 1 < ctx ? pos0 + r_last + 1 : ctx) : ctx;
-    chunk_item<BS, G, OUT_BF16, FP8>(s_ks, s_vt, out, q, k_cache, v_cache,
-                                     block_table + (size_t)seq * max_blocks_per_seq, num_q_heads,
-                                     num_kv_heads, scale_log2, out_scale, causal, tree_mask,
-                                     q_begin, lq, ctx, kvh, r0, 0, (kv_end + kKT - 1) / kKT,
-                                     nullptr);
+    const int item = xcd * chunk_per_xcd + (k - dec_per_xcd);
+    if (k - dec_per_xcd >= chunk_per_xcd || item >= num_slots * num_kv_heads) return;
+    const int kvh = item / num_slots;
+    run_slot<BS, G, OUT_BF16, FP8>(s_ks, s_vt, out, q, cu_q_lens, k_cache, v_cache, block_table,
+                                   max_blocks_per_seq, context_lens, max_context_len, num_seqs,
+                                   num_q_heads, num_kv_heads, scale_log2, out_scale, causal,
+                                   1, tree_mask, kvh, item - kvh * num_slots);
 }
 
 // Stream-K units of sequence i in a call of chunks that fit one workgroup
@@ -1029,6 +1102,65 @@ hipError_t launch_prefill_bs(const PrefillArgs& a, hipStream_t s) {
     }
 }
 
+// Workgroups of the mixed grid's decode role: one per CU (the other slot
+// takes the chunks' query slots).
+constexpr int kMixedDecodePerXcd = 32;
+
+template <int BS, int G, bool OUT_BF16, bool FP8>
+hipError_t launch_mixed_t(const PrefillArgs& a, const DecodeArgs& d, hipStream_t stream) {
+    constexpr int P = kCols / G;
+    auto kern = mixed_kernel<BS, G, OUT_BF16, FP8>;
+    int resident = 0, cus = 0, dev = 0;
+    hipError_t e = resident_workgroups(reinterpret_cast<const void*>(kern), kThreads, 0,
+                                       &resident);
+    if (e == hipSuccess) e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    // the layout the role split assumes: 8 XCDs of kMixedDecodePerXcd CUs
+    // holding two workgroups each, and the decode's prefix sums in the tile
+    // buffers
+    if (cus != 8 * kMixedDecodePerXcd || resident != 2 * cus ||
+        (int64_t)(a.num_seqs + 1) * (int64_t)sizeof(int32_t) > (int64_t)sizeof(uint16_t) * 2 * kKsElems)
+        return hipErrorNotSupported;
+    const int dec_groups = (a.num_kv_heads + 3) / 4;
+    int64_t dec_workers = (8 * kMixedDecodePerXcd) / dec_groups;
+    if (dec_workers > d.max_workers) dec_workers = d.max_workers;
+    if (dec_workers < 1) dec_workers = 1;
+    const int dec_per_xcd = (int)((dec_workers * dec_groups + 7) / 8);
+    const int num_slots = a.num_q_tokens / P + a.num_seqs;
+    const int chunk_per_xcd = (num_slots * a.num_kv_heads + 7) / 8;
+    hipLaunchKernelGGL(kern, dim3(8 * (dec_per_xcd + chunk_per_xcd)), dim3(kThreads), 0, stream,
+                       a.out, a.q, a.cu_q_lens, a.k_cache, a.v_cache, a.block_table,
+                       a.max_blocks_per_seq, a.context_lens, a.max_context_len, a.num_seqs,
+                       a.num_q_heads, a.num_kv_heads, a.scale_log2, a.out_scale, a.causal ? 1 : 0,
+                       d.records, d.seq_workers, (int)dec_workers, dec_groups, dec_per_xcd,
+                       num_slots, chunk_per_xcd, a.tree_mask);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_decode_merge(d, stream);
+}
+
+template <int BS, int G>
+hipError_t launch_mixed_g(const PrefillArgs& a, const DecodeArgs& d, hipStream_t s) {
+    if (a.kv_fp8)
+        return a.out_bf16 ? launch_mixed_t<BS, G, true, true>(a, d, s)
+                          : launch_mixed_t<BS, G, false, true>(a, d, s);
+    return a.out_bf16 ? launch_mixed_t<BS, G, true, false>(a, d, s)
+                      : launch_mixed_t<BS, G, false, false>(a, d, s);
+}
+
+template <int BS>
+hipError_t launch_mixed_bs(const PrefillArgs& a, const DecodeArgs& d, hipStream_t s) {
+    switch (a.num_q_heads / a.num_kv_heads) {
+        case 1: return launch_mixed_g<BS, 1>(a, d, s);
+        case 2: return launch_mixed_g<BS, 2>(a, d, s);
+        case 4: return launch_mixed_g<BS, 4>(a, d, s);
+        case 8: return launch_mixed_g<BS, 8>(a, d, s);
+        case 16: return launch_mixed_g<BS, 16>(a, d, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
 bool prefill_streamk(int max_q_len, int group) {
@@ -1047,6 +1179,10 @@ size_t prefill_streamk_bytes(int num_seqs, int max_q_len, int group, int num_kv_
     const size_t cum = ((size_t)(num_seqs + 1) * sizeof(int32_t) + 255) / 256 * 256;
     return cum + (size_t)prefill_streamk_max_workers(num_seqs, num_kv_heads, max_context_len) *
                      2 * max_q_len * group * kRecStride * sizeof(float);
+}
+
+hipError_t launch_mixed(const PrefillArgs& a, const DecodeArgs& d, hipStream_t stream) {
+    return a.block_size == 16 ? launch_mixed_bs<16>(a, d, stream) : launch_mixed_bs<32>(a, d, stream);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
