@@ -70,13 +70,22 @@ constexpr int kKT = 64;          // keys per K/V tile
 constexpr int kCols = 128;       // query columns per workgroup
 constexpr int kThreads = 256;    // 4 waves
 constexpr int kKsStride = D + 8;      // bf16 elements per K row in LDS (272 B)
-// V^T rows in LDS: 64 keys + 8 fp16 of padding (144 B), with the sixteen
-// 4-key groups of row d stored at group index g ^ vt_swizzle(d).  With
-// both, the staging stores (four bytes, two keys of one dim per lane) and
-// the MFMA operand reads (eight bytes, four keys per lane) each touch every
-// bank equally often.
+// V^T rows in LDS: 64 keys + 8 fp16 of padding (144 B).  A row's keys sit
+// in eight 16-byte units of 8 keys: unit u = 4 kb + 2 ks + h holds keys
+// 32 kb + 16 ks + 4 h .. + 3 and then 32 kb + 16 ks + 8 + 4 h .. + 3 -- the
+// eight keys, in the order the S accumulator hands them to P^T, that MFMA
+// lane half h reads for k-step ks of half tile kb, so each A operand is one
+// 16-byte read.  Unit u of row d is stored at slot u ^ vt_swizzle(d).  With
+// the 144-byte pitch the operand reads (16 bytes per lane, consecutive rows)
+// and the staging stores (8 bytes per lane: 4 keys of one dim) each touch
+// every bank equally often.
 constexpr int kVtStride = kKT + 8;
-__device__ __forceinline__ int vt_swizzle(int d) { return (d >> 3) & 15; }
+__device__ __forceinline__ int vt_swizzle(int d) { return (d >> 3) & 7; }
+// element index of key k (0 .. 63) of dim d in a V^T tile
+__device__ __forceinline__ int vt_index(int d, int k) {
+    const int u = 4 * (k >> 5) + 2 * ((k >> 4) & 1) + ((k >> 2) & 1);
+    return d * kVtStride + 8 * (u ^ vt_swizzle(d)) + 4 * ((k >> 3) & 1) + (k & 3);
+}
 constexpr int kKsElems = kKT * kKsStride;
 constexpr int kVtElems = D * kVtStride;
 
@@ -106,17 +115,29 @@ struct PrefillIds {
 };
 
 // Global -> register staging of one 64-key tile: K chunks (4 x 16 B) and V
-// chunks (2 key pairs x 2 halves of the tile, 4 x 16 B) per thread.
+// chunks (4 consecutive keys, 8 dims each) per thread.
 struct Stage {
     uint4 k[4];
     uint4 v[4];
 };
 
+// The V part of a thread's staging: 8 dims 8 vc .. 8 vc + 7 of the four
+// consecutive keys vkey .. vkey + 3, all inside the wave's 16-key group
+// (vkey = 16 wave + 8 vhalf + 4 vh).  The lane bits are dealt so that the
+// 16 lanes of each quarter wave store 16 different 8-byte slots of the
+// banks: lane bits 0-2 and 4 give vc, bit 3 gives vhalf, bit 5 vh.
+struct VStageMap {
+    int vc, vhalf, vh;
+    __device__ __forceinline__ explicit VStageMap(int lane)
+        : vc((lane & 7) | (((lane >> 4) & 1) << 3)), vhalf((lane >> 3) & 1), vh((lane >> 5) & 1) {}
+    __device__ __forceinline__ int key(int wave) const { return 16 * wave + 8 * vhalf + 4 * vh; }
+};
+
 // This thread's byte offsets inside a block for its staging loads: row
 // within the block times the row pitch, plus its 16-byte chunk of the head's
-// 256 bytes.  K load i carries key k0 + kq + 16 i, V load 2 j + p key
-// k0 + 2 kq + p + 32 j; k0 is a multiple of 64, hence of the block size, so
-// the offsets are the same for every tile.
+// 256 bytes.  K load i carries key k0 + kq + 16 i, V load i key
+// k0 + vkey + i; k0 is a multiple of 64, hence of the block size, so the
+// offsets are the same for every tile.
 template <int BS>
 __device__ __forceinline__ void stage_offsets(uint32_t (&koff)[4], uint32_t (&voff)[4],
                                               uint32_t row_bytes, int tid) {
@@ -124,27 +145,24 @@ __device__ __forceinline__ void stage_offsets(uint32_t (&koff)[4], uint32_t (&vo
     const int kq = tid >> 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) koff[i] = (uint32_t)((kq + 16 * i) % BS) * row_bytes + col * 16;
+    const VStageMap vm(tid & 63);
+    const int vkey = vm.key(tid >> 6);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-            voff[2 * j + p] = (uint32_t)((2 * kq + p + 32 * j) % BS) * row_bytes + col * 16;
+    for (int i = 0; i < 4; ++i) voff[i] = (uint32_t)((vkey + i) % BS) * row_bytes + vm.vc * 16;
 }
 
 // Loads one 64-key tile into registers.  Every load of a wave reads one
-// physical block: K load i lies in the tile's 16-key group i, V load 2 j + p
-// in group 2 j + (kq >= 8), and kq = 4 wave + lane / 16 is at least 8 for
-// waves 2 and 3 only.  So the block's address is a scalar buffer base and
-// the lane offsets are the fixed ones above; keys past kv_end read zeros
-// without a memory access.  kbase / vbase point at this KV head's slice of
-// block 0 of the pools.
+// physical block: K load i lies in the tile's 16-key group i, and all V
+// loads of wave w in group w.  So the block's address is a scalar buffer
+// base and the lane offsets are the fixed ones above; keys past kv_end read
+// zeros without a memory access.  kbase / vbase point at this KV head's
+// slice of block 0 of the pools.
 template <int BS>
 __device__ __forceinline__ void stage_load(Stage& sg, PrefillIds& ids, const char* kbase,
                                            const char* vbase, int k0, int kv_end,
                                            size_t block_bytes, const uint32_t (&koff)[4],
                                            const uint32_t (&voff)[4], int tid, int lane) {
     const int kq = tid >> 4;
-    const bool upper = (tid >> 6) >= 2;  // wave-uniform: kq >= 8
     // ids of the tile's four 16-key groups, fetched in increasing order (the
     // window only moves forward)
     int id[4];
@@ -156,18 +174,16 @@ __device__ __forceinline__ void stage_load(Stage& sg, PrefillIds& ids, const cha
         const uint32_t o = k0 + kq + 16 * i < kv_end ? koff[i] : kBufferOob;
         sg.k[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0));
     }
+    // the wave's V group id, chosen with a wave-uniform index so that the
+    // resource stays in scalar registers (no waterfall loop)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int vid = wave == 0 ? id[0] : wave == 1 ? id[1] : wave == 2 ? id[2] : id[3];
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(vbase + (size_t)vid * block_bytes);
+    const int vkey = k0 + VStageMap(lane).key(wave);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        // the id is wave-uniform (upper is); readfirstlane lets the compiler
-        // keep the resource in scalar registers instead of a waterfall loop
-        const int vid = __builtin_amdgcn_readfirstlane(upper ? id[2 * j + 1] : id[2 * j]);
-        const __amdgpu_buffer_rsrc_t r = buffer_rsrc(vbase + (size_t)vid * block_bytes);
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const uint32_t o = k0 + 2 * kq + p + 32 * j < kv_end ? voff[2 * j + p] : kBufferOob;
-            sg.v[2 * j + p] =
-                __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0));
-        }
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t o = vkey + i < kv_end ? voff[i] : kBufferOob;
+        sg.v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0));
     }
 }
 
@@ -185,24 +201,25 @@ __device__ __forceinline__ void stage_store(const Stage& sg, uint16_t* __restric
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         *reinterpret_cast<uint4*>(ks + (kq + 16 * i) * kKsStride + col * 8) = sg.k[i];
-    // V^T[dim][key] as fp16 pairs of adjacent keys: keys 2 kq + 32 j and
-    // the next one are in group kq / 2 + 8 j at offset 2 (kq % 2); this
-    // thread's dims 8 col .. 8 col + 7 all have swizzle col, so the group
-    // lands at (kq / 2 ^ col) ^ 8 j
-    uint16_t* vcol = vt + col * 8 * kVtStride + 4 * ((kq / 2) ^ col) + 2 * (kq % 2);
+    // V^T[dim][key] in fp16: dim 8 vc + w gets this thread's four keys as
+    // one 8-byte store, at the same slot of each of its 8 rows (their
+    // swizzle is vc & 7)
+    const int lane = tid & 63;
+    const VStageMap vm(lane);
+    const int vkey = vm.key(tid >> 6);
+    uint16_t* vrow = vt + vt_index(8 * vm.vc, vkey);
+    const uint32_t w0[4] = {sg.v[0].x, sg.v[0].y, sg.v[0].z, sg.v[0].w};
+    const uint32_t w1[4] = {sg.v[1].x, sg.v[1].y, sg.v[1].z, sg.v[1].w};
+    const uint32_t w2[4] = {sg.v[2].x, sg.v[2].y, sg.v[2].z, sg.v[2].w};
+    const uint32_t w3[4] = {sg.v[3].x, sg.v[3].y, sg.v[3].z, sg.v[3].w};
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const uint4 a = sg.v[2 * j];
-        const uint4 b = sg.v[2 * j + 1];
-        const uint32_t wa[4] = {a.x, a.y, a.z, a.w};
-        const uint32_t wb[4] = {b.x, b.y, b.z, b.w};
-        // XOR with 8 j flips bit 3 of the group index: +-32 fp16
-        uint16_t* vj = vcol + (j == 0 ? 0 : (((kq / 2) ^ col) & 8 ? -32 : 32));
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            *reinterpret_cast<uint32_t*>(vj + (2 * w) * kVtStride) = pack_f16x2(bf16_lo(wa[w]), bf16_lo(wb[w]));
-            *reinterpret_cast<uint32_t*>(vj + (2 * w + 1) * kVtStride) = pack_f16x2(bf16_hi(wa[w]), bf16_hi(wb[w]));
-        }
+    for (int w = 0; w < 4; ++w) {
+        *reinterpret_cast<uint2*>(vrow + (2 * w) * kVtStride) =
+            make_uint2(pack_f16x2(bf16_lo(w0[w]), bf16_lo(w1[w])),
+                       pack_f16x2(bf16_lo(w2[w]), bf16_lo(w3[w])));
+        *reinterpret_cast<uint2*>(vrow + (2 * w + 1) * kVtStride) =
+            make_uint2(pack_f16x2(bf16_hi(w0[w]), bf16_hi(w1[w])),
+                       pack_f16x2(bf16_hi(w2[w]), bf16_hi(w3[w])));
     }
 }
 
@@ -276,9 +293,8 @@ __device__ __forceinline__ void stage_store_fp8(const StageFp8& sg, uint16_t* __
         *reinterpret_cast<uint4*>(row) = make_uint4(b[0], b[1], b[2], b[3]);
         *reinterpret_cast<uint4*>(row + 8) = make_uint4(b[4], b[5], b[6], b[7]);
     }
-    // V^T: keys 2 kq and 2 kq + 1 are the pair at offset 2 (kq % 2) of
-    // 4-key group kq / 2; dim d = 16 col + 4 j + e takes the fp16 pair
-    // (key 2 kq, key 2 kq + 1), its group stored at (kq / 2) ^ swizzle(d)
+    // V^T: dim d = 16 col + 4 j + e takes the fp16 pair (key 2 kq,
+    // key 2 kq + 1), adjacent in the row's layout
     const uint32_t a[4] = {sg.v[0].x, sg.v[0].y, sg.v[0].z, sg.v[0].w};
     const uint32_t c[4] = {sg.v[1].x, sg.v[1].y, sg.v[1].z, sg.v[1].w};
 #pragma unroll
@@ -293,8 +309,7 @@ __device__ __forceinline__ void stage_store_fp8(const StageFp8& sg, uint16_t* __
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int d = 16 * col + 4 * j + e;
-            *reinterpret_cast<uint32_t*>(vt + d * kVtStride + 4 * ((kq >> 1) ^ vt_swizzle(d)) +
-                                         2 * (kq & 1)) = __builtin_bit_cast(uint32_t, vp[e]);
+            *reinterpret_cast<uint32_t*>(vt + vt_index(d, 2 * kq)) = __builtin_bit_cast(uint32_t, vp[e]);
         }
     }
 }
@@ -448,9 +463,13 @@ __device__ __forceinline__ void chunk_item(
     }
     __syncthreads();
 
-    // this lane's part of its V^T operand addresses (see the PV loop)
-    const int vt_lo = (lane & 31) * kVtStride + 4 * (h ^ ((lane & 31) >> 3));
-    const int vt_hi = (lane & 31) * kVtStride + 4 * ((h ^ ((lane & 31) >> 3)) ^ 2);
+    // this lane's part of its V^T operand addresses, per k-step (see the PV
+    // loop): row L = lane % 32 of the 32-row block, unit 4 kb + 2 ks + h at
+    // slot (4 kb + 2 ks + h) ^ ((4 mb + L / 8) & 7); the bits of L / 8 give
+    // the lane's part, kb ^ (mb & 1) a constant
+    const int l3 = (lane & 31) >> 3;
+    const int vt_ks0 = (lane & 31) * kVtStride + 16 * (l3 >> 1) + 8 * (h ^ (l3 & 1));
+    const int vt_ks1 = (lane & 31) * kVtStride + 16 * (1 ^ (l3 >> 1)) + 8 * (h ^ (l3 & 1));
     // One 64-key tile: load the next tile (NEXT), the tile in two 32-key
     // halves -- each S^T = K . Q^T (the first k-step adds to an inline zero),
     // online softmax, then O^T += V^T . P^T with A = V^T rows (dims) and the
@@ -489,15 +508,9 @@ __device__ __forceinline__ void chunk_item(
 #pragma unroll
                 for (int mb = 0; mb < 4; ++mb) {
                     // keys 16 ks + 4 h .. + 3 and 16 ks + 8 + 4 h .. + 3 of the
-                    // half are groups g = 8 kb + 4 ks + h and g + 2 of row
-                    // d = 32 mb + L, swizzle 4 mb + L / 8: the lane's part
-                    // (h ^ L / 8, and that ^ 2) is in vt_lo / vt_hi, the rest
-                    // is a constant offset
-                    const int cg = 4 * ((2 * kb + ks) ^ mb);
-                    const uint16_t* vrow = s_vt[buf] + 32 * mb * kVtStride + 4 * cg;
-                    const uint2 lo4 = *reinterpret_cast<const uint2*>(vrow + vt_lo);
-                    const uint2 hi4 = *reinterpret_cast<const uint2*>(vrow + vt_hi);
-                    const f16x8_t a = __builtin_bit_cast(f16x8_t, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
+                    // half: unit 4 kb + 2 ks + h of row d = 32 mb + L
+                    const uint16_t* vrow = s_vt[buf] + 32 * mb * kVtStride + 32 * (kb ^ (mb & 1));
+                    const f16x8_t a = *reinterpret_cast<const f16x8_t*>(vrow + (ks ? vt_ks1 : vt_ks0));
                     o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[ks], o[mb], 0, 0, 0);
                 }
             }
