@@ -112,6 +112,21 @@ struct PrefillIds {
         }
         return __builtin_amdgcn_readlane(cur, blk - base);
     }
+    // ids of the four 16-key groups of the 64-key tile at k0.  The window
+    // starts at the block of a tile's first key and moves by 64 blocks, so a
+    // tile's 4 (or 2) blocks never straddle it and one move check serves
+    // all four (tiles are visited in increasing order).
+    template <int BS>
+    __device__ __forceinline__ void tile(int k0, int lane, int (&id)[4]) {
+        const int blk0 = k0 / BS;
+        while (blk0 >= base + 64) {
+            cur = nxt;
+            base += 64;
+            nxt = base + 64 + lane < nblk ? row[base + 64 + lane] : 0;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) id[i] = __builtin_amdgcn_readlane(cur, (k0 + 16 * i) / BS - base);
+    }
 };
 
 // Global -> register staging of one 64-key tile: K chunks (4 x 16 B) and V
@@ -157,7 +172,7 @@ __device__ __forceinline__ void stage_offsets(uint32_t (&koff)[4], uint32_t (&vo
 // base and the lane offsets are the fixed ones above; keys past kv_end read
 // zeros without a memory access.  kbase / vbase point at this KV head's
 // slice of block 0 of the pools.
-template <int BS>
+template <int BS, bool CHECK>
 __device__ __forceinline__ void stage_load(Stage& sg, PrefillIds& ids, const char* kbase,
                                            const char* vbase, int k0, int kv_end,
                                            size_t block_bytes, const uint32_t (&koff)[4],
@@ -166,12 +181,11 @@ __device__ __forceinline__ void stage_load(Stage& sg, PrefillIds& ids, const cha
     // ids of the tile's four 16-key groups, fetched in increasing order (the
     // window only moves forward)
     int id[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) id[i] = ids.get((k0 + 16 * i) / BS, lane);
+    ids.tile<BS>(k0, lane, id);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const __amdgpu_buffer_rsrc_t r = buffer_rsrc(kbase + (size_t)id[i] * block_bytes);
-        const uint32_t o = k0 + kq + 16 * i < kv_end ? koff[i] : kBufferOob;
+        const uint32_t o = !CHECK || k0 + kq + 16 * i < kv_end ? koff[i] : kBufferOob;
         sg.k[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0));
     }
     // the wave's V group id, chosen with a wave-uniform index so that the
@@ -182,7 +196,7 @@ __device__ __forceinline__ void stage_load(Stage& sg, PrefillIds& ids, const cha
     const int vkey = k0 + VStageMap(lane).key(wave);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t o = vkey + i < kv_end ? voff[i] : kBufferOob;
+        const uint32_t o = !CHECK || vkey + i < kv_end ? voff[i] : kBufferOob;
         sg.v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0));
     }
 }
@@ -249,7 +263,7 @@ __device__ __forceinline__ void stage_offsets_fp8(uint32_t (&koff)[4], uint32_t 
 
 // A wave's K load i lies in the tile's 16-key group wave / 2 + 2 i and its V
 // loads in group `wave` (t / 8 = 8 wave + lane / 8), one physical block each.
-template <int BS>
+template <int BS, bool CHECK>
 __device__ __forceinline__ void stage_load_fp8(StageFp8& sg, PrefillIds& ids, const char* kbase,
                                                const char* vbase, int k0, int kv_end,
                                                size_t block_bytes, const uint32_t (&koff)[4],
@@ -257,20 +271,19 @@ __device__ __forceinline__ void stage_load_fp8(StageFp8& sg, PrefillIds& ids, co
     const int kq = tid >> 3;
     const int wave = tid >> 6;
     int id[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) id[i] = ids.get((k0 + 16 * i) / BS, lane);
+    ids.tile<BS>(k0, lane, id);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int kid = __builtin_amdgcn_readfirstlane(id[(wave >> 1) + 2 * i]);
         const __amdgpu_buffer_rsrc_t r = buffer_rsrc(kbase + (size_t)kid * block_bytes);
-        const uint32_t o = k0 + kq + 32 * i < kv_end ? koff[i] : kBufferOob;
+        const uint32_t o = !CHECK || k0 + kq + 32 * i < kv_end ? koff[i] : kBufferOob;
         sg.k[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0));
     }
     const int vid = __builtin_amdgcn_readfirstlane(id[wave]);
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc(vbase + (size_t)vid * block_bytes);
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-        const uint32_t o = k0 + 2 * kq + p < kv_end ? voff[p] : kBufferOob;
+        const uint32_t o = !CHECK || k0 + 2 * kq + p < kv_end ? voff[p] : kBufferOob;
         sg.v[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0));
     }
 }
@@ -358,16 +371,25 @@ __device__ __forceinline__ void softmax_half(f32x16_t& s, f16x8_t (&pf)[2], f32x
             for (int e = 0; e < 16; ++e) o[mb][e] *= alpha;
     }
     const float mn = m_run;
-    float ls4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         float p = fast_exp2(fmaf(s[e], cl2, -mn));
         // a dropped key must give 0 even for a zero scale
         if (MASK) p = s[e] == -3.402823466e38f ? 0.0f : p;
-        ls4[e & 3] += p;
         pf[e >> 3][e & 7] = (_Float16)p;
     }
-    l_run = fmaf(l_run, alpha, (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]));
+    // the sum of the fp16 weights P V uses (so the normalised weights are
+    // those weights exactly): fp32 dot products of their pairs with (1, 1)
+    const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+    float ls2[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+            const f16x2_t pr = {pf[k][2 * q2], pf[k][2 * q2 + 1]};
+            ls2[q2 & 1] = __builtin_amdgcn_fdot2(pr, one, ls2[q2 & 1], false);
+        }
+    l_run = fmaf(l_run, alpha, ls2[0] + ls2[1]);
 }
 
 constexpr int kRecStride = D + 4;  // floats per partial record: O[128], m, l, 2 pad
@@ -444,11 +466,13 @@ __device__ __forceinline__ void chunk_item(
     PrefillIds ids;
     ids.init(bt_row, (ctx + BS - 1) / BS, t0 * kKT / BS, lane);
     using StageT = std::conditional_t<FP8, StageFp8, Stage>;
-    auto load_next = [&](StageT& x, int k0n) {
+    // check_c: whether keys of the tile may lie at or past kv_end
+    auto load_next = [&](StageT& x, int k0n, auto check_c) {
+        constexpr bool CHECK = decltype(check_c)::value;
         if constexpr (FP8)
-            stage_load_fp8<BS>(x, ids, kbase, vbase, k0n, kv_end, block_bytes, koff, voff, tid, lane);
+            stage_load_fp8<BS, CHECK>(x, ids, kbase, vbase, k0n, kv_end, block_bytes, koff, voff, tid, lane);
         else
-            stage_load<BS>(x, ids, kbase, vbase, k0n, kv_end, block_bytes, koff, voff, tid, lane);
+            stage_load<BS, CHECK>(x, ids, kbase, vbase, k0n, kv_end, block_bytes, koff, voff, tid, lane);
     };
     auto store_tile = [&](const StageT& x, int b) {
         if constexpr (FP8)
@@ -458,7 +482,7 @@ __device__ __forceinline__ void chunk_item(
     };
     StageT sg;
     if (t1 > t0) {
-        load_next(sg, t0 * kKT);
+        load_next(sg, t0 * kKT, std::true_type{});
         store_tile(sg, t0 & 1);
     }
     __syncthreads();
@@ -478,12 +502,12 @@ __device__ __forceinline__ void chunk_item(
     // this column's token-tree mask over the chunk's keys (none: all seen)
     const int tbase = tree_mask ? pos0 : 0x7fffffff;
     const uint64_t tmask = tree_mask && col_valid ? tree_mask[q_begin + r] : ~0ull;
-    auto run_tile = [&](int j, auto mask_c, bool next) {
+    auto run_tile = [&](int j, auto mask_c, bool next, auto check_c) {
         constexpr bool MASK = decltype(mask_c)::value;
         const int k0 = j * kKT;
         const int buf = j & 1;
         if (next)
-            load_next(sg, k0 + kKT);
+            load_next(sg, k0 + kKT, check_c);
         // S for both halves first, so that each half's softmax (VALU) has
         // matrix-core work in flight beside it: the second half's S during
         // the first softmax, the first half's P V during the second
@@ -531,7 +555,7 @@ __device__ __forceinline__ void chunk_item(
     if (r0 + (wave * 32) / G >= lq) {
         for (int jj = t0; jj < t1; ++jj) {
             if (jj + 1 < t1) {
-                load_next(sg, (jj + 1) * kKT);
+                load_next(sg, (jj + 1) * kKT, std::true_type{});
                 store_tile(sg, (jj + 1) & 1);
             }
             __syncthreads();
@@ -545,9 +569,13 @@ __device__ __forceinline__ void chunk_item(
     const int j_tail = ctx >= kKT ? (ctx - kKT) / kKT + 1 : 0;
     int j_plain = j_diag < j_tail ? j_diag : j_tail;
     j_plain = j_plain < t1 - 1 ? j_plain : t1 - 1;
+    // A tile before j_plain lies wholly before kv_end (it ends before the
+    // first query position and the context's end), so while the next tile
+    // is one of those its loads need no bounds check.
     int j = t0;
-    for (; j < j_plain; ++j) run_tile(j, std::false_type{}, true);
-    for (; j < t1; ++j) run_tile(j, std::true_type{}, j + 1 < t1);
+    for (; j < j_plain - 1; ++j) run_tile(j, std::false_type{}, true, std::false_type{});
+    for (; j < j_plain; ++j) run_tile(j, std::false_type{}, true, std::true_type{});
+    for (; j < t1; ++j) run_tile(j, std::true_type{}, j + 1 < t1, std::true_type{});
 
     // ---- finish: total l over both halves, then out = O / l
     const float lt = l_run + xor_lane(l_run, 32);
