@@ -82,6 +82,18 @@ __device__ __forceinline__ float xor_lane(float x, int mask) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(x)));
 }
 
+// Max / sum of x over lanes l and l ^ 32, with gfx950's 32-lane swap (a
+// VALU exchange; the LDS crossbar is not involved).  Each lane ends up with
+// both halves' values, so the symmetric reductions need no lane select.
+__device__ __forceinline__ float max_lane_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_lane_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {

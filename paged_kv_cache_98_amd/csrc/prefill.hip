@@ -70,17 +70,22 @@ constexpr int kKT = 64;          // keys per K/V tile
 constexpr int kCols = 128;       // query columns per workgroup
 constexpr int kThreads = 256;    // 4 waves
 constexpr int kKsStride = D + 8;      // bf16 elements per K row in LDS (272 B)
-// V^T rows in LDS: 64 keys + 8 fp16 of padding (144 B).  A row's keys sit
+// V^T rows in LDS: 64 keys + 16 fp16 of padding (160 B).  A row's keys sit
 // in eight 16-byte units of 8 keys: unit u = 4 kb + 2 ks + h holds keys
 // 32 kb + 16 ks + 4 h .. + 3 and then 32 kb + 16 ks + 8 + 4 h .. + 3 -- the
 // eight keys, in the order the S accumulator hands them to P^T, that MFMA
 // lane half h reads for k-step ks of half tile kb, so each A operand is one
-// 16-byte read.  Unit u of row d is stored at slot u ^ vt_swizzle(d).  With
-// the 144-byte pitch the operand reads (16 bytes per lane, consecutive rows)
-// and the staging stores (8 bytes per lane: 4 keys of one dim) each touch
-// every bank equally often.
-constexpr int kVtStride = kKT + 8;
-__device__ __forceinline__ int vt_swizzle(int d) { return (d >> 3) & 7; }
+// 16-byte read.  Unit u of row d is stored at slot u ^ vt_swizzle(d).  The
+// pitch and the swizzle were chosen by measuring the LDS bank-conflict
+// counter for the exact access patterns of the operand reads and the
+// staging stores (the 64 four-byte banks do not serve the lanes of a wave
+// in any simple grouping): with a 160-byte pitch and a swizzle constant
+// over 16 rows the operand reads run at the conflict-free rate and the
+// 8-byte staging stores at half of it; a 144-byte pitch halves the reads'
+// rate too, a 192-byte one is conflict-free for both but does not leave
+// room for two workgroups per CU.
+constexpr int kVtStride = kKT + 16;
+__device__ __forceinline__ int vt_swizzle(int d) { return (d >> 4) & 7; }
 // element index of key k (0 .. 63) of dim d in a V^T tile
 __device__ __forceinline__ int vt_index(int d, int k) {
     const int u = 4 * (k >> 5) + 2 * ((k >> 4) & 1) + ((k >> 2) & 1);
@@ -217,7 +222,7 @@ __device__ __forceinline__ void stage_store(const Stage& sg, uint16_t* __restric
         *reinterpret_cast<uint4*>(ks + (kq + 16 * i) * kKsStride + col * 8) = sg.k[i];
     // V^T[dim][key] in fp16: dim 8 vc + w gets this thread's four keys as
     // one 8-byte store, at the same slot of each of its 8 rows (their
-    // swizzle is vc & 7)
+    // swizzle is vc / 2)
     const int lane = tid & 63;
     const VStageMap vm(lane);
     const int vkey = vm.key(tid >> 6);
@@ -355,7 +360,7 @@ __device__ __forceinline__ void softmax_half(f32x16_t& s, f16x8_t (&pf)[2], f32x
         mt4[e & 3] = fmaxf(mt4[e & 3], s[e]);
     }
     float mt = fmaxf(fmaxf(mt4[0], mt4[1]), fmaxf(mt4[2], mt4[3]));
-    mt = fmaxf(mt, xor_lane(mt, 32)) * cl2;
+    mt = max_lane_halves(mt) * cl2;
     // Lazy reference maximum: m_run moves only when a score exceeds it by
     // more than kLazyMax (log2 units), so p = 2^(s - m_run) stays below
     // 2^kLazyMax (far inside fp16) and O and l are rescaled only on those
@@ -487,13 +492,11 @@ __device__ __forceinline__ void chunk_item(
     }
     __syncthreads();
 
-    // this lane's part of its V^T operand addresses, per k-step (see the PV
-    // loop): row L = lane % 32 of the 32-row block, unit 4 kb + 2 ks + h at
-    // slot (4 kb + 2 ks + h) ^ ((4 mb + L / 8) & 7); the bits of L / 8 give
-    // the lane's part, kb ^ (mb & 1) a constant
-    const int l3 = (lane & 31) >> 3;
-    const int vt_ks0 = (lane & 31) * kVtStride + 16 * (l3 >> 1) + 8 * (h ^ (l3 & 1));
-    const int vt_ks1 = (lane & 31) * kVtStride + 16 * (1 ^ (l3 >> 1)) + 8 * (h ^ (l3 & 1));
+    // this lane's part of its V^T operand addresses (see the PV loop): row
+    // L = lane % 32 of the 32-row block mb, unit 4 kb + 2 ks + h at slot
+    // (4 kb + 2 ks + h) ^ (2 mb + L / 16): bit 0 of the slot is h ^ L / 16,
+    // the lane's part; bits 1 and 2 are constants
+    const int vt_lane = (lane & 31) * kVtStride + 8 * (h ^ ((lane & 31) >> 4));
     // One 64-key tile: load the next tile (NEXT), the tile in two 32-key
     // halves -- each S^T = K . Q^T (the first k-step adds to an inline zero),
     // online softmax, then O^T += V^T . P^T with A = V^T rows (dims) and the
@@ -524,20 +527,27 @@ __device__ __forceinline__ void chunk_item(
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+            // the half's eight V^T operands, read before its softmax so the
+            // LDS latency hides behind it: keys 16 ks + 4 h .. + 3 and
+            // 16 ks + 8 + 4 h .. + 3 of the half, unit 4 kb + 2 ks + h of
+            // row d = 32 mb + L
+            f16x8_t va[2][4];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb) {
+                    const uint16_t* vrow = s_vt[buf] + 32 * mb * kVtStride + 32 * (kb ^ (mb >> 1)) +
+                                           16 * (ks ^ (mb & 1));
+                    va[ks][mb] = *reinterpret_cast<const f16x8_t*>(vrow + vt_lane);
+                }
             f16x8_t pf[2];  // P^T fragments, keys 16 ks .. 16 ks + 15 of the half
             softmax_half<MASK>(sc[kb], pf, o, m_run, l_run, cl2, k0 + 32 * kb, h, pos, ctx, diag,
                                tmask, tbase);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
+            for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb) {
-                    // keys 16 ks + 4 h .. + 3 and 16 ks + 8 + 4 h .. + 3 of the
-                    // half: unit 4 kb + 2 ks + h of row d = 32 mb + L
-                    const uint16_t* vrow = s_vt[buf] + 32 * mb * kVtStride + 32 * (kb ^ (mb & 1));
-                    const f16x8_t a = *reinterpret_cast<const f16x8_t*>(vrow + (ks ? vt_ks1 : vt_ks0));
-                    o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[ks], o[mb], 0, 0, 0);
-                }
-            }
+                for (int mb = 0; mb < 4; ++mb)
+                    o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[ks][mb], pf[ks], o[mb], 0, 0, 0);
         }
         if (next) store_tile(sg, buf ^ 1);
         __syncthreads();
@@ -578,7 +588,7 @@ __device__ __forceinline__ void chunk_item(
     for (; j < t1; ++j) run_tile(j, std::true_type{}, j + 1 < t1, std::true_type{});
 
     // ---- finish: total l over both halves, then out = O / l
-    const float lt = l_run + xor_lane(l_run, 32);
+    const float lt = sum_lane_halves(l_run);
     if (!col_valid) return;
     if (rec_col) {  // part of the item's keys: the record of this column
         float* rp = rec_col;
