@@ -632,16 +632,17 @@ __device__ __forceinline__ void chunk_item(
 // skips a needed slot), and holds its rows (y - T(i)) P onwards; runs all
 // its key tiles, or nothing for a slot past its chunk's rows or (with the
 // decode rows taken elsewhere) of a single-row sequence.
-template <int BS, int G, bool OUT_BF16, bool FP8>
-__device__ __forceinline__ void run_slot(
-    uint16_t (&s_ks)[2][kKsElems], uint16_t (&s_vt)[2][kVtElems], void* __restrict__ out,
-    const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q_lens,
-    const void* __restrict__ k_cache, const void* __restrict__ v_cache,
-    const int32_t* __restrict__ block_table, int max_blocks_per_seq,
-    const int32_t* __restrict__ context_lens, int max_context_len, int num_seqs,
-    int num_q_heads, int num_kv_heads, float scale_log2, float out_scale, int causal,
-    int decode_rows_elsewhere, const uint64_t* __restrict__ tree_mask, int kvh, int slot) {
-    constexpr int P = kCols / G;
+// The sequence and rows of query slot `slot` (P positions per slot): false
+// for a slot with nothing to do.  Wave-uniform; every wave of the block
+// takes the same decision.
+struct SlotRows {
+    int seq, q_begin, lq, r0, ctx, ntiles;
+};
+template <int P>
+__device__ __forceinline__ bool slot_rows(SlotRows& sr, const int32_t* __restrict__ cu_q_lens,
+                                          const int32_t* __restrict__ context_lens,
+                                          int max_context_len, int num_seqs, int causal,
+                                          int decode_rows_elsewhere, int slot) {
     const int lane = threadIdx.x & 63;
     // ---- which sequence owns this slot: 64-way search over T(i)
     int lo = 0, hi = num_seqs;  // T(lo) <= slot < T(hi), T(num_seqs) = grid size
@@ -655,22 +656,94 @@ __device__ __forceinline__ void run_slot(
         const int nh = lo + step;
         hi = nh < hi ? nh : hi;
     }
-    const int seq = lo;
-    const int q_begin = cu_q_lens[seq];
-    const int lq = cu_q_lens[seq + 1] - q_begin;
-    const int r0 = (slot - (q_begin / P + seq)) * P;
-    if (r0 >= lq) return;
-    if (decode_rows_elsewhere && lq == 1) return;
-    int ctx = context_lens[seq];
-    ctx = ctx < 0 ? 0 : (ctx > max_context_len ? max_context_len : ctx);
-    const int pos0 = ctx - lq;
-    const int r_last = (r0 + P < lq ? r0 + P : lq) - 1;
-    const int kv_end = causal ? (pos0 + r_last + 1 < ctx ? pos0 + r_last + 1 : ctx) : ctx;
+    sr.seq = lo;
+    sr.q_begin = cu_q_lens[lo];
+    sr.lq = cu_q_lens[lo + 1] - sr.q_begin;
+    sr.r0 = (slot - (sr.q_begin / P + lo)) * P;
+    if (sr.r0 >= sr.lq) return false;
+    if (decode_rows_elsewhere && sr.lq == 1) return false;
+    int ctx = context_lens[lo];
+    sr.ctx = ctx < 0 ? 0 : (ctx > max_context_len ? max_context_len : ctx);
+    const int pos0 = sr.ctx - sr.lq;
+    const int r_last = (sr.r0 + P < sr.lq ? sr.r0 + P : sr.lq) - 1;
+    const int kv_end = causal ? (pos0 + r_last + 1 < sr.ctx ? pos0 + r_last + 1 : sr.ctx) : sr.ctx;
+    sr.ntiles = (kv_end + kKT - 1) / kKT;
+    return true;
+}
+
+template <int BS, int G, bool OUT_BF16, bool FP8>
+__device__ __forceinline__ void run_slot(
+    uint16_t (&s_ks)[2][kKsElems], uint16_t (&s_vt)[2][kVtElems], void* __restrict__ out,
+    const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q_lens,
+    const void* __restrict__ k_cache, const void* __restrict__ v_cache,
+    const int32_t* __restrict__ block_table, int max_blocks_per_seq,
+    const int32_t* __restrict__ context_lens, int max_context_len, int num_seqs,
+    int num_q_heads, int num_kv_heads, float scale_log2, float out_scale, int causal,
+    int decode_rows_elsewhere, const uint64_t* __restrict__ tree_mask, int kvh, int slot) {
+    SlotRows sr;
+    if (!slot_rows<kCols / G>(sr, cu_q_lens, context_lens, max_context_len, num_seqs, causal,
+                              decode_rows_elsewhere, slot))
+        return;
     chunk_item<BS, G, OUT_BF16, FP8>(s_ks, s_vt, out, q, k_cache, v_cache,
-                                     block_table + (size_t)seq * max_blocks_per_seq, num_q_heads,
+                                     block_table + (size_t)sr.seq * max_blocks_per_seq, num_q_heads,
                                      num_kv_heads, scale_log2, out_scale, causal, tree_mask,
-                                     q_begin, lq, ctx, kvh, r0, 0, (kv_end + kKT - 1) / kKT,
-                                     nullptr);
+                                     sr.q_begin, sr.lq, sr.ctx, kvh, sr.r0, 0, sr.ntiles, nullptr);
+}
+
+// The position, inside an XCD's run of (KV head, slot) items
+// [run0, run0 + cnt) of a (slots, KV heads) grid, of the item whose rank by
+// key tiles (descending, ties by position) is `want`.  LDS scratch:
+// 2 num_seqs + 2 + cnt ints; every thread of the block calls it, and the
+// scratch is free again when it returns.
+template <int P, int NT>
+__device__ __forceinline__ int ranked_item(int* scratch, const int32_t* __restrict__ cu_q_lens,
+                                           const int32_t* __restrict__ context_lens,
+                                           int max_context_len, int num_seqs, int causal,
+                                           int decode_rows_elsewhere, int run0, int cnt, int want) {
+    const int tid = threadIdx.x;
+    int* s_cu = scratch;  // cu_q_lens, context_lens, works, pick
+    int* s_ctx = s_cu + num_seqs + 1;
+    int* s_w = s_ctx + num_seqs;
+    int* s_pick = s_w + cnt;
+    for (int i = tid; i <= num_seqs; i += NT) {
+        s_cu[i] = cu_q_lens[i];
+        if (i < num_seqs) s_ctx[i] = context_lens[i];
+    }
+    __syncthreads();
+    for (int t = tid; t < cnt; t += NT) {
+        const int sl = (run0 + t) % (int)gridDim.x;
+        int lo = 0, hi = num_seqs;  // the last i with T(i) = cu_q_lens[i] / P + i <= sl
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_cu[mid] / P + mid <= sl) lo = mid; else hi = mid;
+        }
+        const int lq = s_cu[lo + 1] - s_cu[lo];
+        const int r0 = (sl - (s_cu[lo] / P + lo)) * P;
+        int work = 0;
+        if (r0 < lq && !(decode_rows_elsewhere && lq == 1)) {
+            int ctx = s_ctx[lo];
+            ctx = ctx < 0 ? 0 : (ctx > max_context_len ? max_context_len : ctx);
+            const int r_last = (r0 + P < lq ? r0 + P : lq) - 1;
+            const int kv_end = causal ? (ctx - lq + r_last + 1 < ctx ? ctx - lq + r_last + 1 : ctx)
+                                      : ctx;
+            work = (kv_end + kKT - 1) / kKT;
+        }
+        s_w[t] = work;
+    }
+    __syncthreads();
+    for (int t = tid; t < cnt; t += NT) {
+        const int wt = s_w[t];
+        int rank = 0;
+        for (int u = 0; u < cnt; ++u) {
+            const int wu = s_w[u];
+            rank += (wu > wt || (wu == wt && u < t)) ? 1 : 0;
+        }
+        if (rank == want) *s_pick = t;
+    }
+    __syncthreads();
+    const int pick = *s_pick;
+    __syncthreads();  // the scratch goes back to its owner
+    return pick;
 }
 
 // Grid: (num_q_tokens / P + num_seqs, num_kv_heads), P = 128 / G query
@@ -712,51 +785,12 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
         // each CU holds a heavy and a light item; the rest follow in order.
         // A permutation of the run (ties by position), so still a bijection.
         const int cnt = per + (xcd < rem ? 1 : 0);
-        int* s_cu = reinterpret_cast<int*>(&s_ks[0][0]);  // cu_q_lens, context_lens, works
-        int* s_ctx = s_cu + num_seqs + 1;
-        int* s_w = s_ctx + num_seqs;
-        int* s_pick = s_w + cnt;
-        for (int i = tid; i <= num_seqs; i += kThreads) {
-            s_cu[i] = cu_q_lens[i];
-            if (i < num_seqs) s_ctx[i] = context_lens[i];
-        }
-        __syncthreads();
-        for (int t = tid; t < cnt; t += kThreads) {
-            const int sl = (run0 + t) % (int)gridDim.x;
-            int lo = 0, hi = num_seqs;  // the last i with T(i) = cu_q_lens[i] / P + i <= sl
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (s_cu[mid] / P + mid <= sl) lo = mid; else hi = mid;
-            }
-            const int lq = s_cu[lo + 1] - s_cu[lo];
-            const int r0 = (sl - (s_cu[lo] / P + lo)) * P;
-            int work = 0;
-            if (r0 < lq && !(decode_rows_elsewhere && lq == 1)) {
-                int ctx = s_ctx[lo];
-                ctx = ctx < 0 ? 0 : (ctx > max_context_len ? max_context_len : ctx);
-                const int r_last = (r0 + P < lq ? r0 + P : lq) - 1;
-                const int kv_end = causal ? (ctx - lq + r_last + 1 < ctx ? ctx - lq + r_last + 1 : ctx)
-                                          : ctx;
-                work = (kv_end + kKT - 1) / kKT;
-            }
-            s_w[t] = work;
-        }
-        __syncthreads();
         const int p = lin / 8;
         const int m = cnt < 2 * pair_cus ? cnt : 2 * pair_cus;
         const int want = p < pair_cus ? p : (p < m ? m + pair_cus - 1 - p : p);
-        for (int t = tid; t < cnt; t += kThreads) {
-            const int wt = s_w[t];
-            int rank = 0;
-            for (int u = 0; u < cnt; ++u) {
-                const int wu = s_w[u];
-                rank += (wu > wt || (wu == wt && u < t)) ? 1 : 0;
-            }
-            if (rank == want) *s_pick = t;
-        }
-        __syncthreads();
-        item = run0 + *s_pick;
-        __syncthreads();  // the LDS goes back to the K tiles
+        item = run0 + ranked_item<P, kThreads>(reinterpret_cast<int*>(&s_ks[0][0]), cu_q_lens,
+                                               context_lens, max_context_len, num_seqs, causal,
+                                               decode_rows_elsewhere, run0, cnt, want);
     }
     const int kvh = item / gridDim.x;
     const int slot = item - kvh * gridDim.x;
