@@ -2,6 +2,8 @@
 // kernel (the worker of decode_core.h over a grid of persistent workgroups),
 // the log-sum-exp merge of sequences shared by several workers, and the
 // launchers.
+#include <type_traits>
+
 #include "decode_core.h"
 
 namespace pkv {
@@ -140,21 +142,23 @@ hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s) {
                       : launch_decode_t<KV, BS, G, false>(a, s);
 }
 
-template <typename KV, int BS>
-hipError_t launch_decode_bs(const DecodeArgs& a, hipStream_t s) {
+// bf16 pools: P V on fp16 dot products over token pairs where it is most of
+// the tile's VALU work (8 and 16 query heads per KV head) and the compiled
+// loop keeps its schedule: with 32-token blocks the 70B-shaped batch went
+// from 382 to 351 us per call; with 16-token blocks the same source
+// compiled to a loop with three times the hazard waits (s_nop) between
+// its DPP row sums and ran 3.5 % slower, so those keep fp32 FMAs.
+template <int BS>
+hipError_t launch_decode_bf16_bs(const DecodeArgs& a, hipStream_t s) {
+    using Wide = std::conditional_t<BS == 32, KvBf16Paired, KvBf16>;
     switch (a.num_q_heads / a.num_kv_heads) {
-        case 1: return launch_decode_g<KV, BS, 1>(a, s);
-        case 2: return launch_decode_g<KV, BS, 2>(a, s);
-        case 4: return launch_decode_g<KV, BS, 4>(a, s);
-        case 8: return launch_decode_g<KV, BS, 8>(a, s);
-        case 16: return launch_decode_g<KV, BS, 16>(a, s);
+        case 1: return launch_decode_g<KvBf16, BS, 1>(a, s);
+        case 2: return launch_decode_g<KvBf16, BS, 2>(a, s);
+        case 4: return launch_decode_g<KvBf16, BS, 4>(a, s);
+        case 8: return launch_decode_g<Wide, BS, 8>(a, s);
+        case 16: return launch_decode_g<Wide, BS, 16>(a, s);
         default: return hipErrorInvalidValue;
     }
-}
-
-template <typename KV>
-hipError_t launch_decode_kv(const DecodeArgs& a, hipStream_t s) {
-    return a.block_size == 16 ? launch_decode_bs<KV, 16>(a, s) : launch_decode_bs<KV, 32>(a, s);
 }
 
 // FP8 pools: the wide layout (16 dims per lane) up to 4 query heads per KV
@@ -234,7 +238,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     if (a.kv_fp8)
         return a.block_size == 16 ? launch_decode_fp8_bs<16>(a, stream)
                                   : launch_decode_fp8_bs<32>(a, stream);
-    return launch_decode_kv<KvBf16>(a, stream);
+    return a.block_size == 16 ? launch_decode_bf16_bs<16>(a, stream)
+                              : launch_decode_bf16_bs<32>(a, stream);
 }
 
 }  // namespace pkv

@@ -82,6 +82,29 @@ struct KvBf16 {
     }
 };
 
+// bf16 pools with P V on fp16 dot products over token pairs, as the FP8
+// pools below: for every dim the values of a lane's tokens i and i + 1 are
+// widened to floats and rounded to one fp16 pair (exact for |v| in
+// [2^-14, 65504], the fp16 normal range; smaller magnitudes keep an
+// absolute error below 2^-25), and P rounds to fp16 once per query head, so
+// one v_dot2_f32_f16 does the work of two fp32 FMAs.  Worth it where P V
+// dominates the tile's VALU work (8 and 16 query heads per KV head).
+struct KvBf16Paired : KvBf16 {
+    static constexpr bool kPairedPV = true;
+    // vp[e] = (value of token a, value of token b) at dim 4 j + e: words
+    // 2 j and 2 j + 1 of each token hold dims 4 j .. 4 j + 3
+    static __device__ __forceinline__ void v_pairs4(const Word& a, const Word& b, int j,
+                                                    f16x2_t (&vp)[4]) {
+        const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
+        const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+        const uint32_t a0 = aw[2 * j], a1 = aw[2 * j + 1], b0 = bw[2 * j], b1 = bw[2 * j + 1];
+        vp[0] = f16x2_t{(_Float16)bf16_lo(a0), (_Float16)bf16_lo(b0)};
+        vp[1] = f16x2_t{(_Float16)bf16_hi(a0), (_Float16)bf16_hi(b0)};
+        vp[2] = f16x2_t{(_Float16)bf16_lo(a1), (_Float16)bf16_lo(b1)};
+        vp[3] = f16x2_t{(_Float16)bf16_hi(a1), (_Float16)bf16_hi(b1)};
+    }
+};
+
 // FP8 codes in the OCP E4M3 format, decoded by the hardware conversions.
 // Their P V runs on fp16 dot products over token pairs: a lane's tokens i
 // and i + 1 give, for every dim, the pair (v_i, v_i+1) (a byte permute puts
