@@ -152,7 +152,7 @@ size_t pkv_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_head
  *   out[i, h, :] = sum_t softmax_t(scale * <q[i,h], K_i[t]>) V_i[t]
  * with K_i, V_i the KV head h / G rows of sequence i reached through its
  * block table.  fp32 accumulation throughout.  With 8 or 16 query heads per
- * KV head and 32-token blocks, P V takes the values of two keys at a time as
+ * KV head, P V takes the values of two keys at a time as
  * an fp16 pair (exact for |v| in [2^-14, 65504]; smaller magnitudes keep an
  * absolute error below 2^-25, |v| > 65504 is outside the supported range)
  * and P in fp16 (relative error 2^-11); otherwise V and P stay fp32.

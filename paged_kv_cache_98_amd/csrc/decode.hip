@@ -2,8 +2,6 @@
 // kernel (the worker of decode_core.h over a grid of persistent workgroups),
 // the log-sum-exp merge of sequences shared by several workers, and the
 // launchers.
-#include <type_traits>
-
 #include "decode_core.h"
 
 namespace pkv {
@@ -143,20 +141,16 @@ hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s) {
 }
 
 // bf16 pools: P V on fp16 dot products over token pairs where it is most of
-// the tile's VALU work (8 and 16 query heads per KV head) and the compiled
-// loop keeps its schedule: with 32-token blocks the 70B-shaped batch went
-// from 382 to 351 us per call; with 16-token blocks the same source
-// compiled to a loop with three times the hazard waits (s_nop) between
-// its DPP row sums and ran 3.5 % slower, so those keep fp32 FMAs.
+// the tile's VALU work (8 and 16 query heads per KV head), fp32 FMAs below
+// (with 4 the batch is bound by memory and the pairs gained nothing).
 template <int BS>
 hipError_t launch_decode_bf16_bs(const DecodeArgs& a, hipStream_t s) {
-    using Wide = std::conditional_t<BS == 32, KvBf16Paired, KvBf16>;
     switch (a.num_q_heads / a.num_kv_heads) {
         case 1: return launch_decode_g<KvBf16, BS, 1>(a, s);
         case 2: return launch_decode_g<KvBf16, BS, 2>(a, s);
         case 4: return launch_decode_g<KvBf16, BS, 4>(a, s);
-        case 8: return launch_decode_g<Wide, BS, 8>(a, s);
-        case 16: return launch_decode_g<Wide, BS, 16>(a, s);
+        case 8: return launch_decode_g<KvBf16Paired, BS, 8>(a, s);
+        case 16: return launch_decode_g<KvBf16Paired, BS, 16>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -202,10 +202,10 @@ struct Layout {
     static constexpr int kLoads = kTileTokens / kRows;       // loads per lane per tile
 };
 
-template <int LANES>
-__device__ __forceinline__ float row_sum(float x) {
-    if constexpr (LANES == 16) return row_sum16(x);
-    else return row_sum8(x);
+template <int LANES, int N>
+__device__ __forceinline__ void row_sums(float (&x)[N]) {
+    if constexpr (LANES == 16) row_sums16(x);
+    else row_sums8(x);
 }
 
 template <typename KV>
@@ -248,7 +248,11 @@ __device__ __forceinline__ void process_tile(State<G, KV::kDims>& st, const Tile
     constexpr int kLoads = Layout<KV>::kLoads;
     constexpr int kRows = Layout<KV>::kRows;
     constexpr int ND = KV::kDims;
-    float s[kLoads][G];
+    // partial dot products of every (token, head), then their row sums
+    // together (a step across all of them before the next, so no DPP read
+    // waits on the instruction just before it); with 16 query heads the
+    // registers cannot hold them all, so each is summed as it is made
+    float sf[kLoads * G];
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
         uint32_t k[ND / 2];
@@ -258,8 +262,21 @@ __device__ __forceinline__ void process_tile(State<G, KV::kDims>& st, const Tile
             float d = dot2_bf16(k[0], qv[g][0], 0.0f);
 #pragma unroll
             for (int j = 1; j < ND / 2; ++j) d = dot2_bf16(k[j], qv[g][j], d);
-            s[i][g] = row_sum<Layout<KV>::kRowLanes>(d);
+            if constexpr (G <= 8) {
+                sf[i * G + g] = d;
+            } else {
+                float one[1] = {d};
+                row_sums<Layout<KV>::kRowLanes>(one);
+                sf[i * G + g] = one[0];
+            }
         }
+    }
+    if constexpr (G <= 8) row_sums<Layout<KV>::kRowLanes>(sf);
+    float s[kLoads][G];
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) s[i][g] = sf[i * G + g];
         if (PARTIAL) {
             // Tokens past the end may hold anything: they must not raise the
             // maximum (lowest finite value, so that a zero scale stays finite)

@@ -68,12 +68,37 @@ __device__ __forceinline__ float row_sum16(float x) {
     return x;
 }
 
+// row_sum16 of N independent values, one butterfly step across all of them
+// before the next: a DPP read of a register written by the VALU instruction
+// just before it needs hazard wait states, and N independent chains keep
+// the producer of each step N instructions back.
+template <int N>
+__device__ __forceinline__ void row_sums16(float (&x)[N]) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) x[n] += dpp_mov<kDppQuadXor1>(x[n]);
+#pragma unroll
+    for (int n = 0; n < N; ++n) x[n] += dpp_mov<kDppQuadXor2>(x[n]);
+#pragma unroll
+    for (int n = 0; n < N; ++n) x[n] += dpp_mov<kDppRowHalfMirror>(x[n]);
+#pragma unroll
+    for (int n = 0; n < N; ++n) x[n] += dpp_mov<kDppRowMirror>(x[n]);
+}
+
 // The same over each half row of 8 lanes (a wave seen as 8 rows of 8).
 __device__ __forceinline__ float row_sum8(float x) {
     x += dpp_mov<kDppQuadXor1>(x);
     x += dpp_mov<kDppQuadXor2>(x);
     x += dpp_mov<kDppRowHalfMirror>(x);
     return x;
+}
+template <int N>
+__device__ __forceinline__ void row_sums8(float (&x)[N]) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) x[n] += dpp_mov<kDppQuadXor1>(x[n]);
+#pragma unroll
+    for (int n = 0; n < N; ++n) x[n] += dpp_mov<kDppQuadXor2>(x[n]);
+#pragma unroll
+    for (int n = 0; n < N; ++n) x[n] += dpp_mov<kDppRowHalfMirror>(x[n]);
 }
 
 // Exchange across rows: value of lane ^ 16 / lane ^ 32 (LDS-crossbar permute).
