@@ -152,10 +152,11 @@ size_t pkv_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_head
  *   out[i, h, :] = sum_t softmax_t(scale * <q[i,h], K_i[t]>) V_i[t]
  * with K_i, V_i the KV head h / G rows of sequence i reached through its
  * block table.  fp32 accumulation throughout.  With 8 or 16 query heads per
- * KV head, P V takes the values of two keys at a time as
- * an fp16 pair (exact for |v| in [2^-14, 65504]; smaller magnitudes keep an
+ * KV head over bf16 pools the tile runs on the matrix cores: q.k as bf16 x
+ * bf16 MFMA (exact products), P V as fp16 x fp16 MFMA with V rounded to
+ * fp16 (exact for |v| in [2^-14, 65504]; smaller magnitudes keep an
  * absolute error below 2^-25, |v| > 65504 is outside the supported range)
- * and P in fp16 (relative error 2^-11); otherwise V and P stay fp32.
+ * and P in fp16 (relative error 2^-11); with 1, 2 or 4 V and P stay fp32.
  */
 int pkv_paged_decode_attn(void *out, int out_dtype, const void *q, const void *k_cache,
                           const void *v_cache, const int32_t *block_table,

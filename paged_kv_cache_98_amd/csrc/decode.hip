@@ -14,7 +14,7 @@ using namespace dec;
 // its group (all KV heads when there are at most 8, else groups of 8);
 // dynamic LDS (num_seqs + 1) int32 for the tile prefix sums.
 template <typename KV, int BS, int G, bool OUT_BF16>
-__global__ void __launch_bounds__(64 * max_waves_per_worker<G>())
+__global__ void __launch_bounds__((64 * max_waves_per_worker_kv<KV, G>()))
 decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* __restrict__ seq_workers,
                       const uint16_t* __restrict__ q, const void* __restrict__ k_cache,
                       const void* __restrict__ v_cache, const int32_t* __restrict__ block_table,
@@ -22,12 +22,15 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
                       int max_context_len, int num_seqs, int num_q_heads, int num_kv_heads,
                       float scale_log2, float out_scale, int num_workers,
                       const int32_t* __restrict__ cu_q_lens) {
+    constexpr int kWaves = max_waves_per_worker_kv<KV, G>();
     extern __shared__ int32_t s_cum[];
-    __shared__ int32_t s_part[max_waves_per_worker<G>()];
-    decode_worker<KV, BS, G, OUT_BF16, max_waves_per_worker<G>()>(
+    __shared__ int32_t s_part[kWaves];
+    // the matrix-core tile's per-wave V staging (one element otherwise)
+    __shared__ __attribute__((aligned(16))) uint16_t s_vx[KV::kMfma ? kWaves * kVxWaveElems : 8];
+    decode_worker<KV, BS, G, OUT_BF16, kWaves>(
         out, rec, seq_workers, q, k_cache, v_cache, block_table, max_blocks_per_seq,
         context_lens, max_context_len, num_seqs, num_q_heads, num_kv_heads, scale_log2, out_scale,
-        num_workers, cu_q_lens, s_cum, s_part, blockIdx.x, blockIdx.y);
+        num_workers, cu_q_lens, s_cum, s_part, blockIdx.x, blockIdx.y, s_vx);
 }
 
 // Finishes every (sequence, query head): zero rows for empty contexts, and
@@ -108,7 +111,7 @@ decode_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
 template <typename KV, int BS, int G, bool OUT_BF16>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     auto kern = decode_streamk_kernel<KV, BS, G, OUT_BF16>;
-    constexpr int kMax = max_waves_per_worker<G>();
+    constexpr int kMax = max_waves_per_worker_kv<KV, G>();
     // head groups of kMax waves; the API admits 1..8 and 16 KV heads
     const int waves = a.num_kv_heads <= kMax ? a.num_kv_heads
                                              : (a.num_kv_heads % kMax == 0 ? kMax : 1);
@@ -140,17 +143,21 @@ hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s) {
                       : launch_decode_t<KV, BS, G, false>(a, s);
 }
 
-// bf16 pools: P V on fp16 dot products over token pairs where it is most of
-// the tile's VALU work (8 and 16 query heads per KV head), fp32 FMAs below
-// (with 4 the batch is bound by memory and the pairs gained nothing).
+// bf16 pools: the tile math on the matrix cores for 8 and 16 query heads
+// per KV head, where the VALU layout is bound by its own arithmetic
+// (70B-shaped batch, 8 heads: 334 -> 308 us per call against fp16 dot
+// products on the VALU).  Up to 4 heads the VALU tile keeps P and V in fp32
+// (errors near 1e-6 against the fp64 oracle); the matrix-core tile, with P
+// and V in fp16 (errors near 1e-4), was 2.5 % faster on the 8B-shaped batch
+// (4 heads), which did not buy that loss.
 template <int BS>
 hipError_t launch_decode_bf16_bs(const DecodeArgs& a, hipStream_t s) {
     switch (a.num_q_heads / a.num_kv_heads) {
         case 1: return launch_decode_g<KvBf16, BS, 1>(a, s);
         case 2: return launch_decode_g<KvBf16, BS, 2>(a, s);
         case 4: return launch_decode_g<KvBf16, BS, 4>(a, s);
-        case 8: return launch_decode_g<KvBf16Paired, BS, 8>(a, s);
-        case 16: return launch_decode_g<KvBf16Paired, BS, 16>(a, s);
+        case 8: return launch_decode_g<KvBf16Mfma, BS, 8>(a, s);
+        case 16: return launch_decode_g<KvBf16Mfma, BS, 16>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -67,6 +67,7 @@ struct KvBf16 {
     static constexpr int kElemBytes = 2;
     static constexpr int kDims = 8;
     static constexpr bool kPairedPV = false;
+    static constexpr bool kMfma = false;
     using Word = uint4;
     static __device__ __forceinline__ Word load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
         return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
@@ -82,28 +83,28 @@ struct KvBf16 {
     }
 };
 
-// bf16 pools with P V on fp16 dot products over token pairs, as the FP8
-// pools below: for every dim the values of a lane's tokens i and i + 1 are
-// widened to floats and rounded to one fp16 pair (exact for |v| in
-// [2^-14, 65504], the fp16 normal range; smaller magnitudes keep an
-// absolute error below 2^-25), and P rounds to fp16 once per query head, so
-// one v_dot2_f32_f16 does the work of two fp32 FMAs.  Worth it where P V
-// dominates the tile's VALU work (8 and 16 query heads per KV head).
-struct KvBf16Paired : KvBf16 {
-    static constexpr bool kPairedPV = true;
-    // vp[e] = (value of token a, value of token b) at dim 4 j + e: words
-    // 2 j and 2 j + 1 of each token hold dims 4 j .. 4 j + 3
-    static __device__ __forceinline__ void v_pairs4(const Word& a, const Word& b, int j,
-                                                    f16x2_t (&vp)[4]) {
-        const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
-        const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
-        const uint32_t a0 = aw[2 * j], a1 = aw[2 * j + 1], b0 = bw[2 * j], b1 = bw[2 * j + 1];
-        vp[0] = f16x2_t{(_Float16)bf16_lo(a0), (_Float16)bf16_lo(b0)};
-        vp[1] = f16x2_t{(_Float16)bf16_hi(a0), (_Float16)bf16_hi(b0)};
-        vp[2] = f16x2_t{(_Float16)bf16_lo(a1), (_Float16)bf16_lo(b1)};
-        vp[3] = f16x2_t{(_Float16)bf16_hi(a1), (_Float16)bf16_hi(b1)};
-    }
+// bf16 pools on the matrix cores, for 8 or 16 query heads per KV head: the
+// layout above repeats the G heads' dot products, their row sums and the
+// softmax in every lane of a row, which makes the VALU work the bound from
+// 8 heads on.  A tile of 16 tokens:
+//   S[16 tokens][16 cols] = K Q^T: four v_mfma_f32_16x16x32_bf16, K straight
+//     from HBM in the operand layout (lane l: token l % 16, dims
+//     32 kb + 8 (l / 16) .. + 7), Q^T in registers (column l % 16 is query
+//     head l % 16; columns past G are zero);
+//   lane l then holds the scores of tokens 4 (l / 16) .. + 3 of head l % 16,
+//     so the softmax takes 4 exponentials per lane, and the head's running
+//     max is shared by its 4 lanes (a max over lanes l ^ 16, l ^ 32);
+//   O[16 rows][128 dims] += P V: eight v_mfma_f32_16x16x16_f16 (one per 16
+//     dims), P in fp16 straight from the score accumulator's layout, V
+//     rounded to fp16 (exact for |v| in [2^-14, 65504]) and passed through a
+//     16 x 128 tile of LDS that each wave owns, to read it back as 4 tokens
+//     of one dim per lane.
+// Lane l holds O rows (heads) 4 (l / 16) .. + 3, dim 16 nb + l % 16.
+struct KvBf16Mfma : KvBf16 {
+    static constexpr bool kMfma = true;
 };
+constexpr int kVxStride = kHeadDim + 8;         // fp16 per token row of a wave's V tile
+constexpr int kVxWaveElems = kTileTokens * kVxStride;
 
 // FP8 codes in the OCP E4M3 format, decoded by the hardware conversions.
 // Their P V runs on fp16 dot products over token pairs: a lane's tokens i
@@ -117,6 +118,7 @@ struct KvFp8Base {
     static constexpr int kElemBytes = 1;
     static constexpr int kDims = 4 * NWORDS;
     static constexpr bool kPairedPV = true;
+    static constexpr bool kMfma = false;
     template <bool HIGH>  // codes 2, 3 of the word instead of 0, 1
     static __device__ __forceinline__ uint32_t bf16_pair(uint32_t codes) {
         return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(
@@ -421,12 +423,16 @@ constexpr int kMinTilesPerWorker = 4;   // fewer waves for tiny batches
 // 256 registers (two waves per SIMD), else 4.
 template <int G>
 constexpr int max_waves_per_worker() { return G <= 4 ? 8 : 4; }
+template <typename KV, int G>
+constexpr int max_waves_per_worker_kv() { return KV::kMfma ? 8 : max_waves_per_worker<G>(); }
 constexpr int64_t kMaxWorkers = 1024;    // workgroups of 8 waves an MI355X holds at most
 // Cost of a sequence boundary inside a worker's range, in quarter tiles
 // (per query heads per KV head: the tile math grows with G, the boundary's
 // round trips do not).
 template <int G>
 constexpr int64_t seq_cost() { return G <= 4 ? 6 : 16; }
+template <typename KV, int G>
+constexpr int64_t seq_cost_kv() { return KV::kMfma ? 6 : seq_cost<G>(); }
 
 __device__ __forceinline__ int clamp_ctx(int ctx, int max_context_len) {
     return ctx < 0 ? 0 : (ctx > max_context_len ? max_context_len : ctx);
@@ -500,7 +506,7 @@ __device__ __forceinline__ void decode_worker(
     int max_blocks_per_seq, const int32_t* __restrict__ context_lens, int max_context_len,
     int num_seqs, int num_q_heads, int num_kv_heads, float scale_log2, float out_scale,
     int num_workers, const int32_t* __restrict__ cu_q_lens, int32_t* __restrict__ s_cum,
-    int32_t* __restrict__ s_part, int worker, int group) {
+    int32_t* __restrict__ s_part, int worker, int group, uint16_t* __restrict__ s_vx = nullptr) {
     constexpr int D = kHeadDim;
     const int tid = threadIdx.x;
     const int nthr = blockDim.x;  // at most NWAVES waves
@@ -557,7 +563,7 @@ __device__ __forceinline__ void decode_worker(
     // Worker wi starts at the first tile t with cost(t) >= wi * total / W,
     // cost(t) = 4 t + kSeqCost * seq(t); the sequence is found among the
     // costs of the sequences' first tiles.
-    constexpr int64_t kSeqCost = seq_cost<G>();
+    constexpr int64_t kSeqCost = seq_cost_kv<KV, G>();
     const int64_t cost_total = 4 * U + kSeqCost * (int64_t)(num_seqs - 1);
     auto range_start = [&](int64_t wi) -> int64_t {
         if (wi >= W) return U;
@@ -600,8 +606,169 @@ __device__ __forceinline__ void decode_worker(
         const int64_t piece_end = t_end < seg_t1 ? t_end : seg_t1;
         const int ntile = (int)(piece_end - t);
         const int ctx = clamp_ctx(context_lens[seq], max_context_len);
-
         const size_t head_row = ((size_t)row_of(cu_q_lens, seq) * num_q_heads + (size_t)kvh * G) * D;
+        const bool whole = (t == seg_t0) && (piece_end == seg_t1);
+        const int slot = first_piece ? 0 : 1;
+        // which workers hold a sequence's first and last tiles (and the
+        // record slot of the first), for the merge kernel
+        if (tid == 0 && group == 0) {
+            if (t == seg_t0) seq_workers[seq] = (int32_t)w | (slot << 30);
+            if (piece_end == seg_t1) seq_workers[num_seqs + seq] = (int32_t)w;
+        }
+        const int n = ntile;
+        const bool tail = piece_end == seg_t1 && (ctx % kTileTokens) != 0;
+        IdWindow ids;
+        ids.init(block_table + (size_t)seq * max_blocks_per_seq, (ctx + BS - 1) / BS,
+                 (tile0 * kTileTokens) / BS, lane);
+
+      if constexpr (KV::kMfma) {
+        typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+        typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+        typedef float f32x4_t __attribute__((ext_vector_type(4)));
+        const int r16 = lane & 15, q4 = lane >> 4;
+        // Q^T operand: column r16 = query head r16, rows = dims 32 kb + 8 q4 .. + 7
+        bf16x8_t qb[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            uint4 x = make_uint4(0, 0, 0, 0);
+            if (r16 < G) {
+                x = *reinterpret_cast<const uint4*>(q + head_row + (size_t)r16 * D + 32 * kb + 8 * q4);
+                x.x ^= neg; x.y ^= neg; x.z ^= neg; x.w ^= neg;
+            }
+            qb[kb] = __builtin_bit_cast(bf16x8_t, x);
+        }
+        f32x4_t o[8];
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) o[nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        float m = kNegBig;  // head r16's running max, the same in its 4 lanes
+        float l = 0.0f;     // sum over this lane's tokens of head r16
+        // byte offsets of token r16's chunk of k-block kb in a tile
+        uint32_t koff[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+            koff[kb] = (uint32_t)(r16 * row_bytes + ((size_t)kvh * D + 32 * kb + 8 * q4) * 2);
+        uint16_t* const vx = s_vx + (tid >> 6) * kVxWaveElems;  // this wave's V tile
+        struct MTile { uint4 k[4]; uint4 v[4]; };
+        auto ntok_of = [&](int j) { return (tail && j == n - 1) ? ctx - (tile0 + j) * kTileTokens : kTileTokens; };
+        auto fetch = [&](MTile& x, int j) {
+            const size_t o0 = tile_bytes<BS>(ids, tile0 + j, row_bytes, lane);
+            const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kbase + o0);
+            const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vbase + o0);
+            const bool valid = r16 < ntok_of(j);  // tokens past the end read zeros
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const uint32_t off = valid ? koff[kb] : kBufferOob;
+                x.k[kb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+                x.v[kb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+            }
+        };
+        auto process = [&](const MTile& x, int ntok) {
+            // V as fp16 into the wave's LDS tile, token r16, dims 32 kb + 8 q4 .. + 7
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const uint32_t wd[4] = {x.v[kb].x, x.v[kb].y, x.v[kb].z, x.v[kb].w};
+                uint32_t hv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const f16x2_t hp = {(_Float16)bf16_lo(wd[e]), (_Float16)bf16_hi(wd[e])};
+                    hv[e] = __builtin_bit_cast(uint32_t, hp);
+                }
+                *reinterpret_cast<uint4*>(vx + r16 * kVxStride + 32 * kb + 8 * q4) =
+                    make_uint4(hv[0], hv[1], hv[2], hv[3]);
+            }
+            // S = K Q^T: lane holds tokens 4 q4 .. + 3 of head r16
+            f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x.k[kb]),
+                                                             qb[kb], sc, 0, 0, 0);
+            float sv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sv[i] = (4 * q4 + i) < ntok ? sc[i] : -3.402823466e38f;
+            float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+            mt = max_lane_quads(mt) * c;
+            const float mn = fmaxf(m, mt);
+            const bool grew = mn > m;
+            const float alpha = fast_exp2(m - mn);
+            m = mn;
+            float p[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[i] = fast_exp2(fmaf(sv[i], c, -mn));
+                p[i] = (4 * q4 + i) < ntok ? p[i] : 0.0f;
+            }
+            l = fmaf(l, alpha, (p[0] + p[1]) + (p[2] + p[3]));
+            if (__any(grew)) {
+                // O row 4 q4 + i is head 4 q4 + i, whose alpha lane 4 q4 + i holds
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float ai = __shfl(alpha, 4 * q4 + i);
+#pragma unroll
+                    for (int nb = 0; nb < 8; ++nb) o[nb][i] *= ai;
+                }
+            }
+            const f16x4_t pa = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+            // V operand: tokens 4 q4 .. + 3 of dim 16 nb + r16 (the wave's own
+            // stores above are done: a wave's LDS operations run in order)
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+                const uint16_t* vc = vx + (4 * q4) * kVxStride + 16 * nb + r16;
+                const f16x4_t vb = {__builtin_bit_cast(_Float16, vc[0]),
+                                    __builtin_bit_cast(_Float16, vc[kVxStride]),
+                                    __builtin_bit_cast(_Float16, vc[2 * kVxStride]),
+                                    __builtin_bit_cast(_Float16, vc[3 * kVxStride])};
+                o[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb, o[nb], 0, 0, 0);
+            }
+        };
+        MTile a, b;
+        fetch(a, 0);
+        if (n == 1) {
+            process(a, ntok_of(0));
+        } else {
+            fetch(b, 1);
+            int j = 0;
+            for (; j + 3 < n; j += 2) {  // tiles j + 2 and j + 3 exist and are full
+                process(a, kTileTokens);
+                fetch(a, j + 2);
+                process(b, kTileTokens);
+                fetch(b, j + 3);
+                if (NWAVES == 8) __syncthreads();
+            }
+            process(a, kTileTokens);
+            if (n - j == 3) {
+                fetch(a, j + 2);
+                process(b, kTileTokens);
+                process(a, ntok_of(j + 2));
+            } else {
+                process(b, ntok_of(j + 1));
+            }
+        }
+        // ---- the piece's result: l over the head's 4 lanes; a lane's O rows
+        // are heads 4 q4 .. + 3, whose (m, l) lanes 4 q4 .. + 3 hold
+        const float lt = sum_lane_quads(l);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int h = 4 * q4 + i;
+            const float mh = __shfl(m, h);
+            const float lh = __shfl(lt, h);
+            if (h >= G) continue;
+            if (whole) {
+                const float inv = out_scale / lh;
+#pragma unroll
+                for (int nb = 0; nb < 8; ++nb)
+                    store1<OUT_BF16>(out, head_row + (size_t)h * D + 16 * nb + r16, o[nb][i] * inv);
+            } else {
+                float* r = rec + ((size_t)(w * 2 + slot) * num_q_heads + (size_t)kvh * G + h) * kRecStride;
+#pragma unroll
+                for (int nb = 0; nb < 8; ++nb) r[16 * nb + r16] = o[nb][i];
+                if (r16 == 0) {
+                    r[D] = mh;
+                    r[D + 1] = lh;
+                }
+            }
+        }
+      } else {
         uint32_t qv[G][ND / 2];  // this lane's dims of each query head, bf16 pairs
 #pragma unroll
         for (int g = 0; g < G; ++g)
@@ -621,18 +788,12 @@ __device__ __forceinline__ void decode_worker(
             for (int d = 0; d < ND; ++d) st.acc[g][d] = 0.0f;
         }
 
-        IdWindow ids;
-        ids.init(block_table + (size_t)seq * max_blocks_per_seq, (ctx + BS - 1) / BS,
-                 (tile0 * kTileTokens) / BS, lane);
-
         // Two-deep load pipeline over the piece's tiles 0 .. n-1 (buffers a
         // and b alternate).  The steady-state loop issues both of its loads
         // unconditionally, so while one buffer is processed the other's
         // eight loads stay in flight (a load issued on some paths only would
         // force the wait counters to drain it).  Only the sequence's last
         // tile can be partial, and it is never inside the loop.
-        const int n = ntile;
-        const bool tail = piece_end == seg_t1 && (ctx % kTileTokens) != 0;
         auto fetch = [&](Tile<KV>& x, int j) {
             const size_t o = tile_bytes<BS>(ids, tile0 + j, row_bytes, lane);
             load_tile(x, kbase + o, vbase + o, voff);
@@ -698,14 +859,6 @@ __device__ __forceinline__ void decode_worker(
             st.l[g] = lt;
         }
 
-        const bool whole = (t == seg_t0) && (piece_end == seg_t1);
-        const int slot = first_piece ? 0 : 1;
-        // which workers hold a sequence's first and last tiles (and the
-        // record slot of the first), for the merge kernel
-        if (tid == 0 && group == 0) {
-            if (t == seg_t0) seq_workers[seq] = (int32_t)w | (slot << 30);
-            if (piece_end == seg_t1) seq_workers[num_seqs + seq] = (int32_t)w;
-        }
         // Row r stores heads g = r, r + kRows, ...
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -732,6 +885,7 @@ __device__ __forceinline__ void decode_worker(
                 }
             }
         }
+      }
         first_piece = false;
         t = piece_end;
     }

@@ -119,6 +119,17 @@ __device__ __forceinline__ float sum_lane_halves(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Max / sum of x over lanes l, l ^ 16, l ^ 32, l ^ 48 (the same position in
+// the four 16-lane rows), with gfx950's 16- and 32-lane swaps.
+__device__ __forceinline__ float max_lane_quads(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return max_lane_halves(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float sum_lane_quads(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return sum_lane_halves(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
