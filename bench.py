@@ -91,6 +91,8 @@ TRAFFIC_SPEC = {
                                   "args": "--workload mixed_prefill"},
     "llama8b_decode_b64_fp8": {"kernels": _DECODE_K, "sources": _DECODE_SRC,
                                "args": "--workload llama8b_decode_fp8"},
+    "llama70b_decode_b256_bs16_fp8": {"kernels": _DECODE_K, "sources": _DECODE_SRC,
+                                      "args": "--workload llama70b_decode_bs16_fp8"},
     "spec_verify_b64_q6": {"kernels": _VERIFY_K, "sources": _PREFILL_SRC,
                            "args": "--workload spec_verify"},
     "spec_verify_b8_q6": {"kernels": _VERIFY_K, "sources": _PREFILL_SRC,
@@ -296,8 +298,9 @@ def workload_by_name(name):
         "llama70b_decode_bs16": lambda: W.llama70b_decode(block_size=16),
         "llama70b_decode_bs32": lambda: W.llama70b_decode(block_size=32),
         "tiny_decode": lambda: W.tiny_decode(),
-        # the 8B-shaped batch over an FP8 (E4M3) cache
+        # the 8B- and 70B-shaped batches over an FP8 (E4M3) cache
         "llama8b_decode_fp8": lambda: W.llama8b_decode(),
+        "llama70b_decode_bs16_fp8": lambda: W.llama70b_decode(block_size=16),
         # chunked prefill: the 4 x 512-query chunks alone, then with the 128
         # decodes riding along in the same call
         "prefill_chunks": lambda: W.mixed_prefill(num_decodes=0),

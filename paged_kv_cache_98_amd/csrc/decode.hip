@@ -162,18 +162,19 @@ hipError_t launch_decode_bf16_bs(const DecodeArgs& a, hipStream_t s) {
     }
 }
 
-// FP8 pools: the wide layout (16 dims per lane) up to 4 query heads per KV
-// head; with 8 or 16 its accumulators would take more registers than the
-// VALU work it saves (8: 491 VGPRs, measured 8 % slower than the narrow
-// layout), so those keep 8 dims per lane.
+// FP8 pools: the matrix-core tile at every group size.  Its P V is fp16 on
+// both paths, so it costs no accuracy; measured against the VALU tiles (16
+// dims per lane up to 4 heads, 8 dims beyond): 70B-shaped batch (8 heads)
+// 303 -> 171 us, 8B-shaped batch (4 heads) 74.6 -> 59.7 us, 1 and 2 heads
+// 2-3 % faster.
 template <int BS>
 hipError_t launch_decode_fp8_bs(const DecodeArgs& a, hipStream_t s) {
     switch (a.num_q_heads / a.num_kv_heads) {
-        case 1: return launch_decode_g<KvFp8Wide, BS, 1>(a, s);
-        case 2: return launch_decode_g<KvFp8Wide, BS, 2>(a, s);
-        case 4: return launch_decode_g<KvFp8Wide, BS, 4>(a, s);
-        case 8: return launch_decode_g<KvFp8, BS, 8>(a, s);
-        case 16: return launch_decode_g<KvFp8, BS, 16>(a, s);
+        case 1: return launch_decode_g<KvFp8Mfma, BS, 1>(a, s);
+        case 2: return launch_decode_g<KvFp8Mfma, BS, 2>(a, s);
+        case 4: return launch_decode_g<KvFp8Mfma, BS, 4>(a, s);
+        case 8: return launch_decode_g<KvFp8Mfma, BS, 8>(a, s);
+        case 16: return launch_decode_g<KvFp8Mfma, BS, 16>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

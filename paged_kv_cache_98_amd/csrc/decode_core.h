@@ -102,6 +102,25 @@ struct KvBf16 {
 // Lane l holds O rows (heads) 4 (l / 16) .. + 3, dim 16 nb + l % 16.
 struct KvBf16Mfma : KvBf16 {
     static constexpr bool kMfma = true;
+    // loads per lane and token for a tile's K (and V): 16 bytes each, load j
+    // holding the 8 dims of k-block j, dims 32 j + 8 q4 .. + 7 for the lanes
+    // of quarter q4 (64 contiguous bytes of a token per load)
+    static constexpr int kMfmaLoads = 4;
+    static __device__ __forceinline__ int mfma_dim(int kb, int q4) { return 32 * kb + 8 * q4; }
+    static __device__ __forceinline__ uint32_t mfma_byte(int j, int q4) { return 2 * mfma_dim(j, q4); }
+    // k-block kb of a token as 8 bf16 (the MFMA operand) and as 8 fp16 (the
+    // V tile's format)
+    static __device__ __forceinline__ uint4 k_bf16x8(const Word (&w)[4], int kb) { return w[kb]; }
+    static __device__ __forceinline__ uint4 v_f16x8(const Word (&w)[4], int kb) {
+        const uint32_t wd[4] = {w[kb].x, w[kb].y, w[kb].z, w[kb].w};
+        uint32_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const f16x2_t hp = {(_Float16)bf16_lo(wd[e]), (_Float16)bf16_hi(wd[e])};
+            h[e] = __builtin_bit_cast(uint32_t, hp);
+        }
+        return make_uint4(h[0], h[1], h[2], h[3]);
+    }
 };
 constexpr int kVxStride = kHeadDim + 8;         // fp16 per token row of a wave's V tile
 constexpr int kVxWaveElems = kTileTokens * kVxStride;
@@ -193,6 +212,40 @@ struct KvFp8Wide : KvFp8Base<4> {
         const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
         const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
         pairs4(aw[j], bw[j], vp);
+    }
+};
+
+// FP8 pools on the matrix cores: the tile of KvBf16Mfma, codes widened by
+// the hardware conversions to bf16 for K and fp16 for V (both exact for
+// E4M3), so the results differ from the VALU tiles' by rounding only (P in
+// fp16 there too).  A lane loads 16 codes per load, two loads per token:
+// load j of quarter q4 holds dims 64 j + 16 q4 .. + 15, and k-block kb takes
+// half kb & 1 of load kb >> 1.  The dot product does not care which dims a
+// k-block holds as long as the Q operand holds the same ones.
+struct KvFp8Mfma : KvFp8Wide {
+    static constexpr bool kMfma = true;
+    static constexpr int kMfmaLoads = 2;
+    static __device__ __forceinline__ int mfma_dim(int kb, int q4) {
+        return 64 * (kb >> 1) + 16 * q4 + 8 * (kb & 1);
+    }
+    static __device__ __forceinline__ uint32_t mfma_byte(int j, int q4) { return 64 * j + 16 * q4; }
+    static __device__ __forceinline__ uint2 half_of(const Word (&w)[2], int kb) {
+        const Word& x = w[kb >> 1];
+        return (kb & 1) ? make_uint2(x.z, x.w) : make_uint2(x.x, x.y);
+    }
+    static __device__ __forceinline__ uint4 k_bf16x8(const Word (&w)[2], int kb) {
+        const uint2 c = half_of(w, kb);
+        return make_uint4(bf16_pair<false>(c.x), bf16_pair<true>(c.x), bf16_pair<false>(c.y),
+                          bf16_pair<true>(c.y));
+    }
+    static __device__ __forceinline__ uint4 v_f16x8(const Word (&w)[2], int kb) {
+        const uint2 c = half_of(w, kb);
+        const f16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)c.x, 1.0f, false);
+        const f16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)c.x, 1.0f, true);
+        const f16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)c.y, 1.0f, false);
+        const f16x2_t e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)c.y, 1.0f, true);
+        return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                          __builtin_bit_cast(uint32_t, d), __builtin_bit_cast(uint32_t, e));
     }
 };
 
@@ -626,13 +679,13 @@ __device__ __forceinline__ void decode_worker(
         typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
         typedef float f32x4_t __attribute__((ext_vector_type(4)));
         const int r16 = lane & 15, q4 = lane >> 4;
-        // Q^T operand: column r16 = query head r16, rows = dims 32 kb + 8 q4 .. + 7
+        // Q^T operand: column r16 = query head r16, rows = the 8 dims of k-block kb
         bf16x8_t qb[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             uint4 x = make_uint4(0, 0, 0, 0);
             if (r16 < G) {
-                x = *reinterpret_cast<const uint4*>(q + head_row + (size_t)r16 * D + 32 * kb + 8 * q4);
+                x = *reinterpret_cast<const uint4*>(q + head_row + (size_t)r16 * D + KV::mfma_dim(kb, q4));
                 x.x ^= neg; x.y ^= neg; x.z ^= neg; x.w ^= neg;
             }
             qb[kb] = __builtin_bit_cast(bf16x8_t, x);
@@ -642,13 +695,14 @@ __device__ __forceinline__ void decode_worker(
         for (int nb = 0; nb < 8; ++nb) o[nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
         float m = kNegBig;  // head r16's running max, the same in its 4 lanes
         float l = 0.0f;     // sum over this lane's tokens of head r16
-        // byte offsets of token r16's chunk of k-block kb in a tile
-        uint32_t koff[4];
+        // byte offsets of token r16's loads in a tile
+        constexpr int NL = KV::kMfmaLoads;
+        uint32_t koff[NL];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-            koff[kb] = (uint32_t)(r16 * row_bytes + ((size_t)kvh * D + 32 * kb + 8 * q4) * 2);
+        for (int j = 0; j < NL; ++j)
+            koff[j] = (uint32_t)(r16 * row_bytes + (size_t)kvh * D * KV::kElemBytes + KV::mfma_byte(j, q4));
         uint16_t* const vx = s_vx + (tid >> 6) * kVxWaveElems;  // this wave's V tile
-        struct MTile { uint4 k[4]; uint4 v[4]; };
+        struct MTile { typename KV::Word k[NL]; typename KV::Word v[NL]; };
         auto ntok_of = [&](int j) { return (tail && j == n - 1) ? ctx - (tile0 + j) * kTileTokens : kTileTokens; };
         auto fetch = [&](MTile& x, int j) {
             const size_t o0 = tile_bytes<BS>(ids, tile0 + j, row_bytes, lane);
@@ -656,32 +710,23 @@ __device__ __forceinline__ void decode_worker(
             const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vbase + o0);
             const bool valid = r16 < ntok_of(j);  // tokens past the end read zeros
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const uint32_t off = valid ? koff[kb] : kBufferOob;
-                x.k[kb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-                x.v[kb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+            for (int j = 0; j < NL; ++j) {
+                const uint32_t off = valid ? koff[j] : kBufferOob;
+                x.k[j] = KV::load(rk, off);
+                x.v[j] = KV::load(rv, off);
             }
         };
         auto process = [&](const MTile& x, int ntok) {
-            // V as fp16 into the wave's LDS tile, token r16, dims 32 kb + 8 q4 .. + 7
+            // V as fp16 into the wave's LDS tile, token r16, k-block kb's dims
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const uint32_t wd[4] = {x.v[kb].x, x.v[kb].y, x.v[kb].z, x.v[kb].w};
-                uint32_t hv[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const f16x2_t hp = {(_Float16)bf16_lo(wd[e]), (_Float16)bf16_hi(wd[e])};
-                    hv[e] = __builtin_bit_cast(uint32_t, hp);
-                }
-                *reinterpret_cast<uint4*>(vx + r16 * kVxStride + 32 * kb + 8 * q4) =
-                    make_uint4(hv[0], hv[1], hv[2], hv[3]);
-            }
+            for (int kb = 0; kb < 4; ++kb)
+                *reinterpret_cast<uint4*>(vx + r16 * kVxStride + KV::mfma_dim(kb, q4)) = KV::v_f16x8(x.v, kb);
             // S = K Q^T: lane holds tokens 4 q4 .. + 3 of head r16
             f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
-                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x.k[kb]),
-                                                             qb[kb], sc, 0, 0, 0);
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, KV::k_bf16x8(x.k, kb)), qb[kb], sc, 0, 0, 0);
             float sv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)

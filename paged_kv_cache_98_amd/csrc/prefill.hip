@@ -812,7 +812,7 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
 // slot freed later.  The decode workers' partial results are merged by the
 // decode merge kernel afterwards.
 // LDS: the chunk path's K / V^T tile buffers; a decode worker keeps its tile
-// prefix sums in them instead.
+// prefix sums, its waves' V tiles and their partial sums in them instead.
 template <int BS, int G, bool OUT_BF16, bool FP8>
 __global__ void __launch_bounds__(kThreads, 2)
 mixed_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
@@ -832,14 +832,20 @@ mixed_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
     if (k < dec_per_xcd) {
         const int d = xcd * dec_per_xcd + k;
         if (d >= dec_workers * dec_groups) return;
+        // the tile policies of the decode call (dispatched in decode.hip);
+        // the waves' V tiles of the matrix-core ones, then the wave partials
+        using KV = std::conditional_t<FP8, dec::KvFp8Mfma,
+                                      std::conditional_t<(G >= 8), dec::KvBf16Mfma, dec::KvBf16>>;
+        constexpr int kVxElems = (kThreads / 64) * dec::kVxWaveElems;
+        static_assert(2 * kVxElems + 4 * (kThreads / 64) <= (int)sizeof(s_vt), "decode LDS");
         int32_t* s_cum = reinterpret_cast<int32_t*>(&s_ks[0][0]);
-        int32_t* s_part = reinterpret_cast<int32_t*>(&s_vt[0][0]);
-        using KV = std::conditional_t<FP8, std::conditional_t<(G <= 4), dec::KvFp8Wide, dec::KvFp8>,
-                                      dec::KvBf16>;
+        uint16_t* s_vx = &s_vt[0][0];
+        int32_t* s_part = reinterpret_cast<int32_t*>(s_vx + kVxElems);
         dec::decode_worker<KV, BS, G, OUT_BF16, kThreads / 64>(
             out, dec_rec, dec_seq_workers, q, k_cache, v_cache, block_table, max_blocks_per_seq,
             context_lens, max_context_len, num_seqs, num_q_heads, num_kv_heads, scale_log2,
-            out_scale, dec_workers, cu_q_lens, s_cum, s_part, d % dec_workers, d / dec_workers);
+            out_scale, dec_workers, cu_q_lens, s_cum, s_part, d % dec_workers, d / dec_workers,
+            s_vx);
         return;
     }
     const int item = xcd * chunk_per_xcd + (k - dec_per_xcd);
