@@ -223,8 +223,10 @@ int pkv_kv_append_fp8(const void *k_new, const void *v_new, const int64_t *slot_
  *   out[i, h, :] = sum_t softmax_t(scale * <q[i,h], k_scale * Kc_i[t]>) v_scale * Vc_i[t]
  * with Kc, Vc the E4M3 values of the codes.  Same arguments, workspace and
  * limits as pkv_paged_decode_attn, plus the two scales.  The codes are
- * widened in registers (K to bf16 pairs, exactly; V to fp32); accumulation
- * is fp32.  Codes of tokens past a sequence's length are never used.
+ * widened in registers, exactly: K to bf16, for q.k as bf16 x bf16 MFMA,
+ * and V to fp16, for P V as fp16 x fp16 MFMA with P in fp16 (relative error
+ * 2^-11); accumulation is fp32.  Codes of tokens past a sequence's length
+ * are never used.
  */
 int pkv_paged_decode_attn_fp8(void *out, int out_dtype, const void *q, const void *k_cache,
                               const void *v_cache, float k_scale, float v_scale,

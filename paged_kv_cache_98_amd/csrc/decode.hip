@@ -14,7 +14,7 @@ using namespace dec;
 // its group (all KV heads when there are at most 8, else groups of 8);
 // dynamic LDS (num_seqs + 1) int32 for the tile prefix sums.
 template <typename KV, int BS, int G, bool OUT_BF16>
-__global__ void __launch_bounds__((64 * max_waves_per_worker_kv<KV, G>()))
+__global__ void __launch_bounds__(64 * kMaxWavesPerWorker)
 decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* __restrict__ seq_workers,
                       const uint16_t* __restrict__ q, const void* __restrict__ k_cache,
                       const void* __restrict__ v_cache, const int32_t* __restrict__ block_table,
@@ -22,7 +22,7 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
                       int max_context_len, int num_seqs, int num_q_heads, int num_kv_heads,
                       float scale_log2, float out_scale, int num_workers,
                       const int32_t* __restrict__ cu_q_lens) {
-    constexpr int kWaves = max_waves_per_worker_kv<KV, G>();
+    constexpr int kWaves = kMaxWavesPerWorker;
     extern __shared__ int32_t s_cum[];
     __shared__ int32_t s_part[kWaves];
     // the matrix-core tile's per-wave V staging (one element otherwise)
@@ -111,7 +111,7 @@ decode_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
 template <typename KV, int BS, int G, bool OUT_BF16>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     auto kern = decode_streamk_kernel<KV, BS, G, OUT_BF16>;
-    constexpr int kMax = max_waves_per_worker_kv<KV, G>();
+    constexpr int kMax = kMaxWavesPerWorker;
     // head groups of kMax waves; the API admits 1..8 and 16 KV heads
     const int waves = a.num_kv_heads <= kMax ? a.num_kv_heads
                                              : (a.num_kv_heads % kMax == 0 ? kMax : 1);
@@ -162,16 +162,17 @@ hipError_t launch_decode_bf16_bs(const DecodeArgs& a, hipStream_t s) {
     }
 }
 
-// FP8 pools: the matrix-core tile at every group size.  Its P V is fp16 on
-// both paths, so it costs no accuracy; measured against the VALU tiles (16
-// dims per lane up to 4 heads, 8 dims beyond): 70B-shaped batch (8 heads)
-// 303 -> 171 us, 8B-shaped batch (4 heads) 74.6 -> 59.7 us, 1 and 2 heads
-// 2-3 % faster.
+// FP8 pools: the matrix-core tile from 4 query heads per KV head, whose
+// heads fill 4 of the MFMA's 16 columns or more.  Its P V is fp16 as on the
+// VALU tiles, so it costs no accuracy; measured against them: 70B-shaped
+// batch (8 heads) 303 -> 171 us, 8B-shaped batch (4 heads) 74.6 -> 59.7 us.
+// With 1 or 2 heads the columns are mostly padding and the gain was 2-3 %,
+// so those keep the VALU tile (16 dims per lane).
 template <int BS>
 hipError_t launch_decode_fp8_bs(const DecodeArgs& a, hipStream_t s) {
     switch (a.num_q_heads / a.num_kv_heads) {
-        case 1: return launch_decode_g<KvFp8Mfma, BS, 1>(a, s);
-        case 2: return launch_decode_g<KvFp8Mfma, BS, 2>(a, s);
+        case 1: return launch_decode_g<KvFp8Wide, BS, 1>(a, s);
+        case 2: return launch_decode_g<KvFp8Wide, BS, 2>(a, s);
         case 4: return launch_decode_g<KvFp8Mfma, BS, 4>(a, s);
         case 8: return launch_decode_g<KvFp8Mfma, BS, 8>(a, s);
         case 16: return launch_decode_g<KvFp8Mfma, BS, 16>(a, s);

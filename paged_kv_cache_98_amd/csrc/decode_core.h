@@ -173,25 +173,6 @@ struct KvFp8Base {
     }
 };
 
-// FP8 pools, 8 dims (8 bytes) per lane and token, rows of 16 lanes: for 8
-// and 16 query heads per KV head, whose accumulators fill the registers.
-struct KvFp8 : KvFp8Base<2> {
-    using Word = uint2;
-    static __device__ __forceinline__ Word load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-        return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-    }
-    static __device__ __forceinline__ void k_pairs(const Word& w, uint32_t (&kp)[4]) {
-        k_pairs_of({w.x, w.y}, kp);
-    }
-    static __device__ __forceinline__ void v_floats(const Word& w, float (&v)[8]) {
-        v_floats_of({w.x, w.y}, v);
-    }
-    static __device__ __forceinline__ void v_pairs4(const Word& a, const Word& b, int j,
-                                                    f16x2_t (&vp)[4]) {
-        pairs4(j == 0 ? a.x : a.y, j == 0 ? b.x : b.y, vp);
-    }
-};
-
 // FP8 pools, 16 dims (16 bytes) per lane and token, rows of 8 lanes: half
 // the lanes share a token, so the row sums take three DPP steps instead of
 // four and each softmax value is computed by 8 lanes instead of 16 (up to 4
@@ -303,10 +284,10 @@ __device__ __forceinline__ void process_tile(State<G, KV::kDims>& st, const Tile
     constexpr int kLoads = Layout<KV>::kLoads;
     constexpr int kRows = Layout<KV>::kRows;
     constexpr int ND = KV::kDims;
+    static_assert(G <= 4, "8 and 16 query heads per KV head run the matrix-core tile");
     // partial dot products of every (token, head), then their row sums
     // together (a step across all of them before the next, so no DPP read
-    // waits on the instruction just before it); with 16 query heads the
-    // registers cannot hold them all, so each is summed as it is made
+    // waits on the instruction just before it)
     float sf[kLoads * G];
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
@@ -317,16 +298,10 @@ __device__ __forceinline__ void process_tile(State<G, KV::kDims>& st, const Tile
             float d = dot2_bf16(k[0], qv[g][0], 0.0f);
 #pragma unroll
             for (int j = 1; j < ND / 2; ++j) d = dot2_bf16(k[j], qv[g][j], d);
-            if constexpr (G <= 8) {
-                sf[i * G + g] = d;
-            } else {
-                float one[1] = {d};
-                row_sums<Layout<KV>::kRowLanes>(one);
-                sf[i * G + g] = one[0];
-            }
+            sf[i * G + g] = d;
         }
     }
-    if constexpr (G <= 8) row_sums<Layout<KV>::kRowLanes>(sf);
+    row_sums<Layout<KV>::kRowLanes>(sf);
     float s[kLoads][G];
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
@@ -472,20 +447,12 @@ __device__ __forceinline__ void store1(void* out, size_t elem, float x) {
 
 constexpr int kRecStride = kHeadDim + 4;  // floats per record: acc[128], m, l, 2 pad
 constexpr int kMinTilesPerWorker = 4;   // fewer waves for tiny batches
-// KV heads (one wave each) served by one workgroup: 8 while a wave fits in
-// 256 registers (two waves per SIMD), else 4.
-template <int G>
-constexpr int max_waves_per_worker() { return G <= 4 ? 8 : 4; }
-template <typename KV, int G>
-constexpr int max_waves_per_worker_kv() { return KV::kMfma ? 8 : max_waves_per_worker<G>(); }
+// KV heads (one wave each) served by one workgroup: every tile fits a wave
+// in 256 registers, two waves per SIMD.
+constexpr int kMaxWavesPerWorker = 8;
 constexpr int64_t kMaxWorkers = 1024;    // workgroups of 8 waves an MI355X holds at most
-// Cost of a sequence boundary inside a worker's range, in quarter tiles
-// (per query heads per KV head: the tile math grows with G, the boundary's
-// round trips do not).
-template <int G>
-constexpr int64_t seq_cost() { return G <= 4 ? 6 : 16; }
-template <typename KV, int G>
-constexpr int64_t seq_cost_kv() { return KV::kMfma ? 6 : seq_cost<G>(); }
+// Cost of a sequence boundary inside a worker's range, in quarter tiles.
+constexpr int64_t kSeqCost = 6;
 
 __device__ __forceinline__ int clamp_ctx(int ctx, int max_context_len) {
     return ctx < 0 ? 0 : (ctx > max_context_len ? max_context_len : ctx);
@@ -616,7 +583,6 @@ __device__ __forceinline__ void decode_worker(
     // Worker wi starts at the first tile t with cost(t) >= wi * total / W,
     // cost(t) = 4 t + kSeqCost * seq(t); the sequence is found among the
     // costs of the sequences' first tiles.
-    constexpr int64_t kSeqCost = seq_cost_kv<KV, G>();
     const int64_t cost_total = 4 * U + kSeqCost * (int64_t)(num_seqs - 1);
     auto range_start = [&](int64_t wi) -> int64_t {
         if (wi >= W) return U;

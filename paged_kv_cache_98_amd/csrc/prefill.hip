@@ -834,7 +834,7 @@ mixed_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
         if (d >= dec_workers * dec_groups) return;
         // the tile policies of the decode call (dispatched in decode.hip);
         // the waves' V tiles of the matrix-core ones, then the wave partials
-        using KV = std::conditional_t<FP8, dec::KvFp8Mfma,
+        using KV = std::conditional_t<FP8, std::conditional_t<(G >= 4), dec::KvFp8Mfma, dec::KvFp8Wide>,
                                       std::conditional_t<(G >= 8), dec::KvBf16Mfma, dec::KvBf16>>;
         constexpr int kVxElems = (kThreads / 64) * dec::kVxWaveElems;
         static_assert(2 * kVxElems + 4 * (kThreads / 64) <= (int)sizeof(s_vt), "decode LDS");
