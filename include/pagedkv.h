@@ -236,17 +236,25 @@ int pkv_paged_decode_attn_fp8(void *out, int out_dtype, const void *q, const voi
                               float scale, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Workspace needed by pkv_paged_prefill_attn (bytes, >= 0; 0 for
- * inconsistent sizes).  Two parts, either of which may be absent: the
- * decode workspace for the batch's single-row sequences, and the part of the
- * stream-K chunk path.  That path takes calls whose chunks fit one
- * workgroup (2 <= max_q_len and max_q_len * num_q_heads / num_kv_heads <=
- * 128 query columns, as in speculative-decoding verification): its part is
- * the (num_seqs + 1) int32 unit prefix sums, 256-byte aligned, then records
- * of 132 floats for 2 * max_q_len * (num_q_heads / num_kv_heads) columns
- * of each of up to min(1024, num_seqs * num_kv_heads *
- * ceil(max_context_len / 64)) workers.  A call whose every sequence has
- * exactly max_q_len rows, more than 128 query columns per KV head, needs
+ * Workspace needed by pkv_paged_prefill_attn and its FP8 and tree variants
+ * (bytes, >= 0; 0 for inconsistent sizes), the larger of what the call's
+ * path needs over bf16 and over FP8 pools.  With C = max_q_len *
+ * (num_q_heads / num_kv_heads) query columns per KV head:
+ *  - the rows path (2 <= max_q_len <= 16 and C <= 16, or C <= 32 over FP8
+ *    pools; num_seqs <= 16383, num_kv_heads 1..8 or 16): 2 * num_seqs int32,
+ *    256-byte aligned, then records of 132 floats for
+ *    2 * max_q_len * num_q_heads columns of each of up to
+ *    min(ceil(num_seqs * ceil(max_context_len / 16) / 4), 1024,
+ *    2048 / num_kv_heads) workers;
+ *  - else two parts, either of which may be absent: the decode workspace for
+ *    the batch's single-row sequences, and the part of the stream-K chunk
+ *    path, which takes calls whose chunks fit one workgroup
+ *    (2 <= max_q_len and C <= 128): the (num_seqs + 1) int32 unit prefix
+ *    sums, 256-byte aligned, then records of 132 floats for
+ *    2 * max_q_len * (num_q_heads / num_kv_heads) columns of each of up to
+ *    min(1024, num_seqs * num_kv_heads * ceil(max_context_len / 64))
+ *    workers.
+ * A call whose every sequence has exactly max_q_len rows, C > 128, needs
  * none (workspace may be NULL).  num_q_tokens is checked for consistency.
  */
 size_t pkv_prefill_workspace_bytes(int num_seqs, int num_q_tokens, int max_q_len,
@@ -276,11 +284,15 @@ size_t pkv_prefill_workspace_bytes(int num_seqs, int num_q_tokens, int max_q_len
  * one workgroup, one grid runs them side by side on a 256-CU device (a
  * stream-K decode worker beside a chunk workgroup on every CU), then the
  * decode merge kernel; on another device the decode kernels follow the
- * chunk kernel on the same stream.  Chunks that fit one workgroup (the
- * workspace comment above) run stream-K: all (sequence, KV head, 64-key
- * tile) units cut into equal ranges over the workgroups the GPU holds at
- * once, items shared by two workers merged by a log-sum-exp fold in a
- * second kernel.  num_seqs <= 16383 and num_kv_heads in 1..8 or 16 when
+ * chunk kernel on the same stream.  Short chunks (speculative-decoding
+ * verification; the sizes of the rows path in the workspace comment above)
+ * run on the decode kernel's stream-K split and matrix-core tile, a
+ * sequence's (row, head) pairs the columns of its S = K Q^T, rows masked on
+ * the tiles that reach the chunk, then the decode merge kernel.  Other
+ * chunks that fit one workgroup run stream-K on the chunk kernel: all
+ * (sequence, KV head, 64-key tile) units cut into equal ranges over the
+ * workgroups the GPU holds at once, items shared by two workers merged by a
+ * log-sum-exp fold in a second kernel.  num_seqs <= 16383 and num_kv_heads in 1..8 or 16 when
  * single-row sequences can be present; num_seqs <= 16383 for chunks that fit
  * one workgroup (PKV_ERR_UNSUPPORTED otherwise).  QK^T runs as bf16 x bf16 MFMA with fp32 accumulation;
  * P V runs as fp16 x fp16 MFMA with fp32 accumulation, V converted from bf16

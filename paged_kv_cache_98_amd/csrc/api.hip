@@ -82,11 +82,22 @@ void* scratch_address(hipError_t* err) {
     return g_scratch_ptr[dev];
 }
 
-// Prefill workspace: the decode kernels' part for single-row sequences,
-// then, when the call's chunks fit one workgroup (stream-K), that kernel's
-// prefix sums and records at *chunk_offset.
-size_t prefill_workspace(int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads,
-                         int head_dim, int max_context_len, size_t* chunk_offset) {
+// Calls whose chunks have at most 16 rows and 16 (row, head) columns per KV
+// head, 32 over FP8 pools (speculative-decoding verification), run whole on
+// the decode kernel's matrix-core tile, every sequence's rows as columns of
+// its S = K Q^T; wider ones on the chunk kernels.
+constexpr int kRowsPathMaxRows = 16;
+bool rows_path(int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads, bool kv_fp8) {
+    const int cols = max_q_len * (num_q_heads / num_kv_heads);
+    return max_q_len >= 2 && max_q_len <= kRowsPathMaxRows && cols <= (kv_fp8 ? 32 : 16) &&
+           num_seqs <= kMaxDecodeSeqs && (num_kv_heads <= 8 || num_kv_heads == kMaxDecodeKvHeads);
+}
+
+// The chunk kernels' workspace: the decode kernels' part for single-row
+// sequences, then, when the call's chunks fit one workgroup (stream-K), that
+// kernel's prefix sums and records at *chunk_offset.
+size_t chunk_workspace(int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads,
+                       int head_dim, int max_context_len, size_t* chunk_offset) {
     // decode records are per query head, so the KV head count does not matter here
     const size_t dec = pkv::decode_workspace_bytes(num_seqs, num_q_heads, 1, head_dim,
                                                    max_context_len);
@@ -97,6 +108,29 @@ size_t prefill_workspace(int num_seqs, int max_q_len, int num_q_heads, int num_k
     if (chunk_offset) *chunk_offset = off;
     return off + pkv::prefill_streamk_bytes(num_seqs, max_q_len, group, num_kv_heads,
                                             max_context_len);
+}
+
+// The rows path's workspace: the decode kernels' for max_q_len rows.
+size_t rows_workspace(int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads,
+                      int head_dim, int max_context_len) {
+    return pkv::decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                       max_context_len, max_q_len);
+}
+
+// What a prefill call of these sizes needs over either pool type (the FP8
+// pools take the rows path for more columns than the bf16 ones).
+size_t prefill_workspace(int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads,
+                         int head_dim, int max_context_len) {
+    size_t n = 0;
+    if (rows_path(num_seqs, max_q_len, num_q_heads, num_kv_heads, true))
+        n = rows_workspace(num_seqs, max_q_len, num_q_heads, num_kv_heads, head_dim,
+                           max_context_len);
+    if (!rows_path(num_seqs, max_q_len, num_q_heads, num_kv_heads, false)) {
+        const size_t c = chunk_workspace(num_seqs, max_q_len, num_q_heads, num_kv_heads,
+                                         head_dim, max_context_len, nullptr);
+        n = c > n ? c : n;
+    }
+    return n;
 }
 
 }  // namespace
@@ -304,7 +338,7 @@ size_t pkv_prefill_workspace_bytes(int num_seqs, int num_q_tokens, int max_q_len
         num_q_tokens < 0 || max_q_len < 0 || num_q_heads % num_kv_heads != 0)
         return 0;
     return prefill_workspace(num_seqs, max_q_len, num_q_heads, num_kv_heads, head_dim,
-                             max_context_len, nullptr);
+                             max_context_len);
 }
 
 }  // extern "C"
@@ -337,15 +371,19 @@ int prefill_call(void* out, int out_dtype, const void* q, const int32_t* cu_q_le
     const bool any_decode_rows = !uniform_chunks;
     const bool decode_limits_ok = num_seqs <= kMaxDecodeSeqs &&
                                   (num_kv_heads <= 8 || num_kv_heads == kMaxDecodeKvHeads);
-    const bool streamk = pkv::prefill_streamk(max_q_len, num_q_heads / num_kv_heads);
+    const bool rows = rows_path(num_seqs, max_q_len, num_q_heads, num_kv_heads, kv_fp8);
+    const bool streamk = !rows && pkv::prefill_streamk(max_q_len, num_q_heads / num_kv_heads);
     if (any_decode_rows && !decode_limits_ok) return PKV_ERR_UNSUPPORTED;
     // the stream-K chunk kernel keeps the sequences' unit prefix sums in LDS
     // beside its two tile buffers
     if (streamk && num_seqs > kMaxDecodeSeqs) return PKV_ERR_UNSUPPORTED;
     size_t chunk_off = 0;
-    if (any_decode_rows || streamk) {
-        const size_t need = prefill_workspace(num_seqs, max_q_len, num_q_heads, num_kv_heads,
-                                              head_dim, max_context_len, &chunk_off);
+    if (any_decode_rows || streamk || rows) {
+        const size_t need =
+            rows ? rows_workspace(num_seqs, max_q_len, num_q_heads, num_kv_heads, head_dim,
+                                  max_context_len)
+                 : chunk_workspace(num_seqs, max_q_len, num_q_heads, num_kv_heads, head_dim,
+                                   max_context_len, &chunk_off);
         if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
         if (!aligned16(workspace)) return PKV_ERR_ALIGN;
     }
@@ -383,7 +421,7 @@ int prefill_call(void* out, int out_dtype, const void* q, const int32_t* cu_q_le
     }
     a.tree_mask = tree_mask;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (!any_decode_rows) return to_status(pkv::launch_prefill(a, s));
+    if (!any_decode_rows && !rows) return to_status(pkv::launch_prefill(a, s));
 
     pkv::DecodeArgs d;
     d.out = out;
@@ -407,6 +445,13 @@ int prefill_call(void* out, int out_dtype, const void* q, const int32_t* cu_q_le
                                          align_up((size_t)2 * num_seqs * sizeof(int32_t), 256));
     d.max_workers = pkv::decode_max_workers(num_seqs, max_context_len);
     d.cu_q_lens = cu_q_lens;
+    if (rows) {
+        d.rows = max_q_len;
+        d.causal = causal != 0;
+        d.tree_mask = tree_mask;
+        d.max_workers = pkv::decode_max_workers(num_seqs, max_context_len, max_q_len, num_kv_heads);
+        return to_status(pkv::launch_decode(d, s));
+    }
     if (max_q_len > 1 && !streamk) {
         // chunks and decode rows in one grid, sharing the CUs
         const hipError_t e = pkv::launch_mixed(a, d, s);

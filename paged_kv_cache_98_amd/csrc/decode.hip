@@ -12,8 +12,12 @@ using namespace dec;
 
 // Grid: (num_workers, head groups); a workgroup has one wave per KV head of
 // its group (all KV heads when there are at most 8, else groups of 8);
-// dynamic LDS (num_seqs + 1) int32 for the tile prefix sums.
-template <typename KV, int BS, int G, bool OUT_BF16>
+// dynamic LDS (num_seqs + 1) int32 for the tile prefix sums.  With
+// max_rows > 1 (short chunks, as in speculative-decoding verification) every
+// sequence of up to max_rows rows, causal or under per-row tree masks, its
+// (row, head) pairs the columns of the matrix-core tile: NCB blocks of 16
+// per KV head (the Q operands of two blocks in LDS).
+template <typename KV, int BS, int G, bool OUT_BF16, int NCB>
 __global__ void __launch_bounds__(64 * kMaxWavesPerWorker)
 decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* __restrict__ seq_workers,
                       const uint16_t* __restrict__ q, const void* __restrict__ k_cache,
@@ -21,35 +25,41 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
                       int max_blocks_per_seq, const int32_t* __restrict__ context_lens,
                       int max_context_len, int num_seqs, int num_q_heads, int num_kv_heads,
                       float scale_log2, float out_scale, int num_workers,
-                      const int32_t* __restrict__ cu_q_lens) {
+                      const int32_t* __restrict__ cu_q_lens, int max_rows, int causal,
+                      const uint64_t* __restrict__ tree_mask) {
     constexpr int kWaves = kMaxWavesPerWorker;
     extern __shared__ int32_t s_cum[];
     __shared__ int32_t s_part[kWaves];
     // the matrix-core tile's per-wave V staging (one element otherwise)
     __shared__ __attribute__((aligned(16))) uint16_t s_vx[KV::kMfma ? kWaves * kVxWaveElems : 8];
-    decode_worker<KV, BS, G, OUT_BF16, kWaves>(
+    __shared__ uint4 s_q[NCB > 1 ? kWaves * NCB * 4 * 64 : 1];
+    decode_worker<KV, BS, G, OUT_BF16, kWaves, NCB>(
         out, rec, seq_workers, q, k_cache, v_cache, block_table, max_blocks_per_seq,
         context_lens, max_context_len, num_seqs, num_q_heads, num_kv_heads, scale_log2, out_scale,
-        num_workers, cu_q_lens, s_cum, s_part, blockIdx.x, blockIdx.y, s_vx);
+        num_workers, cu_q_lens, s_cum, s_part, blockIdx.x, blockIdx.y, s_vx, max_rows, causal,
+        tree_mask, s_q);
 }
 
-// Finishes every (sequence, query head): zero rows for empty contexts, and
-// the log-sum-exp merge of a sequence's pieces when several workers shared
-// it: M = max_k m_k, L = sum_k l_k 2^(m_k - M), out = sum_k acc_k 2^(m_k - M) / L.
-// Grid: (ceil(num_q_heads / 4), num_seqs); block: 4 waves, one query head each.
+// Finishes every (sequence, query row, query head): zero rows for empty
+// contexts, and the log-sum-exp merge of a sequence's pieces when several
+// workers shared it: M = max_k m_k, L = sum_k l_k 2^(m_k - M),
+// out = sum_k acc_k 2^(m_k - M) / L.
+// Grid: (ceil(num_q_heads / 4), num_seqs, max_rows); block: 4 waves, one
+// query head each.
 template <bool OUT_BF16>
 __global__ void __launch_bounds__(256)
 decode_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
                     const int32_t* __restrict__ seq_workers, const int32_t* __restrict__ context_lens,
                     int max_context_len, int num_seqs, int num_q_heads,
-                    float out_scale, const int32_t* __restrict__ cu_q_lens) {
+                    float out_scale, const int32_t* __restrict__ cu_q_lens, int max_rows) {
     constexpr int D = kHeadDim;
     const int lane = threadIdx.x & 63;
     const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int seq = blockIdx.y;
+    const int r = blockIdx.z;
     if (h >= num_q_heads) return;
-    if (!is_decode_row(cu_q_lens, seq)) return;  // a prefill chunk: not ours
-    const size_t e = ((size_t)row_of(cu_q_lens, seq) * num_q_heads + h) * D + 2 * lane;
+    if (r >= rows_of(cu_q_lens, seq, max_rows)) return;  // not a row of ours
+    const size_t e = ((size_t)(row_of(cu_q_lens, seq) + r) * num_q_heads + h) * D + 2 * lane;
     const int ctx = clamp_ctx(context_lens[seq], max_context_len);
     if (ctx == 0) {  // nothing to attend to: a defined all-zero row
         store1<OUT_BF16>(out, e, 0.0f);
@@ -65,7 +75,7 @@ decode_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
 
     auto rec_of = [&](int64_t w) {
         const int slot = w == wf ? slot_f : 0;
-        return rec + ((size_t)(w * 2 + slot) * num_q_heads + h) * kRecStride;
+        return rec + (((size_t)(w * 2 + slot) * max_rows + r) * num_q_heads + h) * kRecStride;
     };
     // maximum over the pieces' running maxima, one piece per lane; the
     // first 64 pieces' (m, l) stay in their lanes
@@ -108,9 +118,9 @@ decode_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
     store1<OUT_BF16>(out, e + 1, a1 * inv);
 }
 
-template <typename KV, int BS, int G, bool OUT_BF16>
+template <typename KV, int BS, int G, bool OUT_BF16, int NCB>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-    auto kern = decode_streamk_kernel<KV, BS, G, OUT_BF16>;
+    auto kern = decode_streamk_kernel<KV, BS, G, OUT_BF16, NCB>;
     constexpr int kMax = kMaxWavesPerWorker;
     // head groups of kMax waves; the API admits 1..8 and 16 KV heads
     const int waves = a.num_kv_heads <= kMax ? a.num_kv_heads
@@ -127,20 +137,48 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     int64_t workers = resident / groups;
     if (workers > a.max_workers) workers = a.max_workers;
     if (workers < 1) workers = 1;
-    hipLaunchKernelGGL((decode_streamk_kernel<KV, BS, G, OUT_BF16>), dim3((int)workers, groups),
+    hipLaunchKernelGGL(kern, dim3((int)workers, groups),
                        dim3(threads), lds, stream, a.out, a.records, a.seq_workers, a.q, a.k_cache,
                        a.v_cache, a.block_table, a.max_blocks_per_seq, a.context_lens,
                        a.max_context_len, a.num_seqs, a.num_q_heads, a.num_kv_heads, a.scale_log2,
-                       a.out_scale, (int)workers, a.cu_q_lens);
+                       a.out_scale, (int)workers, a.cu_q_lens, a.rows, a.causal ? 1 : 0,
+                       a.tree_mask);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_decode_merge(a, stream);
 }
 
-template <typename KV, int BS, int G>
+template <typename KV, int BS, int G, int NCB = 1>
 hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s) {
-    return a.out_bf16 ? launch_decode_t<KV, BS, G, true>(a, s)
-                      : launch_decode_t<KV, BS, G, false>(a, s);
+    return a.out_bf16 ? launch_decode_t<KV, BS, G, true, NCB>(a, s)
+                      : launch_decode_t<KV, BS, G, false, NCB>(a, s);
+}
+
+// Sequences of up to a.rows > 1 query rows: the matrix-core tile over their
+// (row, head) pairs as columns, one block of 16 per KV head, or two for FP8
+// pools (whose 16 VGPRs per tile in flight leave room for the second block's
+// accumulators; a bf16 tile's 32 do not, and spilled, it lost to the
+// stream-K chunk kernel).  The host admits rows <= 16 and rows x G <= 16,
+// or <= 32 over FP8 pools.
+template <typename KV, int BS, int G>
+hipError_t launch_rows_g(const DecodeArgs& a, hipStream_t s) {
+    if (a.rows * G <= 16) return launch_decode_g<KV, BS, G, 1>(a, s);
+    if constexpr (G >= 2 && KV::kElemBytes == 1) {
+        if (a.rows * G <= 32) return launch_decode_g<KV, BS, G, 2>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename KV, int BS>
+hipError_t launch_rows_bs(const DecodeArgs& a, hipStream_t s) {
+    switch (a.num_q_heads / a.num_kv_heads) {
+        case 1: return launch_rows_g<KV, BS, 1>(a, s);
+        case 2: return launch_rows_g<KV, BS, 2>(a, s);
+        case 4: return launch_rows_g<KV, BS, 4>(a, s);
+        case 8: return launch_rows_g<KV, BS, 8>(a, s);
+        case 16: return launch_rows_g<KV, BS, 16>(a, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 // bf16 pools: the tile math on the matrix cores for 8 and 16 query heads
@@ -152,6 +190,7 @@ hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s) {
 // (4 heads), which did not buy that loss.
 template <int BS>
 hipError_t launch_decode_bf16_bs(const DecodeArgs& a, hipStream_t s) {
+    if (a.rows > 1) return launch_rows_bs<KvBf16Mfma, BS>(a, s);
     switch (a.num_q_heads / a.num_kv_heads) {
         case 1: return launch_decode_g<KvBf16, BS, 1>(a, s);
         case 2: return launch_decode_g<KvBf16, BS, 2>(a, s);
@@ -170,6 +209,7 @@ hipError_t launch_decode_bf16_bs(const DecodeArgs& a, hipStream_t s) {
 // so those keep the VALU tile (16 dims per lane).
 template <int BS>
 hipError_t launch_decode_fp8_bs(const DecodeArgs& a, hipStream_t s) {
+    if (a.rows > 1) return launch_rows_bs<KvFp8Mfma, BS>(a, s);
     switch (a.num_q_heads / a.num_kv_heads) {
         case 1: return launch_decode_g<KvFp8Wide, BS, 1>(a, s);
         case 2: return launch_decode_g<KvFp8Wide, BS, 2>(a, s);
@@ -209,31 +249,39 @@ hipError_t resident_workgroups(const void* kern, int threads, size_t lds, int* o
     return hipSuccess;
 }
 
-int64_t decode_max_workers(int num_seqs, int max_context_len) {
+int64_t decode_max_workers(int num_seqs, int max_context_len, int rows, int num_kv_heads) {
     const int64_t tiles = (int64_t)num_seqs * ((max_context_len + kTileTokens - 1) / kTileTokens);
     int64_t w = (tiles + kMinTilesPerWorker - 1) / kMinTilesPerWorker;
     if (w > kMaxWorkers) w = kMaxWorkers;
+    // several rows per sequence: records grow with the rows, so no more
+    // workers than a 256-CU device holds at once (8 waves per CU, one per
+    // KV head)
+    if (rows > 1) {
+        const int64_t cap = kRowsMaxWaves / (num_kv_heads < 1 ? 1 : num_kv_heads);
+        if (w > cap) w = cap;
+    }
     return w < 1 ? 1 : w;
 }
 
 size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                              int max_context_len) {
-    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
+                              int max_context_len, int rows) {
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || rows < 1)
+        return 0;
     const size_t cum = ((size_t)2 * num_seqs * sizeof(int32_t) + 255) / 256 * 256;
-    return cum + (size_t)decode_max_workers(num_seqs, max_context_len) * 2 * num_q_heads *
-                     kRecStride * sizeof(float);
+    return cum + (size_t)decode_max_workers(num_seqs, max_context_len, rows, num_kv_heads) * 2 *
+                     rows * num_q_heads * kRecStride * sizeof(float);
 }
 
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
-    dim3 mgrid((a.num_q_heads + 3) / 4, a.num_seqs);
+    dim3 mgrid((a.num_q_heads + 3) / 4, a.num_seqs, a.rows);
     if (a.out_bf16)
         hipLaunchKernelGGL((decode_merge_kernel<true>), mgrid, dim3(256), 0, stream, a.out,
                            a.records, a.seq_workers, a.context_lens, a.max_context_len,
-                           a.num_seqs, a.num_q_heads, a.out_scale, a.cu_q_lens);
+                           a.num_seqs, a.num_q_heads, a.out_scale, a.cu_q_lens, a.rows);
     else
         hipLaunchKernelGGL((decode_merge_kernel<false>), mgrid, dim3(256), 0, stream, a.out,
                            a.records, a.seq_workers, a.context_lens, a.max_context_len,
-                           a.num_seqs, a.num_q_heads, a.out_scale, a.cu_q_lens);
+                           a.num_seqs, a.num_q_heads, a.out_scale, a.cu_q_lens, a.rows);
     return hipGetLastError();
 }
 

@@ -451,6 +451,7 @@ constexpr int kMinTilesPerWorker = 4;   // fewer waves for tiny batches
 // in 256 registers, two waves per SIMD.
 constexpr int kMaxWavesPerWorker = 8;
 constexpr int64_t kMaxWorkers = 1024;    // workgroups of 8 waves an MI355X holds at most
+constexpr int64_t kRowsMaxWaves = 2048;  // waves an MI355X holds at two per SIMD
 // Cost of a sequence boundary inside a worker's range, in quarter tiles.
 constexpr int64_t kSeqCost = 6;
 
@@ -467,10 +468,19 @@ __device__ __forceinline__ bool is_decode_row(const int32_t* __restrict__ cu_q_l
 __device__ __forceinline__ int row_of(const int32_t* __restrict__ cu_q_lens, int i) {
     return cu_q_lens == nullptr ? i : cu_q_lens[i];
 }
+// Query rows of sequence i this path handles: with max_rows == 1 the
+// single-row sequences (1), else any sequence of 1 .. max_rows rows (its
+// row count); 0 for the rest.
+__device__ __forceinline__ int rows_of(const int32_t* __restrict__ cu_q_lens, int i, int max_rows) {
+    if (cu_q_lens == nullptr) return 1;
+    const int lq = cu_q_lens[i + 1] - cu_q_lens[i];
+    if (max_rows == 1) return lq == 1 ? 1 : 0;
+    return lq >= 1 && lq <= max_rows ? lq : 0;
+}
 __device__ __forceinline__ int tiles_of(const int32_t* __restrict__ context_lens,
                                         const int32_t* __restrict__ cu_q_lens, int i,
-                                        int max_context_len) {
-    if (!is_decode_row(cu_q_lens, i)) return 0;
+                                        int max_context_len, int max_rows) {
+    if (rows_of(cu_q_lens, i, max_rows) == 0) return 0;
     return (clamp_ctx(context_lens[i], max_context_len) + kTileTokens - 1) / kTileTokens;
 }
 
@@ -517,8 +527,8 @@ __device__ __forceinline__ size_t tile_bytes(IdWindow& ids, int tile, size_t row
 // physical block's K rows of all heads of the group (contiguous) are fetched
 // at the same time.  s_cum: (num_seqs + 1) int32 of LDS for the tile prefix
 // sums (s_cum[i] = tiles per KV head of sequences < i), s_part: NWAVES int32.
-// Records: [W][2][num_q_heads][kRecStride] floats.
-template <typename KV, int BS, int G, bool OUT_BF16, int NWAVES>
+// Records: [W][2][max_rows][num_q_heads][kRecStride] floats.
+template <typename KV, int BS, int G, bool OUT_BF16, int NWAVES, int NCB = 1>
 __device__ __forceinline__ void decode_worker(
     void* __restrict__ out, float* __restrict__ rec, int32_t* __restrict__ seq_workers,
     const uint16_t* __restrict__ q, const void* __restrict__ k_cache,
@@ -526,7 +536,10 @@ __device__ __forceinline__ void decode_worker(
     int max_blocks_per_seq, const int32_t* __restrict__ context_lens, int max_context_len,
     int num_seqs, int num_q_heads, int num_kv_heads, float scale_log2, float out_scale,
     int num_workers, const int32_t* __restrict__ cu_q_lens, int32_t* __restrict__ s_cum,
-    int32_t* __restrict__ s_part, int worker, int group, uint16_t* __restrict__ s_vx = nullptr) {
+    int32_t* __restrict__ s_part, int worker, int group, uint16_t* __restrict__ s_vx = nullptr,
+    int max_rows = 1, int causal = 1, const uint64_t* __restrict__ tree_mask = nullptr,
+    uint4* __restrict__ s_q = nullptr) {
+    static_assert(NCB == 1 || KV::kMfma, "two column blocks need the matrix-core tile");
     constexpr int D = kHeadDim;
     const int tid = threadIdx.x;
     const int nthr = blockDim.x;  // at most NWAVES waves
@@ -539,7 +552,7 @@ __device__ __forceinline__ void decode_worker(
     for (int k = 0; k < per; ++k) {
         const int i = tid * per + k;
         if (i < num_seqs)
-            local += tiles_of(context_lens, cu_q_lens, i, max_context_len);
+            local += tiles_of(context_lens, cu_q_lens, i, max_context_len, max_rows);
     }
     int incl = local;
 #pragma unroll
@@ -559,7 +572,7 @@ __device__ __forceinline__ void decode_worker(
         const int i = tid * per + k;
         if (i < num_seqs) {
             s_cum[i] = run;
-            run += tiles_of(context_lens, cu_q_lens, i, max_context_len);
+            run += tiles_of(context_lens, cu_q_lens, i, max_context_len, max_rows);
         }
     }
     if (tid == 0) s_cum[num_seqs] = total;
@@ -625,7 +638,8 @@ __device__ __forceinline__ void decode_worker(
         const int64_t piece_end = t_end < seg_t1 ? t_end : seg_t1;
         const int ntile = (int)(piece_end - t);
         const int ctx = clamp_ctx(context_lens[seq], max_context_len);
-        const size_t head_row = ((size_t)row_of(cu_q_lens, seq) * num_q_heads + (size_t)kvh * G) * D;
+        const int row0 = row_of(cu_q_lens, seq);  // the sequence's first q / out row
+        const size_t head_row = ((size_t)row0 * num_q_heads + (size_t)kvh * G) * D;
         const bool whole = (t == seg_t0) && (piece_end == seg_t1);
         const int slot = first_piece ? 0 : 1;
         // which workers hold a sequence's first and last tiles (and the
@@ -644,23 +658,61 @@ __device__ __forceinline__ void decode_worker(
         typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
         typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
         typedef float f32x4_t __attribute__((ext_vector_type(4)));
+        typedef short v4i16_t __attribute__((ext_vector_type(4)));
         const int r16 = lane & 15, q4 = lane >> 4;
-        // Q^T operand: column r16 = query head r16, rows = the 8 dims of k-block kb
-        bf16x8_t qb[4];
+        // The columns of the S = K Q^T product: column cc = 16 cb + r16 of
+        // block cb is query row cc / G of the sequence, head kvh G + cc % G;
+        // with one row per sequence (decode) simply head r16.
+        const int lq = rows_of(cu_q_lens, seq, max_rows);
+        // keys a row may see: causal rows up to their own position
+        // ctx - lq + r; the rows of a token tree of those only the keys
+        // before the chunk and the chunk keys their mask selects (a
+        // single-row sequence sees all its keys, as on the decode path);
+        // else all ctx keys
+        const int cpos = ctx - lq;
+        const int mask_from = tree_mask != nullptr ? cpos : (causal ? cpos + 1 : ctx);
+        // Q^T operands (rows = the 8 dims of k-block kb): in registers for
+        // one block, in the wave's LDS for two (the registers hold the
+        // second block's O instead)
+        bf16x8_t qreg[NCB == 1 ? 4 : 1];
+        uint4* const sq = s_q + (size_t)(tid >> 6) * (NCB * 4 * 64);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            uint4 x = make_uint4(0, 0, 0, 0);
-            if (r16 < G) {
-                x = *reinterpret_cast<const uint4*>(q + head_row + (size_t)r16 * D + KV::mfma_dim(kb, q4));
-                x.x ^= neg; x.y ^= neg; x.z ^= neg; x.w ^= neg;
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int cc = 16 * cb + r16;
+            const int r = cc / G;
+            const size_t qrow = ((size_t)(row0 + r) * num_q_heads + (size_t)kvh * G + cc % G) * D;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                uint4 x = make_uint4(0, 0, 0, 0);
+                if (r < lq) {
+                    x = *reinterpret_cast<const uint4*>(q + qrow + KV::mfma_dim(kb, q4));
+                    x.x ^= neg; x.y ^= neg; x.z ^= neg; x.w ^= neg;
+                }
+                if constexpr (NCB == 1) qreg[kb] = __builtin_bit_cast(bf16x8_t, x);
+                else sq[(cb * 4 + kb) * 64 + lane] = x;
             }
-            qb[kb] = __builtin_bit_cast(bf16x8_t, x);
         }
-        f32x4_t o[8];
+        auto qop = [&](int cb, int kb) -> bf16x8_t {
+            if constexpr (NCB == 1) {
+                return qreg[kb];
+            } else {
+                // read per use: an offset the compiler cannot see through
+                // keeps it from hoisting the loop-invariant reads back into
+                // registers
+                int idx = (cb * 4 + kb) * 64 + lane;
+                asm volatile("" : "+v"(idx));
+                return __builtin_bit_cast(bf16x8_t, sq[idx]);
+            }
+        };
+        f32x4_t o[NCB][8];
+        float m[NCB], l[NCB];  // column r16's running max (the same in its 4 lanes) and sum
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) o[nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        float m = kNegBig;  // head r16's running max, the same in its 4 lanes
-        float l = 0.0f;     // sum over this lane's tokens of head r16
+        for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) o[cb][nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            m[cb] = kNegBig;
+            l[cb] = 0.0f;
+        }
         // byte offsets of token r16's loads in a tile
         constexpr int NL = KV::kMfmaLoads;
         uint32_t koff[NL];
@@ -669,113 +721,149 @@ __device__ __forceinline__ void decode_worker(
             koff[j] = (uint32_t)(r16 * row_bytes + (size_t)kvh * D * KV::kElemBytes + KV::mfma_byte(j, q4));
         uint16_t* const vx = s_vx + (tid >> 6) * kVxWaveElems;  // this wave's V tile
         struct MTile { typename KV::Word k[NL]; typename KV::Word v[NL]; };
-        auto ntok_of = [&](int j) { return (tail && j == n - 1) ? ctx - (tile0 + j) * kTileTokens : kTileTokens; };
+        // tiles that reach the keys some row may not see take the mask
+        auto masked_of = [&](int j) { return (tile0 + j + 1) * kTileTokens > mask_from; };
         auto fetch = [&](MTile& x, int j) {
             const size_t o0 = tile_bytes<BS>(ids, tile0 + j, row_bytes, lane);
             const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kbase + o0);
             const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vbase + o0);
-            const bool valid = r16 < ntok_of(j);  // tokens past the end read zeros
+            // tokens past the end read zeros
+            const bool valid = (tile0 + j) * kTileTokens + r16 < ctx;
 #pragma unroll
-            for (int j = 0; j < NL; ++j) {
-                const uint32_t off = valid ? koff[j] : kBufferOob;
-                x.k[j] = KV::load(rk, off);
-                x.v[j] = KV::load(rv, off);
+            for (int jj = 0; jj < NL; ++jj) {
+                const uint32_t off = valid ? koff[jj] : kBufferOob;
+                x.k[jj] = KV::load(rk, off);
+                x.v[jj] = KV::load(rv, off);
             }
         };
-        auto process = [&](const MTile& x, int ntok) {
+        auto process = [&](const MTile& x, int j, bool masked) {
             // V as fp16 into the wave's LDS tile, token r16, k-block kb's dims
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
                 *reinterpret_cast<uint4*>(vx + r16 * kVxStride + KV::mfma_dim(kb, q4)) = KV::v_f16x8(x.v, kb);
-            // S = K Q^T: lane holds tokens 4 q4 .. + 3 of head r16
-            f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+            const int tok0 = (tile0 + j) * kTileTokens + 4 * q4;  // this lane's first token
+            f16x4_t pa[NCB];
+            float alpha[NCB];
+            bool grew = false;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8_t, KV::k_bf16x8(x.k, kb)), qb[kb], sc, 0, 0, 0);
-            float sv[4];
+            for (int cb = 0; cb < NCB; ++cb) {
+                // S = K Q^T: lane holds tokens 4 q4 .. + 3 of column 16 cb + r16
+                f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                sv[i] = (4 * q4 + i) < ntok ? sc[i] : -3.402823466e38f;
-            float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-            mt = max_lane_quads(mt) * c;
-            const float mn = fmaxf(m, mt);
-            const bool grew = mn > m;
-            const float alpha = fast_exp2(m - mn);
-            m = mn;
-            float p[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                p[i] = fast_exp2(fmaf(sv[i], c, -mn));
-                p[i] = (4 * q4 + i) < ntok ? p[i] : 0.0f;
-            }
-            l = fmaf(l, alpha, (p[0] + p[1]) + (p[2] + p[3]));
-            if (__any(grew)) {
-                // O row 4 q4 + i is head 4 q4 + i, whose alpha lane 4 q4 + i holds
+                for (int kb = 0; kb < 4; ++kb)
+                    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, KV::k_bf16x8(x.k, kb)), qop(cb, kb), sc, 0, 0, 0);
+                bool vis[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float ai = __shfl(alpha, 4 * q4 + i);
-#pragma unroll
-                    for (int nb = 0; nb < 8; ++nb) o[nb][i] *= ai;
+                    vis[i] = true;
+                    if (masked) {
+                        // the column's limits, taken again here: masked tiles are rare
+                        const int r = (16 * cb + r16) / G;
+                        const int tok = tok0 + i;
+                        vis[i] = tok <= (causal ? cpos + r : ctx - 1);
+                        if (tree_mask != nullptr && lq > 1) {
+                            const int sh = tok - cpos;  // <= r < 16 where tok <= the limit
+                            const uint64_t bits = r < lq ? tree_mask[row0 + r] : 0;
+                            vis[i] = vis[i] && (sh < 0 || ((bits >> (sh & 63)) & 1));
+                        }
+                    }
                 }
+                float sv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sv[i] = vis[i] ? sc[i] : -3.402823466e38f;
+                float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+                mt = max_lane_quads(mt) * c;
+                const float mn = fmaxf(m[cb], mt);
+                grew |= mn > m[cb];
+                alpha[cb] = fast_exp2(m[cb] - mn);
+                m[cb] = mn;
+                float p[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) p[i] = vis[i] ? fast_exp2(fmaf(sv[i], c, -mn)) : 0.0f;
+                l[cb] = fmaf(l[cb], alpha[cb], (p[0] + p[1]) + (p[2] + p[3]));
+                pa[cb] = f16x4_t{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
             }
-            const f16x4_t pa = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
-            // V operand: tokens 4 q4 .. + 3 of dim 16 nb + r16 (the wave's own
-            // stores above are done: a wave's LDS operations run in order)
+            if (__any(grew)) {
+                // O row 4 q4 + i is column 4 q4 + i, whose alpha lane 4 q4 + i holds
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float ai = __shfl(alpha[cb], 4 * q4 + i);
+#pragma unroll
+                        for (int nb = 0; nb < 8; ++nb) o[cb][nb][i] *= ai;
+                    }
+            }
+            // V operand: tokens 4 q4 .. + 3 of dim 16 nb + r16, by one
+            // transposing read (ds_read_b64_tr_b16: within each 16 lanes,
+            // lane i gets element i % 4 of the 8-byte chunks that lanes
+            // 4 k + i / 4 address, k = 0 .. 3; so lane (r16, q4) addresses
+            // token 4 q4 + r16 / 4, dims 16 nb + 4 (r16 % 4) .. + 3).  The
+            // wave's own stores above are done: its LDS operations run in
+            // order.
+            const uint16_t* const vrow = vx + (4 * q4 + (r16 >> 2)) * kVxStride + 4 * (r16 & 3);
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) {
-                const uint16_t* vc = vx + (4 * q4) * kVxStride + 16 * nb + r16;
-                const f16x4_t vb = {__builtin_bit_cast(_Float16, vc[0]),
-                                    __builtin_bit_cast(_Float16, vc[kVxStride]),
-                                    __builtin_bit_cast(_Float16, vc[2 * kVxStride]),
-                                    __builtin_bit_cast(_Float16, vc[3 * kVxStride])};
-                o[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb, o[nb], 0, 0, 0);
+                const f16x4_t vb = __builtin_bit_cast(f16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4i16_t*)(vrow + 16 * nb)));
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    o[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa[cb], vb, o[cb][nb], 0, 0, 0);
             }
         };
+        // Only a sequence's last two tiles can need the mask (rows <= 16).
         MTile a, b;
         fetch(a, 0);
         if (n == 1) {
-            process(a, ntok_of(0));
+            process(a, 0, masked_of(0));
         } else {
             fetch(b, 1);
             int j = 0;
-            for (; j + 3 < n; j += 2) {  // tiles j + 2 and j + 3 exist and are full
-                process(a, kTileTokens);
+            for (; j + 3 < n; j += 2) {  // tiles j, j + 1 are neither of the last two
+                process(a, j, false);
                 fetch(a, j + 2);
-                process(b, kTileTokens);
+                process(b, j + 1, false);
                 fetch(b, j + 3);
                 if (NWAVES == 8) __syncthreads();
             }
-            process(a, kTileTokens);
+            process(a, j, masked_of(j));
             if (n - j == 3) {
                 fetch(a, j + 2);
-                process(b, kTileTokens);
-                process(a, ntok_of(j + 2));
+                process(b, j + 1, masked_of(j + 1));
+                process(a, j + 2, masked_of(j + 2));
             } else {
-                process(b, ntok_of(j + 1));
+                process(b, j + 1, masked_of(j + 1));
             }
         }
-        // ---- the piece's result: l over the head's 4 lanes; a lane's O rows
-        // are heads 4 q4 .. + 3, whose (m, l) lanes 4 q4 .. + 3 hold
-        const float lt = sum_lane_quads(l);
+        // ---- the piece's result: l over the column's 4 lanes; a lane's O
+        // rows are columns 4 q4 .. + 3 of each block, whose (m, l) lanes
+        // 4 q4 .. + 3 hold
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int h = 4 * q4 + i;
-            const float mh = __shfl(m, h);
-            const float lh = __shfl(lt, h);
-            if (h >= G) continue;
-            if (whole) {
-                const float inv = out_scale / lh;
+        for (int cb = 0; cb < NCB; ++cb) {
+            const float lt = sum_lane_quads(l[cb]);
 #pragma unroll
-                for (int nb = 0; nb < 8; ++nb)
-                    store1<OUT_BF16>(out, head_row + (size_t)h * D + 16 * nb + r16, o[nb][i] * inv);
-            } else {
-                float* r = rec + ((size_t)(w * 2 + slot) * num_q_heads + (size_t)kvh * G + h) * kRecStride;
+            for (int i = 0; i < 4; ++i) {
+                const int cc = 16 * cb + 4 * q4 + i;
+                const float mh = __shfl(m[cb], 4 * q4 + i);
+                const float lh = __shfl(lt, 4 * q4 + i);
+                const int r = cc / G;
+                if (r >= lq) continue;
+                const size_t qh = (size_t)kvh * G + cc % G;
+                if (whole) {
+                    const float inv = out_scale / lh;
+                    const size_t e = ((size_t)(row0 + r) * num_q_heads + qh) * D;
 #pragma unroll
-                for (int nb = 0; nb < 8; ++nb) r[16 * nb + r16] = o[nb][i];
-                if (r16 == 0) {
-                    r[D] = mh;
-                    r[D + 1] = lh;
+                    for (int nb = 0; nb < 8; ++nb)
+                        store1<OUT_BF16>(out, e + 16 * nb + r16, o[cb][nb][i] * inv);
+                } else {
+                    float* rr = rec + (((size_t)(w * 2 + slot) * max_rows + r) * num_q_heads + qh) * kRecStride;
+#pragma unroll
+                    for (int nb = 0; nb < 8; ++nb) rr[16 * nb + r16] = o[cb][nb][i];
+                    if (r16 == 0) {
+                        rr[D] = mh;
+                        rr[D + 1] = lh;
+                    }
                 }
             }
         }

@@ -66,6 +66,12 @@ struct DecodeArgs {
     // prefill batch: only sequences with one query row are handled, reading
     // and writing row cu_q_lens[i].
     const int32_t* cu_q_lens;
+    // With rows > 1 (and cu_q_lens) every sequence of 1 .. rows query rows,
+    // rows cu_q_lens[i] ..: causal, or under one 64-bit key mask per row
+    // over the chunk's keys (tree_mask, [num_q_tokens]).
+    int rows = 1;
+    bool causal = true;
+    const uint64_t* tree_mask = nullptr;
 };
 
 struct PrefillArgs {
@@ -125,9 +131,10 @@ size_t prefill_streamk_bytes(int num_seqs, int max_q_len, int group, int num_kv_
 hipError_t resident_workgroups(const void* kern, int threads, size_t lds, int* out);
 
 // Decode workspace: which workers hold each sequence's first and last tiles,
-// then the partial-result records.
+// then the partial-result records ([workers][2][rows][num_q_heads] of them;
+// rows > 1 for sequences of several query rows).
 size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                              int max_context_len);
-int64_t decode_max_workers(int num_seqs, int max_context_len);
+                              int max_context_len, int rows = 1);
+int64_t decode_max_workers(int num_seqs, int max_context_len, int rows = 1, int num_kv_heads = 1);
 
 }  // namespace pkv

@@ -234,13 +234,16 @@ def test_prefill_fp8_chunks(bs, group):
                what=f"{w.name} causal={causal}")
 
 
-@pytest.mark.parametrize("group,rows", [(4, 6), (8, 16), (16, 8)])
+@pytest.mark.parametrize("group,rows", [(4, 6), (4, 8), (16, 2), (2, 16), (8, 16), (16, 8)])
 def test_prefill_fp8_streamk(group, rows):
-    """Chunks that fit one workgroup run stream-K over FP8 pools: items cut
-    between workers are merged with the v_scale; bf16 output equals the fp32
-    output rounded; determinism."""
+    """Short chunks over FP8 pools: up to 32 (row, head) columns per KV head
+    on the decode kernel's matrix-core tile (two blocks of 16 from 17 on),
+    wider ones on the stream-K chunk kernel; sequences cut between workers
+    are merged with the v_scale; bf16 output equals the fp32 output rounded;
+    determinism."""
     from tests.gpu_common import bf16_parity
-    cases = [(3000, rows), (2500, 1), (40, 3), (4100, rows), (700, rows - 1), (129, 2)]
+    cases = [(3000, rows), (2500, 1), (40, min(3, rows)), (4100, rows), (700, max(rows - 1, 1)),
+             (129, 2)]
     w = W.make_workload(f"fp8_streamk_g{group}_r{rows}", [c for c, _ in cases],
                         [q for _, q in cases], num_q_heads=2 * group, num_kv_heads=2,
                         block_size=16, seed=3500 + group + rows)

@@ -139,3 +139,53 @@ def test_tree_over_fp8_pools():
                                      tree_mask=masks.to(DEV))
     torch.cuda.synchronize()
     parity(out, ref, what=w.name)
+
+
+@pytest.mark.parametrize("group,nodes", [(1, 16), (4, 4), (2, 8)])
+def test_tree_rows_path(group, nodes):
+    """Trees of at most 16 (node, head) columns per KV head take the rows
+    path (the decode kernel's matrix-core tile, masks on the last two
+    tiles): trees straddling tile and block edges, a single-row sequence and
+    an empty one in the call, bf16 output and determinism."""
+    hkv = 2
+    ctx = [nodes, nodes + 1, 16, 17, 31, 32, 33, 64, 65, 1000, 4097]
+    cases = [(c, nodes) for c in ctx if c >= nodes] + [(300, 1), (50, 0), (129, nodes - 1)]
+    w = W.make_workload(f"tree_rows_g{group}_n{nodes}", [c for c, _ in cases],
+                        [q for _, q in cases], num_q_heads=hkv * group, num_kv_heads=hkv,
+                        block_size=16, seed=5400 + group + nodes)
+    print(f"[tree rows path] {w.name}", flush=True)
+    bc = W.materialize(w, logical=True, poison=True)
+    masks = W.tree_masks(w)
+    b = bc.to(DEV)
+    o32, o32b = run(b, masks), run(b, masks)
+    o16 = run(b, masks, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o32, o32b)
+    ref = oracle_tree(bc, masks)
+    parity(o32, ref, what=w.name)
+    bf16_parity(o16, o32, ref, what=w.name + " bf16 out", fp32_err=1e-3, min_within=0.95)
+
+
+def test_tree_rows_path_fp8_two_blocks():
+    """8-node trees with 4 query heads per KV head over FP8 pools: 32
+    columns, the rows path's two blocks."""
+    from oracle import fp8
+    cases = [(8, 8), (9, 8), (31, 8), (33, 8), (1000, 8), (300, 1), (129, 5)]
+    w = W.make_workload("tree_rows_fp8_g4", [c for c, _ in cases], [q for _, q in cases],
+                        num_q_heads=8, num_kv_heads=2, block_size=16, seed=5500)
+    print(f"[tree rows fp8] {w.name}", flush=True)
+    bc = W.materialize(w, logical=True, poison=True)
+    kc, vc = W.fp8_pools(bc)
+    masks = W.tree_masks(w)
+    kv = [torch.from_numpy((fp8.e4m3_value(c.numpy()) * W.FP8_SCALE).astype(np.float32))
+          .to(torch.bfloat16) for c in (kc, vc)]
+    ref = tree.paged_attention_tree(bits16(bc.q), bits16(kv[0]), bits16(kv[1]),
+                                    bc.block_table.numpy(), bc.context_lens.numpy(),
+                                    bc.cu_q_lens.numpy(), masks.numpy().view(np.uint64), w.scale)
+    b = bc.to(DEV)
+    out = pkv.paged_prefill_attn_fp8(b.q, b.cu_q_lens, kc.to(DEV), vc.to(DEV), W.FP8_SCALE,
+                                     W.FP8_SCALE, b.block_table, b.context_lens, w.scale,
+                                     max_context_len=w.max_context_len, max_q_len=w.max_q_len,
+                                     tree_mask=masks.to(DEV))
+    torch.cuda.synchronize()
+    parity(out, ref, what=w.name)

@@ -111,7 +111,7 @@ def test_streamk_widths_and_many_pieces(name, hq, hkv, cases):
     parity(out, ref, what=name)
 
 
-@pytest.mark.parametrize("group,rows", [(2, 8), (8, 16), (16, 8)])
+@pytest.mark.parametrize("group,rows", [(2, 16), (8, 16), (16, 8)])
 def test_streamk_merge_query_heads_grouped(group, rows):
     """With at least half as many (sequence, KV head) items as stream-K
     workers, the merge kernel takes several query heads of one KV head per
@@ -156,5 +156,81 @@ def test_streamk_merge_query_heads_grouped_tree():
     out = pkv.paged_prefill_attn(b.q, b.cu_q_lens, b.k_cache, b.v_cache, b.block_table,
                                  b.context_lens, w.scale, max_context_len=w.max_context_len,
                                  max_q_len=w.max_q_len, tree_mask=masks.to(DEV))
+    torch.cuda.synchronize()
+    parity(out, ref, what=w.name)
+
+
+def rows_cases(rows):
+    """(context length, rows) for the rows path: full row groups ending at,
+    straddling and starting tile (16-key) and block edges, a decode row and
+    an empty sequence in the same call, whole prompts."""
+    ctx = [rows, rows + 1, 16, 17, 31, 32, 33, 47, 48, 49, 63, 64, 65, 100, 1000, 4097]
+    cases = [(c, rows) for c in ctx if c >= rows]
+    return cases + [(500, 1), (70, 0), (129, max(rows - 1, 1)), (2, min(rows, 2))]
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_rows_path_groups_and_edges(bs, group):
+    """Chunks of at most 16 (row, head) columns per KV head take the decode
+    kernel's matrix-core tile (the rows path): 16 rows at one query head per
+    KV head down to 2 at eight, causal and not, against the fp64 oracle."""
+    rows, hkv = 16 // group, 2
+    cases = rows_cases(rows)
+    w = W.make_workload(f"rows_g{group}_bs{bs}", [c for c, _ in cases], [q for _, q in cases],
+                        num_q_heads=hkv * group, num_kv_heads=hkv, block_size=bs,
+                        seed=4400 + group + bs)
+    print(f"[rows path] {w.name}", flush=True)
+    bc = W.materialize(w, logical=True, poison=True)
+    b = bc.to(DEV)
+    for causal in (True, False):
+        ref = oracle.paged_attention(bc.q, bc.k_cache, bc.v_cache, bc.block_table,
+                                     bc.context_lens, w.scale, cu_q_lens=bc.cu_q_lens,
+                                     causal=causal)
+        out = pkv.paged_prefill_attn(b.q, b.cu_q_lens, b.k_cache, b.v_cache, b.block_table,
+                                     b.context_lens, w.scale, max_context_len=w.max_context_len,
+                                     max_q_len=w.max_q_len, causal=causal)
+        torch.cuda.synchronize()
+        parity(out, ref, what=f"{w.name} causal={causal}")
+
+
+def test_rows_path_split_bf16_out_and_determinism():
+    """The rows path with sequences cut between stream-K workers (few long
+    contexts) and 8 KV heads: records per (worker, row, head) merged after
+    the tile kernel; bf16 output equals the fp32 output rounded; bitwise
+    determinism."""
+    from tests.gpu_common import bf16_parity
+    cases = [(30000, 4), (2500, 4), (40, 3), (18000, 2), (700, 1), (9000, 4), (5, 4)]
+    w = W.make_workload("rows_split_g4", [c for c, _ in cases], [q for _, q in cases],
+                        num_q_heads=32, num_kv_heads=8, block_size=16, seed=4500)
+    print(f"[rows path split] {w.name}", flush=True)
+    bc = W.materialize(w, logical=True, poison=True)
+    b = bc.to(DEV)
+    ref = oracle.paged_attention(bc.q, bc.k_cache, bc.v_cache, bc.block_table, bc.context_lens,
+                                 w.scale, cu_q_lens=bc.cu_q_lens, causal=True)
+    call = lambda dt: pkv.paged_prefill_attn(
+        b.q, b.cu_q_lens, b.k_cache, b.v_cache, b.block_table, b.context_lens, w.scale,
+        max_context_len=w.max_context_len, max_q_len=w.max_q_len, causal=True, out_dtype=dt)
+    o32, o32b, o16 = call(torch.float32), call(torch.float32), call(torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o32, o32b)
+    parity(o32, ref, what=w.name)
+    bf16_parity(o16, o32, ref, what=w.name + " bf16 out", fp32_err=1e-3, min_within=0.95)
+
+
+@pytest.mark.parametrize("hkv,group", [(16, 1), (16, 4), (3, 2), (5, 8)])
+def test_rows_path_kv_head_layouts(hkv, group):
+    """The rows path's workgroups: 16 KV heads in two groups of 8 waves,
+    and KV head counts that are not powers of two."""
+    rows = 16 // group
+    cases = [(2000, rows), (77, rows), (16, rows), (900, 1)]
+    w = W.make_workload(f"rows_hkv{hkv}_g{group}", [c for c, _ in cases], [q for _, q in cases],
+                        num_q_heads=hkv * group, num_kv_heads=hkv, block_size=16,
+                        seed=4600 + hkv + group)
+    print(f"[rows path heads] {w.name}", flush=True)
+    bc = W.materialize(w, logical=True, poison=True)
+    ref = oracle.paged_attention(bc.q, bc.k_cache, bc.v_cache, bc.block_table, bc.context_lens,
+                                 w.scale, cu_q_lens=bc.cu_q_lens, causal=True)
+    out = run(bc.to(DEV))
     torch.cuda.synchronize()
     parity(out, ref, what=w.name)
