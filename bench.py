@@ -99,7 +99,8 @@ TRAFFIC_SPEC = {
                           "args": "--workload spec_verify_long"},
     "spec_tree_b64_n16": {"kernels": _VERIFY_K, "sources": _PREFILL_SRC,
                           "args": "--workload spec_verify_tree"},
-    "spec_verify_b64_q6_fp8": {"kernels": _VERIFY_K, "sources": _PREFILL_SRC,
+    # over FP8 pools the 6-row chunks take the rows path (the decode kernels)
+    "spec_verify_b64_q6_fp8": {"kernels": _DECODE_K, "sources": _DECODE_SRC,
                                "args": "--workload spec_verify_fp8"},
     "mixed_prefill_c4x512_d0_fp8": {"kernels": ["prefill_mfma_kernel"], "sources": _PREFILL_SRC,
                                     "args": "--workload prefill_chunks_fp8"},
