@@ -193,6 +193,62 @@ def test_decode_fp8_full_8b_batch_sampled():
         parity(out[i:i + 1], ref, what=f"fp8 full batch seq {i} (ctx {n})")
 
 
+def test_decode_fp8_full_70b_batch_sampled():
+    """The 256-sequence 70B-shaped batch (8 query heads per KV head: the
+    matrix-core tile) over FP8 pools, as the benchmark times it; sampled
+    sequences against the oracle."""
+    w = W.llama70b_decode(block_size=16)
+    print(f"[fp8 full 70b] {w.name}", flush=True)
+    b = W.materialize(w, device=DEV, poison=True)
+    kd, vd = W.fp8_pools(b)
+    out = run_fp8(b.q, kd, vd, b.block_table, b.context_lens, w)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(out))
+    ctx = list(w.context_lens)
+    seqs = sorted({ctx.index(max(ctx)), ctx.index(min(ctx)), 0, 100, 255})
+    bt = b.block_table.cpu()
+    for i in seqs:
+        n = ctx[i]
+        ids = bt[i, : -(-n // w.block_size)].to(torch.int64)
+        sub_k = codes(kd.index_select(0, ids.to(DEV)))
+        sub_v = codes(vd.index_select(0, ids.to(DEV)))
+        ref = fp8.paged_decode_fp8(bits16(b.q[i:i + 1]), sub_k, sub_v, W.FP8_SCALE, W.FP8_SCALE,
+                                   np.arange(len(ids), dtype=np.int32)[None, :],
+                                   np.array([n], dtype=np.int32), w.scale)
+        parity(out[i:i + 1], ref, what=f"fp8 70b batch seq {i} (ctx {n})")
+
+
+def test_verify_fp8_full_batch_sampled():
+    """The 64-sequence 6-row verify batch over FP8 pools, as the benchmark
+    times it (the rows path: two column blocks per wave); every row of
+    sampled sequences against the oracle."""
+    w = W.spec_verify()
+    print(f"[fp8 verify full] {w.name}", flush=True)
+    b = W.materialize(w, device=DEV, poison=True)
+    kd, vd = W.fp8_pools(b)
+    out = pkv.paged_prefill_attn_fp8(b.q, b.cu_q_lens, kd, vd, W.FP8_SCALE, W.FP8_SCALE,
+                                     b.block_table, b.context_lens, w.scale,
+                                     max_context_len=w.max_context_len, max_q_len=w.max_q_len,
+                                     causal=True)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(out))
+    ctx = list(w.context_lens)
+    cu = b.cu_q_lens.cpu()
+    bt = b.block_table.cpu()
+    for i in sorted({ctx.index(max(ctx)), ctx.index(min(ctx)), 0, 31, 63}):
+        n = ctx[i]
+        ids = bt[i, : -(-n // w.block_size)].to(torch.int64)
+        sub_k = codes(kd.index_select(0, ids.to(DEV)))
+        sub_v = codes(vd.index_select(0, ids.to(DEV)))
+        rows = slice(int(cu[i]), int(cu[i + 1]))
+        ref = fp8.paged_prefill_fp8(bits16(b.q[rows]), sub_k, sub_v, W.FP8_SCALE, W.FP8_SCALE,
+                                    np.arange(len(ids), dtype=np.int32)[None, :],
+                                    np.array([n], dtype=np.int32),
+                                    np.array([0, rows.stop - rows.start], dtype=np.int32),
+                                    w.scale, causal=True)
+        parity(out[rows], ref, what=f"fp8 verify batch seq {i} (ctx {n})")
+
+
 # (context length including the chunk, chunk rows): whole prompts, chunks
 # straddling key tiles, decode rows and an empty sequence in the same call
 FP8_CHUNKS = [(37, 37), (141, 100), (300, 200), (64, 1), (520, 129), (1000, 64), (77, 0),
