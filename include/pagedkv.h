@@ -240,7 +240,7 @@ int pkv_paged_decode_attn_fp8(void *out, int out_dtype, const void *q, const voi
  * (bytes, >= 0; 0 for inconsistent sizes), the larger of what the call's
  * path needs over bf16 and over FP8 pools.  With C = max_q_len *
  * (num_q_heads / num_kv_heads) query columns per KV head:
- *  - the rows path (2 <= max_q_len <= 16 and C <= 16, or C <= 32 over FP8
+ *  - the rows path (2 <= max_q_len <= 16 and C <= 64, or C <= 32 over FP8
  *    pools; num_seqs <= 16383, num_kv_heads 1..8 or 16): 2 * num_seqs int32,
  *    256-byte aligned, then records of 132 floats for
  *    2 * max_q_len * num_q_heads columns of each of up to

@@ -82,14 +82,14 @@ void* scratch_address(hipError_t* err) {
     return g_scratch_ptr[dev];
 }
 
-// Calls whose chunks have at most 16 rows and 16 (row, head) columns per KV
-// head, 32 over FP8 pools (speculative-decoding verification), run whole on
-// the decode kernel's matrix-core tile, every sequence's rows as columns of
-// its S = K Q^T; wider ones on the chunk kernels.
+// Calls whose chunks have at most 16 rows and 64 (row, head) columns per KV
+// head, 32 over FP8 pools (speculative-decoding verification, token trees),
+// run whole on the decode kernel's matrix-core tile, every sequence's rows
+// as columns of its S = K Q^T; wider ones on the chunk kernels.
 constexpr int kRowsPathMaxRows = 16;
 bool rows_path(int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads, bool kv_fp8) {
     const int cols = max_q_len * (num_q_heads / num_kv_heads);
-    return max_q_len >= 2 && max_q_len <= kRowsPathMaxRows && cols <= (kv_fp8 ? 32 : 16) &&
+    return max_q_len >= 2 && max_q_len <= kRowsPathMaxRows && cols <= (kv_fp8 ? 32 : 64) &&
            num_seqs <= kMaxDecodeSeqs && (num_kv_heads <= 8 || num_kv_heads == kMaxDecodeKvHeads);
 }
 
@@ -117,17 +117,18 @@ size_t rows_workspace(int num_seqs, int max_q_len, int num_q_heads, int num_kv_h
                                        max_context_len, max_q_len);
 }
 
-// What a prefill call of these sizes needs over either pool type (the FP8
-// pools take the rows path for more columns than the bf16 ones).
+// What a prefill call of these sizes needs over either pool type (the rows
+// path takes more columns over bf16 pools than over FP8 ones).
 size_t prefill_workspace(int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads,
                          int head_dim, int max_context_len) {
     size_t n = 0;
-    if (rows_path(num_seqs, max_q_len, num_q_heads, num_kv_heads, true))
-        n = rows_workspace(num_seqs, max_q_len, num_q_heads, num_kv_heads, head_dim,
-                           max_context_len);
-    if (!rows_path(num_seqs, max_q_len, num_q_heads, num_kv_heads, false)) {
-        const size_t c = chunk_workspace(num_seqs, max_q_len, num_q_heads, num_kv_heads,
-                                         head_dim, max_context_len, nullptr);
+    for (const bool fp8 : {false, true}) {
+        const size_t c =
+            rows_path(num_seqs, max_q_len, num_q_heads, num_kv_heads, fp8)
+                ? rows_workspace(num_seqs, max_q_len, num_q_heads, num_kv_heads, head_dim,
+                                 max_context_len)
+                : chunk_workspace(num_seqs, max_q_len, num_q_heads, num_kv_heads, head_dim,
+                                  max_context_len, nullptr);
         n = c > n ? c : n;
     }
     return n;

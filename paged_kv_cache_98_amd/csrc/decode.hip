@@ -17,7 +17,7 @@ using namespace dec;
 // sequence of up to max_rows rows, causal or under per-row tree masks, its
 // (row, head) pairs the columns of the matrix-core tile: NCB blocks of 16
 // per KV head (the Q operands of two blocks in LDS).
-template <typename KV, int BS, int G, bool OUT_BF16, int NCB>
+template <typename KV, int BS, int G, bool OUT_BF16, int NCB, int CSPLIT>
 __global__ void __launch_bounds__(64 * kMaxWavesPerWorker)
 decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* __restrict__ seq_workers,
                       const uint16_t* __restrict__ q, const void* __restrict__ k_cache,
@@ -31,13 +31,15 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
     extern __shared__ int32_t s_cum[];
     __shared__ int32_t s_part[kWaves];
     // the matrix-core tile's per-wave V staging (one element otherwise)
-    __shared__ __attribute__((aligned(16))) uint16_t s_vx[KV::kMfma ? kWaves * kVxWaveElems : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t s_vx[KV::kMfma && CSPLIT == 1 ? kWaves * kVxWaveElems : 8];
     __shared__ uint4 s_q[NCB > 1 ? kWaves * NCB * 4 * 64 : 1];
-    decode_worker<KV, BS, G, OUT_BF16, kWaves, NCB>(
+    // shared staging (4-wave workgroups): two 32-token K and V tiles per KV head
+    __shared__ __attribute__((aligned(16))) uint16_t s_st[CSPLIT > 1 ? (4 / CSPLIT) * 4 * 32 * (kHeadDim + 8) : 8];
+    decode_worker<KV, BS, G, OUT_BF16, kWaves, NCB, CSPLIT>(
         out, rec, seq_workers, q, k_cache, v_cache, block_table, max_blocks_per_seq,
         context_lens, max_context_len, num_seqs, num_q_heads, num_kv_heads, scale_log2, out_scale,
         num_workers, cu_q_lens, s_cum, s_part, blockIdx.x, blockIdx.y, s_vx, max_rows, causal,
-        tree_mask, s_q);
+        tree_mask, s_q, s_st);
 }
 
 // Finishes every (sequence, query row, query head): zero rows for empty
@@ -118,14 +120,18 @@ decode_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
     store1<OUT_BF16>(out, e + 1, a1 * inv);
 }
 
-template <typename KV, int BS, int G, bool OUT_BF16, int NCB>
+template <typename KV, int BS, int G, bool OUT_BF16, int NCB, int CSPLIT>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-    auto kern = decode_streamk_kernel<KV, BS, G, OUT_BF16, NCB>;
+    auto kern = decode_streamk_kernel<KV, BS, G, OUT_BF16, NCB, CSPLIT>;
     constexpr int kMax = kMaxWavesPerWorker;
-    // head groups of kMax waves; the API admits 1..8 and 16 KV heads
-    const int waves = a.num_kv_heads <= kMax ? a.num_kv_heads
-                                             : (a.num_kv_heads % kMax == 0 ? kMax : 1);
-    const int groups = a.num_kv_heads / waves;
+    // head groups of kMax waves; the API admits 1..8 and 16 KV heads.  With
+    // shared staging: workgroups of 4 waves, 4 / CSPLIT KV heads each (the
+    // last group's missing heads leave at once).
+    const int hpg = 4 / CSPLIT;
+    const int waves = CSPLIT > 1 ? 4
+                      : (a.num_kv_heads <= kMax ? a.num_kv_heads
+                                                : (a.num_kv_heads % kMax == 0 ? kMax : 1));
+    const int groups = CSPLIT > 1 ? (a.num_kv_heads + hpg - 1) / hpg : a.num_kv_heads / waves;
     const int threads = 64 * waves;
     const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int32_t);
     int resident = 0;
@@ -148,10 +154,10 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     return launch_decode_merge(a, stream);
 }
 
-template <typename KV, int BS, int G, int NCB = 1>
+template <typename KV, int BS, int G, int NCB = 1, int CSPLIT = 1>
 hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s) {
-    return a.out_bf16 ? launch_decode_t<KV, BS, G, true, NCB>(a, s)
-                      : launch_decode_t<KV, BS, G, false, NCB>(a, s);
+    return a.out_bf16 ? launch_decode_t<KV, BS, G, true, NCB, CSPLIT>(a, s)
+                      : launch_decode_t<KV, BS, G, false, NCB, CSPLIT>(a, s);
 }
 
 // Sequences of up to a.rows > 1 query rows: the matrix-core tile over their
@@ -165,6 +171,10 @@ hipError_t launch_rows_g(const DecodeArgs& a, hipStream_t s) {
     if (a.rows * G <= 16) return launch_decode_g<KV, BS, G, 1>(a, s);
     if constexpr (G >= 2 && KV::kElemBytes == 1) {
         if (a.rows * G <= 32) return launch_decode_g<KV, BS, G, 2>(a, s);
+    }
+    if constexpr (G >= 2 && KV::kElemBytes == 2) {
+        if (a.rows * G <= 32) return launch_decode_g<KV, BS, G, 1, 2>(a, s);
+        if (a.rows * G <= 64) return launch_decode_g<KV, BS, G, 1, 4>(a, s);
     }
     return hipErrorInvalidValue;
 }

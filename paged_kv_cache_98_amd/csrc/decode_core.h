@@ -528,7 +528,7 @@ __device__ __forceinline__ size_t tile_bytes(IdWindow& ids, int tile, size_t row
 // at the same time.  s_cum: (num_seqs + 1) int32 of LDS for the tile prefix
 // sums (s_cum[i] = tiles per KV head of sequences < i), s_part: NWAVES int32.
 // Records: [W][2][max_rows][num_q_heads][kRecStride] floats.
-template <typename KV, int BS, int G, bool OUT_BF16, int NWAVES, int NCB = 1>
+template <typename KV, int BS, int G, bool OUT_BF16, int NWAVES, int NCB = 1, int CSPLIT = 1>
 __device__ __forceinline__ void decode_worker(
     void* __restrict__ out, float* __restrict__ rec, int32_t* __restrict__ seq_workers,
     const uint16_t* __restrict__ q, const void* __restrict__ k_cache,
@@ -538,8 +538,10 @@ __device__ __forceinline__ void decode_worker(
     int num_workers, const int32_t* __restrict__ cu_q_lens, int32_t* __restrict__ s_cum,
     int32_t* __restrict__ s_part, int worker, int group, uint16_t* __restrict__ s_vx = nullptr,
     int max_rows = 1, int causal = 1, const uint64_t* __restrict__ tree_mask = nullptr,
-    uint4* __restrict__ s_q = nullptr) {
+    uint4* __restrict__ s_q = nullptr, uint16_t* __restrict__ s_st = nullptr) {
     static_assert(NCB == 1 || KV::kMfma, "two column blocks need the matrix-core tile");
+    static_assert(CSPLIT == 1 || (KV::kMfma && NCB == 1 && KV::kElemBytes == 2),
+                  "shared staging: the bf16 matrix-core tile, one block per wave");
     constexpr int D = kHeadDim;
     const int tid = threadIdx.x;
     const int nthr = blockDim.x;  // at most NWAVES waves
@@ -584,7 +586,10 @@ __device__ __forceinline__ void decode_worker(
     using L = Layout<KV>;
     constexpr int ND = KV::kDims;
     const int lane = tid & 63;
-    const int kvh = group * (nthr >> 6) + (tid >> 6);
+    // CSPLIT waves per KV head (sub = which of them), each on its own 16
+    // columns, sharing the KV head's tiles through LDS
+    const int kvh = group * ((nthr >> 6) / CSPLIT) + (tid >> 6) / CSPLIT;
+    const int sub = (tid >> 6) % CSPLIT;
     if (kvh >= num_kv_heads) return;  // a wave with no head: nothing below waits for it
     const int row = lane / L::kRowLanes;
     const int col = lane % L::kRowLanes;
@@ -654,7 +659,187 @@ __device__ __forceinline__ void decode_worker(
         ids.init(block_table + (size_t)seq * max_blocks_per_seq, (ctx + BS - 1) / BS,
                  (tile0 * kTileTokens) / BS, lane);
 
-      if constexpr (KV::kMfma) {
+      if constexpr (CSPLIT > 1) {
+        typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+        typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+        typedef float f32x4_t __attribute__((ext_vector_type(4)));
+        typedef short v4i16_t __attribute__((ext_vector_type(4)));
+        const int r16 = lane & 15, q4 = lane >> 4;
+        // column cbase + r16: query row (cbase + r16) / G, head
+        // kvh G + (cbase + r16) % G
+        const int cbase = 16 * sub;
+        const int lq = rows_of(cu_q_lens, seq, max_rows);
+        const int cpos = ctx - lq;
+        const int mask_from = tree_mask != nullptr ? cpos : (causal ? cpos + 1 : ctx);
+        const int cr = (cbase + r16) / G;
+        bf16x8_t qb[4];
+        {
+            const size_t qrow =
+                ((size_t)(row0 + cr) * num_q_heads + (size_t)kvh * G + (cbase + r16) % G) * D;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                uint4 x = make_uint4(0, 0, 0, 0);
+                if (cr < lq) {
+                    x = *reinterpret_cast<const uint4*>(q + qrow + 32 * kb + 8 * q4);
+                    x.x ^= neg; x.y ^= neg; x.z ^= neg; x.w ^= neg;
+                }
+                qb[kb] = __builtin_bit_cast(bf16x8_t, x);
+            }
+        }
+        f32x4_t o[8];
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) o[nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        float m = kNegBig, l = 0.0f;
+        // The KV head's LDS: two buffers of a 32-token tile, K (bf16) then V
+        // (fp16), rows of kStRow elements.  A 32-token tile is 16 loads of
+        // 16 bytes per lane (8 of K, 8 of V, load i carrying tokens
+        // 4 i + lane / 16, bytes 16 (lane % 16) of the head's row); the
+        // KV head's waves take 16 / CSPLIT of them each.
+        constexpr int kStRow = kHeadDim + 8;
+        constexpr int kStTile = 32 * kStRow;
+        constexpr int NLD = 16 / CSPLIT;
+        uint16_t* const st = s_st + (size_t)((tid >> 6) / CSPLIT) * (4 * kStTile);
+        const int n2 = (n + 1) / 2;  // 32-token tiles of the piece
+        struct Part { uint4 w[NLD]; };
+        auto st_load = [&](Part& x, int jj) {
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) {
+                const int ii = sub * NLD + i;       // 0 .. 7 K, 8 .. 15 V
+                const int tok = 4 * (ii & 7) + (lane >> 4);  // 0 .. 31
+                const int j = 2 * jj + (tok >> 4);  // 16-token tile of the piece
+                const bool valid = j < n && (tile0 + j) * kTileTokens + (tok & 15) < ctx;
+                const size_t o0 = tile_bytes<BS>(ids, tile0 + (j < n ? j : n - 1), row_bytes, lane);
+                const __amdgpu_buffer_rsrc_t r = buffer_rsrc((ii < 8 ? kbase : vbase) + o0);
+                const uint32_t off = valid ? (uint32_t)((tok & 15) * row_bytes +
+                                                        (size_t)kvh * D * 2 + 16 * (lane & 15))
+                                           : kBufferOob;
+                x.w[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+            }
+        };
+        auto st_store = [&](const Part& x, int jj) {
+            uint16_t* const b = st + (jj & 1) * (2 * kStTile);
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) {
+                const int ii = sub * NLD + i;
+                const int tok = 4 * (ii & 7) + (lane >> 4);
+                uint4 wv = x.w[i];
+                if (ii >= 8) {  // V as fp16
+                    const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+                    uint32_t hh[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const f16x2_t hp = {(_Float16)bf16_lo(wd[e]), (_Float16)bf16_hi(wd[e])};
+                        hh[e] = __builtin_bit_cast(uint32_t, hp);
+                    }
+                    wv = make_uint4(hh[0], hh[1], hh[2], hh[3]);
+                }
+                *reinterpret_cast<uint4*>(b + (ii >= 8 ? kStTile : 0) + tok * kStRow + 8 * (lane & 15)) = wv;
+            }
+        };
+        // one 16-token tile (half s of 32-token tile jj) from LDS
+        auto st_compute = [&](int jj, int s2) {
+            const int j = 2 * jj + s2;
+            if (j >= n) return;
+            const bool masked = (tile0 + j + 1) * kTileTokens > mask_from;
+            const uint16_t* const kt = st + (jj & 1) * (2 * kStTile) + 16 * s2 * kStRow;
+            const uint16_t* const vt = kt + kStTile;
+            f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kt + r16 * kStRow + 32 * kb + 8 * q4)),
+                    qb[kb], sc, 0, 0, 0);
+            const int tok0 = (tile0 + j) * kTileTokens + 4 * q4;
+            bool vis[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                vis[i] = true;
+                if (masked) {
+                    const int tok = tok0 + i;
+                    vis[i] = tok <= (causal ? cpos + cr : ctx - 1);
+                    if (tree_mask != nullptr && lq > 1) {
+                        const int sh = tok - cpos;  // <= cr < 16 where tok <= the limit
+                        const uint64_t bits = cr < lq ? tree_mask[row0 + cr] : 0;
+                        vis[i] = vis[i] && (sh < 0 || ((bits >> (sh & 63)) & 1));
+                    }
+                }
+            }
+            float sv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sv[i] = vis[i] ? sc[i] : -3.402823466e38f;
+            float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+            mt = max_lane_quads(mt) * c;
+            const float mn = fmaxf(m, mt);
+            const bool grew = mn > m;
+            const float alpha = fast_exp2(m - mn);
+            m = mn;
+            float p[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p[i] = vis[i] ? fast_exp2(fmaf(sv[i], c, -mn)) : 0.0f;
+            l = fmaf(l, alpha, (p[0] + p[1]) + (p[2] + p[3]));
+            if (__any(grew)) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float ai = __shfl(alpha, 4 * q4 + i);
+#pragma unroll
+                    for (int nb = 0; nb < 8; ++nb) o[nb][i] *= ai;
+                }
+            }
+            const f16x4_t pa = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+            const uint16_t* const vrow = vt + (4 * q4 + (r16 >> 2)) * kStRow + 4 * (r16 & 3);
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+                const f16x4_t vb = __builtin_bit_cast(f16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4i16_t*)(vrow + 16 * nb)));
+                o[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb, o[nb], 0, 0, 0);
+            }
+        };
+        // two register sets, roles alternating over pairs of 32-token tiles:
+        // tile jj + 1 is in flight in one while jj is computed, and is stored
+        // to LDS at the end of jj, behind the workgroup's barrier
+        Part ra, rb;
+        st_load(ra, 0);
+        if (n2 > 1) st_load(rb, 1);
+        st_store(ra, 0);
+        __syncthreads();
+        for (int jj = 0; jj < n2; jj += 2) {
+            if (jj + 2 < n2) st_load(ra, jj + 2);
+            st_compute(jj, 0);
+            st_compute(jj, 1);
+            if (jj + 1 < n2) st_store(rb, jj + 1);
+            __syncthreads();
+            if (jj + 1 >= n2) break;
+            if (jj + 3 < n2) st_load(rb, jj + 3);
+            st_compute(jj + 1, 0);
+            st_compute(jj + 1, 1);
+            if (jj + 2 < n2) st_store(ra, jj + 2);
+            __syncthreads();
+        }
+        const float lt = sum_lane_quads(l);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int cc = cbase + 4 * q4 + i;
+            const float mh = __shfl(m, 4 * q4 + i);
+            const float lh = __shfl(lt, 4 * q4 + i);
+            const int r = cc / G;
+            if (r >= lq) continue;
+            const size_t qh = (size_t)kvh * G + cc % G;
+            if (whole) {
+                const float inv = out_scale / lh;
+                const size_t e = ((size_t)(row0 + r) * num_q_heads + qh) * D;
+#pragma unroll
+                for (int nb = 0; nb < 8; ++nb) store1<OUT_BF16>(out, e + 16 * nb + r16, o[nb][i] * inv);
+            } else {
+                float* rr = rec + (((size_t)(w * 2 + slot) * max_rows + r) * num_q_heads + qh) * kRecStride;
+#pragma unroll
+                for (int nb = 0; nb < 8; ++nb) rr[16 * nb + r16] = o[nb][i];
+                if (r16 == 0) {
+                    rr[D] = mh;
+                    rr[D + 1] = lh;
+                }
+            }
+        }
+      } else if constexpr (KV::kMfma) {
         typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
         typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
         typedef float f32x4_t __attribute__((ext_vector_type(4)));

@@ -252,30 +252,25 @@ def test_prefill_workspace_size(lib):
     up = lambda x: (x + 255) // 256 * 256
     sk = lambda b, lq, g, hkv, ctx: (up((b + 1) * 4) + min(1024, b * hkv * -(-ctx // 64))
                                      * 2 * lq * g * 132 * 4)
-    # the rows path (up to 16 rows; 16 (row, head) columns per KV head, 32
+    # the rows path (up to 16 rows; 64 (row, head) columns per KV head, 32
     # over FP8 pools): the decode layout with records for every row, at most
     # one worker per 4 tiles, 1024 in all and 2048 / Hkv
     rp = lambda b, lq, hq, hkv, ctx: (up(2 * b * 4) + min(-(-b * -(-ctx // 16) // 4), 1024,
                                                           2048 // hkv) * 2 * lq * hq * 132 * 4)
     # 512-row chunks (2048 columns per KV head): only the decode part
     assert ws(4, 2048, 512, 32, 8, 128, 4096) == dec(4, 4096)
-    # 64 four-row verify chunks (16 columns per KV head): the rows path for
-    # both pool types, 256 workers for 8 KV heads
+    # 64 four- and six-row verify chunks (16, 24 columns per KV head): the
+    # rows path for both pool types, 256 workers for 8 KV heads
     assert ws(64, 256, 4, 32, 8, 128, 4096) == rp(64, 4, 32, 8, 4096) == 512 + 256 * 2 * 4 * 32 * 528
-    # six rows (24 columns): the rows path over FP8 pools, stream-K over bf16
-    # ones; the size covers both (64 x 8 x 64 units -> 1024 stream-K workers)
-    classic = up(dec(64, 4096)) + sk(64, 6, 4, 8, 4096)
-    assert ws(64, 384, 6, 32, 8, 128, 4096) == max(rp(64, 6, 32, 8, 4096), classic) == classic
-    # few tiles: one worker per 4 (2 seqs x 7 tiles) on the rows path; one
-    # per unit on stream-K (2 seqs x 2 heads x 2 tiles)
-    assert ws(2, 12, 6, 8, 2, 128, 100) == max(
-        rp(2, 6, 8, 2, 100),
-        up(lib.pkv_decode_workspace_bytes(2, 8, 2, 128, 100)) + up(3 * 4) + 8 * 2 * 6 * 4 * 132 * 4)
-    # 16 query heads per KV head, 2 rows: 32 columns; 4 rows: stream-K only
-    assert ws(8, 16, 2, 32, 2, 128, 5000) == max(
-        rp(8, 2, 32, 2, 5000), up(lib.pkv_decode_workspace_bytes(8, 32, 2, 128, 5000)) + sk(8, 2, 16, 2, 5000))
-    assert ws(8, 32, 4, 32, 2, 128, 5000) == (
-        up(lib.pkv_decode_workspace_bytes(8, 32, 2, 128, 5000)) + sk(8, 4, 16, 2, 5000))
+    assert ws(64, 384, 6, 32, 8, 128, 4096) == rp(64, 6, 32, 8, 4096) == 512 + 256 * 2 * 6 * 32 * 528
+    # few tiles: one worker per 4 (2 seqs x 7 tiles)
+    assert ws(2, 12, 6, 8, 2, 128, 100) == rp(2, 6, 8, 2, 100) == 256 + 4 * 2 * 6 * 8 * 528
+    # 16 query heads per KV head: 2 rows (32 columns) the rows path for both;
+    # 4 rows (64) the rows path over bf16 pools, stream-K over FP8 ones, the
+    # size covering both
+    assert ws(8, 16, 2, 32, 2, 128, 5000) == rp(8, 2, 32, 2, 5000)
+    classic = up(lib.pkv_decode_workspace_bytes(8, 32, 2, 128, 5000)) + sk(8, 4, 16, 2, 5000)
+    assert ws(8, 32, 4, 32, 2, 128, 5000) == max(rp(8, 4, 32, 2, 5000), classic)
     # 17 rows: stream-K (34 columns per KV head)
     assert ws(8, 136, 17, 16, 8, 128, 5000) == (
         up(lib.pkv_decode_workspace_bytes(8, 16, 8, 128, 5000)) + sk(8, 17, 2, 8, 5000))

@@ -141,12 +141,14 @@ def test_tree_over_fp8_pools():
     parity(out, ref, what=w.name)
 
 
-@pytest.mark.parametrize("group,nodes", [(1, 16), (4, 4), (2, 8)])
+@pytest.mark.parametrize("group,nodes", [(1, 16), (4, 4), (2, 8), (4, 8), (4, 16)])
 def test_tree_rows_path(group, nodes):
-    """Trees of at most 16 (node, head) columns per KV head take the rows
-    path (the decode kernel's matrix-core tile, masks on the last two
-    tiles): trees straddling tile and block edges, a single-row sequence and
-    an empty one in the call, bf16 output and determinism."""
+    """Trees of at most 16 nodes and 64 (node, head) columns per KV head
+    take the rows path (the decode kernel's matrix-core tile, masks on the
+    last two tiles; beyond 16 columns two or four waves per KV head sharing
+    its tiles through LDS): trees straddling tile and block edges, a
+    single-row sequence and an empty one in the call, bf16 output and
+    determinism."""
     hkv = 2
     ctx = [nodes, nodes + 1, 16, 17, 31, 32, 33, 64, 65, 1000, 4097]
     cases = [(c, nodes) for c in ctx if c >= nodes] + [(300, 1), (50, 0), (129, nodes - 1)]

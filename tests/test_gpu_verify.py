@@ -57,13 +57,13 @@ def test_verify_full_batch():
 
 
 def test_verify_split_variants():
-    """Stream-K chunks (items shared between workers, merged after the chunk
-    kernel) in every setting they meet: 16 query heads per KV head with 4
-    rows, non-causal, bf16 output, single-row sequences in the same call
-    (whose decode workspace sits in front of the stream-K part), and bitwise
-    determinism."""
+    """Stream-K chunks on the chunk kernel (items shared between workers,
+    merged after it) in every setting they meet: 16 query heads per KV head
+    with 8 rows (128 columns, too wide for the rows path), non-causal, bf16
+    output, single-row sequences in the same call (whose decode workspace
+    sits in front of the stream-K part), and bitwise determinism."""
     from tests.gpu_common import bf16_parity
-    cases = [(3000, 4), (2500, 1), (40, 3), (1800, 2), (4100, 4), (700, 1), (129, 4)]
+    cases = [(3000, 8), (2500, 1), (40, 3), (1800, 2), (4100, 8), (700, 1), (129, 4)]
     w = W.make_workload("verify_split_g16", [c for c, _ in cases], [q for _, q in cases],
                         num_q_heads=32, num_kv_heads=2, block_size=16, seed=4100)
     bc = W.materialize(w, logical=True, poison=True)
@@ -95,7 +95,9 @@ def test_verify_split_variants():
     ("sk_g4_r32", 16, 4, [(2000, 32), (32, 32), (700, 1), (4097, 17), (100, 0), (65, 32)]),
     ("sk_g1_r128", 2, 2, [(1500, 128), (128, 128), (3000, 77), (129, 1)]),
     # one long item over every worker: more pieces than the merge's 64 lanes
+    # (on the rows path with 24 columns, on the chunk kernel with 96)
     ("sk_one_long", 4, 1, [(100000, 6)]),
+    ("sk_one_long_g16", 16, 1, [(100000, 6)]),
 ])
 def test_streamk_widths_and_many_pieces(name, hq, hkv, cases):
     print(f"[stream-K] {name}", flush=True)
@@ -111,7 +113,7 @@ def test_streamk_widths_and_many_pieces(name, hq, hkv, cases):
     parity(out, ref, what=name)
 
 
-@pytest.mark.parametrize("group,rows", [(2, 16), (8, 16), (16, 8)])
+@pytest.mark.parametrize("group,rows", [(2, 24), (8, 16), (16, 8)])
 def test_streamk_merge_query_heads_grouped(group, rows):
     """With at least half as many (sequence, KV head) items as stream-K
     workers, the merge kernel takes several query heads of one KV head per
@@ -172,10 +174,12 @@ def rows_cases(rows):
 @pytest.mark.parametrize("bs", [16, 32])
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
 def test_rows_path_groups_and_edges(bs, group):
-    """Chunks of at most 16 (row, head) columns per KV head take the decode
-    kernel's matrix-core tile (the rows path): 16 rows at one query head per
-    KV head down to 2 at eight, causal and not, against the fp64 oracle."""
-    rows, hkv = 16 // group, 2
+    """Chunks of at most 16 rows and 64 (row, head) columns per KV head take
+    the decode kernel's matrix-core tile (the rows path): one wave per KV
+    head up to 16 columns, two or four sharing the KV head's tiles through
+    LDS beyond; 16 rows at one query head per KV head down to 8 at eight,
+    causal and not, against the fp64 oracle."""
+    rows, hkv = min(16, 64 // group), 2
     cases = rows_cases(rows)
     w = W.make_workload(f"rows_g{group}_bs{bs}", [c for c, _ in cases], [q for _, q in cases],
                         num_q_heads=hkv * group, num_kv_heads=hkv, block_size=bs,
@@ -218,11 +222,13 @@ def test_rows_path_split_bf16_out_and_determinism():
     bf16_parity(o16, o32, ref, what=w.name + " bf16 out", fp32_err=1e-3, min_within=0.95)
 
 
-@pytest.mark.parametrize("hkv,group", [(16, 1), (16, 4), (3, 2), (5, 8)])
-def test_rows_path_kv_head_layouts(hkv, group):
-    """The rows path's workgroups: 16 KV heads in two groups of 8 waves,
-    and KV head counts that are not powers of two."""
-    rows = 16 // group
+@pytest.mark.parametrize("hkv,group,rows", [(16, 1, 16), (16, 4, 4), (3, 2, 8), (5, 8, 2),
+                                            (3, 4, 8), (5, 4, 16), (16, 8, 8)])
+def test_rows_path_kv_head_layouts(hkv, group, rows):
+    """The rows path's workgroups: 16 KV heads in two groups of 8 waves, KV
+    head counts that are not powers of two, and the shared-staging
+    workgroups (two KV heads of two waves, or one of four) with a last group
+    short of a KV head."""
     cases = [(2000, rows), (77, rows), (16, rows), (900, 1)]
     w = W.make_workload(f"rows_hkv{hkv}_g{group}", [c for c, _ in cases], [q for _, q in cases],
                         num_q_heads=hkv * group, num_kv_heads=hkv, block_size=16,
