@@ -75,7 +75,6 @@ _DECODE_SRC = ["paged_kv_cache_98_amd/csrc/decode.hip", "paged_kv_cache_98_amd/c
 _PREFILL_SRC = ["paged_kv_cache_98_amd/csrc/prefill.hip", "paged_kv_cache_98_amd/csrc/decode_core.h",
                 "paged_kv_cache_98_amd/csrc/pkv_device.h"]
 _DECODE_K = ["decode_streamk_kernel", "decode_merge_kernel"]
-_VERIFY_K = ["prefill_streamk_kernel", "prefill_streamk_merge_kernel"]
 TRAFFIC_SPEC = {
     "llama8b_decode_b64": {"kernels": _DECODE_K, "sources": _DECODE_SRC, "args": ""},
     "long_context_decode_b8": {"kernels": _DECODE_K, "sources": _DECODE_SRC,
@@ -93,13 +92,14 @@ TRAFFIC_SPEC = {
                                "args": "--workload llama8b_decode_fp8"},
     "llama70b_decode_b256_bs16_fp8": {"kernels": _DECODE_K, "sources": _DECODE_SRC,
                                       "args": "--workload llama70b_decode_bs16_fp8"},
-    "spec_verify_b64_q6": {"kernels": _VERIFY_K, "sources": _PREFILL_SRC,
+    # the verify batches (6 rows, or 16-node trees, at 4 query heads per KV
+    # head) take the rows path: the decode kernels
+    "spec_verify_b64_q6": {"kernels": _DECODE_K, "sources": _DECODE_SRC,
                            "args": "--workload spec_verify"},
-    "spec_verify_b8_q6": {"kernels": _VERIFY_K, "sources": _PREFILL_SRC,
+    "spec_verify_b8_q6": {"kernels": _DECODE_K, "sources": _DECODE_SRC,
                           "args": "--workload spec_verify_long"},
-    "spec_tree_b64_n16": {"kernels": _VERIFY_K, "sources": _PREFILL_SRC,
+    "spec_tree_b64_n16": {"kernels": _DECODE_K, "sources": _DECODE_SRC,
                           "args": "--workload spec_verify_tree"},
-    # over FP8 pools the 6-row chunks take the rows path (the decode kernels)
     "spec_verify_b64_q6_fp8": {"kernels": _DECODE_K, "sources": _DECODE_SRC,
                                "args": "--workload spec_verify_fp8"},
     "mixed_prefill_c4x512_d0_fp8": {"kernels": ["prefill_mfma_kernel"], "sources": _PREFILL_SRC,
