@@ -13,7 +13,13 @@ Readings where the pages leave a step open:
     (bias 7), 3 mantissa bits; exponent 0 holds the subnormals m * 2^-9;
     S.1111.111 is NaN, so the largest finite magnitude is 448.
   * One scale per cache (k_scale for K, v_scale for V), given by the caller,
-    as in vLLM's fp8 KV cache: value = code_value * scale.
+    as in vLLM's fp8 KV cache: value = code_value * scale.  Or, as a second
+    form, one scale per (physical block, KV head) for each of K and V: every
+    scale argument below takes either a number or a [num_blocks,
+    num_kv_heads] array, and a value stored in block b for KV head h means
+    code_value * scale[b, h].  The caller chooses the scales (finite, > 0),
+    for instance from a block's absolute maximum; the append quantises with
+    the scale of the block a slot lies in.
   * Quantising x (a bf16 value): y = x / scale in IEEE binary32 (one correctly
     rounded division), clamped to [-448, 448], then rounded to the nearest
     E4M3 value, ties to the even code (the one with an even mantissa).
@@ -65,26 +71,42 @@ def e4m3_encode(y):
     return (sign | code).astype(np.uint8)
 
 
+def scale_table(scale, num_blocks, num_kv_heads):
+    """A cache's scale as a [num_blocks, num_kv_heads] float64 array: a
+    number is the same scale everywhere; an array must have that shape.
+    Every scale must be finite and > 0."""
+    a = np.asarray(scale, dtype=np.float64)
+    if a.ndim == 0:
+        a = np.full((num_blocks, num_kv_heads), float(a))
+    if a.shape != (num_blocks, num_kv_heads):
+        raise ValueError(f"scale table of shape {a.shape}, want {(num_blocks, num_kv_heads)}")
+    if not np.all(np.isfinite(a) & (a > 0)):
+        raise ValueError("scales must be finite and > 0")
+    return a
+
+
 def quantise(x_bf16_bits, scale):
-    """bf16 values (uint16 bit patterns, any shape) -> E4M3 codes, with the
-    cache's scale."""
+    """bf16 values (uint16 bit patterns, any shape) -> E4M3 codes, with a
+    scale (a number, or binary32 values broadcast against the input)."""
     bits = np.asarray(x_bf16_bits).astype(np.uint16).astype(np.uint32) << 16
     x = bits.view(np.float32)
-    y = x / np.float32(scale)                       # one binary32 division
+    y = x / np.asarray(scale, dtype=np.float32)     # one binary32 division
     y = np.clip(y, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
     return e4m3_encode(y)
 
 
 def kv_append_fp8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale):
     """Quantised append: token t's K/V rows (bf16 bits [T, Hkv, D]) are
-    quantised and written at slot s = slot_mapping[t] of the code pools
-    ([NB, bs, Hkv, D] uint8), skipped when s < 0.  Returns new pools."""
+    quantised with the scales of the block their slot s = slot_mapping[t]
+    lies in (block s // bs, one scale per KV head) and written at slot s of
+    the code pools ([NB, bs, Hkv, D] uint8), skipped when s < 0.  Returns
+    new pools."""
     kc, vc = np.array(k_cache, dtype=np.uint8), np.array(v_cache, dtype=np.uint8)
     nb, bs, hkv, d = kc.shape
     slots = np.asarray(slot_mapping, dtype=np.int64)
-    kq = quantise(k_new, k_scale)
-    vq = quantise(v_new, v_scale)
-    if kq.shape != (slots.shape[0], hkv, d) or vq.shape != kq.shape:
+    ks, vs = scale_table(k_scale, nb, hkv), scale_table(v_scale, nb, hkv)
+    k_new, v_new = np.asarray(k_new), np.asarray(v_new)
+    if k_new.shape != (slots.shape[0], hkv, d) or v_new.shape != k_new.shape:
         raise ValueError("shape mismatch")
     flat_k = kc.reshape(nb * bs, hkv, d)
     flat_v = vc.reshape(nb * bs, hkv, d)
@@ -93,9 +115,19 @@ def kv_append_fp8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale
             continue
         if s >= nb * bs:
             raise ValueError(f"slot {s} outside the pool")
-        flat_k[s] = kq[t]
-        flat_v[s] = vq[t]
+        blk = s // bs
+        flat_k[s] = quantise(k_new[t], ks[blk][:, None])
+        flat_v[s] = quantise(v_new[t], vs[blk][:, None])
     return kc, vc
+
+
+def dequantise_rows(codes, scales, ids, n):
+    """The first n token rows of a sequence whose blocks are `ids`, as values:
+    code value x the scale of (block, KV head).  codes [NB, bs, Hkv, D],
+    scales [NB, Hkv]; returns [n, Hkv, D] float64."""
+    nb, bs, hkv, d = codes.shape
+    vals = e4m3_value(codes[ids]) * scales[ids][:, None, :, None]
+    return vals.reshape(len(ids) * bs, hkv, d)[:n]
 
 
 def paged_decode_fp8(q_bf16_bits, k_codes, v_codes, k_scale, v_scale, block_table,
@@ -103,8 +135,9 @@ def paged_decode_fp8(q_bf16_bits, k_codes, v_codes, k_scale, v_scale, block_tabl
     """fp64 decode attention over FP8 pools: for sequence i and query head h
     (KV head h // (Hq / Hkv)), gather the first context_lens[i] token rows
     through the block table, dequantise (code value x cache scale), then
-    softmax(scale * q.K) . V with the stable three-sweep softmax.  A row with
-    no keys is all zeros.  Returns [B, Hq, D] float64."""
+    softmax(scale * q.K) . V with the stable three-sweep softmax.  The scales
+    are numbers or [NB, Hkv] tables (see scale_table).  A row with no keys is
+    all zeros.  Returns [B, Hq, D] float64."""
     qb = np.asarray(q_bf16_bits).astype(np.uint16).astype(np.uint32) << 16
     q = qb.view(np.float32).astype(np.float64)
     kc, vc = np.asarray(k_codes, dtype=np.uint8), np.asarray(v_codes, dtype=np.uint8)
@@ -115,6 +148,7 @@ def paged_decode_fp8(q_bf16_bits, k_codes, v_codes, k_scale, v_scale, block_tabl
     if d2 != d or hq % hkv or bt.shape[0] != b or ctx.shape != (b,):
         raise ValueError("shape mismatch")
     g = hq // hkv
+    ks, vs = scale_table(k_scale, nb, hkv), scale_table(v_scale, nb, hkv)
     out = np.zeros((b, hq, d), dtype=np.float64)
     for i in range(b):
         n = int(ctx[i])
@@ -124,8 +158,8 @@ def paged_decode_fp8(q_bf16_bits, k_codes, v_codes, k_scale, v_scale, block_tabl
         ids = bt[i, :nblk]
         if np.any(ids < 0) or np.any(ids >= nb):
             raise ValueError(f"sequence {i}: block id outside the pool")
-        k = e4m3_value(kc[ids].reshape(nblk * bs, hkv, d)[:n]) * float(k_scale)
-        v = e4m3_value(vc[ids].reshape(nblk * bs, hkv, d)[:n]) * float(v_scale)
+        k = dequantise_rows(kc, ks, ids, n)
+        v = dequantise_rows(vc, vs, ids, n)
         for h in range(hq):
             kv = h // g
             s = float(scale) * (k[:, kv, :] @ q[i, h])
@@ -139,9 +173,9 @@ def paged_prefill_fp8(q_bf16_bits, k_codes, v_codes, k_scale, v_scale, block_tab
     """fp64 chunked attention over FP8 pools: sequence i has query rows
     cu_q_lens[i] .. cu_q_lens[i + 1] - 1; row r sits at position
     context_lens[i] - Lq_i + r and sees keys 0 .. position (all
-    context_lens[i] keys when not causal), dequantised (code value x cache
-    scale), with the stable three-sweep softmax.  Returns [sum Lq, Hq, D]
-    float64."""
+    context_lens[i] keys when not causal), dequantised (code value x its
+    scale: a number, or an [NB, Hkv] table), with the stable three-sweep
+    softmax.  Returns [sum Lq, Hq, D] float64."""
     qb = np.asarray(q_bf16_bits).astype(np.uint16).astype(np.uint32) << 16
     q = qb.view(np.float32).astype(np.float64)
     kc, vc = np.asarray(k_codes, dtype=np.uint8), np.asarray(v_codes, dtype=np.uint8)
@@ -155,6 +189,7 @@ def paged_prefill_fp8(q_bf16_bits, k_codes, v_codes, k_scale, v_scale, block_tab
     if cu[-1] != t:
         raise ValueError("cu_q_lens does not end at the number of query rows")
     g = hq // hkv
+    ks, vs = scale_table(k_scale, nb, hkv), scale_table(v_scale, nb, hkv)
     out = np.zeros((t, hq, d), dtype=np.float64)
     for i in range(ctx.shape[0]):
         n, lq = int(ctx[i]), int(cu[i + 1] - cu[i])
@@ -166,8 +201,8 @@ def paged_prefill_fp8(q_bf16_bits, k_codes, v_codes, k_scale, v_scale, block_tab
         ids = bt[i, :nblk]
         if np.any(ids < 0) or np.any(ids >= nb):
             raise ValueError(f"sequence {i}: block id outside the pool")
-        k = e4m3_value(kc[ids].reshape(nblk * bs, hkv, d)[:n]) * float(k_scale)
-        v = e4m3_value(vc[ids].reshape(nblk * bs, hkv, d)[:n]) * float(v_scale)
+        k = dequantise_rows(kc, ks, ids, n)
+        v = dequantise_rows(vc, vs, ids, n)
         for r in range(lq):
             seen = n - lq + r + 1 if causal else n
             for h in range(hq):

@@ -1,8 +1,9 @@
 """The FP8 (E4M3) oracle pinned: the format's defining values, the encoder
 against brute-force nearest-value search, the quantiser's direction and
-clamp, the quantised append against the C oracle's byte copy, and the FP8
-decode against the C oracle's bf16 attention on exactly representable
-values."""
+clamp, the quantised append against the C oracle's byte copy (and, with
+per-(block, head) scales, against brute-force encoding), and the FP8 decode
+and chunked prefill against the C oracle's bf16 attention on exactly
+representable values, with one scale per cache or per (block, head)."""
 import numpy as np
 import pytest
 
@@ -148,6 +149,97 @@ def test_pin_prefill_against_bf16_oracle(causal):
     assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
     dec = fp8.paged_decode_fp8(q[cu[2]:cu[3]], kc, vc, k_scale, v_scale, bt[2:3], ctx[2:3], scale)
     assert np.allclose(got[cu[2]:cu[3]], dec, rtol=1e-12, atol=1e-12)
+
+
+def test_pin_append_per_block_head_scales():
+    """Per-(block, head) scales: every written code is the brute-force
+    nearest E4M3 value to the binary32 quotient of the input by the scale of
+    the slot's block and the row's KV head, clamped to +-448; a table holding
+    one value everywhere gives the per-cache append bit for bit."""
+    rng = np.random.default_rng(21)
+    nb, bs, hkv, d, t = 5, 16, 3, 128, 30
+    k_new = bf16_bits(rng.standard_normal((t, hkv, d)) * 40.0)
+    v_new = bf16_bits(rng.standard_normal((t, hkv, d)))
+    slots = rng.permutation(nb * bs)[:t].astype(np.int64)
+    slots[::5] = -1
+    ks = np.exp(rng.uniform(np.log(2.0 ** -4), np.log(2.0 ** 3), size=(nb, hkv))).astype(np.float32)
+    vs = np.exp(rng.uniform(np.log(2.0 ** -8), np.log(1.0), size=(nb, hkv))).astype(np.float32)
+    k0 = rng.integers(0, 256, size=(nb, bs, hkv, d), dtype=np.uint8)
+    v0 = rng.integers(0, 256, size=(nb, bs, hkv, d), dtype=np.uint8)
+    kc, vc = fp8.kv_append_fp8(k_new, v_new, slots, k0, v0, ks, vs)
+    flat_k, flat_v = kc.reshape(nb * bs, hkv, d), vc.reshape(nb * bs, hkv, d)
+    for ti, sl in enumerate(slots):
+        if sl < 0:
+            continue
+        for h in range(hkv):
+            for src, dst, tab in ((k_new, flat_k, ks), (v_new, flat_v, vs)):
+                x = (src[ti, h].astype(np.uint32) << 16).view(np.float32)
+                y = np.clip(x / np.float32(tab[sl // bs, h]), np.float32(-448.0), np.float32(448.0))
+                assert np.array_equal(dst[sl, h], brute_encode(y)), (ti, h)
+    untouched = np.setdiff1d(np.arange(nb * bs), slots[slots >= 0])
+    assert np.array_equal(flat_k[untouched], k0.reshape(nb * bs, hkv, d)[untouched])
+    one = np.full((nb, hkv), 0.25, dtype=np.float32)
+    a = fp8.kv_append_fp8(k_new, v_new, slots, k0, v0, one, one)
+    b = fp8.kv_append_fp8(k_new, v_new, slots, k0, v0, 0.25, 0.25)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    with pytest.raises(ValueError):
+        fp8.kv_append_fp8(k_new, v_new, slots, k0, v0, ks[:, :2], vs)
+    with pytest.raises(ValueError):
+        fp8.kv_append_fp8(k_new, v_new, slots, k0, v0, -ks, vs)
+
+
+def _pow2_tables(rng, nb, hkv):
+    """Power-of-two scales per (block, head): code values times them stay
+    exactly representable in bf16, so the C oracle can take them as pools."""
+    ks = np.ldexp(1.0, rng.integers(-3, 4, size=(nb, hkv))).astype(np.float32)
+    vs = np.ldexp(1.0, rng.integers(-3, 4, size=(nb, hkv))).astype(np.float32)
+    return ks, vs
+
+
+def _values_as_bf16(codes, tab):
+    vals = fp8.e4m3_value(codes) * tab[:, None, :, None]
+    b = bf16_bits(vals.astype(np.float32))
+    assert np.array_equal((b.astype(np.uint32) << 16).view(np.float32), vals.astype(np.float32))
+    return b
+
+
+def test_pin_decode_per_block_head_against_bf16_oracle():
+    """With power-of-two scales per (block, head), pools holding each code's
+    value times its block's scale are exact bf16 pools, and the C oracle's
+    attention over them is the FP8 decode with those scale tables."""
+    rng = np.random.default_rng(22)
+    b, hq, hkv, d, bs, nb = 5, 8, 2, 128, 16, 40
+    ctx = np.array([1, 17, 64, 100, 0], dtype=np.int32)
+    kc = rng.integers(0, 256, size=(nb, bs, hkv, d), dtype=np.uint8) & 0xDF
+    vc = rng.integers(0, 256, size=(nb, bs, hkv, d), dtype=np.uint8) & 0xDF
+    ks, vs = _pow2_tables(rng, nb, hkv)
+    bt = rng.permutation(nb)[: b * 8].reshape(b, 8).astype(np.int32)
+    q = bf16_bits(rng.standard_normal((b, hq, d)) * 0.05)
+    scale = 2.0 ** -4
+    got = fp8.paged_decode_fp8(q, kc, vc, ks, vs, bt, ctx, scale)
+    ref = oracle.paged_attention(q, _values_as_bf16(kc, ks), _values_as_bf16(vc, vs), bt, ctx, scale)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+    assert np.all(got[4] == 0.0)
+
+
+def test_pin_prefill_per_block_head_against_bf16_oracle():
+    """The chunked FP8 reference with per-(block, head) power-of-two scales
+    equals the C oracle's chunked attention over the scaled values as bf16."""
+    rng = np.random.default_rng(23)
+    hq, hkv, d, bs, nb = 8, 2, 128, 32, 30
+    ctx = np.array([37, 141, 64, 100, 9], dtype=np.int32)
+    lq = np.array([37, 20, 1, 7, 3], dtype=np.int32)
+    cu = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    kc = rng.integers(0, 256, size=(nb, bs, hkv, d), dtype=np.uint8) & 0xDF
+    vc = rng.integers(0, 256, size=(nb, bs, hkv, d), dtype=np.uint8) & 0xDF
+    ks, vs = _pow2_tables(rng, nb, hkv)
+    bt = rng.permutation(nb)[: 5 * 5].reshape(5, 5).astype(np.int32)
+    q = bf16_bits(rng.standard_normal((int(cu[-1]), hq, d)) * 0.05)
+    scale = 2.0 ** -4
+    got = fp8.paged_prefill_fp8(q, kc, vc, ks, vs, bt, ctx, cu, scale)
+    ref = oracle.paged_attention(q, _values_as_bf16(kc, ks), _values_as_bf16(vc, vs), bt, ctx,
+                                 scale, cu_q_lens=cu, causal=True)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
 
 
 def _attend(q, k, v, scale):
