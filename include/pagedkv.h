@@ -236,6 +236,54 @@ int pkv_paged_decode_attn_fp8(void *out, int out_dtype, const void *q, const voi
                               float scale, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * FP8 pools with one scale per (physical block, KV head) for K and one for
+ * V, instead of one per cache (the same pages: FP8 quantisation of the KV
+ * cache; a finer scale keeps a head or block of large values from pushing
+ * the others' codes toward the subnormals).  k_scales / v_scales: device
+ * arrays of fp32, [num_blocks][num_kv_heads], 4-byte aligned, owned by the
+ * caller; a value stored in block b for KV head h stands for
+ * E4M3(code) * scale[b][h].  The caller chooses the scales (for instance
+ * from a block's absolute maximum when the block is first written) and
+ * keeps them with the block: a block's scale must not change while it holds
+ * codes.  Scales must be finite and > 0; other values give unspecified
+ * results (never a memory access outside the arrays the caller passes).
+ *
+ * kv_append_fp8_per_block -- pkv_kv_append_fp8 with the scale of the block
+ * each slot lies in (slot / block_size) and of the row's KV head: each
+ * value x is stored as the E4M3 code nearest to x / scale[b][h] (one
+ * correctly rounded binary32 division), clamped to +-448, ties to the even
+ * code.  Slots past num_blocks * block_size, or negative, are skipped.
+ * PKV_ERR_NULL if a table is NULL, PKV_ERR_ALIGN if one is not 4-byte
+ * aligned; the other errors as pkv_kv_append_fp8.
+ */
+int pkv_kv_append_fp8_per_block(const void *k_new, const void *v_new,
+                                const int64_t *slot_mapping, int64_t num_tokens, void *k_cache,
+                                void *v_cache, int64_t num_blocks, int block_size,
+                                int num_kv_heads, int head_dim, const float *k_scales,
+                                const float *v_scales, void *stream);
+
+/*
+ * paged_decode_attn_fp8_per_block -- pkv_paged_decode_attn over FP8 pools
+ * with per-(block, KV head) scales:
+ *   out[i, h, :] = sum_t softmax_t(scale * <q[i,h], ks(t) * Kc_i[t]>) vs(t) * Vc_i[t]
+ * with ks(t), vs(t) the scales of the block holding token t, for KV head
+ * h / G.  Same arguments, workspace and limits as pkv_paged_decode_attn,
+ * plus the two tables.  Each 16-token tile reads its block's two scales:
+ * the K scale joins that tile's score scale, the V scale weights its P V
+ * product as the ratio to the largest V scale seen so far (P times that
+ * ratio rounds to fp16, relative error 2^-11); the rest as
+ * pkv_paged_decode_attn_fp8.
+ */
+int pkv_paged_decode_attn_fp8_per_block(void *out, int out_dtype, const void *q,
+                                        const void *k_cache, const void *v_cache,
+                                        const float *k_scales, const float *v_scales,
+                                        const int32_t *block_table, int max_blocks_per_seq,
+                                        const int32_t *context_lens, int max_context_len,
+                                        int num_seqs, int num_q_heads, int num_kv_heads,
+                                        int head_dim, int block_size, float scale,
+                                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Workspace needed by pkv_paged_prefill_attn and its FP8 and tree variants
  * (bytes, >= 0; 0 for inconsistent sizes), the larger of what the call's
  * path needs over bf16 and over FP8 pools.  With C = max_q_len *

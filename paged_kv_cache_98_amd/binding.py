@@ -40,7 +40,8 @@ EXPORTED = ("pkv_status_string", "pkv_version", "pkv_kv_append", "pkv_decode_wor
             "pkv_bm_allocate", "pkv_bm_allocate_cached", "pkv_bm_num_cached", "pkv_bm_free", "pkv_bm_fork", "pkv_bm_append", "pkv_bm_append_batch",
             "pkv_bm_seq_info",
             "pkv_bm_refcount", "pkv_bm_block_table", "pkv_paged_decode_attn_noalloc",
-            "pkv_decode_noalloc_max_bytes")
+            "pkv_decode_noalloc_max_bytes", "pkv_kv_append_fp8_per_block",
+            "pkv_paged_decode_attn_fp8_per_block")
 
 _lib = None
 
@@ -122,6 +123,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_paged_decode_attn_fp8.argtypes = [_vp, _i32, _vp, _vp, _vp, _f32, _f32, _vp, _i32, _vp,
                                               _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz,
                                               _vp]
+    lib.pkv_kv_append_fp8_per_block.restype = _i32
+    lib.pkv_kv_append_fp8_per_block.argtypes = [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i32, _i32,
+                                                _i32, _vp, _vp, _vp]
+    lib.pkv_paged_decode_attn_fp8_per_block.restype = _i32
+    lib.pkv_paged_decode_attn_fp8_per_block.argtypes = [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                        _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                                        _i32, _f32, _vp, _sz, _vp]
     lib.pkv_copy_blocks.restype = _i32
     lib.pkv_copy_blocks.argtypes = [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _i64, _vp]
     lib.pkv_bm_create.restype = _vp
@@ -229,6 +237,30 @@ def kv_append_fp8(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.
                                  float(k_scale), float(v_scale), _stream(stream)))
 
 
+def _scale_table(t: torch.Tensor, name: str, nb: int, hkv: int) -> int:
+    if t.shape != (nb, hkv):
+        raise ValueError(f"{name}: want [{nb}, {hkv}] (num_blocks, num_kv_heads), got {tuple(t.shape)}")
+    return _dev(t, name, torch.float32)
+
+
+def kv_append_fp8_per_block(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                            k_cache: torch.Tensor, v_cache: torch.Tensor, k_scales: torch.Tensor,
+                            v_scales: torch.Tensor, stream=None) -> None:
+    """pkv_kv_append_fp8_per_block: as kv_append_fp8, with one scale per
+    (block, KV head): k_scales / v_scales fp32 [NB, Hkv] on the device."""
+    lib = load_library()
+    nb, bs, hkv, d = k_cache.shape
+    t = slot_mapping.shape[0]
+    if k_new.shape != (t, hkv, d) or v_new.shape != k_new.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between new rows, slots and pools")
+    _check(lib.pkv_kv_append_fp8_per_block(
+        _dev(k_new, "k_new", torch.bfloat16), _dev(v_new, "v_new", torch.bfloat16),
+        _dev(slot_mapping, "slot_mapping", torch.int64), t, _dev(k_cache, "k_cache", torch.uint8),
+        _dev(v_cache, "v_cache", torch.uint8), nb, bs, hkv, d,
+        _scale_table(k_scales, "k_scales", nb, hkv), _scale_table(v_scales, "v_scales", nb, hkv),
+        _stream(stream)))
+
+
 def paged_prefill_attn_fp8(q: torch.Tensor, cu_q_lens: torch.Tensor, k_cache: torch.Tensor,
                            v_cache: torch.Tensor, k_scale: float, v_scale: float,
                            block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
@@ -304,6 +336,40 @@ def paged_decode_attn_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
         float(k_scale), float(v_scale), _dev(block_table, "block_table", torch.int32),
         block_table.shape[1], _dev(context_lens, "context_lens", torch.int32), max_context_len,
         b, hq, hkv, d, bs, float(scale), ws_ptr, ws_len, _stream(stream)))
+    return out
+
+
+def paged_decode_attn_fp8_per_block(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                    k_scales: torch.Tensor, v_scales: torch.Tensor,
+                                    block_table: torch.Tensor, context_lens: torch.Tensor,
+                                    scale: float, max_context_len: Optional[int] = None,
+                                    out: Optional[torch.Tensor] = None, out_dtype=torch.float32,
+                                    workspace: Optional[torch.Tensor] = None,
+                                    stream=None) -> torch.Tensor:
+    """pkv_paged_decode_attn_fp8_per_block: q [B, Hq, D] bf16 over FP8 pools
+    whose values are code * k_scales[block, KV head] (fp32 [NB, Hkv] tables,
+    likewise for V) -> out [B, Hq, D]."""
+    lib = load_library()
+    b, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if d2 != d or block_table.dim() != 2 or block_table.shape[0] != b:
+        raise ValueError("shape mismatch")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if b else 0
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=out_dtype, device=q.device)
+    need = lib.pkv_decode_workspace_bytes(b, hq, hkv, d, max_context_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pkv_paged_decode_attn_fp8_per_block(
+        _dev(out, "out"), _out_code(out.dtype), _dev(q, "q", torch.bfloat16),
+        _dev(k_cache, "k_cache", torch.uint8), _dev(v_cache, "v_cache", torch.uint8),
+        _scale_table(k_scales, "k_scales", nb, hkv), _scale_table(v_scales, "v_scales", nb, hkv),
+        _dev(block_table, "block_table", torch.int32), block_table.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), max_context_len, b, hq, hkv, d, bs,
+        float(scale), ws_ptr, ws_len, _stream(stream)))
     return out
 
 

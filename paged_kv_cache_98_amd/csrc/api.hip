@@ -27,6 +27,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // A cache scale: finite and positive.
 bool valid_scale(float s) { return s > 0.0f && s <= 3.402823466e38f; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
 
@@ -216,7 +217,8 @@ int decode_call(void* out, int out_dtype, const void* q, const void* k_cache, co
                 int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
                 int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                 float scale, void* workspace, size_t workspace_bytes, void* stream,
-                bool fixed_scratch = false) {
+                bool fixed_scratch = false, const float* k_scales = nullptr,
+                const float* v_scales = nullptr) {
     int st = check_attention_shape(max_blocks_per_seq, max_context_len, num_seqs, num_q_heads,
                                    num_kv_heads, head_dim, block_size, out_dtype);
     if (st != PKV_OK) return st;
@@ -227,6 +229,10 @@ int decode_call(void* out, int out_dtype, const void* q, const void* k_cache, co
     if (!out || !q || !k_cache || !v_cache || !block_table || !context_lens) return PKV_ERR_NULL;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
         return PKV_ERR_ALIGN;
+    if (kv_fp8 && (k_scales != nullptr || v_scales != nullptr)) {
+        if (!k_scales || !v_scales) return PKV_ERR_NULL;
+        if (!aligned4(k_scales) || !aligned4(v_scales)) return PKV_ERR_ALIGN;
+    }
     const size_t need = pkv::decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                     max_context_len);
     if (fixed_scratch) {
@@ -257,6 +263,10 @@ int decode_call(void* out, int out_dtype, const void* q, const void* k_cache, co
     a.block_size = block_size;
     a.scale_log2 = scale * 1.4426950408889634f;
     if (kv_fp8) a.scale_log2 *= k_scale;
+    if (kv_fp8 && k_scales) {
+        a.k_scales = k_scales;
+        a.v_scales = v_scales;
+    }
     a.seq_workers = static_cast<int32_t*>(workspace);
     a.records = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                          align_up((size_t)2 * num_seqs * sizeof(int32_t), 256));
@@ -306,10 +316,29 @@ int pkv_paged_decode_attn_fp8(void* out, int out_dtype, const void* q, const voi
                        stream);
 }
 
-int pkv_kv_append_fp8(const void* k_new, const void* v_new, const int64_t* slot_mapping,
-                      int64_t num_tokens, void* k_cache, void* v_cache, int64_t num_blocks,
-                      int block_size, int num_kv_heads, int head_dim, float k_scale,
-                      float v_scale, void* stream) {
+int pkv_paged_decode_attn_fp8_per_block(void* out, int out_dtype, const void* q,
+                                        const void* k_cache, const void* v_cache,
+                                        const float* k_scales, const float* v_scales,
+                                        const int32_t* block_table, int max_blocks_per_seq,
+                                        const int32_t* context_lens, int max_context_len,
+                                        int num_seqs, int num_q_heads, int num_kv_heads,
+                                        int head_dim, int block_size, float scale,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+    if (num_seqs > 0 && (!k_scales || !v_scales)) return PKV_ERR_NULL;
+    return decode_call(out, out_dtype, q, k_cache, v_cache, true, 1.0f, 1.0f, block_table,
+                       max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
+                       num_kv_heads, head_dim, block_size, scale, workspace, workspace_bytes,
+                       stream, false, k_scales, v_scales);
+}
+
+}  // extern "C"
+
+namespace {
+
+int append_fp8_call(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                    int64_t num_tokens, void* k_cache, void* v_cache, int64_t num_blocks,
+                    int block_size, int num_kv_heads, int head_dim, float k_scale, float v_scale,
+                    const float* k_scales, const float* v_scales, void* stream) {
     if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0) return PKV_ERR_SHAPE;
     if (head_dim != pkv::kHeadDim) return PKV_ERR_UNSUPPORTED;
     if (block_size != 16 && block_size != 32) return PKV_ERR_UNSUPPORTED;
@@ -318,6 +347,10 @@ int pkv_kv_append_fp8(const void* k_new, const void* v_new, const int64_t* slot_
     if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PKV_ERR_NULL;
     if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
         return PKV_ERR_ALIGN;
+    if (k_scales || v_scales) {
+        if (!k_scales || !v_scales) return PKV_ERR_NULL;
+        if (!aligned4(k_scales) || !aligned4(v_scales)) return PKV_ERR_ALIGN;
+    }
     pkv::AppendFp8Args a;
     a.k_new = static_cast<const uint16_t*>(k_new);
     a.v_new = static_cast<const uint16_t*>(v_new);
@@ -329,7 +362,34 @@ int pkv_kv_append_fp8(const void* k_new, const void* v_new, const int64_t* slot_
     a.num_slots = num_blocks * block_size;
     a.k_scale = k_scale;
     a.v_scale = v_scale;
+    a.k_scales = k_scales;
+    a.v_scales = v_scales;
+    a.block_size = block_size;
     return to_status(pkv::launch_kv_append_fp8(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_kv_append_fp8(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                      int64_t num_tokens, void* k_cache, void* v_cache, int64_t num_blocks,
+                      int block_size, int num_kv_heads, int head_dim, float k_scale,
+                      float v_scale, void* stream) {
+    return append_fp8_call(k_new, v_new, slot_mapping, num_tokens, k_cache, v_cache, num_blocks,
+                           block_size, num_kv_heads, head_dim, k_scale, v_scale, nullptr,
+                           nullptr, stream);
+}
+
+int pkv_kv_append_fp8_per_block(const void* k_new, const void* v_new,
+                                const int64_t* slot_mapping, int64_t num_tokens, void* k_cache,
+                                void* v_cache, int64_t num_blocks, int block_size,
+                                int num_kv_heads, int head_dim, const float* k_scales,
+                                const float* v_scales, void* stream) {
+    if (num_tokens > 0 && (!k_scales || !v_scales)) return PKV_ERR_NULL;
+    return append_fp8_call(k_new, v_new, slot_mapping, num_tokens, k_cache, v_cache, num_blocks,
+                           block_size, num_kv_heads, head_dim, 1.0f, 1.0f, k_scales, v_scales,
+                           stream);
 }
 
 size_t pkv_prefill_workspace_bytes(int num_seqs, int num_q_tokens, int max_q_len,

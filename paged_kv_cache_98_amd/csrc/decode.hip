@@ -26,7 +26,8 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
                       int max_context_len, int num_seqs, int num_q_heads, int num_kv_heads,
                       float scale_log2, float out_scale, int num_workers,
                       const int32_t* __restrict__ cu_q_lens, int max_rows, int causal,
-                      const uint64_t* __restrict__ tree_mask) {
+                      const uint64_t* __restrict__ tree_mask, const float* __restrict__ k_scales,
+                      const float* __restrict__ v_scales) {
     constexpr int kWaves = kMaxWavesPerWorker;
     extern __shared__ int32_t s_cum[];
     __shared__ int32_t s_part[kWaves];
@@ -39,7 +40,7 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
         out, rec, seq_workers, q, k_cache, v_cache, block_table, max_blocks_per_seq,
         context_lens, max_context_len, num_seqs, num_q_heads, num_kv_heads, scale_log2, out_scale,
         num_workers, cu_q_lens, s_cum, s_part, blockIdx.x, blockIdx.y, s_vx, max_rows, causal,
-        tree_mask, s_q, s_st);
+        tree_mask, s_q, s_st, k_scales, v_scales);
 }
 
 // Finishes every (sequence, query row, query head): zero rows for empty
@@ -148,7 +149,7 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
                        a.v_cache, a.block_table, a.max_blocks_per_seq, a.context_lens,
                        a.max_context_len, a.num_seqs, a.num_q_heads, a.num_kv_heads, a.scale_log2,
                        a.out_scale, (int)workers, a.cu_q_lens, a.rows, a.causal ? 1 : 0,
-                       a.tree_mask);
+                       a.tree_mask, a.k_scales, a.v_scales);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_decode_merge(a, stream);
@@ -217,8 +218,26 @@ hipError_t launch_decode_bf16_bs(const DecodeArgs& a, hipStream_t s) {
 // batch (8 heads) 303 -> 171 us, 8B-shaped batch (4 heads) 74.6 -> 59.7 us.
 // With 1 or 2 heads the columns are mostly padding and the gain was 2-3 %,
 // so those keep the VALU tile (16 dims per lane).
+// FP8 pools with per-(block, KV head) scales: single-row decodes only (the
+// two-column-block tile of the rows path would spill with the scales' extra
+// registers).
+template <int BS>
+hipError_t launch_decode_fp8_bh_bs(const DecodeArgs& a, hipStream_t s) {
+    if (a.rows > 1 || a.cu_q_lens != nullptr) return hipErrorInvalidValue;
+    switch (a.num_q_heads / a.num_kv_heads) {
+        case 1: return launch_decode_g<KvFp8WideBh, BS, 1>(a, s);
+        case 2: return launch_decode_g<KvFp8WideBh, BS, 2>(a, s);
+        case 4: return launch_decode_g<KvFp8MfmaBh, BS, 4>(a, s);
+        case 8: return launch_decode_g<KvFp8MfmaBh, BS, 8>(a, s);
+        case 16: return launch_decode_g<KvFp8MfmaBh, BS, 16>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <int BS>
 hipError_t launch_decode_fp8_bs(const DecodeArgs& a, hipStream_t s) {
+    // per-(block, KV head) scales: the same tiles reading them per tile
+    if (a.k_scales != nullptr) return launch_decode_fp8_bh_bs<BS>(a, s);
     if (a.rows > 1) return launch_rows_bs<KvFp8Mfma, BS>(a, s);
     switch (a.num_q_heads / a.num_kv_heads) {
         case 1: return launch_decode_g<KvFp8Wide, BS, 1>(a, s);

@@ -59,7 +59,8 @@ namespace dec {
 //     exact: every E4M3 value is a bf16 value);
 //   * V comes out as floats, or, for FP8, as fp16 pairs over two tokens.
 // The FP8 cache's two scales are applied outside the tile loop: k_scale
-// inside the score scale, v_scale on the finished output.
+// inside the score scale, v_scale on the finished output.  Pools with one
+// scale per (block, KV head) (kBlockScales) take them per tile instead.
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 // bf16 pools: 8 dims (16 bytes) per lane and token, rows of 16 lanes.
@@ -68,6 +69,7 @@ struct KvBf16 {
     static constexpr int kDims = 8;
     static constexpr bool kPairedPV = false;
     static constexpr bool kMfma = false;
+    static constexpr bool kBlockScales = false;
     using Word = uint4;
     static __device__ __forceinline__ Word load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
         return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
@@ -138,6 +140,7 @@ struct KvFp8Base {
     static constexpr int kDims = 4 * NWORDS;
     static constexpr bool kPairedPV = true;
     static constexpr bool kMfma = false;
+    static constexpr bool kBlockScales = false;
     template <bool HIGH>  // codes 2, 3 of the word instead of 0, 1
     static __device__ __forceinline__ uint32_t bf16_pair(uint32_t codes) {
         return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(
@@ -230,6 +233,32 @@ struct KvFp8Mfma : KvFp8Wide {
     }
 };
 
+// FP8 pools with one scale per (physical block, KV head) for K and one for
+// V, read per tile (a 16-token tile lies in one block): the K scale joins
+// the score scale of that tile; the V scale enters P V as the ratio
+// vs / vref <= 1 to a reference that only grows (the largest V scale the
+// piece has met; the accumulator is rescaled by vref_old / vref_new when
+// it moves, as for a running maximum), so P * ratio stays in [0, 1] for its
+// fp16 rounding, and the piece's result is multiplied by vref at its end.
+// The running sum l takes the unscaled weights.
+struct KvFp8WideBh : KvFp8Wide {
+    static constexpr bool kBlockScales = true;
+};
+struct KvFp8MfmaBh : KvFp8Mfma {
+    static constexpr bool kBlockScales = true;
+};
+
+// A tile's two scales, from the [num_blocks][num_kv_heads] fp32 tables:
+// lane-uniform buffer loads, issued with the tile's own loads (vector
+// memory, so they complete in order with them).
+__device__ __forceinline__ void load_block_scales(const float* k_scales, const float* v_scales,
+                                                  int phys, int num_kv_heads, int kvh, float& ks,
+                                                  float& vs) {
+    const size_t e = (size_t)phys * num_kv_heads + kvh;
+    ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(k_scales + e), 0, 0, 0));
+    vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(v_scales + e), 0, 0, 0));
+}
+
 template <typename KV>
 struct Layout {
     static constexpr int kDims = KV::kDims;                  // per lane and token
@@ -248,6 +277,7 @@ template <typename KV>
 struct Tile {
     typename KV::Word k[Layout<KV>::kLoads];
     typename KV::Word v[Layout<KV>::kLoads];
+    float ks, vs;  // the block's scales (kBlockScales)
 };
 
 // Loads one tile: `kt` / `vt` address the tile's first row for this KV head
@@ -280,7 +310,7 @@ struct State {
 template <typename KV, int G, bool PARTIAL>
 __device__ __forceinline__ void process_tile(State<G, KV::kDims>& st, const Tile<KV>& t,
                                              const uint32_t (&qv)[G][KV::kDims / 2], float c,
-                                             int row, int ntok_left) {
+                                             int row, int ntok_left, float vr = 1.0f) {
     constexpr int kLoads = Layout<KV>::kLoads;
     constexpr int kRows = Layout<KV>::kRows;
     constexpr int ND = KV::kDims;
@@ -388,7 +418,12 @@ __device__ __forceinline__ void process_tile(State<G, KV::kDims>& st, const Tile
         for (int i = 0; i < kLoads; i += 2) {
             f16x2_t pp[G];
 #pragma unroll
-            for (int g = 0; g < G; ++g) pp[g] = f16x2_t{(_Float16)p[i][g], (_Float16)p[i + 1][g]};
+            for (int g = 0; g < G; ++g) {
+                if constexpr (KV::kBlockScales)
+                    pp[g] = f16x2_t{(_Float16)(p[i][g] * vr), (_Float16)(p[i + 1][g] * vr)};
+                else
+                    pp[g] = f16x2_t{(_Float16)p[i][g], (_Float16)p[i + 1][g]};
+            }
             // four dims at a time, so few pairs are live at once
 #pragma unroll
             for (int j = 0; j < ND / 4; ++j) {
@@ -416,8 +451,9 @@ __device__ __forceinline__ void process_tile(State<G, KV::kDims>& st, const Tile
             }
 #pragma unroll
             for (int g = 0; g < G; ++g) {
+                const float pw = KV::kBlockScales ? p[i][g] * vr : p[i][g];
 #pragma unroll
-                for (int d = 0; d < ND; ++d) st.acc[g][d] = fmaf(p[i][g], v[d], st.acc[g][d]);
+                for (int d = 0; d < ND; ++d) st.acc[g][d] = fmaf(pw, v[d], st.acc[g][d]);
             }
         }
     }
@@ -513,12 +549,19 @@ struct IdWindow {
     }
 };
 
-// Byte offset (wave-uniform) of a tile's first token row in a pool.
+// Physical block (wave-uniform) holding a tile, and the byte offset of the
+// tile's first token row in a pool.
+template <int BS>
+__device__ __forceinline__ int tile_block(IdWindow& ids, int tile, int lane) {
+    return ids.get(tile * kTileTokens / BS, lane);
+}
+template <int BS>
+__device__ __forceinline__ size_t tile_offset(int phys, int tile, size_t row_bytes) {
+    return ((size_t)phys * BS + (tile * kTileTokens) % BS) * row_bytes;
+}
 template <int BS>
 __device__ __forceinline__ size_t tile_bytes(IdWindow& ids, int tile, size_t row_bytes, int lane) {
-    const int tok = tile * kTileTokens;
-    const int phys = ids.get(tok / BS, lane);
-    return ((size_t)phys * BS + (tok % BS)) * row_bytes;
+    return tile_offset<BS>(tile_block<BS>(ids, tile, lane), tile, row_bytes);
 }
 
 // One decode worker: the workgroup's waves (at most NWAVES, one per KV head
@@ -538,7 +581,8 @@ __device__ __forceinline__ void decode_worker(
     int num_workers, const int32_t* __restrict__ cu_q_lens, int32_t* __restrict__ s_cum,
     int32_t* __restrict__ s_part, int worker, int group, uint16_t* __restrict__ s_vx = nullptr,
     int max_rows = 1, int causal = 1, const uint64_t* __restrict__ tree_mask = nullptr,
-    uint4* __restrict__ s_q = nullptr, uint16_t* __restrict__ s_st = nullptr) {
+    uint4* __restrict__ s_q = nullptr, uint16_t* __restrict__ s_st = nullptr,
+    const float* __restrict__ k_scales = nullptr, const float* __restrict__ v_scales = nullptr) {
     static_assert(NCB == 1 || KV::kMfma, "two column blocks need the matrix-core tile");
     static_assert(CSPLIT == 1 || (KV::kMfma && NCB == 1 && KV::kElemBytes == 2),
                   "shared staging: the bf16 matrix-core tile, one block per wave");
@@ -905,11 +949,15 @@ __device__ __forceinline__ void decode_worker(
         for (int j = 0; j < NL; ++j)
             koff[j] = (uint32_t)(r16 * row_bytes + (size_t)kvh * D * KV::kElemBytes + KV::mfma_byte(j, q4));
         uint16_t* const vx = s_vx + (tid >> 6) * kVxWaveElems;  // this wave's V tile
-        struct MTile { typename KV::Word k[NL]; typename KV::Word v[NL]; };
+        struct MTile { typename KV::Word k[NL]; typename KV::Word v[NL]; float ks, vs; };
+        float vref = 0.0f;  // the piece's V reference scale (kBlockScales)
         // tiles that reach the keys some row may not see take the mask
         auto masked_of = [&](int j) { return (tile0 + j + 1) * kTileTokens > mask_from; };
         auto fetch = [&](MTile& x, int j) {
-            const size_t o0 = tile_bytes<BS>(ids, tile0 + j, row_bytes, lane);
+            const int phys = tile_block<BS>(ids, tile0 + j, lane);
+            if constexpr (KV::kBlockScales)
+                load_block_scales(k_scales, v_scales, phys, num_kv_heads, kvh, x.ks, x.vs);
+            const size_t o0 = tile_offset<BS>(phys, tile0 + j, row_bytes);
             const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kbase + o0);
             const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vbase + o0);
             // tokens past the end read zeros
@@ -927,6 +975,19 @@ __device__ __forceinline__ void decode_worker(
             for (int kb = 0; kb < 4; ++kb)
                 *reinterpret_cast<uint4*>(vx + r16 * kVxStride + KV::mfma_dim(kb, q4)) = KV::v_f16x8(x.v, kb);
             const int tok0 = (tile0 + j) * kTileTokens + 4 * q4;  // this lane's first token
+            float ct = c, vr = 1.0f;  // this tile's score scale and V ratio
+            if constexpr (KV::kBlockScales) {
+                ct = c * x.ks;
+                if (x.vs > vref) {
+                    const float f = vref / x.vs;
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                        for (int nb = 0; nb < 8; ++nb) o[cb][nb] *= f;
+                    vref = x.vs;
+                }
+                vr = x.vs / vref;
+            }
             f16x4_t pa[NCB];
             float alpha[NCB];
             bool grew = false;
@@ -958,16 +1019,20 @@ __device__ __forceinline__ void decode_worker(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sv[i] = vis[i] ? sc[i] : -3.402823466e38f;
                 float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-                mt = max_lane_quads(mt) * c;
+                mt = max_lane_quads(mt) * ct;
                 const float mn = fmaxf(m[cb], mt);
                 grew |= mn > m[cb];
                 alpha[cb] = fast_exp2(m[cb] - mn);
                 m[cb] = mn;
                 float p[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) p[i] = vis[i] ? fast_exp2(fmaf(sv[i], c, -mn)) : 0.0f;
+                for (int i = 0; i < 4; ++i) p[i] = vis[i] ? fast_exp2(fmaf(sv[i], ct, -mn)) : 0.0f;
                 l[cb] = fmaf(l[cb], alpha[cb], (p[0] + p[1]) + (p[2] + p[3]));
-                pa[cb] = f16x4_t{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+                if constexpr (KV::kBlockScales)
+                    pa[cb] = f16x4_t{(_Float16)(p[0] * vr), (_Float16)(p[1] * vr),
+                                     (_Float16)(p[2] * vr), (_Float16)(p[3] * vr)};
+                else
+                    pa[cb] = f16x4_t{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
             }
             if (__any(grew)) {
                 // O row 4 q4 + i is column 4 q4 + i, whose alpha lane 4 q4 + i holds
@@ -1035,8 +1100,11 @@ __device__ __forceinline__ void decode_worker(
                 const int r = cc / G;
                 if (r >= lq) continue;
                 const size_t qh = (size_t)kvh * G + cc % G;
+                // O in absolute units: times the V reference scale
+                const float ou = KV::kBlockScales ? out_scale * vref : out_scale;
+                const float vu = KV::kBlockScales ? vref : 1.0f;
                 if (whole) {
-                    const float inv = out_scale / lh;
+                    const float inv = ou / lh;
                     const size_t e = ((size_t)(row0 + r) * num_q_heads + qh) * D;
 #pragma unroll
                     for (int nb = 0; nb < 8; ++nb)
@@ -1044,7 +1112,8 @@ __device__ __forceinline__ void decode_worker(
                 } else {
                     float* rr = rec + (((size_t)(w * 2 + slot) * max_rows + r) * num_q_heads + qh) * kRecStride;
 #pragma unroll
-                    for (int nb = 0; nb < 8; ++nb) rr[16 * nb + r16] = o[cb][nb][i];
+                    for (int nb = 0; nb < 8; ++nb)
+                        rr[16 * nb + r16] = KV::kBlockScales ? o[cb][nb][i] * vu : o[cb][nb][i];
                     if (r16 == 0) {
                         rr[D] = mh;
                         rr[D + 1] = lh;
@@ -1079,14 +1148,44 @@ __device__ __forceinline__ void decode_worker(
         // force the wait counters to drain it).  Only the sequence's last
         // tile can be partial, and it is never inside the loop.
         auto fetch = [&](Tile<KV>& x, int j) {
-            const size_t o = tile_bytes<BS>(ids, tile0 + j, row_bytes, lane);
+            const int phys = tile_block<BS>(ids, tile0 + j, lane);
+            if constexpr (KV::kBlockScales)
+                load_block_scales(k_scales, v_scales, phys, num_kv_heads, kvh, x.ks, x.vs);
+            const size_t o = tile_offset<BS>(phys, tile0 + j, row_bytes);
             load_tile(x, kbase + o, vbase + o, voff);
         };
+        // a tile's score scale and V ratio; with per-(block, head) scales the
+        // V reference moves first (the same in every lane: one block and
+        // one KV head per tile and wave)
+        float vref = 0.0f;
+        auto scales_of = [&](const Tile<KV>& x, float& ct, float& vr) {
+            ct = c;
+            vr = 1.0f;
+            if constexpr (KV::kBlockScales) {
+                ct = c * x.ks;
+                if (x.vs > vref) {
+                    const float f = vref / x.vs;
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+#pragma unroll
+                        for (int d = 0; d < ND; ++d) st.acc[g][d] *= f;
+                    vref = x.vs;
+                }
+                vr = x.vs / vref;
+            }
+        };
+        auto full = [&](const Tile<KV>& x) {
+            float ct, vr;
+            scales_of(x, ct, vr);
+            process_tile<KV, G, false>(st, x, qv, ct, row, kTileTokens, vr);
+        };
         auto finish = [&](const Tile<KV>& x, int j) {
+            float ct, vr;
+            scales_of(x, ct, vr);
             if (tail && j == n - 1)
-                process_tile<KV, G, true>(st, x, qv, c, row, ctx - (tile0 + j) * kTileTokens);
+                process_tile<KV, G, true>(st, x, qv, ct, row, ctx - (tile0 + j) * kTileTokens, vr);
             else
-                process_tile<KV, G, false>(st, x, qv, c, row, kTileTokens);
+                process_tile<KV, G, false>(st, x, qv, ct, row, kTileTokens, vr);
         };
         Tile<KV> a, b;
         fetch(a, 0);
@@ -1096,9 +1195,9 @@ __device__ __forceinline__ void decode_worker(
             fetch(b, 1);
             int j = 0;
             for (; j + 3 < n; j += 2) {  // tiles j + 2 and j + 3 exist and are full
-                process_tile<KV, G, false>(st, a, qv, c, row, kTileTokens);
+                full(a);
                 fetch(a, j + 2);
-                process_tile<KV, G, false>(st, b, qv, c, row, kTileTokens);
+                full(b);
                 fetch(b, j + 3);
                 // Eight waves stream their heads with nothing else tying them
                 // together, and two share each SIMD: left alone they drift
@@ -1110,10 +1209,10 @@ __device__ __forceinline__ void decode_worker(
                 if (NWAVES == 8) __syncthreads();
             }
             // two or three tiles left: j (in a), j + 1 (in b), maybe j + 2
-            process_tile<KV, G, false>(st, a, qv, c, row, kTileTokens);
+            full(a);
             if (n - j == 3) {
                 fetch(a, j + 2);
-                process_tile<KV, G, false>(st, b, qv, c, row, kTileTokens);
+                full(b);
                 finish(a, j + 2);
             } else {
                 finish(b, j + 1);
@@ -1148,7 +1247,8 @@ __device__ __forceinline__ void decode_worker(
         for (int g = 0; g < G; ++g) {
             if (g % L::kRows != row) continue;
             if (whole) {
-                const float inv = out_scale / st.l[g];
+                // with per-(block, head) scales the accumulator is in units of vref
+                const float inv = (KV::kBlockScales ? out_scale * vref : out_scale) / st.l[g];
 #pragma unroll
                 for (int w8 = 0; w8 < ND / 8; ++w8) {
                     float o[8];
@@ -1159,10 +1259,16 @@ __device__ __forceinline__ void decode_worker(
             } else {
                 float* r = rec + ((size_t)(w * 2 + slot) * num_q_heads + (size_t)kvh * G + g) * kRecStride;
                 float4* pa = reinterpret_cast<float4*>(r + col * ND);
+                const float vu = KV::kBlockScales ? vref : 1.0f;
 #pragma unroll
-                for (int w4 = 0; w4 < ND / 4; ++w4)
-                    pa[w4] = make_float4(st.acc[g][4 * w4], st.acc[g][4 * w4 + 1],
-                                         st.acc[g][4 * w4 + 2], st.acc[g][4 * w4 + 3]);
+                for (int w4 = 0; w4 < ND / 4; ++w4) {
+                    if constexpr (KV::kBlockScales)
+                        pa[w4] = make_float4(st.acc[g][4 * w4] * vu, st.acc[g][4 * w4 + 1] * vu,
+                                             st.acc[g][4 * w4 + 2] * vu, st.acc[g][4 * w4 + 3] * vu);
+                    else
+                        pa[w4] = make_float4(st.acc[g][4 * w4], st.acc[g][4 * w4 + 1],
+                                             st.acc[g][4 * w4 + 2], st.acc[g][4 * w4 + 3]);
+                }
                 if (col == 0) {
                     r[D] = st.m[g];
                     r[D + 1] = st.l[g];

@@ -64,11 +64,17 @@ __device__ __forceinline__ uint2 quantise8(uint4 x, float scale) {
     return r;
 }
 
+// With BLOCK_SCALES the scales are per (block, KV head): [num_blocks]
+// [num_kv_heads] fp32 tables, read for the block slot s lies in (s / bs)
+// and the word's KV head (kHeadDim / 8 words per head).
+template <bool BLOCK_SCALES>
 __global__ void __launch_bounds__(256)
 kv_append_fp8_kernel(const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
                      const int64_t* __restrict__ slot_mapping, int64_t num_words,
                      uint2* __restrict__ k_cache, uint2* __restrict__ v_cache, int words_per_row,
-                     float k_scale, float v_scale, int64_t num_slots) {
+                     float k_scale, float v_scale, int64_t num_slots,
+                     const float* __restrict__ k_scales, const float* __restrict__ v_scales,
+                     int block_size) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < num_words; w += stride) {
         const int64_t t = w / words_per_row;
@@ -76,8 +82,14 @@ kv_append_fp8_kernel(const uint4* __restrict__ k_new, const uint4* __restrict__ 
         const int64_t s = slot_mapping[t];
         if (s < 0 || s >= num_slots) continue;
         const int64_t dst = s * words_per_row + c;
-        k_cache[dst] = quantise8(k_new[w], k_scale);
-        v_cache[dst] = quantise8(v_new[w], v_scale);
+        float ks = k_scale, vs = v_scale;
+        if constexpr (BLOCK_SCALES) {
+            const int64_t e = (s / block_size) * (words_per_row / (kHeadDim / 8)) + c / (kHeadDim / 8);
+            ks = k_scales[e];
+            vs = v_scales[e];
+        }
+        k_cache[dst] = quantise8(k_new[w], ks);
+        v_cache[dst] = quantise8(v_new[w], vs);
     }
 }
 
@@ -147,11 +159,18 @@ hipError_t launch_kv_append_fp8(const AppendFp8Args& a, hipStream_t stream) {
     if (num_words == 0) return hipSuccess;
     const int64_t want = (num_words + 255) / 256;
     const int blocks = (int)(want < 65536 ? want : 65536);
-    hipLaunchKernelGGL(kv_append_fp8_kernel, dim3(blocks), dim3(256), 0, stream,
-                       reinterpret_cast<const uint4*>(a.k_new), reinterpret_cast<const uint4*>(a.v_new),
-                       a.slot_mapping, num_words, reinterpret_cast<uint2*>(a.k_cache),
-                       reinterpret_cast<uint2*>(a.v_cache), words_per_row, a.k_scale, a.v_scale,
-                       a.num_slots);
+    if (a.k_scales != nullptr)
+        hipLaunchKernelGGL(kv_append_fp8_kernel<true>, dim3(blocks), dim3(256), 0, stream,
+                           reinterpret_cast<const uint4*>(a.k_new), reinterpret_cast<const uint4*>(a.v_new),
+                           a.slot_mapping, num_words, reinterpret_cast<uint2*>(a.k_cache),
+                           reinterpret_cast<uint2*>(a.v_cache), words_per_row, 1.0f, 1.0f,
+                           a.num_slots, a.k_scales, a.v_scales, a.block_size);
+    else
+        hipLaunchKernelGGL(kv_append_fp8_kernel<false>, dim3(blocks), dim3(256), 0, stream,
+                           reinterpret_cast<const uint4*>(a.k_new), reinterpret_cast<const uint4*>(a.v_new),
+                           a.slot_mapping, num_words, reinterpret_cast<uint2*>(a.k_cache),
+                           reinterpret_cast<uint2*>(a.v_cache), words_per_row, a.k_scale, a.v_scale,
+                           a.num_slots, nullptr, nullptr, a.block_size);
     return hipGetLastError();
 }
 

@@ -31,6 +31,10 @@ struct AppendFp8Args {
     int64_t num_slots;  // num_blocks * block_size: slots at or past it are skipped
     float k_scale;
     float v_scale;
+    // or one scale per (block, KV head): [num_blocks][num_kv_heads] fp32
+    const float* k_scales = nullptr;
+    const float* v_scales = nullptr;
+    int block_size = 16;
 };
 
 struct CopyBlocksArgs {
@@ -72,6 +76,10 @@ struct DecodeArgs {
     int rows = 1;
     bool causal = true;
     const uint64_t* tree_mask = nullptr;
+    // FP8 pools with one scale per (block, KV head): [num_blocks][num_kv_heads]
+    // fp32 tables for K and V (then scale_log2 and out_scale carry none)
+    const float* k_scales = nullptr;
+    const float* v_scales = nullptr;
 };
 
 struct PrefillArgs {

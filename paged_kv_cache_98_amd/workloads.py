@@ -414,6 +414,30 @@ def fp8_pools(b: Batch, k_scale: float = FP8_SCALE, v_scale: float = FP8_SCALE):
     return cast(b.k_cache, k_scale), cast(b.v_cache, v_scale)
 
 
+def fp8_block_pools(b: Batch, seed: int, k_spread: float = 2.0, v_spread: float = 1.0):
+    """(k_codes, v_codes, k_scales, v_scales): the batch's pools as uint8 E4M3
+    codes with one scale per (block, KV head).  Each (block, head) of K is
+    first multiplied by 2^u, u uniform in [-k_spread, k_spread] (V likewise
+    with v_spread), so blocks and heads differ in magnitude; its scale is
+    then its absolute maximum / 448 (1.0 for a block with no finite value),
+    and its codes torch's float8 cast of value / scale.  Scales are fp32
+    [num_blocks, num_kv_heads] on the pools' device."""
+    nb, hkv = b.k_cache.shape[0], b.k_cache.shape[2]
+    g = torch.Generator().manual_seed(seed)
+
+    def one(pool, spread):
+        f = torch.exp2((torch.rand((nb, hkv), generator=g) * 2 - 1) * spread).to(pool.device)
+        x = pool.float() * f[:, None, :, None]
+        amax = torch.nan_to_num(x, nan=0.0).abs().amax(dim=(1, 3))
+        scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax)).to(torch.float32)
+        codes = (x / scale[:, None, :, None]).clamp(-448.0, 448.0)
+        return codes.to(torch.float8_e4m3fn).view(torch.uint8), scale.contiguous()
+
+    kc, ks = one(b.k_cache, k_spread)
+    vc, vs = one(b.v_cache, v_spread)
+    return kc, vc, ks, vs
+
+
 def permute_pool(b: Batch, seed: int) -> Batch:
     """The same logical batch with physical ids relabelled by a random
     permutation: block data moved and tables rewritten accordingly."""

@@ -226,6 +226,50 @@ def test_fp8_validation(lib):
     assert ap(t=0, kn=None) == E.PKV_OK
 
 
+def test_fp8_per_block_validation(lib):
+    """The per-(block, KV head) scale calls: the tables are required and
+    4-byte aligned; the rest is checked as for the per-cache calls."""
+    E = binding
+    ALIGN4 = ctypes.c_void_p(0x10004)
+    MIS4 = ctypes.c_void_p(0x10002)
+
+    def dec(**kw):
+        a = dict(out=P, out_dtype=0, q=P, k=P, v=P, kst=P2, vst=P2, bt=P, mb=8, cl=P,
+                 maxctx=100, nseq=4, hq=8, hkv=2, d=128, bs=16, scale=0.1, ws=None, wsb=0,
+                 stream=None)
+        a.update(kw)
+        return lib.pkv_paged_decode_attn_fp8_per_block(
+            a["out"], a["out_dtype"], a["q"], a["k"], a["v"], a["kst"], a["vst"], a["bt"],
+            a["mb"], a["cl"], a["maxctx"], a["nseq"], a["hq"], a["hkv"], a["d"], a["bs"],
+            a["scale"], a["ws"], a["wsb"], a["stream"])
+
+    assert dec(kst=None) == E.PKV_ERR_NULL
+    assert dec(vst=None) == E.PKV_ERR_NULL
+    assert dec(kst=MIS4) == E.PKV_ERR_ALIGN
+    assert dec(q=None) == E.PKV_ERR_NULL
+    assert dec(k=MIS) == E.PKV_ERR_ALIGN
+    assert dec(d=64) == E.PKV_ERR_UNSUPPORTED
+    assert dec(hq=6, hkv=4) == E.PKV_ERR_SHAPE
+    assert dec(kst=ALIGN4, maxctx=2000, mb=200) == E.PKV_ERR_WORKSPACE
+    assert dec(nseq=0, q=None, kst=None, vst=None) == E.PKV_OK
+
+    def ap(**kw):
+        a = dict(kn=P, vn=P, sm=P, t=5, kc=P, vc=P, nb=10, bs=16, hkv=8, d=128, kst=P2, vst=P2,
+                 stream=None)
+        a.update(kw)
+        return lib.pkv_kv_append_fp8_per_block(a["kn"], a["vn"], a["sm"], a["t"], a["kc"],
+                                               a["vc"], a["nb"], a["bs"], a["hkv"], a["d"],
+                                               a["kst"], a["vst"], a["stream"])
+
+    assert ap(kst=None) == E.PKV_ERR_NULL
+    assert ap(vst=None) == E.PKV_ERR_NULL
+    assert ap(vst=MIS4) == E.PKV_ERR_ALIGN
+    assert ap(sm=None) == E.PKV_ERR_NULL
+    assert ap(bs=8) == E.PKV_ERR_UNSUPPORTED
+    assert ap(t=-1) == E.PKV_ERR_SHAPE
+    assert ap(t=0, kn=None, kst=None) == E.PKV_OK
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros(1, 8, 128, dtype=torch.bfloat16)

@@ -317,3 +317,168 @@ def test_prefill_fp8_streamk(group, rows):
     parity(o32, ref, what=w.name)
     bf16_parity(o16, o32, ref, what=w.name + " bf16 out",
                 fp32_err=1e-3, min_within=0.95)
+
+
+# ---- FP8 pools with one scale per (block, KV head) ----
+
+def scale_table(nb, hkv, g, lo=-12.0, hi=4.0):
+    """fp32 [nb, hkv] scales 2^u, u uniform in [lo, hi]; every third one a
+    power of two."""
+    u = torch.rand((nb, hkv), generator=g) * (hi - lo) + lo
+    t = torch.exp2(u)
+    t.view(-1)[::3] = torch.exp2(torch.round(u.view(-1)[::3]))
+    return t.to(torch.float32)
+
+
+@pytest.mark.parametrize("bs,hkv", [(16, 8), (32, 2), (16, 1)])
+def test_kv_append_fp8_per_block_bit_exact(bs, hkv):
+    """Each token row is quantised with the scales of its slot's block and
+    its KV head: bit for bit against the oracle's quantiser, including the
+    rounding midpoints and the clamp of the scale each row meets."""
+    print(f"[fp8 append per block] bs={bs} hkv={hkv}", flush=True)
+    g = torch.Generator().manual_seed(700 + bs + hkv)
+    nb, t, d = 40, 260, 128
+    mag = torch.exp2(torch.randint(-16, 12, (t, hkv, d), generator=g).float())
+    k_new = (torch.randn((t, hkv, d), generator=g) * mag).to(torch.bfloat16)
+    v_new = (torch.randn((t, hkv, d), generator=g) * mag.flip(0)).to(torch.bfloat16)
+    slots = torch.randperm(nb * bs, generator=g)[:t].to(torch.int64)
+    slots[5::11] = -1
+    ks, vs = scale_table(nb, hkv, g), scale_table(nb, hkv, g, lo=-6.0, hi=2.0)
+    # rows 0 and 1: the rounding midpoints and clamp region of their own scale
+    for r in (0, 1):
+        blk = int(slots[r]) // bs
+        for h in range(hkv):
+            k_new[r, h] = edge_values(float(ks[blk, h]))[r * d:(r + 1) * d]
+            v_new[r, h] = edge_values(float(vs[blk, h]))[(r + 2) * d:(r + 3) * d]
+    k0 = torch.randint(0, 256, (nb, bs, hkv, d), generator=g, dtype=torch.int32).to(torch.uint8)
+    v0 = torch.randint(0, 256, (nb, bs, hkv, d), generator=g, dtype=torch.int32).to(torch.uint8)
+    ref_k, ref_v = fp8.kv_append_fp8(bits16(k_new), bits16(v_new), slots.numpy(), codes(k0),
+                                     codes(v0), ks.numpy(), vs.numpy())
+    kd, vd = k0.to(DEV), v0.to(DEV)
+    pkv.kv_append_fp8_per_block(k_new.to(DEV), v_new.to(DEV), slots.to(DEV), kd, vd,
+                                ks.to(DEV), vs.to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(codes(kd), ref_k)
+    assert np.array_equal(codes(vd), ref_v)
+
+
+def run_fp8_pb(b, kc, vc, ks, vs, w, out_dtype=torch.float32):
+    return pkv.paged_decode_attn_fp8_per_block(b.q, kc, vc, ks, vs, b.block_table, b.context_lens,
+                                               w.scale, max_context_len=w.max_context_len,
+                                               out_dtype=out_dtype)
+
+
+def oracle_fp8_pb(b_cpu, kc, vc, ks, vs):
+    w = b_cpu.workload
+    return fp8.paged_decode_fp8(bits16(b_cpu.q), codes(kc), codes(vc), ks.cpu().numpy(),
+                                vs.cpu().numpy(), b_cpu.block_table.numpy(),
+                                b_cpu.context_lens.numpy(), w.scale)
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("group", [1, 2, 4, 8, 16])
+def test_decode_fp8_per_block_groups_and_edges(bs, group):
+    """Per-(block, head) scales that differ by up to 16x between blocks, at
+    contexts on both sides of every tile and block edge, every group size
+    (the VALU tile at 1 and 2 query heads per KV head, the matrix-core tile
+    from 4)."""
+    hkv = 2
+    w = W.make_workload(f"fp8pb_edges_g{group}_bs{bs}", EDGE_CTX, num_q_heads=hkv * group,
+                        num_kv_heads=hkv, block_size=bs, seed=3300 + group + bs)
+    print(f"[fp8 per block] {w.name}", flush=True)
+    bc = W.materialize(w, logical=True, poison=True)
+    kc, vc, ks, vs = W.fp8_block_pools(bc, seed=group * 100 + bs)
+    ref = oracle_fp8_pb(bc, kc, vc, ks, vs)
+    b = bc.to(DEV)
+    out = run_fp8_pb(b, kc.to(DEV), vc.to(DEV), ks.to(DEV), vs.to(DEV), w)
+    torch.cuda.synchronize()
+    parity(out, ref, what=f"fp8 per block g{group} bs{bs}")
+
+
+def test_decode_fp8_per_block_constant_tables_match_per_cache():
+    """A table holding one scale everywhere gives the per-cache decode: the
+    same scores and weights, differing only where a split sequence's pieces
+    are merged (the scale applied before the merge instead of after)."""
+    w = W.make_workload("fp8pb_const", EDGE_CTX + [4000, 7000], num_q_heads=8, num_kv_heads=2,
+                        seed=3390)
+    print(f"[fp8 per block] {w.name}", flush=True)
+    b = W.materialize(w, device=DEV, poison=True)
+    kc, vc = W.fp8_pools(b)
+    nb = kc.shape[0]
+    ks = torch.full((nb, 2), W.FP8_SCALE, dtype=torch.float32, device=DEV)
+    a = run_fp8(b.q, kc, vc, b.block_table, b.context_lens, w)
+    p = run_fp8_pb(b, kc, vc, ks, ks.clone(), w)
+    torch.cuda.synchronize()
+    torch.testing.assert_close(p, a, rtol=1e-6, atol=1e-7)
+
+
+def test_decode_fp8_per_block_bf16_output_and_determinism():
+    w = W.make_workload("fp8pb_bf16", EDGE_CTX, num_q_heads=8, num_kv_heads=2, block_size=32,
+                        seed=3391)
+    print(f"[fp8 per block] {w.name}", flush=True)
+    bc = W.materialize(w, logical=True, poison=True)
+    kc, vc, ks, vs = W.fp8_block_pools(bc, seed=5)
+    ref = oracle_fp8_pb(bc, kc, vc, ks, vs)
+    b = bc.to(DEV)
+    kd, vd, ksd, vsd = kc.to(DEV), vc.to(DEV), ks.to(DEV), vs.to(DEV)
+    f32 = run_fp8_pb(b, kd, vd, ksd, vsd, w)
+    f32b = run_fp8_pb(b, kd, vd, ksd, vsd, w)
+    h = run_fp8_pb(b, kd, vd, ksd, vsd, w, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(f32, f32b)
+    parity(f32, ref, what="fp8 per block fp32")
+    bf16_parity(h, f32, ref, what="fp8 per block bf16", fp32_err=1e-3, min_within=0.99)
+
+
+def test_fp8_per_block_append_then_decode():
+    """A decode step on a per-block-scaled cache: the new tokens quantised
+    into their blocks by the library (with those blocks' scales), then the
+    decode over them, against the oracle's append and decode."""
+    w = W.make_workload("fp8pb_step", [33, 64, 100, 257, 1000], num_q_heads=16, num_kv_heads=2,
+                        seed=3392)
+    print(f"[fp8 per block] {w.name}", flush=True)
+    bc = W.materialize(w, logical=True, poison=True)
+    kc, vc, ks, vs = W.fp8_block_pools(bc, seed=6)
+    g = torch.Generator().manual_seed(3393)
+    bt, ctx = bc.block_table, bc.context_lens
+    slots = torch.tensor([int(bt[i, (int(ctx[i]) - 1) // w.block_size]) * w.block_size +
+                          (int(ctx[i]) - 1) % w.block_size for i in range(len(ctx))],
+                         dtype=torch.int64)
+    k_new = torch.randn((len(ctx), 2, 128), generator=g).to(torch.bfloat16)
+    v_new = torch.randn((len(ctx), 2, 128), generator=g).to(torch.bfloat16)
+    rk, rv = fp8.kv_append_fp8(bits16(k_new), bits16(v_new), slots.numpy(), codes(kc), codes(vc),
+                               ks.numpy(), vs.numpy())
+    ref = fp8.paged_decode_fp8(bits16(bc.q), rk, rv, ks.numpy(), vs.numpy(), bt.numpy(),
+                               ctx.numpy(), w.scale)
+    b = bc.to(DEV)
+    kd, vd, ksd, vsd = kc.to(DEV), vc.to(DEV), ks.to(DEV), vs.to(DEV)
+    pkv.kv_append_fp8_per_block(k_new.to(DEV), v_new.to(DEV), slots.to(DEV), kd, vd, ksd, vsd)
+    out = run_fp8_pb(b, kd, vd, ksd, vsd, w)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes(kd), rk) and np.array_equal(codes(vd), rv)
+    parity(out, ref, what="fp8 per block append + decode")
+
+
+def test_decode_fp8_per_block_full_8b_batch_sampled():
+    """The 64-sequence 8B-shaped batch over per-(block, head)-scaled FP8 pools,
+    as the benchmark times it; sampled sequences against the oracle."""
+    w = W.llama8b_decode()
+    print(f"[fp8 per block full 8b] {w.name}", flush=True)
+    b = W.materialize(w, device=DEV, poison=True)
+    kd, vd, ksd, vsd = W.fp8_block_pools(b, seed=7)
+    out = run_fp8_pb(b, kd, vd, ksd, vsd, w)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(out))
+    ctx = list(w.context_lens)
+    bt = b.block_table.cpu()
+    for i in sorted({ctx.index(max(ctx)), ctx.index(min(ctx)), 0, 31, 63}):
+        n = ctx[i]
+        ids = bt[i, : -(-n // w.block_size)].to(torch.int64)
+        idd = ids.to(DEV)
+        ref = fp8.paged_decode_fp8(bits16(b.q[i:i + 1]), codes(kd.index_select(0, idd)),
+                                   codes(vd.index_select(0, idd)),
+                                   ksd.index_select(0, idd).cpu().numpy(),
+                                   vsd.index_select(0, idd).cpu().numpy(),
+                                   np.arange(len(ids), dtype=np.int32)[None, :],
+                                   np.array([n], dtype=np.int32), w.scale)
+        parity(out[i:i + 1], ref, what=f"fp8 per block 8b batch seq {i} (ctx {n})")
