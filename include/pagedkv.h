@@ -572,6 +572,37 @@ int pkv_paged_prefill_attn_tree_fp8(void *out, int out_dtype, const void *q,
                                     int block_size, float scale, void *workspace,
                                     size_t workspace_bytes, void *stream);
 
+/*
+ * paged_prefill_attn_fp8_per_block / paged_prefill_attn_tree_fp8_per_block
+ * -- pkv_paged_prefill_attn_fp8 and pkv_paged_prefill_attn_tree_fp8 over FP8
+ * pools with per-(block, KV head) scales (the tables of
+ * pkv_paged_decode_attn_fp8_per_block; same arguments otherwise, and the
+ * same workspace, pkv_prefill_workspace_bytes).  Every key's score takes
+ * the K scale of its block, and its value the V scale, as a ratio to the
+ * largest V scale of the item's tiles so far: on the chunk kernels V is
+ * staged as fp16(code x ratio) (the ratio rounded to fp16, the product
+ * rounded once more); on the rows path, which takes chunks of at most 16
+ * (row, head) columns per KV head here, P is scaled as in the decode.
+ * Chunks and single-row sequences in one call run one after the other (the
+ * chunk kernel, then the decode kernels), not in one grid.
+ */
+int pkv_paged_prefill_attn_fp8_per_block(void *out, int out_dtype, const void *q,
+                                         const int32_t *cu_q_lens, const void *k_cache,
+                                         const void *v_cache, const float *k_scales,
+                                         const float *v_scales, const int32_t *block_table,
+                                         int max_blocks_per_seq, const int32_t *context_lens,
+                                         int max_context_len, int max_q_len, int num_q_tokens,
+                                         int num_seqs, int num_q_heads, int num_kv_heads,
+                                         int head_dim, int block_size, float scale, int causal,
+                                         void *workspace, size_t workspace_bytes, void *stream);
+int pkv_paged_prefill_attn_tree_fp8_per_block(
+    void *out, int out_dtype, const void *q, const int32_t *cu_q_lens, const uint64_t *tree_mask,
+    const void *k_cache, const void *v_cache, const float *k_scales, const float *v_scales,
+    const int32_t *block_table, int max_blocks_per_seq, const int32_t *context_lens,
+    int max_context_len, int max_q_len, int num_q_tokens, int num_seqs, int num_q_heads,
+    int num_kv_heads, int head_dim, int block_size, float scale, void *workspace,
+    size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

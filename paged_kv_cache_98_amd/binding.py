@@ -41,7 +41,8 @@ EXPORTED = ("pkv_status_string", "pkv_version", "pkv_kv_append", "pkv_decode_wor
             "pkv_bm_seq_info",
             "pkv_bm_refcount", "pkv_bm_block_table", "pkv_paged_decode_attn_noalloc",
             "pkv_decode_noalloc_max_bytes", "pkv_kv_append_fp8_per_block",
-            "pkv_paged_decode_attn_fp8_per_block")
+            "pkv_paged_decode_attn_fp8_per_block", "pkv_paged_prefill_attn_fp8_per_block",
+            "pkv_paged_prefill_attn_tree_fp8_per_block")
 
 _lib = None
 
@@ -126,6 +127,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_kv_append_fp8_per_block.restype = _i32
     lib.pkv_kv_append_fp8_per_block.argtypes = [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i32, _i32,
                                                 _i32, _vp, _vp, _vp]
+    lib.pkv_paged_prefill_attn_fp8_per_block.restype = _i32
+    lib.pkv_paged_prefill_attn_fp8_per_block.argtypes = [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                         _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                                         _i32, _i32, _i32, _i32, _f32, _i32, _vp,
+                                                         _sz, _vp]
+    lib.pkv_paged_prefill_attn_tree_fp8_per_block.restype = _i32
+    lib.pkv_paged_prefill_attn_tree_fp8_per_block.argtypes = [_vp, _i32, _vp, _vp, _vp, _vp, _vp,
+                                                              _vp, _vp, _vp, _i32, _vp, _i32,
+                                                              _i32, _i32, _i32, _i32, _i32, _i32,
+                                                              _i32, _f32, _vp, _sz, _vp]
     lib.pkv_paged_decode_attn_fp8_per_block.restype = _i32
     lib.pkv_paged_decode_attn_fp8_per_block.argtypes = [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                                         _i32, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -302,6 +313,54 @@ def paged_prefill_attn_fp8(q: torch.Tensor, cu_q_lens: torch.Tensor, k_cache: to
         _dev(out, "out"), _out_code(out.dtype), _dev(q, "q", torch.bfloat16),
         _dev(cu_q_lens, "cu_q_lens", torch.int32), _dev(k_cache, "k_cache", torch.uint8),
         _dev(v_cache, "v_cache", torch.uint8), float(k_scale), float(v_scale),
+        _dev(block_table, "block_table", torch.int32), block_table.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), max_context_len, max_q_len, tq, nseq,
+        hq, hkv, d, bs, float(scale), 1 if causal else 0, ws_ptr, ws_len, _stream(stream)))
+    return out
+
+
+def paged_prefill_attn_fp8_per_block(q: torch.Tensor, cu_q_lens: torch.Tensor,
+                                     k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                     k_scales: torch.Tensor, v_scales: torch.Tensor,
+                                     block_table: torch.Tensor, context_lens: torch.Tensor,
+                                     scale: float, max_context_len: int, max_q_len: int,
+                                     causal: bool = True, out: Optional[torch.Tensor] = None,
+                                     out_dtype=torch.float32,
+                                     workspace: Optional[torch.Tensor] = None, stream=None,
+                                     tree_mask: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """pkv_paged_prefill_attn_fp8_per_block: as paged_prefill_attn_fp8 over
+    FP8 pools with one scale per (block, KV head) (k_scales / v_scales fp32
+    [NB, Hkv]); with tree_mask, pkv_paged_prefill_attn_tree_fp8_per_block."""
+    lib = load_library()
+    tq, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    nseq = context_lens.shape[0]
+    if d2 != d or cu_q_lens.shape[0] != nseq + 1 or block_table.shape[0] != nseq:
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty((tq, hq, d), dtype=out_dtype, device=q.device)
+    need = lib.pkv_prefill_workspace_bytes(nseq, tq, max_q_len, hq, hkv, d, max_context_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    kst = _scale_table(k_scales, "k_scales", nb, hkv)
+    vst = _scale_table(v_scales, "v_scales", nb, hkv)
+    if tree_mask is not None:
+        if tree_mask.shape != (tq,):
+            raise ValueError("tree_mask must hold one mask per query row")
+        _check(lib.pkv_paged_prefill_attn_tree_fp8_per_block(
+            _dev(out, "out"), _out_code(out.dtype), _dev(q, "q", torch.bfloat16),
+            _dev(cu_q_lens, "cu_q_lens", torch.int32), _dev(tree_mask, "tree_mask", torch.int64),
+            _dev(k_cache, "k_cache", torch.uint8), _dev(v_cache, "v_cache", torch.uint8), kst,
+            vst, _dev(block_table, "block_table", torch.int32), block_table.shape[1],
+            _dev(context_lens, "context_lens", torch.int32), max_context_len, max_q_len, tq, nseq,
+            hq, hkv, d, bs, float(scale), ws_ptr, ws_len, _stream(stream)))
+        return out
+    _check(lib.pkv_paged_prefill_attn_fp8_per_block(
+        _dev(out, "out"), _out_code(out.dtype), _dev(q, "q", torch.bfloat16),
+        _dev(cu_q_lens, "cu_q_lens", torch.int32), _dev(k_cache, "k_cache", torch.uint8),
+        _dev(v_cache, "v_cache", torch.uint8), kst, vst,
         _dev(block_table, "block_table", torch.int32), block_table.shape[1],
         _dev(context_lens, "context_lens", torch.int32), max_context_len, max_q_len, tq, nseq,
         hq, hkv, d, bs, float(scale), 1 if causal else 0, ws_ptr, ws_len, _stream(stream)))

@@ -84,13 +84,16 @@ void* scratch_address(hipError_t* err) {
 }
 
 // Calls whose chunks have at most 16 rows and 64 (row, head) columns per KV
-// head, 32 over FP8 pools (speculative-decoding verification, token trees),
-// run whole on the decode kernel's matrix-core tile, every sequence's rows
-// as columns of its S = K Q^T; wider ones on the chunk kernels.
+// head, 32 over FP8 pools, 16 over FP8 pools with per-(block, KV head)
+// scales (speculative-decoding verification, token trees), run whole on the
+// decode kernel's matrix-core tile, every sequence's rows as columns of its
+// S = K Q^T; wider ones on the chunk kernels.
 constexpr int kRowsPathMaxRows = 16;
-bool rows_path(int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads, bool kv_fp8) {
+bool rows_path(int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads, bool kv_fp8,
+               bool block_scales = false) {
     const int cols = max_q_len * (num_q_heads / num_kv_heads);
-    return max_q_len >= 2 && max_q_len <= kRowsPathMaxRows && cols <= (kv_fp8 ? 32 : 64) &&
+    const int max_cols = block_scales ? 16 : (kv_fp8 ? 32 : 64);
+    return max_q_len >= 2 && max_q_len <= kRowsPathMaxRows && cols <= max_cols &&
            num_seqs <= kMaxDecodeSeqs && (num_kv_heads <= 8 || num_kv_heads == kMaxDecodeKvHeads);
 }
 
@@ -118,14 +121,15 @@ size_t rows_workspace(int num_seqs, int max_q_len, int num_q_heads, int num_kv_h
                                        max_context_len, max_q_len);
 }
 
-// What a prefill call of these sizes needs over either pool type (the rows
-// path takes more columns over bf16 pools than over FP8 ones).
+// What a prefill call of these sizes needs over any pool format (the rows
+// path takes more columns over bf16 pools than over FP8 ones, and fewest
+// with per-block scales).
 size_t prefill_workspace(int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads,
                          int head_dim, int max_context_len) {
     size_t n = 0;
-    for (const bool fp8 : {false, true}) {
+    for (const int fmt : {0, 1, 2}) {
         const size_t c =
-            rows_path(num_seqs, max_q_len, num_q_heads, num_kv_heads, fp8)
+            rows_path(num_seqs, max_q_len, num_q_heads, num_kv_heads, fmt > 0, fmt == 2)
                 ? rows_workspace(num_seqs, max_q_len, num_q_heads, num_kv_heads, head_dim,
                                  max_context_len)
                 : chunk_workspace(num_seqs, max_q_len, num_q_heads, num_kv_heads, head_dim,
@@ -413,7 +417,7 @@ int prefill_call(void* out, int out_dtype, const void* q, const int32_t* cu_q_le
                  int max_q_len, int num_q_tokens, int num_seqs, int num_q_heads,
                  int num_kv_heads, int head_dim, int block_size, float scale, int causal,
                  const uint64_t* tree_mask, void* workspace, size_t workspace_bytes,
-                 void* stream) {
+                 void* stream, const float* k_scales = nullptr, const float* v_scales = nullptr) {
     int st = check_attention_shape(max_blocks_per_seq, max_context_len, num_seqs, num_q_heads,
                                    num_kv_heads, head_dim, block_size, out_dtype);
     if (st != PKV_OK) return st;
@@ -426,13 +430,19 @@ int prefill_call(void* out, int out_dtype, const void* q, const int32_t* cu_q_le
         return PKV_ERR_NULL;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
         return PKV_ERR_ALIGN;
+    const bool block_scales = kv_fp8 && (k_scales != nullptr || v_scales != nullptr);
+    if (block_scales) {
+        if (!k_scales || !v_scales) return PKV_ERR_NULL;
+        if (!aligned4(k_scales) || !aligned4(v_scales)) return PKV_ERR_ALIGN;
+    }
     // Rows of sequences with a single query go to the bandwidth-bound decode
     // kernels; they can exist unless every sequence has max_q_len > 1 rows.
     const bool uniform_chunks = max_q_len > 1 && (int64_t)num_q_tokens == (int64_t)num_seqs * max_q_len;
     const bool any_decode_rows = !uniform_chunks;
     const bool decode_limits_ok = num_seqs <= kMaxDecodeSeqs &&
                                   (num_kv_heads <= 8 || num_kv_heads == kMaxDecodeKvHeads);
-    const bool rows = rows_path(num_seqs, max_q_len, num_q_heads, num_kv_heads, kv_fp8);
+    const bool rows = rows_path(num_seqs, max_q_len, num_q_heads, num_kv_heads, kv_fp8,
+                                block_scales);
     const bool streamk = !rows && pkv::prefill_streamk(max_q_len, num_q_heads / num_kv_heads);
     if (any_decode_rows && !decode_limits_ok) return PKV_ERR_UNSUPPORTED;
     // the stream-K chunk kernel keeps the sequences' unit prefix sums in LDS
@@ -481,6 +491,10 @@ int prefill_call(void* out, int out_dtype, const void* q, const int32_t* cu_q_le
         a.max_workers = pkv::prefill_streamk_max_workers(num_seqs, num_kv_heads, max_context_len);
     }
     a.tree_mask = tree_mask;
+    if (block_scales) {
+        a.k_scales = k_scales;
+        a.v_scales = v_scales;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (!any_decode_rows && !rows) return to_status(pkv::launch_prefill(a, s));
 
@@ -506,6 +520,8 @@ int prefill_call(void* out, int out_dtype, const void* q, const int32_t* cu_q_le
                                          align_up((size_t)2 * num_seqs * sizeof(int32_t), 256));
     d.max_workers = pkv::decode_max_workers(num_seqs, max_context_len);
     d.cu_q_lens = cu_q_lens;
+    d.k_scales = a.k_scales;
+    d.v_scales = a.v_scales;
     if (rows) {
         d.rows = max_q_len;
         d.causal = causal != 0;
@@ -513,8 +529,9 @@ int prefill_call(void* out, int out_dtype, const void* q, const int32_t* cu_q_le
         d.max_workers = pkv::decode_max_workers(num_seqs, max_context_len, max_q_len, num_kv_heads);
         return to_status(pkv::launch_decode(d, s));
     }
-    if (max_q_len > 1 && !streamk) {
-        // chunks and decode rows in one grid, sharing the CUs
+    if (max_q_len > 1 && !streamk && !block_scales) {
+        // chunks and decode rows in one grid, sharing the CUs (per-block
+        // scales: the chunk kernel, then the decode kernels)
         const hipError_t e = pkv::launch_mixed(a, d, s);
         if (e != hipErrorNotSupported) return to_status(e);
     }
@@ -588,6 +605,41 @@ int pkv_paged_prefill_attn_tree_fp8(void* out, int out_dtype, const void* q,
                         block_table, max_blocks_per_seq, context_lens, max_context_len, max_q_len,
                         num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                         scale, 1, tree_mask, workspace, workspace_bytes, stream);
+}
+
+int pkv_paged_prefill_attn_fp8_per_block(void* out, int out_dtype, const void* q,
+                                         const int32_t* cu_q_lens, const void* k_cache,
+                                         const void* v_cache, const float* k_scales,
+                                         const float* v_scales, const int32_t* block_table,
+                                         int max_blocks_per_seq, const int32_t* context_lens,
+                                         int max_context_len, int max_q_len, int num_q_tokens,
+                                         int num_seqs, int num_q_heads, int num_kv_heads,
+                                         int head_dim, int block_size, float scale, int causal,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+    if (num_seqs > 0 && num_q_tokens > 0 && (!k_scales || !v_scales)) return PKV_ERR_NULL;
+    return prefill_call(out, out_dtype, q, cu_q_lens, k_cache, v_cache, true, 1.0f, 1.0f,
+                        block_table, max_blocks_per_seq, context_lens, max_context_len, max_q_len,
+                        num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                        scale, causal, nullptr, workspace, workspace_bytes, stream, k_scales,
+                        v_scales);
+}
+
+int pkv_paged_prefill_attn_tree_fp8_per_block(
+    void* out, int out_dtype, const void* q, const int32_t* cu_q_lens, const uint64_t* tree_mask,
+    const void* k_cache, const void* v_cache, const float* k_scales, const float* v_scales,
+    const int32_t* block_table, int max_blocks_per_seq, const int32_t* context_lens,
+    int max_context_len, int max_q_len, int num_q_tokens, int num_seqs, int num_q_heads,
+    int num_kv_heads, int head_dim, int block_size, float scale, void* workspace,
+    size_t workspace_bytes, void* stream) {
+    if (max_q_len > kMaxTreeNodes) return PKV_ERR_UNSUPPORTED;
+    if (num_seqs > 0 && num_q_tokens > 0 && !tree_mask) return PKV_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(tree_mask) & 7) return PKV_ERR_ALIGN;
+    if (num_seqs > 0 && num_q_tokens > 0 && (!k_scales || !v_scales)) return PKV_ERR_NULL;
+    return prefill_call(out, out_dtype, q, cu_q_lens, k_cache, v_cache, true, 1.0f, 1.0f,
+                        block_table, max_blocks_per_seq, context_lens, max_context_len, max_q_len,
+                        num_q_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                        scale, 1, tree_mask, workspace, workspace_bytes, stream, k_scales,
+                        v_scales);
 }
 
 }  // extern "C"

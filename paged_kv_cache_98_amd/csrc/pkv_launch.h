@@ -110,6 +110,10 @@ struct PrefillArgs {
     float* records = nullptr;    // workspace: [max_workers][2][max_q_len * group][132]
     int64_t max_workers = 0;     // workers whose records fit the workspace
     const uint64_t* tree_mask = nullptr;  // [num_q_tokens] token-tree masks, or none
+    // FP8 pools with one scale per (block, KV head): [num_blocks][num_kv_heads]
+    // fp32 tables (then scale_log2 and out_scale carry none)
+    const float* k_scales = nullptr;
+    const float* v_scales = nullptr;
 };
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);

@@ -254,6 +254,19 @@ struct StageFp8 {
     uint4 v[2];
 };
 
+// FP8 pools with one scale per (block, KV head): lane l also carries the K
+// and V scales of the tile's 16-key group l % 4 (their blocks' scales), so
+// a wave has all four at hand through readlane.  A thread's two V rows are
+// adjacent keys of 16-key group `wave` (one block), so one V ratio serves
+// all its V values: they are staged as fp16(code x ratio), the ratio being
+// the group's V scale over the tile's reference (the largest V scale of the
+// item's tiles so far).  The K scales go to LDS beside the tile and
+// multiply its scores.
+struct StageFp8Bs : StageFp8 {
+    float ks;
+    float vs;
+};
+
 template <int BS>
 __device__ __forceinline__ void stage_offsets_fp8(uint32_t (&koff)[4], uint32_t (&voff)[4],
                                                   uint32_t row_bytes, int tid) {
@@ -293,8 +306,10 @@ __device__ __forceinline__ void stage_load_fp8(StageFp8& sg, PrefillIds& ids, co
     }
 }
 
+template <bool RATIO = false>
 __device__ __forceinline__ void stage_store_fp8(const StageFp8& sg, uint16_t* __restrict__ ks,
-                                                uint16_t* __restrict__ vt, int tid) {
+                                                uint16_t* __restrict__ vt, int tid,
+                                                float vratio = 1.0f) {
     const int col = tid & 7;
     const int kq = tid >> 3;
     // K: 16 codes -> 16 bf16 in row kq + 32 i, elements 16 col .. + 15
@@ -320,10 +335,18 @@ __device__ __forceinline__ void stage_store_fp8(const StageFp8& sg, uint16_t* __
         // bytes (a.k, c.k, a.k+1, c.k+1) of the two rows' words, k = 0 and 2
         const uint32_t w0 = __builtin_amdgcn_perm(c[j], a[j], 0x05010400u);
         const uint32_t w1 = __builtin_amdgcn_perm(c[j], a[j], 0x07030602u);
-        const f16x2_t vp[4] = {__builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w0, 1.0f, false),
-                               __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w0, 1.0f, true),
-                               __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w1, 1.0f, false),
-                               __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w1, 1.0f, true)};
+        f16x2_t vp[4] = {__builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w0, 1.0f, false),
+                         __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w0, 1.0f, true),
+                         __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w1, 1.0f, false),
+                         __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w1, 1.0f, true)};
+        if constexpr (RATIO) {
+            // code x ratio (<= 1) in fp16: the exact code value times the
+            // ratio rounded to fp16, rounded once more
+            const _Float16 r16 = (_Float16)vratio;
+            const f16x2_t rr = {r16, r16};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vp[e] = vp[e] * rr;
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int d = 16 * col + 4 * j + e;
@@ -408,14 +431,19 @@ constexpr int64_t kMaxChunkWorkers = 1024;  // stream-K workgroups, at most
 // rec_col is this lane's column record, or NULL for the final output: with
 // a record the unnormalised O^T, the reference maximum m and the sum l are
 // stored instead of O / l.
-template <int BS, int G, bool OUT_BF16, bool FP8>
+// BSC: FP8 pools with per-(block, KV head) scales (k_scales / v_scales,
+// [num_blocks][num_kv_heads]; s_sc: 2 x 8 floats of LDS, a tile buffer's
+// four K scales and its V reference).
+template <int BS, int G, bool OUT_BF16, bool FP8, bool BSC = false>
 __device__ __forceinline__ void chunk_item(
     uint16_t (&s_ks)[2][kKsElems], uint16_t (&s_vt)[2][kVtElems], void* __restrict__ out,
     const uint16_t* __restrict__ q, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, const int32_t* __restrict__ bt_row, int num_q_heads,
     int num_kv_heads, float scale_log2, float out_scale, int causal,
     const uint64_t* __restrict__ tree_mask, int q_begin, int lq, int ctx, int kvh, int r0, int t0,
-    int t1, float* rec_col) {
+    int t1, float* rec_col, const float* __restrict__ k_scales = nullptr,
+    const float* __restrict__ v_scales = nullptr, float* __restrict__ s_sc = nullptr) {
+    static_assert(!BSC || FP8, "per-block scales are an FP8 pool format");
     constexpr int P = kCols / G;  // query positions per workgroup
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -470,7 +498,7 @@ __device__ __forceinline__ void chunk_item(
         stage_offsets<BS>(koff, voff, row_bytes, tid);
     PrefillIds ids;
     ids.init(bt_row, (ctx + BS - 1) / BS, t0 * kKT / BS, lane);
-    using StageT = std::conditional_t<FP8, StageFp8, Stage>;
+    using StageT = std::conditional_t<FP8, std::conditional_t<BSC, StageFp8Bs, StageFp8>, Stage>;
     // check_c: whether keys of the tile may lie at or past kv_end
     auto load_next = [&](StageT& x, int k0n, auto check_c) {
         constexpr bool CHECK = decltype(check_c)::value;
@@ -478,12 +506,35 @@ __device__ __forceinline__ void chunk_item(
             stage_load_fp8<BS, CHECK>(x, ids, kbase, vbase, k0n, kv_end, block_bytes, koff, voff, tid, lane);
         else
             stage_load<BS, CHECK>(x, ids, kbase, vbase, k0n, kv_end, block_bytes, koff, voff, tid, lane);
+        if constexpr (BSC) {
+            // the scales of 16-key group lane % 4 (blocks past the context
+            // read as block 0: their keys are masked)
+            int id[4];
+            ids.tile<BS>(k0n, lane, id);
+            const int gq = lane & 3;
+            const int idg = gq == 0 ? id[0] : (gq == 1 ? id[1] : (gq == 2 ? id[2] : id[3]));
+            const size_t e = (size_t)idg * num_kv_heads + kvh;
+            x.ks = k_scales[e];
+            x.vs = v_scales[e];
+        }
     };
+    float vref_st = 0.0f;  // V reference of the last staged tile (BSC)
     auto store_tile = [&](const StageT& x, int b) {
-        if constexpr (FP8)
+        if constexpr (BSC) {
+            float vg[4];
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq)
+                vg[gq] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x.vs), gq));
+            const float vnew = fmaxf(fmaxf(vref_st, fmaxf(vg[0], vg[1])), fmaxf(vg[2], vg[3]));
+            vref_st = vnew;
+            stage_store_fp8<true>(x, s_ks[b], s_vt[b], tid, vg[tid >> 6] / vnew);
+            if (tid < 4) s_sc[8 * b + tid] = x.ks;
+            if (tid == 0) s_sc[8 * b + 4] = vnew;
+        } else if constexpr (FP8) {
             stage_store_fp8(x, s_ks[b], s_vt[b], tid);
-        else
+        } else {
             stage_store(x, s_ks[b], s_vt[b], tid);
+        }
     };
     StageT sg;
     if (t1 > t0) {
@@ -505,10 +556,24 @@ __device__ __forceinline__ void chunk_item(
     // this column's token-tree mask over the chunk's keys (none: all seen)
     const int tbase = tree_mask ? pos0 : 0x7fffffff;
     const uint64_t tmask = tree_mask && col_valid ? tree_mask[q_begin + r] : ~0ull;
+    float vref_o = 0.0f;  // units of O (BSC): the V reference of the last tile computed
     auto run_tile = [&](int j, auto mask_c, bool next, auto check_c) {
         constexpr bool MASK = decltype(mask_c)::value;
         const int k0 = j * kKT;
         const int buf = j & 1;
+        if constexpr (BSC) {
+            // this tile's V values are in units of its reference, which only
+            // grows: bring O to it first
+            const float vb = s_sc[8 * buf + 4];
+            if (vb > vref_o) {
+                const float f = vref_o / vb;
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) o[mb][e] *= f;
+                vref_o = vb;
+            }
+        }
         if (next)
             load_next(sg, k0 + kKT, check_c);
         // S for both halves first, so that each half's softmax (VALU) has
@@ -540,6 +605,13 @@ __device__ __forceinline__ void chunk_item(
                                            16 * (ks ^ (mb & 1));
                     va[ks][mb] = *reinterpret_cast<const f16x8_t*>(vrow + vt_lane);
                 }
+            if constexpr (BSC) {
+                // the half's keys 0 .. 15 (elements 0 .. 7) lie in 16-key
+                // group 2 kb, keys 16 .. 31 in group 2 kb + 1
+                const float ka = s_sc[8 * buf + 2 * kb], kz = s_sc[8 * buf + 2 * kb + 1];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) sc[kb][e] *= e < 8 ? ka : kz;
+            }
             f16x8_t pf[2];  // P^T fragments, keys 16 ks .. 16 ks + 15 of the half
             softmax_half<MASK>(sc[kb], pf, o, m_run, l_run, cl2, k0 + 32 * kb, h, pos, ctx, diag,
                                tmask, tbase);
@@ -590,6 +662,13 @@ __device__ __forceinline__ void chunk_item(
     // ---- finish: total l over both halves, then out = O / l
     const float lt = sum_lane_halves(l_run);
     if (!col_valid) return;
+    if constexpr (BSC) {
+        // O in absolute units
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[mb][e] *= vref_o;
+    }
     if (rec_col) {  // part of the item's keys: the record of this column
         float* rp = rec_col;
 #pragma unroll
@@ -671,7 +750,7 @@ __device__ __forceinline__ bool slot_rows(SlotRows& sr, const int32_t* __restric
     return true;
 }
 
-template <int BS, int G, bool OUT_BF16, bool FP8>
+template <int BS, int G, bool OUT_BF16, bool FP8, bool BSC = false>
 __device__ __forceinline__ void run_slot(
     uint16_t (&s_ks)[2][kKsElems], uint16_t (&s_vt)[2][kVtElems], void* __restrict__ out,
     const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q_lens,
@@ -679,15 +758,18 @@ __device__ __forceinline__ void run_slot(
     const int32_t* __restrict__ block_table, int max_blocks_per_seq,
     const int32_t* __restrict__ context_lens, int max_context_len, int num_seqs,
     int num_q_heads, int num_kv_heads, float scale_log2, float out_scale, int causal,
-    int decode_rows_elsewhere, const uint64_t* __restrict__ tree_mask, int kvh, int slot) {
+    int decode_rows_elsewhere, const uint64_t* __restrict__ tree_mask, int kvh, int slot,
+    const float* __restrict__ k_scales = nullptr, const float* __restrict__ v_scales = nullptr,
+    float* __restrict__ s_sc = nullptr) {
     SlotRows sr;
     if (!slot_rows<kCols / G>(sr, cu_q_lens, context_lens, max_context_len, num_seqs, causal,
                               decode_rows_elsewhere, slot))
         return;
-    chunk_item<BS, G, OUT_BF16, FP8>(s_ks, s_vt, out, q, k_cache, v_cache,
-                                     block_table + (size_t)sr.seq * max_blocks_per_seq, num_q_heads,
-                                     num_kv_heads, scale_log2, out_scale, causal, tree_mask,
-                                     sr.q_begin, sr.lq, sr.ctx, kvh, sr.r0, 0, sr.ntiles, nullptr);
+    chunk_item<BS, G, OUT_BF16, FP8, BSC>(s_ks, s_vt, out, q, k_cache, v_cache,
+                                          block_table + (size_t)sr.seq * max_blocks_per_seq,
+                                          num_q_heads, num_kv_heads, scale_log2, out_scale, causal,
+                                          tree_mask, sr.q_begin, sr.lq, sr.ctx, kvh, sr.r0, 0,
+                                          sr.ntiles, nullptr, k_scales, v_scales, s_sc);
 }
 
 // The position, inside an XCD's run of (KV head, slot) items
@@ -751,7 +833,7 @@ __device__ __forceinline__ int ranked_item(int* scratch, const int32_t* __restri
 // sequence i is y - T(i),
 // T(i) = cu_q_lens[i] / P + i; T never skips a needed slot.  Each
 // workgroup runs all key tiles of its (slot, KV head) item.
-template <int BS, int G, bool OUT_BF16, bool FP8>
+template <int BS, int G, bool OUT_BF16, bool FP8, bool BSC = false>
 __global__ void __launch_bounds__(kThreads, 2)
 prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
                     const int32_t* __restrict__ cu_q_lens, const void* __restrict__ k_cache,
@@ -759,10 +841,12 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
                     int max_blocks_per_seq, const int32_t* __restrict__ context_lens,
                     int max_context_len, int num_seqs, int num_q_heads, int num_kv_heads,
                     float scale_log2, float out_scale, int causal, int decode_rows_elsewhere,
-                    const uint64_t* __restrict__ tree_mask, int pair_cus) {
+                    const uint64_t* __restrict__ tree_mask, int pair_cus,
+                    const float* __restrict__ k_scales, const float* __restrict__ v_scales) {
     constexpr int P = kCols / G;
     __shared__ __attribute__((aligned(16))) uint16_t s_ks[2][kKsElems];
     __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kVtElems];
+    __shared__ float s_sc[BSC ? 16 : 1];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     // The dispatcher deals workgroups to the 8 XCDs in turn, each with its
@@ -794,10 +878,11 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
     }
     const int kvh = item / gridDim.x;
     const int slot = item - kvh * gridDim.x;
-    run_slot<BS, G, OUT_BF16, FP8>(s_ks, s_vt, out, q, cu_q_lens, k_cache, v_cache, block_table,
-                                   max_blocks_per_seq, context_lens, max_context_len, num_seqs,
-                                   num_q_heads, num_kv_heads, scale_log2, out_scale, causal,
-                                   decode_rows_elsewhere, tree_mask, kvh, slot);
+    run_slot<BS, G, OUT_BF16, FP8, BSC>(s_ks, s_vt, out, q, cu_q_lens, k_cache, v_cache,
+                                        block_table, max_blocks_per_seq, context_lens,
+                                        max_context_len, num_seqs, num_q_heads, num_kv_heads,
+                                        scale_log2, out_scale, causal, decode_rows_elsewhere,
+                                        tree_mask, kvh, slot, k_scales, v_scales, s_sc);
 }
 
 // A mixed batch in one grid ("LLM 推理优化技术全景", Chunked Prefill,
@@ -887,7 +972,7 @@ __device__ __forceinline__ int streamk_units(const int32_t* __restrict__ cu_q_le
 // unit prefix sums, which workgroup 0 also stores in cum_out.
 // Records: [num_workers][2][max_q_len * G][kRecStride] floats, column
 // c = r G + g.
-template <int BS, int G, bool OUT_BF16, bool FP8>
+template <int BS, int G, bool OUT_BF16, bool FP8, bool BSC = false>
 __global__ void __launch_bounds__(kThreads, 2)
 prefill_streamk_kernel(void* __restrict__ out, float* __restrict__ rec,
                        int32_t* __restrict__ cum_out, const uint16_t* __restrict__ q,
@@ -896,10 +981,12 @@ prefill_streamk_kernel(void* __restrict__ out, float* __restrict__ rec,
                        int max_blocks_per_seq, const int32_t* __restrict__ context_lens,
                        int max_context_len, int num_seqs, int num_q_heads, int num_kv_heads,
                        float scale_log2, float out_scale, int causal, int decode_rows_elsewhere,
-                       int num_workers, int max_q_len, const uint64_t* __restrict__ tree_mask) {
+                       int num_workers, int max_q_len, const uint64_t* __restrict__ tree_mask,
+                       const float* __restrict__ k_scales, const float* __restrict__ v_scales) {
     const int rec_cols = max_q_len * G;  // columns per record slot
     __shared__ __attribute__((aligned(16))) uint16_t s_ks[2][kKsElems];
     __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kVtElems];
+    __shared__ float s_sc[BSC ? 16 : 1];
     __shared__ int32_t s_part[kThreads / 64];
     extern __shared__ int32_t s_cum[];  // s_cum[i] = units of sequences < i
     const int tid = threadIdx.x;
@@ -977,10 +1064,11 @@ prefill_streamk_kernel(void* __restrict__ out, float* __restrict__ rec,
         float* rc = (tile0 != 0 || t1 != n)
                         ? rec + ((size_t)(w * 2 + slot) * rec_cols + col) * kRecStride
                         : nullptr;
-        chunk_item<BS, G, OUT_BF16, FP8>(s_ks, s_vt, out, q, k_cache, v_cache,
-                                         block_table + (size_t)seq * max_blocks_per_seq,
-                                         num_q_heads, num_kv_heads, scale_log2, out_scale, causal,
-                                         tree_mask, q_begin, lq, ctx, kvh, 0, tile0, t1, rc);
+        chunk_item<BS, G, OUT_BF16, FP8, BSC>(s_ks, s_vt, out, q, k_cache, v_cache,
+                                              block_table + (size_t)seq * max_blocks_per_seq,
+                                              num_q_heads, num_kv_heads, scale_log2, out_scale,
+                                              causal, tree_mask, q_begin, lq, ctx, kvh, 0, tile0,
+                                              t1, rc, k_scales, v_scales, s_sc);
         slot = 1;
         t = seg_end;
     }
@@ -1104,11 +1192,11 @@ prefill_streamk_merge_kernel(void* __restrict__ out, const float* __restrict__ r
     }
 }
 
-template <int BS, int G, bool OUT_BF16, bool FP8>
+template <int BS, int G, bool OUT_BF16, bool FP8, bool BSC = false>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     constexpr int P = kCols / G;
     if (a.streamk) {
-        auto kern = prefill_streamk_kernel<BS, G, OUT_BF16, FP8>;
+        auto kern = prefill_streamk_kernel<BS, G, OUT_BF16, FP8, BSC>;
         const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int32_t);
         int resident = 0;
         hipError_t e = resident_workgroups(reinterpret_cast<const void*>(kern), kThreads, lds,
@@ -1124,7 +1212,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
                            a.max_context_len, a.num_seqs, a.num_q_heads, a.num_kv_heads,
                            a.scale_log2, a.out_scale, a.causal ? 1 : 0,
                            a.decode_rows_elsewhere ? 1 : 0, (int)workers, a.max_q_len,
-                           a.tree_mask);
+                           a.tree_mask, a.k_scales, a.v_scales);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         // With about as many items (sequence, KV head) as workers, an item
@@ -1149,7 +1237,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     // Pair heavy and light slots on each CU when the whole grid is at most
     // about two rounds of the chip (the order is ranked in each workgroup,
     // in LDS the K tiles take later).
-    auto kern = prefill_mfma_kernel<BS, G, OUT_BF16, FP8>;
+    auto kern = prefill_mfma_kernel<BS, G, OUT_BF16, FP8, BSC>;
     int pair_cus = 0;
     {
         int resident = 0, cus = 0, dev = 0;
@@ -1169,12 +1257,16 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
                        dim3(kThreads), 0, stream, a.out, a.q, a.cu_q_lens, a.k_cache, a.v_cache,
                        a.block_table, a.max_blocks_per_seq, a.context_lens, a.max_context_len,
                        a.num_seqs, a.num_q_heads, a.num_kv_heads, a.scale_log2, a.out_scale,
-                       a.causal ? 1 : 0, a.decode_rows_elsewhere ? 1 : 0, a.tree_mask, pair_cus);
+                       a.causal ? 1 : 0, a.decode_rows_elsewhere ? 1 : 0, a.tree_mask, pair_cus,
+                       a.k_scales, a.v_scales);
     return hipGetLastError();
 }
 
 template <int BS, int G>
 hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t s) {
+    if (a.kv_fp8 && a.k_scales != nullptr)
+        return a.out_bf16 ? launch_prefill_t<BS, G, true, true, true>(a, s)
+                          : launch_prefill_t<BS, G, false, true, true>(a, s);
     if (a.kv_fp8)
         return a.out_bf16 ? launch_prefill_t<BS, G, true, true>(a, s)
                           : launch_prefill_t<BS, G, false, true>(a, s);

@@ -482,3 +482,94 @@ def test_decode_fp8_per_block_full_8b_batch_sampled():
                                    np.arange(len(ids), dtype=np.int32)[None, :],
                                    np.array([n], dtype=np.int32), w.scale)
         parity(out[i:i + 1], ref, what=f"fp8 per block 8b batch seq {i} (ctx {n})")
+
+
+def run_prefill_fp8_pb(b, kd, vd, ksd, vsd, causal=True, out_dtype=torch.float32, tree_mask=None):
+    w = b.workload
+    return pkv.paged_prefill_attn_fp8_per_block(b.q, b.cu_q_lens, kd, vd, ksd, vsd, b.block_table,
+                                                b.context_lens, w.scale,
+                                                max_context_len=w.max_context_len,
+                                                max_q_len=w.max_q_len, causal=causal,
+                                                out_dtype=out_dtype, tree_mask=tree_mask)
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("group", [1, 4, 16])
+def test_prefill_fp8_per_block_chunks(bs, group):
+    """Wide chunks (the grid chunk kernel) and single-row sequences (the
+    decode kernels, after it) over FP8 pools with per-(block, head) scales,
+    causal and not."""
+    hkv = 2
+    w = W.make_workload(f"fp8pb_chunks_g{group}_bs{bs}", [c for c, _ in FP8_CHUNKS],
+                        [q for _, q in FP8_CHUNKS], num_q_heads=hkv * group, num_kv_heads=hkv,
+                        block_size=bs, seed=3600 + group + bs)
+    print(f"[fp8 per block prefill] {w.name}", flush=True)
+    bc = W.materialize(w, logical=True, poison=True)
+    kc, vc, ks, vs = W.fp8_block_pools(bc, seed=group + bs)
+    b = bc.to(DEV)
+    kd, vd, ksd, vsd = kc.to(DEV), vc.to(DEV), ks.to(DEV), vs.to(DEV)
+    for causal in (True, False):
+        out = run_prefill_fp8_pb(b, kd, vd, ksd, vsd, causal)
+        torch.cuda.synchronize()
+        parity(out, oracle_prefill_fp8(bc, kc, vc, causal, ks.numpy(), vs.numpy()),
+               what=f"{w.name} causal={causal}")
+
+
+@pytest.mark.parametrize("group,rows", [(4, 4), (1, 16), (4, 6), (16, 2), (8, 16), (2, 12)])
+def test_prefill_fp8_per_block_short_chunks(group, rows):
+    """Short chunks over per-(block, head)-scaled FP8 pools: up to 16 (row,
+    head) columns per KV head on the decode kernel's matrix-core tile (the
+    rows path), wider ones on the stream-K chunk kernel with its merge;
+    bf16 output equals the fp32 output rounded; determinism."""
+    cases = [(3000, rows), (2500, 1), (40, min(3, rows)), (4100, rows), (700, max(rows - 1, 1)),
+             (129, 2), (17, rows)]
+    w = W.make_workload(f"fp8pb_short_g{group}_r{rows}", [c for c, _ in cases],
+                        [q for _, q in cases], num_q_heads=2 * group, num_kv_heads=2,
+                        block_size=16, seed=3700 + group + rows)
+    print(f"[fp8 per block short chunks] {w.name}", flush=True)
+    bc = W.materialize(w, logical=True, poison=True)
+    kc, vc, ks, vs = W.fp8_block_pools(bc, seed=group * 7 + rows)
+    b = bc.to(DEV)
+    kd, vd, ksd, vsd = kc.to(DEV), vc.to(DEV), ks.to(DEV), vs.to(DEV)
+    o32 = run_prefill_fp8_pb(b, kd, vd, ksd, vsd)
+    o32b = run_prefill_fp8_pb(b, kd, vd, ksd, vsd)
+    o16 = run_prefill_fp8_pb(b, kd, vd, ksd, vsd, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o32, o32b)
+    ref = oracle_prefill_fp8(bc, kc, vc, True, ks.numpy(), vs.numpy())
+    parity(o32, ref, what=w.name)
+    bf16_parity(o16, o32, ref, what=w.name + " bf16 out", fp32_err=1e-3, min_within=0.95)
+
+
+@pytest.mark.parametrize("group,nodes", [(1, 16), (4, 16), (2, 6)])
+def test_tree_fp8_per_block(group, nodes):
+    """Token trees over per-(block, head)-scaled FP8 pools, against the tree
+    oracle on the values: with power-of-two scales every code's value is a
+    bf16 value, so the oracle takes them as bf16 pools.  16 columns per KV
+    head or fewer take the rows path, more the stream-K chunk kernel."""
+    from oracle import tree
+    hkv = 2
+    ctx = [nodes, nodes + 1, 31, 33, 64, 65, 1000, 4097]
+    cases = [(c, nodes) for c in ctx] + [(300, 1), (50, 0), (129, nodes - 1)]
+    w = W.make_workload(f"tree_fp8pb_g{group}_n{nodes}", [c for c, _ in cases],
+                        [q for _, q in cases], num_q_heads=hkv * group, num_kv_heads=hkv,
+                        block_size=16, seed=3800 + group + nodes)
+    print(f"[tree fp8 per block] {w.name}", flush=True)
+    bc = W.materialize(w, logical=True, poison=True)
+    kc, vc, ks, vs = W.fp8_block_pools(bc, seed=nodes)
+    ks, vs = torch.exp2(torch.round(torch.log2(ks))), torch.exp2(torch.round(torch.log2(vs)))
+    masks = W.tree_masks(w)
+
+    def values(c, t):
+        x = fp8.e4m3_value(c.numpy()) * t.numpy()[:, None, :, None].astype(np.float64)
+        return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+
+    kv = [values(kc, ks), values(vc, vs)]
+    ref = tree.paged_attention_tree(bits16(bc.q), bits16(kv[0]), bits16(kv[1]),
+                                    bc.block_table.numpy(), bc.context_lens.numpy(),
+                                    bc.cu_q_lens.numpy(), masks.numpy().view(np.uint64), w.scale)
+    b = bc.to(DEV)
+    out = run_prefill_fp8_pb(b, kc.to(DEV), vc.to(DEV), ks.to(DEV), vs.to(DEV),
+                             tree_mask=masks.to(DEV))
+    torch.cuda.synchronize()
+    parity(out, ref, what=w.name)
