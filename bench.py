@@ -104,6 +104,17 @@ TRAFFIC_SPEC = {
                                "args": "--workload spec_verify_fp8"},
     "mixed_prefill_c4x512_d0_fp8": {"kernels": ["prefill_mfma_kernel"], "sources": _PREFILL_SRC,
                                     "args": "--workload prefill_chunks_fp8"},
+    # FP8 pools with per-(block, KV head) scales: the 6-row verify's 24
+    # columns per KV head take the stream-K chunk kernel there
+    "llama8b_decode_b64_fp8_per_block": {"kernels": _DECODE_K, "sources": _DECODE_SRC,
+                                         "args": "--workload llama8b_decode_fp8_per_block"},
+    "spec_verify_b64_q6_fp8_per_block": {"kernels": ["prefill_streamk_kernel",
+                                                     "prefill_streamk_merge_kernel"],
+                                         "sources": _PREFILL_SRC,
+                                         "args": "--workload spec_verify_fp8_per_block"},
+    "mixed_prefill_c4x512_d0_fp8_per_block": {"kernels": ["prefill_mfma_kernel"],
+                                              "sources": _PREFILL_SRC,
+                                              "args": "--workload prefill_chunks_fp8_per_block"},
     "cow_copy_4096x32k": {"kernels": ["copy_blocks_kernel"],
                           "sources": ["paged_kv_cache_98_amd/csrc/kv_append.hip"],
                           "args": "--workload cow_copy"},
@@ -314,6 +325,10 @@ def workload_by_name(name):
         # the chunk and verify batches over an FP8 (E4M3) cache
         "prefill_chunks_fp8": lambda: W.mixed_prefill(num_decodes=0),
         "spec_verify_fp8": lambda: W.spec_verify(),
+        # the same over FP8 pools with one scale per (block, KV head)
+        "llama8b_decode_fp8_per_block": lambda: W.llama8b_decode(),
+        "prefill_chunks_fp8_per_block": lambda: W.mixed_prefill(num_decodes=0),
+        "spec_verify_fp8_per_block": lambda: W.spec_verify(),
     }
     if name not in table:
         raise SystemExit(f"unknown workload {name}; choose from {sorted(table)}")
@@ -400,10 +415,11 @@ def hbm_ceiling(dev):
                     "written per call), median of 10 event-timed calls"}
 
 
-def cpu_baseline_fp8(batch, w, seqs=8, min_seconds=10.0):
+def cpu_baseline_fp8(batch, w, seqs=8, min_seconds=10.0, scales=None):
     """The fp64 FP8-cache oracle (numpy, one process), as it stands, on the
     first `seqs` sequences of the batch (host copies of their blocks),
-    repeated for at least min_seconds; the rate is the mean."""
+    repeated for at least min_seconds; the rate is the mean.  scales: the
+    (k, v) per-(block, head) tables of per-block pools, else None."""
     import numpy as np
     import torch
     from oracle import fp8
@@ -420,11 +436,14 @@ def cpu_baseline_fp8(batch, w, seqs=8, min_seconds=10.0):
         table[i, :need[i]] = np.arange(base, base + need[i])
         base += need[i]
     q = batch.q[:seqs].cpu().view(torch.int16).numpy().view(np.uint16)
+    ks = vs = W.FP8_SCALE
+    if scales is not None:
+        idd = ids.to(scales[0].device)
+        ks, vs = (t.index_select(0, idd).cpu().numpy() for t in scales)
     reps, total = 0, 0.0
     while reps < 2 or total < min_seconds:
         t0 = time.perf_counter()
-        fp8.paged_decode_fp8(q, kc, vc, W.FP8_SCALE, W.FP8_SCALE, table,
-                             np.array(ctx, np.int32), w.scale)
+        fp8.paged_decode_fp8(q, kc, vc, ks, vs, table, np.array(ctx, np.int32), w.scale)
         total += time.perf_counter() - t0
         reps += 1
     t = total / reps
@@ -480,12 +499,20 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = workload_by_name(args.workload)
-    kv_fp8 = args.workload.endswith("_fp8")
-    wname = w.name + ("_fp8" if kv_fp8 else "")
-    print(f"[bench] workload {w.describe()}{' FP8 KV' if kv_fp8 else ''}", file=sys.stderr,
-          flush=True)
+    kv_pb = args.workload.endswith("_fp8_per_block")
+    kv_fp8 = kv_pb or args.workload.endswith("_fp8")
+    wname = w.name + ("_fp8_per_block" if kv_pb else ("_fp8" if kv_fp8 else ""))
+    print(f"[bench] workload {w.describe()}"
+          f"{' FP8 KV, per-(block, head) scales' if kv_pb else (' FP8 KV' if kv_fp8 else '')}",
+          file=sys.stderr, flush=True)
     b = W.materialize(w, device=dev, poison=False)
-    if kv_fp8:
+    ksc = vsc = None
+    if kv_pb:
+        # E4M3 codes with a scale per (block, KV head), from each block's
+        # absolute maximum after a per-block magnitude spread
+        b.k_cache, b.v_cache, ksc, vsc = W.fp8_block_pools(b, seed=1)
+        torch.cuda.empty_cache()
+    elif kv_fp8:
         # E4M3 code pools made by torch's float8 cast; the bf16 pools go
         b.k_cache, b.v_cache = W.fp8_pools(b)
         torch.cuda.empty_cache()
@@ -503,7 +530,19 @@ def main():
     tree_mask = W.tree_masks(w).to(dev) if is_tree else None
 
     def attend():
-        if kv_fp8 and w.is_decode:
+        if kv_pb and w.is_decode:
+            pkv.paged_decode_attn_fp8_per_block(b.q, b.k_cache, b.v_cache, ksc, vsc,
+                                                b.block_table, b.context_lens, w.scale,
+                                                max_context_len=w.max_context_len, out=out,
+                                                workspace=ws, stream=stream)
+        elif kv_pb:
+            pkv.paged_prefill_attn_fp8_per_block(b.q, b.cu_q_lens, b.k_cache, b.v_cache, ksc, vsc,
+                                                 b.block_table, b.context_lens, w.scale,
+                                                 max_context_len=w.max_context_len,
+                                                 max_q_len=w.max_q_len, causal=True, out=out,
+                                                 workspace=ws if ws_bytes else None,
+                                                 stream=stream)
+        elif kv_fp8 and w.is_decode:
             pkv.paged_decode_attn_fp8(b.q, b.k_cache, b.v_cache, W.FP8_SCALE, W.FP8_SCALE,
                                       b.block_table, b.context_lens, w.scale,
                                       max_context_len=w.max_context_len, out=out, workspace=ws,
@@ -528,7 +567,10 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        if kv_fp8:
+        if kv_pb:
+            pkv.kv_append_fp8_per_block(b.k_new, b.v_new, b.slot_mapping, b.k_cache, b.v_cache,
+                                        ksc, vsc, stream=stream)
+        elif kv_fp8:
             pkv.kv_append_fp8(b.k_new, b.v_new, b.slot_mapping, b.k_cache, b.v_cache,
                               W.FP8_SCALE, W.FP8_SCALE, stream=stream)
         else:
@@ -676,7 +718,8 @@ def main():
                         "bracketed by device synchronisation",
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline_fp8(b, w) if kv_fp8 else cpu_baseline(b, w)
+        rec["cpu_baseline"] = (cpu_baseline_fp8(b, w, scales=(ksc, vsc) if kv_pb else None)
+                               if kv_fp8 else cpu_baseline(b, w))
         if not kv_fp8:
             rec["cpu_baseline_1t"] = cpu_baseline_1t(b, w)
         rec["hbm_ceiling"] = hbm_ceiling(dev)

@@ -250,7 +250,8 @@ struct KvFp8MfmaBh : KvFp8Mfma {
 
 // A tile's two scales, from the [num_blocks][num_kv_heads] fp32 tables:
 // lane-uniform buffer loads, issued with the tile's own loads (vector
-// memory, so they complete in order with them).
+// memory, so they complete in order with them).  Scalar loads measured no
+// fewer vector registers and more spills on the two-block rows tile.
 __device__ __forceinline__ void load_block_scales(const float* k_scales, const float* v_scales,
                                                   int phys, int num_kv_heads, int kvh, float& ks,
                                                   float& vs) {

@@ -362,11 +362,14 @@ __device__ __forceinline__ void stage_store_fp8(const StageFp8& sg, uint16_t* __
 // column's position or past the context.
 constexpr float kLazyMax = 8.0f;  // p < 2^8 between rescales
 
-template <bool MASK>
+// TWO: elements 0 .. 7 (the half's first 16 keys) take the score scale cl2
+// and elements 8 .. 15 cl2b (per-block K scales folded into each 16-key
+// group's scale; the scales are >= 0, so a group's maximum scales with it).
+template <bool MASK, bool TWO = false>
 __device__ __forceinline__ void softmax_half(f32x16_t& s, f16x8_t (&pf)[2], f32x16_t (&o)[4],
                                              float& m_run, float& l_run, float cl2, int kb0, int h,
                                              int pos, int ctx, bool diag, uint64_t tmask,
-                                             int tbase) {
+                                             int tbase, float cl2b = 0.0f) {
     // four independent partial maxima / sums, so neither is one long
     // dependent chain
     float mt4[4] = {-3.402823466e38f, -3.402823466e38f, -3.402823466e38f, -3.402823466e38f};
@@ -380,10 +383,22 @@ __device__ __forceinline__ void softmax_half(f32x16_t& s, f16x8_t (&pf)[2], f32x
                             (key < tbase || ((tmask >> ((key - tbase) & 63)) & 1));
             s[e] = ok ? s[e] : -3.402823466e38f;
         }
-        mt4[e & 3] = fmaxf(mt4[e & 3], s[e]);
+        if constexpr (TWO) {
+            // partial maxima 0, 1 over elements 0 .. 7, 2, 3 over 8 .. 15
+            const int k = 2 * (e >> 3) + (e & 1);
+            mt4[k] = fmaxf(mt4[k], s[e]);
+        } else {
+            mt4[e & 3] = fmaxf(mt4[e & 3], s[e]);
+        }
     }
-    float mt = fmaxf(fmaxf(mt4[0], mt4[1]), fmaxf(mt4[2], mt4[3]));
-    mt = max_lane_halves(mt) * cl2;
+    float mt;
+    if constexpr (TWO) {
+        mt = fmaxf(fmaxf(mt4[0], mt4[1]) * cl2, fmaxf(mt4[2], mt4[3]) * cl2b);
+        mt = max_lane_halves(mt);
+    } else {
+        mt = fmaxf(fmaxf(mt4[0], mt4[1]), fmaxf(mt4[2], mt4[3]));
+        mt = max_lane_halves(mt) * cl2;
+    }
     // Lazy reference maximum: m_run moves only when a score exceeds it by
     // more than kLazyMax (log2 units), so p = 2^(s - m_run) stays below
     // 2^kLazyMax (far inside fp16) and O and l are rescaled only on those
@@ -401,7 +416,7 @@ __device__ __forceinline__ void softmax_half(f32x16_t& s, f16x8_t (&pf)[2], f32x
     const float mn = m_run;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-        float p = fast_exp2(fmaf(s[e], cl2, -mn));
+        float p = fast_exp2(fmaf(s[e], TWO && e >= 8 ? cl2b : cl2, -mn));
         // a dropped key must give 0 even for a zero scale
         if (MASK) p = s[e] == -3.402823466e38f ? 0.0f : p;
         pf[e >> 3][e & 7] = (_Float16)p;
@@ -605,16 +620,18 @@ __device__ __forceinline__ void chunk_item(
                                            16 * (ks ^ (mb & 1));
                     va[ks][mb] = *reinterpret_cast<const f16x8_t*>(vrow + vt_lane);
                 }
+            f16x8_t pf[2];  // P^T fragments, keys 16 ks .. 16 ks + 15 of the half
             if constexpr (BSC) {
                 // the half's keys 0 .. 15 (elements 0 .. 7) lie in 16-key
-                // group 2 kb, keys 16 .. 31 in group 2 kb + 1
-                const float ka = s_sc[8 * buf + 2 * kb], kz = s_sc[8 * buf + 2 * kb + 1];
-#pragma unroll
-                for (int e = 0; e < 16; ++e) sc[kb][e] *= e < 8 ? ka : kz;
+                // group 2 kb, keys 16 .. 31 in group 2 kb + 1: each group's
+                // K scale joins its score scale
+                const float ka = cl2 * s_sc[8 * buf + 2 * kb], kz = cl2 * s_sc[8 * buf + 2 * kb + 1];
+                softmax_half<MASK, true>(sc[kb], pf, o, m_run, l_run, ka, k0 + 32 * kb, h, pos, ctx,
+                                         diag, tmask, tbase, kz);
+            } else {
+                softmax_half<MASK>(sc[kb], pf, o, m_run, l_run, cl2, k0 + 32 * kb, h, pos, ctx,
+                                   diag, tmask, tbase);
             }
-            f16x8_t pf[2];  // P^T fragments, keys 16 ks .. 16 ks + 15 of the half
-            softmax_half<MASK>(sc[kb], pf, o, m_run, l_run, cl2, k0 + 32 * kb, h, pos, ctx, diag,
-                               tmask, tbase);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
