@@ -104,13 +104,10 @@ TRAFFIC_SPEC = {
                                "args": "--workload spec_verify_fp8"},
     "mixed_prefill_c4x512_d0_fp8": {"kernels": ["prefill_mfma_kernel"], "sources": _PREFILL_SRC,
                                     "args": "--workload prefill_chunks_fp8"},
-    # FP8 pools with per-(block, KV head) scales: the 6-row verify's 24
-    # columns per KV head take the stream-K chunk kernel there
+    # FP8 pools with per-(block, KV head) scales
     "llama8b_decode_b64_fp8_per_block": {"kernels": _DECODE_K, "sources": _DECODE_SRC,
                                          "args": "--workload llama8b_decode_fp8_per_block"},
-    "spec_verify_b64_q6_fp8_per_block": {"kernels": ["prefill_streamk_kernel",
-                                                     "prefill_streamk_merge_kernel"],
-                                         "sources": _PREFILL_SRC,
+    "spec_verify_b64_q6_fp8_per_block": {"kernels": _DECODE_K, "sources": _DECODE_SRC,
                                          "args": "--workload spec_verify_fp8_per_block"},
     "mixed_prefill_c4x512_d0_fp8_per_block": {"kernels": ["prefill_mfma_kernel"],
                                               "sources": _PREFILL_SRC,

@@ -581,8 +581,9 @@ int pkv_paged_prefill_attn_tree_fp8(void *out, int out_dtype, const void *q,
  * the K scale of its block, and its value the V scale, as a ratio to the
  * largest V scale of the item's tiles so far: on the chunk kernels V is
  * staged as fp16(code x ratio) (the ratio rounded to fp16, the product
- * rounded once more); on the rows path, which takes chunks of at most 16
- * (row, head) columns per KV head here, P is scaled as in the decode.
+ * rounded once more); on the rows path (as over FP8 pools: chunks of at
+ * most 16 rows and 32 (row, head) columns per KV head) P is scaled as in
+ * the decode.
  * Chunks and single-row sequences in one call run one after the other (the
  * chunk kernel, then the decode kernels), not in one grid.
  */

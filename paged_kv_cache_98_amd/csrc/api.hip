@@ -84,16 +84,13 @@ void* scratch_address(hipError_t* err) {
 }
 
 // Calls whose chunks have at most 16 rows and 64 (row, head) columns per KV
-// head, 32 over FP8 pools, 16 over FP8 pools with per-(block, KV head)
-// scales (speculative-decoding verification, token trees), run whole on the
-// decode kernel's matrix-core tile, every sequence's rows as columns of its
-// S = K Q^T; wider ones on the chunk kernels.
+// head, 32 over FP8 pools (speculative-decoding verification, token trees),
+// run whole on the decode kernel's matrix-core tile, every sequence's rows
+// as columns of its S = K Q^T; wider ones on the chunk kernels.
 constexpr int kRowsPathMaxRows = 16;
-bool rows_path(int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads, bool kv_fp8,
-               bool block_scales = false) {
+bool rows_path(int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads, bool kv_fp8) {
     const int cols = max_q_len * (num_q_heads / num_kv_heads);
-    const int max_cols = block_scales ? 16 : (kv_fp8 ? 32 : 64);
-    return max_q_len >= 2 && max_q_len <= kRowsPathMaxRows && cols <= max_cols &&
+    return max_q_len >= 2 && max_q_len <= kRowsPathMaxRows && cols <= (kv_fp8 ? 32 : 64) &&
            num_seqs <= kMaxDecodeSeqs && (num_kv_heads <= 8 || num_kv_heads == kMaxDecodeKvHeads);
 }
 
@@ -121,15 +118,14 @@ size_t rows_workspace(int num_seqs, int max_q_len, int num_q_heads, int num_kv_h
                                        max_context_len, max_q_len);
 }
 
-// What a prefill call of these sizes needs over any pool format (the rows
-// path takes more columns over bf16 pools than over FP8 ones, and fewest
-// with per-block scales).
+// What a prefill call of these sizes needs over either pool type (the rows
+// path takes more columns over bf16 pools than over FP8 ones).
 size_t prefill_workspace(int num_seqs, int max_q_len, int num_q_heads, int num_kv_heads,
                          int head_dim, int max_context_len) {
     size_t n = 0;
-    for (const int fmt : {0, 1, 2}) {
+    for (const bool fp8 : {false, true}) {
         const size_t c =
-            rows_path(num_seqs, max_q_len, num_q_heads, num_kv_heads, fmt > 0, fmt == 2)
+            rows_path(num_seqs, max_q_len, num_q_heads, num_kv_heads, fp8)
                 ? rows_workspace(num_seqs, max_q_len, num_q_heads, num_kv_heads, head_dim,
                                  max_context_len)
                 : chunk_workspace(num_seqs, max_q_len, num_q_heads, num_kv_heads, head_dim,
@@ -441,8 +437,7 @@ int prefill_call(void* out, int out_dtype, const void* q, const int32_t* cu_q_le
     const bool any_decode_rows = !uniform_chunks;
     const bool decode_limits_ok = num_seqs <= kMaxDecodeSeqs &&
                                   (num_kv_heads <= 8 || num_kv_heads == kMaxDecodeKvHeads);
-    const bool rows = rows_path(num_seqs, max_q_len, num_q_heads, num_kv_heads, kv_fp8,
-                                block_scales);
+    const bool rows = rows_path(num_seqs, max_q_len, num_q_heads, num_kv_heads, kv_fp8);
     const bool streamk = !rows && pkv::prefill_streamk(max_q_len, num_q_heads / num_kv_heads);
     if (any_decode_rows && !decode_limits_ok) return PKV_ERR_UNSUPPORTED;
     // the stream-K chunk kernel keeps the sequences' unit prefix sums in LDS

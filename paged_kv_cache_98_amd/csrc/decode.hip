@@ -170,7 +170,7 @@ hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s) {
 template <typename KV, int BS, int G>
 hipError_t launch_rows_g(const DecodeArgs& a, hipStream_t s) {
     if (a.rows * G <= 16) return launch_decode_g<KV, BS, G, 1>(a, s);
-    if constexpr (G >= 2 && KV::kElemBytes == 1 && !KV::kBlockScales) {
+    if constexpr (G >= 2 && KV::kElemBytes == 1) {
         if (a.rows * G <= 32) return launch_decode_g<KV, BS, G, 2>(a, s);
     }
     if constexpr (G >= 2 && KV::kElemBytes == 2) {
@@ -218,9 +218,9 @@ hipError_t launch_decode_bf16_bs(const DecodeArgs& a, hipStream_t s) {
 // batch (8 heads) 303 -> 171 us, 8B-shaped batch (4 heads) 74.6 -> 59.7 us.
 // With 1 or 2 heads the columns are mostly padding and the gain was 2-3 %,
 // so those keep the VALU tile (16 dims per lane).
-// FP8 pools with per-(block, KV head) scales.  The rows path takes one
-// block of 16 columns per wave only (the two-block tile would spill with
-// the scales' registers); the host routes wider chunks to the chunk kernel.
+// FP8 pools with per-(block, KV head) scales, the rows path included (its
+// two-block tile spills 32-76 bytes with the scales' registers and still
+// beats the stream-K chunk kernel: 6-row verify 77.9 against 99.8 us).
 template <int BS>
 hipError_t launch_decode_fp8_bh_bs(const DecodeArgs& a, hipStream_t s) {
     if (a.rows > 1) return launch_rows_bs<KvFp8MfmaBh, BS>(a, s);

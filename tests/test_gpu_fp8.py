@@ -515,12 +515,13 @@ def test_prefill_fp8_per_block_chunks(bs, group):
                what=f"{w.name} causal={causal}")
 
 
-@pytest.mark.parametrize("group,rows", [(4, 4), (1, 16), (4, 6), (16, 2), (8, 16), (2, 12)])
+@pytest.mark.parametrize("group,rows", [(4, 4), (1, 16), (4, 6), (16, 2), (8, 16), (4, 12)])
 def test_prefill_fp8_per_block_short_chunks(group, rows):
-    """Short chunks over per-(block, head)-scaled FP8 pools: up to 16 (row,
+    """Short chunks over per-(block, head)-scaled FP8 pools: up to 32 (row,
     head) columns per KV head on the decode kernel's matrix-core tile (the
-    rows path), wider ones on the stream-K chunk kernel with its merge;
-    bf16 output equals the fp32 output rounded; determinism."""
+    rows path; two blocks of 16 from 17 on), wider ones on the stream-K
+    chunk kernel with its merge; bf16 output equals the fp32 output
+    rounded; determinism."""
     cases = [(3000, rows), (2500, 1), (40, min(3, rows)), (4100, rows), (700, max(rows - 1, 1)),
              (129, 2), (17, rows)]
     w = W.make_workload(f"fp8pb_short_g{group}_r{rows}", [c for c, _ in cases],
@@ -541,11 +542,11 @@ def test_prefill_fp8_per_block_short_chunks(group, rows):
     bf16_parity(o16, o32, ref, what=w.name + " bf16 out", fp32_err=1e-3, min_within=0.95)
 
 
-@pytest.mark.parametrize("group,nodes", [(1, 16), (4, 16), (2, 6)])
+@pytest.mark.parametrize("group,nodes", [(1, 16), (4, 16), (2, 6), (2, 16)])
 def test_tree_fp8_per_block(group, nodes):
     """Token trees over per-(block, head)-scaled FP8 pools, against the tree
     oracle on the values: with power-of-two scales every code's value is a
-    bf16 value, so the oracle takes them as bf16 pools.  16 columns per KV
+    bf16 value, so the oracle takes them as bf16 pools.  32 columns per KV
     head or fewer take the rows path, more the stream-K chunk kernel."""
     from oracle import tree
     hkv = 2
