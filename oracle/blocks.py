@@ -56,6 +56,33 @@ matchable until they are reused.  Readings:
     replaces an older one;
   * a hit on a free block takes it out of the free list; the all-or-nothing
     check counts those blocks as no longer free.
+
+Radix-tree prefix sharing ("LLM 推理优化技术全景", section "Prefix Caching 与
+RadixAttention"; "让 Agent 跑得快", section 七, RadixAttention): cached
+prefixes are matched at token granularity, the longest common prefix with
+any cached one, and the matched part's KV is reused; cached prefixes hold
+references that keep their KV alive, and when memory runs short the least
+recently used ones are dropped.  Readings on a pool of block_size-token
+blocks (SGLang's pages hold one token, so there every match is whole pages):
+  * an entry is a prompt's tokens up to its last full block, with those
+    blocks, registered when the prompt is allocated; it holds one reference
+    on each of its blocks.  The partly filled last block stays out: the
+    sequence keeps writing into it;
+  * a lookup finds L, the longest common prefix of the prompt with any
+    entry's tokens; among entries reaching L the most recently used (a
+    registration or a hit refreshes an entry) is the donor;
+  * the new sequence shares the donor's first L // block_size blocks; when
+    L falls inside a block, it gets a fresh block and a copy (the donor's
+    block -> the fresh one) to perform before prefill, which starts at
+    token L (the copy brings tokens up to L; the caller overwrites the
+    rest);
+  * the new entry is not registered when its tokens are a prefix of the
+    donor's (it would name the donor's blocks again);
+  * when fewer blocks are free than the allocation takes, entries are
+    dropped in least-recently-used order, never the donor, each releasing
+    its references, until enough blocks are free; if even dropping every
+    other entry would not free enough, nothing changes (MemoryError);
+  * entries and the hash-chain cache above are independent.
 """
 from collections import deque
 
@@ -72,6 +99,8 @@ class BlockPool:
         self.lengths = {}  # seq_id -> tokens held
         self.cache = {}    # block identity -> physical block
         self.key_of = [None] * num_blocks
+        self.radix = []    # radix entries: {"tokens", "blocks", "stamp"}
+        self.clock = 0     # last-use stamps of radix entries
 
     def num_free(self) -> int:
         return len(self.free_list)
@@ -141,6 +170,78 @@ class BlockPool:
         self.lengths[seq_id] = n
         return list(blocks), len(hits) * bs
 
+    def allocate_radix(self, seq_id, tokens):
+        """A new sequence holding `tokens`, reusing the longest cached prefix.
+
+        Returns (blocks, cached_tokens, copies): the block table, the number
+        of leading tokens whose K/V the shared and copied blocks hold
+        (prefill starts there), and the (source, destination) block copies
+        to perform first (at most one).
+        """
+        if seq_id in self.tables:
+            raise KeyError(f"sequence {seq_id} exists")
+        tokens = [int(t) for t in tokens]
+        bs, n = self.block_size, len(tokens)
+
+        def lcp(a, b):
+            k = 0
+            while k < len(a) and k < len(b) and a[k] == b[k]:
+                k += 1
+            return k
+
+        donor, length = None, 0
+        for e in self.radix:
+            k = lcp(e["tokens"], tokens)
+            if k > 0 and (k > length or (k == length and e["stamp"] > donor["stamp"])):
+                donor, length = e, k
+        shared = donor["blocks"][:length // bs] if donor else []
+        partial = donor is not None and length % bs != 0
+        fresh = -(-n // bs) - len(shared)
+        # what dropping entries in LRU order (never the donor) would free,
+        # the new sequence's references on the shared blocks counted first
+        count = list(self.refcount)
+        for b in shared:
+            count[b] += 1
+        free, drop = len(self.free_list), []
+        for e in sorted((e for e in self.radix if e is not donor), key=lambda e: e["stamp"]):
+            if free >= fresh:
+                break
+            drop.append(e)
+            for b in e["blocks"]:
+                count[b] -= 1
+                free += count[b] == 0
+        if free < fresh:
+            raise MemoryError("not enough free KV blocks")
+        for b in shared:
+            self.refcount[b] += 1
+        for e in drop:
+            self.radix.remove(e)
+            for b in e["blocks"]:
+                self._release(b)
+        blocks = list(shared) + [self._take() for _ in range(fresh)]
+        copies = [(donor["blocks"][length // bs], blocks[length // bs])] if partial else []
+        if donor is not None:
+            self.clock += 1
+            donor["stamp"] = self.clock
+        full = (n // bs) * bs
+        if full > 0 and not (donor is not None and length >= full and
+                             donor["tokens"][:full] == tokens[:full]):
+            for b in blocks[:n // bs]:
+                self.refcount[b] += 1
+            self.clock += 1
+            self.radix.append({"tokens": tokens[:full], "blocks": blocks[:n // bs],
+                               "stamp": self.clock})
+        self.tables[seq_id] = blocks
+        self.lengths[seq_id] = n
+        return list(blocks), length, copies
+
+    def radix_clear(self) -> None:
+        """Drop every radix entry, releasing its references."""
+        for e in self.radix:
+            for b in e["blocks"]:
+                self._release(b)
+        self.radix = []
+
     def free(self, seq_id: int) -> None:
         """Drop a sequence; blocks nobody else references go back to the pool.
         An unknown id is ignored."""
@@ -206,10 +307,14 @@ class BlockPool:
 
     def check(self) -> None:
         """Pool invariants: every block is free exactly once with count 0, or
-        referenced by exactly refcount sequence tables."""
+        referenced by exactly refcount sequence tables and radix entries."""
         seen = [0] * self.num_blocks
         for blocks in self.tables.values():
             for b in blocks:
+                seen[b] += 1
+        for e in self.radix:  # radix entries hold references too
+            assert len(e["tokens"]) == len(e["blocks"]) * self.block_size
+            for b in e["blocks"]:
                 seen[b] += 1
         free = set(self.free_list)
         assert len(free) == len(self.free_list), "a block is free twice"

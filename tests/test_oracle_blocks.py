@@ -297,3 +297,184 @@ def test_pin_prefix_cache_free_hits_count_against_room():
     blocks, cached = pool.allocate_cached("b", list(range(32)) + list(range(100, 132)))
     assert cached == 32 and blocks[:2] == [0, 1]
     pool.check()
+
+
+# ---------------------------------------------------- radix-tree prefix sharing
+
+class KvModel:
+    """What the blocks of a pool hold, as token ids per slot (None: never
+    written): prefill writes a prompt's tokens, a copy duplicates a block.
+    Independent of how the pool decides what to share."""
+
+    def __init__(self, pool):
+        self.pool = pool
+        self.slots = {}
+
+    def copy(self, src, dst):
+        bs = self.pool.block_size
+        for o in range(bs):
+            self.slots[dst * bs + o] = self.slots.get(src * bs + o)
+
+    def prefill(self, blocks, tokens, start):
+        bs = self.pool.block_size
+        for p in range(start, len(tokens)):
+            self.slots[blocks[p // bs] * bs + p % bs] = tokens[p]
+
+    def holds(self, blocks, tokens, upto):
+        bs = self.pool.block_size
+        return all(self.slots.get(blocks[p // bs] * bs + p % bs) == tokens[p] for p in range(upto))
+
+
+def radix_alloc(pool, kv, sid, tokens):
+    """allocate_radix, then what the caller does: the copies, the prefill
+    from the cached length; checks that the reused blocks held the prefix."""
+    blocks, cached, copies = pool.allocate_radix(sid, tokens)
+    assert len(copies) <= 1 and len(blocks) == -(-len(tokens) // pool.block_size)
+    for src, dst in copies:
+        kv.copy(src, dst)
+    assert kv.holds(blocks, tokens, cached), (sid, cached)
+    kv.prefill(blocks, tokens, cached)
+    assert kv.holds(blocks, tokens, len(tokens))
+    pool.check()
+    return blocks, cached, copies
+
+
+def test_pin_radix_shares_the_pages_1000_token_prefix():
+    """Two requests whose first 1000 tokens agree and then differ ("让 Agent
+    跑得快", section 七: the radix tree shares those 1000 tokens where a
+    whole-prompt key would miss): with 16-token blocks the second request
+    shares 62 full blocks and copies the 63rd (8 tokens of it are the
+    prefix), and prefill starts at token 1000; block-level prefix caching
+    stops at the last whole block, 992 tokens."""
+    common = list(range(1000))
+    a, b = common + [5000 + i for i in range(200)], common + [7000 + i for i in range(150)]
+    pool = BlockPool(400, 16)
+    kv = KvModel(pool)
+    blocks_a, cached_a, _ = radix_alloc(pool, kv, "a", a)
+    assert cached_a == 0
+    blocks_b, cached_b, copies = radix_alloc(pool, kv, "b", b)
+    assert cached_b == 1000
+    assert blocks_b[:62] == blocks_a[:62] and blocks_b[62] != blocks_a[62]
+    assert copies == [(blocks_a[62], blocks_b[62])]
+    hc = BlockPool(400, 16)
+    hc.allocate_cached("a", a)
+    assert hc.allocate_cached("b", b)[1] == 992
+
+
+def test_pin_radix_equals_block_caching_on_block_aligned_prefixes():
+    """A shared system prompt that fills whole blocks: both schemes reuse the
+    same blocks and start prefill at the same token ("LLM 推理优化技术全景",
+    vLLM APC against SGLang RadixAttention: alike when the prompt divides
+    into whole blocks)."""
+    sys_prompt = list(range(50, 50 + 800))  # 50 blocks of 16
+    rng = random.Random(3)
+    radix, hc = BlockPool(2000, 16), BlockPool(2000, 16)
+    kv = KvModel(radix)
+    for i in range(6):
+        p = sys_prompt + [rng.randrange(10_000, 20_000) for _ in range(rng.randrange(1, 300))]
+        blocks_r, cached_r, copies = radix_alloc(radix, kv, i, p)
+        blocks_h, cached_h = hc.allocate_cached(i, p)
+        assert cached_r == cached_h == (0 if i == 0 else 800)
+        assert copies == []
+
+
+def test_pin_radix_longest_prefix_and_most_recent_donor():
+    """The longest match wins whichever entry holds it; among entries that
+    reach the same length, the most recently used one donates."""
+    pool = BlockPool(100, 4)
+    kv = KvModel(pool)
+    radix_alloc(pool, kv, 1, [1, 2, 3, 4, 5, 6, 7, 8, 9, 10])          # entry: 8 tokens
+    radix_alloc(pool, kv, 2, [1, 2, 3, 4, 5, 6, 70, 80, 90, 100, 11])  # shares 6, copies one
+    # entries stop at the last full block: 2's holds 8 tokens, so 90 is not matched
+    _, cached, copies = radix_alloc(pool, kv, 3, [1, 2, 3, 4, 5, 6, 70, 80, 90, 1])
+    assert cached == 8 and copies == [] and pool.tables[3][:2] == pool.tables[2][:2]
+    # 1, 2, 3 appears in all three; the last registered or hit (3) donates
+    _, cached, copies = radix_alloc(pool, kv, 4, [1, 2, 3, 9, 9])
+    assert cached == 3 and copies == [(pool.tables[3][0], pool.tables[4][0])]
+    # a prompt that is a prefix of an entry registers nothing new
+    entries = len(pool.radix)
+    _, cached, copies = radix_alloc(pool, kv, 5, [1, 2, 3, 4, 5, 6, 7, 8])
+    assert cached == 8 and copies == [] and len(pool.radix) == entries
+    assert pool.tables[5] == pool.tables[1][:2]
+
+
+def test_pin_radix_lru_eviction_and_all_or_nothing():
+    """Entries keep their blocks after the sequences go; when blocks run
+    short the least recently used entries go first (a hit refreshes one),
+    and a call that cannot be met even by dropping every entry other than
+    its donor changes nothing."""
+    pool = BlockPool(6, 4)
+    kv = KvModel(pool)
+    a, b = [1] * 8, [2] * 8
+    radix_alloc(pool, kv, "a", a)
+    radix_alloc(pool, kv, "b", b)
+    pool.free("a")
+    pool.free("b")
+    assert pool.num_free() == 2 and len(pool.radix) == 2
+    _, cached, _ = radix_alloc(pool, kv, "a2", a)       # hit: a's entry refreshed
+    assert cached == 8 and pool.num_free() == 2
+    pool.free("a2")
+    _, cached, _ = radix_alloc(pool, kv, "c", [3] * 12)  # 3 blocks: b's entry goes
+    assert cached == 0 and [e["tokens"] for e in pool.radix] == [a, [3] * 12]
+    import copy
+    snap = copy.deepcopy((pool.free_list, pool.refcount, pool.radix, pool.tables))
+    with pytest.raises(MemoryError):
+        pool.allocate_radix("d", [1] * 8 + [4] * 20)  # shares 2, needs 5 more: 4 at most
+    assert snap == (pool.free_list, pool.refcount, pool.radix, pool.tables)
+    pool.radix_clear()
+    pool.check()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_pin_radix_random_workload_reuses_only_true_prefixes(seed):
+    """Random prompts over a few shared stems, appends, forks and frees on a
+    tight pool: every reuse hands over exactly the prompt's prefix (the
+    KV model), every reference is accounted for, and the reported prefix is
+    the longest any live entry offers."""
+    rng = random.Random(seed)
+    bs = rng.choice([4, 8, 16])
+    pool = BlockPool(rng.randrange(30, 90), bs)
+    kv = KvModel(pool)
+    stems = [[rng.randrange(100) for _ in range(rng.randrange(0, 5 * bs))] for _ in range(4)]
+    live, next_id = [], 0
+    for _ in range(160):
+        op = rng.random()
+        if op < 0.55:
+            p = rng.choice(stems)[: rng.randrange(0, 5 * bs + 1)]
+            p = p + [rng.randrange(100, 200) for _ in range(rng.randrange(1, 3 * bs))]
+            best = max((sum(1 for _ in iter_common(e["tokens"], p)) for e in pool.radix), default=0)
+            try:
+                _, cached, _ = radix_alloc(pool, kv, next_id, p)
+            except MemoryError:
+                pool.check()
+                continue
+            assert cached == best
+            live.append(next_id)
+            next_id += 1
+        elif op < 0.75 and live:
+            pool.free(live.pop(rng.randrange(len(live))))
+            pool.check()
+        elif op < 0.9 and live:
+            s = rng.choice(live)
+            try:
+                slots, copies = pool.append(s, rng.randrange(1, 2 * bs))
+            except MemoryError:
+                continue
+            for src, dst in copies:
+                kv.copy(src, dst)
+            pool.check()
+        elif live:
+            try:
+                pool.fork(rng.choice(live), next_id)
+            except MemoryError:
+                continue
+            live.append(next_id)
+            next_id += 1
+            pool.check()
+
+
+def iter_common(a, b):
+    for x, y in zip(a, b):
+        if x != y:
+            return
+        yield x
