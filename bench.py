@@ -261,6 +261,20 @@ def bench_copy_blocks(args):
     prompt_tokens = sum(p.numel() for p in prompts)
     print(f"[bench] prefix cache: {pc_us:.1f} us per prompt (64 prompts), "
           f"{sum(cached)} of {prompt_tokens} prompt tokens cached", file=sys.stderr, flush=True)
+    # radix-tree sharing: the same tails after a 1000-token shared prefix,
+    # which does not end on a block edge (62 blocks + 8 tokens)
+    system2 = torch.randint(0, 32000, (1000,), generator=gp, dtype=torch.int32)
+    prompts2 = [torch.cat([system2, p[800:]]) for p in prompts]
+    with pkv.BlockManager(16384, bs) as bm:
+        t1 = time.perf_counter()
+        radix = [bm.allocate_radix(i, p) for i, p in enumerate(prompts2)]
+        rx_us = (time.perf_counter() - t1) * 1e6 / len(prompts2)
+    with pkv.BlockManager(16384, bs) as bm:
+        chain2 = [bm.allocate_cached(i, p) for i, p in enumerate(prompts2)]
+    rx_tokens = sum(p.numel() for p in prompts2)
+    print(f"[bench] radix prefix sharing: {rx_us:.1f} us per prompt (64 prompts), "
+          f"{sum(r[0] for r in radix)} of {rx_tokens} prompt tokens cached "
+          f"({sum(chain2)} by whole blocks)", file=sys.stderr, flush=True)
     print(f"[bench] copy_blocks {call_ms * 1e3:.1f} us per call of {npairs} pairs: "
           f"{achieved:.0f} GB/s | host manager {statistics.median(host_us):.0f} us per "
           f"256-beam step", file=sys.stderr, flush=True)
@@ -276,6 +290,11 @@ def bench_copy_blocks(args):
         "host_block_manager_us_per_256_beam_step": round(statistics.median(host_us), 1),
         "host_prefix_cache": {"us_per_prompt": round(pc_us, 1), "prompts": len(prompts),
                               "prompt_tokens": prompt_tokens, "cached_tokens": sum(cached)},
+        "host_radix_prefix": {"us_per_prompt": round(rx_us, 1), "prompts": len(prompts2),
+                              "prompt_tokens": rx_tokens,
+                              "cached_tokens": sum(r[0] for r in radix),
+                              "block_cache_cached_tokens": sum(chain2),
+                              "copies": sum(r[1] is not None for r in radix)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": hbm_traffic(COPY_WORKLOAD),

@@ -445,6 +445,40 @@ int pkv_bm_allocate_cached(pkv_block_manager *bm, int64_t seq_id, const int32_t 
 /* Registered (matchable) blocks, or -1 for a NULL manager. */
 int64_t pkv_bm_num_cached(const pkv_block_manager *bm);
 
+/*
+ * Radix-tree prefix sharing ("LLM 推理优化技术全景", section "Prefix Caching 与
+ * RadixAttention"; "让 Agent 跑得快", section 七, RadixAttention): a new
+ * sequence seq_id holding tokens[0 .. num_tokens) reuses the longest prefix
+ * it shares, token by token, with any cached prompt.  Cached prompts are the
+ * entries of a compressed trie over tokens: each allocation registers its
+ * prompt's tokens up to its last full block, with those blocks, and the
+ * entry holds one reference on each (so their K/V outlives the sequence;
+ * the partly filled last block is not registered).  With L the longest
+ * common prefix and the donor the most recently used entry reaching it:
+ * the new table shares the donor's first L / block_size blocks, and when L
+ * is not a multiple of block_size the next block is a fresh one that the
+ * caller fills by copying the donor's (copy_pair, with pkv_copy_blocks)
+ * before prefilling tokens L .. num_tokens - 1.  A hit or a registration
+ * makes an entry the most recently used.  When fewer blocks are free than
+ * the call takes, entries are dropped least recently used first (never the
+ * donor), releasing their references.  Independent of
+ * pkv_bm_allocate_cached's chain cache.
+ *   num_cached_tokens  (written) L: prefill starts there
+ *   copy_pair          (written) [2] int64: (source, destination) block of
+ *                      the copy, or (-1, -1)
+ * PKV_ERR_STATE if seq_id exists; PKV_ERR_NO_MEMORY if the blocks do not fit
+ * even with every entry but the donor dropped; nothing changes on failure.
+ */
+int pkv_bm_allocate_radix(pkv_block_manager *bm, int64_t seq_id, const int32_t *tokens,
+                          int64_t num_tokens, int64_t *num_cached_tokens, int64_t *copy_pair);
+
+/* Radix entries held, or -1 for a NULL manager. */
+int64_t pkv_bm_radix_num_entries(const pkv_block_manager *bm);
+
+/* Drop every radix entry, least recently used first, releasing its
+ * references (blocks that reach zero join the free list in that order). */
+int pkv_bm_radix_clear(pkv_block_manager *bm);
+
 /* Drop seq_id; each of its blocks loses one reference and returns to the free
  * list at zero.  An unknown seq_id is ignored (PKV_OK). */
 int pkv_bm_free(pkv_block_manager *bm, int64_t seq_id);

@@ -236,8 +236,9 @@ class BlockPool:
         return list(blocks), length, copies
 
     def radix_clear(self) -> None:
-        """Drop every radix entry, releasing its references."""
-        for e in self.radix:
+        """Drop every radix entry, least recently used first, releasing its
+        references."""
+        for e in sorted(self.radix, key=lambda e: e["stamp"]):
             for b in e["blocks"]:
                 self._release(b)
         self.radix = []

@@ -42,7 +42,8 @@ EXPORTED = ("pkv_status_string", "pkv_version", "pkv_kv_append", "pkv_decode_wor
             "pkv_bm_refcount", "pkv_bm_block_table", "pkv_paged_decode_attn_noalloc",
             "pkv_decode_noalloc_max_bytes", "pkv_kv_append_fp8_per_block",
             "pkv_paged_decode_attn_fp8_per_block", "pkv_paged_prefill_attn_fp8_per_block",
-            "pkv_paged_prefill_attn_tree_fp8_per_block")
+            "pkv_paged_prefill_attn_tree_fp8_per_block", "pkv_bm_allocate_radix",
+            "pkv_bm_radix_num_entries", "pkv_bm_radix_clear")
 
 _lib = None
 
@@ -155,6 +156,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_bm_allocate_cached.argtypes = [_vp, _i64, _vp, _i64, _i64, _vp]
     lib.pkv_bm_num_cached.restype = _i64
     lib.pkv_bm_num_cached.argtypes = [_vp]
+    lib.pkv_bm_allocate_radix.restype = _i32
+    lib.pkv_bm_allocate_radix.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp]
+    lib.pkv_bm_radix_num_entries.restype = _i64
+    lib.pkv_bm_radix_num_entries.argtypes = [_vp]
+    lib.pkv_bm_radix_clear.restype = _i32
+    lib.pkv_bm_radix_clear.argtypes = [_vp]
     lib.pkv_bm_free.restype = _i32
     lib.pkv_bm_free.argtypes = [_vp, _i64]
     lib.pkv_bm_fork.restype = _i32
@@ -628,6 +635,28 @@ class BlockManager:
 
     def num_cached(self) -> int:
         return self._lib.pkv_bm_num_cached(self._handle())
+
+    def allocate_radix(self, seq_id: int, tokens):
+        """A new sequence holding the prompt `tokens`, reusing the longest
+        cached prefix (radix tree, token granularity).  Returns
+        (cached_tokens, copy): prefill starts at cached_tokens, after the
+        block copy (source, destination), or None, is performed."""
+        t = tokens if isinstance(tokens, torch.Tensor) else torch.tensor(list(tokens), dtype=torch.int32)
+        if t.is_cuda:
+            raise TypeError("block-manager arguments live on the host")
+        t = t.to(torch.int32).contiguous()
+        n = ctypes.c_int64(0)
+        pair = (ctypes.c_int64 * 2)()
+        _check(self._lib.pkv_bm_allocate_radix(self._handle(), seq_id,
+                                               t.data_ptr() if t.numel() else None, t.numel(),
+                                               ctypes.byref(n), pair))
+        return n.value, (None if pair[0] < 0 else (pair[0], pair[1]))
+
+    def radix_num_entries(self) -> int:
+        return self._lib.pkv_bm_radix_num_entries(self._handle())
+
+    def radix_clear(self) -> None:
+        _check(self._lib.pkv_bm_radix_clear(self._handle()))
 
     def free(self, seq_id: int) -> None:
         _check(self._lib.pkv_bm_free(self._handle(), seq_id))

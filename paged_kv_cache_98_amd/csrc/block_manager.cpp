@@ -33,6 +33,22 @@
 // a fixed capacity (the table is sized at the first cached allocation), so
 // giving blocks back and undoing a failed batch never allocate.  A call
 // that would run out of blocks part-way changes nothing.
+//
+// Radix-tree prefix sharing ("LLM 推理优化技术全景", section "Prefix Caching 与
+// RadixAttention"; "让 Agent 跑得快", section 七): cached prompts live in a
+// compressed trie over their tokens (each edge a run of tokens, children
+// told apart by their first token), so the longest prefix a new prompt
+// shares with any of them is one walk down the trie, token by token.  An
+// entry is a prompt's tokens up to its last full block with those blocks,
+// on each of which it holds a reference; the partly filled last block
+// stays out, since the sequence keeps writing into it.  A new prompt
+// shares the donor's blocks that the match covers whole, and when the
+// match ends inside a block it gets a fresh block plus a copy of the
+// donor's (prefill then starts at the match's end).  The donor is the most
+// recently used entry below the match point.  When blocks run short,
+// entries are dropped least recently used first (never the donor), each
+// releasing its references; a call that cannot be met that way changes
+// nothing.
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
@@ -83,6 +99,28 @@ struct pkv_block_manager {
     std::vector<uint64_t> slot_hash;  // open addressing, linear probing
     std::vector<int64_t> slot_block;  // -1: empty
     int64_t cached = 0;
+
+    // radix tree: node 0 is the root (empty label); dead nodes and entries
+    // are recycled through their free lists
+    struct RNode {
+        std::vector<int32_t> label;  // tokens on the edge from the parent
+        int parent = -1;
+        std::vector<int> kids;       // children, first tokens all different
+        std::vector<int> entries;    // entries whose tokens end here
+    };
+    struct REntry {
+        std::vector<int64_t> blocks;  // one per block_size tokens
+        int64_t stamp = 0;            // last registration or hit
+        int node = -1;                // where its tokens end; -1: dead
+    };
+    std::vector<RNode> rnodes;
+    std::vector<int> rnode_free;
+    std::vector<REntry> rentries;
+    std::vector<int> rentry_free;
+    int64_t rclock = 0, rlive = 0;
+    std::vector<int> rscratch;                        // trie walks
+    std::vector<std::pair<int64_t, int>> rorder;      // eviction order
+    std::unordered_map<int64_t, int32_t> rdrop;       // simulated releases
 
     int64_t blocks_for(int64_t tokens) const { return (tokens + block_size - 1) / block_size; }
 
@@ -236,6 +274,144 @@ struct pkv_block_manager {
         return PKV_OK;
     }
 
+    // ---- radix tree
+    int kid_with(int node, int32_t tok) const {
+        for (int c : rnodes[(size_t)node].kids)
+            if (rnodes[(size_t)c].label[0] == tok) return c;
+        return -1;
+    }
+    // Longest prefix of tokens[0, n) in the trie: its length, and the node
+    // below which every entry reaches it (the child whose edge it stops in,
+    // or the node it ends at).
+    int64_t radix_match(const int32_t* tokens, int64_t n, int* below) const {
+        int node = 0;
+        int64_t d = 0;
+        while (d < n) {
+            const int c = kid_with(node, tokens[d]);
+            if (c < 0) break;
+            const std::vector<int32_t>& lab = rnodes[(size_t)c].label;
+            size_t m = 0;
+            while (m < lab.size() && d + (int64_t)m < n && lab[m] == tokens[d + (int64_t)m]) ++m;
+            d += (int64_t)m;
+            node = c;
+            if (m < lab.size()) break;
+        }
+        *below = node;
+        return d;
+    }
+    // The most recently used live entry in the subtree of `node`.
+    int radix_newest(int node) {
+        int best = -1;
+        rscratch.clear();
+        rscratch.push_back(node);
+        while (!rscratch.empty()) {
+            const int x = rscratch.back();
+            rscratch.pop_back();
+            for (int e : rnodes[(size_t)x].entries)
+                if (best < 0 || rentries[(size_t)e].stamp > rentries[(size_t)best].stamp) best = e;
+            for (int c : rnodes[(size_t)x].kids) rscratch.push_back(c);
+        }
+        return best;
+    }
+    // Adding an entry for tokens[0, n) creates at most two nodes: the
+    // middle of an edge the tokens leave part-way (split after m tokens) and
+    // a leaf for the rest.  prepare() does everything that allocates, into
+    // this plan; commit() then changes the trie without allocating.
+    struct InsertPlan {
+        int at = 0;          // node the walk stopped at
+        int split = -1;      // child whose edge is split, or -1
+        size_t m = 0;        // tokens of that edge kept in the middle node
+        bool leaf = false;   // a leaf for tokens[d, n) hangs below
+        RNode mid, lf;
+    };
+    void radix_prepare(const int32_t* tokens, int64_t n, InsertPlan& pl) {
+        int node = 0;
+        int64_t d = 0;
+        while (d < n) {
+            const int c = kid_with(node, tokens[d]);
+            if (c < 0) break;
+            const std::vector<int32_t>& lab = rnodes[(size_t)c].label;
+            size_t m = 0;
+            while (m < lab.size() && d + (int64_t)m < n && lab[m] == tokens[d + (int64_t)m]) ++m;
+            if (m < lab.size()) {
+                pl.split = c;
+                pl.m = m;
+                pl.mid.label.assign(lab.begin(), lab.begin() + (long)m);
+                pl.mid.kids.reserve(2);
+                pl.mid.entries.reserve(1);
+                d += (int64_t)m;
+                break;
+            }
+            node = c;
+            d += (int64_t)m;
+        }
+        pl.at = node;
+        if (d < n) {
+            pl.leaf = true;
+            pl.lf.label.assign(tokens + d, tokens + n);
+            pl.lf.entries.reserve(1);
+            if (pl.split < 0) rnodes[(size_t)node].kids.reserve(rnodes[(size_t)node].kids.size() + 1);
+        } else if (pl.split < 0) {
+            rnodes[(size_t)node].entries.reserve(rnodes[(size_t)node].entries.size() + 1);
+        }
+        rnodes.reserve(rnodes.size() + 2);
+        rnode_free.reserve(rnodes.capacity());
+    }
+    int place_rnode(RNode&& x) {  // capacity reserved: no allocation
+        if (!rnode_free.empty()) {
+            const int i = rnode_free.back();
+            rnode_free.pop_back();
+            rnodes[(size_t)i] = std::move(x);
+            return i;
+        }
+        rnodes.push_back(std::move(x));
+        return (int)rnodes.size() - 1;
+    }
+    void radix_commit(InsertPlan& pl, int e) {
+        int node = pl.at;
+        if (pl.split >= 0) {
+            const int c = pl.split;
+            pl.mid.parent = node;
+            pl.mid.kids.push_back(c);
+            const int mid = place_rnode(std::move(pl.mid));
+            RNode& cn = rnodes[(size_t)c];
+            cn.label.erase(cn.label.begin(), cn.label.begin() + (long)pl.m);
+            cn.parent = mid;
+            for (int& k : rnodes[(size_t)node].kids)
+                if (k == c) k = mid;
+            node = mid;
+        }
+        if (pl.leaf) {
+            pl.lf.parent = node;
+            const int leaf = place_rnode(std::move(pl.lf));
+            rnodes[(size_t)node].kids.push_back(leaf);
+            node = leaf;
+        }
+        rnodes[(size_t)node].entries.push_back(e);
+        rentries[(size_t)e].node = node;
+    }
+    // Drops entry e: its references go back, and nodes left with neither
+    // entries nor children leave the trie.
+    void radix_remove(int e) {
+        REntry& en = rentries[(size_t)e];
+        int node = en.node;
+        std::vector<int>& es = rnodes[(size_t)node].entries;
+        es.erase(std::find(es.begin(), es.end(), e));
+        while (node != 0 && rnodes[(size_t)node].entries.empty() && rnodes[(size_t)node].kids.empty()) {
+            const int p = rnodes[(size_t)node].parent;
+            std::vector<int>& ks = rnodes[(size_t)p].kids;
+            ks.erase(std::find(ks.begin(), ks.end(), node));
+            rnodes[(size_t)node].label.clear();
+            rnode_free.push_back(node);
+            node = p;
+        }
+        for (int64_t b : en.blocks) release(b);
+        en.blocks.clear();
+        en.node = -1;
+        rentry_free.push_back(e);
+        --rlive;
+    }
+
     void rollback(const Undo& u) {
         Seq& s = *u.seq;
         while (s.blocks.size() > u.old_blocks) {
@@ -270,6 +446,7 @@ pkv_block_manager* pkv_bm_create(int64_t num_blocks, int block_size) {
         bm->key_parent.assign(n, 0);
         bm->key_salt.assign(n, 0);
         for (int64_t b = 0; b < num_blocks; ++b) bm->link_back(b);
+        bm->rnodes.emplace_back();  // the radix tree's root
     } catch (...) {
         delete bm;
         return nullptr;
@@ -365,6 +542,118 @@ int pkv_bm_allocate_cached(pkv_block_manager* bm, int64_t seq_id, const int32_t*
 }
 
 int64_t pkv_bm_num_cached(const pkv_block_manager* bm) { return bm == nullptr ? -1 : bm->cached; }
+
+int pkv_bm_allocate_radix(pkv_block_manager* bm, int64_t seq_id, const int32_t* tokens,
+                          int64_t num_tokens, int64_t* num_cached_tokens, int64_t* copy_pair) {
+    if (bm == nullptr || num_cached_tokens == nullptr || copy_pair == nullptr ||
+        (num_tokens > 0 && tokens == nullptr))
+        return PKV_ERR_NULL;
+    if (num_tokens < 0) return PKV_ERR_SHAPE;
+    if (bm->seqs.count(seq_id)) return PKV_ERR_STATE;
+    const int bs = bm->block_size;
+    const int64_t n = num_tokens;
+    const int64_t nblk = bm->blocks_for(n);
+    const int64_t nfull = n / bs;
+    int64_t L = 0, shared = 0, fresh = nblk;
+    int donor = -1, e = -1;
+    bool reg = false;
+    size_t ndrop = 0;
+    pkv_block_manager::Seq s;
+    pkv_block_manager::InsertPlan plan;
+    try {
+        // the longest cached prefix and its donor
+        int below = 0;
+        L = bm->radix_match(tokens, n, &below);
+        donor = L > 0 ? bm->radix_newest(below) : -1;
+        if (donor < 0) L = 0;
+        shared = L / bs;
+        fresh = nblk - shared;
+        reg = nfull > 0 && L < nfull * bs;  // else a prefix of the donor's tokens
+        // what dropping entries least recently used first (never the donor)
+        // would give back; nothing changes until the whole call is known to fit
+        int64_t free = bm->num_free;
+        if (free < fresh) {
+            bm->rorder.clear();
+            for (size_t k = 0; k < bm->rentries.size(); ++k)
+                if (bm->rentries[k].node >= 0 && (int)k != donor)
+                    bm->rorder.emplace_back(bm->rentries[k].stamp, (int)k);
+            std::sort(bm->rorder.begin(), bm->rorder.end());
+            bm->rdrop.clear();
+            while (free < fresh && ndrop < bm->rorder.size()) {
+                for (int64_t b : bm->rentries[(size_t)bm->rorder[ndrop].second].blocks)
+                    if (bm->refcount[(size_t)b] - ++bm->rdrop[b] == 0) ++free;
+                ++ndrop;
+            }
+            if (free < fresh) return PKV_ERR_NO_MEMORY;
+        }
+        // everything the call adds, allocated before anything changes
+        s.blocks.reserve((size_t)nblk);
+        if (reg) {
+            bm->radix_prepare(tokens, nfull * bs, plan);
+            if (bm->rentry_free.empty()) {
+                bm->rentries.emplace_back();
+                e = (int)bm->rentries.size() - 1;
+            } else {
+                e = bm->rentry_free.back();
+            }
+            bm->rentries[(size_t)e].blocks.reserve((size_t)nfull);
+        }
+        // dropped nodes and entries go to their free lists without allocating
+        bm->rnode_free.reserve(bm->rnodes.capacity());
+        bm->rentry_free.reserve(bm->rentries.capacity());
+        bm->seqs.emplace(seq_id, pkv_block_manager::Seq{});
+    } catch (...) {
+        return PKV_ERR_HOST_ALLOC;
+    }
+    if (reg && !bm->rentry_free.empty() && bm->rentry_free.back() == e) bm->rentry_free.pop_back();
+    // the new sequence's references on the shared blocks, then the drops
+    for (int64_t i = 0; i < shared; ++i) {
+        const int64_t b = bm->rentries[(size_t)donor].blocks[(size_t)i];
+        ++bm->refcount[(size_t)b];  // held by the donor as well: never free here
+        s.blocks.push_back(b);
+    }
+    for (size_t k = 0; k < ndrop; ++k) bm->radix_remove(bm->rorder[k].second);
+    for (int64_t i = shared; i < nblk; ++i) s.blocks.push_back(bm->take());
+    copy_pair[0] = copy_pair[1] = -1;
+    if (L % bs != 0) {  // the match ends inside block `shared`: the donor's copy
+        copy_pair[0] = bm->rentries[(size_t)donor].blocks[(size_t)shared];
+        copy_pair[1] = s.blocks[(size_t)shared];
+    }
+    if (donor >= 0) bm->rentries[(size_t)donor].stamp = ++bm->rclock;
+    if (reg) {
+        pkv_block_manager::REntry& en = bm->rentries[(size_t)e];
+        en.blocks.assign(s.blocks.begin(), s.blocks.begin() + (long)nfull);  // capacity reserved
+        for (int64_t b : en.blocks) ++bm->refcount[(size_t)b];
+        en.stamp = ++bm->rclock;
+        bm->radix_commit(plan, e);
+        ++bm->rlive;
+    }
+    s.length = n;
+    bm->seqs[seq_id] = std::move(s);
+    *num_cached_tokens = L;
+    return PKV_OK;
+}
+
+int64_t pkv_bm_radix_num_entries(const pkv_block_manager* bm) {
+    return bm == nullptr ? -1 : bm->rlive;
+}
+
+int pkv_bm_radix_clear(pkv_block_manager* bm) {
+    if (bm == nullptr) return PKV_ERR_NULL;
+    // least recently used first, as the drops of an allocation go
+    try {
+        bm->rorder.clear();
+        for (size_t e = 0; e < bm->rentries.size(); ++e)
+            if (bm->rentries[e].node >= 0) bm->rorder.emplace_back(bm->rentries[e].stamp, (int)e);
+        bm->rnode_free.reserve(bm->rnodes.capacity());
+        bm->rentry_free.reserve(bm->rentries.capacity());
+    } catch (...) {
+        return PKV_ERR_HOST_ALLOC;
+    }
+    std::sort(bm->rorder.begin(), bm->rorder.end());
+    for (const auto& o : bm->rorder) bm->radix_remove(o.second);
+    return PKV_OK;
+}
 
 int pkv_bm_free(pkv_block_manager* bm, int64_t seq_id) {
     if (bm == nullptr) return PKV_ERR_NULL;

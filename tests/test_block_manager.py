@@ -433,3 +433,105 @@ def test_allocate_cached_abi_edges(lib):
         assert lib.pkv_bm_num_cached(None) == -1
     finally:
         lib.pkv_bm_destroy(h)
+
+
+@pytest.mark.parametrize("seed,num_blocks,bs", [(31, 40, 16), (32, 400, 16), (33, 30, 4),
+                                                 (34, 60, 5), (35, 25, 8)])
+def test_native_radix_matches_oracle(seed, num_blocks, bs):
+    """Radix allocations of prompts grown from a few stems (so prompts share
+    prefixes that end inside blocks as well as on their edges), mixed with
+    chain-cached and plain allocations, appends, forks, frees and clears, on
+    pools small enough that entries are dropped: the native trie's matched
+    lengths, copies, entry counts, tables and reference counts equal the
+    oracle's at every step."""
+    rng = random.Random(seed)
+    pool, nat = BlockPool(num_blocks, bs), Native(num_blocks, bs)
+    stems = [[rng.randrange(40) for _ in range(rng.randrange(bs, 6 * bs))] for _ in range(4)]
+    ids = list(range(14))
+    seen = {"ok": 0, "partial": 0, "aligned": 0, "nomem": 0, "dropped": 0}
+    for step in range(1500):
+        op = rng.choices(["radix", "cached", "alloc", "append", "fork", "free", "clear"],
+                         weights=[6, 1, 1, 3, 1, 3, 0.05])[0]
+        s = rng.choice(ids)
+        if op == "radix":
+            stem = rng.choice(stems)
+            toks = stem[: rng.randrange(0, len(stem) + 1)] + \
+                [rng.randrange(40, 80) for _ in range(rng.randrange(0, 3 * bs))]
+            before = len(pool.radix)
+            try:
+                blocks, cached, copies = pool.allocate_radix(s, toks)
+                ref = ("ok", cached, copies[0] if copies else None)
+            except MemoryError:
+                ref = ("nomem", None, None)
+            except KeyError:
+                ref = ("state", None, None)
+            try:
+                cached, copy = nat.bm.allocate_radix(s, toks)
+                got = ("ok", cached, copy)
+            except MemoryError:
+                got = ("nomem", None, None)
+            except KeyError:
+                got = ("state", None, None)
+            assert got == ref, (step, s, len(toks))
+            if ref[0] == "ok":
+                seen["ok"] += 1
+                seen["partial"] += ref[2] is not None
+                seen["aligned"] += ref[1] > 0 and ref[2] is None
+                seen["dropped"] += len(pool.radix) < before
+            seen["nomem"] += ref[0] == "nomem"
+        elif op == "cached":
+            toks = rng.choice(stems) + [rng.randrange(50) for _ in range(rng.randrange(0, bs))]
+            ref = outcome(lambda: pool.allocate_cached(s, toks)[1])
+            assert outcome(lambda: nat.bm.allocate_cached(s, toks)) == ref, step
+        elif op == "alloc":
+            n = rng.randrange(0, 3 * bs)
+            assert outcome(nat.allocate, s, n)[0] == outcome(pool.allocate, s, n)[0]
+        elif op == "append" and s in pool.tables:
+            n = rng.choice([1, 1, 2, rng.randrange(1, 2 * bs)])
+            assert outcome(nat.append, s, n) == outcome(pool.append, s, n), step
+        elif op == "fork" and s in pool.tables:
+            c = rng.choice(ids)
+            if c not in pool.tables:
+                pool.fork(s, c)
+                nat.fork(s, c)
+        elif op == "free":
+            pool.free(s)
+            nat.free(s)
+        elif op == "clear":
+            pool.radix_clear()
+            nat.bm.radix_clear()
+        pool.check()
+        compare_state(nat, pool, ids)
+        assert nat.bm.radix_num_entries() == len(pool.radix), step
+    print(f"[radix] {seen}")
+    assert seen["ok"] > 100 and seen["partial"] > 10 and seen["aligned"] > 5, seen
+    if num_blocks < 100:
+        assert seen["dropped"] > 0, seen
+    nat.bm.close()
+
+
+def test_radix_abi_edges(lib):
+    bm = lib.pkv_bm_create(8, 4)
+    try:
+        n = ctypes.c_int64(-5)
+        pair = (ctypes.c_int64 * 2)(7, 7)
+        toks = (ctypes.c_int32 * 6)(1, 2, 3, 4, 5, 6)
+        assert lib.pkv_bm_allocate_radix(None, 0, toks, 6, ctypes.byref(n), pair) == binding.PKV_ERR_NULL
+        assert lib.pkv_bm_allocate_radix(bm, 0, None, 6, ctypes.byref(n), pair) == binding.PKV_ERR_NULL
+        assert lib.pkv_bm_allocate_radix(bm, 0, toks, 6, None, pair) == binding.PKV_ERR_NULL
+        assert lib.pkv_bm_allocate_radix(bm, 0, toks, 6, ctypes.byref(n), None) == binding.PKV_ERR_NULL
+        assert lib.pkv_bm_allocate_radix(bm, 0, toks, -1, ctypes.byref(n), pair) == binding.PKV_ERR_SHAPE
+        assert lib.pkv_bm_allocate_radix(bm, 0, None, 0, ctypes.byref(n), pair) == binding.PKV_OK
+        assert n.value == 0 and list(pair) == [-1, -1]
+        assert lib.pkv_bm_allocate_radix(bm, 0, toks, 6, ctypes.byref(n), pair) == binding.PKV_ERR_STATE
+        assert lib.pkv_bm_allocate_radix(bm, 1, toks, 6, ctypes.byref(n), pair) == binding.PKV_OK
+        assert n.value == 0 and lib.pkv_bm_radix_num_entries(bm) == 1
+        # the first 4 tokens (one full block) are cached; 2 more match inside nothing
+        assert lib.pkv_bm_allocate_radix(bm, 2, toks, 6, ctypes.byref(n), pair) == binding.PKV_OK
+        assert n.value == 4 and list(pair) == [-1, -1]
+        assert lib.pkv_bm_radix_num_entries(None) == -1
+        assert lib.pkv_bm_radix_clear(None) == binding.PKV_ERR_NULL
+        assert lib.pkv_bm_radix_clear(bm) == binding.PKV_OK
+        assert lib.pkv_bm_radix_num_entries(bm) == 0
+    finally:
+        lib.pkv_bm_destroy(bm)
