@@ -179,3 +179,72 @@ def test_beam_fork_decode_end_to_end(bs, prompt_len):
         # the partly filled prompt block was shared: copies happened exactly
         # when a beam wrote into a block someone else still held
         assert copies_seen >= (3 if prompt_len % bs else 0)
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_radix_prefix_sharing_end_to_end(bs):
+    """Prompts that share prefixes ending inside blocks and on their edges
+    (the pages' 1000-token case among them) are allocated through the radix
+    tree on a pool small enough that entries are dropped: each call's block
+    copy runs on the device, only tokens from the matched length on are
+    written, and every sequence then decodes against the fp64 oracle over
+    its K/V laid out afresh.  A token's K/V is a fixed function of the token
+    and its position, as a model's would be of the prefix, so reused rows
+    must equal the rows the sequence would have written itself."""
+    hq, hkv, d = 32, 8, 128
+    scale = d ** -0.5
+    print(f"[radix e2e] bs={bs}", flush=True)
+    gen = torch.Generator().manual_seed(77 + bs)
+    vocab, maxpos = 500, 2048
+    tok_k = torch.randn((vocab, hkv, d), generator=gen)
+    tok_v = torch.randn((vocab, hkv, d), generator=gen)
+    pos_k = torch.randn((maxpos, hkv, d), generator=gen) * 0.5
+    pos_v = torch.randn((maxpos, hkv, d), generator=gen) * 0.5
+
+    def rows(tokens, lo, hi):
+        t = torch.tensor(tokens[lo:hi], dtype=torch.int64)
+        p = torch.arange(lo, hi)
+        return (tok_k[t] + pos_k[p]).to(torch.bfloat16), (tok_v[t] + pos_v[p]).to(torch.bfloat16)
+
+    common = torch.randint(0, vocab, (1000,), generator=gen).tolist()
+    other = torch.randint(0, vocab, (700,), generator=gen).tolist()
+
+    def tail(n):
+        return torch.randint(0, vocab, (n,), generator=gen).tolist()
+
+    prompts = [common + tail(200), common + tail(150), common[:992] + tail(40),
+               common[:503] + tail(300), other + tail(90), common + tail(1),
+               other[:650] + tail(11), common[:37] + tail(5), common + tail(300)]
+    nb = {16: 132, 32: 67}[bs]  # tight: later prompts make room by dropping entries
+    k_pool = torch.zeros((nb, bs, hkv, d), dtype=torch.bfloat16, device=DEV)
+    v_pool = torch.zeros_like(k_pool)
+    dense = DenseSeqs()
+    copies = dropped = 0
+    with pkv.BlockManager(nb, bs) as bm:
+        live = []
+        for i, p in enumerate(prompts):
+            if len(live) == 2:  # keep the pool tight: the entries must make room
+                bm.free(live.pop(0))
+            entries = bm.radix_num_entries()
+            cached, copy = bm.allocate_radix(i, p)
+            dropped += bm.radix_num_entries() < entries + (0 if cached >= len(p) // bs * bs else 1)
+            if copy is not None:
+                copies += 1
+                pkv.copy_blocks(k_pool, v_pool, torch.tensor([copy], dtype=torch.int64, device=DEV))
+            nblk = bm.seq_info(i)[1]
+            table, _ = bm.block_table([i], nblk)
+            slots = torch.tensor([int(table[0, q // bs]) * bs + q % bs for q in range(cached, len(p))],
+                                 dtype=torch.int64)
+            kr, vr = rows(p, cached, len(p))
+            if len(slots):
+                pkv.kv_append(kr.to(DEV), vr.to(DEV), slots.to(DEV), k_pool, v_pool)
+            kf, vf = rows(p, 0, len(p))
+            dense.add(i, kf, vf)
+            live.append(i)
+            q = torch.randn((1, hq, d), generator=gen).to(torch.bfloat16)
+            out = pkv.paged_decode_attn(q.to(DEV), k_pool, v_pool, table.to(torch.int32).to(DEV),
+                                        torch.tensor([len(p)], dtype=torch.int32, device=DEV),
+                                        scale, max_context_len=len(p))
+            torch.cuda.synchronize()
+            parity(out, dense.oracle_decode([i], q, bs, scale), what=f"radix prompt {i} (cached {cached})")
+    assert copies >= 4 and dropped >= 2, (copies, dropped)
