@@ -17,6 +17,14 @@ using namespace dec;
 // sequence of up to max_rows rows, causal or under per-row tree masks, its
 // (row, head) pairs the columns of the matrix-core tile: NCB blocks of 16
 // per KV head (the Q operands of two blocks in LDS).
+// Shared staging: workgroups of 8 waves (four KV heads of two waves) for
+// CSPLIT = 2, of 4 waves (one KV head of four) for CSPLIT = 4.  In A/Bs
+// against 4 waves for both: long-context verify 429.4 -> 406.7 us, the
+// 6-row verify unchanged (126.7 / 126.3); token trees (CSPLIT = 4) went
+// 169.0 -> 178.7 with 8, so they keep 4.
+template <int CSPLIT>
+constexpr int cs_waves() { return CSPLIT == 2 ? 8 : 4; }
+
 template <typename KV, int BS, int G, bool OUT_BF16, int NCB, int CSPLIT>
 __global__ void __launch_bounds__(64 * kMaxWavesPerWorker)
 decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* __restrict__ seq_workers,
@@ -34,8 +42,8 @@ decode_streamk_kernel(void* __restrict__ out, float* __restrict__ rec, int32_t* 
     // the matrix-core tile's per-wave V staging (one element otherwise)
     __shared__ __attribute__((aligned(16))) uint16_t s_vx[KV::kMfma && CSPLIT == 1 ? kWaves * kVxWaveElems : 8];
     __shared__ uint4 s_q[NCB > 1 ? kWaves * NCB * 4 * 64 : 1];
-    // shared staging (4-wave workgroups): two 32-token K and V tiles per KV head
-    __shared__ __attribute__((aligned(16))) uint16_t s_st[CSPLIT > 1 ? (4 / CSPLIT) * 4 * 32 * (kHeadDim + 8) : 8];
+    // shared staging (cs_waves waves): two 32-token K and V tiles per KV head
+    __shared__ __attribute__((aligned(16))) uint16_t s_st[CSPLIT > 1 ? (cs_waves<CSPLIT>() / CSPLIT) * 4 * 32 * (kHeadDim + 8) : 8];
     decode_worker<KV, BS, G, OUT_BF16, kWaves, NCB, CSPLIT>(
         out, rec, seq_workers, q, k_cache, v_cache, block_table, max_blocks_per_seq,
         context_lens, max_context_len, num_seqs, num_q_heads, num_kv_heads, scale_log2, out_scale,
@@ -126,10 +134,11 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     auto kern = decode_streamk_kernel<KV, BS, G, OUT_BF16, NCB, CSPLIT>;
     constexpr int kMax = kMaxWavesPerWorker;
     // head groups of kMax waves; the API admits 1..8 and 16 KV heads.  With
-    // shared staging: workgroups of 4 waves, 4 / CSPLIT KV heads each (the
-    // last group's missing heads leave at once).
-    const int hpg = 4 / CSPLIT;
-    const int waves = CSPLIT > 1 ? 4
+    // shared staging: workgroups of cs_waves waves, cs_waves / CSPLIT KV
+    // heads each (the last group's missing heads leave at once; a wave that
+    // has ended no longer holds back the others' barriers).
+    const int hpg = cs_waves<CSPLIT>() / CSPLIT;
+    const int waves = CSPLIT > 1 ? cs_waves<CSPLIT>()
                       : (a.num_kv_heads <= kMax ? a.num_kv_heads
                                                 : (a.num_kv_heads % kMax == 0 ? kMax : 1));
     const int groups = CSPLIT > 1 ? (a.num_kv_heads + hpg - 1) / hpg : a.num_kv_heads / waves;
