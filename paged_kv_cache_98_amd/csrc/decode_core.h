@@ -489,8 +489,14 @@ constexpr int kMinTilesPerWorker = 4;   // fewer waves for tiny batches
 constexpr int kMaxWavesPerWorker = 8;
 constexpr int64_t kMaxWorkers = 1024;    // workgroups of 8 waves an MI355X holds at most
 constexpr int64_t kRowsMaxWaves = 2048;  // waves an MI355X holds at two per SIMD
-// Cost of a sequence boundary inside a worker's range, in quarter tiles.
+// Cost of a sequence boundary inside a worker's range, in quarter tiles:
+// single-row decodes, and the rows path (several query rows per sequence,
+// whose boundary also reloads the column blocks' queries and, with shared
+// staging, refills the LDS pipeline).  Rows path, in A/Bs against 6:
+// 6-row verify 127.1 -> 126.3 us, token trees 169.9 -> 168.7, FP8 verify
+// 73.0 -> 70.9 (16 measured between the two).
 constexpr int64_t kSeqCost = 6;
+constexpr int64_t kSeqCostRows = 32;
 
 __device__ __forceinline__ int clamp_ctx(int ctx, int max_context_len) {
     return ctx < 0 ? 0 : (ctx > max_context_len ? max_context_len : ctx);
@@ -640,22 +646,23 @@ __device__ __forceinline__ void decode_worker(
     const int col = lane % L::kRowLanes;
     const int64_t w = worker;
     // Ranges of equal cost, not equal tiles: a tile costs 4 units and every
-    // sequence boundary kSeqCost more (a worker that starts a new sequence
+    // sequence boundary kSeqC more (a worker that starts a new sequence
     // restarts its load pipeline and loads another query and block-id
     // window), so workers that cross more boundaries get fewer tiles.
     // Worker wi starts at the first tile t with cost(t) >= wi * total / W,
-    // cost(t) = 4 t + kSeqCost * seq(t); the sequence is found among the
+    // cost(t) = 4 t + kSeqC * seq(t); the sequence is found among the
     // costs of the sequences' first tiles.
-    const int64_t cost_total = 4 * U + kSeqCost * (int64_t)(num_seqs - 1);
+    const int64_t kSeqC = max_rows > 1 ? kSeqCostRows : kSeqCost;
+    const int64_t cost_total = 4 * U + kSeqC * (int64_t)(num_seqs - 1);
     auto range_start = [&](int64_t wi) -> int64_t {
         if (wi >= W) return U;
         const int64_t target = wi * cost_total / W;
-        int lo = 0, hi = num_seqs;  // largest i with 4 cum[i] + kSeqCost i <= target
+        int lo = 0, hi = num_seqs;  // largest i with 4 cum[i] + kSeqC i <= target
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
-            if (4 * (int64_t)s_cum[mid] + kSeqCost * (int64_t)mid <= target) lo = mid; else hi = mid;
+            if (4 * (int64_t)s_cum[mid] + kSeqC * (int64_t)mid <= target) lo = mid; else hi = mid;
         }
-        int64_t tt = (target - kSeqCost * (int64_t)lo + 3) / 4;
+        int64_t tt = (target - kSeqC * (int64_t)lo + 3) / 4;
         tt = tt < s_cum[lo] ? s_cum[lo] : tt;
         return tt > s_cum[lo + 1] ? s_cum[lo + 1] : tt;
     };
