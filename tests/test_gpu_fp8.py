@@ -574,3 +574,22 @@ def test_tree_fp8_per_block(group, nodes):
                              tree_mask=masks.to(DEV))
     torch.cuda.synchronize()
     parity(out, ref, what=w.name)
+
+
+@pytest.mark.parametrize("hkv,group", [(1, 4), (8, 2), (16, 1), (16, 8)])
+def test_decode_fp8_per_block_kv_heads(hkv, group):
+    """Per-(block, head) scales with 1, 8 and 16 KV heads (16: two head
+    groups of 8 waves), an empty sequence among them: each wave reads its own
+    head's scale of every block."""
+    w = W.make_workload(f"fp8pb_hkv{hkv}_g{group}", [5, 700, 0, 1500, 33],
+                        num_q_heads=hkv * group, num_kv_heads=hkv, block_size=16,
+                        seed=3150 + hkv + group)
+    print(f"[fp8 per block] {w.name}", flush=True)
+    bc = W.materialize(w, logical=True, poison=True)
+    kc, vc, ks, vs = W.fp8_block_pools(bc, seed=hkv * 3 + group)
+    ref = oracle_fp8_pb(bc, kc, vc, ks, vs)
+    b = bc.to(DEV)
+    out = run_fp8_pb(b, kc.to(DEV), vc.to(DEV), ks.to(DEV), vs.to(DEV), w)
+    torch.cuda.synchronize()
+    assert torch.all(out[2] == 0)
+    parity(out, ref, what=w.name)
