@@ -340,10 +340,12 @@ def workload_by_name(name):
         "mixed_prefill": lambda: W.mixed_prefill(),
         # the chunk and verify batches over an FP8 (E4M3) cache
         "prefill_chunks_fp8": lambda: W.mixed_prefill(num_decodes=0),
+        "mixed_prefill_fp8": lambda: W.mixed_prefill(),
         "spec_verify_fp8": lambda: W.spec_verify(),
         # the same over FP8 pools with one scale per (block, KV head)
         "llama8b_decode_fp8_per_block": lambda: W.llama8b_decode(),
         "prefill_chunks_fp8_per_block": lambda: W.mixed_prefill(num_decodes=0),
+        "mixed_prefill_fp8_per_block": lambda: W.mixed_prefill(),
         "spec_verify_fp8_per_block": lambda: W.spec_verify(),
     }
     if name not in table:

@@ -617,9 +617,8 @@ int pkv_paged_prefill_attn_tree_fp8(void *out, int out_dtype, const void *q,
  * staged as fp16(code x ratio) (the ratio rounded to fp16, the product
  * rounded once more); on the rows path (as over FP8 pools: chunks of at
  * most 16 rows and 32 (row, head) columns per KV head) P is scaled as in
- * the decode.
- * Chunks and single-row sequences in one call run one after the other (the
- * chunk kernel, then the decode kernels), not in one grid.
+ * the decode.  Chunks and single-row sequences in one call share one grid,
+ * as over per-cache pools.
  */
 int pkv_paged_prefill_attn_fp8_per_block(void *out, int out_dtype, const void *q,
                                          const int32_t *cu_q_lens, const void *k_cache,

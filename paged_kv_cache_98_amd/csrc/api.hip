@@ -524,9 +524,8 @@ int prefill_call(void* out, int out_dtype, const void* q, const int32_t* cu_q_le
         d.max_workers = pkv::decode_max_workers(num_seqs, max_context_len, max_q_len, num_kv_heads);
         return to_status(pkv::launch_decode(d, s));
     }
-    if (max_q_len > 1 && !streamk && !block_scales) {
-        // chunks and decode rows in one grid, sharing the CUs (per-block
-        // scales: the chunk kernel, then the decode kernels)
+    if (max_q_len > 1 && !streamk) {
+        // chunks and decode rows in one grid, sharing the CUs
         const hipError_t e = pkv::launch_mixed(a, d, s);
         if (e != hipErrorNotSupported) return to_status(e);
     }

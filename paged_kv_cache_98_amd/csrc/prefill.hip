@@ -915,7 +915,7 @@ prefill_mfma_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
 // decode merge kernel afterwards.
 // LDS: the chunk path's K / V^T tile buffers; a decode worker keeps its tile
 // prefix sums, its waves' V tiles and their partial sums in them instead.
-template <int BS, int G, bool OUT_BF16, bool FP8>
+template <int BS, int G, bool OUT_BF16, bool FP8, bool BSC = false>
 __global__ void __launch_bounds__(kThreads, 2)
 mixed_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
              const int32_t* __restrict__ cu_q_lens, const void* __restrict__ k_cache,
@@ -925,9 +925,11 @@ mixed_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
              float scale_log2, float out_scale, int causal, float* __restrict__ dec_rec,
              int32_t* __restrict__ dec_seq_workers, int dec_workers, int dec_groups,
              int dec_per_xcd, int num_slots, int chunk_per_xcd,
-             const uint64_t* __restrict__ tree_mask) {
+             const uint64_t* __restrict__ tree_mask, const float* __restrict__ k_scales,
+             const float* __restrict__ v_scales) {
     __shared__ __attribute__((aligned(16))) uint16_t s_ks[2][kKsElems];
     __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kVtElems];
+    __shared__ float s_sc[BSC ? 16 : 1];
     const int b = blockIdx.x;
     const int xcd = b % 8;
     const int k = b / 8;
@@ -936,8 +938,9 @@ mixed_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
         if (d >= dec_workers * dec_groups) return;
         // the tile policies of the decode call (dispatched in decode.hip);
         // the waves' V tiles of the matrix-core ones, then the wave partials
-        using KV = std::conditional_t<FP8, std::conditional_t<(G >= 4), dec::KvFp8Mfma, dec::KvFp8Wide>,
-                                      std::conditional_t<(G >= 8), dec::KvBf16Mfma, dec::KvBf16>>;
+        using KV8 = std::conditional_t<BSC, std::conditional_t<(G >= 4), dec::KvFp8MfmaBh, dec::KvFp8WideBh>,
+                                       std::conditional_t<(G >= 4), dec::KvFp8Mfma, dec::KvFp8Wide>>;
+        using KV = std::conditional_t<FP8, KV8, std::conditional_t<(G >= 8), dec::KvBf16Mfma, dec::KvBf16>>;
         constexpr int kVxElems = (kThreads / 64) * dec::kVxWaveElems;
         static_assert(2 * kVxElems + 4 * (kThreads / 64) <= (int)sizeof(s_vt), "decode LDS");
         int32_t* s_cum = reinterpret_cast<int32_t*>(&s_ks[0][0]);
@@ -947,16 +950,17 @@ mixed_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
             out, dec_rec, dec_seq_workers, q, k_cache, v_cache, block_table, max_blocks_per_seq,
             context_lens, max_context_len, num_seqs, num_q_heads, num_kv_heads, scale_log2,
             out_scale, dec_workers, cu_q_lens, s_cum, s_part, d % dec_workers, d / dec_workers,
-            s_vx);
+            s_vx, 1, 1, nullptr, nullptr, nullptr, k_scales, v_scales);
         return;
     }
     const int item = xcd * chunk_per_xcd + (k - dec_per_xcd);
     if (k - dec_per_xcd >= chunk_per_xcd || item >= num_slots * num_kv_heads) return;
     const int kvh = item / num_slots;
-    run_slot<BS, G, OUT_BF16, FP8>(s_ks, s_vt, out, q, cu_q_lens, k_cache, v_cache, block_table,
-                                   max_blocks_per_seq, context_lens, max_context_len, num_seqs,
-                                   num_q_heads, num_kv_heads, scale_log2, out_scale, causal,
-                                   1, tree_mask, kvh, item - kvh * num_slots);
+    run_slot<BS, G, OUT_BF16, FP8, BSC>(s_ks, s_vt, out, q, cu_q_lens, k_cache, v_cache,
+                                        block_table, max_blocks_per_seq, context_lens,
+                                        max_context_len, num_seqs, num_q_heads, num_kv_heads,
+                                        scale_log2, out_scale, causal, 1, tree_mask, kvh,
+                                        item - kvh * num_slots, k_scales, v_scales, s_sc);
 }
 
 // Stream-K units of sequence i in a call of chunks that fit one workgroup
@@ -1309,10 +1313,10 @@ hipError_t launch_prefill_bs(const PrefillArgs& a, hipStream_t s) {
 constexpr int kMixedCusPerXcd = 32;
 constexpr int kMixedDecodePerXcd = 48;
 
-template <int BS, int G, bool OUT_BF16, bool FP8>
+template <int BS, int G, bool OUT_BF16, bool FP8, bool BSC = false>
 hipError_t launch_mixed_t(const PrefillArgs& a, const DecodeArgs& d, hipStream_t stream) {
     constexpr int P = kCols / G;
-    auto kern = mixed_kernel<BS, G, OUT_BF16, FP8>;
+    auto kern = mixed_kernel<BS, G, OUT_BF16, FP8, BSC>;
     int resident = 0, cus = 0, dev = 0;
     hipError_t e = resident_workgroups(reinterpret_cast<const void*>(kern), kThreads, 0,
                                        &resident);
@@ -1337,7 +1341,7 @@ hipError_t launch_mixed_t(const PrefillArgs& a, const DecodeArgs& d, hipStream_t
                        a.max_blocks_per_seq, a.context_lens, a.max_context_len, a.num_seqs,
                        a.num_q_heads, a.num_kv_heads, a.scale_log2, a.out_scale, a.causal ? 1 : 0,
                        d.records, d.seq_workers, (int)dec_workers, dec_groups, dec_per_xcd,
-                       num_slots, chunk_per_xcd, a.tree_mask);
+                       num_slots, chunk_per_xcd, a.tree_mask, a.k_scales, a.v_scales);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_decode_merge(d, stream);
@@ -1345,6 +1349,9 @@ hipError_t launch_mixed_t(const PrefillArgs& a, const DecodeArgs& d, hipStream_t
 
 template <int BS, int G>
 hipError_t launch_mixed_g(const PrefillArgs& a, const DecodeArgs& d, hipStream_t s) {
+    if (a.kv_fp8 && a.k_scales != nullptr)
+        return a.out_bf16 ? launch_mixed_t<BS, G, true, true, true>(a, d, s)
+                          : launch_mixed_t<BS, G, false, true, true>(a, d, s);
     if (a.kv_fp8)
         return a.out_bf16 ? launch_mixed_t<BS, G, true, true>(a, d, s)
                           : launch_mixed_t<BS, G, false, true>(a, d, s);
