@@ -593,3 +593,37 @@ def test_decode_fp8_per_block_kv_heads(hkv, group):
     torch.cuda.synchronize()
     assert torch.all(out[2] == 0)
     parity(out, ref, what=w.name)
+
+
+def test_mixed_fp8_per_block_full_batch_sampled():
+    """The full mixed batch (4 x 512-row chunks and 128 decodes behind an
+    800-token shared prefix) over per-(block, head)-scaled FP8 pools, in the
+    one grid the benchmark times; every row of one chunk and of sampled
+    decode rows against the oracle, and a second call gives the same bits."""
+    w = W.mixed_prefill()
+    print(f"[fp8 per block mixed full] {w.name}", flush=True)
+    b = W.materialize(w, device=DEV, poison=True)
+    kd, vd, ksd, vsd = W.fp8_block_pools(b, seed=9)
+    out = run_prefill_fp8_pb(b, kd, vd, ksd, vsd)
+    again = run_prefill_fp8_pb(b, kd, vd, ksd, vsd)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(out)) and torch.equal(out, again)
+    ctx, ql = list(w.context_lens), list(w.q_lens)
+    cu = b.cu_q_lens.cpu()
+    bt = b.block_table.cpu()
+    chunks = [i for i in range(len(ql)) if ql[i] > 1]
+    decodes = [i for i in range(len(ql)) if ql[i] == 1]
+    for i in [chunks[-1]] + [decodes[k] for k in (0, len(decodes) // 2, len(decodes) - 1)]:
+        n = ctx[i]
+        ids = bt[i, : -(-n // w.block_size)].to(torch.int64)
+        idd = ids.to(DEV)
+        rows = slice(int(cu[i]), int(cu[i + 1]))
+        ref = fp8.paged_prefill_fp8(bits16(b.q[rows]), codes(kd.index_select(0, idd)),
+                                    codes(vd.index_select(0, idd)),
+                                    ksd.index_select(0, idd).cpu().numpy(),
+                                    vsd.index_select(0, idd).cpu().numpy(),
+                                    np.arange(len(ids), dtype=np.int32)[None, :],
+                                    np.array([n], dtype=np.int32),
+                                    np.array([0, rows.stop - rows.start], dtype=np.int32),
+                                    w.scale, causal=True)
+        parity(out[rows], ref, what=f"fp8 per block mixed seq {i} (ctx {n}, rows {ql[i]})")
