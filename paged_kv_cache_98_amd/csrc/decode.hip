@@ -69,18 +69,22 @@ decode_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
     const int seq = blockIdx.y;
     const int r = blockIdx.z;
     if (h >= num_q_heads) return;
-    if (r >= rows_of(cu_q_lens, seq, max_rows)) return;  // not a row of ours
+    // the row count, the context length and the workers holding the
+    // sequence's first and last tiles are independent loads: all four are
+    // issued before any of them is needed (the worker ids are read even
+    // where the sequence turns out to have no tiles; they are in bounds)
+    const int rows = rows_of(cu_q_lens, seq, max_rows);
+    const int ctx_raw = context_lens[seq];
+    const int32_t first = seq_workers[seq];
+    const int64_t wl = seq_workers[num_seqs + seq];
+    if (r >= rows) return;  // not a row of ours
     const size_t e = ((size_t)(row_of(cu_q_lens, seq) + r) * num_q_heads + h) * D + 2 * lane;
-    const int ctx = clamp_ctx(context_lens[seq], max_context_len);
-    if (ctx == 0) {  // nothing to attend to: a defined all-zero row
+    if (clamp_ctx(ctx_raw, max_context_len) == 0) {  // nothing to attend to: a defined all-zero row
         store1<OUT_BF16>(out, e, 0.0f);
         store1<OUT_BF16>(out, e + 1, 0.0f);
         return;
     }
-    // the workers holding the sequence's first and last tiles (it has tiles)
-    const int32_t first = seq_workers[seq];
     const int64_t wf = first & 0x3fffffff;
-    const int64_t wl = seq_workers[num_seqs + seq];
     if (wf == wl) return;  // finalised by its only worker
     const int slot_f = (first >> 30) & 1;
 
@@ -88,6 +92,17 @@ decode_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
         const int slot = w == wf ? slot_f : 0;
         return rec + (((size_t)(w * 2 + slot) * max_rows + r) * num_q_heads + h) * kRecStride;
     };
+    // accumulator rows of pieces p .. p + 7 (those that exist), loaded
+    // eight pieces ahead of their use; the first eight go out together
+    // with the pieces' (m, l)
+    float2 av[8];
+    auto load8 = [&](int64_t p) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            av[u] = p + u <= wl ? *reinterpret_cast<const float2*>(rec_of(p + u) + 2 * lane)
+                                : make_float2(0.0f, 0.0f);
+    };
+    load8(wf);
     // maximum over the pieces' running maxima, one piece per lane; the
     // first 64 pieces' (m, l) stay in their lanes
     float2 ml0 = make_float2(-INFINITY, 0.0f);
@@ -97,8 +112,7 @@ decode_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
     // then the pieces in worker order, 64 at a time: lane k holds the scale
-    // exp2(m - mx) and the sum l of piece base + k, and the accumulator
-    // rows are loaded eight pieces ahead of their use
+    // exp2(m - mx) and the sum l of piece base + k
     float L = 0.0f, a0 = 0.0f, a1 = 0.0f;
     for (int64_t base = wf; base <= wl; base += 64) {
         const int cnt = wl - base + 1 < 64 ? (int)(wl - base + 1) : 64;
@@ -109,18 +123,17 @@ decode_merge_kernel(void* __restrict__ out, const float* __restrict__ rec,
         const float fk = lane < cnt ? fast_exp2(ml.x - mx) : 0.0f;
         const float lk = ml.y;
         for (int k = 0; k < cnt; k += 8) {
-            float2 av[8];
+            float2 cur[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                av[u] = k + u < cnt ? *reinterpret_cast<const float2*>(rec_of(base + k + u) + 2 * lane)
-                                    : make_float2(0.0f, 0.0f);
+            for (int u = 0; u < 8; ++u) cur[u] = av[u];
+            if (base + k + 8 <= wl) load8(base + k + 8);
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 if (k + u >= cnt) break;
                 const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fk), k + u));
                 L = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(lk), k + u)), f, L);
-                a0 = fmaf(av[u].x, f, a0);
-                a1 = fmaf(av[u].y, f, a1);
+                a0 = fmaf(cur[u].x, f, a0);
+                a1 = fmaf(cur[u].y, f, a1);
             }
         }
     }
