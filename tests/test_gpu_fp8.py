@@ -2,6 +2,8 @@
 against the oracle's quantiser, and decode attention over FP8 pools against
 the fp64 oracle on the same codes (codes made by torch's own float8 cast,
 never by this library)."""
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -34,6 +36,47 @@ def oracle_fp8(b_cpu, kc, vc, k_scale=W.FP8_SCALE, v_scale=W.FP8_SCALE):
     w = b_cpu.workload
     return fp8.paged_decode_fp8(bits16(b_cpu.q), codes(kc), codes(vc), k_scale, v_scale,
                                 b_cpu.block_table.numpy(), b_cpu.context_lens.numpy(), w.scale)
+
+
+def fp8_every_seq(out, b, kd, vd, ks, vs, what, seqs=None, rows=False):
+    """Sequences of a full-size batch (all of them unless seqs names some)
+    against the fp64 oracle, each over its own blocks: decode (one row per
+    sequence) or, with rows, the causal rows cu_q_lens gives it.  The
+    oracle runs on host threads, one sequence each (numpy leaves the GIL
+    in its array work); the comparisons follow in sequence order."""
+    w = b.workload
+    kc, vc = codes(kd), codes(vd)
+    ksn = ks if np.isscalar(ks) else ks.detach().cpu().numpy()
+    vsn = vs if np.isscalar(vs) else vs.detach().cpu().numpy()
+    qb = bits16(b.q)
+    ctx = b.context_lens.cpu().numpy()
+    bt = b.block_table.cpu().numpy()
+    cu = b.cu_q_lens.cpu().numpy() if rows else None
+    seqs = list(range(len(ctx))) if seqs is None else list(seqs)
+
+    def out_rows(i):
+        return slice(i, i + 1) if cu is None else slice(int(cu[i]), int(cu[i + 1]))
+
+    def one(i):
+        n = int(ctx[i])
+        ids = bt[i, : -(-n // w.block_size)].astype(np.int64)
+        sk = ksn if np.isscalar(ksn) else ksn[ids]
+        sv = vsn if np.isscalar(vsn) else vsn[ids]
+        local = np.arange(len(ids), dtype=np.int32)[None, :]
+        r = out_rows(i)
+        if cu is None:
+            return fp8.paged_decode_fp8(qb[r], kc[ids], vc[ids], sk, sv, local,
+                                        np.array([n], dtype=np.int32), w.scale)
+        return fp8.paged_prefill_fp8(qb[r], kc[ids], vc[ids], sk, sv, local,
+                                     np.array([n], dtype=np.int32),
+                                     np.array([0, r.stop - r.start], dtype=np.int32),
+                                     w.scale, causal=True)
+
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        refs = list(ex.map(one, seqs))
+    for i, ref in zip(seqs, refs):
+        parity(out[out_rows(i)], ref, what=f"{what} seq {i} (ctx {int(ctx[i])})")
+    print(f"[{what}] {len(seqs)} sequences against the oracle", flush=True)
 
 
 def edge_values(scale):
@@ -170,33 +213,22 @@ def test_fp8_append_then_decode():
     parity(out, ref, what="fp8 append + decode")
 
 
-def test_decode_fp8_full_8b_batch_sampled():
+def test_decode_fp8_full_8b_batch():
     """The full 64-sequence 8B-shaped batch in the launch configuration the
-    benchmark times; sampled sequences checked against the oracle."""
+    benchmark times; every sequence against the oracle."""
     w = W.llama8b_decode()
     print(f"[fp8 full] {w.name}", flush=True)
     b = W.materialize(w, device=DEV, poison=True)
     kd, vd = W.fp8_pools(b)
     out = run_fp8(b.q, kd, vd, b.block_table, b.context_lens, w)
     torch.cuda.synchronize()
-    ctx = list(w.context_lens)
-    seqs = sorted({ctx.index(max(ctx)), ctx.index(min(ctx)), 0, 17, 42, 63})
-    bt = b.block_table.cpu()
-    for i in seqs:
-        n = ctx[i]
-        ids = bt[i, : -(-n // w.block_size)].to(torch.int64)
-        sub_k = codes(kd.index_select(0, ids.to(DEV)))
-        sub_v = codes(vd.index_select(0, ids.to(DEV)))
-        ref = fp8.paged_decode_fp8(bits16(b.q[i:i + 1]), sub_k, sub_v, W.FP8_SCALE, W.FP8_SCALE,
-                                   np.arange(len(ids), dtype=np.int32)[None, :],
-                                   np.array([n], dtype=np.int32), w.scale)
-        parity(out[i:i + 1], ref, what=f"fp8 full batch seq {i} (ctx {n})")
+    fp8_every_seq(out, b, kd, vd, W.FP8_SCALE, W.FP8_SCALE, "fp8 full 8b batch")
 
 
-def test_decode_fp8_full_70b_batch_sampled():
+def test_decode_fp8_full_70b_batch():
     """The 256-sequence 70B-shaped batch (8 query heads per KV head: the
-    matrix-core tile) over FP8 pools, as the benchmark times it; sampled
-    sequences against the oracle."""
+    matrix-core tile) over FP8 pools, as the benchmark times it; every
+    sequence against the oracle."""
     w = W.llama70b_decode(block_size=16)
     print(f"[fp8 full 70b] {w.name}", flush=True)
     b = W.materialize(w, device=DEV, poison=True)
@@ -204,24 +236,13 @@ def test_decode_fp8_full_70b_batch_sampled():
     out = run_fp8(b.q, kd, vd, b.block_table, b.context_lens, w)
     torch.cuda.synchronize()
     assert torch.all(torch.isfinite(out))
-    ctx = list(w.context_lens)
-    seqs = sorted({ctx.index(max(ctx)), ctx.index(min(ctx)), 0, 100, 255})
-    bt = b.block_table.cpu()
-    for i in seqs:
-        n = ctx[i]
-        ids = bt[i, : -(-n // w.block_size)].to(torch.int64)
-        sub_k = codes(kd.index_select(0, ids.to(DEV)))
-        sub_v = codes(vd.index_select(0, ids.to(DEV)))
-        ref = fp8.paged_decode_fp8(bits16(b.q[i:i + 1]), sub_k, sub_v, W.FP8_SCALE, W.FP8_SCALE,
-                                   np.arange(len(ids), dtype=np.int32)[None, :],
-                                   np.array([n], dtype=np.int32), w.scale)
-        parity(out[i:i + 1], ref, what=f"fp8 70b batch seq {i} (ctx {n})")
+    fp8_every_seq(out, b, kd, vd, W.FP8_SCALE, W.FP8_SCALE, "fp8 70b batch")
 
 
-def test_verify_fp8_full_batch_sampled():
+def test_verify_fp8_full_batch():
     """The 64-sequence 6-row verify batch over FP8 pools, as the benchmark
-    times it (the rows path: two column blocks per wave); every row of
-    sampled sequences against the oracle."""
+    times it (the rows path: two column blocks per wave); every row of every
+    sequence against the oracle."""
     w = W.spec_verify()
     print(f"[fp8 verify full] {w.name}", flush=True)
     b = W.materialize(w, device=DEV, poison=True)
@@ -232,21 +253,7 @@ def test_verify_fp8_full_batch_sampled():
                                      causal=True)
     torch.cuda.synchronize()
     assert torch.all(torch.isfinite(out))
-    ctx = list(w.context_lens)
-    cu = b.cu_q_lens.cpu()
-    bt = b.block_table.cpu()
-    for i in sorted({ctx.index(max(ctx)), ctx.index(min(ctx)), 0, 31, 63}):
-        n = ctx[i]
-        ids = bt[i, : -(-n // w.block_size)].to(torch.int64)
-        sub_k = codes(kd.index_select(0, ids.to(DEV)))
-        sub_v = codes(vd.index_select(0, ids.to(DEV)))
-        rows = slice(int(cu[i]), int(cu[i + 1]))
-        ref = fp8.paged_prefill_fp8(bits16(b.q[rows]), sub_k, sub_v, W.FP8_SCALE, W.FP8_SCALE,
-                                    np.arange(len(ids), dtype=np.int32)[None, :],
-                                    np.array([n], dtype=np.int32),
-                                    np.array([0, rows.stop - rows.start], dtype=np.int32),
-                                    w.scale, causal=True)
-        parity(out[rows], ref, what=f"fp8 verify batch seq {i} (ctx {n})")
+    fp8_every_seq(out, b, kd, vd, W.FP8_SCALE, W.FP8_SCALE, "fp8 verify batch", rows=True)
 
 
 # (context length including the chunk, chunk rows): whole prompts, chunks
@@ -459,9 +466,9 @@ def test_fp8_per_block_append_then_decode():
     parity(out, ref, what="fp8 per block append + decode")
 
 
-def test_decode_fp8_per_block_full_8b_batch_sampled():
+def test_decode_fp8_per_block_full_8b_batch():
     """The 64-sequence 8B-shaped batch over per-(block, head)-scaled FP8 pools,
-    as the benchmark times it; sampled sequences against the oracle."""
+    as the benchmark times it; every sequence against the oracle."""
     w = W.llama8b_decode()
     print(f"[fp8 per block full 8b] {w.name}", flush=True)
     b = W.materialize(w, device=DEV, poison=True)
@@ -469,19 +476,24 @@ def test_decode_fp8_per_block_full_8b_batch_sampled():
     out = run_fp8_pb(b, kd, vd, ksd, vsd, w)
     torch.cuda.synchronize()
     assert torch.all(torch.isfinite(out))
-    ctx = list(w.context_lens)
-    bt = b.block_table.cpu()
-    for i in sorted({ctx.index(max(ctx)), ctx.index(min(ctx)), 0, 31, 63}):
-        n = ctx[i]
-        ids = bt[i, : -(-n // w.block_size)].to(torch.int64)
-        idd = ids.to(DEV)
-        ref = fp8.paged_decode_fp8(bits16(b.q[i:i + 1]), codes(kd.index_select(0, idd)),
-                                   codes(vd.index_select(0, idd)),
-                                   ksd.index_select(0, idd).cpu().numpy(),
-                                   vsd.index_select(0, idd).cpu().numpy(),
-                                   np.arange(len(ids), dtype=np.int32)[None, :],
-                                   np.array([n], dtype=np.int32), w.scale)
-        parity(out[i:i + 1], ref, what=f"fp8 per block 8b batch seq {i} (ctx {n})")
+    fp8_every_seq(out, b, kd, vd, ksd, vsd, "fp8 per block 8b batch")
+
+
+def test_verify_fp8_per_block_full_batch():
+    """The 64-sequence 6-row verify batch over per-(block, head)-scaled FP8
+    pools, as the benchmark times it (the rows path); every row of every
+    sequence against the oracle."""
+    w = W.spec_verify()
+    print(f"[fp8 per block verify full] {w.name}", flush=True)
+    b = W.materialize(w, device=DEV, poison=True)
+    kd, vd, ksd, vsd = W.fp8_block_pools(b, seed=8)
+    out = pkv.paged_prefill_attn_fp8_per_block(b.q, b.cu_q_lens, kd, vd, ksd, vsd, b.block_table,
+                                               b.context_lens, w.scale,
+                                               max_context_len=w.max_context_len,
+                                               max_q_len=w.max_q_len, causal=True)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(out))
+    fp8_every_seq(out, b, kd, vd, ksd, vsd, "fp8 per block verify batch", rows=True)
 
 
 def run_prefill_fp8_pb(b, kd, vd, ksd, vsd, causal=True, out_dtype=torch.float32, tree_mask=None):
@@ -595,11 +607,11 @@ def test_decode_fp8_per_block_kv_heads(hkv, group):
     parity(out, ref, what=w.name)
 
 
-def test_mixed_fp8_per_block_full_batch_sampled():
+def test_mixed_fp8_per_block_full_batch():
     """The full mixed batch (4 x 512-row chunks and 128 decodes behind an
     800-token shared prefix) over per-(block, head)-scaled FP8 pools, in the
-    one grid the benchmark times; every row of one chunk and of sampled
-    decode rows against the oracle, and a second call gives the same bits."""
+    one grid the benchmark times; every row of every chunk and decode
+    against the oracle, and a second call gives the same bits."""
     w = W.mixed_prefill()
     print(f"[fp8 per block mixed full] {w.name}", flush=True)
     b = W.materialize(w, device=DEV, poison=True)
@@ -608,22 +620,4 @@ def test_mixed_fp8_per_block_full_batch_sampled():
     again = run_prefill_fp8_pb(b, kd, vd, ksd, vsd)
     torch.cuda.synchronize()
     assert torch.all(torch.isfinite(out)) and torch.equal(out, again)
-    ctx, ql = list(w.context_lens), list(w.q_lens)
-    cu = b.cu_q_lens.cpu()
-    bt = b.block_table.cpu()
-    chunks = [i for i in range(len(ql)) if ql[i] > 1]
-    decodes = [i for i in range(len(ql)) if ql[i] == 1]
-    for i in [chunks[-1]] + [decodes[k] for k in (0, len(decodes) // 2, len(decodes) - 1)]:
-        n = ctx[i]
-        ids = bt[i, : -(-n // w.block_size)].to(torch.int64)
-        idd = ids.to(DEV)
-        rows = slice(int(cu[i]), int(cu[i + 1]))
-        ref = fp8.paged_prefill_fp8(bits16(b.q[rows]), codes(kd.index_select(0, idd)),
-                                    codes(vd.index_select(0, idd)),
-                                    ksd.index_select(0, idd).cpu().numpy(),
-                                    vsd.index_select(0, idd).cpu().numpy(),
-                                    np.arange(len(ids), dtype=np.int32)[None, :],
-                                    np.array([n], dtype=np.int32),
-                                    np.array([0, rows.stop - rows.start], dtype=np.int32),
-                                    w.scale, causal=True)
-        parity(out[rows], ref, what=f"fp8 per block mixed seq {i} (ctx {n}, rows {ql[i]})")
+    fp8_every_seq(out, b, kd, vd, ksd, vsd, "fp8 per block mixed batch", rows=True)
