@@ -255,9 +255,12 @@ struct KvFp8MfmaBh : KvFp8Mfma {
 __device__ __forceinline__ void load_block_scales(const float* k_scales, const float* v_scales,
                                                   int phys, int num_kv_heads, int kvh, float& ks,
                                                   float& vs) {
-    const size_t e = (size_t)phys * num_kv_heads + kvh;
-    ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(k_scales + e), 0, 0, 0));
-    vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(v_scales + e), 0, 0, 0));
+    // the block's row of the table as the (wave-uniform) buffer base, the
+    // head as the offset: a per-lane base would put a loop around each load
+    const size_t b = (size_t)phys * num_kv_heads;
+    const uint32_t off = (uint32_t)kvh * (uint32_t)sizeof(float);
+    ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(k_scales + b), off, 0, 0));
+    vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(v_scales + b), off, 0, 0));
 }
 
 template <typename KV>
@@ -640,7 +643,7 @@ __device__ __forceinline__ void decode_worker(
     // CSPLIT waves per KV head (sub = which of them), each on its own 16
     // columns, sharing the KV head's tiles through LDS
     const int kvh = group * ((nthr >> 6) / CSPLIT) + (tid >> 6) / CSPLIT;
-    const int sub = (tid >> 6) % CSPLIT;
+    const int sub = __builtin_amdgcn_readfirstlane((tid >> 6) % CSPLIT);  // wave-uniform
     if (kvh >= num_kv_heads) return;  // a wave with no head: nothing below waits for it
     const int row = lane / L::kRowLanes;
     const int col = lane % L::kRowLanes;
@@ -758,7 +761,10 @@ __device__ __forceinline__ void decode_worker(
             for (int i = 0; i < NLD; ++i) {
                 const int ii = sub * NLD + i;       // 0 .. 7 K, 8 .. 15 V
                 const int tok = 4 * (ii & 7) + (lane >> 4);  // 0 .. 31
-                const int j = 2 * jj + (tok >> 4);  // 16-token tile of the piece
+                // 16-token tile of the piece: tok / 16, which is the same in
+                // every lane of load i, so the tile's block id and buffer
+                // base stay wave-uniform (no per-lane loop around the load)
+                const int j = 2 * jj + ((ii & 7) >> 2);
                 const bool valid = j < n && (tile0 + j) * kTileTokens + (tok & 15) < ctx;
                 const size_t o0 = tile_bytes<BS>(ids, tile0 + (j < n ? j : n - 1), row_bytes, lane);
                 const __amdgpu_buffer_rsrc_t r = buffer_rsrc((ii < 8 ? kbase : vbase) + o0);
